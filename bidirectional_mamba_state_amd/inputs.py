@@ -1,0 +1,134 @@
+"""Seeded synthetic inputs for the bidirectional Mamba state hot path.
+
+This module only draws and rounds numbers; it contains none of the scan's arithmetic.
+Both the HIP path and the CPU oracle receive the arrays it returns, so both see the
+same already-rounded values.
+
+Distributions (every config), following the workload recipe:
+  x ~ N(0, 1);  B, C ~ N(0, 1/16);
+  dt = softplus(z), z ~ N(-4, 1), computed in float64 and clipped to [1e-3, 0.1]
+       (dt is handed over post-softplus: the scan itself applies no softplus or clamp);
+  A_h = -exp(U(0, ln 16)) per head (float32);  D_h ~ N(0, 1) per head (float32).
+bf16 configs round x, dt, B and C from float64 to bfloat16 with round-to-nearest-even
+and hand over the 16-bit patterns (numpy uint16); fp32 configs round to float32.
+
+Seeding: every tensor of every (config, stream, segment, step, direction) has its own
+PCG64 generator seeded by SeedSequence(0, spawn_key=(config, stream, segment, step,
+direction, tensor)); values are drawn in token-major order, so drawing a segment in
+consecutive token chunks reproduces a single draw (see ``SegmentStream``).
+"""
+from dataclasses import dataclass
+
+import numpy as np
+
+from .configs import BF16, F32, Config
+
+ROOT_SEED = 0
+
+# segment ids
+PREFIX = 0
+
+
+def BLOCK(k):
+    return 1 + k
+
+
+# direction ids
+FWD, REV, CLEAN = 0, 1, 2
+# tensor ids
+T_X, T_DT, T_B, T_C = 0, 1, 2, 3
+_PARAM_KEY = 0x7FFF
+
+
+def _rng(*key):
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(ROOT_SEED, spawn_key=key)))
+
+
+def round_bf16_bits(v):
+    """float64 -> bfloat16 bit patterns, round-to-nearest-even, without passing through
+    float32 (which would round twice)."""
+    v = np.asarray(v, dtype=np.float64)
+    _, e = np.frexp(v)
+    qexp = np.maximum(e - 8, -133)          # 8 significant bits; bf16 subnormal quantum 2^-133
+    r = np.ldexp(np.rint(np.ldexp(v, -qexp)), qexp)   # np.rint: ties to even
+    f = r.astype(np.float32)                # exact: r has at most 8 significant bits
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits):
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _round(v, dtype):
+    if dtype == BF16:
+        return round_bf16_bits(v)
+    if dtype == F32:
+        return np.asarray(v, dtype=np.float64).astype(np.float32)
+    raise ValueError(dtype)
+
+
+def as_f32(a, dtype):
+    """Decode an input array handed out by this module to float32 (exact)."""
+    return bf16_bits_to_f32(a) if dtype == BF16 else np.asarray(a, dtype=np.float32)
+
+
+def params(cfg: Config):
+    """Per-head A (negative) and D, float32."""
+    u = _rng(cfg.index, _PARAM_KEY, 0).uniform(0.0, np.log(16.0), size=cfg.nheads)
+    A = (-np.exp(u)).astype(np.float32)
+    D = _rng(cfg.index, _PARAM_KEY, 1).standard_normal(cfg.nheads).astype(np.float32)
+    return A, D
+
+
+@dataclass
+class Seq:
+    """One token segment: x [b, len, H, P], dt [b, len, H], B and C [b, len, G, N].
+    Arrays are uint16 bf16 patterns or float32, per ``dtype``."""
+    x: np.ndarray
+    dt: np.ndarray
+    B: np.ndarray
+    C: np.ndarray
+    dtype: int
+
+    @property
+    def length(self):
+        return self.x.shape[1]
+
+
+class SegmentStream:
+    """Draws one stream's segment token chunk by token chunk (token-major order)."""
+
+    def __init__(self, cfg: Config, stream: int, segment: int, step: int, direction: int):
+        key = (cfg.index, stream, segment, step, direction)
+        self.cfg = cfg
+        self.g = {t: _rng(*key, t) for t in (T_X, T_DT, T_B, T_C)}
+
+    def next(self, ntok):
+        c = self.cfg
+        x = self.g[T_X].standard_normal((ntok, c.nheads, c.headdim))
+        z = -4.0 + self.g[T_DT].standard_normal((ntok, c.nheads))
+        dt = np.clip(np.log1p(np.exp(z)), 1e-3, 0.1)
+        B = 0.25 * self.g[T_B].standard_normal((ntok, c.ngroups, c.d_state))
+        C = 0.25 * self.g[T_C].standard_normal((ntok, c.ngroups, c.d_state))
+        d = c.in_dtype
+        return _round(x, d), _round(dt, d), _round(B, d), _round(C, d)
+
+
+def segment(cfg: Config, segment_id: int, step: int, direction: int, length: int,
+            streams=None) -> Seq:
+    """Draw a whole segment of ``length`` tokens for the given streams (default: all)."""
+    streams = range(cfg.batch) if streams is None else streams
+    parts = [SegmentStream(cfg, s, segment_id, step, direction).next(length) for s in streams]
+    x, dt, B, C = (np.stack([p[i] for p in parts]) for i in range(4))
+    return Seq(x, dt, B, C, cfg.in_dtype)
+
+
+def prefix(cfg: Config, streams=None, length=None) -> Seq:
+    return segment(cfg, PREFIX, 0, FWD, cfg.prefix_len if length is None else length, streams)
+
+
+def block(cfg: Config, k: int, step: int, direction: int, streams=None, length=None) -> Seq:
+    """Inputs of block ``k`` at denoising ``step`` (direction FWD or REV), or the block's
+    clean inputs for the commit (direction CLEAN, step 0)."""
+    n = length if length is not None else (cfg.commit_len if direction == CLEAN else cfg.block_len)
+    return segment(cfg, BLOCK(k), step, direction, n, streams)

@@ -1,0 +1,167 @@
+"""Python access to the CPU float64 oracle (``bdssm_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the oracle is the plain sequential recurrence that the HIP
+path is checked against. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+benchmark's CPU-baseline leg may import it. It does not import the HIP package, and
+the HIP package never imports it.
+
+Arrays come in as numpy: inputs are float32 or uint16 bfloat16 bit patterns (decoded
+exactly by the C code), states and outputs are float64.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "bdssm_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+
+def build(force=True):
+    """Compile the oracle with gcc (plain -O2, OpenMP over independent heads)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                        "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("nheads", ctypes.c_int32),
+                ("headdim", ctypes.c_int32), ("d_state", ctypes.c_int32),
+                ("ngroups", ctypes.c_int32), ("in_dtype", ctypes.c_int32)]
+
+
+class _Seq(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("dt", ctypes.c_void_p),
+                ("B", ctypes.c_void_p), ("C", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        lib.oracle_scan.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int64, ctypes.c_int64,
+                                    ctypes.POINTER(_Seq), P, P, P, P, P, P, P, ctypes.c_int]
+        lib.oracle_block_step.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int64, P,
+                                          ctypes.POINTER(_Seq), ctypes.POINTER(_Seq),
+                                          P, P, P, P, P, P, ctypes.c_int]
+        lib.oracle_commit.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int64,
+                                      ctypes.POINTER(_Seq), P, P, P, P, P, ctypes.c_int]
+        for f in (lib.oracle_scan, lib.oracle_block_step, lib.oracle_commit):
+            f.restype = ctypes.c_int
+        lib.oracle_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def max_threads():
+    return _load().oracle_max_threads()
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _in(a, dtype):
+    want = np.uint16 if dtype == 1 else np.float32
+    a = np.ascontiguousarray(a)
+    if a.dtype != want:
+        raise TypeError(f"oracle input must be {np.dtype(want)}, got {a.dtype}")
+    return a
+
+
+class _Call:
+    """Holds the contiguous arrays alive for the duration of one C call."""
+
+    def __init__(self, seq):
+        self.dtype = seq.dtype
+        self.x, self.dt, self.B, self.C = (_in(a, seq.dtype) for a in (seq.x, seq.dt, seq.B, seq.C))
+        self.s = _Seq(_ptr(self.x), _ptr(self.dt), _ptr(self.B), _ptr(self.C))
+
+
+def _dims(seq, ngroups):
+    b, _, H, P = seq.x.shape
+    N = seq.B.shape[3]
+    return _Dims(b, H, P, N, ngroups, seq.dtype)
+
+
+def _f64(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _mask(heads, H):
+    if heads is None:
+        return None
+    m = np.zeros(H, dtype=np.int8)
+    m[list(heads)] = 1
+    return m
+
+
+def scan(seq, A, D, chunk, h_init=None, want_y=True, want_chunk_states=True, heads=None,
+         nthreads=0):
+    """Prefix scan. Returns (y [b,len,H,P] or None, chunk_states [b,nch,H,N,P] or None,
+    h_out [b,H,N,P]); all float64. ``heads``: optional subset of heads to compute."""
+    c = _Call(seq)
+    b, L, H, P = seq.x.shape
+    G, N = seq.B.shape[2], seq.B.shape[3]
+    nch = -(-L // chunk)
+    y = np.zeros((b, L, H, P)) if want_y else None
+    cs = np.zeros((b, nch, H, N, P)) if want_chunk_states else None
+    h_out = np.zeros((b, H, N, P))
+    hi = _f64(h_init)
+    A = np.ascontiguousarray(A, np.float32)
+    D = np.ascontiguousarray(D, np.float32)
+    m = _mask(heads, H)
+    rc = _load().oracle_scan(ctypes.byref(_dims(seq, G)), L, chunk, ctypes.byref(c.s),
+                             _ptr(A), _ptr(D), _ptr(hi), _ptr(y), _ptr(cs), _ptr(h_out),
+                             _ptr(m), nthreads)
+    if rc:
+        raise ValueError("oracle_scan rejected its arguments")
+    return y, cs, h_out
+
+
+def block_step(h_prefix, fwd, rev, A, D, heads=None, nthreads=0):
+    """Block step. Returns (y, y_fwd, y_rev), each [b,T,H,P] float64; y includes D x_fwd."""
+    cf, cr = _Call(fwd), _Call(rev)
+    b, T, H, P = fwd.x.shape
+    G = fwd.B.shape[2]
+    y = np.zeros((b, T, H, P))
+    yf = np.zeros_like(y)
+    yr = np.zeros_like(y)
+    hp = _f64(h_prefix)
+    A = np.ascontiguousarray(A, np.float32)
+    D = np.ascontiguousarray(D, np.float32)
+    m = _mask(heads, H)
+    rc = _load().oracle_block_step(ctypes.byref(_dims(fwd, G)), T, _ptr(hp), ctypes.byref(cf.s),
+                                   ctypes.byref(cr.s), _ptr(A), _ptr(D), _ptr(y), _ptr(yf),
+                                   _ptr(yr), _ptr(m), nthreads)
+    if rc:
+        raise ValueError("oracle_block_step rejected its arguments")
+    return y, yf, yr
+
+
+def commit(h, clean, A, D, want_y=False, heads=None, nthreads=0):
+    """Commit. Returns (h_new [b,H,N,P], y [b,T,H,P] or None), float64; h is not modified."""
+    c = _Call(clean)
+    b, T, H, P = clean.x.shape
+    G = clean.B.shape[2]
+    hn = np.array(h, dtype=np.float64, copy=True, order="C")
+    y = np.zeros((b, T, H, P)) if want_y else None
+    A = np.ascontiguousarray(A, np.float32)
+    D = np.ascontiguousarray(D, np.float32)
+    m = _mask(heads, H)
+    rc = _load().oracle_commit(ctypes.byref(_dims(clean, G)), T, ctypes.byref(c.s), _ptr(A),
+                               _ptr(D), _ptr(hn), _ptr(y), _ptr(m), nthreads)
+    if rc:
+        raise ValueError("oracle_commit rejected its arguments")
+    return hn, y

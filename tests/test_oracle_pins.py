@@ -1,0 +1,330 @@
+"""Pins of the float64 oracle against facts other than itself.
+
+The pages print no numeric example for the scan, so the oracle is pinned by:
+  * a hand-worked example (tests/golden/hand_worked_n1p1.json);
+  * the quadratic "state-space dual" form of the same recurrence, brute-forced in numpy
+    on tiny inputs (a different formula: a sum over all source tokens with cumulative
+    log-decays, instead of a token-by-token recurrence);
+  * closed forms (one token; A = 0 gives a cumulative sum; constant decay gives a
+    geometric series);
+  * invariants: reverse == flip . forward . flip, associativity of the scan (scan of
+    U||V from h0 == scan of V from the state after U), linearity, group replication;
+  * planted mistakes: a copy of the oracle with one plausible error compiled on the CPU
+    must fail these pins.
+"""
+import ctypes
+import json
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from bidirectional_mamba_state_amd.inputs import Seq, round_bf16_bits, bf16_bits_to_f32
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+F32, BF16 = 0, 1
+
+
+def rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return np.linalg.norm((a - b).ravel()) / max(np.linalg.norm(b.ravel()), 1e-300)
+
+
+def rand_seq(rng, b, L, H, P, N, G, dtype=F32):
+    x = rng.standard_normal((b, L, H, P))
+    dt = np.clip(np.log1p(np.exp(rng.normal(-3.0, 1.0, (b, L, H)))), 1e-3, 0.5)
+    B = 0.25 * rng.standard_normal((b, L, G, N))
+    C = 0.25 * rng.standard_normal((b, L, G, N))
+    if dtype == BF16:
+        cv = round_bf16_bits
+    else:
+        def cv(v):
+            return v.astype(np.float32)
+    return Seq(cv(x), cv(dt), cv(B), cv(C), dtype)
+
+
+def dec(seq):
+    f = (lambda a: bf16_bits_to_f32(a).astype(np.float64)) if seq.dtype == BF16 else \
+        (lambda a: np.asarray(a, np.float64))
+    return f(seq.x), f(seq.dt), f(seq.B), f(seq.C)
+
+
+def rand_params(rng, H):
+    A = (-np.exp(rng.uniform(0, np.log(16), H))).astype(np.float32)
+    D = rng.standard_normal(H).astype(np.float32)
+    return A, D
+
+
+# ---------------------------------------------------------------- quadratic (dual) form
+def quad_forward(seq, A, D, h0, with_D=True):
+    """y_t = exp(cs_t) C_t.h0 + sum_{s<=t} exp(cs_t - cs_s) dt_s (C_t.B_s) x_s (+ D x_t),
+    S_t = exp(cs_t) h0 + sum_{s<=t} exp(cs_t - cs_s) dt_s B_s x_s^T, with cs the
+    inclusive cumulative sum of dt*A. Returns (y [b,L,H,P], states [b,L,H,N,P])."""
+    x, dt, B, C = dec(seq)
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    hpg = H // G
+    y = np.zeros((b, L, H, P))
+    S = np.zeros((b, L, H, N, P))
+    tril = np.tril(np.ones((L, L)))
+    for bi in range(b):
+        for h in range(H):
+            g = h // hpg
+            cs = np.cumsum(dt[bi, :, h] * np.float64(A[h]))
+            W = np.exp(np.where(tril > 0, cs[:, None] - cs[None, :], -np.inf))  # [t, s]
+            Wd = W * dt[bi, None, :, h]
+            CB = C[bi, :, g, :] @ B[bi, :, g, :].T
+            y[bi, :, h] = (np.exp(cs)[:, None] * (C[bi, :, g, :] @ h0[bi, h])
+                           + (CB * Wd) @ x[bi, :, h])
+            if with_D:
+                y[bi, :, h] += np.float64(D[h]) * x[bi, :, h]
+            S[bi, :, h] = (np.exp(cs)[:, None, None] * h0[bi, h][None]
+                           + np.einsum("ts,sn,sp->tnp", Wd, B[bi, :, g, :], x[bi, :, h]))
+    return y, S
+
+
+def quad_reverse(seq, A):
+    """y_t = sum_{s>=t} exp(sum_{k=t}^{s-1} dt_k A) dt_s (C_t.B_s) x_s (zero state at the
+    right end of the block)."""
+    x, dt, B, C = dec(seq)
+    b, L, H, P = x.shape
+    G = B.shape[2]
+    hpg = H // G
+    y = np.zeros((b, L, H, P))
+    triu = np.triu(np.ones((L, L)))
+    for bi in range(b):
+        for h in range(H):
+            g = h // hpg
+            a = dt[bi, :, h] * np.float64(A[h])
+            rcs = np.cumsum(a[::-1])[::-1]                  # rcs_t = sum_{k>=t} a_k
+            W = np.exp(np.where(triu > 0, rcs[:, None] - rcs[None, :], -np.inf))
+            CB = C[bi, :, g, :] @ B[bi, :, g, :].T
+            y[bi, :, h] = (CB * W * dt[bi, None, :, h]) @ x[bi, :, h]
+    return y
+
+
+# ------------------------------------------------------------------------- tests
+def _golden_seq(d):
+    a = lambda k: np.array(d[k], np.float32).reshape(1, -1, 1, 1)
+    dt = np.array(d["dt"], np.float32).reshape(1, -1, 1)
+    return Seq(a("x"), dt, a("B"), a("C"), F32)
+
+
+def test_golden_hand_worked():
+    g = json.load(open(os.path.join(HERE, "golden", "hand_worked_n1p1.json")))
+    A = np.array([g["A"]], np.float32)
+    D = np.array([g["D"]], np.float32)
+    h0 = np.full((1, 1, 1, 1), g["h0"])
+    fwd, rev = _golden_seq(g["fwd"]), _golden_seq(g["rev"])
+    y, cs, hT = oracle.scan(fwd, A, D, chunk=1, h_init=h0)
+    tol = 1e-6  # A = -ln2 is rounded to float32
+    np.testing.assert_allclose(y.ravel(), g["scan_y_with_D"], rtol=tol, atol=tol)
+    np.testing.assert_allclose(cs.ravel(), g["scan_states"], rtol=tol, atol=tol)
+    np.testing.assert_allclose(hT.ravel(), g["scan_states"][-1:], rtol=tol, atol=tol)
+    yb, yf, yr = oracle.block_step(h0, fwd, rev, A, D)
+    np.testing.assert_allclose(yf.ravel(), g["block_y_fwd"], rtol=tol, atol=tol)
+    np.testing.assert_allclose(yr.ravel(), g["block_y_rev"], rtol=tol, atol=tol)
+    np.testing.assert_allclose(yb.ravel(), g["block_y"], rtol=tol, atol=tol)
+    hc, yc = oracle.commit(h0, fwd, A, D, want_y=True)
+    np.testing.assert_allclose(hc.ravel(), g["scan_states"][-1:], rtol=tol, atol=tol)
+    np.testing.assert_allclose(yc.ravel(), g["scan_y_with_D"], rtol=tol, atol=tol)
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("G", [1, 2])
+def test_scan_matches_quadratic_form(dtype, G):
+    rng = np.random.default_rng(11 + G + 10 * dtype)
+    b, L, H, P, N, Q = 2, 40, 4, 5, 6, 16
+    seq = rand_seq(rng, b, L, H, P, N, G, dtype)
+    A, D = rand_params(rng, H)
+    h0 = rng.standard_normal((b, H, N, P))
+    y, cs, hT = oracle.scan(seq, A, D, chunk=Q, h_init=h0)
+    yq, Sq = quad_forward(seq, A, D, h0)
+    assert rel(y, yq) < 1e-12
+    assert rel(y - np.float64(D)[None, None, :, None] * dec(seq)[0],
+               yq - np.float64(D)[None, None, :, None] * dec(seq)[0]) < 1e-12
+    ends = [min(L, (c + 1) * Q) - 1 for c in range(-(-L // Q))]
+    assert rel(cs, Sq[:, ends]) < 1e-12          # state after each chunk (ragged tail too)
+    assert rel(hT, Sq[:, -1]) < 1e-12
+
+
+@pytest.mark.parametrize("G", [1, 2])
+def test_block_step_matches_quadratic_form(G):
+    rng = np.random.default_rng(5 + G)
+    b, T, H, P, N = 2, 24, 4, 3, 5
+    fwd = rand_seq(rng, b, T, H, P, N, G)
+    rev = rand_seq(rng, b, T, H, P, N, G)
+    A, D = rand_params(rng, H)
+    h0 = rng.standard_normal((b, H, N, P))
+    h0_copy = h0.copy()
+    y, yf, yr = oracle.block_step(h0, fwd, rev, A, D)
+    yfq, _ = quad_forward(fwd, A, D, h0, with_D=False)
+    yrq = quad_reverse(rev, A)
+    assert rel(yf, yfq) < 1e-12
+    assert rel(yr, yrq) < 1e-12
+    xf = dec(fwd)[0]
+    assert rel(y, yfq + yrq + np.float64(D)[None, None, :, None] * xf) < 1e-12
+    assert np.array_equal(h0, h0_copy)           # the cached state is never written
+
+
+def test_reverse_is_flipped_forward():
+    rng = np.random.default_rng(3)
+    b, T, H, P, N, G = 1, 20, 2, 4, 3, 1
+    rev = rand_seq(rng, b, T, H, P, N, G)
+    zero_fwd = Seq(np.zeros_like(rev.x), rev.dt, rev.B, rev.C, rev.dtype)
+    A, D = rand_params(rng, H)
+    y, _, yr = oracle.block_step(np.zeros((b, H, N, P)), zero_fwd, rev, A, D)
+    flip = Seq(*(np.ascontiguousarray(a[:, ::-1]) for a in (rev.x, rev.dt, rev.B, rev.C)), rev.dtype)
+    yflip, _, _ = oracle.scan(flip, A, np.zeros(H, np.float32), chunk=T)
+    assert rel(yr, yflip[:, ::-1]) < 1e-14
+    assert rel(y, yr) < 1e-14                   # zero forward input and state: y = y_rev
+
+
+def test_scan_associativity_and_commit_chain():
+    rng = np.random.default_rng(4)
+    b, H, P, N, G = 2, 4, 3, 4, 2
+    U = rand_seq(rng, b, 37, H, P, N, G)
+    V = rand_seq(rng, b, 29, H, P, N, G)
+    A, D = rand_params(rng, H)
+    h0 = rng.standard_normal((b, H, N, P))
+    UV = Seq(*(np.concatenate([u, v], axis=1) for u, v in
+               zip((U.x, U.dt, U.B, U.C), (V.x, V.dt, V.B, V.C))), U.dtype)
+    yUV, _, hUV = oracle.scan(UV, A, D, chunk=8, h_init=h0)
+    _, _, hU = oracle.scan(U, A, D, chunk=8, h_init=h0)
+    yV, _, hV = oracle.scan(V, A, D, chunk=8, h_init=hU)
+    assert rel(hV, hUV) < 1e-13
+    assert rel(yV, yUV[:, 37:]) < 1e-13
+    # commits of consecutive pieces == one scan over their concatenation
+    h = h0.copy()
+    for s in range(0, 66, 11):
+        piece = Seq(*(np.ascontiguousarray(a[:, s:s + 11]) for a in (UV.x, UV.dt, UV.B, UV.C)), UV.dtype)
+        h, yc = oracle.commit(h, piece, A, D, want_y=True)
+        assert rel(yc, yUV[:, s:s + 11]) < 1e-13
+    assert rel(h, hUV) < 1e-13
+
+
+def test_closed_forms():
+    # one token: h = alpha h0 + dt B x^T, y = C.h + D x
+    rng = np.random.default_rng(6)
+    H, P, N = 3, 4, 5
+    s1 = rand_seq(rng, 1, 1, H, P, N, 1)
+    A, D = rand_params(rng, H)
+    h0 = rng.standard_normal((1, H, N, P))
+    y, _, hT = oracle.scan(s1, A, D, chunk=4, h_init=h0)
+    x, dt, B, C = dec(s1)
+    for h in range(H):
+        al = np.exp(dt[0, 0, h] * np.float64(A[h]))
+        hh = al * h0[0, h] + dt[0, 0, h] * np.outer(B[0, 0, 0], x[0, 0, h])
+        assert rel(hT[0, h], hh) < 1e-14
+        assert rel(y[0, 0, h], C[0, 0, 0] @ hh + np.float64(D[h]) * x[0, 0, h]) < 1e-14
+    # A = 0: no decay, the state is the running sum of dt B x^T
+    L = 30
+    s = rand_seq(rng, 1, L, H, P, N, 1)
+    _, cs, hT = oracle.scan(s, np.zeros(H, np.float32), D, chunk=1)
+    x, dt, B, C = dec(s)
+    incr = np.einsum("th,tn,thp->thnp", dt[0], B[0, :, 0], x[0])
+    assert rel(cs[0], np.cumsum(incr, axis=0)) < 1e-13
+    # constant dt, B, x: geometric series h_t = a^(t+1) h0 + w (1 - a^(t+1)) / (1 - a)
+    dtc = np.full((1, L, H), 0.05, np.float32)
+    Bc = np.tile(s.B[:, :1], (1, L, 1, 1))
+    xc = np.tile(s.x[:, :1], (1, L, 1, 1))
+    sc = Seq(xc, dtc, Bc, s.C, F32)
+    h0 = rng.standard_normal((1, H, N, P))
+    _, cs, _ = oracle.scan(sc, A, D, chunk=1, h_init=h0)
+    for h in range(H):
+        a = np.exp(np.float64(np.float32(0.05)) * np.float64(A[h]))
+        w = np.float64(np.float32(0.05)) * np.outer(np.float64(Bc[0, 0, 0]), np.float64(xc[0, 0, h]))
+        k = np.arange(1, L + 1)[:, None, None]
+        ref = a ** k * h0[0, h][None] + w[None] * (1 - a ** k) / (1 - a)
+        assert rel(cs[0, :, h], ref) < 1e-13
+
+
+def test_linearity_and_zero():
+    rng = np.random.default_rng(8)
+    b, L, H, P, N, G = 1, 25, 2, 3, 4, 1
+    s = rand_seq(rng, b, L, H, P, N, G)
+    A, D = rand_params(rng, H)
+    # dyadic inputs so that x1 + 2 x2 is exact in float32
+    x1 = (np.round(rng.standard_normal(s.x.shape) * 64) / 64).astype(np.float32)
+    x2 = (np.round(rng.standard_normal(s.x.shape) * 64) / 64).astype(np.float32)
+    h1 = np.round(rng.standard_normal((b, H, N, P)) * 64) / 64
+    h2 = np.round(rng.standard_normal((b, H, N, P)) * 64) / 64
+    mk = lambda x: Seq(x, s.dt, s.B, s.C, F32)
+    y1, c1, _ = oracle.scan(mk(x1), A, D, chunk=5, h_init=h1)
+    y2, c2, _ = oracle.scan(mk(x2), A, D, chunk=5, h_init=h2)
+    y12, c12, _ = oracle.scan(mk(x1 + 2 * x2), A, D, chunk=5, h_init=h1 + 2 * h2)
+    assert rel(y12, y1 + 2 * y2) < 1e-13
+    assert rel(c12, c1 + 2 * c2) < 1e-13
+    # exact: zero input and zero state give exactly zero (SSM part and D part)
+    y0, c0, hT0 = oracle.scan(mk(np.zeros_like(x1)), A, D, chunk=5)
+    assert not y0.any() and not c0.any() and not hT0.any()
+
+
+def test_group_replication():
+    rng = np.random.default_rng(9)
+    b, L, H, P, N = 1, 21, 4, 3, 5
+    s = rand_seq(rng, b, L, H, P, N, 1)
+    A, D = rand_params(rng, H)
+    s2 = Seq(s.x, s.dt, np.ascontiguousarray(np.repeat(s.B, 2, axis=2)),
+             np.ascontiguousarray(np.repeat(s.C, 2, axis=2)), F32)
+    y1, c1, h1 = oracle.scan(s, A, D, chunk=7)
+    y2, c2, h2 = oracle.scan(s2, A, D, chunk=7)
+    assert np.array_equal(y1, y2) and np.array_equal(c1, c2) and np.array_equal(h1, h2)
+
+
+def test_head_subset_matches_full():
+    rng = np.random.default_rng(10)
+    s = rand_seq(rng, 2, 17, 4, 3, 4, 2)
+    A, D = rand_params(rng, 4)
+    y, c, h = oracle.scan(s, A, D, chunk=8)
+    ys, cs_, hs = oracle.scan(s, A, D, chunk=8, heads=[1, 3])
+    assert np.array_equal(y[:, :, [1, 3]], ys[:, :, [1, 3]])
+    assert np.array_equal(h[:, [1, 3]], hs[:, [1, 3]])
+    assert not hs[:, [0, 2]].any()
+
+
+# ------------------------------------------------------------ planted mistakes
+PLANTS = {
+    "dropped dt on the input term": ("const double w = dt * val(in->B", "const double w = val(in->B"),
+    "decay applied after the input": ("row[p] = alpha * row[p] + w * xv[p];",
+                                      "row[p] = alpha * (row[p] + w * xv[p]);"),
+    "reverse uses the forward dt": ("const double dt = val(rev->dt", "const double dt = val(fwd->dt"),
+    "wrong group index": ("const int g = h / (H / G);\n    const int dty",
+                          "const int g = h % G;\n    const int dty"),
+    "D applied twice in the block step": ("(double)D[h] * val(fwd->x, dty, o);",
+                                          "2.0 * (double)D[h] * val(fwd->x, dty, o);"),
+    "C and B swapped in the forward output": (
+        "acc += val(in->C, dty, (tok * G + g) * N + n) * S",
+        "acc += val(in->B, dty, (tok * G + g) * N + n) * S"),
+}
+
+
+def _planted_lib(tmp_path, name, old, new):
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "bdssm_oracle.c")).read()
+    assert src.count(old) >= 1, name
+    path_c = tmp_path / "planted.c"
+    path_c.write_text(src.replace(old, new))
+    so = tmp_path / "planted.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o", str(so),
+                    str(path_c), "-lm"], check=True)
+    return str(so)
+
+
+@pytest.mark.parametrize("name", sorted(PLANTS))
+def test_planted_mistake_is_caught(tmp_path, monkeypatch, name):
+    old, new = PLANTS[name]
+    so = _planted_lib(tmp_path, name, old, new)
+    monkeypatch.setattr(oracle, "_LIB", so)
+    monkeypatch.setattr(oracle, "_lib", None)
+    failed = []
+    for test in (test_golden_hand_worked, lambda: test_scan_matches_quadratic_form(F32, 2),
+                 lambda: test_block_step_matches_quadratic_form(2)):
+        try:
+            test()
+        except AssertionError:
+            failed.append(test)
+    monkeypatch.setattr(oracle, "_lib", None)
+    assert failed, f"planted mistake '{name}' passed every pin"
