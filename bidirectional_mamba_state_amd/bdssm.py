@@ -1,0 +1,160 @@
+"""ctypes binding of libbdssm.so (the C ABI in include/bdssm.h).
+
+Argument marshalling only: every step of the computation runs in the HIP kernels. The
+functions take torch CUDA tensors (PyTorch provides device memory and streams), pass
+their device pointers to the library, and raise ``BdssmError`` on a non-OK status.
+There is no fallback: if the library is not built, loading raises.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbdssm.so")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_ALIAS, ERR_WORKSPACE, ERR_HIP = range(8)
+F32, BF16 = 0, 1
+
+# every symbol include/bdssm.h declares
+EXPORTS = ("bdssm_abi_version", "bdssm_status_str", "bdssm_prefix_scan_workspace",
+           "bdssm_prefix_scan", "bdssm_block_step", "bdssm_commit")
+
+
+class BdssmError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(msg)
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("nheads", ctypes.c_int32),
+                ("headdim", ctypes.c_int32), ("d_state", ctypes.c_int32),
+                ("ngroups", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
+                ("y_dtype", ctypes.c_int32)]
+
+
+class SeqPtrs(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("dt", ctypes.c_void_p),
+                ("B", ctypes.c_void_p), ("C", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load():
+    """Load the built library (raises OSError if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise OSError(f"{LIB_PATH} is not built; run bidirectional_mamba_state_amd/build.py")
+        lib = ctypes.CDLL(LIB_PATH)
+        V, P, I32, I64, SZ = ctypes.c_void_p, ctypes.POINTER, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        lib.bdssm_abi_version.restype = ctypes.c_int
+        lib.bdssm_abi_version.argtypes = []
+        lib.bdssm_status_str.restype = ctypes.c_char_p
+        lib.bdssm_status_str.argtypes = [ctypes.c_int]
+        lib.bdssm_prefix_scan_workspace.restype = SZ
+        lib.bdssm_prefix_scan_workspace.argtypes = [P(Dims), I64, I32, I32, I32]
+        lib.bdssm_prefix_scan.restype = ctypes.c_int
+        lib.bdssm_prefix_scan.argtypes = [P(Dims), I64, I32, P(SeqPtrs), V, V, V, V, V, V, V, SZ, V]
+        lib.bdssm_block_step.restype = ctypes.c_int
+        lib.bdssm_block_step.argtypes = [P(Dims), I32, V, P(SeqPtrs), P(SeqPtrs), V, V, V, V]
+        lib.bdssm_commit.restype = ctypes.c_int
+        lib.bdssm_commit.argtypes = [P(Dims), I32, P(SeqPtrs), V, V, V, V, V]
+        _lib = lib
+    return _lib
+
+
+def status_str(status):
+    return load().bdssm_status_str(status).decode()
+
+
+def abi_version():
+    return load().bdssm_abi_version()
+
+
+def _check(rc):
+    if rc != OK:
+        raise BdssmError(rc, status_str(rc))
+
+
+def _ptr(t):
+    """Device pointer of a torch CUDA tensor (None -> NULL). Refuses host tensors and
+    non-contiguous views: the library takes contiguous device buffers only."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not getattr(t, "is_cuda", False):
+        raise TypeError("bdssm takes device (CUDA/HIP) tensors only")
+    if not t.is_contiguous():
+        raise ValueError("bdssm takes contiguous tensors only")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def dims(batch, nheads, headdim, d_state, ngroups, in_dtype, y_dtype=F32):
+    return Dims(batch, nheads, headdim, d_state, ngroups, in_dtype, y_dtype)
+
+
+def _seq(s):
+    if s is None:
+        return None
+    x, dt, B, C = s
+    return SeqPtrs(_ptr(x), _ptr(dt), _ptr(B), _ptr(C))
+
+
+def _byref(v):
+    return None if v is None else ctypes.byref(v)
+
+
+def prefix_scan_workspace(d, length, chunk, with_y, with_chunk_states):
+    return load().bdssm_prefix_scan_workspace(ctypes.byref(d), length, chunk, int(with_y),
+                                              int(with_chunk_states))
+
+
+def prefix_scan(d, length, chunk, seq, A, D, h_init, y, chunk_states, h_out,
+                workspace=None, workspace_bytes=None, stream=None):
+    """bdssm_prefix_scan. seq = (x, dt, B, C) tensors; C may be None when y is None."""
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().bdssm_prefix_scan(ctypes.byref(d), length, chunk, _byref(_seq(seq)), _ptr(A),
+                                    _ptr(D), _ptr(h_init), _ptr(y), _ptr(chunk_states),
+                                    _ptr(h_out), _ptr(workspace), workspace_bytes,
+                                    _stream(stream)))
+
+
+def block_step(d, block_len, h_prefix, fwd, rev, A, D, y, stream=None):
+    """bdssm_block_step. fwd, rev = (x, dt, B, C) tensors."""
+    _check(load().bdssm_block_step(ctypes.byref(d), block_len, _ptr(h_prefix), _byref(_seq(fwd)),
+                                   _byref(_seq(rev)), _ptr(A), _ptr(D), _ptr(y), _stream(stream)))
+
+
+def commit(d, block_len, clean, A, D, h, y=None, stream=None):
+    """bdssm_commit. clean = (x, dt, B, C) tensors (C may be None when y is None)."""
+    _check(load().bdssm_commit(ctypes.byref(d), block_len, _byref(_seq(clean)), _ptr(A), _ptr(D),
+                               _ptr(h), _ptr(y), _stream(stream)))
+
+
+# ------------------------------------------------------------------ data movement helpers
+def to_device(arr, device="cuda"):
+    """numpy input array (float32, or uint16 bfloat16 patterns) -> torch device tensor."""
+    import torch
+    a = np.ascontiguousarray(arr)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(a).to(device)
+
+
+def seq_to_device(seq, device="cuda"):
+    """An inputs.Seq -> (x, dt, B, C) device tensors."""
+    return tuple(to_device(a, device) for a in (seq.x, seq.dt, seq.B, seq.C))

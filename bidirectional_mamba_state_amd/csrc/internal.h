@@ -1,0 +1,61 @@
+// Internal declarations shared by the host library and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bdssm {
+
+struct Shape {
+    int b, H, P, N, G;
+    int in_dt, y_dt;  // 0 = float32, 1 = bfloat16
+};
+
+struct Seq {
+    const void *x, *dt, *B, *C;
+};
+
+// Forward recurrence over segments of one token range (prefix chunks, or a commit block).
+// Segment c of stream b covers tokens [c*Q, min(len, (c+1)*Q)).
+struct ForwardArgs {
+    Shape s;
+    int64_t len;          // tokens per stream in `in`
+    int Q;                // segment length
+    int nseg;             // ceil(len / Q)
+    Seq in;
+    const float *A, *D;
+    const float *first_state;  // state entering segment 0, [b][H][N][P]; NULL = zero
+    const float *prev_states;  // state entering segment c>0 = prev_states[b][c-1][h]; NULL = zero
+    void *y;                   // [b][len][H][P] in s.y_dt, with D x; NULL = no output
+    float *state_out;          // final state of each segment, [b][nseg][H][N][P]; NULL = none
+    float *decay_out;          // sum over the segment of dt*A, [b][nseg][H]; NULL = none
+};
+
+// Inter-chunk state passing: h_c = exp(decay_c) h_{c-1} + local_c, in place over `states`.
+struct PassArgs {
+    Shape s;
+    int nch;
+    const float *h_init;   // NULL = zero
+    float *states;         // [b][nch][H][N][P]: chunk-local states in, chunk states out
+    const float *decay;    // [b][nch][H]
+    int write_all;         // write every chunk state back (else only the final one)
+    float *h_out;          // [b][H][N][P] or NULL
+};
+
+struct BlockArgs {
+    Shape s;
+    int T;
+    const float *h_prefix;
+    Seq fwd, rev;
+    const float *A, *D;
+    void *y;
+};
+
+bool valu_supported(int N, int P);
+hipError_t launch_forward_valu(const ForwardArgs &a, hipStream_t st);
+hipError_t launch_block_step_valu(const BlockArgs &a, hipStream_t st);
+hipError_t launch_state_pass(const PassArgs &a, hipStream_t st);
+hipError_t launch_copy_f32(float *dst, const float *src, int64_t n, hipStream_t st);
+hipError_t launch_fill_f32(float *dst, float v, int64_t n, hipStream_t st);
+
+}  // namespace bdssm

@@ -12,11 +12,14 @@ Distributions (every config), following the workload recipe:
 bf16 configs round x, dt, B and C from float64 to bfloat16 with round-to-nearest-even
 and hand over the 16-bit patterns (numpy uint16); fp32 configs round to float32.
 
-Seeding: every tensor of every (config, stream, segment, step, direction) has its own
-PCG64 generator seeded by SeedSequence(0, spawn_key=(config, stream, segment, step,
-direction, tensor)); values are drawn in token-major order, so drawing a segment in
-consecutive token chunks reproduces a single draw (see ``SegmentStream``).
+Seeding: each tensor of each (config, stream, segment, step, direction) is cut into
+pieces of PIECE tokens; every piece has its own PCG64 generator seeded by
+SeedSequence(0, spawn_key=(config, stream, segment, step, direction, tensor, piece)) and
+is drawn in token-major order. Any token range can therefore be drawn on its own and in
+parallel, and drawing a segment in token chunks reproduces a single draw.
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 
 import numpy as np
@@ -38,6 +41,7 @@ FWD, REV, CLEAN = 0, 1, 2
 # tensor ids
 T_X, T_DT, T_B, T_C = 0, 1, 2, 3
 _PARAM_KEY = 0x7FFF
+PIECE = 4096
 
 
 def _rng(*key):
@@ -95,32 +99,78 @@ class Seq:
         return self.x.shape[1]
 
 
-class SegmentStream:
-    """Draws one stream's segment token chunk by token chunk (token-major order)."""
+def _tail(cfg, tensor):
+    if tensor == T_X:
+        return (cfg.nheads, cfg.headdim)
+    if tensor == T_DT:
+        return (cfg.nheads,)
+    return (cfg.ngroups, cfg.d_state)
 
-    def __init__(self, cfg: Config, stream: int, segment: int, step: int, direction: int):
-        key = (cfg.index, stream, segment, step, direction)
-        self.cfg = cfg
-        self.g = {t: _rng(*key, t) for t in (T_X, T_DT, T_B, T_C)}
 
-    def next(self, ntok):
-        c = self.cfg
-        x = self.g[T_X].standard_normal((ntok, c.nheads, c.headdim))
-        z = -4.0 + self.g[T_DT].standard_normal((ntok, c.nheads))
-        dt = np.clip(np.log1p(np.exp(z)), 1e-3, 0.1)
-        B = 0.25 * self.g[T_B].standard_normal((ntok, c.ngroups, c.d_state))
-        C = 0.25 * self.g[T_C].standard_normal((ntok, c.ngroups, c.d_state))
-        d = c.in_dtype
-        return _round(x, d), _round(dt, d), _round(B, d), _round(C, d)
+def _draw_piece(cfg, key, tensor, piece, ntok):
+    """The first ``ntok`` tokens of one PIECE-token piece of one tensor, rounded."""
+    g = _rng(*key, tensor, piece)
+    v = g.standard_normal((ntok,) + _tail(cfg, tensor))
+    if tensor == T_X:
+        pass
+    elif tensor == T_DT:
+        v = np.clip(np.log1p(np.exp(v - 4.0)), 1e-3, 0.1)
+    else:
+        v *= 0.25
+    return _round(v, cfg.in_dtype)
+
+
+def _out_dtype(cfg):
+    return np.uint16 if cfg.in_dtype == BF16 else np.float32
+
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        _POOL = ThreadPoolExecutor(max_workers=max(1, min(16, os.cpu_count() or 1)))
+    return _POOL
+
+
+_POOL = None
+
+
+def draw(cfg: Config, stream: int, segment_id: int, step: int, direction: int, t0: int, t1: int,
+         out=None):
+    """Tokens [t0, t1) of one stream's segment: returns (x, dt, B, C), or fills ``out``
+    (a tuple of four arrays shaped [t1 - t0, ...]). Any token range can be drawn on its
+    own: each PIECE-token piece of each tensor has its own generator."""
+    key = (cfg.index, stream, segment_id, step, direction)
+    n = t1 - t0
+    if out is None:
+        out = tuple(np.empty((n,) + _tail(cfg, t), _out_dtype(cfg)) for t in (T_X, T_DT, T_B, T_C))
+    jobs = []
+    for piece in range(t0 // PIECE, (t1 + PIECE - 1) // PIECE if n > 0 else 0):
+        p0 = piece * PIECE
+        lo, hi = max(t0, p0), min(t1, p0 + PIECE)
+        for ti, t in enumerate((T_X, T_DT, T_B, T_C)):
+            jobs.append((ti, t, piece, p0, lo, hi))
+
+    def run(job):
+        ti, t, piece, p0, lo, hi = job
+        out[ti][lo - t0:hi - t0] = _draw_piece(cfg, key, t, piece, hi - p0)[lo - p0:]
+
+    if len(jobs) > 4:
+        list(_pool().map(run, jobs))
+    else:
+        for j in jobs:
+            run(j)
+    return out
 
 
 def segment(cfg: Config, segment_id: int, step: int, direction: int, length: int,
             streams=None) -> Seq:
     """Draw a whole segment of ``length`` tokens for the given streams (default: all)."""
-    streams = range(cfg.batch) if streams is None else streams
-    parts = [SegmentStream(cfg, s, segment_id, step, direction).next(length) for s in streams]
-    x, dt, B, C = (np.stack([p[i] for p in parts]) for i in range(4))
-    return Seq(x, dt, B, C, cfg.in_dtype)
+    streams = list(range(cfg.batch) if streams is None else streams)
+    dt_ = _out_dtype(cfg)
+    arrs = tuple(np.empty((len(streams), length) + _tail(cfg, t), dt_) for t in (T_X, T_DT, T_B, T_C))
+    for i, s in enumerate(streams):
+        draw(cfg, s, segment_id, step, direction, 0, length, out=tuple(a[i] for a in arrs))
+    return Seq(*arrs, cfg.in_dtype)
 
 
 def prefix(cfg: Config, streams=None, length=None) -> Seq:

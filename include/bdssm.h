@@ -1,0 +1,152 @@
+/*
+ * bdssm.h - C ABI of the bidirectional block-diffusion Mamba state hot path on MI355X.
+ *
+ * The method ("Training Hybrid Block Diffusion Language Models with Partial
+ * Bidirectionality", eqs. (9)-(13) and the cache discussion around them) factors each
+ * Mamba layer into a timestep-free prefix operator, which folds the clean prefix into a
+ * cached forward state, and an active-block continuation, which runs a forward scan
+ * seeded from that state plus a reverse scan confined to the active block. The three
+ * calls below are those three operations:
+ *
+ *   bdssm_prefix_scan  - eq. (10): s_k = F_fwd(c), the forward scan of a prefix,
+ *                        returning the boundary state (and optionally y and the state
+ *                        after every chunk of the scan).
+ *   bdssm_block_step   - eqs. (11)-(13): y = F_fwd(b; s_k) + rev(F_rev(rev(b))) + D x,
+ *                        for one denoising step of the active block. The cached state is
+ *                        read, never written (the cache must not depend on the step).
+ *   bdssm_commit       - the clean forward pass over a finalized block that extends the
+ *                        cache: s_{k+1} = F_fwd(b*; s_k), in place.
+ *
+ * The scan F is the selective state-space recurrence of eq. (1) in its Mamba-2 form,
+ * with one negative scalar A[h] per head:
+ *     alpha_t = exp(dt[t,h] * A[h])
+ *     S_t     = alpha_t * S_{t-1} + dt[t,h] * B[t,g] x[t,h]^T        (S is N x P)
+ *     y[t,h]  = C[t,g] . S_t   (+ D[h] * x[t,h] where stated)
+ * with g = h / (H/G): each group of H/G consecutive heads shares B and C. The reverse
+ * scan starts from a zero state at the block's right end and runs t = T-1 ... 0 over
+ * inputs given in natural token order; its outputs are in natural order too.
+ *
+ * Layouts (row-major, contiguous, b = stream):
+ *     x  [b][len][H][P]     dt [b][len][H]     B, C [b][len][G][N]
+ *     state [b][H][N][P] (float32)     chunk states [b][ceil(len/chunk)][H][N][P]
+ *     y  [b][len][H][P]     A, D [H] (float32)
+ * dt is the final step size (already passed through softplus and any clamp).
+ *
+ * Conventions for every call:
+ *  - Pointers are device pointers (hipMalloc'd, or torch CUDA tensors); the caller owns
+ *    every buffer. Base pointers must be 16-byte aligned. The library allocates nothing
+ *    and never synchronizes.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
+ *    asynchronously; the returned status covers argument validation and the launch.
+ *    Faults during execution surface at the caller's next synchronization.
+ *  - Errors are status codes; nothing is thrown across the ABI. Invalid arguments are
+ *    rejected before anything is launched, with no buffer modified.
+ *  - Supported shapes: ngroups divides nheads; (d_state, headdim) in {(16,16), (128,64)};
+ *    chunk in {16, 32, 64, 128, 256}; block_len in [0, 256]. batch, len and block_len
+ *    may be 0 (nothing to do: a prefix scan of zero tokens returns h_init, or zero).
+ *  - Thread-safe and re-entrant. Calls on one stream run in order.
+ */
+#ifndef BDSSM_H
+#define BDSSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BDSSM_ABI_VERSION 1
+
+typedef enum {
+    BDSSM_OK = 0,
+    BDSSM_ERR_NULL = 1,        /* a required pointer is NULL */
+    BDSSM_ERR_SHAPE = 2,       /* a size is negative or inconsistent (e.g. H % G != 0) */
+    BDSSM_ERR_UNSUPPORTED = 3, /* a valid size or dtype with no compiled kernel */
+    BDSSM_ERR_ALIGN = 4,       /* a base pointer is not 16-byte aligned */
+    BDSSM_ERR_ALIAS = 5,       /* an output overlaps an input it must not overlap */
+    BDSSM_ERR_WORKSPACE = 6,   /* workspace missing or smaller than the query returned */
+    BDSSM_ERR_HIP = 7          /* the HIP runtime reported an error at launch */
+} bdssm_status;
+
+typedef enum { BDSSM_F32 = 0, BDSSM_BF16 = 1 } bdssm_dtype;
+
+typedef struct {
+    int32_t batch;    /* independent streams b */
+    int32_t nheads;   /* H */
+    int32_t headdim;  /* P */
+    int32_t d_state;  /* N */
+    int32_t ngroups;  /* G */
+    int32_t in_dtype; /* bdssm_dtype of x, dt, B, C */
+    int32_t y_dtype;  /* bdssm_dtype of y (F32 for parity checks, BF16 as activations) */
+} bdssm_dims;
+
+/* One token segment's inputs (device pointers, layouts above). */
+typedef struct {
+    const void *x, *dt, *B, *C;
+} bdssm_seq;
+
+/* ABI version implemented by the library (BDSSM_ABI_VERSION at build time). */
+int bdssm_abi_version(void);
+
+/* Static, human-readable name of a status code; never NULL. */
+const char *bdssm_status_str(int status);
+
+/* Bytes of device workspace bdssm_prefix_scan needs for these arguments. with_y and
+ * with_chunk_states say whether y and chunk_states will be passed non-NULL. Returns 0
+ * when no workspace is needed, and SIZE_MAX for arguments bdssm_prefix_scan would
+ * reject. */
+size_t bdssm_prefix_scan_workspace(const bdssm_dims *dims, int64_t len, int32_t chunk,
+                                   int32_t with_y, int32_t with_chunk_states);
+
+/*
+ * Prefix scan: eq. (10), s_k = F_fwd(c^(k)), the forward recurrence over `len` prefix
+ * tokens of every stream, computed chunk by chunk (chunk = Q tokens; the last chunk may
+ * be shorter).
+ *   in            prefix inputs, len tokens
+ *   A, D          [H] float32
+ *   h_init        [b][H][N][P] float32 starting state, or NULL for zero
+ *   y             [b][len][H][P] in dims->y_dtype, y_t = C_t . S_t + D x_t; NULL = state only
+ *   chunk_states  [b][ceil(len/Q)][H][N][P] float32: the state after tokens Q-1, 2Q-1, ...
+ *                 and after the last token (so the last entry equals h_out); NULL = none
+ *   h_out         [b][H][N][P] float32 final state; required; may be the same pointer as
+ *                 h_init (updated in place) but must not otherwise overlap anything
+ *   workspace     device buffer of at least bdssm_prefix_scan_workspace(...) bytes
+ * y and chunk_states must not overlap any input or each other.
+ */
+bdssm_status bdssm_prefix_scan(const bdssm_dims *dims, int64_t len, int32_t chunk,
+                               const bdssm_seq *in, const float *A, const float *D,
+                               const float *h_init, void *y, float *chunk_states,
+                               float *h_out, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/*
+ * Block step: eqs. (11)-(13), one denoising step of the active block of T = block_len
+ * tokens:
+ *   y_t = C_t . S_t            (forward scan from h_prefix over fwd, eq. 11)
+ *       + C'_t . R_t           (reverse scan over rev from R_T = 0, eq. 12)
+ *       + D[h] * x_fwd[t]      (skip term of eq. 1, applied once)
+ *   h_prefix  [b][H][N][P] float32 cached state; read only, never written
+ *   fwd, rev  the two directions' inputs, T tokens each, natural token order
+ *   y         [b][T][H][P] in dims->y_dtype; must not overlap any input
+ */
+bdssm_status bdssm_block_step(const bdssm_dims *dims, int32_t block_len,
+                              const float *h_prefix, const bdssm_seq *fwd,
+                              const bdssm_seq *rev, const float *A, const float *D, void *y,
+                              void *stream);
+
+/*
+ * Commit: the clean forward pass over a finalized block of T = block_len tokens that
+ * extends the cache, S <- F_fwd(clean; S), in place on h.
+ *   clean  the block's clean inputs; clean->C may be NULL when y is NULL
+ *   h      [b][H][N][P] float32, read then overwritten with the advanced state
+ *   y      NULL, or [b][T][H][P] in dims->y_dtype: y_t = C_t . S_t + D x_t of the pass
+ */
+bdssm_status bdssm_commit(const bdssm_dims *dims, int32_t block_len, const bdssm_seq *clean,
+                          const float *A, const float *D, float *h, void *y, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BDSSM_H */

@@ -1,0 +1,109 @@
+"""Helpers shared by the GPU tests: run the HIP path through the C ABI on numpy inputs
+from the seeded generator, and compare with the oracle."""
+import numpy as np
+
+from bidirectional_mamba_state_amd import bdssm
+from bidirectional_mamba_state_amd.inputs import Seq
+
+TOL_F32 = 1e-5   # relative L2 bound, float32 inputs
+TOL_BF16 = 5e-3  # relative L2 bound, bfloat16 inputs with float32 state
+
+
+def tol_for(dtype):
+    return TOL_BF16 if dtype == 1 else TOL_F32
+
+
+def rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    den = np.linalg.norm(b.ravel())
+    num = np.linalg.norm((a - b).ravel())
+    return num / den if den > 0 else num
+
+
+def max_head_rel(a, b, head_axis):
+    """Largest per-head relative L2 error (exposes errors confined to a few heads)."""
+    a = np.moveaxis(np.asarray(a, np.float64), head_axis, 0)
+    b = np.moveaxis(np.asarray(b, np.float64), head_axis, 0)
+    return max(rel(a[i], b[i]) for i in range(a.shape[0]))
+
+
+def torch():
+    import torch as _t
+    return _t
+
+
+def dims_of(seq, y_dtype=bdssm.F32):
+    b, _, H, P = seq.x.shape
+    G, N = seq.B.shape[2], seq.B.shape[3]
+    return bdssm.dims(b, H, P, N, G, seq.dtype, y_dtype)
+
+
+def _y_torch_dtype(y_dtype):
+    t = torch()
+    return t.bfloat16 if y_dtype == bdssm.BF16 else t.float32
+
+
+def to_np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def dev_f32(a):
+    t = torch()
+    return t.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def gpu_prefix(seq, A, D, chunk, h_init=None, want_y=True, want_cs=True, y_dtype=bdssm.F32,
+               in_place=False, dev_seq=None):
+    """Runs bdssm_prefix_scan; returns (y, chunk_states, h_out) as float64 numpy (None
+    where not requested)."""
+    t = torch()
+    b, L, H, P = seq.x.shape
+    N = seq.B.shape[3]
+    d = dims_of(seq, y_dtype)
+    xs = dev_seq if dev_seq is not None else bdssm.seq_to_device(seq)
+    nch = -(-L // chunk)
+    y = t.empty((b, L, H, P), dtype=_y_torch_dtype(y_dtype), device="cuda") if want_y else None
+    cs = t.empty((b, nch, H, N, P), dtype=t.float32, device="cuda") if want_cs else None
+    hi = dev_f32(h_init) if h_init is not None else None
+    ho = hi if (in_place and hi is not None) else t.empty((b, H, N, P), dtype=t.float32, device="cuda")
+    wsb = bdssm.prefix_scan_workspace(d, L, chunk, want_y, want_cs)
+    ws = t.empty(max(wsb, 1), dtype=t.uint8, device="cuda") if wsb else None
+    bdssm.prefix_scan(d, L, chunk, xs, dev_f32(A), dev_f32(D), hi, y, cs, ho, ws, wsb)
+    t.cuda.synchronize()
+    return (to_np(y) if want_y else None, to_np(cs) if want_cs else None, to_np(ho))
+
+
+def gpu_block_step(h_prefix, fwd, rev, A, D, y_dtype=bdssm.F32, dev_h=None):
+    t = torch()
+    b, T, H, P = fwd.x.shape
+    d = dims_of(fwd, y_dtype)
+    hp = dev_h if dev_h is not None else dev_f32(h_prefix)
+    y = t.empty((b, T, H, P), dtype=_y_torch_dtype(y_dtype), device="cuda")
+    bdssm.block_step(d, T, hp, bdssm.seq_to_device(fwd), bdssm.seq_to_device(rev), dev_f32(A),
+                     dev_f32(D), y)
+    t.cuda.synchronize()
+    return to_np(y)
+
+
+def gpu_commit(h, clean, A, D, want_y=False, y_dtype=bdssm.F32):
+    t = torch()
+    b, T, H, P = clean.x.shape
+    d = dims_of(clean, y_dtype)
+    hd = dev_f32(h)
+    y = t.empty((b, T, H, P), dtype=_y_torch_dtype(y_dtype), device="cuda") if want_y else None
+    bdssm.commit(d, T, bdssm.seq_to_device(clean), dev_f32(A), dev_f32(D), hd, y)
+    t.cuda.synchronize()
+    return to_np(hd), (to_np(y) if want_y else None)
+
+
+def slice_seq(seq, t0, t1):
+    return Seq(*(np.ascontiguousarray(a[:, t0:t1]) for a in (seq.x, seq.dt, seq.B, seq.C)), seq.dtype)
+
+
+def streams_of(seq, idx):
+    return Seq(*(np.ascontiguousarray(a[idx]) for a in (seq.x, seq.dt, seq.B, seq.C)), seq.dtype)
+
+
+def f32_round(a):
+    return np.asarray(a, np.float64).astype(np.float32).astype(np.float64)

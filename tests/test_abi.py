@@ -1,0 +1,134 @@
+"""The C ABI on the CPU: the library loads, exports every symbol include/bdssm.h declares,
+and rejects bad arguments before launching anything. No call here reaches a kernel:
+every argument set is one the validation refuses."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bidirectional_mamba_state_amd import bdssm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_symbols():
+    text = open(os.path.join(ROOT, "include", "bdssm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bdssm_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(bdssm.LIB_PATH)
+    syms = header_symbols()
+    assert syms == sorted(bdssm.EXPORTS)
+    for s in syms:
+        assert hasattr(lib, s), s
+    assert bdssm.abi_version() == 1
+    for st in range(8):
+        assert bdssm.status_str(st).startswith("BDSSM_")
+    assert "unknown" in bdssm.status_str(99)
+
+
+FAKE = 0x100000  # 16-byte aligned, never dereferenced (every call below is rejected first)
+
+
+def seq(x=FAKE, dt=FAKE, B=FAKE, C=FAKE):
+    return bdssm.SeqPtrs(x, dt, B, C)
+
+
+def call_prefix(d, length=64, chunk=64, s=None, A=FAKE, D=FAKE, h_init=None, y=None, cs=None,
+                h_out=FAKE + 4096, ws=None, wsb=0):
+    lib = bdssm.load()
+    s = seq() if s is None else s
+    return lib.bdssm_prefix_scan(None if d is None else ctypes.byref(d), length, chunk,
+                                 ctypes.byref(s), A, D, h_init, y, cs, h_out, ws, wsb, None)
+
+
+def call_block(d, T=16, h=FAKE, f=None, r=None, A=FAKE, D=FAKE, y=FAKE + (1 << 24)):
+    lib = bdssm.load()
+    f = seq() if f is None else f
+    r = seq() if r is None else r
+    return lib.bdssm_block_step(None if d is None else ctypes.byref(d), T, h, ctypes.byref(f),
+                                ctypes.byref(r), A, D, y, None)
+
+
+def call_commit(d, T=16, c=None, A=FAKE, D=FAKE, h=FAKE + (1 << 24), y=None):
+    lib = bdssm.load()
+    c = seq() if c is None else c
+    return lib.bdssm_commit(None if d is None else ctypes.byref(d), T, ctypes.byref(c), A, D, h, y, None)
+
+
+def good():
+    return bdssm.dims(1, 4, 16, 16, 1, bdssm.F32, bdssm.F32)
+
+
+def test_null_dims_and_pointers():
+    assert call_prefix(None) == bdssm.ERR_NULL
+    assert call_block(None) == bdssm.ERR_NULL
+    assert call_commit(None) == bdssm.ERR_NULL
+    assert call_prefix(good(), h_out=None) == bdssm.ERR_NULL
+    assert call_prefix(good(), s=seq(x=None)) == bdssm.ERR_NULL
+    assert call_prefix(good(), s=seq(C=None), y=FAKE + (1 << 26)) == bdssm.ERR_NULL  # C needed for y
+    assert call_block(good(), h=None) == bdssm.ERR_NULL
+    assert call_block(good(), r=seq(B=None)) == bdssm.ERR_NULL
+    assert call_block(good(), y=None) == bdssm.ERR_NULL
+    assert call_commit(good(), h=None) == bdssm.ERR_NULL
+    assert call_commit(good(), c=seq(C=None), y=FAKE + (1 << 26)) == bdssm.ERR_NULL
+
+
+def test_shapes_and_unsupported():
+    d = good()
+    d.ngroups = 3
+    assert call_prefix(d) == bdssm.ERR_SHAPE           # H % G != 0
+    d = good()
+    d.nheads = 0
+    assert call_block(d) == bdssm.ERR_SHAPE
+    d = good()
+    d.batch = -1
+    assert call_commit(d) == bdssm.ERR_SHAPE
+    assert call_prefix(good(), length=-1) == bdssm.ERR_SHAPE
+    assert call_block(good(), T=-1) == bdssm.ERR_SHAPE
+    assert call_commit(good(), T=-1) == bdssm.ERR_SHAPE
+    assert call_block(good(), T=257) == bdssm.ERR_UNSUPPORTED
+    assert call_prefix(good(), chunk=48) == bdssm.ERR_UNSUPPORTED
+    d = good()
+    d.d_state = 32                                      # no kernel for (32, 16)
+    assert call_prefix(d) == bdssm.ERR_UNSUPPORTED
+    d = good()
+    d.in_dtype = 7
+    assert call_block(d) == bdssm.ERR_UNSUPPORTED
+    assert bdssm.prefix_scan_workspace(d, 64, 64, True, True) == ctypes.c_size_t(-1).value
+
+
+def test_alignment_and_alias():
+    assert call_prefix(good(), s=seq(x=FAKE + 2)) == bdssm.ERR_ALIGN
+    assert call_block(good(), h=FAKE + 8) == bdssm.ERR_ALIGN
+    assert call_commit(good(), A=FAKE + 4) == bdssm.ERR_ALIGN
+    # y on top of x
+    assert call_block(good(), y=FAKE) == bdssm.ERR_ALIAS
+    assert call_prefix(good(), y=FAKE, cs=None) == bdssm.ERR_ALIAS
+    # h_out partially overlapping h_init (exact aliasing is allowed)
+    assert call_prefix(good(), h_init=FAKE + (1 << 24), h_out=FAKE + (1 << 24) + 16) == bdssm.ERR_ALIAS
+    # commit state on top of the clean inputs
+    assert call_commit(good(), h=FAKE) == bdssm.ERR_ALIAS
+
+
+def test_workspace_query_and_missing_workspace():
+    d = bdssm.dims(1, 48, 64, 128, 1, bdssm.BF16, bdssm.F32)
+    need = bdssm.prefix_scan_workspace(d, 8192, 256, True, False)
+    assert need >= 32 * 48 * 128 * 64 * 4              # chunk states kept for the y pass
+    assert bdssm.prefix_scan_workspace(d, 8192, 256, True, True) < 1 << 20
+    assert bdssm.prefix_scan_workspace(d, 0, 256, True, True) == 0
+    base = 1 << 32
+    s = seq(base, base + (1 << 28), base + (2 << 28), base + (3 << 28))
+    rc = call_prefix(d, length=8192, chunk=256, s=s, A=base + (4 << 28), D=base + (5 << 28),
+                     y=base + (6 << 28), h_out=base + (7 << 28), ws=None, wsb=0)
+    assert rc == bdssm.ERR_WORKSPACE
+
+
+def test_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    d = good()
+    with pytest.raises(TypeError):
+        bdssm.block_step(d, 16, torch.zeros(4), None, None, None, None, None, stream=0)

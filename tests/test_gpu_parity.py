@@ -1,0 +1,260 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle.
+
+Bounds (relative L2 over the whole tensor, float64): 1e-5 for float32 inputs, 5e-3 for
+bfloat16 inputs with float32 state. y is checked twice: as returned (with D x) and with
+D = 0, because D x dominates y's norm and would hide a wrong scan term.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from bidirectional_mamba_state_amd import bdssm, configs, inputs
+from bidirectional_mamba_state_amd.inputs import Seq
+
+from harness import (TOL_BF16, TOL_F32, gpu_block_step, gpu_commit, gpu_prefix, max_head_rel,
+                     rel, slice_seq, streams_of, tol_for, f32_round)
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _check_prefix(seq, A, D, chunk, h_init=None, want_y=True, want_cs=True, heads=None,
+                  y_dtype=bdssm.F32, in_place=False, label=""):
+    _case(f"prefix {label} len={seq.length} chunk={chunk} y={want_y} cs={want_cs} "
+          f"y_dtype={y_dtype} in_place={in_place}")
+    tol = tol_for(seq.dtype) if y_dtype == bdssm.F32 else max(tol_for(seq.dtype), 5e-3)
+    y, cs, h = gpu_prefix(seq, A, D, chunk, h_init, want_y, want_cs, y_dtype, in_place)
+    yo, cso, ho = oracle.scan(seq, A, D, chunk, h_init=h_init, want_y=want_y,
+                              want_chunk_states=want_cs, heads=heads)
+    hs = slice(None) if heads is None else list(heads)
+    assert rel(h[:, hs], ho[:, hs]) < tol_for(seq.dtype), "final state"
+    if want_cs:
+        assert rel(cs[:, :, hs], cso[:, :, hs]) < tol_for(seq.dtype), "chunk states"
+        assert np.array_equal(cs[:, -1], h), "last chunk state == h_out"
+    if want_y:
+        assert rel(y[:, :, hs], yo[:, :, hs]) < tol, "y"
+        assert max_head_rel(y[:, :, hs], yo[:, :, hs], 2) < 4 * tol
+        # the scan part alone (D = 0)
+        Dz = np.zeros_like(D)
+        yz, _, _ = gpu_prefix(seq, A, Dz, chunk, h_init, True, False, y_dtype)
+        yzo, _, _ = oracle.scan(seq, A, Dz, chunk, h_init=h_init, want_chunk_states=False, heads=heads)
+        assert rel(yz[:, :, hs], yzo[:, :, hs]) < tol, "y - D x"
+    return h
+
+
+def _check_block(h_prefix, fwd, rev, A, D, y_dtype=bdssm.F32, heads=None, label=""):
+    _case(f"block_step {label} T={fwd.length} y_dtype={y_dtype}")
+    tol = tol_for(fwd.dtype) if y_dtype == bdssm.F32 else max(tol_for(fwd.dtype), 5e-3)
+    y = gpu_block_step(h_prefix, fwd, rev, A, D, y_dtype)
+    yo, _, _ = oracle.block_step(h_prefix, fwd, rev, A, D, heads=heads)
+    hs = slice(None) if heads is None else list(heads)
+    assert rel(y[:, :, hs], yo[:, :, hs]) < tol, "block y"
+    Dz = np.zeros_like(D)
+    yz = gpu_block_step(h_prefix, fwd, rev, A, Dz, y_dtype)
+    yzo, _, _ = oracle.block_step(h_prefix, fwd, rev, A, Dz, heads=heads)
+    assert rel(yz[:, :, hs], yzo[:, :, hs]) < tol, "block y - D x"
+    assert max_head_rel(yz[:, :, hs], yzo[:, :, hs], 2) < 4 * tol
+
+
+def _check_commit(h, clean, A, D, label=""):
+    _case(f"commit {label} T={clean.length}")
+    hn, y = gpu_commit(h, clean, A, D, want_y=True)
+    hno, yo = oracle.commit(h, clean, A, D, want_y=True)
+    assert rel(hn, hno) < tol_for(clean.dtype), "commit state"
+    assert rel(y, yo) < tol_for(clean.dtype), "commit y"
+    hn2, _ = gpu_commit(h, clean, A, D, want_y=False)
+    assert np.array_equal(hn, hn2), "commit state does not depend on whether y is written"
+    return hn
+
+
+# ------------------------------------------------------------------ per config
+def test_config0_tiny_fp32_full_path():
+    cfg = configs.get(0)
+    A, D = inputs.params(cfg)
+    pre = inputs.prefix(cfg)
+    h = _check_prefix(pre, A, D, cfg.chunk, label="c0")
+    _check_prefix(pre, A, D, cfg.chunk, y_dtype=bdssm.BF16, want_cs=False, label="c0 bf16 y")
+    h = f32_round(h)
+    for k in range(cfg.n_blocks):
+        for step in range(cfg.steps_per_block):
+            fwd = inputs.block(cfg, k, step, inputs.FWD)
+            rev = inputs.block(cfg, k, step, inputs.REV)
+            _check_block(h, fwd, rev, A, D, label=f"c0 block {k} step {step}")
+        h = f32_round(_check_commit(h, inputs.block(cfg, k, 0, inputs.CLEAN), A, D, label=f"c0 block {k}"))
+
+
+def test_config1_700m():
+    cfg = configs.get(1)
+    A, D = inputs.params(cfg)
+    pre = inputs.prefix(cfg)
+    h = f32_round(_check_prefix(pre, A, D, cfg.chunk, want_cs=False, label="c1"))
+    for step in (0, 1, cfg.steps_per_block - 1):
+        fwd = inputs.block(cfg, 0, step, inputs.FWD)
+        rev = inputs.block(cfg, 0, step, inputs.REV)
+        _check_block(h, fwd, rev, A, D, label=f"c1 step {step}")
+    _check_block(h, inputs.block(cfg, 0, 0, inputs.FWD), inputs.block(cfg, 0, 0, inputs.REV), A, D,
+                 y_dtype=bdssm.BF16, label="c1 bf16 y")
+    _check_commit(h, inputs.block(cfg, 0, 0, inputs.CLEAN), A, D, label="c1")
+
+
+def test_config2_prefix_chunk_states_sampled_heads():
+    cfg = configs.get(2)
+    A, D = inputs.params(cfg)
+    pre = inputs.prefix(cfg)
+    h = _check_prefix(pre, A, D, cfg.chunk, heads=(0, 17, 31), label="c2")
+    _check_commit(f32_round(h), inputs.block(cfg, 0, 0, inputs.CLEAN), A, D, label="c2")
+
+
+def test_config3_long_context_grouped():
+    cfg = configs.get(3)
+    A, D = inputs.params(cfg)
+    pre = inputs.prefix(cfg)
+    # state-only prefix; heads sampled from different groups (10 heads per group)
+    h = _check_prefix(pre, A, D, cfg.chunk, want_y=False, want_cs=False, heads=(0, 29, 79),
+                      label="c3")
+    hf = f32_round(h)
+    fwd = inputs.block(cfg, 0, 0, inputs.FWD)
+    rev = inputs.block(cfg, 0, 0, inputs.REV)
+    _check_block(hf, fwd, rev, A, D, heads=(0, 29, 79), label="c3")
+
+
+# ------------------------------------------------------------------ edge cases
+def _small(b=2, L=100, H=4, P=16, N=16, G=2, dtype=1, seed=0):
+    rng = np.random.default_rng(seed)
+    from test_oracle_pins import rand_seq
+    return rand_seq(rng, b, L, H, P, N, G, dtype), rng
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64, 128, 256])
+def test_chunk_invariance(chunk):
+    seq, rng = _small(L=300, dtype=0)
+    A = (-np.exp(rng.uniform(0, np.log(16), 4))).astype(np.float32)
+    D = rng.standard_normal(4).astype(np.float32)
+    h0 = rng.standard_normal((2, 4, 16, 16)) * 0.1
+    _check_prefix(seq, A, D, chunk, h_init=h0, label=f"chunk sweep {chunk}")
+
+
+@pytest.mark.parametrize("L", [1, 15, 16, 17, 257])
+def test_ragged_lengths(L):
+    seq, rng = _small(L=L, dtype=0)
+    A = (-np.exp(rng.uniform(0, np.log(16), 4))).astype(np.float32)
+    D = rng.standard_normal(4).astype(np.float32)
+    _check_prefix(seq, A, D, 16, label=f"ragged {L}")
+    _check_prefix(seq, A, D, 16, want_y=False, want_cs=False, label=f"ragged {L} state-only")
+
+
+def test_in_place_state_update():
+    seq, rng = _small(L=200, dtype=1, P=64, N=128, H=4, G=1)
+    A = (-np.exp(rng.uniform(0, np.log(16), 4))).astype(np.float32)
+    D = rng.standard_normal(4).astype(np.float32)
+    h0 = rng.standard_normal((2, 4, 128, 64)) * 0.1
+    for want_y, want_cs in ((True, True), (True, False), (False, True), (False, False)):
+        _check_prefix(seq, A, D, 64, h_init=h0, want_y=want_y, want_cs=want_cs, in_place=True,
+                      label="in place")
+
+
+@pytest.mark.parametrize("T", [1, 7, 16, 33, 128, 256])
+def test_block_lengths(T):
+    rng = np.random.default_rng(T)
+    from test_oracle_pins import rand_seq
+    fwd = rand_seq(rng, 2, T, 4, 64, 128, 2, 1)
+    rev = rand_seq(rng, 2, T, 4, 64, 128, 2, 1)
+    A = (-np.exp(rng.uniform(0, np.log(16), 4))).astype(np.float32)
+    D = rng.standard_normal(4).astype(np.float32)
+    h = f32_round(rng.standard_normal((2, 4, 128, 64)) * 0.1)
+    _check_block(h, fwd, rev, A, D, label=f"T={T}")
+    _check_commit(h, fwd, A, D, label=f"T={T}")
+
+
+def test_empty_inputs():
+    t = pytest.importorskip("torch")
+    d = bdssm.dims(1, 4, 16, 16, 1, bdssm.F32)
+    e = t.empty(0, device="cuda")
+    A = t.full((4,), -1.0, device="cuda")
+    D = t.ones(4, device="cuda")
+    h0 = t.randn(1, 4, 16, 16, device="cuda")
+    ho = t.full((1, 4, 16, 16), 7.0, device="cuda")
+    seq = (t.empty(16, device="cuda"),) * 4
+    bdssm.prefix_scan(d, 0, 64, seq, A, D, h0, None, None, ho)   # zero tokens: h_out = h_init
+    t.cuda.synchronize()
+    assert t.equal(ho, h0)
+    bdssm.prefix_scan(d, 0, 64, seq, A, D, None, None, None, ho)  # ... or zero
+    t.cuda.synchronize()
+    assert not ho.any()
+    y = t.full((4,), 3.0, device="cuda")
+    bdssm.block_step(d, 0, h0, seq, seq, A, D, y)                 # nothing to do
+    hb = h0.clone()
+    bdssm.commit(d, 0, seq, A, D, hb)
+    d0 = bdssm.dims(0, 4, 16, 16, 1, bdssm.F32)
+    bdssm.block_step(d0, 16, h0, seq, seq, A, D, y)
+    t.cuda.synchronize()
+    assert t.equal(hb, h0) and bool((y == 3.0).all())
+    del e
+
+
+# ------------------------------------------------------------------ invariants
+def test_cached_state_untouched_and_deterministic():
+    t = pytest.importorskip("torch")
+    cfg = configs.get(1)
+    A, D = inputs.params(cfg)
+    rng = np.random.default_rng(1)
+    h = t.from_numpy((rng.standard_normal((1, 48, 128, 64)) * 0.05).astype(np.float32)).cuda()
+    h_copy = h.clone()
+    fwd = inputs.block(cfg, 0, 0, inputs.FWD)
+    rev = inputs.block(cfg, 0, 0, inputs.REV)
+    d = bdssm.dims(1, 48, 64, 128, 1, bdssm.BF16)
+    Ad, Dd = t.from_numpy(A).cuda(), t.from_numpy(D).cuda()
+    fd, rd = bdssm.seq_to_device(fwd), bdssm.seq_to_device(rev)
+    ys = []
+    for _ in range(8):
+        y = t.empty((1, 32, 48, 64), device="cuda")
+        bdssm.block_step(d, 32, h, fd, rd, Ad, Dd, y)
+        ys.append(y)
+    t.cuda.synchronize()
+    assert t.equal(h, h_copy), "block step wrote the cached state"
+    for y in ys[1:]:
+        assert t.equal(y, ys[0]), "block step is not deterministic"
+
+
+def test_reverse_locality_and_stream_independence():
+    t = pytest.importorskip("torch")
+    rng = np.random.default_rng(2)
+    from test_oracle_pins import rand_seq
+    b, T, H, P, N = 3, 32, 4, 64, 128
+    fwd = rand_seq(rng, b, T, H, P, N, 1, 1)
+    rev = rand_seq(rng, b, T, H, P, N, 1, 1)
+    A = (-np.exp(rng.uniform(0, np.log(16), H))).astype(np.float32)
+    D = np.zeros(H, np.float32)
+    h1 = f32_round(rng.standard_normal((b, H, N, P)) * 0.1)
+    h2 = h1.copy()
+    h2[1] += f32_round(rng.standard_normal((H, N, P)) * 0.1)
+    y1 = gpu_block_step(h1, fwd, rev, A, D)
+    y2 = gpu_block_step(h2, fwd, rev, A, D)
+    assert np.array_equal(y1[[0, 2]], y2[[0, 2]]), "perturbing stream 1 changed other streams"
+    # the change is exactly the forward state term, independent of the reverse inputs
+    zero_x = Seq(np.zeros_like(fwd.x), fwd.dt, fwd.B, fwd.C, fwd.dtype)
+    zero_r = Seq(np.zeros_like(rev.x), rev.dt, rev.B, rev.C, rev.dtype)
+    dh = h2 - h1
+    yd = gpu_block_step(dh, zero_x, zero_r, A, D)
+    ydo, _, _ = oracle.block_step(dh, zero_x, zero_r, A, D)
+    assert rel(yd, ydo) < TOL_BF16
+    assert rel(y2 - y1, ydo) < TOL_BF16
+
+
+def test_commit_chain_equals_prefix_scan():
+    cfg = configs.get(1)
+    A, D = inputs.params(cfg)
+    pre = inputs.prefix(cfg, length=1024)
+    _case("commit chain: 32 commits of 32 tokens vs one 1024-token scan")
+    _, cs, h_scan = gpu_prefix(pre, A, D, 256, want_y=False, want_cs=True)
+    h = np.zeros((1, 48, 128, 64))
+    for k in range(32):
+        h, _ = gpu_commit(h, slice_seq(pre, 32 * k, 32 * (k + 1)), A, D)
+        if (k + 1) % 8 == 0:
+            assert rel(h, cs[:, (k + 1) // 8 - 1]) < 1e-5
+    assert rel(h, h_scan) < 1e-5
+    _, _, ho = oracle.scan(pre, A, D, 256, want_y=False, want_chunk_states=False)
+    assert rel(h, ho) < TOL_BF16

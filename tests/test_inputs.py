@@ -28,17 +28,23 @@ def test_bf16_rounding_is_nearest_even():
 
 def test_deterministic_and_chunk_invariant():
     cfg = configs.get(1)
-    a = inputs.SegmentStream(cfg, 0, inputs.PREFIX, 0, inputs.FWD).next(96)
-    b = inputs.SegmentStream(cfg, 0, inputs.PREFIX, 0, inputs.FWD)
-    parts = [b.next(40), b.next(56)]
+    P = inputs.PREFIX
+    a = inputs.draw(cfg, 0, P, 0, inputs.FWD, 0, 5000)      # crosses a piece boundary
+    parts = [inputs.draw(cfg, 0, P, 0, inputs.FWD, 0, 40),
+             inputs.draw(cfg, 0, P, 0, inputs.FWD, 40, 4100),
+             inputs.draw(cfg, 0, P, 0, inputs.FWD, 4100, 5000)]
     for i in range(4):
         assert np.array_equal(a[i], np.concatenate([p[i] for p in parts]))
-    c = inputs.SegmentStream(cfg, 0, inputs.PREFIX, 0, inputs.FWD).next(96)
+    c = inputs.draw(cfg, 0, P, 0, inputs.FWD, 0, 5000)
     assert all(np.array_equal(a[i], c[i]) for i in range(4))
-    d = inputs.SegmentStream(cfg, 1, inputs.PREFIX, 0, inputs.FWD).next(96)
-    assert not np.array_equal(a[0], d[0])        # streams differ
-    e = inputs.SegmentStream(cfg, 0, inputs.BLOCK(0), 0, inputs.REV).next(96)
-    assert not np.array_equal(a[0], e[0])        # directions differ
+    d = inputs.draw(cfg, 1, P, 0, inputs.FWD, 0, 96)
+    assert not np.array_equal(a[0][:96], d[0])               # streams differ
+    e = inputs.draw(cfg, 0, inputs.BLOCK(0), 0, inputs.REV, 0, 96)
+    assert not np.array_equal(a[0][:96], e[0])               # segments and directions differ
+    f = inputs.draw(cfg, 0, inputs.BLOCK(0), 0, inputs.FWD, 0, 96)
+    assert not np.array_equal(e[0], f[0])
+    seg = inputs.prefix(cfg, streams=[0], length=5000)
+    assert np.array_equal(seg.x[0], a[0]) and np.array_equal(seg.dt[0], a[1])
 
 
 def test_shapes_dtypes_and_distributions():
