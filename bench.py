@@ -1,0 +1,300 @@
+"""Benchmark of the bidirectional Mamba state hot path on one MI355X.
+
+One step = one pass of the whole hot path over one decoding block of the 700M-shape
+layer (48 heads x 64, d_state 128, ngroups 1, batch 1, bf16 inputs, fp32 state):
+  1. bdssm_prefix_scan over the 8192-token prefix (y in bf16, final state),
+  2. 64 denoising steps of bdssm_block_step (T = 32, distinct fwd/rev inputs per step)
+     against that cached state,
+  3. bdssm_commit of the block's clean inputs.
+value = active (denoised) tokens per second = steps * 64 * 32 / wall time.
+
+Per-kernel times come from HIP events recorded on the launch stream around every call in
+the timed region. The roofline object describes the kernel with the largest share of the
+step. Two more workloads are timed the same way and reported under "secondary": the
+64-stream running-set block step (T = 128, HBM-bound) and the 65,536-token prefix scan
+with per-chunk states (matrix-core-bound). The CPU baseline times the float64 oracle on
+the host on one whole step of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
+MFMA_BF16_PEAK = 2.5e15    # flop/s, dense bf16 matrix cores
+METRIC = "block-step active tokens/s + HBM GB/s; prefix-scan tokens/s + MFMA util"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def src_hash():
+    h = hashlib.sha256()
+    cdir = os.path.join(ROOT, "bidirectional_mamba_state_amd", "csrc")
+    for f in sorted(os.listdir(cdir)):
+        h.update(open(os.path.join(cdir, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+class Timer:
+    """HIP events around launches on the current stream; durations read after sync."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def run(self, name, fn):
+        t = self.torch
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        self.pairs.setdefault(name, []).append((a, b))
+
+    def avg_us(self, name):
+        ps = self.pairs.get(name, [])
+        return 1e3 * sum(a.elapsed_time(b) for a, b in ps) / len(ps) if ps else 0.0
+
+    def total_us(self, name):
+        return self.avg_us(name) * len(self.pairs.get(name, []))
+
+
+def block_step_bytes(b, H, P, N, G, T, in_bytes, y_bytes):
+    state = b * H * N * P * 4
+    inputs = 2 * b * T * (H * P + H + 2 * G * N) * in_bytes + 2 * H * 4
+    return state + inputs + b * T * H * P * y_bytes
+
+
+def commit_bytes(b, H, P, N, G, T, in_bytes):
+    return 2 * b * H * N * P * 4 + b * T * (H * P + H + G * N) * in_bytes + 2 * H * 4
+
+
+def prefix_bytes(b, H, P, N, G, L, Q, in_bytes, y_bytes, chunk_states):
+    nch = -(-L // Q)
+    io = b * L * (H * P + H + 2 * G * N) * in_bytes + b * L * H * P * y_bytes
+    return io + b * H * N * P * 4 + (b * nch * H * N * P * 4 if chunk_states else 0)
+
+
+def prefix_flops(b, H, P, N, G, L, Q):
+    """Dense matrix-form flops of the chunked scan: per chunk and head, C.B^T (shared by
+    the H/G heads of a group), the masked (Q x Q)(Q x P) product, the chunk state
+    B^T (Q x P) and the state-to-output product C (N x P)."""
+    nch = -(-L // Q)
+    hpg = H // G
+    per = 2 * Q * Q * N / hpg + 2 * Q * Q * P + 2 * Q * N * P + 2 * Q * N * P
+    return b * nch * H * per
+
+
+def make_roofline(kind, work, avg_us, traffic=None):
+    if kind == "hbm":
+        ach = work / (avg_us * 1e-6) / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                "frac": round(ach / (HBM_PEAK / 1e9), 4), "traffic": traffic}
+    ach = work / (avg_us * 1e-6) / 1e12
+    return {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK / 1e12,
+            "unit": "TFLOP/s", "frac": round(ach / (MFMA_BF16_PEAK / 1e12), 4), "traffic": traffic}
+
+
+def traffic_for(kernel):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on
+    the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    e = d.get(kernel)
+    if not e or e.get("src_hash") != src_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this hot path has no multi-GPU mode "
+              "(streams or heads would shard with no exchange); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from bidirectional_mamba_state_amd import bdssm, configs, inputs
+
+    torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        n = 1 << 28
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": n * 4, "bytes_written": n * 4}))
+        return
+
+    bdssm.load()
+    cfg = configs.get(1)
+    b, H, P, N, G, L, Q, T = (cfg.batch, cfg.nheads, cfg.headdim, cfg.d_state, cfg.ngroups,
+                              cfg.prefix_len, cfg.chunk, cfg.block_len)
+    S = cfg.steps_per_block
+    A, D = inputs.params(cfg)
+    d = bdssm.dims(b, H, P, N, G, cfg.in_dtype, bdssm.BF16)
+    Ad, Dd = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
+    pre_np = inputs.prefix(cfg)
+    pre = bdssm.seq_to_device(pre_np)
+    steps_np = [(inputs.block(cfg, 0, s, inputs.FWD), inputs.block(cfg, 0, s, inputs.REV)) for s in range(S)]
+    steps = [(bdssm.seq_to_device(f), bdssm.seq_to_device(r)) for f, r in steps_np]
+    clean_np = inputs.block(cfg, 0, 0, inputs.CLEAN)
+    clean = bdssm.seq_to_device(clean_np)
+    h = torch.empty((b, H, N, P), device="cuda")
+    y_pre = torch.empty((b, L, H, P), dtype=torch.bfloat16, device="cuda")
+    y_blk = [torch.empty((b, T, H, P), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
+    wsb = bdssm.prefix_scan_workspace(d, L, Q, True, False)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+
+    def one_step(tm):
+        tm.run("prefix_scan", lambda: bdssm.prefix_scan(d, L, Q, pre, Ad, Dd, None, y_pre, None, h, ws, wsb))
+        for s in range(S):
+            f, r = steps[s]
+            tm.run("block_step", lambda: bdssm.block_step(d, T, h, f, r, Ad, Dd, y_blk[s]))
+        tm.run("commit", lambda: bdssm.commit(d, T, clean, Ad, Dd, h))
+
+    for _ in range(args.warmup):
+        one_step(Timer(torch))
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(tm)
+        print(f"[bench] step {i + 1}/{args.steps}", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall / args.steps
+    active = args.steps * S * b * T
+    value = active / wall
+
+    ib, yb = 2, 2
+    k_bytes = {"block_step": block_step_bytes(b, H, P, N, G, T, ib, yb),
+               "commit": commit_bytes(b, H, P, N, G, T, ib),
+               "prefix_scan": prefix_bytes(b, H, P, N, G, L, Q, ib, yb, False)}
+    pf = prefix_flops(b, H, P, N, G, L, Q)
+    breakdown = {}
+    for k in ("prefix_scan", "block_step", "commit"):
+        us = tm.avg_us(k)
+        breakdown[k] = {"launches_per_step": len(tm.pairs[k]) // args.steps, "avg_us": round(us, 3),
+                        "share_of_step": round(tm.total_us(k) / (1e3 * ms_per_step * args.steps), 4),
+                        "alg_bytes": k_bytes[k],
+                        "hbm_frac": round(k_bytes[k] / (us * 1e-6) / HBM_PEAK, 4)}
+    breakdown["prefix_scan"]["tokens_per_s"] = round(b * L / (tm.avg_us("prefix_scan") * 1e-6), 1)
+    breakdown["prefix_scan"]["mfma_frac"] = round(pf / (tm.avg_us("prefix_scan") * 1e-6) / MFMA_BF16_PEAK, 5)
+    breakdown["block_step"]["active_tokens_per_s"] = round(b * T / (tm.avg_us("block_step") * 1e-6), 1)
+    dom = max(("prefix_scan", "block_step", "commit"), key=tm.total_us)
+    if dom == "prefix_scan":
+        roof = make_roofline("mfma", pf, tm.avg_us(dom), traffic_for(dom))
+    else:
+        roof = make_roofline("hbm", k_bytes[dom], tm.avg_us(dom), traffic_for(dom))
+    roof["kernel"] = dom
+    roof["work_per_launch"] = pf if dom == "prefix_scan" else k_bytes[dom]
+
+    out = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic (seeded; random-init layer parameters)",
+           "config": {"workload": "700M-shape Mamba-2 layer, 48 heads x 64, d_state 128, ngroups 1, "
+                                  "batch 1, bf16 inputs, fp32 state: 8192-token prefix scan + "
+                                  "64 block steps (T=32) + commit per step",
+                      "global_batch": b, "seq_len": L, "block_len": T, "steps_per_block": S,
+                      "parallelism": "none (1 GPU)"},
+           "roofline": roof, "breakdown": breakdown}
+
+    if not args.no_secondary:
+        out["secondary"] = secondary(torch, np, bdssm, configs, inputs)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(np, cfg, A, D, pre_np, steps_np, clean_np)
+    print(json.dumps(out), flush=True)
+
+
+def secondary(torch, np, bdssm, configs, inputs, reps=20):
+    res = []
+    # 64-stream running set: T = 128, fp32 state per stream (values do not affect timing;
+    # the state is drawn at random, inputs from the seeded generator)
+    c4 = configs.get(4)
+    b, H, P, N, G, T = c4.batch, c4.nheads, c4.headdim, c4.d_state, c4.ngroups, c4.block_len
+    A, D = inputs.params(c4)
+    Ad, Dd = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
+    d = bdssm.dims(b, H, P, N, G, c4.in_dtype, bdssm.BF16)
+    h = torch.randn((b, H, N, P), device="cuda") * 0.05
+    f = bdssm.seq_to_device(inputs.block(c4, 0, 0, inputs.FWD))
+    r = bdssm.seq_to_device(inputs.block(c4, 0, 0, inputs.REV))
+    y = torch.empty((b, T, H, P), dtype=torch.bfloat16, device="cuda")
+    tm = Timer(torch)
+    for i in range(reps + 3):
+        (tm if i >= 3 else Timer(torch)).run("k", lambda: bdssm.block_step(d, T, h, f, r, Ad, Dd, y))
+    torch.cuda.synchronize()
+    us = tm.avg_us("k")
+    nb = block_step_bytes(b, H, P, N, G, T, 2, 2)
+    res.append({"workload": "block step, 700M shape x 64 streams, running set T=128, bf16 in/out",
+                "avg_us": round(us, 3), "active_tokens_per_s": round(b * T / (us * 1e-6), 1),
+                "roofline": make_roofline("hbm", nb, us, traffic_for("block_step_c4")),
+                "alg_bytes": nb})
+    del h, f, r, y
+    # 350M prefix: 65,536 tokens, chunk 256, bf16 y + fp32 chunk states
+    c2 = configs.get(2)
+    b, H, P, N, G, L, Q = c2.batch, c2.nheads, c2.headdim, c2.d_state, c2.ngroups, c2.prefix_len, c2.chunk
+    A, D = inputs.params(c2)
+    Ad, Dd = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
+    d = bdssm.dims(b, H, P, N, G, c2.in_dtype, bdssm.BF16)
+    pre = bdssm.seq_to_device(inputs.prefix(c2))
+    y = torch.empty((b, L, H, P), dtype=torch.bfloat16, device="cuda")
+    cs = torch.empty((b, -(-L // Q), H, N, P), device="cuda")
+    ho = torch.empty((b, H, N, P), device="cuda")
+    wsb = bdssm.prefix_scan_workspace(d, L, Q, True, True)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    tm = Timer(torch)
+    for i in range(8):
+        (tm if i >= 2 else Timer(torch)).run(
+            "k", lambda: bdssm.prefix_scan(d, L, Q, pre, Ad, Dd, None, y, cs, ho, ws, wsb))
+    torch.cuda.synchronize()
+    us = tm.avg_us("k")
+    fl = prefix_flops(b, H, P, N, G, L, Q)
+    nb = prefix_bytes(b, H, P, N, G, L, Q, 2, 2, True)
+    res.append({"workload": "prefix scan, 350M shape, 65,536 tokens, chunk 256, bf16 y + fp32 chunk states",
+                "avg_us": round(us, 3), "prefix_tokens_per_s": round(b * L / (us * 1e-6), 1),
+                "roofline": make_roofline("mfma", fl, us, traffic_for("prefix_scan_c2")),
+                "hbm_frac": round(nb / (us * 1e-6) / HBM_PEAK, 4), "alg_bytes": nb, "flops": fl})
+    return res
+
+
+def cpu_baseline(np, cfg, A, D, pre_np, steps_np, clean_np):
+    """The float64 oracle on the host cores, one whole step of the same workload."""
+    import oracle
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    _, _, h = oracle.scan(pre_np, A, D, cfg.chunk, want_y=True, want_chunk_states=False)
+    hf = h.astype(np.float32).astype(np.float64)
+    for f, r in steps_np:
+        oracle.block_step(hf, f, r, A, D)
+    oracle.commit(hf, clean_np, A, D)
+    wall = time.perf_counter() - t0
+    active = cfg.steps_per_block * cfg.batch * cfg.block_len
+    return {"value": round(active / wall, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "one whole step (8192-token prefix scan with y, 64 block steps, commit) of the "
+                      f"same workload; {wall:.2f} s of host time"}
+
+
+if __name__ == "__main__":
+    main()
