@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/bdssm.h: argument validation, the prefix
 // scan's work plan and workspace, and kernel dispatch on the caller's stream.
 #include <limits.h>
+#include <stdlib.h>
 #include <stdint.h>
 
 #include <algorithm>
@@ -108,6 +109,23 @@ Plan plan_prefix(const Shape &s, int64_t len, int32_t chunk, bool with_y, bool w
 }
 
 bdssm_status launched(hipError_t e) { return e == hipSuccess ? BDSSM_OK : BDSSM_ERR_HIP; }
+
+// Tuning knobs for launch-shape sweeps: BDSSM_BLOCK_HPW (heads per workgroup, must divide
+// the heads of a group) and BDSSM_BLOCK_PS (column splits: 1, 2 or 4). Invalid values are
+// ignored.
+void override_block_plan(const Shape &s, int *hpw, int *ps)
+{
+    if (const char *e = getenv("BDSSM_BLOCK_HPW")) {
+        const int v = atoi(e);
+        if (v >= 1 && (s.H / s.G) % v == 0)
+            *hpw = v;
+    }
+    if (const char *e = getenv("BDSSM_BLOCK_PS")) {
+        const int v = atoi(e);
+        if (v == 1 || v == 2 || v == 4)
+            *ps = v;
+    }
+}
 
 }  // namespace
 
@@ -273,6 +291,12 @@ bdssm_status bdssm_block_step(const bdssm_dims *dims, int32_t block_len,
         return BDSSM_OK;
     BlockArgs a{s, block_len, h_prefix, Seq{fwd->x, fwd->dt, fwd->B, fwd->C},
                 Seq{rev->x, rev->dt, rev->B, rev->C}, A, D, y};
+    if (block_mfma_supported(s, block_len)) {
+        int hpw, ps;
+        block_mfma_plan(s, &hpw, &ps);
+        override_block_plan(s, &hpw, &ps);
+        return launched(launch_block_step_mfma(a, hpw, ps, static_cast<hipStream_t>(stream)));
+    }
     return launched(launch_block_step_valu(a, static_cast<hipStream_t>(stream)));
 }
 

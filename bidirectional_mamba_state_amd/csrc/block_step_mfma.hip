@@ -1,0 +1,517 @@
+// Block step on bf16 matrix cores (gfx950 v_mfma_f32_16x16x32_bf16), d_state 128, headdim 64.
+//
+// One denoising step of "Training Hybrid Block Diffusion Language Models with Partial
+// Bidirectionality", eqs. (11)-(13), in the matrix ("dual") form of the Mamba-2 scan.
+// With a_t = dt_t A and cumulative sums c_t = sum_{k<=t} a_k (forward) and
+// r_t = sum_{k>=t} a'_k (reverse), for one head:
+//   y_t = exp(c_t) C_t . h_prefix                                   forward, cached state
+//       + sum_{s<=t} exp(c_t - c_s) dt_s (C_t . B_s) x_s            forward, inside the block
+//       + sum_{s>=t} exp(r_t - r_s) dt'_s (C'_t . B'_s) x'_s        reverse, inside the block
+//       + D x_t
+// which equals the two recurrences of the eqs. up to rounding.
+//
+// Work split. A workgroup owns one stream, HPW consecutive heads of one B/C group and a
+// slice of P/PS columns. Its wavefronts each own one "unit": a 16-token row block and a
+// group of 16-column blocks. The score tiles S = C B^T of both directions depend only on
+// the stream's group, so each wavefront computes the NB+1 causal 16x16 tiles of its row
+// block once (forward tiles for s-blocks <= its block, reverse tiles for s-blocks >=
+// it) and keeps them in registers for all HPW heads. Per head:
+//   - the fp32 state is read once from HBM, split into bf16 hi + lo parts and stored
+//     transposed in LDS (the matrix-core operand wants 8 consecutive d_state entries per
+//     lane); x of both directions is read once and stored transposed in LDS;
+//   - the next head's state and x are already being loaded into registers while this
+//     head computes (software pipelining across the head loop);
+//   - each wavefront accumulates C.(h_hi + h_lo) on the matrix cores, scales rows by
+//     exp(c_t), builds the decay-masked A operands M = S o exp2(..) o dt from its register
+//     tiles, accumulates M X for both directions, adds D x and writes y once.
+// The k-index of the M X products is permuted (lane slots j = 0..3 take s-block 2m, slots
+// 4..7 s-block 2m+1) so that the score tiles' accumulator layout is directly the A-operand
+// layout; the X operand uses the same permutation.
+#include "internal.h"
+
+namespace bdssm {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kN = 128, kP = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 ld16(const void *p) { return *static_cast<const bf16x8 *>(p); }
+
+__device__ __forceinline__ float bf2f(__bf16 v) { return static_cast<float>(v); }
+
+// Guarded loads without branches: the address is clamped to a valid row and the value
+// replaced by zero afterwards, so that all loads of a phase can be in flight together
+// (a branch around a load makes the compiler wait for every outstanding load).
+__device__ __forceinline__ bf16x8 sel8(bool ok, bf16x8 v) { return ok ? v : bf16x8{}; }
+__device__ __forceinline__ uint4 sel4(bool ok, uint4 v) { return ok ? v : make_uint4(0, 0, 0, 0); }
+
+__device__ __forceinline__ void store_out(float *p, float v) { *p = v; }
+__device__ __forceinline__ void store_out(__bf16 *p, float v) { *p = static_cast<__bf16>(v); }
+
+template <int NB, int PS>
+struct Geo {
+    static constexpr int TP = NB * 16;        // padded block length
+    static constexpr int PW = kP / PS;        // columns owned by the workgroup
+    static constexpr int PBLK = PW / 16;      // 16-column blocks of the workgroup
+    static constexpr int PBW = PBLK * NB / 8 > 0 ? PBLK * NB / 8 : 1;  // column blocks per unit
+    static constexpr int PGRP = PBLK / PBW;   // column groups per row block
+    static constexpr int UNITS = NB * PGRP;   // one per wavefront
+    static constexpr int THREADS = 64 * UNITS;
+    static constexpr int YW = PBW * 16;       // columns of a unit's output tile
+    // LDS row strides (bf16 elements): transposed state [PW][HS] (16-byte operand reads),
+    // transposed x [PW][XS] (8-byte operand reads), output tile [16][YS]
+    static constexpr int HS = kN + 8;
+    static constexpr int XS = TP + 4;
+    static constexpr int YS = YW + 8;
+    // global-load items: state = 8 rows x 2 columns, x = 4 tokens x 8 columns
+    static constexpr int SITEMS = (kN / 8) * (PW / 2);
+    static constexpr int XITEMS = (TP / 4) * (PW / 8);  // per direction
+    static constexpr int SPT = (SITEMS + THREADS - 1) / THREADS;      // per thread
+    static constexpr int XPT = (2 * XITEMS + THREADS - 1) / THREADS;  // per thread
+};
+
+// One head's global data for this thread, held in registers between load and LDS store.
+// Values are kept exactly as loaded (no masking or conversion): any use right after the
+// load would make the wavefront wait for the whole prefetch.
+template <int SPT, int XPT>
+struct Stage {
+    float2 s[SPT][8];
+    uint4 x[XPT][4];
+    __bf16 d0, d1;  // dt of tokens 2*lane, 2*lane+1 (wavefronts 0 and 1)
+    float A, D;     // the head's A and D
+};
+
+// per-head decay tables (log2 units), one set per LDS buffer
+enum { TAB_CF, TAB_CR, TAB_LGF, TAB_LGR, TAB_COLF, TAB_COLR, TAB_EF, NTAB };
+
+template <int NB, int PS, typename Ty>
+__global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockArgs a, int hpw, int n_hg)
+{
+    using Gm = Geo<NB, PS>;
+    constexpr int TP = Gm::TP, PW = Gm::PW, PBW = Gm::PBW, PGRP = Gm::PGRP, THREADS = Gm::THREADS,
+                  HS = Gm::HS, XS = Gm::XS, YS = Gm::YS, YW = Gm::YW, SITEMS = Gm::SITEMS,
+                  XITEMS = Gm::XITEMS, SPT = Gm::SPT, XPT = Gm::XPT, UNITS = Gm::UNITS;
+    // bf16 outputs leave through a per-wavefront LDS tile as 16-byte row stores
+    constexpr bool YSTAGE = sizeof(Ty) == 2;
+    // two buffers: the next head is staged while the current one is being computed
+    __shared__ __attribute__((aligned(16))) __bf16 hT_hi[2][PW * HS];
+    __shared__ __attribute__((aligned(16))) __bf16 hT_lo[2][PW * HS];
+    __shared__ __attribute__((aligned(16))) __bf16 XTf[2][PW * XS];
+    __shared__ __attribute__((aligned(16))) __bf16 XTr[2][PW * XS];
+    __shared__ __attribute__((aligned(16))) float tab[2][NTAB][TP];
+    __shared__ float hd[2];  // D of the head in each buffer
+    __shared__ __attribute__((aligned(16))) __bf16 ybuf[YSTAGE ? UNITS * 16 * YS : 8];
+
+    // Workgroups sharing a stream (and so its B, C) go to the same XCD: the hardware
+    // deals linear workgroup ids round-robin over the 8 XCDs.
+    const int nwg = gridDim.x;
+    int lid = blockIdx.x;
+    if ((nwg & 7) == 0)
+        lid = (lid & 7) * (nwg >> 3) + (lid >> 3);
+    const int ps = lid % PS;
+    const int hg = (lid / PS) % n_hg;
+    const int b = lid / (PS * n_hg);
+
+    const int T = a.T, H = a.s.H, G = a.s.G;
+    const int h0 = hg * hpw, g = h0 / (H / G);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 4, r16 = lane & 15;
+    const int pbase = ps * PW;
+    const int tb = wave / PGRP, pgrp = wave % PGRP;  // this wavefront's unit
+    const int t = tb * 16 + r16;                      // this lane's row as an A operand
+    const int md = tb >> 1;                           // the 32-token pair holding row block tb
+
+    // per-stream bases (uniform) and row strides in elements; per-lane offsets fit 32 bits
+    const int64_t tok0 = static_cast<int64_t>(b) * T;
+    const int rowBC = G * kN, rowX = H * kP;
+    const __bf16 *Bf = static_cast<const __bf16 *>(a.fwd.B) + tok0 * rowBC + g * kN;
+    const __bf16 *Cf = static_cast<const __bf16 *>(a.fwd.C) + tok0 * rowBC + g * kN;
+    const __bf16 *Br = static_cast<const __bf16 *>(a.rev.B) + tok0 * rowBC + g * kN;
+    const __bf16 *Cr = static_cast<const __bf16 *>(a.rev.C) + tok0 * rowBC + g * kN;
+    const __bf16 *xf = static_cast<const __bf16 *>(a.fwd.x) + tok0 * rowX + pbase;
+    const __bf16 *xr = static_cast<const __bf16 *>(a.rev.x) + tok0 * rowX + pbase;
+    const __bf16 *dtf = static_cast<const __bf16 *>(a.fwd.dt) + tok0 * H;
+    const __bf16 *dtr = static_cast<const __bf16 *>(a.rev.dt) + tok0 * H;
+    const float *hp = a.h_prefix + static_cast<int64_t>(b) * H * (kN * kP) + pbase;
+    Ty *y = static_cast<Ty *>(a.y) + tok0 * rowX + pbase;
+
+    auto load_stage = [&](Stage<SPT, XPT> &st, int h) {
+        const float *hs = hp + h * (kN * kP);
+#pragma unroll
+        for (int k = 0; k < SPT; ++k) {
+            const int i = tid + k * THREADS;
+            if (SITEMS % THREADS == 0 || i < SITEMS) {
+                const int p2 = i % (PW / 2), n8 = (i / (PW / 2)) * 8;
+#pragma unroll
+                for (int r = 0; r < 8; ++r)
+                    st.s[k][r] = *reinterpret_cast<const float2 *>(hs + (n8 + r) * kP + 2 * p2);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < XPT; ++k) {
+            const int i = tid + k * THREADS;
+            if ((2 * XITEMS) % THREADS == 0 || i < 2 * XITEMS) {
+                const bool rv = i >= XITEMS;
+                const int ii = rv ? i - XITEMS : i;
+                const int p8 = ii % (PW / 8), t4 = (ii / (PW / 8)) * 4;
+                const __bf16 *xs = (rv ? xr : xf) + h * kP + p8 * 8;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)  // rows past T are zeroed at store time
+                    st.x[k][r] = *reinterpret_cast<const uint4 *>(xs + min(t4 + r, T - 1) * rowX);
+            }
+        }
+        {   // every wavefront loads (no branch); wavefronts 0 and 1 use them
+            const __bf16 *dts = ((wave & 1) ? dtr : dtf) + h;
+            st.d0 = dts[min(2 * lane, T - 1) * H];  // masked at store time
+            st.d1 = dts[min(2 * lane + 1, T - 1) * H];
+        }
+        st.A = a.A[h];
+        st.D = a.D[h];
+    };
+
+    auto store_stage = [&](const Stage<SPT, XPT> &st, int buf) {
+#pragma unroll
+        for (int k = 0; k < SPT; ++k) {
+            const int i = tid + k * THREADS;
+            if (SITEMS % THREADS == 0 || i < SITEMS) {
+                const int p2 = i % (PW / 2), n8 = (i / (PW / 2)) * 8;
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    bf16x8 hi, lo;
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) {
+                        const float f = c ? st.s[k][r].y : st.s[k][r].x;
+                        const __bf16 fh = static_cast<__bf16>(f);
+                        hi[r] = fh;
+                        lo[r] = static_cast<__bf16>(f - bf2f(fh));
+                    }
+                    *reinterpret_cast<bf16x8 *>(&hT_hi[buf][(2 * p2 + c) * HS + n8]) = hi;
+                    *reinterpret_cast<bf16x8 *>(&hT_lo[buf][(2 * p2 + c) * HS + n8]) = lo;
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < XPT; ++k) {
+            const int i = tid + k * THREADS;
+            if ((2 * XITEMS) % THREADS == 0 || i < 2 * XITEMS) {
+                const bool rv = i >= XITEMS;
+                const int ii = rv ? i - XITEMS : i;
+                const int p8 = ii % (PW / 8), t4 = (ii / (PW / 8)) * 4;
+                __bf16 *dst = (rv ? XTr[buf] : XTf[buf]) + p8 * 8 * XS + t4;
+                uint32_t w[4][4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const uint4 v = sel4(t4 + r < T, st.x[k][r]);
+                    w[r][0] = v.x;
+                    w[r][1] = v.y;
+                    w[r][2] = v.z;
+                    w[r][3] = v.w;
+                }
+                // 4 tokens x 8 columns -> 8 columns x 4 tokens (byte permutes)
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+                    const uint32_t lo2 = __builtin_amdgcn_perm(w[1][c / 2], w[0][c / 2], sel);
+                    const uint32_t hi2 = __builtin_amdgcn_perm(w[3][c / 2], w[2][c / 2], sel);
+                    *reinterpret_cast<uint2 *>(dst + c * XS) = make_uint2(lo2, hi2);
+                }
+            }
+        }
+        if (tid == 0)
+            hd[buf] = st.D;
+        // decay tables: wavefront 0 forward (prefix sums), wavefront 1 reverse (suffix sums);
+        // lane l holds tokens 2l and 2l+1, so 16 lanes cover one 32-token pair
+        if (wave < 2) {
+            const int t0 = 2 * lane, t1 = t0 + 1;
+            const float d0 = t0 < T ? bf2f(st.d0) : 0.f, d1 = t1 < T ? bf2f(st.d1) : 0.f;
+            const float a0 = d0 * st.A, a1 = d1 * st.A;
+            const float loc = a0 + a1;
+            float inc = loc;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float up = __shfl_up(inc, off, 64);
+                if (lane >= off)
+                    inc += up;
+            }
+            const float excl = inc - loc;
+            const float total = __shfl(inc, 63, 64);
+            // forward: c_t inclusive prefix sum; reference at the pair's last token
+            // reverse: r_t inclusive suffix sum; reference at the pair's first token
+            const float c0 = wave == 0 ? (excl + a0) * kLog2e : (total - excl) * kLog2e;
+            const float c1 = wave == 0 ? (excl + loc) * kLog2e : (total - excl - a0) * kLog2e;
+            const float ref = wave == 0 ? __shfl(c1, lane | 15, 64) : __shfl(c0, lane & ~15, 64);
+            if (t0 < TP) {
+                float *cc = tab[buf][wave == 0 ? TAB_CF : TAB_CR];
+                float *lg = tab[buf][wave == 0 ? TAB_LGF : TAB_LGR];
+                float *col = tab[buf][wave == 0 ? TAB_COLF : TAB_COLR];
+                cc[t0] = c0;
+                cc[t1] = c1;
+                lg[t0] = __builtin_amdgcn_logf(d0) - c0;
+                lg[t1] = __builtin_amdgcn_logf(d1) - c1;
+                col[t0] = __builtin_amdgcn_exp2f(ref - c0) * d0;
+                col[t1] = __builtin_amdgcn_exp2f(ref - c1) * d1;
+                if (wave == 0) {
+                    tab[buf][TAB_EF][t0] = __builtin_amdgcn_exp2f(c0);
+                    tab[buf][TAB_EF][t1] = __builtin_amdgcn_exp2f(c1);
+                }
+            }
+        }
+    };
+
+    Stage<SPT, XPT> stage;
+    load_stage(stage, h0);  // the first head's data is in flight while the score tiles are built
+
+    // ---- score tiles of this wavefront's row block, once per workgroup
+    f32x4 S[NB + 1];
+    bf16x8 cfw[4];  // C_t fragments of this row block, kept for the cached-state term
+    {
+        bf16x8 crv[4];
+        const int tc = min(t, T - 1);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            cfw[kk] = sel8(t < T, ld16(Cf + tc * rowBC + 32 * kk + 8 * q));
+            crv[kk] = sel8(t < T, ld16(Cr + tc * rowBC + 32 * kk + 8 * q));
+        }
+#pragma unroll
+        for (int ut = 0; ut <= NB; ++ut) {
+            const bool fwd = ut <= tb;
+            const int s = (fwd ? ut : ut - 1) * 16 + r16, sc = min(s, T - 1);
+            const __bf16 *Bp = (fwd ? Bf : Br) + sc * rowBC + 8 * q;
+            bf16x8 bfrag[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                bfrag[kk] = sel8(s < T, ld16(Bp + 32 * kk));
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                acc = mfma(bfrag[kk], fwd ? cfw[kk] : crv[kk], acc);
+            S[ut] = acc;  // S[t = tb*16 + r16][s = sb*16 + 4q + j]
+        }
+    }
+    store_stage(stage, 0);
+    if (hpw > 1)
+        load_stage(stage, h0 + 1);
+    __syncthreads();
+
+    for (int hh = 0; hh < hpw; ++hh) {
+        const int h = h0 + hh, cur = hh & 1;
+        const __bf16 *hhi = hT_hi[cur], *hlo = hT_lo[cur], *xtf = XTf[cur], *xtr = XTr[cur];
+        const float *cf = tab[cur][TAB_CF], *cr = tab[cur][TAB_CR], *lgf = tab[cur][TAB_LGF],
+                    *lgr = tab[cur][TAB_LGR], *colf = tab[cur][TAB_COLF], *colr = tab[cur][TAB_COLR],
+                    *ef = tab[cur][TAB_EF];
+
+        f32x4 acc[PBW];
+#pragma unroll
+        for (int pb = 0; pb < PBW; ++pb)
+            acc[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // eq. (11), cached-state term: C_t . h, h = hi + lo
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+            for (int pb = 0; pb < PBW; ++pb) {
+                const int pc = (pgrp * PBW + pb) * 16 + r16;
+                acc[pb] = mfma(cfw[kk], ld16(&hhi[pc * HS + 32 * kk + 8 * q]), acc[pb]);
+                acc[pb] = mfma(cfw[kk], ld16(&hlo[pc * HS + 32 * kk + 8 * q]), acc[pb]);
+            }
+        }
+        {
+            const float4 e4 = *reinterpret_cast<const float4 *>(&ef[tb * 16 + 4 * q]);
+#pragma unroll
+            for (int pb = 0; pb < PBW; ++pb) {
+                acc[pb][0] *= e4.x;
+                acc[pb][1] *= e4.y;
+                acc[pb][2] *= e4.z;
+                acc[pb][3] *= e4.w;
+            }
+        }
+        auto mx = [&](const bf16x8 &af, const __bf16 *XT, int m) {
+#pragma unroll
+            for (int pb = 0; pb < PBW; ++pb) {
+                const int pc = (pgrp * PBW + pb) * 16 + r16;
+                const __bf16 *xp = &XT[pc * XS + 32 * m + 4 * q];
+                const bf16x4 lo4 = *reinterpret_cast<const bf16x4 *>(xp);
+                const bf16x4 hi4 = *reinterpret_cast<const bf16x4 *>(xp + 16);
+                acc[pb] = mfma(af, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7), acc[pb]);
+            }
+        };
+        // eq. (11), inside the block (s <= t). Pairs wholly below the row block use the
+        // factored decay exp2(c_t - c_ref) * [exp2(c_ref - c_s) dt_s], c_ref = c at the
+        // pair's last token: both factors are <= 1. The pair holding the row block uses
+        // exp2(c_t - c_s + log2 dt_s) per element, masked to s <= t.
+        const float ctf = cf[t];
+#pragma unroll
+        for (int m = 0; m < NB / 2; ++m) {
+            if (m < md) {
+                const float rowf = __builtin_amdgcn_exp2f(ctf - cf[32 * m + 31]);
+                const float4 c0 = *reinterpret_cast<const float4 *>(&colf[32 * m + 4 * q]);
+                const float4 c1 = *reinterpret_cast<const float4 *>(&colf[32 * m + 16 + 4 * q]);
+                const float cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+                bf16x8 af;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    af[j] = static_cast<__bf16>((j < 4 ? S[2 * m][j] : S[2 * m + 1][j & 3]) * cw[j] * rowf);
+                mx(af, xtf, m);
+            } else if (m == md) {
+                const float4 l0 = *reinterpret_cast<const float4 *>(&lgf[32 * m + 4 * q]);
+                const float4 l1 = *reinterpret_cast<const float4 *>(&lgf[32 * m + 16 + 4 * q]);
+                const float lg[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+                const bool hi_ok = 2 * m + 1 <= tb;
+                bf16x8 af;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int s = 32 * m + (j < 4 ? 0 : 16) + 4 * q + (j & 3);
+                    const float sv = j < 4 ? S[2 * m][j] : (hi_ok ? S[2 * m + 1][j & 3] : 0.f);
+                    const float w = __builtin_amdgcn_exp2f(ctf + lg[j]);
+                    af[j] = static_cast<__bf16>(s <= t ? sv * w : 0.f);
+                }
+                mx(af, xtf, m);
+            }
+        }
+        // eq. (12), reverse inside the block (s >= t); pairs wholly above the row block use
+        // the factored decay with the reference at the pair's first token
+        const float ctr = cr[t];
+#pragma unroll
+        for (int m = 0; m < NB / 2; ++m) {
+            if (m > md) {
+                const float rowr = __builtin_amdgcn_exp2f(ctr - cr[32 * m]);
+                const float4 c0 = *reinterpret_cast<const float4 *>(&colr[32 * m + 4 * q]);
+                const float4 c1 = *reinterpret_cast<const float4 *>(&colr[32 * m + 16 + 4 * q]);
+                const float cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+                bf16x8 af;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    af[j] = static_cast<__bf16>((j < 4 ? S[2 * m + 1][j] : S[2 * m + 2][j & 3]) * cw[j] * rowr);
+                mx(af, xtr, m);
+            } else if (m == md) {
+                const float4 l0 = *reinterpret_cast<const float4 *>(&lgr[32 * m + 4 * q]);
+                const float4 l1 = *reinterpret_cast<const float4 *>(&lgr[32 * m + 16 + 4 * q]);
+                const float lg[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+                const bool lo_ok = 2 * m >= tb;
+                bf16x8 af;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int s = 32 * m + (j < 4 ? 0 : 16) + 4 * q + (j & 3);
+                    const float sv = j < 4 ? (lo_ok ? S[2 * m + 1][j] : 0.f) : S[2 * m + 2][j & 3];
+                    const float w = __builtin_amdgcn_exp2f(ctr + lg[j]);
+                    af[j] = static_cast<__bf16>(s >= t ? sv * w : 0.f);
+                }
+                mx(af, xtr, m);
+            }
+        }
+        // eq. (13) + D x, written once: the lane holds rows tb*16 + 4q + j of column pc
+        const float Dh = hd[cur];
+        Ty *yh = y + h * kP + pgrp * YW;
+        if constexpr (YSTAGE) {
+            __bf16 *yt = &ybuf[wave * 16 * YS];
+#pragma unroll
+            for (int pb = 0; pb < PBW; ++pb) {
+                const int pc = (pgrp * PBW + pb) * 16 + r16;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int tr = tb * 16 + 4 * q + j;
+                    yt[(4 * q + j) * YS + pb * 16 + r16] =
+                        static_cast<__bf16>(fmaf(Dh, bf2f(xtf[pc * XS + tr]), acc[pb][j]));
+                }
+            }
+            // the wavefront reads back its own tile: rows of YW bf16 in 16-byte pieces
+            constexpr int CPR = YW / 8, CHUNKS = 16 * CPR;
+#pragma unroll
+            for (int c0 = 0; c0 < CHUNKS; c0 += 64) {
+                const int c = c0 + lane, row = c / CPR, col = (c % CPR) * 8;
+                if ((CHUNKS % 64 == 0 || c < CHUNKS) && tb * 16 + row < T)
+                    *reinterpret_cast<uint4 *>(yh + (tb * 16 + row) * rowX + col) =
+                        *reinterpret_cast<const uint4 *>(&yt[row * YS + col]);
+            }
+        } else {
+#pragma unroll
+            for (int pb = 0; pb < PBW; ++pb) {
+                const int pc = (pgrp * PBW + pb) * 16 + r16;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int tr = tb * 16 + 4 * q + j;
+                    if (tr < T)
+                        store_out(yh + tr * rowX + pb * 16 + r16, fmaf(Dh, bf2f(xtf[pc * XS + tr]), acc[pb][j]));
+                }
+            }
+        }
+        // stage the next head into the other buffer (its previous contents were last read
+        // before the barrier that ended the previous head), then sync, then prefetch
+        if (hh + 1 < hpw)
+            store_stage(stage, cur ^ 1);
+        __syncthreads();
+        if (hh + 2 < hpw)
+            load_stage(stage, h + 2);
+    }
+}
+
+template <int NB, int PS, typename Ty>
+hipError_t launch_nb(const BlockArgs &a, int hpw, hipStream_t st)
+{
+    const int n_hg = a.s.H / hpw;
+    const int nwg = a.s.b * n_hg * PS;
+    k_block_mfma<NB, PS, Ty><<<dim3(nwg), dim3(Geo<NB, PS>::THREADS), 0, st>>>(a, hpw, n_hg);
+    return hipGetLastError();
+}
+
+template <int PS, typename Ty>
+hipError_t launch_ps(const BlockArgs &a, int hpw, hipStream_t st)
+{
+    if (a.T <= 32)
+        return launch_nb<2, PS, Ty>(a, hpw, st);
+    if (a.T <= 64)
+        return launch_nb<4, PS, Ty>(a, hpw, st);
+    return launch_nb<8, PS, Ty>(a, hpw, st);
+}
+
+template <typename Ty>
+hipError_t launch_ty(const BlockArgs &a, int hpw, int ps, hipStream_t st)
+{
+    switch (ps) {
+    case 1: return launch_ps<1, Ty>(a, hpw, st);
+    case 2: return launch_ps<2, Ty>(a, hpw, st);
+    default: return launch_ps<4, Ty>(a, hpw, st);
+    }
+}
+
+}  // namespace
+
+bool block_mfma_supported(const Shape &s, int T)
+{
+    return s.in_dt == 1 && s.N == kN && s.P == kP && T >= 1 && T <= 128;
+}
+
+void block_mfma_plan(const Shape &s, int *hpw, int *ps)
+{
+    const int hpg = s.H / s.G;
+    const int64_t pairs = static_cast<int64_t>(s.b) * s.H;
+    if (pairs >= 512) {
+        // about one workgroup per CU (256 CUs; 8 wavefronts with up to 256 registers each),
+        // each running the heads of one group that share its score tiles, with the next
+        // head's loads overlapping the current head's matrix work
+        int best = 1;
+        for (int d = 1; d <= hpg; ++d) {
+            if (hpg % d == 0 && pairs / d >= 256)
+                best = d;
+        }
+        *hpw = best;
+        *ps = 1;
+    } else {
+        *hpw = 1;
+        *ps = pairs * 4 <= 4096 ? 4 : 2;
+    }
+}
+
+hipError_t launch_block_step_mfma(const BlockArgs &a, int hpw, int ps, hipStream_t st)
+{
+    return a.s.y_dt ? launch_ty<__bf16>(a, hpw, ps, st) : launch_ty<float>(a, hpw, ps, st);
+}
+
+}  // namespace bdssm

@@ -258,3 +258,53 @@ def test_commit_chain_equals_prefix_scan():
     assert rel(h, h_scan) < 1e-5
     _, _, ho = oracle.scan(pre, A, D, 256, want_y=False, want_chunk_states=False)
     assert rel(h, ho) < TOL_BF16
+
+
+@pytest.mark.parametrize("T", [32, 128])
+def test_block_step_launch_shapes(monkeypatch, T):
+    """Every (heads per workgroup, column split) launch shape gives the oracle's result."""
+    rng = np.random.default_rng(100 + T)
+    from test_oracle_pins import rand_seq
+    b, H, G = 3, 12, 2        # 6 heads per group
+    fwd = rand_seq(rng, b, T, H, 64, 128, G, 1)
+    rev = rand_seq(rng, b, T, H, 64, 128, G, 1)
+    A = (-np.exp(rng.uniform(0, np.log(16), H))).astype(np.float32)
+    D = rng.standard_normal(H).astype(np.float32)
+    h = f32_round(rng.standard_normal((b, H, 128, 64)) * 0.1)
+    yo, _, _ = oracle.block_step(h, fwd, rev, A, D)
+    Dz = np.zeros_like(D)
+    yzo, _, _ = oracle.block_step(h, fwd, rev, A, Dz)
+    for hpw in (1, 2, 3, 6):
+        for ps in (1, 2, 4):
+            monkeypatch.setenv("BDSSM_BLOCK_HPW", str(hpw))
+            monkeypatch.setenv("BDSSM_BLOCK_PS", str(ps))
+            _case(f"launch shape T={T} hpw={hpw} ps={ps}")
+            y = gpu_block_step(h, fwd, rev, A, D)
+            yz = gpu_block_step(h, fwd, rev, A, Dz)
+            assert rel(y, yo) < TOL_BF16, (hpw, ps)
+            assert rel(yz, yzo) < TOL_BF16, (hpw, ps)
+
+
+def test_config4_running_set_shape():
+    """64 streams x 48 heads, T = 128 (the running set of four 32-token blocks), in the
+    launch configuration the benchmark times; cached states from a 1024-token prefix per
+    stream; oracle on streams {0, 31, 63}."""
+    cfg = configs.get(4)
+    A, D = inputs.params(cfg)
+    pre = inputs.prefix(cfg, length=1024)
+    _, _, h = gpu_prefix(pre, A, D, cfg.chunk, want_y=False, want_cs=False)
+    sample = [0, 31, 63]
+    _, _, ho = oracle.scan(streams_of(pre, sample), A, D, cfg.chunk, want_y=False, want_chunk_states=False)
+    assert rel(h[sample], ho) < TOL_BF16
+    fwd = inputs.block(cfg, 0, 0, inputs.FWD)
+    rev = inputs.block(cfg, 0, 0, inputs.REV)
+    for y_dtype in (bdssm.F32, bdssm.BF16):
+        _case(f"c4 block step y_dtype={y_dtype}")
+        y = gpu_block_step(h, fwd, rev, A, D, y_dtype)
+        yo, _, _ = oracle.block_step(h[sample], streams_of(fwd, sample), streams_of(rev, sample), A, D)
+        assert rel(y[sample], yo) < TOL_BF16
+    Dz = np.zeros_like(D)
+    yz = gpu_block_step(h, fwd, rev, A, Dz)
+    yzo, _, _ = oracle.block_step(h[sample], streams_of(fwd, sample), streams_of(rev, sample), A, Dz)
+    assert rel(yz[sample], yzo) < TOL_BF16
+    assert max_head_rel(yz[sample], yzo, 2) < 4 * TOL_BF16
