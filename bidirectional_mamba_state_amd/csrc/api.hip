@@ -156,6 +156,8 @@ size_t bdssm_prefix_scan_workspace(const bdssm_dims *dims, int64_t len, int32_t 
         return SIZE_MAX;
     if (len == 0 || s.b == 0)
         return 0;
+    if (prefix_mfma_supported(s, chunk))
+        return prefix_mfma_plan(s, len, chunk).ws_bytes;
     return plan_prefix(s, len, chunk, with_y != 0, with_chunk_states != 0).ws_bytes;
 }
 
@@ -210,6 +212,20 @@ bdssm_status bdssm_prefix_scan(const bdssm_dims *dims, int64_t len, int32_t chun
     }
 
     const bool with_y = y != nullptr, with_cs = chunk_states != nullptr;
+    const Seq seq{in->x, in->dt, in->B, in->C};
+    if (prefix_mfma_supported(s, chunk)) {
+        const PrefixPlan mp = prefix_mfma_plan(s, len, chunk);
+        if (mp.ws_bytes > 0) {
+            if (!workspace || workspace_bytes < mp.ws_bytes)
+                return BDSSM_ERR_WORKSPACE;
+            const Range rws = rng(workspace, static_cast<int64_t>(mp.ws_bytes));
+            if (hits(rws, q) || overlap(rws, ry) || overlap(rws, rcs) || overlap(rws, rho) ||
+                overlap(rws, rhi) || overlap(rws, rA) || overlap(rws, rD))
+                return BDSSM_ERR_ALIAS;
+        }
+        return launched(run_prefix_mfma(s, len, chunk, seq, A, D, h_init, y, chunk_states, h_out,
+                                        workspace, st));
+    }
     const Plan p = plan_prefix(s, len, chunk, with_y, with_cs);
     if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes))
         return BDSSM_ERR_WORKSPACE;
@@ -220,7 +236,6 @@ bdssm_status bdssm_prefix_scan(const bdssm_dims *dims, int64_t len, int32_t chun
             return BDSSM_ERR_ALIAS;
     }
 
-    const Seq seq{in->x, in->dt, in->B, in->C};
     if (!with_y && !with_cs && p.nseg == 1) {
         // one pass per (stream, head), from h_init straight to h_out (in place is safe:
         // each workgroup reads its whole state before it writes any of it)

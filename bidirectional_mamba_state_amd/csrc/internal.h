@@ -51,7 +51,19 @@ struct BlockArgs {
     void *y;
 };
 
+struct PrefixPlan {
+    int seg_sub;       // 64-token sub-chunks per segment
+    int nseg;          // segments per stream
+    size_t tot_bytes;  // workspace bytes for segment decays (256-byte rounded)
+    size_t ws_bytes;   // total workspace bytes (0 for a single segment)
+};
+
 bool valu_supported(int N, int P);
+bool prefix_mfma_supported(const Shape &s, int chunk);
+PrefixPlan prefix_mfma_plan(const Shape &s, int64_t len, int chunk);
+hipError_t run_prefix_mfma(const Shape &s, int64_t len, int chunk, const Seq &in, const float *A,
+                           const float *D, const float *h_init, void *y, float *chunk_states,
+                           float *h_out, void *ws, hipStream_t st);
 bool block_mfma_supported(const Shape &s, int T);
 void block_mfma_plan(const Shape &s, int *hpw, int *ps);
 hipError_t launch_block_step_mfma(const BlockArgs &a, int hpw, int ps, hipStream_t st);

@@ -1,0 +1,575 @@
+// Prefix scan on bf16 matrix cores (gfx950 v_mfma_f32_16x16x32_bf16), d_state 128, headdim 64.
+//
+// The prefix operator of "Training Hybrid Block Diffusion Language Models with Partial
+// Bidirectionality", eq. (10): the forward Mamba-2 recurrence of eq. (1) over the prefix,
+// computed in the chunked matrix form. A workgroup owns one (stream, head) and a segment
+// of consecutive 64-token sub-chunks, and walks them in order with the N x P state held
+// in matrix-core accumulator registers (wavefront w owns d_state rows 32w .. 32w+31).
+// For one sub-chunk with cumulative log-decays c_t (relative to its start):
+//   state:   h <- exp(c_63) h + sum_s [exp(c_63 - c_s) dt_s B_s] x_s^T      (B~^T X on MFMA)
+//   output:  y_t = exp(c_t) C_t . h_in + sum_{s<=t} exp(c_t - c_s) dt_s (C_t . B_s) x_s + D x_t
+// The output uses the state entering the sub-chunk, staged in LDS as bf16 hi + lo parts.
+//
+// Two modes:
+//   STATE_ONLY  from h_init (or zero): only the state recurrence; writes the segment's end
+//               state and its total log-decay (used by the segment scan, or as h_out).
+//   FULL        from the state entering the segment: also y, the chunk states (every
+//               chunk/64 sub-chunks, the state after the chunk) and the end state.
+// Matrix-form products are exactly the recurrence up to rounding; the weighted B~ operand
+// is split into bf16 hi + lo parts so that the state keeps ~16 significant bits per term.
+#include <algorithm>
+
+#include "internal.h"
+
+namespace bdssm {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kN = 128, kP = 64, SC = 64;  // d_state, headdim, sub-chunk length
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int HS = kN + 8;   // transposed state rows [P][HS]
+constexpr int XS = SC + 8;   // transposed x rows [P][XS]
+constexpr int BS = SC + 8;   // transposed B rows [N][BS]
+constexpr int YS = kP + 8;   // output tile rows [SC][YS]
+constexpr int RS = kN + 8;   // B rows [SC][RS]
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 ld16(const void *p) { return *static_cast<const bf16x8 *>(p); }
+__device__ __forceinline__ float bf2f(__bf16 v) { return static_cast<float>(v); }
+__device__ __forceinline__ bf16x8 sel8(bool ok, bf16x8 v) { return ok ? v : bf16x8{}; }
+__device__ __forceinline__ uint4 sel4(bool ok, uint4 v) { return ok ? v : make_uint4(0, 0, 0, 0); }
+
+enum { TAB_C, TAB_EF, TAB_LG, TAB_COL, TAB_W, NTAB };
+
+// 4 tokens x 8 bf16 (one uint4 per token) -> 8 columns x 4 tokens, written as uint2 rows
+__device__ __forceinline__ void put_transposed(__bf16 *dst, int stride, const uint4 (&v)[4])
+{
+    const uint32_t w[4][4] = {{v[0].x, v[0].y, v[0].z, v[0].w}, {v[1].x, v[1].y, v[1].z, v[1].w},
+                              {v[2].x, v[2].y, v[2].z, v[2].w}, {v[3].x, v[3].y, v[3].z, v[3].w}};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t lo2 = __builtin_amdgcn_perm(w[1][c / 2], w[0][c / 2], sel);
+        const uint32_t hi2 = __builtin_amdgcn_perm(w[3][c / 2], w[2][c / 2], sel);
+        *reinterpret_cast<uint2 *>(dst + c * stride) = make_uint2(lo2, hi2);
+    }
+}
+
+// 2 tokens x 8 bf16 -> 8 columns x 2 tokens, written as uint32 rows
+__device__ __forceinline__ void put_transposed2(__bf16 *dst, int stride, uint4 v0, uint4 v1)
+{
+    const uint32_t w0[4] = {v0.x, v0.y, v0.z, v0.w}, w1[4] = {v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+        *reinterpret_cast<uint32_t *>(dst + c * stride) = __builtin_amdgcn_perm(w1[c / 2], w0[c / 2], sel);
+    }
+}
+
+struct PrefixArgs {
+    Shape s;
+    int64_t len;         // tokens per stream
+    int seg_sub;         // sub-chunks per segment
+    int nseg;            // segments per stream
+    int chunk_sub;       // sub-chunks per output chunk (chunk / 64)
+    int nch;             // output chunks per stream
+    Seq in;
+    const float *A, *D;
+    const float *h_in;   // state entering each segment: [b][nseg][H][N][P] (FULL), or the
+                         // stream's initial state [b][H][N][P] (STATE_ONLY, nseg == 1); NULL = 0
+    float *h_end;        // end state of each segment: [b][nseg][H][N][P]
+    float *tot;          // total log-decay (natural log) of each segment [b][nseg][H], or NULL
+    void *y;             // FULL: [b][len][H][P] in s.y_dt, or NULL
+    float *chunk_states; // FULL: [b][nch][H][N][P], or NULL
+};
+
+// Wavefronts: the state-only pass uses 4 (each owns 32 d_state rows of the state); the
+// full pass uses 8: for the outputs, two per 16-row block, each owning 32 columns; for the
+// state, each owns 16 d_state rows.
+template <bool FULL>
+struct PGeo {
+    static constexpr int WAVES = FULL ? 8 : 4;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int NBW = kN / 16 / WAVES;  // 16-row d_state blocks per wavefront
+};
+
+template <bool FULL, typename Ty>
+__global__ __launch_bounds__(PGeo<FULL>::THREADS, 2) void k_prefix(PrefixArgs a)
+{
+    constexpr int THREADS = PGeo<FULL>::THREADS, NBW = PGeo<FULL>::NBW;
+    __shared__ __attribute__((aligned(16))) __bf16 XT[kP * XS];
+    __shared__ __attribute__((aligned(16))) __bf16 BT[kN * BS];
+    __shared__ __attribute__((aligned(16))) __bf16 Brow[FULL ? SC * RS : 8];  // B rows (score tiles)
+    __shared__ __attribute__((aligned(16))) __bf16 hT_hi[FULL ? kP * HS : 8];
+    __shared__ __attribute__((aligned(16))) __bf16 hT_lo[FULL ? kP * HS : 8];
+    __shared__ __attribute__((aligned(16))) __bf16 ytile[FULL && sizeof(Ty) == 2 ? SC * YS : 8];
+    __shared__ __attribute__((aligned(16))) float tab[NTAB][SC];
+    __shared__ float sub_tot;  // natural-log decay of the sub-chunk
+
+    // workgroups of one segment (all heads of a stream) go to the same XCD
+    const int nwg = gridDim.x;
+    int lid = blockIdx.x;
+    if ((nwg & 7) == 0)
+        lid = (lid & 7) * (nwg >> 3) + (lid >> 3);
+    const int H = a.s.H, G = a.s.G;
+    const int h = lid % H;
+    const int sg = (lid / H) % a.nseg;
+    const int b = lid / (H * a.nseg);
+    const int g = h / (H / G);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 4, r16 = lane & 15;
+
+    const int64_t len = a.len;
+    const int64_t seg_t0 = static_cast<int64_t>(sg) * a.seg_sub * SC;
+    const int nsub = static_cast<int>(min<int64_t>(a.seg_sub, (len - seg_t0 + SC - 1) / SC));
+    const int rowBC = G * kN, rowX = H * kP;
+    const int64_t tok0 = static_cast<int64_t>(b) * len;
+    const __bf16 *Bg = static_cast<const __bf16 *>(a.in.B) + tok0 * rowBC + g * kN;
+    const __bf16 *Cg = static_cast<const __bf16 *>(a.in.C) + tok0 * rowBC + g * kN;
+    const __bf16 *xg = static_cast<const __bf16 *>(a.in.x) + tok0 * rowX + h * kP;
+    const __bf16 *dtg = static_cast<const __bf16 *>(a.in.dt) + tok0 * H + h;
+    const float Ah = a.A[h];
+    const float Dh = a.D[h];
+    const int64_t NP = static_cast<int64_t>(kN) * kP;
+
+    // ---- state registers: wavefront w holds rows n = 16 (NBW w + i) + 4q + j, columns 16pb + r16
+    f32x4 hs[NBW][4];
+    {
+        const float *hin = nullptr;
+        if (FULL)
+            hin = a.h_in ? a.h_in + ((static_cast<int64_t>(b) * a.nseg + sg) * H + h) * NP : nullptr;
+        else
+            hin = a.h_in ? a.h_in + (static_cast<int64_t>(b) * H + h) * NP : nullptr;
+#pragma unroll
+        for (int i = 0; i < NBW; ++i)
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    hs[i][pb][j] = hin ? hin[(16 * (NBW * wave + i) + 4 * q + j) * kP + 16 * pb + r16] : 0.f;
+    }
+    auto publish_state = [&]() {  // hs -> transposed bf16 hi/lo in LDS (FULL only)
+#pragma unroll
+        for (int i = 0; i < NBW; ++i)
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) {
+                bf16x4 hi, lo;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float f = hs[i][pb][j];
+                    hi[j] = static_cast<__bf16>(f);
+                    lo[j] = static_cast<__bf16>(f - bf2f(hi[j]));
+                }
+                const int off = (16 * pb + r16) * HS + 16 * (NBW * wave + i) + 4 * q;
+                *reinterpret_cast<bf16x4 *>(&hT_hi[off]) = hi;
+                *reinterpret_cast<bf16x4 *>(&hT_lo[off]) = lo;
+            }
+    };
+    if (FULL)
+        publish_state();
+
+    // ---- staging registers, DEPTH sub-chunks ahead (state-only: 2, full: 1)
+    constexpr int DEPTH = FULL ? 1 : 2;
+    constexpr int XI = (SC / 2) * (kP / 8), BI = (SC / 2) * (kN / 8);  // items: 2 tokens x 8
+    constexpr int XPT = (XI + THREADS - 1) / THREADS, BPT = (BI + THREADS - 1) / THREADS;
+    struct StageRegs {
+        uint4 x[XPT][2];  // 2 tokens x 8 columns of x
+        uint4 b[BPT][2];  // 2 tokens x 8 d_state of B
+        __bf16 dt;        // dt of token `lane` (wavefront 0 uses it)
+    };
+    StageRegs ring[DEPTH];
+    auto load_sub = [&](StageRegs &r, int k) {
+        const int64_t t0 = seg_t0 + static_cast<int64_t>(k) * SC;
+        const int last = static_cast<int>(min<int64_t>(SC, len - t0)) - 1;
+        const __bf16 *xk = xg + t0 * rowX, *bk = Bg + t0 * rowBC;  // uniform bases
+        // rows past the end are clamped here and zeroed at store time
+#pragma unroll
+        for (int u = 0; u < XPT; ++u) {
+            const int it = tid + u * THREADS;
+            if (XI % THREADS == 0 || it < XI) {
+                const int p8 = it % 8, t2 = (it / 8) * 2;
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    r.x[u][i] = *reinterpret_cast<const uint4 *>(xk + min(t2 + i, last) * rowX + p8 * 8);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) {
+            const int it = tid + u * THREADS;
+            if (BI % THREADS == 0 || it < BI) {
+                const int n8 = it % 16, t2 = (it / 16) * 2;
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    r.b[u][i] = *reinterpret_cast<const uint4 *>(bk + min(t2 + i, last) * rowBC + n8 * 8);
+            }
+        }
+        r.dt = dtg[t0 * H + min(lane, last) * H];
+    };
+    auto store_sub = [&](const StageRegs &r, int k) {
+        const int64_t t0 = seg_t0 + static_cast<int64_t>(k) * SC;
+        const int nvalid = static_cast<int>(min<int64_t>(SC, len - t0));
+#pragma unroll
+        for (int u = 0; u < XPT; ++u) {
+            const int it = tid + u * THREADS;
+            if (XI % THREADS == 0 || it < XI) {
+                const int p8 = it % 8, t2 = (it / 8) * 2;
+                put_transposed2(&XT[p8 * 8 * XS + t2], XS, sel4(t2 < nvalid, r.x[u][0]), sel4(t2 + 1 < nvalid, r.x[u][1]));
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) {
+            const int it = tid + u * THREADS;
+            if (BI % THREADS == 0 || it < BI) {
+                const int n8 = it % 16, t2 = (it / 16) * 2;
+                const uint4 v0 = sel4(t2 < nvalid, r.b[u][0]), v1 = sel4(t2 + 1 < nvalid, r.b[u][1]);
+                put_transposed2(&BT[n8 * 8 * BS + t2], BS, v0, v1);
+                if (FULL) {
+                    *reinterpret_cast<uint4 *>(&Brow[t2 * RS + n8 * 8]) = v0;
+                    *reinterpret_cast<uint4 *>(&Brow[(t2 + 1) * RS + n8 * 8]) = v1;
+                }
+            }
+        }
+        if (wave == 0) {  // cumulative log2-decays of the sub-chunk, one token per lane
+            const float d = lane < nvalid ? bf2f(r.dt) : 0.f;
+            const float av = d * Ah;
+            float inc = av;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float up = __shfl_up(inc, off, 64);
+                if (lane >= off)
+                    inc += up;
+            }
+            const float c = inc * kLog2e;
+            const float clast = __shfl(c, 63, 64);
+            const float ref = __shfl(c, lane | 31, 64);  // end of this lane's 32-token pair
+            tab[TAB_C][lane] = c;
+            tab[TAB_EF][lane] = __builtin_amdgcn_exp2f(c);
+            tab[TAB_LG][lane] = __builtin_amdgcn_logf(d) - c;
+            tab[TAB_COL][lane] = __builtin_amdgcn_exp2f(ref - c) * d;
+            tab[TAB_W][lane] = __builtin_amdgcn_exp2f(clast - c) * d;
+            if (lane == 63)
+                sub_tot = inc;
+        }
+    };
+
+    float seg_tot = 0.f;
+    Ty *yg = FULL ? static_cast<Ty *>(a.y) : nullptr;
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d)
+        if (d < nsub)
+            load_sub(ring[d], d);
+    // one sub-chunk; `cur` holds its staged inputs and receives those DEPTH sub-chunks ahead
+    auto iter = [&](StageRegs &cur, int k) {
+        const int64_t t0 = seg_t0 + static_cast<int64_t>(k) * SC;
+        const int nvalid = static_cast<int>(min<int64_t>(SC, len - t0));
+        // C fragments of this wavefront's 16 rows, issued before the next prefetch so that
+        // waiting for them does not wait for it (masked at use)
+        bf16x8 cfw[4];
+        if (FULL && yg) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                cfw[kk] = ld16(Cg + (t0 + min(16 * (wave >> 1) + r16, nvalid - 1)) * rowBC + 32 * kk + 8 * q);
+        }
+        store_sub(cur, k);
+        __syncthreads();  // (A) sub-chunk k staged; the state entering it is in hT
+        if (k + DEPTH < nsub)
+            load_sub(cur, k + DEPTH);  // in flight during the next DEPTH sub-chunks
+
+        if (FULL && yg) {
+            // ---- outputs of row block tb = wave / 2, columns 32 (wave & 1) .. +31
+            const int tb = wave >> 1, t = tb * 16 + r16, md = tb >> 1, pb0 = 2 * (wave & 1);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                cfw[kk] = sel8(t < nvalid, cfw[kk]);
+            f32x4 S[4];  // S[t][s = 16 sb + 4q + j] for sb <= tb
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) {
+                S[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (sb <= tb) {
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk)
+                        S[sb] = mfma(ld16(&Brow[(16 * sb + r16) * RS + 32 * kk + 8 * q]), cfw[kk], S[sb]);
+                }
+            }
+            f32x4 acc[2];
+#pragma unroll
+            for (int pb = 0; pb < 2; ++pb)
+                acc[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int pb = 0; pb < 2; ++pb) {
+                    const int pc = 16 * (pb0 + pb) + r16;
+                    acc[pb] = mfma(cfw[kk], ld16(&hT_hi[pc * HS + 32 * kk + 8 * q]), acc[pb]);
+                    acc[pb] = mfma(cfw[kk], ld16(&hT_lo[pc * HS + 32 * kk + 8 * q]), acc[pb]);
+                }
+            {
+                const float4 e4 = *reinterpret_cast<const float4 *>(&tab[TAB_EF][16 * tb + 4 * q]);
+#pragma unroll
+                for (int pb = 0; pb < 2; ++pb) {
+                    acc[pb][0] *= e4.x;
+                    acc[pb][1] *= e4.y;
+                    acc[pb][2] *= e4.z;
+                    acc[pb][3] *= e4.w;
+                }
+            }
+            const float ct = tab[TAB_C][t];  // c_t in log2 units
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                if (m > md)
+                    break;
+                bf16x8 af;
+                if (m < md) {  // pair wholly below the row block: factored decay
+                    const float rowf = __builtin_amdgcn_exp2f(ct - tab[TAB_C][32 * m + 31]);
+                    const float4 c0 = *reinterpret_cast<const float4 *>(&tab[TAB_COL][32 * m + 4 * q]);
+                    const float4 c1 = *reinterpret_cast<const float4 *>(&tab[TAB_COL][32 * m + 16 + 4 * q]);
+                    const float cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        af[j] = static_cast<__bf16>((j < 4 ? S[2 * m][j] : S[2 * m + 1][j & 3]) * cw[j] * rowf);
+                } else {  // the pair holding the row block: per element, masked to s <= t
+                    const float4 l0 = *reinterpret_cast<const float4 *>(&tab[TAB_LG][32 * m + 4 * q]);
+                    const float4 l1 = *reinterpret_cast<const float4 *>(&tab[TAB_LG][32 * m + 16 + 4 * q]);
+                    const float lg[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int s = 32 * m + (j < 4 ? 0 : 16) + 4 * q + (j & 3);
+                        const float sv = j < 4 ? S[2 * m][j] : S[2 * m + 1][j & 3];
+                        af[j] = static_cast<__bf16>(s <= t ? sv * __builtin_amdgcn_exp2f(ct + lg[j]) : 0.f);
+                    }
+                }
+#pragma unroll
+                for (int pb = 0; pb < 2; ++pb) {
+                    const __bf16 *xp = &XT[(16 * (pb0 + pb) + r16) * XS + 32 * m + 4 * q];
+                    const bf16x4 lo4 = *reinterpret_cast<const bf16x4 *>(xp);
+                    const bf16x4 hi4 = *reinterpret_cast<const bf16x4 *>(xp + 16);
+                    acc[pb] = mfma(af, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7), acc[pb]);
+                }
+            }
+            Ty *yk = yg + (tok0 + t0) * rowX + h * kP;
+            if constexpr (sizeof(Ty) == 2) {
+#pragma unroll
+                for (int pb = 0; pb < 2; ++pb)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int tr = 16 * tb + 4 * q + j, pc = 16 * (pb0 + pb) + r16;
+                        ytile[tr * YS + pc] = static_cast<__bf16>(fmaf(Dh, bf2f(XT[pc * XS + tr]), acc[pb][j]));
+                    }
+                // the wavefront writes back its own 16 rows x 32 columns as 16-byte pieces
+                {
+                    const int row = 16 * tb + lane / 4, col = 16 * pb0 + (lane % 4) * 8;
+                    if (row < nvalid)
+                        *reinterpret_cast<uint4 *>(yk + row * rowX + col) =
+                            *reinterpret_cast<const uint4 *>(&ytile[row * YS + col]);
+                }
+            } else {
+#pragma unroll
+                for (int pb = 0; pb < 2; ++pb)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int tr = 16 * tb + 4 * q + j, pc = 16 * (pb0 + pb) + r16;
+                        if (tr < nvalid)
+                            yk[tr * rowX + pc] = fmaf(Dh, bf2f(XT[pc * XS + tr]), acc[pb][j]);
+                    }
+            }
+        }
+
+        // ---- state: h <- exp(c_last) h + (w o B)^T X, w_s = exp(c_last - c_s) dt_s
+        {
+            const float alpha = __expf(sub_tot);
+#pragma unroll
+            for (int i = 0; i < NBW; ++i)
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb)
+                    hs[i][pb] *= alpha;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const float4 w0 = *reinterpret_cast<const float4 *>(&tab[TAB_W][32 * ks + 8 * q]);
+                const float4 w1 = *reinterpret_cast<const float4 *>(&tab[TAB_W][32 * ks + 8 * q + 4]);
+                const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+                bf16x8 bx[4];
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb)
+                    bx[pb] = ld16(&XT[(16 * pb + r16) * XS + 32 * ks + 8 * q]);
+#pragma unroll
+                for (int i = 0; i < NBW; ++i) {
+                    const bf16x8 braw = ld16(&BT[(16 * (NBW * wave + i) + r16) * BS + 32 * ks + 8 * q]);
+                    bf16x8 ahi, alo;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const float f = bf2f(braw[j]) * wv[j];
+                        ahi[j] = static_cast<__bf16>(f);
+                        alo[j] = static_cast<__bf16>(f - bf2f(ahi[j]));
+                    }
+#pragma unroll
+                    for (int pb = 0; pb < 4; ++pb) {
+                        hs[i][pb] = mfma(ahi, bx[pb], hs[i][pb]);
+                        hs[i][pb] = mfma(alo, bx[pb], hs[i][pb]);
+                    }
+                }
+            }
+        }
+        seg_tot += sub_tot;
+        __syncthreads();  // (B) every read of XT, BT, hT and the tables for sub-chunk k is done
+        if (FULL) {
+            publish_state();
+            const int64_t gsub = seg_t0 / SC + k;  // sub-chunk index within the stream
+            if (a.chunk_states && ((gsub + 1) % a.chunk_sub == 0 || (k == nsub - 1 && sg == a.nseg - 1))) {
+                const int64_t c = gsub / a.chunk_sub;
+                float *dst = a.chunk_states + ((static_cast<int64_t>(b) * a.nch + c) * H + h) * NP;
+#pragma unroll
+                for (int i = 0; i < NBW; ++i)
+#pragma unroll
+                    for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            dst[(16 * (NBW * wave + i) + 4 * q + j) * kP + 16 * pb + r16] = hs[i][pb][j];
+            }
+        }
+    };
+    // unrolled by the ring depth so that ring slots are compile-time registers
+    for (int k = 0; k < nsub; k += DEPTH) {
+        iter(ring[0], k);
+        if (DEPTH > 1 && k + 1 < nsub)
+            iter(ring[DEPTH - 1], k + 1);
+    }
+
+    // ---- end state of the segment
+    if (a.h_end) {
+        float *dst = a.h_end + ((static_cast<int64_t>(b) * a.nseg + sg) * H + h) * NP;
+#pragma unroll
+        for (int i = 0; i < NBW; ++i)
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    dst[(16 * (NBW * wave + i) + 4 * q + j) * kP + 16 * pb + r16] = hs[i][pb][j];
+    }
+    if (a.tot && tid == 0)
+        a.tot[(static_cast<int64_t>(b) * a.nseg + sg) * H + h] = seg_tot;
+}
+
+// Segment scan, one thread per state element: the end states of segments started from
+// zero become the states entering each segment (in place), and the final state.
+__global__ __launch_bounds__(256) void k_seg_scan(float *buf, const float *tot, int nseg, int H,
+                                                  const float *h_init, float *h_out)
+{
+    const int64_t NP = static_cast<int64_t>(kN) * kP;
+    const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int h = blockIdx.y, b = blockIdx.z;
+    if (e >= NP)
+        return;
+    float v = h_init ? h_init[(static_cast<int64_t>(b) * H + h) * NP + e] : 0.f;
+    for (int s = 0; s < nseg; ++s) {
+        const int64_t bh = (static_cast<int64_t>(b) * nseg + s) * H + h;
+        const float loc = buf[bh * NP + e];
+        buf[bh * NP + e] = v;
+        v = fmaf(__expf(tot[bh]), v, loc);
+    }
+    if (h_out)
+        h_out[(static_cast<int64_t>(b) * H + h) * NP + e] = v;
+}
+
+template <bool FULL, typename Ty>
+hipError_t launch_prefix(const PrefixArgs &a, hipStream_t st)
+{
+    const int nwg = a.s.b * a.nseg * a.s.H;
+    k_prefix<FULL, Ty><<<dim3(nwg), dim3(PGeo<FULL>::THREADS), 0, st>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool prefix_mfma_supported(const Shape &s, int chunk)
+{
+    return s.in_dt == 1 && s.N == kN && s.P == kP && chunk % SC == 0;
+}
+
+// Work plan: segments of whole chunks, enough (stream, head, segment) workgroups to fill
+// the GPU about twice.
+PrefixPlan prefix_mfma_plan(const Shape &s, int64_t len, int chunk)
+{
+    PrefixPlan p{};
+    const int64_t pairs = std::max<int64_t>(1, static_cast<int64_t>(s.b) * s.H);
+    const int64_t nsub = (len + SC - 1) / SC;
+    const int chunk_sub = chunk / SC;
+    const int64_t want = std::max<int64_t>(1, (512 + pairs - 1) / pairs);
+    int64_t seg_sub = (nsub + want - 1) / want;
+    seg_sub = (seg_sub + chunk_sub - 1) / chunk_sub * chunk_sub;
+    p.seg_sub = static_cast<int>(std::max<int64_t>(seg_sub, chunk_sub));
+    p.nseg = static_cast<int>((nsub + p.seg_sub - 1) / p.seg_sub);
+    const int64_t nbh = static_cast<int64_t>(s.b) * p.nseg * s.H;
+    p.tot_bytes = p.nseg > 1 ? static_cast<size_t>((nbh * 4 + 255) / 256 * 256) : 0;
+    p.ws_bytes = p.nseg > 1 ? p.tot_bytes + static_cast<size_t>(nbh) * kN * kP * 4 : 0;
+    return p;
+}
+
+hipError_t run_prefix_mfma(const Shape &s, int64_t len, int chunk, const Seq &in, const float *A,
+                           const float *D, const float *h_init, void *y, float *chunk_states,
+                           float *h_out, void *ws, hipStream_t st)
+{
+    const PrefixPlan p = prefix_mfma_plan(s, len, chunk);
+    PrefixArgs a{};
+    a.s = s;
+    a.len = len;
+    a.seg_sub = p.seg_sub;
+    a.nseg = p.nseg;
+    a.chunk_sub = chunk / SC;
+    a.nch = static_cast<int>((len + chunk - 1) / chunk);
+    a.in = in;
+    a.A = A;
+    a.D = D;
+    const bool full = y || chunk_states;
+    hipError_t e;
+    if (p.nseg == 1) {
+        // one segment per (stream, head): a single pass from h_init straight to h_out
+        a.h_in = h_init;
+        a.h_end = h_out;
+        a.y = y;
+        a.chunk_states = chunk_states;
+        if (!full)
+            return launch_prefix<false, float>(a, st);
+        // FULL reads its entering state with the [b][nseg][H] layout, which for nseg == 1
+        // is the [b][H] layout of h_init
+        return s.y_dt ? launch_prefix<true, __bf16>(a, st) : launch_prefix<true, float>(a, st);
+    }
+    float *tot = static_cast<float *>(ws);
+    float *segs = reinterpret_cast<float *>(static_cast<char *>(ws) + p.tot_bytes);
+    // 1. segment end states from zero
+    a.h_in = nullptr;
+    a.h_end = segs;
+    a.tot = tot;
+    if ((e = launch_prefix<false, float>(a, st)) != hipSuccess)
+        return e;
+    // 2. states entering each segment (in place); the final state when nothing else follows
+    {
+        dim3 grid(static_cast<unsigned>((kN * kP + 255) / 256), s.H, s.b);
+        k_seg_scan<<<grid, 256, 0, st>>>(segs, tot, p.nseg, s.H, h_init, full ? nullptr : h_out);
+        if ((e = hipGetLastError()) != hipSuccess || !full)
+            return e;
+    }
+    // 3. the full pass from the entering states; the last segment's end state is h_out.
+    //    h_end of the other segments is written into the workspace copy (no longer needed).
+    a.h_in = segs;
+    a.tot = nullptr;
+    a.y = y;
+    a.chunk_states = chunk_states;
+    a.h_end = segs;  // [b][nseg][H]: segment end states (scratch), final copied below
+    if ((e = s.y_dt ? launch_prefix<true, __bf16>(a, st) : launch_prefix<true, float>(a, st)) != hipSuccess)
+        return e;
+    const int64_t NP = static_cast<int64_t>(kN) * kP;
+    for (int b = 0; b < s.b; ++b) {
+        e = launch_copy_f32(h_out + static_cast<int64_t>(b) * s.H * NP,
+                            segs + (static_cast<int64_t>(b) * p.nseg + p.nseg - 1) * s.H * NP, s.H * NP, st);
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace bdssm

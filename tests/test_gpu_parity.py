@@ -308,3 +308,25 @@ def test_config4_running_set_shape():
     yzo, _, _ = oracle.block_step(h[sample], streams_of(fwd, sample), streams_of(rev, sample), A, Dz)
     assert rel(yz[sample], yzo) < TOL_BF16
     assert max_head_rel(yz[sample], yzo, 2) < 4 * TOL_BF16
+
+
+@pytest.mark.parametrize("b,H,G,L,chunk,want_y,want_cs,init", [
+    (1, 4, 1, 640, 64, True, True, True),       # several segments, full pass
+    (2, 6, 2, 1000, 128, True, False, False),   # ragged tail, groups, y only
+    (1, 4, 2, 777, 256, False, True, True),     # chunk states only, ragged
+    (1, 4, 1, 4096, 256, False, False, True),   # state only, several segments + scan
+    (64, 8, 1, 192, 64, True, True, True),      # one segment per (stream, head): single pass
+    (64, 8, 4, 300, 64, False, False, True),    # single pass, state only, ragged
+])
+def test_prefix_matrix_core_paths(b, H, G, L, chunk, want_y, want_cs, init):
+    rng = np.random.default_rng(L + H)
+    from test_oracle_pins import rand_seq
+    seq = rand_seq(rng, b, L, H, 64, 128, G, 1)
+    A = (-np.exp(rng.uniform(0, np.log(16), H))).astype(np.float32)
+    D = rng.standard_normal(H).astype(np.float32)
+    h0 = f32_round(rng.standard_normal((b, H, 128, 64)) * 0.1) if init else None
+    _check_prefix(seq, A, D, chunk, h_init=h0, want_y=want_y, want_cs=want_cs,
+                  label=f"mfma paths b={b} H={H} G={G}")
+    if want_y:
+        _check_prefix(seq, A, D, chunk, h_init=h0, want_y=True, want_cs=False,
+                      y_dtype=bdssm.BF16, label="mfma paths bf16 y")
