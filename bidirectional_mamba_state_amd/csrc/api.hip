@@ -344,8 +344,13 @@ bdssm_status bdssm_commit(const bdssm_dims *dims, int32_t block_len, const bdssm
         return BDSSM_ERR_ALIAS;
     if (s.b == 0 || block_len == 0)
         return BDSSM_OK;
-    ForwardArgs f{s, block_len, block_len, 1, Seq{clean->x, clean->dt, clean->B, clean->C}, A, D,
-                  h, nullptr, y, h, nullptr};
+    const Seq seq{clean->x, clean->dt, clean->B, clean->C};
+    // a commit is a prefix scan of the block from h, in place: on the matrix-core prefix
+    // path, one segment per (stream, head) (no workspace)
+    if (prefix_mfma_supported(s, 64))
+        return launched(run_prefix_mfma(s, block_len, 64, seq, A, D, h, y, nullptr, h, nullptr,
+                                        static_cast<hipStream_t>(stream), true));
+    ForwardArgs f{s, block_len, block_len, 1, seq, A, D, h, nullptr, y, h, nullptr};
     return launched(launch_forward_valu(f, static_cast<hipStream_t>(stream)));
 }
 

@@ -60,10 +60,11 @@ struct PrefixPlan {
 
 bool valu_supported(int N, int P);
 bool prefix_mfma_supported(const Shape &s, int chunk);
-PrefixPlan prefix_mfma_plan(const Shape &s, int64_t len, int chunk);
+// single_segment: one segment per (stream, head), no workspace (used by commits)
+PrefixPlan prefix_mfma_plan(const Shape &s, int64_t len, int chunk, bool single_segment = false);
 hipError_t run_prefix_mfma(const Shape &s, int64_t len, int chunk, const Seq &in, const float *A,
                            const float *D, const float *h_init, void *y, float *chunk_states,
-                           float *h_out, void *ws, hipStream_t st);
+                           float *h_out, void *ws, hipStream_t st, bool single_segment = false);
 bool block_mfma_supported(const Shape &s, int T);
 void block_mfma_plan(const Shape &s, int *hpw, int *ps);
 hipError_t launch_block_step_mfma(const BlockArgs &a, int hpw, int ps, hipStream_t st);

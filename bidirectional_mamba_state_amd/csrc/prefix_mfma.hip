@@ -492,13 +492,13 @@ bool prefix_mfma_supported(const Shape &s, int chunk)
 
 // Work plan: segments of whole chunks, enough (stream, head, segment) workgroups to fill
 // the GPU about twice.
-PrefixPlan prefix_mfma_plan(const Shape &s, int64_t len, int chunk)
+PrefixPlan prefix_mfma_plan(const Shape &s, int64_t len, int chunk, bool single_segment)
 {
     PrefixPlan p{};
     const int64_t pairs = std::max<int64_t>(1, static_cast<int64_t>(s.b) * s.H);
     const int64_t nsub = (len + SC - 1) / SC;
     const int chunk_sub = chunk / SC;
-    const int64_t want = std::max<int64_t>(1, (512 + pairs - 1) / pairs);
+    const int64_t want = single_segment ? 1 : std::max<int64_t>(1, (512 + pairs - 1) / pairs);
     int64_t seg_sub = (nsub + want - 1) / want;
     seg_sub = (seg_sub + chunk_sub - 1) / chunk_sub * chunk_sub;
     p.seg_sub = static_cast<int>(std::max<int64_t>(seg_sub, chunk_sub));
@@ -511,9 +511,9 @@ PrefixPlan prefix_mfma_plan(const Shape &s, int64_t len, int chunk)
 
 hipError_t run_prefix_mfma(const Shape &s, int64_t len, int chunk, const Seq &in, const float *A,
                            const float *D, const float *h_init, void *y, float *chunk_states,
-                           float *h_out, void *ws, hipStream_t st)
+                           float *h_out, void *ws, hipStream_t st, bool single_segment)
 {
-    const PrefixPlan p = prefix_mfma_plan(s, len, chunk);
+    const PrefixPlan p = prefix_mfma_plan(s, len, chunk, single_segment);
     PrefixArgs a{};
     a.s = s;
     a.len = len;

@@ -115,10 +115,18 @@ def test_alignment_and_alias():
 
 
 def test_workspace_query_and_missing_workspace():
+    # fp32 inputs (vector-ALU path): chunk-local states are kept for the y pass, in
+    # chunk_states when given, else in the workspace
+    d32 = bdssm.dims(1, 48, 64, 128, 1, bdssm.F32, bdssm.F32)
+    assert bdssm.prefix_scan_workspace(d32, 8192, 256, True, False) >= 32 * 48 * 128 * 64 * 4
+    assert bdssm.prefix_scan_workspace(d32, 8192, 256, True, True) < 1 << 20
+    assert bdssm.prefix_scan_workspace(d32, 0, 256, True, True) == 0
+    # bf16 inputs (matrix-core path): 48 (stream, head) pairs are too few to fill the GPU,
+    # so the tokens are split into segments whose entering states live in the workspace
     d = bdssm.dims(1, 48, 64, 128, 1, bdssm.BF16, bdssm.F32)
     need = bdssm.prefix_scan_workspace(d, 8192, 256, True, False)
-    assert need >= 32 * 48 * 128 * 64 * 4              # chunk states kept for the y pass
-    assert bdssm.prefix_scan_workspace(d, 8192, 256, True, True) < 1 << 20
+    assert need >= 2 * 48 * 128 * 64 * 4
+    assert bdssm.prefix_scan_workspace(d, 8192, 256, True, True) == need
     assert bdssm.prefix_scan_workspace(d, 0, 256, True, True) == 0
     base = 1 << 32
     s = seq(base, base + (1 << 28), base + (2 << 28), base + (3 << 28))
