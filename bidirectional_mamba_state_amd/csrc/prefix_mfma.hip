@@ -2,21 +2,27 @@
 //
 // The prefix operator of "Training Hybrid Block Diffusion Language Models with Partial
 // Bidirectionality", eq. (10): the forward Mamba-2 recurrence of eq. (1) over the prefix,
-// computed in the chunked matrix form. A workgroup owns one (stream, head) and a segment
-// of consecutive 64-token sub-chunks, and walks them in order with the N x P state held
-// in matrix-core accumulator registers (wavefront w owns d_state rows 32w .. 32w+31).
-// For one sub-chunk with cumulative log-decays c_t (relative to its start):
-//   state:   h <- exp(c_63) h + sum_s [exp(c_63 - c_s) dt_s B_s] x_s^T      (B~^T X on MFMA)
+// computed in the chunked matrix form. A workgroup owns HPW heads of one B/C group of one
+// stream and a segment of consecutive 64-token sub-chunks, and walks them in order with
+// the N x P states held in matrix-core accumulators: wavefront w owns columns 16w .. 16w+15
+// of every head's state, so the state is at once the operand of C . h and the target of
+// the state update, with no trip through LDS. For one sub-chunk with cumulative
+// log-decays c_t (relative to its start):
+//   state:   h <- exp(c_63) h + sum_s B_s [exp(c_63 - c_s) dt_s x_s]^T
 //   output:  y_t = exp(c_t) C_t . h_in + sum_{s<=t} exp(c_t - c_s) dt_s (C_t . B_s) x_s + D x_t
-// The output uses the state entering the sub-chunk, staged in LDS as bf16 hi + lo parts.
+// Outputs are computed transposed (y^T = h^T C^T + X^T M^T) so that a lane holds four
+// consecutive columns of one token. The C B^T scores are shared by the workgroup's heads.
+// B, C and x are staged row-major in LDS; operands whose contraction runs over tokens are
+// read with the gfx950 transposing LDS load (ds_read_b64_tr_b16).
 //
 // Two modes:
-//   STATE_ONLY  from h_init (or zero): only the state recurrence; writes the segment's end
-//               state and its total log-decay (used by the segment scan, or as h_out).
-//   FULL        from the state entering the segment: also y, the chunk states (every
-//               chunk/64 sub-chunks, the state after the chunk) and the end state.
-// Matrix-form products are exactly the recurrence up to rounding; the weighted B~ operand
-// is split into bf16 hi + lo parts so that the state keeps ~16 significant bits per term.
+//   STATE  from h_init (or zero): only the state recurrence; writes the segment's end
+//          state and its total log-decay (used by the segment scan, or as h_out).
+//   FULL   from the state entering the segment: also y, the chunk states (the state after
+//          every chunk of Q tokens, and after the last token) and, for the stream's last
+//          segment, the final state.
+// The fp32 states and the weighted x~ operand are split into bf16 hi + lo parts, so that
+// products against them keep ~16 significant bits; B, C and x are exact in bf16.
 #include <algorithm>
 
 #include "internal.h"
@@ -26,53 +32,73 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int v2i32 __attribute__((ext_vector_type(2)));
+typedef int v4i32 __attribute__((ext_vector_type(4)));
 
 constexpr int kN = 128, kP = 64, SC = 64;  // d_state, headdim, sub-chunk length
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int HS = kN + 8;   // transposed state rows [P][HS]
-constexpr int XS = SC + 8;   // transposed x rows [P][XS]
-constexpr int BS = SC + 8;   // transposed B rows [N][BS]
-constexpr int YS = kP + 8;   // output tile rows [SC][YS]
-constexpr int RS = kN + 8;   // B rows [SC][RS]
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ bf16x8 ld16(const void *p) { return *static_cast<const bf16x8 *>(p); }
 __device__ __forceinline__ float bf2f(__bf16 v) { return static_cast<float>(v); }
-__device__ __forceinline__ bf16x8 sel8(bool ok, bf16x8 v) { return ok ? v : bf16x8{}; }
 __device__ __forceinline__ uint4 sel4(bool ok, uint4 v) { return ok ? v : make_uint4(0, 0, 0, 0); }
+__device__ __forceinline__ bf16x8 cat(bf16x4 lo, bf16x4 hi)
+{
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Transposing LDS read: in each 16-lane group, lanes 4r .. 4r+3 address row r (four
+// consecutive elements each) and lane j receives column j of the four rows.
+__device__ __forceinline__ bf16x4 tr_read(const __bf16 *p)
+{
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
+    return __builtin_bit_cast(bf16x4, v);
+}
+
+// LDS tiles are row-major with padded rows. Row reads (pair_frag: 16 rows x the same 16
+// bytes) are conflict-free when the row stride is an odd multiple of 4 dwords; column
+// reads through the transposing load (tr_frag: 8 rows x 32 bytes) when it is an odd
+// multiple of 8. B and C rows are mostly read by rows, x rows only by columns.
+constexpr int BRS = kN + 8;   // B, C (and state copy) row stride: 68 dwords
+constexpr int XRS = kP + 16;  // x row stride: 40 dwords
+// the state-only pass reads B only by columns
+template <bool FULL> constexpr int b_stride() { return FULL ? BRS : kN + 16; }
+
+// Operand fragment with the contraction over rows of a tile: lane (r16, q) gets column
+// col0 + r16 of rows row0 + 4q + e (slots e = 0..3) and row0 + 16 + 4q + e (slots 4..7) --
+// the row order of two stacked 16 x 16 accumulator tiles.
+template <int STRIDE>
+__device__ __forceinline__ bf16x8 tr_frag(const __bf16 *T, int row0, int col0, int q, int r16)
+{
+    const __bf16 *p = T + (row0 + 4 * q + (r16 >> 2)) * STRIDE + col0 + 4 * (r16 & 3);
+    return cat(tr_read(p), tr_read(p + 16 * STRIDE));
+}
+
+// Operand fragment with the contraction along a row: columns 32m + 4q + e and
+// 32m + 16 + 4q + e of `row` (the same order as tr_frag).
+__device__ __forceinline__ bf16x8 pair_frag(const __bf16 *row, int m, int q)
+{
+    return cat(*reinterpret_cast<const bf16x4 *>(row + 32 * m + 4 * q),
+               *reinterpret_cast<const bf16x4 *>(row + 32 * m + 16 + 4 * q));
+}
+
+__device__ __forceinline__ void split8(const float (&f)[8], bf16x8 &hi, bf16x8 &lo)
+{
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        hi[e] = static_cast<__bf16>(f[e]);
+        lo[e] = static_cast<__bf16>(f[e] - bf2f(hi[e]));
+    }
+}
 
 enum { TAB_C, TAB_EF, TAB_LG, TAB_COL, TAB_W, NTAB };
 
-// 4 tokens x 8 bf16 (one uint4 per token) -> 8 columns x 4 tokens, written as uint2 rows
-__device__ __forceinline__ void put_transposed(__bf16 *dst, int stride, const uint4 (&v)[4])
-{
-    const uint32_t w[4][4] = {{v[0].x, v[0].y, v[0].z, v[0].w}, {v[1].x, v[1].y, v[1].z, v[1].w},
-                              {v[2].x, v[2].y, v[2].z, v[2].w}, {v[3].x, v[3].y, v[3].z, v[3].w}};
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t lo2 = __builtin_amdgcn_perm(w[1][c / 2], w[0][c / 2], sel);
-        const uint32_t hi2 = __builtin_amdgcn_perm(w[3][c / 2], w[2][c / 2], sel);
-        *reinterpret_cast<uint2 *>(dst + c * stride) = make_uint2(lo2, hi2);
-    }
-}
-
-// 2 tokens x 8 bf16 -> 8 columns x 2 tokens, written as uint32 rows
-__device__ __forceinline__ void put_transposed2(__bf16 *dst, int stride, uint4 v0, uint4 v1)
-{
-    const uint32_t w0[4] = {v0.x, v0.y, v0.z, v0.w}, w1[4] = {v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-        *reinterpret_cast<uint32_t *>(dst + c * stride) = __builtin_amdgcn_perm(w1[c / 2], w0[c / 2], sel);
-    }
-}
-
-struct PrefixArgs {
+struct ScanArgs {
     Shape s;
     int64_t len;         // tokens per stream
     int seg_sub;         // sub-chunks per segment
@@ -81,163 +107,157 @@ struct PrefixArgs {
     int nch;             // output chunks per stream
     Seq in;
     const float *A, *D;
-    const float *h_in;   // state entering each segment: [b][nseg][H][N][P] (FULL), or the
-                         // stream's initial state [b][H][N][P] (STATE_ONLY, nseg == 1); NULL = 0
-    float *h_end;        // end state of each segment: [b][nseg][H][N][P]
-    float *tot;          // total log-decay (natural log) of each segment [b][nseg][H], or NULL
+    const float *h_in;   // state entering each segment [b][nseg][H][N][P]; NULL = zero
+    float *h_end;        // STATE: end state of each segment [b][nseg][H][N][P]
+    float *h_last;       // FULL: final state [b][H][N][P] (written by the last segment), or NULL
+    float *tot;          // STATE: natural-log decay of each segment [b][nseg][H], or NULL
     void *y;             // FULL: [b][len][H][P] in s.y_dt, or NULL
     float *chunk_states; // FULL: [b][nch][H][N][P], or NULL
 };
 
-// Wavefronts: the state-only pass uses 4 (each owns 32 d_state rows of the state); the
-// full pass uses 8: for the outputs, two per 16-row block, each owning 32 columns; for the
-// state, each owns 16 d_state rows.
-template <bool FULL>
-struct PGeo {
-    static constexpr int WAVES = FULL ? 8 : 4;
-    static constexpr int THREADS = 64 * WAVES;
-    static constexpr int NBW = kN / 16 / WAVES;  // 16-row d_state blocks per wavefront
+template <bool FULL, int HPW>
+struct Lds {
+    __bf16 B[SC * b_stride<FULL>()];
+    __bf16 C[FULL ? SC * BRS : 8];
+    __bf16 X[HPW][SC * XRS];
+    // FULL: each wavefront's state columns as bf16 hi and lo rows [p][n] (private to it)
+    __bf16 hT[FULL ? 4 * HPW : 1][FULL ? 2 : 1][FULL ? 16 * BRS : 8];
+    float tab[HPW][NTAB][SC];
+    float tot[HPW];
 };
 
-template <bool FULL, typename Ty>
-__global__ __launch_bounds__(PGeo<FULL>::THREADS, 2) void k_prefix(PrefixArgs a)
+
+template <bool FULL, bool WITHY, int HPW, typename Ty>
+__global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
 {
-    constexpr int THREADS = PGeo<FULL>::THREADS, NBW = PGeo<FULL>::NBW;
-    __shared__ __attribute__((aligned(16))) __bf16 XT[kP * XS];
-    __shared__ __attribute__((aligned(16))) __bf16 BT[kN * BS];
-    __shared__ __attribute__((aligned(16))) __bf16 Brow[FULL ? SC * RS : 8];  // B rows (score tiles)
-    __shared__ __attribute__((aligned(16))) __bf16 hT_hi[FULL ? kP * HS : 8];
-    __shared__ __attribute__((aligned(16))) __bf16 hT_lo[FULL ? kP * HS : 8];
-    __shared__ __attribute__((aligned(16))) __bf16 ytile[FULL && sizeof(Ty) == 2 ? SC * YS : 8];
-    __shared__ __attribute__((aligned(16))) float tab[NTAB][SC];
-    __shared__ float sub_tot;  // natural-log decay of the sub-chunk
+    __shared__ __attribute__((aligned(16))) Lds<FULL, HPW> L;
 
     // workgroups of one segment (all heads of a stream) go to the same XCD
     const int nwg = gridDim.x;
     int lid = blockIdx.x;
     if ((nwg & 7) == 0)
         lid = (lid & 7) * (nwg >> 3) + (lid >> 3);
-    const int H = a.s.H, G = a.s.G;
-    const int h = lid % H;
-    const int sg = (lid / H) % a.nseg;
-    const int b = lid / (H * a.nseg);
-    const int g = h / (H / G);
+    const int H = a.s.H, G = a.s.G, NGRP = H / HPW;
+    const int h0 = (lid % NGRP) * HPW;
+    const int sg = (lid / NGRP) % a.nseg;
+    const int b = lid / (NGRP * a.nseg);
+    const int g = h0 / (H / G);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 4, r16 = lane & 15;
+    const int p0 = 16 * wave;  // this wavefront's state columns
 
     const int64_t len = a.len;
     const int64_t seg_t0 = static_cast<int64_t>(sg) * a.seg_sub * SC;
     const int nsub = static_cast<int>(min<int64_t>(a.seg_sub, (len - seg_t0 + SC - 1) / SC));
+    const int64_t nsub_all = (len + SC - 1) / SC;
     const int rowBC = G * kN, rowX = H * kP;
     const int64_t tok0 = static_cast<int64_t>(b) * len;
     const __bf16 *Bg = static_cast<const __bf16 *>(a.in.B) + tok0 * rowBC + g * kN;
     const __bf16 *Cg = static_cast<const __bf16 *>(a.in.C) + tok0 * rowBC + g * kN;
-    const __bf16 *xg = static_cast<const __bf16 *>(a.in.x) + tok0 * rowX + h * kP;
-    const __bf16 *dtg = static_cast<const __bf16 *>(a.in.dt) + tok0 * H + h;
-    const float Ah = a.A[h];
-    const float Dh = a.D[h];
+    const __bf16 *xg = static_cast<const __bf16 *>(a.in.x) + tok0 * rowX + h0 * kP;
+    const __bf16 *dtg = static_cast<const __bf16 *>(a.in.dt) + tok0 * H + h0;
     const int64_t NP = static_cast<int64_t>(kN) * kP;
+    const int th = min(wave, HPW - 1);  // head whose dt this wavefront stages
+    const float Ath = a.A[h0 + th];
+    float Dh[HPW];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh)
+        Dh[hh] = a.D[h0 + hh];
 
-    // ---- state registers: wavefront w holds rows n = 16 (NBW w + i) + 4q + j, columns 16pb + r16
-    f32x4 hs[NBW][4];
-    {
-        const float *hin = nullptr;
-        if (FULL)
-            hin = a.h_in ? a.h_in + ((static_cast<int64_t>(b) * a.nseg + sg) * H + h) * NP : nullptr;
-        else
-            hin = a.h_in ? a.h_in + (static_cast<int64_t>(b) * H + h) * NP : nullptr;
+    // ---- states: hs[hh][i] holds h[16 i + 4 q + j][p0 + r16] of head h0 + hh
+    f32x4 hs[HPW][8];
 #pragma unroll
-        for (int i = 0; i < NBW; ++i)
+    for (int hh = 0; hh < HPW; ++hh) {
 #pragma unroll
-            for (int pb = 0; pb < 4; ++pb)
+        for (int i = 0; i < 8; ++i)
+            hs[hh][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (a.h_in) {
+            const float *hin = a.h_in + ((static_cast<int64_t>(b) * a.nseg + sg) * H + h0 + hh) * NP;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    hs[i][pb][j] = hin ? hin[(16 * (NBW * wave + i) + 4 * q + j) * kP + 16 * pb + r16] : 0.f;
+                    hs[hh][i][j] = hin[(16 * i + 4 * q + j) * kP + p0 + r16];
+        }
     }
-    auto publish_state = [&]() {  // hs -> transposed bf16 hi/lo in LDS (FULL only)
+    auto publish_state = [&]() {  // hs -> this wavefront's hi/lo rows in LDS (FULL only)
+        if constexpr (FULL && WITHY) {
 #pragma unroll
-        for (int i = 0; i < NBW; ++i)
+            for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
-            for (int pb = 0; pb < 4; ++pb) {
-                bf16x4 hi, lo;
+                for (int i = 0; i < 8; ++i) {
+                    bf16x4 hi, lo;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float f = hs[i][pb][j];
-                    hi[j] = static_cast<__bf16>(f);
-                    lo[j] = static_cast<__bf16>(f - bf2f(hi[j]));
+                    for (int j = 0; j < 4; ++j) {
+                        hi[j] = static_cast<__bf16>(hs[hh][i][j]);
+                        lo[j] = static_cast<__bf16>(hs[hh][i][j] - bf2f(hi[j]));
+                    }
+                    *reinterpret_cast<bf16x4 *>(&L.hT[wave * HPW + hh][0][r16 * BRS + 16 * i + 4 * q]) = hi;
+                    *reinterpret_cast<bf16x4 *>(&L.hT[wave * HPW + hh][1][r16 * BRS + 16 * i + 4 * q]) = lo;
                 }
-                const int off = (16 * pb + r16) * HS + 16 * (NBW * wave + i) + 4 * q;
-                *reinterpret_cast<bf16x4 *>(&hT_hi[off]) = hi;
-                *reinterpret_cast<bf16x4 *>(&hT_lo[off]) = lo;
-            }
+        }
     };
-    if (FULL)
-        publish_state();
+    auto store_state = [&](float *base) {  // base: [HPW heads][N][P] with head stride NP
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    base[hh * NP + (16 * i + 4 * q + j) * kP + p0 + r16] = hs[hh][i][j];
+    };
 
-    // ---- staging registers, DEPTH sub-chunks ahead (state-only: 2, full: 1)
-    constexpr int DEPTH = FULL ? 1 : 2;
-    constexpr int XI = (SC / 2) * (kP / 8), BI = (SC / 2) * (kN / 8);  // items: 2 tokens x 8
-    constexpr int XPT = (XI + THREADS - 1) / THREADS, BPT = (BI + THREADS - 1) / THREADS;
-    struct StageRegs {
-        uint4 x[XPT][2];  // 2 tokens x 8 columns of x
-        uint4 b[BPT][2];  // 2 tokens x 8 d_state of B
-        __bf16 dt;        // dt of token `lane` (wavefront 0 uses it)
-    };
-    StageRegs ring[DEPTH];
-    auto load_sub = [&](StageRegs &r, int k) {
+    // ---- staging registers, one sub-chunk ahead
+    constexpr int BPT = SC * kN / 8 / 256;        // uint4 per thread for B (and C): 4
+    constexpr int XPT = SC * kP * HPW / 8 / 256;  // uint4 per thread for x: 2 HPW
+    struct Stage {
+        uint4 bq[BPT];
+        uint4 cq[FULL ? BPT : 1];
+        uint4 xq[XPT];
+        __bf16 dt;
+    } st;
+    // rows past the end are clamped here and zeroed at store time
+    auto load_c = [&](int k) {
         const int64_t t0 = seg_t0 + static_cast<int64_t>(k) * SC;
         const int last = static_cast<int>(min<int64_t>(SC, len - t0)) - 1;
-        const __bf16 *xk = xg + t0 * rowX, *bk = Bg + t0 * rowBC;  // uniform bases
-        // rows past the end are clamped here and zeroed at store time
-#pragma unroll
-        for (int u = 0; u < XPT; ++u) {
-            const int it = tid + u * THREADS;
-            if (XI % THREADS == 0 || it < XI) {
-                const int p8 = it % 8, t2 = (it / 8) * 2;
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-                    r.x[u][i] = *reinterpret_cast<const uint4 *>(xk + min(t2 + i, last) * rowX + p8 * 8);
-            }
-        }
 #pragma unroll
         for (int u = 0; u < BPT; ++u) {
-            const int it = tid + u * THREADS;
-            if (BI % THREADS == 0 || it < BI) {
-                const int n8 = it % 16, t2 = (it / 16) * 2;
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-                    r.b[u][i] = *reinterpret_cast<const uint4 *>(bk + min(t2 + i, last) * rowBC + n8 * 8);
-            }
+            const int it = tid + 256 * u, row = min(it >> 4, last), c16 = it & 15;
+            st.cq[u] = *reinterpret_cast<const uint4 *>(Cg + (t0 + row) * rowBC + c16 * 8);
         }
-        r.dt = dtg[t0 * H + min(lane, last) * H];
     };
-    auto store_sub = [&](const StageRegs &r, int k) {
+    auto load_stage = [&](int k) {  // all but C
+        const int64_t t0 = seg_t0 + static_cast<int64_t>(k) * SC;
+        const int last = static_cast<int>(min<int64_t>(SC, len - t0)) - 1;
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) {
+            const int it = tid + 256 * u, row = min(it >> 4, last), c16 = it & 15;
+            st.bq[u] = *reinterpret_cast<const uint4 *>(Bg + (t0 + row) * rowBC + c16 * 8);
+        }
+#pragma unroll
+        for (int u = 0; u < XPT; ++u) {
+            const int it = tid + 256 * u, row = min(it / (8 * HPW), last), c = it % (8 * HPW);
+            st.xq[u] = *reinterpret_cast<const uint4 *>(xg + (t0 + row) * rowX + c * 8);
+        }
+        st.dt = dtg[(t0 + min(lane, last)) * H + th];
+    };
+    auto store_stage = [&](int k) {
         const int64_t t0 = seg_t0 + static_cast<int64_t>(k) * SC;
         const int nvalid = static_cast<int>(min<int64_t>(SC, len - t0));
 #pragma unroll
-        for (int u = 0; u < XPT; ++u) {
-            const int it = tid + u * THREADS;
-            if (XI % THREADS == 0 || it < XI) {
-                const int p8 = it % 8, t2 = (it / 8) * 2;
-                put_transposed2(&XT[p8 * 8 * XS + t2], XS, sel4(t2 < nvalid, r.x[u][0]), sel4(t2 + 1 < nvalid, r.x[u][1]));
-            }
+        for (int u = 0; u < BPT; ++u) {
+            const int it = tid + 256 * u, row = it >> 4, c16 = it & 15;
+            *reinterpret_cast<uint4 *>(&L.B[row * b_stride<FULL>() + c16 * 8]) = sel4(row < nvalid, st.bq[u]);
+            if (FULL)
+                *reinterpret_cast<uint4 *>(&L.C[row * BRS + c16 * 8]) = sel4(row < nvalid, st.cq[u]);
         }
 #pragma unroll
-        for (int u = 0; u < BPT; ++u) {
-            const int it = tid + u * THREADS;
-            if (BI % THREADS == 0 || it < BI) {
-                const int n8 = it % 16, t2 = (it / 16) * 2;
-                const uint4 v0 = sel4(t2 < nvalid, r.b[u][0]), v1 = sel4(t2 + 1 < nvalid, r.b[u][1]);
-                put_transposed2(&BT[n8 * 8 * BS + t2], BS, v0, v1);
-                if (FULL) {
-                    *reinterpret_cast<uint4 *>(&Brow[t2 * RS + n8 * 8]) = v0;
-                    *reinterpret_cast<uint4 *>(&Brow[(t2 + 1) * RS + n8 * 8]) = v1;
-                }
-            }
+        for (int u = 0; u < XPT; ++u) {
+            const int it = tid + 256 * u, row = it / (8 * HPW), c = it % (8 * HPW);
+            *reinterpret_cast<uint4 *>(&L.X[c >> 3][row * XRS + (c & 7) * 8]) = sel4(row < nvalid, st.xq[u]);
         }
-        if (wave == 0) {  // cumulative log2-decays of the sub-chunk, one token per lane
-            const float d = lane < nvalid ? bf2f(r.dt) : 0.f;
-            const float av = d * Ah;
-            float inc = av;
+        if (wave < HPW) {  // cumulative log2-decays of head h0 + wave, one token per lane
+            const float d = lane < nvalid ? bf2f(st.dt) : 0.f;
+            float inc = d * Ath;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float up = __shfl_up(inc, off, 64);
@@ -246,212 +266,218 @@ __global__ __launch_bounds__(PGeo<FULL>::THREADS, 2) void k_prefix(PrefixArgs a)
             }
             const float c = inc * kLog2e;
             const float clast = __shfl(c, 63, 64);
-            const float ref = __shfl(c, lane | 31, 64);  // end of this lane's 32-token pair
-            tab[TAB_C][lane] = c;
-            tab[TAB_EF][lane] = __builtin_amdgcn_exp2f(c);
-            tab[TAB_LG][lane] = __builtin_amdgcn_logf(d) - c;
-            tab[TAB_COL][lane] = __builtin_amdgcn_exp2f(ref - c) * d;
-            tab[TAB_W][lane] = __builtin_amdgcn_exp2f(clast - c) * d;
+            const float ref = __shfl(c, lane | 31, 64);  // end of this token's 32-token pair
+            float(*tb)[SC] = L.tab[wave];
+            tb[TAB_C][lane] = c;
+            tb[TAB_EF][lane] = __builtin_amdgcn_exp2f(c);
+            tb[TAB_LG][lane] = __builtin_amdgcn_logf(d) - c;
+            tb[TAB_COL][lane] = __builtin_amdgcn_exp2f(ref - c) * d;
+            tb[TAB_W][lane] = __builtin_amdgcn_exp2f(clast - c) * d;
             if (lane == 63)
-                sub_tot = inc;
+                L.tot[wave] = inc;
         }
     };
 
-    float seg_tot = 0.f;
-    Ty *yg = FULL ? static_cast<Ty *>(a.y) : nullptr;
+    float seg_tot[HPW];
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d)
-        if (d < nsub)
-            load_sub(ring[d], d);
-    // one sub-chunk; `cur` holds its staged inputs and receives those DEPTH sub-chunks ahead
-    auto iter = [&](StageRegs &cur, int k) {
+    for (int hh = 0; hh < HPW; ++hh)
+        seg_tot[hh] = 0.f;
+    auto emit_chunk_state = [&](int k) {  // state after sub-chunk k, at chunk ends and the end
+        const int64_t gsub = seg_t0 / SC + k;  // sub-chunk index within the stream
+        if ((gsub + 1) % a.chunk_sub == 0 || gsub == nsub_all - 1) {
+            const int64_t c = gsub / a.chunk_sub;
+            store_state(a.chunk_states + ((static_cast<int64_t>(b) * a.nch + c) * H + h0) * NP);
+        }
+    };
+    // The loads for sub-chunk k+1 are issued once the chunk-state stores of sub-chunk k-1
+    // are out, and only the (branch-free) y stores of sub-chunk k follow them before their
+    // use, so that waiting for them never waits for a store issued after them.
+    load_stage(0);
+    if (FULL)
+        load_c(0);
+    publish_state();
+    store_stage(0);
+    for (int k = 0; k < nsub; ++k) {
         const int64_t t0 = seg_t0 + static_cast<int64_t>(k) * SC;
         const int nvalid = static_cast<int>(min<int64_t>(SC, len - t0));
-        // C fragments of this wavefront's 16 rows, issued before the next prefetch so that
-        // waiting for them does not wait for it (masked at use)
-        bf16x8 cfw[4];
-        if (FULL && yg) {
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                cfw[kk] = ld16(Cg + (t0 + min(16 * (wave >> 1) + r16, nvalid - 1)) * rowBC + 32 * kk + 8 * q);
-        }
-        store_sub(cur, k);
-        __syncthreads();  // (A) sub-chunk k staged; the state entering it is in hT
-        if (k + DEPTH < nsub)
-            load_sub(cur, k + DEPTH);  // in flight during the next DEPTH sub-chunks
+        __syncthreads();  // (A) sub-chunk k staged
+        if (FULL && a.chunk_states && k > 0)
+            emit_chunk_state(k - 1);
+        load_stage(min(k + 1, nsub - 1));  // in flight during sub-chunk k
+        __builtin_amdgcn_sched_barrier(0);  // keep the loads here, ahead of the compute
 
-        if (FULL && yg) {
-            // ---- outputs of row block tb = wave / 2, columns 32 (wave & 1) .. +31
-            const int tb = wave >> 1, t = tb * 16 + r16, md = tb >> 1, pb0 = 2 * (wave & 1);
+        // x~ fragments (contraction over tokens, columns p0 .. p0+15), per head and 32-token pair
+        bf16x8 xf[HPW][2];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                cfw[kk] = sel8(t < nvalid, cfw[kk]);
-            f32x4 S[4];  // S[t][s = 16 sb + 4q + j] for sb <= tb
+        for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
-            for (int sb = 0; sb < 4; ++sb) {
-                S[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (sb <= tb) {
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk)
-                        S[sb] = mfma(ld16(&Brow[(16 * sb + r16) * RS + 32 * kk + 8 * q]), cfw[kk], S[sb]);
-                }
-            }
-            f32x4 acc[2];
-#pragma unroll
-            for (int pb = 0; pb < 2; ++pb)
-                acc[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-                for (int pb = 0; pb < 2; ++pb) {
-                    const int pc = 16 * (pb0 + pb) + r16;
-                    acc[pb] = mfma(cfw[kk], ld16(&hT_hi[pc * HS + 32 * kk + 8 * q]), acc[pb]);
-                    acc[pb] = mfma(cfw[kk], ld16(&hT_lo[pc * HS + 32 * kk + 8 * q]), acc[pb]);
-                }
-            {
-                const float4 e4 = *reinterpret_cast<const float4 *>(&tab[TAB_EF][16 * tb + 4 * q]);
-#pragma unroll
-                for (int pb = 0; pb < 2; ++pb) {
-                    acc[pb][0] *= e4.x;
-                    acc[pb][1] *= e4.y;
-                    acc[pb][2] *= e4.z;
-                    acc[pb][3] *= e4.w;
-                }
-            }
-            const float ct = tab[TAB_C][t];  // c_t in log2 units
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                if (m > md)
-                    break;
-                bf16x8 af;
-                if (m < md) {  // pair wholly below the row block: factored decay
-                    const float rowf = __builtin_amdgcn_exp2f(ct - tab[TAB_C][32 * m + 31]);
-                    const float4 c0 = *reinterpret_cast<const float4 *>(&tab[TAB_COL][32 * m + 4 * q]);
-                    const float4 c1 = *reinterpret_cast<const float4 *>(&tab[TAB_COL][32 * m + 16 + 4 * q]);
-                    const float cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        af[j] = static_cast<__bf16>((j < 4 ? S[2 * m][j] : S[2 * m + 1][j & 3]) * cw[j] * rowf);
-                } else {  // the pair holding the row block: per element, masked to s <= t
-                    const float4 l0 = *reinterpret_cast<const float4 *>(&tab[TAB_LG][32 * m + 4 * q]);
-                    const float4 l1 = *reinterpret_cast<const float4 *>(&tab[TAB_LG][32 * m + 16 + 4 * q]);
-                    const float lg[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const int s = 32 * m + (j < 4 ? 0 : 16) + 4 * q + (j & 3);
-                        const float sv = j < 4 ? S[2 * m][j] : S[2 * m + 1][j & 3];
-                        af[j] = static_cast<__bf16>(s <= t ? sv * __builtin_amdgcn_exp2f(ct + lg[j]) : 0.f);
-                    }
-                }
-#pragma unroll
-                for (int pb = 0; pb < 2; ++pb) {
-                    const __bf16 *xp = &XT[(16 * (pb0 + pb) + r16) * XS + 32 * m + 4 * q];
-                    const bf16x4 lo4 = *reinterpret_cast<const bf16x4 *>(xp);
-                    const bf16x4 hi4 = *reinterpret_cast<const bf16x4 *>(xp + 16);
-                    acc[pb] = mfma(af, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7), acc[pb]);
-                }
-            }
-            Ty *yk = yg + (tok0 + t0) * rowX + h * kP;
-            if constexpr (sizeof(Ty) == 2) {
-#pragma unroll
-                for (int pb = 0; pb < 2; ++pb)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int tr = 16 * tb + 4 * q + j, pc = 16 * (pb0 + pb) + r16;
-                        ytile[tr * YS + pc] = static_cast<__bf16>(fmaf(Dh, bf2f(XT[pc * XS + tr]), acc[pb][j]));
-                    }
-                // the wavefront writes back its own 16 rows x 32 columns as 16-byte pieces
-                {
-                    const int row = 16 * tb + lane / 4, col = 16 * pb0 + (lane % 4) * 8;
-                    if (row < nvalid)
-                        *reinterpret_cast<uint4 *>(yk + row * rowX + col) =
-                            *reinterpret_cast<const uint4 *>(&ytile[row * YS + col]);
-                }
-            } else {
-#pragma unroll
-                for (int pb = 0; pb < 2; ++pb)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int tr = 16 * tb + 4 * q + j, pc = 16 * (pb0 + pb) + r16;
-                        if (tr < nvalid)
-                            yk[tr * rowX + pc] = fmaf(Dh, bf2f(XT[pc * XS + tr]), acc[pb][j]);
-                    }
-            }
-        }
+            for (int m = 0; m < 2; ++m)
+                xf[hh][m] = tr_frag<XRS>(L.X[hh], 32 * m, p0, q, r16);
 
-        // ---- state: h <- exp(c_last) h + (w o B)^T X, w_s = exp(c_last - c_s) dt_s
-        {
-            const float alpha = __expf(sub_tot);
+        if constexpr (FULL && WITHY) {
+            // y rows of this sub-chunk; rows past the end fall outside the buffer range and
+            // their stores are dropped by the hardware
+            const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
+                static_cast<Ty *>(a.y) + (tok0 + t0) * rowX, 0, nvalid * rowX * static_cast<int>(sizeof(Ty)),
+                0x00020000);
 #pragma unroll
-            for (int i = 0; i < NBW; ++i)
+            for (int hh = 0; hh < HPW; ++hh) {
+                const float(*tbl)[SC] = L.tab[hh];
+                // state entering the sub-chunk as y^T operands (rows p, contraction over n in
+                // the order of two stacked accumulator tiles), from this wavefront's LDS copy
+                const __bf16 *hTh = &L.hT[wave * HPW + hh][0][r16 * BRS];
+                const __bf16 *hTl = &L.hT[wave * HPW + hh][1][r16 * BRS];
+                // Two halves of row blocks (0-1, 2-3). Per half, scores S[tb][sb] = B_s . C_t
+                // (s in block sb <= tb, t in block tb) and y^T[p][t] = sum_n h[n][p] C[t][n]:
+                // each C fragment is read once, and the products of one 32-wide slice of n
+                // are independent.
 #pragma unroll
-                for (int pb = 0; pb < 4; ++pb)
-                    hs[i][pb] *= alpha;
+                for (int half = 0; half < 2; ++half) {
+                f32x4 S[2][4], acc[2];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const float4 w0 = *reinterpret_cast<const float4 *>(&tab[TAB_W][32 * ks + 8 * q]);
-                const float4 w1 = *reinterpret_cast<const float4 *>(&tab[TAB_W][32 * ks + 8 * q + 4]);
-                const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-                bf16x8 bx[4];
+                for (int u = 0; u < 2; ++u) {
+                    acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int pb = 0; pb < 4; ++pb)
-                    bx[pb] = ld16(&XT[(16 * pb + r16) * XS + 32 * ks + 8 * q]);
+                    for (int sb = 0; sb < 4; ++sb)
+                        S[u][sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
 #pragma unroll
-                for (int i = 0; i < NBW; ++i) {
-                    const bf16x8 braw = ld16(&BT[(16 * (NBW * wave + i) + r16) * BS + 32 * ks + 8 * q]);
-                    bf16x8 ahi, alo;
+                for (int m = 0; m < 4; ++m) {
+                    const bf16x8 hfh = pair_frag(hTh, m, q), hfl = pair_frag(hTl, m, q);
+                    bf16x8 bf[4];
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const float f = bf2f(braw[j]) * wv[j];
-                        ahi[j] = static_cast<__bf16>(f);
-                        alo[j] = static_cast<__bf16>(f - bf2f(ahi[j]));
-                    }
+                    for (int sb = 0; sb < 2 * half + 2; ++sb)
+                        bf[sb] = pair_frag(&L.B[(16 * sb + r16) * BRS], m, q);
 #pragma unroll
-                    for (int pb = 0; pb < 4; ++pb) {
-                        hs[i][pb] = mfma(ahi, bx[pb], hs[i][pb]);
-                        hs[i][pb] = mfma(alo, bx[pb], hs[i][pb]);
+                    for (int u = 0; u < 2; ++u) {
+                        const int tb = 2 * half + u;
+                        const bf16x8 cf = pair_frag(&L.C[(16 * tb + r16) * BRS], m, q);
+#pragma unroll
+                        for (int sb = 0; sb <= tb; ++sb)
+                            S[u][sb] = mfma(bf[sb], cf, S[u][sb]);
+                        acc[u] = mfma(hfh, cf, acc[u]);
+                        acc[u] = mfma(hfl, cf, acc[u]);
                     }
                 }
-            }
-        }
-        seg_tot += sub_tot;
-        __syncthreads();  // (B) every read of XT, BT, hT and the tables for sub-chunk k is done
-        if (FULL) {
-            publish_state();
-            const int64_t gsub = seg_t0 / SC + k;  // sub-chunk index within the stream
-            if (a.chunk_states && ((gsub + 1) % a.chunk_sub == 0 || (k == nsub - 1 && sg == a.nseg - 1))) {
-                const int64_t c = gsub / a.chunk_sub;
-                float *dst = a.chunk_states + ((static_cast<int64_t>(b) * a.nch + c) * H + h) * NP;
 #pragma unroll
-                for (int i = 0; i < NBW; ++i)
+                for (int u = 0; u < 2; ++u) {
+                    const int tb = 2 * half + u;
+                    const int t = 16 * tb + r16, md = tb >> 1;
+                    const float ct = tbl[TAB_C][t];
+                    acc[u] *= tbl[TAB_EF][t];
+                    // ---- + sum_{s<=t} M[t][s] x_s, per 32-token pair
 #pragma unroll
-                    for (int pb = 0; pb < 4; ++pb)
+                    for (int m = 0; m <= md; ++m) {
+                        float mv[8];
+                        if (m < md) {  // pair wholly below the row block: factored decay
+                            const float rowf = __builtin_amdgcn_exp2f(ct - tbl[TAB_C][32 * m + 31]);
+                            const float4 c0 = *reinterpret_cast<const float4 *>(&tbl[TAB_COL][32 * m + 4 * q]);
+                            const float4 c1 = *reinterpret_cast<const float4 *>(&tbl[TAB_COL][32 * m + 16 + 4 * q]);
+                            const float cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+                            for (int e = 0; e < 8; ++e)
+                                mv[e] = (e < 4 ? S[u][2 * m][e] : S[u][2 * m + 1][e & 3]) * cw[e] * rowf;
+                        } else {  // the pair holding the row block: per element, masked to s <= t
+                            const float4 l0 = *reinterpret_cast<const float4 *>(&tbl[TAB_LG][32 * m + 4 * q]);
+                            const float4 l1 = *reinterpret_cast<const float4 *>(&tbl[TAB_LG][32 * m + 16 + 4 * q]);
+                            const float lg[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) {
+                                const int s = 32 * m + (e < 4 ? 0 : 16) + 4 * q + (e & 3);
+                                const float sv = e < 4 ? S[u][2 * m][e] : S[u][2 * m + 1][e & 3];
+                                mv[e] = s <= t ? sv * __builtin_amdgcn_exp2f(ct + lg[e]) : 0.f;
+                            }
+                        }
+                        bf16x8 mf;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            mf[e] = static_cast<__bf16>(mv[e]);
+                        acc[u] = mfma(xf[hh][m], mf, acc[u]);
+                    }
+                    // ---- + D x_t; lane holds y[t][p0 + 4q .. p0 + 4q + 3]
+                    {
+                        const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(&L.X[hh][t * XRS + p0 + 4 * q]);
+                        float o[4];
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
-                            dst[(16 * (NBW * wave + i) + 4 * q + j) * kP + 16 * pb + r16] = hs[i][pb][j];
+                            o[j] = fmaf(Dh[hh], bf2f(xv[j]), acc[u][j]);
+                        const int off = ((t * H + h0 + hh) * kP + p0 + 4 * q) * static_cast<int>(sizeof(Ty));
+                        if constexpr (sizeof(Ty) == 2) {
+                            bf16x4 ov;
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                ov[j] = static_cast<__bf16>(o[j]);
+                            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2i32, ov), yr, off, 0, 0);
+                        } else {
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                v4i32{__float_as_int(o[0]), __float_as_int(o[1]), __float_as_int(o[2]), __float_as_int(o[3])},
+                                yr, off, 0, 0);
+                        }
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);  // one half at a time
+                }
             }
         }
-    };
-    // unrolled by the ring depth so that ring slots are compile-time registers
-    for (int k = 0; k < nsub; k += DEPTH) {
-        iter(ring[0], k);
-        if (DEPTH > 1 && k + 1 < nsub)
-            iter(ring[DEPTH - 1], k + 1);
-    }
 
-    // ---- end state of the segment
-    if (a.h_end) {
-        float *dst = a.h_end + ((static_cast<int64_t>(b) * a.nseg + sg) * H + h) * NP;
+        if (FULL) {  // C rows of sub-chunk k+1 (shared by all heads, mostly L2 hits)
+            load_c(min(k + 1, nsub - 1));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // ---- state: h <- exp(c_63) h + B^T (w o x), w_s = exp(c_63 - c_s) dt_s
 #pragma unroll
-        for (int i = 0; i < NBW; ++i)
+        for (int hh = 0; hh < HPW; ++hh) {
+            const float tot = L.tot[hh];
+            seg_tot[hh] += tot;
+            const float alpha = __expf(tot);
 #pragma unroll
-            for (int pb = 0; pb < 4; ++pb)
+            for (int i = 0; i < 8; ++i)
+                hs[hh][i] *= alpha;
+        }
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    dst[(16 * (NBW * wave + i) + 4 * q + j) * kP + 16 * pb + r16] = hs[i][pb][j];
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 bt[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                bt[i] = tr_frag<b_stride<FULL>()>(L.B, 32 * ks, 16 * i, q, r16);
+#pragma unroll
+            for (int hh = 0; hh < HPW; ++hh) {
+                const float4 w0 = *reinterpret_cast<const float4 *>(&L.tab[hh][TAB_W][32 * ks + 4 * q]);
+                const float4 w1 = *reinterpret_cast<const float4 *>(&L.tab[hh][TAB_W][32 * ks + 16 + 4 * q]);
+                const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+                float xw[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    xw[e] = bf2f(xf[hh][ks][e]) * wv[e];
+                bf16x8 xhi, xlo;
+                split8(xw, xhi, xlo);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    hs[hh][i] = mfma(bt[i], xhi, hs[hh][i]);
+                    hs[hh][i] = mfma(bt[i], xlo, hs[hh][i]);
+                }
+            }
+        }
+        publish_state();  // private to the wavefront: no barrier needed before its next use
+        __syncthreads();  // (B) every LDS read for sub-chunk k is done
+        // unconditional, so that no path reaches the loop head with loads in flight (after
+        // the last sub-chunk it stages data nobody reads)
+        store_stage(k + 1);
     }
-    if (a.tot && tid == 0)
-        a.tot[(static_cast<int64_t>(b) * a.nseg + sg) * H + h] = seg_tot;
+    if (FULL && a.chunk_states)
+        emit_chunk_state(nsub - 1);
+
+    // ---- end of the segment
+    if (!FULL && a.h_end)
+        store_state(a.h_end + ((static_cast<int64_t>(b) * a.nseg + sg) * H + h0) * NP);
+    if (FULL && a.h_last && sg == a.nseg - 1)
+        store_state(a.h_last + (static_cast<int64_t>(b) * H + h0) * NP);
+    if (!FULL && a.tot && tid == 0) {
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh)
+            a.tot[(static_cast<int64_t>(b) * a.nseg + sg) * H + h0 + hh] = seg_tot[hh];
+    }
 }
 
 // Segment scan, one thread per state element: the end states of segments started from
@@ -475,12 +501,42 @@ __global__ __launch_bounds__(256) void k_seg_scan(float *buf, const float *tot, 
         h_out[(static_cast<int64_t>(b) * H + h) * NP + e] = v;
 }
 
-template <bool FULL, typename Ty>
-hipError_t launch_prefix(const PrefixArgs &a, hipStream_t st)
+template <bool FULL, int HPW, typename Ty>
+hipError_t launch_scan(const ScanArgs &a, hipStream_t st)
 {
-    const int nwg = a.s.b * a.nseg * a.s.H;
-    k_prefix<FULL, Ty><<<dim3(nwg), dim3(PGeo<FULL>::THREADS), 0, st>>>(a);
+    const int nwg = a.s.b * a.nseg * (a.s.H / HPW);
+    if constexpr (FULL) {
+        if (a.y) {
+            k_scan<true, true, HPW, Ty><<<dim3(nwg), dim3(256), 0, st>>>(a);
+            return hipGetLastError();
+        }
+    }
+    k_scan<FULL, false, HPW, Ty><<<dim3(nwg), dim3(256), 0, st>>>(a);
     return hipGetLastError();
+}
+
+template <bool FULL, typename Ty>
+hipError_t launch_scan_hpw(const ScanArgs &a, int hpw, hipStream_t st)
+{
+    if constexpr (!FULL) {
+        if (hpw == 2)
+            return launch_scan<FULL, 2, Ty>(a, st);
+    }
+    return launch_scan<FULL, 1, Ty>(a, st);
+}
+
+// Heads per workgroup: as many as the pass allows (shared B/C staging and scores), but
+// no fewer workgroups than CUs when the segment count is fixed at one.
+int pick_hpw(const Shape &s, bool full, bool single_segment)
+{
+    const int hpg = s.H / s.G;
+    int hpw = full ? 1 : (static_cast<int64_t>(s.b) * s.H >= 2048 ? 2 : 1);
+    while (hpw > 1 && hpg % hpw != 0)
+        hpw /= 2;
+    if (single_segment)
+        while (hpw > 1 && static_cast<int64_t>(s.b) * (s.H / hpw) < 256)
+            hpw /= 2;
+    return hpw;
 }
 
 }  // namespace
@@ -490,19 +546,19 @@ bool prefix_mfma_supported(const Shape &s, int chunk)
     return s.in_dt == 1 && s.N == kN && s.P == kP && chunk % SC == 0;
 }
 
-// Work plan: segments of whole chunks, enough (stream, head, segment) workgroups to fill
-// the GPU about twice.
+// Work plan: segments of consecutive sub-chunks, enough (stream, head group, segment)
+// workgroups to fill the GPU about twice.
 PrefixPlan prefix_mfma_plan(const Shape &s, int64_t len, int chunk, bool single_segment)
 {
+    (void)chunk;
     PrefixPlan p{};
-    const int64_t pairs = std::max<int64_t>(1, static_cast<int64_t>(s.b) * s.H);
-    const int64_t nsub = (len + SC - 1) / SC;
-    const int chunk_sub = chunk / SC;
-    const int64_t want = single_segment ? 1 : std::max<int64_t>(1, (512 + pairs - 1) / pairs);
-    int64_t seg_sub = (nsub + want - 1) / want;
-    seg_sub = (seg_sub + chunk_sub - 1) / chunk_sub * chunk_sub;
-    p.seg_sub = static_cast<int>(std::max<int64_t>(seg_sub, chunk_sub));
-    p.nseg = static_cast<int>((nsub + p.seg_sub - 1) / p.seg_sub);
+    const int hpw = pick_hpw(s, true, single_segment);
+    const int64_t groups = std::max<int64_t>(1, static_cast<int64_t>(s.b) * (s.H / hpw));
+    const int64_t nsub = std::max<int64_t>(1, (len + SC - 1) / SC);
+    const int64_t want = single_segment ? 1 : std::max<int64_t>(1, (512 + groups - 1) / groups);
+    const int64_t seg_sub = (nsub + want - 1) / want;
+    p.seg_sub = static_cast<int>(seg_sub);
+    p.nseg = static_cast<int>((nsub + seg_sub - 1) / seg_sub);
     const int64_t nbh = static_cast<int64_t>(s.b) * p.nseg * s.H;
     p.tot_bytes = p.nseg > 1 ? static_cast<size_t>((nbh * 4 + 255) / 256 * 256) : 0;
     p.ws_bytes = p.nseg > 1 ? p.tot_bytes + static_cast<size_t>(nbh) * kN * kP * 4 : 0;
@@ -514,7 +570,10 @@ hipError_t run_prefix_mfma(const Shape &s, int64_t len, int chunk, const Seq &in
                            float *h_out, void *ws, hipStream_t st, bool single_segment)
 {
     const PrefixPlan p = prefix_mfma_plan(s, len, chunk, single_segment);
-    PrefixArgs a{};
+    const bool full = y || chunk_states;
+    const int hpw_full = pick_hpw(s, true, single_segment);
+    const int hpw_state = pick_hpw(s, false, single_segment || p.nseg == 1);
+    ScanArgs a{};
     a.s = s;
     a.len = len;
     a.seg_sub = p.seg_sub;
@@ -524,27 +583,30 @@ hipError_t run_prefix_mfma(const Shape &s, int64_t len, int chunk, const Seq &in
     a.in = in;
     a.A = A;
     a.D = D;
-    const bool full = y || chunk_states;
-    hipError_t e;
-    if (p.nseg == 1) {
-        // one segment per (stream, head): a single pass from h_init straight to h_out
-        a.h_in = h_init;
-        a.h_end = h_out;
+    auto run_full = [&]() {
         a.y = y;
         a.chunk_states = chunk_states;
-        if (!full)
-            return launch_prefix<false, float>(a, st);
-        // FULL reads its entering state with the [b][nseg][H] layout, which for nseg == 1
-        // is the [b][H] layout of h_init
-        return s.y_dt ? launch_prefix<true, __bf16>(a, st) : launch_prefix<true, float>(a, st);
+        a.h_last = h_out;
+        return s.y_dt ? launch_scan_hpw<true, __bf16>(a, hpw_full, st)
+                      : launch_scan_hpw<true, float>(a, hpw_full, st);
+    };
+    if (p.nseg == 1) {
+        // one segment per (stream, head): a single pass from h_init straight to h_out
+        // (the [b][nseg][H] layouts are the [b][H] layouts for nseg == 1)
+        a.h_in = h_init;
+        if (full)
+            return run_full();
+        a.h_end = h_out;
+        return launch_scan_hpw<false, float>(a, hpw_state, st);
     }
+    hipError_t e;
     float *tot = static_cast<float *>(ws);
     float *segs = reinterpret_cast<float *>(static_cast<char *>(ws) + p.tot_bytes);
     // 1. segment end states from zero
     a.h_in = nullptr;
     a.h_end = segs;
     a.tot = tot;
-    if ((e = launch_prefix<false, float>(a, st)) != hipSuccess)
+    if ((e = launch_scan_hpw<false, float>(a, hpw_state, st)) != hipSuccess)
         return e;
     // 2. states entering each segment (in place); the final state when nothing else follows
     {
@@ -553,23 +615,11 @@ hipError_t run_prefix_mfma(const Shape &s, int64_t len, int chunk, const Seq &in
         if ((e = hipGetLastError()) != hipSuccess || !full)
             return e;
     }
-    // 3. the full pass from the entering states; the last segment's end state is h_out.
-    //    h_end of the other segments is written into the workspace copy (no longer needed).
+    // 3. the full pass from the entering states; the last segment writes h_out
     a.h_in = segs;
+    a.h_end = nullptr;
     a.tot = nullptr;
-    a.y = y;
-    a.chunk_states = chunk_states;
-    a.h_end = segs;  // [b][nseg][H]: segment end states (scratch), final copied below
-    if ((e = s.y_dt ? launch_prefix<true, __bf16>(a, st) : launch_prefix<true, float>(a, st)) != hipSuccess)
-        return e;
-    const int64_t NP = static_cast<int64_t>(kN) * kP;
-    for (int b = 0; b < s.b; ++b) {
-        e = launch_copy_f32(h_out + static_cast<int64_t>(b) * s.H * NP,
-                            segs + (static_cast<int64_t>(b) * p.nseg + p.nseg - 1) * s.H * NP, s.H * NP, st);
-        if (e != hipSuccess)
-            return e;
-    }
-    return hipSuccess;
+    return run_full();
 }
 
 }  // namespace bdssm
