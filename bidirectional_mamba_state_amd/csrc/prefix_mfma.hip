@@ -60,31 +60,37 @@ __device__ __forceinline__ bf16x4 tr_read(const __bf16 *p)
     return __builtin_bit_cast(bf16x4, v);
 }
 
-// LDS tiles are row-major with padded rows. Row reads (pair_frag: 16 rows x the same 16
-// bytes) are conflict-free when the row stride is an odd multiple of 4 dwords; column
-// reads through the transposing load (tr_frag: 8 rows x 32 bytes) when it is an odd
-// multiple of 8. B and C rows are mostly read by rows, x rows only by columns.
-constexpr int BRS = kN + 8;   // B, C (and state copy) row stride: 68 dwords
-constexpr int XRS = kP + 16;  // x row stride: 40 dwords
-// the state-only pass reads B only by columns
-template <bool FULL> constexpr int b_stride() { return FULL ? BRS : kN + 16; }
+// LDS tiles are stored fragment-major. A tile of 64 rows x K columns is cut into 8-byte
+// pieces (4 columns); the piece holding columns c .. c+3 of row r lives in the 512-byte
+// region of (16-row block r/16, 32-column slice c/32, 16-column half (c/16)%2), at slot
+// 16 q + (r%16 ^ 4q) with q = (c/4)%4. A matrix-core operand fragment (lane (r16, q): row
+// 16 blk + r16, columns 32m + 4q + e and 32m + 16 + 4q + e) is then two contiguous
+// 512-byte reads, and a transposing read (4 rows x 16 columns per 16 lanes) touches 16
+// distinct 8-byte bank slots.
+template <int K>
+__device__ __forceinline__ int f8_off(int r, int c)  // in bf16 elements; c a multiple of 4
+{
+    const int blk = r >> 4, r16 = r & 15, m = c >> 5, hf = (c >> 4) & 1, q = (c >> 2) & 3;
+    return ((((blk * (K / 32) + m) * 2 + hf) * 64) + 16 * q + (r16 ^ (4 * q))) * 4;
+}
+
+// Operand fragment with the contraction along rows 16 blk + r16 of a tile: columns
+// 32m + 4q + e (slots e = 0..3) and 32m + 16 + 4q + e (slots 4..7).
+template <int K>
+__device__ __forceinline__ bf16x8 frag(const __bf16 *T, int blk, int m, int q, int r16)
+{
+    const __bf16 *p = T + f8_off<K>(16 * blk + r16, 32 * m + 4 * q);
+    return cat(*reinterpret_cast<const bf16x4 *>(p), *reinterpret_cast<const bf16x4 *>(p + 256));
+}
 
 // Operand fragment with the contraction over rows of a tile: lane (r16, q) gets column
 // col0 + r16 of rows row0 + 4q + e (slots e = 0..3) and row0 + 16 + 4q + e (slots 4..7) --
-// the row order of two stacked 16 x 16 accumulator tiles.
-template <int STRIDE>
+// the row order of two stacked 16 x 16 accumulator tiles. row0 and col0: multiples of 16.
+template <int K>
 __device__ __forceinline__ bf16x8 tr_frag(const __bf16 *T, int row0, int col0, int q, int r16)
 {
-    const __bf16 *p = T + (row0 + 4 * q + (r16 >> 2)) * STRIDE + col0 + 4 * (r16 & 3);
-    return cat(tr_read(p), tr_read(p + 16 * STRIDE));
-}
-
-// Operand fragment with the contraction along a row: columns 32m + 4q + e and
-// 32m + 16 + 4q + e of `row` (the same order as tr_frag).
-__device__ __forceinline__ bf16x8 pair_frag(const __bf16 *row, int m, int q)
-{
-    return cat(*reinterpret_cast<const bf16x4 *>(row + 32 * m + 4 * q),
-               *reinterpret_cast<const bf16x4 *>(row + 32 * m + 16 + 4 * q));
+    const __bf16 *p = T + f8_off<K>(row0 + 4 * q + (r16 >> 2), col0 + 4 * (r16 & 3));
+    return cat(tr_read(p), tr_read(p + (K / 32) * 2 * 64 * 4));  // the next 16-row block
 }
 
 __device__ __forceinline__ void split8(const float (&f)[8], bf16x8 &hi, bf16x8 &lo)
@@ -117,11 +123,11 @@ struct ScanArgs {
 
 template <bool FULL, int HPW>
 struct Lds {
-    __bf16 B[SC * b_stride<FULL>()];
-    __bf16 C[FULL ? SC * BRS : 8];
-    __bf16 X[HPW][SC * XRS];
+    __bf16 B[SC * kN];
+    __bf16 C[FULL ? SC * kN : 8];
+    __bf16 X[HPW][SC * kP];
     // FULL: each wavefront's state columns as bf16 hi and lo rows [p][n] (private to it)
-    __bf16 hT[FULL ? 4 * HPW : 1][FULL ? 2 : 1][FULL ? 16 * BRS : 8];
+    __bf16 hT[FULL ? 4 * HPW : 1][FULL ? 2 : 1][FULL ? 16 * kN : 8];
     float tab[HPW][NTAB][SC];
     float tot[HPW];
 };
@@ -191,8 +197,8 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
                         hi[j] = static_cast<__bf16>(hs[hh][i][j]);
                         lo[j] = static_cast<__bf16>(hs[hh][i][j] - bf2f(hi[j]));
                     }
-                    *reinterpret_cast<bf16x4 *>(&L.hT[wave * HPW + hh][0][r16 * BRS + 16 * i + 4 * q]) = hi;
-                    *reinterpret_cast<bf16x4 *>(&L.hT[wave * HPW + hh][1][r16 * BRS + 16 * i + 4 * q]) = lo;
+                    *reinterpret_cast<bf16x4 *>(&L.hT[wave * HPW + hh][0][f8_off<kN>(r16, 16 * i + 4 * q)]) = hi;
+                    *reinterpret_cast<bf16x4 *>(&L.hT[wave * HPW + hh][1][f8_off<kN>(r16, 16 * i + 4 * q)]) = lo;
                 }
         }
     };
@@ -221,7 +227,7 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
         const int last = static_cast<int>(min<int64_t>(SC, len - t0)) - 1;
 #pragma unroll
         for (int u = 0; u < BPT; ++u) {
-            const int it = tid + 256 * u, row = min(it >> 4, last), c16 = it & 15;
+            const int it = tid + 256 * u, row = min(16 * (it >> 8) + (it & 15), last), c16 = (it >> 4) & 15;
             st.cq[u] = *reinterpret_cast<const uint4 *>(Cg + (t0 + row) * rowBC + c16 * 8);
         }
     };
@@ -230,12 +236,13 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
         const int last = static_cast<int>(min<int64_t>(SC, len - t0)) - 1;
 #pragma unroll
         for (int u = 0; u < BPT; ++u) {
-            const int it = tid + 256 * u, row = min(it >> 4, last), c16 = it & 15;
+            const int it = tid + 256 * u, row = min(16 * (it >> 8) + (it & 15), last), c16 = (it >> 4) & 15;
             st.bq[u] = *reinterpret_cast<const uint4 *>(Bg + (t0 + row) * rowBC + c16 * 8);
         }
 #pragma unroll
         for (int u = 0; u < XPT; ++u) {
-            const int it = tid + 256 * u, row = min(it / (8 * HPW), last), c = it % (8 * HPW);
+            const int it = tid + 256 * u, c = (it >> 4) % (8 * HPW);
+            const int row = min(16 * ((it >> 4) / (8 * HPW)) + (it & 15), last);
             st.xq[u] = *reinterpret_cast<const uint4 *>(xg + (t0 + row) * rowX + c * 8);
         }
         st.dt = dtg[(t0 + min(lane, last)) * H + th];
@@ -243,17 +250,25 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
     auto store_stage = [&](int k) {
         const int64_t t0 = seg_t0 + static_cast<int64_t>(k) * SC;
         const int nvalid = static_cast<int>(min<int64_t>(SC, len - t0));
+        // each 16-byte row piece goes to LDS as two 8-byte pieces
+        auto put = [&](__bf16 *T, int off_lo, int off_hi, uint4 v) {
+            *reinterpret_cast<uint2 *>(T + off_lo) = make_uint2(v.x, v.y);
+            *reinterpret_cast<uint2 *>(T + off_hi) = make_uint2(v.z, v.w);
+        };
 #pragma unroll
         for (int u = 0; u < BPT; ++u) {
-            const int it = tid + 256 * u, row = it >> 4, c16 = it & 15;
-            *reinterpret_cast<uint4 *>(&L.B[row * b_stride<FULL>() + c16 * 8]) = sel4(row < nvalid, st.bq[u]);
+            const int it = tid + 256 * u, row = 16 * (it >> 8) + (it & 15), c16 = (it >> 4) & 15;
+            const int o0 = f8_off<kN>(row, c16 * 8), o1 = f8_off<kN>(row, c16 * 8 + 4);
+            put(L.B, o0, o1, sel4(row < nvalid, st.bq[u]));
             if (FULL)
-                *reinterpret_cast<uint4 *>(&L.C[row * BRS + c16 * 8]) = sel4(row < nvalid, st.cq[u]);
+                put(L.C, o0, o1, sel4(row < nvalid, st.cq[u]));
         }
 #pragma unroll
         for (int u = 0; u < XPT; ++u) {
-            const int it = tid + 256 * u, row = it / (8 * HPW), c = it % (8 * HPW);
-            *reinterpret_cast<uint4 *>(&L.X[c >> 3][row * XRS + (c & 7) * 8]) = sel4(row < nvalid, st.xq[u]);
+            const int it = tid + 256 * u, c = (it >> 4) % (8 * HPW);
+            const int row = 16 * ((it >> 4) / (8 * HPW)) + (it & 15);
+            put(L.X[c >> 3], f8_off<kP>(row, (c & 7) * 8), f8_off<kP>(row, (c & 7) * 8 + 4),
+                sel4(row < nvalid, st.xq[u]));
         }
         if (wave < HPW) {  // cumulative log2-decays of head h0 + wave, one token per lane
             const float d = lane < nvalid ? bf2f(st.dt) : 0.f;
@@ -312,7 +327,7 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
         for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
             for (int m = 0; m < 2; ++m)
-                xf[hh][m] = tr_frag<XRS>(L.X[hh], 32 * m, p0, q, r16);
+                xf[hh][m] = tr_frag<kP>(L.X[hh], 32 * m, p0, q, r16);
 
         if constexpr (FULL && WITHY) {
             // y rows of this sub-chunk; rows past the end fall outside the buffer range and
@@ -325,17 +340,17 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
                 const float(*tbl)[SC] = L.tab[hh];
                 // state entering the sub-chunk as y^T operands (rows p, contraction over n in
                 // the order of two stacked accumulator tiles), from this wavefront's LDS copy
-                const __bf16 *hTh = &L.hT[wave * HPW + hh][0][r16 * BRS];
-                const __bf16 *hTl = &L.hT[wave * HPW + hh][1][r16 * BRS];
-                // Two halves of row blocks (0-1, 2-3). Per half, scores S[tb][sb] = B_s . C_t
-                // (s in block sb <= tb, t in block tb) and y^T[p][t] = sum_n h[n][p] C[t][n]:
-                // each C fragment is read once, and the products of one 32-wide slice of n
-                // are independent.
+                const __bf16 *hTh = L.hT[wave * HPW + hh][0], *hTl = L.hT[wave * HPW + hh][1];
+                // Groups of NRB row blocks. Per group, scores S[tb][sb] = B_s . C_t (s in block
+                // sb <= tb, t in block tb) and y^T[p][t] = sum_n h[n][p] C[t][n]: each C
+                // fragment is read once, and the products of one 32-wide slice of n are
+                // independent.
+                constexpr int NRB = 2;
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                f32x4 S[2][4], acc[2];
+                for (int half = 0; half < 4 / NRB; ++half) {
+                f32x4 S[NRB][4], acc[NRB];
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
+                for (int u = 0; u < NRB; ++u) {
                     acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int sb = 0; sb < 4; ++sb)
@@ -343,15 +358,15 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
                 }
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    const bf16x8 hfh = pair_frag(hTh, m, q), hfl = pair_frag(hTl, m, q);
+                    const bf16x8 hfh = frag<kN>(hTh, 0, m, q, r16), hfl = frag<kN>(hTl, 0, m, q, r16);
                     bf16x8 bf[4];
 #pragma unroll
-                    for (int sb = 0; sb < 2 * half + 2; ++sb)
-                        bf[sb] = pair_frag(&L.B[(16 * sb + r16) * BRS], m, q);
+                    for (int sb = 0; sb < NRB * half + NRB; ++sb)
+                        bf[sb] = frag<kN>(L.B, sb, m, q, r16);
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const int tb = 2 * half + u;
-                        const bf16x8 cf = pair_frag(&L.C[(16 * tb + r16) * BRS], m, q);
+                    for (int u = 0; u < NRB; ++u) {
+                        const int tb = NRB * half + u;
+                        const bf16x8 cf = frag<kN>(L.C, tb, m, q, r16);
 #pragma unroll
                         for (int sb = 0; sb <= tb; ++sb)
                             S[u][sb] = mfma(bf[sb], cf, S[u][sb]);
@@ -360,8 +375,8 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
                     }
                 }
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int tb = 2 * half + u;
+                for (int u = 0; u < NRB; ++u) {
+                    const int tb = NRB * half + u;
                     const int t = 16 * tb + r16, md = tb >> 1;
                     const float ct = tbl[TAB_C][t];
                     acc[u] *= tbl[TAB_EF][t];
@@ -396,7 +411,7 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
                     }
                     // ---- + D x_t; lane holds y[t][p0 + 4q .. p0 + 4q + 3]
                     {
-                        const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(&L.X[hh][t * XRS + p0 + 4 * q]);
+                        const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(&L.X[hh][f8_off<kP>(t, p0 + 4 * q)]);
                         float o[4];
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
@@ -415,7 +430,7 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
                         }
                     }
                 }
-                __builtin_amdgcn_sched_barrier(0);  // one half at a time
+                __builtin_amdgcn_sched_barrier(0);  // one group at a time
                 }
             }
         }
@@ -440,7 +455,7 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
             bf16x8 bt[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                bt[i] = tr_frag<b_stride<FULL>()>(L.B, 32 * ks, 16 * i, q, r16);
+                bt[i] = tr_frag<kN>(L.B, 32 * ks, 16 * i, q, r16);
 #pragma unroll
             for (int hh = 0; hh < HPW; ++hh) {
                 const float4 w0 = *reinterpret_cast<const float4 *>(&L.tab[hh][TAB_W][32 * ks + 4 * q]);
