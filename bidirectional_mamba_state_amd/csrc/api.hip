@@ -11,6 +11,32 @@
 
 using namespace bdssm;
 
+namespace bdssm {
+
+// Compute units of the current device, cached per device (the only global state). Without
+// a usable device (for instance a workspace query on a host without GPUs) the MI355X count
+// is assumed, so that plans stay deterministic.
+int device_cus()
+{
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    int v = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+    if (v <= 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) {
+            (void)hipGetLastError();
+            v = 256;
+        }
+        __atomic_store_n(&cache[dev], v, __ATOMIC_RELAXED);
+    }
+    return v;
+}
+
+}  // namespace bdssm
+
 namespace {
 
 struct Range {
@@ -157,7 +183,7 @@ size_t bdssm_prefix_scan_workspace(const bdssm_dims *dims, int64_t len, int32_t 
     if (len == 0 || s.b == 0)
         return 0;
     if (prefix_mfma_supported(s, chunk))
-        return prefix_mfma_plan(s, len, chunk).ws_bytes;
+        return prefix_mfma_plan(s, len, chunk, with_y || with_chunk_states).ws_bytes;
     return plan_prefix(s, len, chunk, with_y != 0, with_chunk_states != 0).ws_bytes;
 }
 
@@ -214,7 +240,7 @@ bdssm_status bdssm_prefix_scan(const bdssm_dims *dims, int64_t len, int32_t chun
     const bool with_y = y != nullptr, with_cs = chunk_states != nullptr;
     const Seq seq{in->x, in->dt, in->B, in->C};
     if (prefix_mfma_supported(s, chunk)) {
-        const PrefixPlan mp = prefix_mfma_plan(s, len, chunk);
+        const PrefixPlan mp = prefix_mfma_plan(s, len, chunk, with_y || with_cs);
         if (mp.ws_bytes > 0) {
             if (!workspace || workspace_bytes < mp.ws_bytes)
                 return BDSSM_ERR_WORKSPACE;

@@ -58,10 +58,12 @@ struct PrefixPlan {
     size_t ws_bytes;   // total workspace bytes (0 for a single segment)
 };
 
+int device_cus();  // compute units of the current device (cached)
 bool valu_supported(int N, int P);
 bool prefix_mfma_supported(const Shape &s, int chunk);
-// single_segment: one segment per (stream, head), no workspace (used by commits)
-PrefixPlan prefix_mfma_plan(const Shape &s, int64_t len, int chunk, bool single_segment = false);
+// full: y or chunk states are wanted; single_segment: one segment per (stream, head), no
+// workspace (used by commits)
+PrefixPlan prefix_mfma_plan(const Shape &s, int64_t len, int chunk, bool full, bool single_segment = false);
 hipError_t run_prefix_mfma(const Shape &s, int64_t len, int chunk, const Seq &in, const float *A,
                            const float *D, const float *h_init, void *y, float *chunk_states,
                            float *h_out, void *ws, hipStream_t st, bool single_segment = false);

@@ -104,6 +104,26 @@ __device__ __forceinline__ void split8(const float (&f)[8], bf16x8 &hi, bf16x8 &
 
 enum { TAB_C, TAB_EF, TAB_LG, TAB_COL, TAB_W, NTAB };
 
+// DPP move of x from another lane (lanes with no source, or outside ROW_MASK, read 0)
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_move(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, false));
+}
+
+// Inclusive sum over the 64 lanes of a wavefront: shifts by 1, 2, 4, 8 within rows of 16,
+// then the last lane of each row is added to the rows after it.
+__device__ __forceinline__ float wave_inclusive_sum(float v)
+{
+    v += dpp_move<0x111, 0xf>(v);  // row_shr:1
+    v += dpp_move<0x112, 0xf>(v);  // row_shr:2
+    v += dpp_move<0x114, 0xf>(v);  // row_shr:4
+    v += dpp_move<0x118, 0xf>(v);  // row_shr:8
+    v += dpp_move<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+    v += dpp_move<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
 struct ScanArgs {
     Shape s;
     int64_t len;         // tokens per stream
@@ -128,8 +148,8 @@ struct Lds {
     __bf16 X[HPW][SC * kP];
     // FULL: each wavefront's state columns as bf16 hi and lo rows [p][n] (private to it)
     __bf16 hT[FULL ? 4 * HPW : 1][FULL ? 2 : 1][FULL ? 16 * kN : 8];
-    float tab[HPW][NTAB][SC];
-    float tot[HPW];
+    float tab[2][HPW][NTAB][SC];  // decay tables of sub-chunks k and k+1 (by parity)
+    float tot[2][HPW];
 };
 
 
@@ -219,7 +239,7 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
         uint4 bq[BPT];
         uint4 cq[FULL ? BPT : 1];
         uint4 xq[XPT];
-        __bf16 dt;
+        __bf16 dt;  // dt of sub-chunk k+2, token `lane`, head h0 + min(wave, HPW-1)
     } st;
     // rows past the end are clamped here and zeroed at store time
     auto load_c = [&](int k) {
@@ -245,6 +265,11 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
             const int row = min(16 * ((it >> 4) / (8 * HPW)) + (it & 15), last);
             st.xq[u] = *reinterpret_cast<const uint4 *>(xg + (t0 + row) * rowX + c * 8);
         }
+    };
+    // dt two sub-chunks ahead of the stage (clamped to the segment's last sub-chunk)
+    auto load_dt = [&](int k) {
+        const int64_t t0 = seg_t0 + static_cast<int64_t>(k) * SC;
+        const int last = static_cast<int>(min<int64_t>(SC, len - t0)) - 1;
         st.dt = dtg[(t0 + min(lane, last)) * H + th];
     };
     auto store_stage = [&](int k) {
@@ -270,26 +295,27 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
             put(L.X[c >> 3], f8_off<kP>(row, (c & 7) * 8), f8_off<kP>(row, (c & 7) * 8 + 4),
                 sel4(row < nvalid, st.xq[u]));
         }
-        if (wave < HPW) {  // cumulative log2-decays of head h0 + wave, one token per lane
+    };
+    // cumulative log2-decays of sub-chunk k for head h0 + wave (wavefronts below HPW), one
+    // token per lane, from the dt in st.dt; into table buffer k % 2
+    auto tables = [&](int k) {
+        if (wave < HPW) {
+            const int64_t t0 = seg_t0 + static_cast<int64_t>(k) * SC;
+            const int nvalid = static_cast<int>(min<int64_t>(SC, len - t0));
             const float d = lane < nvalid ? bf2f(st.dt) : 0.f;
-            float inc = d * Ath;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float up = __shfl_up(inc, off, 64);
-                if (lane >= off)
-                    inc += up;
-            }
+            const float inc = wave_inclusive_sum(d * Ath);
             const float c = inc * kLog2e;
-            const float clast = __shfl(c, 63, 64);
-            const float ref = __shfl(c, lane | 31, 64);  // end of this token's 32-token pair
-            float(*tb)[SC] = L.tab[wave];
+            const float c31 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 31));
+            const float clast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 63));
+            const float ref = lane < 32 ? c31 : clast;  // end of this token's 32-token pair
+            float(*tb)[SC] = L.tab[k & 1][wave];
             tb[TAB_C][lane] = c;
             tb[TAB_EF][lane] = __builtin_amdgcn_exp2f(c);
             tb[TAB_LG][lane] = __builtin_amdgcn_logf(d) - c;
             tb[TAB_COL][lane] = __builtin_amdgcn_exp2f(ref - c) * d;
             tb[TAB_W][lane] = __builtin_amdgcn_exp2f(clast - c) * d;
             if (lane == 63)
-                L.tot[wave] = inc;
+                L.tot[k & 1][wave] = inc;
         }
     };
 
@@ -308,17 +334,25 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
     // are out, and only the (branch-free) y stores of sub-chunk k follow them before their
     // use, so that waiting for them never waits for a store issued after them.
     load_stage(0);
+    load_dt(0);
     if (FULL)
         load_c(0);
     publish_state();
     store_stage(0);
+    tables(0);
+    load_dt(min(1, nsub - 1));
     for (int k = 0; k < nsub; ++k) {
         const int64_t t0 = seg_t0 + static_cast<int64_t>(k) * SC;
         const int nvalid = static_cast<int>(min<int64_t>(SC, len - t0));
-        __syncthreads();  // (A) sub-chunk k staged
+        __syncthreads();  // (A) sub-chunk k staged, its tables written
+        if (k + 1 < nsub)
+            tables(k + 1);  // other buffer; visible after barrier (B)
         if (FULL && a.chunk_states && k > 0)
             emit_chunk_state(k - 1);
         load_stage(min(k + 1, nsub - 1));  // in flight during sub-chunk k
+        if (FULL)
+            load_c(min(k + 1, nsub - 1));
+        load_dt(min(k + 2, nsub - 1));
         __builtin_amdgcn_sched_barrier(0);  // keep the loads here, ahead of the compute
 
         // x~ fragments (contraction over tokens, columns p0 .. p0+15), per head and 32-token pair
@@ -337,7 +371,7 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
                 0x00020000);
 #pragma unroll
             for (int hh = 0; hh < HPW; ++hh) {
-                const float(*tbl)[SC] = L.tab[hh];
+                const float(*tbl)[SC] = L.tab[k & 1][hh];
                 // state entering the sub-chunk as y^T operands (rows p, contraction over n in
                 // the order of two stacked accumulator tiles), from this wavefront's LDS copy
                 const __bf16 *hTh = L.hT[wave * HPW + hh][0], *hTl = L.hT[wave * HPW + hh][1];
@@ -435,15 +469,11 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
             }
         }
 
-        if (FULL) {  // C rows of sub-chunk k+1 (shared by all heads, mostly L2 hits)
-            load_c(min(k + 1, nsub - 1));
-            __builtin_amdgcn_sched_barrier(0);
-        }
 
         // ---- state: h <- exp(c_63) h + B^T (w o x), w_s = exp(c_63 - c_s) dt_s
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh) {
-            const float tot = L.tot[hh];
+            const float tot = L.tot[k & 1][hh];
             seg_tot[hh] += tot;
             const float alpha = __expf(tot);
 #pragma unroll
@@ -458,8 +488,8 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
                 bt[i] = tr_frag<kN>(L.B, 32 * ks, 16 * i, q, r16);
 #pragma unroll
             for (int hh = 0; hh < HPW; ++hh) {
-                const float4 w0 = *reinterpret_cast<const float4 *>(&L.tab[hh][TAB_W][32 * ks + 4 * q]);
-                const float4 w1 = *reinterpret_cast<const float4 *>(&L.tab[hh][TAB_W][32 * ks + 16 + 4 * q]);
+                const float4 w0 = *reinterpret_cast<const float4 *>(&L.tab[k & 1][hh][TAB_W][32 * ks + 4 * q]);
+                const float4 w1 = *reinterpret_cast<const float4 *>(&L.tab[k & 1][hh][TAB_W][32 * ks + 16 + 4 * q]);
                 const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
                 float xw[8];
 #pragma unroll
@@ -561,16 +591,19 @@ bool prefix_mfma_supported(const Shape &s, int chunk)
     return s.in_dt == 1 && s.N == kN && s.P == kP && chunk % SC == 0;
 }
 
-// Work plan: segments of consecutive sub-chunks, enough (stream, head group, segment)
-// workgroups to fill the GPU about twice.
-PrefixPlan prefix_mfma_plan(const Shape &s, int64_t len, int chunk, bool single_segment)
+// Work plan: segments of consecutive sub-chunks, as many (stream, head group, segment)
+// workgroups as the GPU holds at once -- a few more would run as a second, mostly empty
+// round. The full pass holds 2 workgroups per CU, the state-only pass with one head per
+// workgroup 4.
+PrefixPlan prefix_mfma_plan(const Shape &s, int64_t len, int chunk, bool full, bool single_segment)
 {
     (void)chunk;
     PrefixPlan p{};
-    const int hpw = pick_hpw(s, true, single_segment);
+    const int hpw = pick_hpw(s, full, single_segment);
     const int64_t groups = std::max<int64_t>(1, static_cast<int64_t>(s.b) * (s.H / hpw));
     const int64_t nsub = std::max<int64_t>(1, (len + SC - 1) / SC);
-    const int64_t want = single_segment ? 1 : std::max<int64_t>(1, (512 + groups - 1) / groups);
+    const int64_t slots = static_cast<int64_t>(full || hpw > 1 ? 2 : 4) * device_cus();
+    const int64_t want = single_segment ? 1 : std::max<int64_t>(1, slots / groups);
     const int64_t seg_sub = (nsub + want - 1) / want;
     p.seg_sub = static_cast<int>(seg_sub);
     p.nseg = static_cast<int>((nsub + seg_sub - 1) / seg_sub);
@@ -584,8 +617,8 @@ hipError_t run_prefix_mfma(const Shape &s, int64_t len, int chunk, const Seq &in
                            const float *D, const float *h_init, void *y, float *chunk_states,
                            float *h_out, void *ws, hipStream_t st, bool single_segment)
 {
-    const PrefixPlan p = prefix_mfma_plan(s, len, chunk, single_segment);
     const bool full = y || chunk_states;
+    const PrefixPlan p = prefix_mfma_plan(s, len, chunk, full, single_segment);
     const int hpw_full = pick_hpw(s, true, single_segment);
     const int hpw_state = pick_hpw(s, false, single_segment || p.nseg == 1);
     ScanArgs a{};
