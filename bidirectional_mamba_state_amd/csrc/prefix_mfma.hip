@@ -26,81 +26,16 @@
 #include <algorithm>
 
 #include "internal.h"
+#include "mfma_tiles.h"
 
 namespace bdssm {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int v2i32 __attribute__((ext_vector_type(2)));
 typedef int v4i32 __attribute__((ext_vector_type(4)));
 
 constexpr int kN = 128, kP = 64, SC = 64;  // d_state, headdim, sub-chunk length
 constexpr float kLog2e = 1.4426950408889634f;
-
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ float bf2f(__bf16 v) { return static_cast<float>(v); }
-__device__ __forceinline__ uint4 sel4(bool ok, uint4 v) { return ok ? v : make_uint4(0, 0, 0, 0); }
-__device__ __forceinline__ bf16x8 cat(bf16x4 lo, bf16x4 hi)
-{
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// Transposing LDS read: in each 16-lane group, lanes 4r .. 4r+3 address row r (four
-// consecutive elements each) and lane j receives column j of the four rows.
-__device__ __forceinline__ bf16x4 tr_read(const __bf16 *p)
-{
-    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
-    return __builtin_bit_cast(bf16x4, v);
-}
-
-// LDS tiles are stored fragment-major. A tile of 64 rows x K columns is cut into 8-byte
-// pieces (4 columns); the piece holding columns c .. c+3 of row r lives in the 512-byte
-// region of (16-row block r/16, 32-column slice c/32, 16-column half (c/16)%2), at slot
-// 16 q + (r%16 ^ 4q) with q = (c/4)%4. A matrix-core operand fragment (lane (r16, q): row
-// 16 blk + r16, columns 32m + 4q + e and 32m + 16 + 4q + e) is then two contiguous
-// 512-byte reads, and a transposing read (4 rows x 16 columns per 16 lanes) touches 16
-// distinct 8-byte bank slots.
-template <int K>
-__device__ __forceinline__ int f8_off(int r, int c)  // in bf16 elements; c a multiple of 4
-{
-    const int blk = r >> 4, r16 = r & 15, m = c >> 5, hf = (c >> 4) & 1, q = (c >> 2) & 3;
-    return ((((blk * (K / 32) + m) * 2 + hf) * 64) + 16 * q + (r16 ^ (4 * q))) * 4;
-}
-
-// Operand fragment with the contraction along rows 16 blk + r16 of a tile: columns
-// 32m + 4q + e (slots e = 0..3) and 32m + 16 + 4q + e (slots 4..7).
-template <int K>
-__device__ __forceinline__ bf16x8 frag(const __bf16 *T, int blk, int m, int q, int r16)
-{
-    const __bf16 *p = T + f8_off<K>(16 * blk + r16, 32 * m + 4 * q);
-    return cat(*reinterpret_cast<const bf16x4 *>(p), *reinterpret_cast<const bf16x4 *>(p + 256));
-}
-
-// Operand fragment with the contraction over rows of a tile: lane (r16, q) gets column
-// col0 + r16 of rows row0 + 4q + e (slots e = 0..3) and row0 + 16 + 4q + e (slots 4..7) --
-// the row order of two stacked 16 x 16 accumulator tiles. row0 and col0: multiples of 16.
-template <int K>
-__device__ __forceinline__ bf16x8 tr_frag(const __bf16 *T, int row0, int col0, int q, int r16)
-{
-    const __bf16 *p = T + f8_off<K>(row0 + 4 * q + (r16 >> 2), col0 + 4 * (r16 & 3));
-    return cat(tr_read(p), tr_read(p + (K / 32) * 2 * 64 * 4));  // the next 16-row block
-}
-
-__device__ __forceinline__ void split8(const float (&f)[8], bf16x8 &hi, bf16x8 &lo)
-{
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        hi[e] = static_cast<__bf16>(f[e]);
-        lo[e] = static_cast<__bf16>(f[e] - bf2f(hi[e]));
-    }
-}
 
 enum { TAB_C, TAB_EF, TAB_LG, TAB_COL, TAB_W, NTAB };
 
@@ -275,25 +210,18 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
     auto store_stage = [&](int k) {
         const int64_t t0 = seg_t0 + static_cast<int64_t>(k) * SC;
         const int nvalid = static_cast<int>(min<int64_t>(SC, len - t0));
-        // each 16-byte row piece goes to LDS as two 8-byte pieces
-        auto put = [&](__bf16 *T, int off_lo, int off_hi, uint4 v) {
-            *reinterpret_cast<uint2 *>(T + off_lo) = make_uint2(v.x, v.y);
-            *reinterpret_cast<uint2 *>(T + off_hi) = make_uint2(v.z, v.w);
-        };
 #pragma unroll
         for (int u = 0; u < BPT; ++u) {
             const int it = tid + 256 * u, row = 16 * (it >> 8) + (it & 15), c16 = (it >> 4) & 15;
-            const int o0 = f8_off<kN>(row, c16 * 8), o1 = f8_off<kN>(row, c16 * 8 + 4);
-            put(L.B, o0, o1, sel4(row < nvalid, st.bq[u]));
+            put16<kN>(L.B, row, c16 * 8, sel4(row < nvalid, st.bq[u]));
             if (FULL)
-                put(L.C, o0, o1, sel4(row < nvalid, st.cq[u]));
+                put16<kN>(L.C, row, c16 * 8, sel4(row < nvalid, st.cq[u]));
         }
 #pragma unroll
         for (int u = 0; u < XPT; ++u) {
             const int it = tid + 256 * u, c = (it >> 4) % (8 * HPW);
             const int row = 16 * ((it >> 4) / (8 * HPW)) + (it & 15);
-            put(L.X[c >> 3], f8_off<kP>(row, (c & 7) * 8), f8_off<kP>(row, (c & 7) * 8 + 4),
-                sel4(row < nvalid, st.xq[u]));
+            put16<kP>(L.X[c >> 3], row, (c & 7) * 8, sel4(row < nvalid, st.xq[u]));
         }
     };
     // cumulative log2-decays of sub-chunk k for head h0 + wave (wavefronts below HPW), one

@@ -21,6 +21,12 @@ def rel(a, b):
     return num / den if den > 0 else num
 
 
+def within(err, tol, what):
+    """Reports a measured relative error next to its bound; true when it is inside."""
+    print(f"[parity] {what}: rel {err:.3e} (bound {tol:.0e})", flush=True)
+    return err < tol
+
+
 def max_head_rel(a, b, head_axis):
     """Largest per-head relative L2 error (exposes errors confined to a few heads)."""
     a = np.moveaxis(np.asarray(a, np.float64), head_axis, 0)

@@ -11,7 +11,7 @@ import oracle
 from bidirectional_mamba_state_amd import bdssm, configs, inputs
 from bidirectional_mamba_state_amd.inputs import Seq
 
-from harness import (TOL_BF16, TOL_F32, gpu_block_step, gpu_commit, gpu_prefix, max_head_rel,
+from harness import (within, TOL_BF16, TOL_F32, gpu_block_step, gpu_commit, gpu_prefix, max_head_rel,
                      rel, slice_seq, streams_of, tol_for, f32_round)
 
 pytestmark = pytest.mark.gpu
@@ -30,18 +30,18 @@ def _check_prefix(seq, A, D, chunk, h_init=None, want_y=True, want_cs=True, head
     yo, cso, ho = oracle.scan(seq, A, D, chunk, h_init=h_init, want_y=want_y,
                               want_chunk_states=want_cs, heads=heads)
     hs = slice(None) if heads is None else list(heads)
-    assert rel(h[:, hs], ho[:, hs]) < tol_for(seq.dtype), "final state"
+    assert within(rel(h[:, hs], ho[:, hs]), tol_for(seq.dtype), "final state")
     if want_cs:
-        assert rel(cs[:, :, hs], cso[:, :, hs]) < tol_for(seq.dtype), "chunk states"
+        assert within(rel(cs[:, :, hs], cso[:, :, hs]), tol_for(seq.dtype), "chunk states")
         assert np.array_equal(cs[:, -1], h), "last chunk state == h_out"
     if want_y:
-        assert rel(y[:, :, hs], yo[:, :, hs]) < tol, "y"
-        assert max_head_rel(y[:, :, hs], yo[:, :, hs], 2) < 4 * tol
+        assert within(rel(y[:, :, hs], yo[:, :, hs]), tol, "y")
+        assert within(max_head_rel(y[:, :, hs], yo[:, :, hs], 2), 4 * tol, "y, worst head")
         # the scan part alone (D = 0)
         Dz = np.zeros_like(D)
         yz, _, _ = gpu_prefix(seq, A, Dz, chunk, h_init, True, False, y_dtype)
         yzo, _, _ = oracle.scan(seq, A, Dz, chunk, h_init=h_init, want_chunk_states=False, heads=heads)
-        assert rel(yz[:, :, hs], yzo[:, :, hs]) < tol, "y - D x"
+        assert within(rel(yz[:, :, hs], yzo[:, :, hs]), tol, "y - D x")
     return h
 
 
@@ -51,20 +51,20 @@ def _check_block(h_prefix, fwd, rev, A, D, y_dtype=bdssm.F32, heads=None, label=
     y = gpu_block_step(h_prefix, fwd, rev, A, D, y_dtype)
     yo, _, _ = oracle.block_step(h_prefix, fwd, rev, A, D, heads=heads)
     hs = slice(None) if heads is None else list(heads)
-    assert rel(y[:, :, hs], yo[:, :, hs]) < tol, "block y"
+    assert within(rel(y[:, :, hs], yo[:, :, hs]), tol, "block y")
     Dz = np.zeros_like(D)
     yz = gpu_block_step(h_prefix, fwd, rev, A, Dz, y_dtype)
     yzo, _, _ = oracle.block_step(h_prefix, fwd, rev, A, Dz, heads=heads)
-    assert rel(yz[:, :, hs], yzo[:, :, hs]) < tol, "block y - D x"
-    assert max_head_rel(yz[:, :, hs], yzo[:, :, hs], 2) < 4 * tol
+    assert within(rel(yz[:, :, hs], yzo[:, :, hs]), tol, "block y - D x")
+    assert within(max_head_rel(yz[:, :, hs], yzo[:, :, hs], 2), 4 * tol, "block y - D x, worst head")
 
 
 def _check_commit(h, clean, A, D, label=""):
     _case(f"commit {label} T={clean.length}")
     hn, y = gpu_commit(h, clean, A, D, want_y=True)
     hno, yo = oracle.commit(h, clean, A, D, want_y=True)
-    assert rel(hn, hno) < tol_for(clean.dtype), "commit state"
-    assert rel(y, yo) < tol_for(clean.dtype), "commit y"
+    assert within(rel(hn, hno), tol_for(clean.dtype), "commit state")
+    assert within(rel(y, yo), tol_for(clean.dtype), "commit y")
     hn2, _ = gpu_commit(h, clean, A, D, want_y=False)
     assert np.array_equal(hn, hn2), "commit state does not depend on whether y is written"
     return hn
@@ -240,8 +240,8 @@ def test_reverse_locality_and_stream_independence():
     dh = h2 - h1
     yd = gpu_block_step(dh, zero_x, zero_r, A, D)
     ydo, _, _ = oracle.block_step(dh, zero_x, zero_r, A, D)
-    assert rel(yd, ydo) < TOL_BF16
-    assert rel(y2 - y1, ydo) < TOL_BF16
+    assert within(rel(yd, ydo), TOL_BF16, "state term alone")
+    assert within(rel(y2 - y1, ydo), TOL_BF16, "difference of two steps = state term")
 
 
 def test_commit_chain_equals_prefix_scan():
@@ -254,10 +254,10 @@ def test_commit_chain_equals_prefix_scan():
     for k in range(32):
         h, _ = gpu_commit(h, slice_seq(pre, 32 * k, 32 * (k + 1)), A, D)
         if (k + 1) % 8 == 0:
-            assert rel(h, cs[:, (k + 1) // 8 - 1]) < 1e-5
-    assert rel(h, h_scan) < 1e-5
+            assert within(rel(h, cs[:, (k + 1) // 8 - 1]), 1e-5, "commit chain vs chunk state (same kernels)")
+    assert within(rel(h, h_scan), 1e-5, "commit chain vs scan final state")
     _, _, ho = oracle.scan(pre, A, D, 256, want_y=False, want_chunk_states=False)
-    assert rel(h, ho) < TOL_BF16
+    assert within(rel(h, ho), TOL_BF16, "commit chain vs oracle")
 
 
 @pytest.mark.parametrize("T", [32, 128])
@@ -281,8 +281,8 @@ def test_block_step_launch_shapes(monkeypatch, T):
             _case(f"launch shape T={T} hpw={hpw} ps={ps}")
             y = gpu_block_step(h, fwd, rev, A, D)
             yz = gpu_block_step(h, fwd, rev, A, Dz)
-            assert rel(y, yo) < TOL_BF16, (hpw, ps)
-            assert rel(yz, yzo) < TOL_BF16, (hpw, ps)
+            assert within(rel(y, yo), TOL_BF16, f"y hpw={hpw} ps={ps}")
+            assert within(rel(yz, yzo), TOL_BF16, f"y - D x hpw={hpw} ps={ps}")
 
 
 def test_config4_running_set_shape():
@@ -295,19 +295,19 @@ def test_config4_running_set_shape():
     _, _, h = gpu_prefix(pre, A, D, cfg.chunk, want_y=False, want_cs=False)
     sample = [0, 31, 63]
     _, _, ho = oracle.scan(streams_of(pre, sample), A, D, cfg.chunk, want_y=False, want_chunk_states=False)
-    assert rel(h[sample], ho) < TOL_BF16
+    assert within(rel(h[sample], ho), TOL_BF16, "c4 prefix state (sampled streams)")
     fwd = inputs.block(cfg, 0, 0, inputs.FWD)
     rev = inputs.block(cfg, 0, 0, inputs.REV)
     for y_dtype in (bdssm.F32, bdssm.BF16):
         _case(f"c4 block step y_dtype={y_dtype}")
         y = gpu_block_step(h, fwd, rev, A, D, y_dtype)
         yo, _, _ = oracle.block_step(h[sample], streams_of(fwd, sample), streams_of(rev, sample), A, D)
-        assert rel(y[sample], yo) < TOL_BF16
+        assert within(rel(y[sample], yo), TOL_BF16, "c4 block y (sampled streams)")
     Dz = np.zeros_like(D)
     yz = gpu_block_step(h, fwd, rev, A, Dz)
     yzo, _, _ = oracle.block_step(h[sample], streams_of(fwd, sample), streams_of(rev, sample), A, Dz)
-    assert rel(yz[sample], yzo) < TOL_BF16
-    assert max_head_rel(yz[sample], yzo, 2) < 4 * TOL_BF16
+    assert within(rel(yz[sample], yzo), TOL_BF16, "c4 block y - D x (sampled streams)")
+    assert within(max_head_rel(yz[sample], yzo, 2), 4 * TOL_BF16, "y - D x, worst head")
 
 
 @pytest.mark.parametrize("b,H,G,L,chunk,want_y,want_cs,init", [
