@@ -267,6 +267,26 @@ def main():
                       "parallelism": "none (1 GPU)"},
            "roofline": roof, "breakdown": breakdown}
 
+    # the same 64 block steps + commit through the library's decode-loop graph (one HIP
+    # graph recorded by bdssm_decode_graph_create), timed per replay
+    dg = bdssm.DecodeGraph(d, T, h, [f for f, _ in steps], [r for _, r in steps], Ad, Dd, y_blk, clean)
+    for _ in range(2):
+        dg.launch()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        dg.launch()
+    e1.record()
+    torch.cuda.synchronize()
+    blk_us = 1e3 * e0.elapsed_time(e1) / reps
+    dg.close()
+    out["decode_graph"] = {"workload": "bdssm_decode_graph: 64 block steps (T=32) + commit of one block, "
+                                       "700M shape, replayed back to back",
+                           "us_per_block": round(blk_us, 2), "us_per_launch": round(blk_us / (S + 1), 3),
+                           "active_tokens_per_s": round(S * b * T / (blk_us * 1e-6), 1)}
+
     if not args.no_secondary:
         out["secondary"] = secondary(torch, np, bdssm, configs, inputs)
     if not args.no_cpu_baseline:

@@ -18,7 +18,8 @@ F32, BF16 = 0, 1
 
 # every symbol include/bdssm.h declares
 EXPORTS = ("bdssm_abi_version", "bdssm_status_str", "bdssm_prefix_scan_workspace",
-           "bdssm_prefix_scan", "bdssm_block_step", "bdssm_commit")
+           "bdssm_prefix_scan", "bdssm_block_step", "bdssm_commit", "bdssm_decode_graph_create",
+           "bdssm_decode_graph_launch", "bdssm_decode_graph_destroy")
 
 
 class BdssmError(RuntimeError):
@@ -62,6 +63,13 @@ def load():
         lib.bdssm_block_step.argtypes = [P(Dims), I32, V, P(SeqPtrs), P(SeqPtrs), V, V, V, V]
         lib.bdssm_commit.restype = ctypes.c_int
         lib.bdssm_commit.argtypes = [P(Dims), I32, P(SeqPtrs), V, V, V, V, V]
+        lib.bdssm_decode_graph_create.restype = ctypes.c_int
+        lib.bdssm_decode_graph_create.argtypes = [P(Dims), I32, I32, V, P(SeqPtrs), P(SeqPtrs), V, V,
+                                                  P(V), P(SeqPtrs), V, V, P(V)]
+        lib.bdssm_decode_graph_launch.restype = ctypes.c_int
+        lib.bdssm_decode_graph_launch.argtypes = [V, V]
+        lib.bdssm_decode_graph_destroy.restype = None
+        lib.bdssm_decode_graph_destroy.argtypes = [V]
         _lib = lib
     return _lib
 
@@ -143,6 +151,43 @@ def commit(d, block_len, clean, A, D, h, y=None, stream=None):
     """bdssm_commit. clean = (x, dt, B, C) tensors (C may be None when y is None)."""
     _check(load().bdssm_commit(ctypes.byref(d), block_len, _byref(_seq(clean)), _ptr(A), _ptr(D),
                                _ptr(h), _ptr(y), _stream(stream)))
+
+
+class DecodeGraph:
+    """bdssm_decode_graph_*: the steps of one active block and its commit, recorded once
+    and replayed with launch(). Keeps references to the tensors whose addresses it holds."""
+
+    def __init__(self, d, block_len, h, fwd_steps, rev_steps, A, D, ys, clean=None, y_commit=None):
+        import torch
+        steps = len(ys)
+        if len(fwd_steps) != steps or len(rev_steps) != steps:
+            raise ValueError("one fwd, rev and y per step")
+        self._keep = (h, fwd_steps, rev_steps, A, D, ys, clean, y_commit)
+        fw = (SeqPtrs * max(steps, 1))(*[_seq(s) for s in fwd_steps])
+        rv = (SeqPtrs * max(steps, 1))(*[_seq(s) for s in rev_steps])
+        yp = (ctypes.c_void_p * max(steps, 1))(*[_ptr(t) for t in ys])
+        # record on a side stream: the legacy default stream cannot be captured
+        side = torch.cuda.Stream()
+        handle = ctypes.c_void_p()
+        rc = load().bdssm_decode_graph_create(ctypes.byref(d), block_len, steps, _ptr(h), fw, rv,
+                                              _ptr(A), _ptr(D), yp, _byref(_seq(clean)),
+                                              _ptr(y_commit), side.cuda_stream, ctypes.byref(handle))
+        _check(rc)
+        self._handle = handle
+
+    def launch(self, stream=None):
+        _check(load().bdssm_decode_graph_launch(self._handle, _stream(stream)))
+
+    def close(self):
+        if getattr(self, "_handle", None):
+            load().bdssm_decode_graph_destroy(self._handle)
+            self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 # ------------------------------------------------------------------ data movement helpers

@@ -17,6 +17,10 @@
  *   bdssm_commit       - the clean forward pass over a finalized block that extends the
  *                        cache: s_{k+1} = F_fwd(b*; s_k), in place.
  *
+ * bdssm_decode_graph_* record the calls of one active block (its denoising steps, then its
+ * commit) once into a HIP graph and replay it, removing per-call launch latency from a
+ * decode loop with static shapes.
+ *
  * The scan F is the selective state-space recurrence of eq. (1) in its Mamba-2 form,
  * with one negative scalar A[h] per head:
  *     alpha_t = exp(dt[t,h] * A[h])
@@ -35,7 +39,7 @@
  * Conventions for every call:
  *  - Pointers are device pointers (hipMalloc'd, or torch CUDA tensors); the caller owns
  *    every buffer. Base pointers must be 16-byte aligned. The library allocates nothing
- *    and never synchronizes.
+ *    (except the graph object of bdssm_decode_graph_create) and never synchronizes.
  *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
  *    asynchronously; the returned status covers argument validation and the launch.
  *    Faults during execution surface at the caller's next synchronization.
@@ -144,6 +148,39 @@ bdssm_status bdssm_block_step(const bdssm_dims *dims, int32_t block_len,
  */
 bdssm_status bdssm_commit(const bdssm_dims *dims, int32_t block_len, const bdssm_seq *clean,
                           const float *A, const float *D, float *h, void *y, void *stream);
+
+/*
+ * Decode loop of one active block as a HIP graph: `steps` calls of bdssm_block_step (step
+ * k reads fwd[k], rev[k] and writes y[k], all from the cached state h), followed, when
+ * clean is not NULL, by bdssm_commit(clean, h, y_commit). This is the static-shape block
+ * buffer of block-diffusion decoding, whose inputs change from step to step in place.
+ *   fwd, rev   host arrays of `steps` input descriptors (device pointers)
+ *   y          host array of `steps` device output pointers, [b][T][H][P] in y_dtype
+ *   h          [b][H][N][P] float32: read by every step, then advanced by the commit
+ *   clean      the commit's inputs, or NULL for steps only; y_commit as in bdssm_commit
+ *   stream     the stream the calls are recorded on; must not be NULL (the legacy default
+ *              stream cannot be captured). Nothing runs during creation.
+ *   out        receives the graph; NULL on error
+ * Every call is validated as bdssm_block_step / bdssm_commit validate it; the first
+ * failing status is returned and no graph is made. The device pointers are baked into
+ * the graph: the buffers must stay allocated, at the same addresses, while it exists.
+ * Errors: BDSSM_ERR_NULL (dims, out, fwd, rev, y or stream NULL; steps < 1 with no commit),
+ * BDSSM_ERR_SHAPE (steps < 0), the statuses of the recorded calls, BDSSM_ERR_HIP
+ * (capture or instantiation failed).
+ */
+typedef struct bdssm_decode_graph bdssm_decode_graph;
+bdssm_status bdssm_decode_graph_create(const bdssm_dims *dims, int32_t block_len, int32_t steps,
+                                       float *h, const bdssm_seq *fwd, const bdssm_seq *rev,
+                                       const float *A, const float *D, void *const *y,
+                                       const bdssm_seq *clean, void *y_commit, void *stream,
+                                       bdssm_decode_graph **out);
+
+/* Enqueues one replay of the recorded calls on `stream` (NULL = default stream). Runs
+ * asynchronously, like the calls it replaces; allocates nothing. */
+bdssm_status bdssm_decode_graph_launch(const bdssm_decode_graph *graph, void *stream);
+
+/* Frees the graph (NULL is ignored). Replays already enqueued are not affected. */
+void bdssm_decode_graph_destroy(bdssm_decode_graph *graph);
 
 #ifdef __cplusplus
 }

@@ -140,3 +140,28 @@ def test_binding_refuses_host_tensors():
     d = good()
     with pytest.raises(TypeError):
         bdssm.block_step(d, 16, torch.zeros(4), None, None, None, None, None, stream=0)
+
+
+def test_decode_graph_argument_checks():
+    """bdssm_decode_graph_*: argument errors are reported before any HIP call."""
+    lib = bdssm.load()
+    d = good()
+    out = ctypes.c_void_p(1234)
+    f = (bdssm.SeqPtrs * 2)(seq(), seq())
+    ys = (ctypes.c_void_p * 2)(FAKE + (1 << 24), FAKE + (1 << 25))
+    create = lib.bdssm_decode_graph_create
+    # NULL stream (the legacy default stream cannot be captured); out is cleared
+    assert create(ctypes.byref(d), 16, 2, FAKE, f, f, FAKE, FAKE, ys, None, None, None,
+                  ctypes.byref(out)) == bdssm.ERR_NULL
+    assert out.value is None
+    assert create(None, 16, 2, FAKE, f, f, FAKE, FAKE, ys, None, None, FAKE, ctypes.byref(out)) == bdssm.ERR_NULL
+    assert create(ctypes.byref(d), 16, 2, FAKE, f, f, FAKE, FAKE, ys, None, None, FAKE, None) == bdssm.ERR_NULL
+    assert create(ctypes.byref(d), 16, -1, FAKE, f, f, FAKE, FAKE, ys, None, None, FAKE,
+                  ctypes.byref(out)) == bdssm.ERR_SHAPE
+    assert create(ctypes.byref(d), 16, 2, FAKE, None, f, FAKE, FAKE, ys, None, None, FAKE,
+                  ctypes.byref(out)) == bdssm.ERR_NULL
+    # no steps and no commit: nothing to record
+    assert create(ctypes.byref(d), 16, 0, FAKE, None, None, FAKE, FAKE, None, None, None, FAKE,
+                  ctypes.byref(out)) == bdssm.ERR_NULL
+    assert lib.bdssm_decode_graph_launch(None, None) == bdssm.ERR_NULL
+    lib.bdssm_decode_graph_destroy(None)
