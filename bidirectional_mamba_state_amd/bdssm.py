@@ -18,7 +18,8 @@ F32, BF16 = 0, 1
 
 # every symbol include/bdssm.h declares
 EXPORTS = ("bdssm_abi_version", "bdssm_status_str", "bdssm_prefix_scan_workspace",
-           "bdssm_prefix_scan", "bdssm_block_step", "bdssm_commit", "bdssm_decode_graph_create",
+           "bdssm_prefix_scan", "bdssm_block_step", "bdssm_block_step_ex", "bdssm_commit",
+           "bdssm_decode_graph_create",
            "bdssm_decode_graph_launch", "bdssm_decode_graph_destroy")
 
 
@@ -61,6 +62,8 @@ def load():
         lib.bdssm_prefix_scan.argtypes = [P(Dims), I64, I32, P(SeqPtrs), V, V, V, V, V, V, V, SZ, V]
         lib.bdssm_block_step.restype = ctypes.c_int
         lib.bdssm_block_step.argtypes = [P(Dims), I32, V, P(SeqPtrs), P(SeqPtrs), V, V, V, V]
+        lib.bdssm_block_step_ex.restype = ctypes.c_int
+        lib.bdssm_block_step_ex.argtypes = [P(Dims), I32, V, P(SeqPtrs), P(SeqPtrs), V, V, V, V, V, V]
         lib.bdssm_commit.restype = ctypes.c_int
         lib.bdssm_commit.argtypes = [P(Dims), I32, P(SeqPtrs), V, V, V, V, V]
         lib.bdssm_decode_graph_create.restype = ctypes.c_int
@@ -145,6 +148,14 @@ def block_step(d, block_len, h_prefix, fwd, rev, A, D, y, stream=None):
     """bdssm_block_step. fwd, rev = (x, dt, B, C) tensors."""
     _check(load().bdssm_block_step(ctypes.byref(d), block_len, _ptr(h_prefix), _byref(_seq(fwd)),
                                    _byref(_seq(rev)), _ptr(A), _ptr(D), _ptr(y), _stream(stream)))
+
+
+def block_step_ex(d, block_len, h_prefix, fwd, rev, A, D, A_rev, D_rev, y, stream=None):
+    """bdssm_block_step_ex: separate reverse-direction decay A_rev and skip weight D_rev
+    (None = no reverse skip term)."""
+    _check(load().bdssm_block_step_ex(ctypes.byref(d), block_len, _ptr(h_prefix), _byref(_seq(fwd)),
+                                      _byref(_seq(rev)), _ptr(A), _ptr(D), _ptr(A_rev), _ptr(D_rev),
+                                      _ptr(y), _stream(stream)))
 
 
 def commit(d, block_len, clean, A, D, h, y=None, stream=None):

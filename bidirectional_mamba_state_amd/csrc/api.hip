@@ -306,6 +306,14 @@ bdssm_status bdssm_block_step(const bdssm_dims *dims, int32_t block_len,
                               const bdssm_seq *rev, const float *A, const float *D, void *y,
                               void *stream)
 {
+    return bdssm_block_step_ex(dims, block_len, h_prefix, fwd, rev, A, D, A, nullptr, y, stream);
+}
+
+bdssm_status bdssm_block_step_ex(const bdssm_dims *dims, int32_t block_len,
+                                 const float *h_prefix, const bdssm_seq *fwd,
+                                 const bdssm_seq *rev, const float *A, const float *D,
+                                 const float *A_rev, const float *D_rev, void *y, void *stream)
+{
     Shape s;
     bdssm_status rc = check_dims(dims, &s);
     if (rc != BDSSM_OK)
@@ -314,24 +322,26 @@ bdssm_status bdssm_block_step(const bdssm_dims *dims, int32_t block_len,
         return BDSSM_ERR_SHAPE;
     if (block_len > 256)
         return BDSSM_ERR_UNSUPPORTED;
-    if (!h_prefix || !A || !D || !y)
+    if (!h_prefix || !A || !D || !A_rev || !y)
         return BDSSM_ERR_NULL;
     SeqRanges qf{}, qr{};
     if ((rc = check_seq(fwd, s, block_len, true, &qf)) != BDSSM_OK)
         return rc;
     if ((rc = check_seq(rev, s, block_len, true, &qr)) != BDSSM_OK)
         return rc;
-    if (!aligned(h_prefix) || !aligned(A) || !aligned(D) || !aligned(y))
+    if (!aligned(h_prefix) || !aligned(A) || !aligned(D) || !aligned(A_rev) || !aligned(D_rev) ||
+        !aligned(y))
         return BDSSM_ERR_ALIGN;
     const int64_t NP = static_cast<int64_t>(s.N) * s.P;
     const Range ry = rng(y, static_cast<int64_t>(s.b) * block_len * s.H * s.P * elt(s.y_dt));
     if (hits(ry, qf) || hits(ry, qr) || overlap(ry, rng(h_prefix, static_cast<int64_t>(s.b) * s.H * NP * 4)) ||
-        overlap(ry, rng(A, s.H * 4)) || overlap(ry, rng(D, s.H * 4)))
+        overlap(ry, rng(A, s.H * 4)) || overlap(ry, rng(D, s.H * 4)) || overlap(ry, rng(A_rev, s.H * 4)) ||
+        overlap(ry, rng(D_rev, s.H * 4)))
         return BDSSM_ERR_ALIAS;
     if (s.b == 0 || block_len == 0)
         return BDSSM_OK;
     BlockArgs a{s, block_len, h_prefix, Seq{fwd->x, fwd->dt, fwd->B, fwd->C},
-                Seq{rev->x, rev->dt, rev->B, rev->C}, A, D, y};
+                Seq{rev->x, rev->dt, rev->B, rev->C}, A, D, y, A_rev, D_rev};
     if (block_mfma_supported(s, block_len)) {
         int hpw, ps;
         block_mfma_plan(s, &hpw, &ps);

@@ -88,6 +88,7 @@ struct Stage {
     uint4 x[XPT][4];
     __bf16 d0, d1;  // dt of tokens 2*lane, 2*lane+1 (wavefronts 0 and 1)
     float A, D;     // the head's A and D
+    float Ar, Dr;   // the reverse direction's A and skip weight (0 without one)
 };
 
 // per-head decay tables (log2 units), one set per LDS buffer
@@ -108,7 +109,7 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
     __shared__ __attribute__((aligned(16))) __bf16 XTf[2][PW * XS];
     __shared__ __attribute__((aligned(16))) __bf16 XTr[2][PW * XS];
     __shared__ __attribute__((aligned(16))) float tab[2][NTAB][TP];
-    __shared__ float hd[2];  // D of the head in each buffer
+    __shared__ float hd[2], hdr[2];  // D and the reverse skip weight of the head in each buffer
     __shared__ __attribute__((aligned(16))) __bf16 ybuf[YSTAGE ? UNITS * 16 * YS : 8];
 
     // Workgroups sharing a stream (and so its B, C) go to the same XCD: the hardware
@@ -175,6 +176,8 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
         }
         st.A = a.A[h];
         st.D = a.D[h];
+        st.Ar = a.A_rev[h];
+        st.Dr = a.D_rev ? a.D_rev[h] : 0.f;
     };
 
     auto store_stage = [&](const Stage<SPT, XPT> &st, int buf) {
@@ -225,14 +228,17 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
                 }
             }
         }
-        if (tid == 0)
+        if (tid == 0) {
             hd[buf] = st.D;
+            hdr[buf] = st.Dr;
+        }
         // decay tables: wavefront 0 forward (prefix sums), wavefront 1 reverse (suffix sums);
         // lane l holds tokens 2l and 2l+1, so 16 lanes cover one 32-token pair
         if (wave < 2) {
             const int t0 = 2 * lane, t1 = t0 + 1;
             const float d0 = t0 < T ? bf2f(st.d0) : 0.f, d1 = t1 < T ? bf2f(st.d1) : 0.f;
-            const float a0 = d0 * st.A, a1 = d1 * st.A;
+            const float Aw = wave == 0 ? st.A : st.Ar;  // the reverse scan has its own decay
+            const float a0 = d0 * Aw, a1 = d1 * Aw;
             const float loc = a0 + a1;
             float inc = loc;
 #pragma unroll
@@ -407,7 +413,13 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
             }
         }
         // eq. (13) + D x, written once: the lane holds rows tb*16 + 4q + j of column pc
-        const float Dh = hd[cur];
+        // (+ D_rev x_rev when the reverse direction has its own skip term)
+        const float Dh = hd[cur], Dr = hdr[cur];
+        const bool with_dr = a.D_rev != nullptr;
+        auto skip = [&](int pc, int tr, float v) {
+            v = fmaf(Dh, bf2f(xtf[pc * XS + tr]), v);
+            return with_dr ? fmaf(Dr, bf2f(xtr[pc * XS + tr]), v) : v;
+        };
         Ty *yh = y + h * kP + pgrp * YW;
         if constexpr (YSTAGE) {
             __bf16 *yt = &ybuf[wave * 16 * YS];
@@ -417,8 +429,7 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int tr = tb * 16 + 4 * q + j;
-                    yt[(4 * q + j) * YS + pb * 16 + r16] =
-                        static_cast<__bf16>(fmaf(Dh, bf2f(xtf[pc * XS + tr]), acc[pb][j]));
+                    yt[(4 * q + j) * YS + pb * 16 + r16] = static_cast<__bf16>(skip(pc, tr, acc[pb][j]));
                 }
             }
             // the wavefront reads back its own tile: rows of YW bf16 in 16-byte pieces
@@ -438,7 +449,7 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
                 for (int j = 0; j < 4; ++j) {
                     const int tr = tb * 16 + 4 * q + j;
                     if (tr < T)
-                        store_out(yh + tr * rowX + pb * 16 + r16, fmaf(Dh, bf2f(xtf[pc * XS + tr]), acc[pb][j]));
+                        store_out(yh + tr * rowX + pb * 16 + r16, skip(pc, tr, acc[pb][j]));
                 }
             }
         }

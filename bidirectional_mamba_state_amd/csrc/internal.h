@@ -49,6 +49,8 @@ struct BlockArgs {
     Seq fwd, rev;
     const float *A, *D;
     void *y;
+    const float *A_rev;  // decay of the reverse scan (A when the directions share it)
+    const float *D_rev;  // skip term of the reverse input, or NULL for none
 };
 
 struct PrefixPlan {

@@ -137,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void k_block_step(BlockArgs a)
     const int tid = threadIdx.x, p = tid / L::R, r = tid % L::R;
     const int H = a.s.H, G = a.s.G, g = h / (H / G), T = a.T;
     constexpr int64_t NP = static_cast<int64_t>(N) * P;
-    const float Ah = a.A[h];
+    const float Ah = a.A[h], Ahr = a.A_rev[h];
 
     float S[L::NPT];
     const float *hp = a.h_prefix + (static_cast<int64_t>(b) * H + h) * NP;
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void k_block_step(BlockArgs a)
         for (int t = T - 1; t >= 0; --t) {
             const int64_t tok = static_cast<int64_t>(b) * T + t;
             const float dtv = load_in(dt, tok * H + h);
-            const float alpha = expf(dtv * Ah);
+            const float alpha = expf(dtv * Ahr);
             const float xv = load_in(x, (tok * H + h) * P + p);
             const int64_t bc = (tok * G + g) * N;
             float part = token<Tin, L::R, L::NPT, true>(S, Bm + bc, Cm + bc, alpha, dtv * xv, r);
@@ -185,12 +185,17 @@ __global__ __launch_bounds__(kThreads) void k_block_step(BlockArgs a)
     __syncthreads();
     // eq. (13) plus D x_fwd, written once, coalesced along p
     const Tin *xf = static_cast<const Tin *>(a.fwd.x);
+    const Tin *xr = static_cast<const Tin *>(a.rev.x);
     Ty *y = static_cast<Ty *>(a.y);
     const float Dh = a.D[h];
+    const float Dr = a.D_rev ? a.D_rev[h] : 0.f;
     for (int i = tid; i < T * P; i += kThreads) {
         const int t = i / P, pp = i % P;
         const int64_t o = ((static_cast<int64_t>(b) * T + t) * H + h) * P + pp;
-        store_y(y, o, fmaf(Dh, load_in(xf, o), ybuf[i]));
+        float v = fmaf(Dh, load_in(xf, o), ybuf[i]);
+        if (a.D_rev)
+            v = fmaf(Dr, load_in(xr, o), v);
+        store_y(y, o, v);
     }
 }
 

@@ -140,6 +140,21 @@ bdssm_status bdssm_block_step(const bdssm_dims *dims, int32_t block_len,
                               void *stream);
 
 /*
+ * Block step with separate parameters for the reverse direction (eq. (12) gives the
+ * reverse scan its own parameters): the reverse recurrence decays with A_rev[h] instead of
+ * A[h], and each direction keeps its own skip term,
+ *   y_t = C_t . S_t + C'_t . R_t + D[h] * x_fwd[t] + D_rev[h] * x_rev[t].
+ *   A_rev  [H] float32, required (pass A for a shared decay)
+ *   D_rev  [H] float32, or NULL for no reverse skip term
+ * Everything else as bdssm_block_step, which equals this call with A_rev = A, D_rev = NULL.
+ * y must not overlap A_rev or D_rev either.
+ */
+bdssm_status bdssm_block_step_ex(const bdssm_dims *dims, int32_t block_len,
+                                 const float *h_prefix, const bdssm_seq *fwd,
+                                 const bdssm_seq *rev, const float *A, const float *D,
+                                 const float *A_rev, const float *D_rev, void *y, void *stream);
+
+/*
  * Commit: the clean forward pass over a finalized block of T = block_len tokens that
  * extends the cache, S <- F_fwd(clean; S), in place on h.
  *   clean  the block's clean inputs; clean->C may be NULL when y is NULL

@@ -55,9 +55,12 @@ def _load():
         lib.oracle_block_step.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int64, P,
                                           ctypes.POINTER(_Seq), ctypes.POINTER(_Seq),
                                           P, P, P, P, P, P, ctypes.c_int]
+        lib.oracle_block_step_ex.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int64, P,
+                                             ctypes.POINTER(_Seq), ctypes.POINTER(_Seq),
+                                             P, P, P, P, P, P, P, P, ctypes.c_int]
         lib.oracle_commit.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int64,
                                       ctypes.POINTER(_Seq), P, P, P, P, P, ctypes.c_int]
-        for f in (lib.oracle_scan, lib.oracle_block_step, lib.oracle_commit):
+        for f in (lib.oracle_scan, lib.oracle_block_step, lib.oracle_block_step_ex, lib.oracle_commit):
             f.restype = ctypes.c_int
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -130,8 +133,10 @@ def scan(seq, A, D, chunk, h_init=None, want_y=True, want_chunk_states=True, hea
     return y, cs, h_out
 
 
-def block_step(h_prefix, fwd, rev, A, D, heads=None, nthreads=0):
-    """Block step. Returns (y, y_fwd, y_rev), each [b,T,H,P] float64; y includes D x_fwd."""
+def block_step(h_prefix, fwd, rev, A, D, heads=None, nthreads=0, A_rev=None, D_rev=None):
+    """Block step. Returns (y, y_fwd, y_rev), each [b,T,H,P] float64; y includes D x_fwd.
+    With A_rev and/or D_rev (separate reverse-direction parameters, oracle_block_step_ex)
+    the reverse scan decays with A_rev and y also includes D_rev x_rev."""
     cf, cr = _Call(fwd), _Call(rev)
     b, T, H, P = fwd.x.shape
     G = fwd.B.shape[2]
@@ -142,9 +147,16 @@ def block_step(h_prefix, fwd, rev, A, D, heads=None, nthreads=0):
     A = np.ascontiguousarray(A, np.float32)
     D = np.ascontiguousarray(D, np.float32)
     m = _mask(heads, H)
-    rc = _load().oracle_block_step(ctypes.byref(_dims(fwd, G)), T, _ptr(hp), ctypes.byref(cf.s),
-                                   ctypes.byref(cr.s), _ptr(A), _ptr(D), _ptr(y), _ptr(yf),
-                                   _ptr(yr), _ptr(m), nthreads)
+    if A_rev is None and D_rev is None:
+        rc = _load().oracle_block_step(ctypes.byref(_dims(fwd, G)), T, _ptr(hp), ctypes.byref(cf.s),
+                                       ctypes.byref(cr.s), _ptr(A), _ptr(D), _ptr(y), _ptr(yf),
+                                       _ptr(yr), _ptr(m), nthreads)
+    else:
+        Ar = None if A_rev is None else np.ascontiguousarray(A_rev, np.float32)
+        Dr = None if D_rev is None else np.ascontiguousarray(D_rev, np.float32)
+        rc = _load().oracle_block_step_ex(ctypes.byref(_dims(fwd, G)), T, _ptr(hp), ctypes.byref(cf.s),
+                                          ctypes.byref(cr.s), _ptr(A), _ptr(D), _ptr(Ar), _ptr(Dr),
+                                          _ptr(y), _ptr(yf), _ptr(yr), _ptr(m), nthreads)
     if rc:
         raise ValueError("oracle_block_step rejected its arguments")
     return y, yf, yr

@@ -26,6 +26,10 @@
  *    the active block, started from a zero state at the block's right end, with outputs
  *    in natural token order (eq. 12: rev(F_rev(rev(b)))); their sum (eq. 13) plus the
  *    skip term D[h] * x_fwd of eq. (1), applied once.
+ *  - oracle_block_step_ex: the same with separate parameters for the reverse direction
+ *    (eq. 12 gives the reverse scan its own parameters): the reverse recurrence decays
+ *    with A_rev[h], and D_rev[h] * x_rev is added to y. Reading: each direction is a full
+ *    Mamba-2 scan with its own skip term; the sum of eq. (13) adds both.
  *  - oracle_commit: the "clean forward pass over the new block" that extends the cache
  *    once a block is finalized: the recurrence over the block's clean inputs, updating
  *    the state in place (optionally writing y, with D).
@@ -169,13 +173,14 @@ int oracle_scan(const oracle_dims *d, int64_t len, int64_t chunk, const oracle_s
 
 /* Block step (eqs. 11-13). h_prefix is read only. y = y_fwd + y_rev + D x_fwd.
  * y_fwd and y_rev (without D) are optional extra outputs. */
-int oracle_block_step(const oracle_dims *d, int64_t T, const double *h_prefix,
-                      const oracle_seq *fwd, const oracle_seq *rev, const float *A,
-                      const float *D, double *y, double *y_fwd, double *y_rev,
-                      const int8_t *head_mask, int nthreads)
+int oracle_block_step_ex(const oracle_dims *d, int64_t T, const double *h_prefix,
+                         const oracle_seq *fwd, const oracle_seq *rev, const float *A,
+                         const float *D, const float *A_rev, const float *D_rev, double *y,
+                         double *y_fwd, double *y_rev, const int8_t *head_mask, int nthreads)
 {
     if (check(d) || T < 1 || !h_prefix || !fwd || !rev || !A || !D || !y)
         return 1;
+    const float *Ar = A_rev ? A_rev : A;
     set_threads(nthreads);
     const int H = d->nheads, P = d->headdim, N = d->d_state, G = d->ngroups;
     const int dty = d->in_dtype;
@@ -215,7 +220,7 @@ int oracle_block_step(const oracle_dims *d, int64_t T, const double *h_prefix,
         for (int64_t t = T - 1; t >= 0; --t) {
             const int64_t tok = (int64_t)b * T + t;
             const double dt = val(rev->dt, dty, tok * H + h);
-            const double alpha = exp(dt * A[h]);
+            const double alpha = exp(dt * Ar[h]);
             for (int p = 0; p < P; ++p)
                 xv[p] = val(rev->x, dty, (tok * H + h) * P + p);
             for (int n = 0; n < N; ++n) {
@@ -230,12 +235,15 @@ int oracle_block_step(const oracle_dims *d, int64_t T, const double *h_prefix,
                 yr[t * P + p] = acc;
             }
         }
-        /* eq. (13) plus the skip term of eq. (1), applied once to the forward input */
+        /* eq. (13) plus the skip term of eq. (1), applied once to the forward input, and
+         * the reverse direction's own skip term when it has one */
         for (int64_t t = 0; t < T; ++t) {
             const int64_t tok = (int64_t)b * T + t;
             for (int p = 0; p < P; ++p) {
                 const int64_t o = (tok * H + h) * P + p;
                 y[o] = yf[t * P + p] + yr[t * P + p] + (double)D[h] * val(fwd->x, dty, o);
+                if (D_rev)
+                    y[o] += (double)D_rev[h] * val(rev->x, dty, o);
                 if (y_fwd)
                     y_fwd[o] = yf[t * P + p];
                 if (y_rev)
@@ -248,6 +256,15 @@ int oracle_block_step(const oracle_dims *d, int64_t T, const double *h_prefix,
         free(xv);
     }
     return 0;
+}
+
+int oracle_block_step(const oracle_dims *d, int64_t T, const double *h_prefix,
+                      const oracle_seq *fwd, const oracle_seq *rev, const float *A,
+                      const float *D, double *y, double *y_fwd, double *y_rev,
+                      const int8_t *head_mask, int nthreads)
+{
+    return oracle_block_step_ex(d, T, h_prefix, fwd, rev, A, D, NULL, NULL, y, y_fwd, y_rev,
+                                head_mask, nthreads);
 }
 
 /* Commit: the clean forward pass over a finalized block, advancing h in place.

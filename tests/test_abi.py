@@ -165,3 +165,18 @@ def test_decode_graph_argument_checks():
                   ctypes.byref(out)) == bdssm.ERR_NULL
     assert lib.bdssm_decode_graph_launch(None, None) == bdssm.ERR_NULL
     lib.bdssm_decode_graph_destroy(None)
+
+
+def test_block_step_ex_argument_checks():
+    lib = bdssm.load()
+    d = good()
+    f, r = seq(), seq()
+
+    def call(A_rev=FAKE + 64, D_rev=None, y=FAKE + (1 << 24)):
+        return lib.bdssm_block_step_ex(ctypes.byref(d), 16, FAKE, ctypes.byref(f), ctypes.byref(r),
+                                       FAKE, FAKE, A_rev, D_rev, y, None)
+    assert call(A_rev=None) == bdssm.ERR_NULL          # the reverse decay is required
+    assert call(A_rev=FAKE + 4) == bdssm.ERR_ALIGN
+    assert call(D_rev=FAKE + 8) == bdssm.ERR_ALIGN
+    assert call(A_rev=FAKE + (1 << 24)) == bdssm.ERR_ALIAS   # y on top of A_rev
+    assert call(D_rev=FAKE + (1 << 24)) == bdssm.ERR_ALIAS   # y on top of D_rev

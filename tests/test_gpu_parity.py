@@ -330,3 +330,40 @@ def test_prefix_matrix_core_paths(b, H, G, L, chunk, want_y, want_cs, init):
     if want_y:
         _check_prefix(seq, A, D, chunk, h_init=h0, want_y=True, want_cs=False,
                       y_dtype=bdssm.BF16, label="mfma paths bf16 y")
+
+
+@pytest.mark.parametrize("cfg_index", [0, 1])
+def test_block_step_separate_reverse_params(cfg_index):
+    """bdssm_block_step_ex: the reverse scan with its own decay A_rev and skip weight
+    D_rev, against the oracle; with A_rev = A and no D_rev it is bdssm_block_step."""
+    import torch
+    cfg = configs.get(cfg_index)
+    A, D = inputs.params(cfg)
+    rng = np.random.default_rng(40 + cfg_index)
+    H = cfg.nheads
+    A_rev = (-np.exp(rng.uniform(0, np.log(16), H))).astype(np.float32)
+    D_rev = rng.standard_normal(H).astype(np.float32)
+    pre = inputs.prefix(cfg, length=min(cfg.prefix_len, 512))
+    _, _, h = oracle.scan(pre, A, D, cfg.chunk, want_y=False, want_chunk_states=False)
+    h = f32_round(h)
+    fwd = inputs.block(cfg, 0, 0, inputs.FWD)
+    rev = inputs.block(cfg, 0, 0, inputs.REV)
+    b, T, _, P = fwd.x.shape
+    d = bdssm.dims(b, H, P, cfg.d_state, cfg.ngroups, cfg.in_dtype, bdssm.F32)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+    hd, fd, rd = dev(h), bdssm.seq_to_device(fwd), bdssm.seq_to_device(rev)
+    tol = TOL_BF16 if cfg.in_dtype == 1 else TOL_F32
+    _case(f"block step, separate reverse parameters, config {cfg_index}")
+    for Dv, Drv, what in ((D, D_rev, "y"), (np.zeros_like(D), None, "y - skip terms")):
+        y = torch.empty((b, T, H, P), device="cuda")
+        bdssm.block_step_ex(d, T, hd, fd, rd, dev(A), dev(Dv), dev(A_rev),
+                            None if Drv is None else dev(Drv), y)
+        torch.cuda.synchronize()
+        yo, _, _ = oracle.block_step(h, fwd, rev, A, Dv, A_rev=A_rev, D_rev=Drv)
+        assert within(rel(y.cpu().numpy(), yo), tol, f"block step ex {what}")
+    y1 = torch.empty((b, T, H, P), device="cuda")
+    y2 = torch.empty((b, T, H, P), device="cuda")
+    bdssm.block_step(d, T, hd, fd, rd, dev(A), dev(D), y1)
+    bdssm.block_step_ex(d, T, hd, fd, rd, dev(A), dev(D), dev(A), None, y2)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)

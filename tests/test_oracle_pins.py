@@ -170,6 +170,29 @@ def test_block_step_matches_quadratic_form(G):
     assert np.array_equal(h0, h0_copy)           # the cached state is never written
 
 
+def test_block_step_separate_reverse_params():
+    """Separate reverse-direction parameters: the reverse scan decays with A_rev (quadratic
+    form with A_rev), y gains D_rev x_rev; with A_rev = A and no D_rev the plain step."""
+    rng = np.random.default_rng(12)
+    b, T, H, P, N, G = 2, 24, 4, 3, 5, 2
+    fwd = rand_seq(rng, b, T, H, P, N, G)
+    rev = rand_seq(rng, b, T, H, P, N, G)
+    A, D = rand_params(rng, H)
+    Ar, Dr = rand_params(rng, H)
+    h0 = 0.3 * rng.standard_normal((b, H, N, P))
+    y, yf, yr = oracle.block_step(h0, fwd, rev, A, D, A_rev=Ar, D_rev=Dr)
+    qf, _ = quad_forward(fwd, A, D, h0, with_D=False)
+    qr = quad_reverse(rev, Ar)
+    xf, xr = dec(fwd)[0], dec(rev)[0]
+    expect = qf + qr + np.float64(1) * D[None, None, :, None] * xf + Dr[None, None, :, None] * xr
+    assert rel(yf, qf) < 1e-12
+    assert rel(yr, qr) < 1e-12
+    assert rel(y, expect) < 1e-12
+    y0, _, _ = oracle.block_step(h0, fwd, rev, A, D)
+    y1, _, _ = oracle.block_step(h0, fwd, rev, A, D, A_rev=A)
+    assert np.array_equal(y0, y1)
+
+
 def test_reverse_is_flipped_forward():
     rng = np.random.default_rng(3)
     b, T, H, P, N, G = 1, 20, 2, 4, 3, 1
@@ -296,6 +319,9 @@ PLANTS = {
                           "const int g = h % G;\n    const int dty"),
     "D applied twice in the block step": ("(double)D[h] * val(fwd->x, dty, o);",
                                           "2.0 * (double)D[h] * val(fwd->x, dty, o);"),
+    "reverse scan decays with the forward A": ("exp(dt * Ar[h])", "exp(dt * A[h])"),
+    "reverse skip term on the forward input": ("(double)D_rev[h] * val(rev->x, dty, o)",
+                                               "(double)D_rev[h] * val(fwd->x, dty, o)"),
     "C and B swapped in the forward output": (
         "acc += val(in->C, dty, (tok * G + g) * N + n) * S",
         "acc += val(in->B, dty, (tok * G + g) * N + n) * S"),
@@ -321,7 +347,8 @@ def test_planted_mistake_is_caught(tmp_path, monkeypatch, name):
     monkeypatch.setattr(oracle, "_lib", None)
     failed = []
     for test in (test_golden_hand_worked, lambda: test_scan_matches_quadratic_form(F32, 2),
-                 lambda: test_block_step_matches_quadratic_form(2)):
+                 lambda: test_block_step_matches_quadratic_form(2),
+                 test_block_step_separate_reverse_params):
         try:
             test()
         except AssertionError:
