@@ -19,6 +19,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -45,10 +46,16 @@ def parse():
 
 
 def src_hash():
+    """Hash of the kernel sources with comments and blank lines removed (a comment edit
+    leaves the counters valid; any code change invalidates them)."""
     h = hashlib.sha256()
     cdir = os.path.join(ROOT, "bidirectional_mamba_state_amd", "csrc")
     for f in sorted(os.listdir(cdir)):
-        h.update(open(os.path.join(cdir, f), "rb").read())
+        text = open(os.path.join(cdir, f), encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        lines = [ln.rstrip() for ln in text.splitlines() if ln.strip()]
+        h.update(f.encode() + b"\0" + "\n".join(lines).encode())
     return h.hexdigest()[:16]
 
 

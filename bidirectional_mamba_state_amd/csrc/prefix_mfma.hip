@@ -12,8 +12,10 @@
 //   output:  y_t = exp(c_t) C_t . h_in + sum_{s<=t} exp(c_t - c_s) dt_s (C_t . B_s) x_s + D x_t
 // Outputs are computed transposed (y^T = h^T C^T + X^T M^T) so that a lane holds four
 // consecutive columns of one token. The C B^T scores are shared by the workgroup's heads.
-// B, C and x are staged row-major in LDS; operands whose contraction runs over tokens are
-// read with the gfx950 transposing LDS load (ds_read_b64_tr_b16).
+// B, C and x are staged in LDS in the fragment-major order of mfma_tiles.h (an operand
+// fragment is one contiguous 512-byte read per wavefront); operands whose contraction runs
+// over tokens are read from the same tiles with the gfx950 transposing LDS load
+// (ds_read_b64_tr_b16), which that order keeps free of bank conflicts.
 //
 // Two modes:
 //   STATE  from h_init (or zero): only the state recurrence; writes the segment's end
