@@ -8,7 +8,8 @@ Distributions (every config), following the workload recipe:
   x ~ N(0, 1);  B, C ~ N(0, 1/16);
   dt = softplus(z), z ~ N(-4, 1), computed in float64 and clipped to [1e-3, 0.1]
        (dt is handed over post-softplus: the scan itself applies no softplus or clamp);
-  A_h = -exp(U(0, ln 16)) per head (float32);  D_h ~ N(0, 1) per head (float32).
+  A_h = -exp(U(0, ln 16)) per head (float32);  D_h ~ N(0, 1) per head (float32);
+  convolution weights and bias (when used) ~ U(-1/sqrt(W), 1/sqrt(W)), float32.
 bf16 configs round x, dt, B and C from float64 to bfloat16 with round-to-nearest-even
 and hand over the 16-bit patterns (numpy uint16); fp32 configs round to float32.
 
@@ -82,6 +83,18 @@ def params(cfg: Config):
     A = (-np.exp(u)).astype(np.float32)
     D = _rng(cfg.index, _PARAM_KEY, 1).standard_normal(cfg.nheads).astype(np.float32)
     return A, D
+
+
+def conv_params(cfg: Config, width: int = 4, direction: int = FWD):
+    """Depthwise convolution weights [H*P + 2*G*N, width] and bias [H*P + 2*G*N] of one
+    direction, float32, both U(-1/sqrt(width), 1/sqrt(width)) (a conv layer's usual
+    initialization with fan-in = width)."""
+    ch = cfg.nheads * cfg.headdim + 2 * cfg.ngroups * cfg.d_state
+    bound = 1.0 / np.sqrt(width)
+    g = _rng(cfg.index, _PARAM_KEY, 2 + direction, width)
+    w = g.uniform(-bound, bound, (ch, width)).astype(np.float32)
+    bias = g.uniform(-bound, bound, ch).astype(np.float32)
+    return w, bias
 
 
 @dataclass

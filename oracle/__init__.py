@@ -60,7 +60,11 @@ def _load():
                                              P, P, P, P, P, P, P, P, ctypes.c_int]
         lib.oracle_commit.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int64,
                                       ctypes.POINTER(_Seq), P, P, P, P, P, ctypes.c_int]
-        for f in (lib.oracle_scan, lib.oracle_block_step, lib.oracle_block_step_ex, lib.oracle_commit):
+        lib.oracle_conv.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int64, ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.c_int32, P, P, P,
+                                    ctypes.POINTER(_Seq), ctypes.POINTER(_Seq), P, ctypes.c_int]
+        for f in (lib.oracle_scan, lib.oracle_block_step, lib.oracle_block_step_ex, lib.oracle_commit,
+                  lib.oracle_conv):
             f.restype = ctypes.c_int
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -177,3 +181,67 @@ def commit(h, clean, A, D, want_y=False, heads=None, nthreads=0):
     if rc:
         raise ValueError("oracle_commit rejected its arguments")
     return hn, y
+
+
+class ConvSeq:
+    """A token segment produced by ``conv``: x, dt, B, C arrays of the input dtype."""
+
+    def __init__(self, x, dt, B, C, dtype):
+        self.x, self.dt, self.B, self.C, self.dtype = x, dt, B, C, dtype
+
+    @property
+    def length(self):
+        return self.x.shape[1]
+
+
+def conv_channels(seq):
+    b, _, H, P = seq.x.shape
+    G, N = seq.B.shape[2], seq.B.shape[3]
+    return H * P + 2 * G * N
+
+
+def conv(seq, weight, bias, act, reverse=False, state_in=None, want_state=True, nthreads=0):
+    """Depthwise convolution + activation of the x, B, C channels (oracle_conv).
+
+    weight [CH, W] float32 (CH = H*P + 2*G*N, channels x, B, C), bias [CH] float32 or None,
+    act 0 (identity) or 1 (SiLU), state_in [b, W-1, CH] in the input dtype or None (zero
+    history). Returns (out, state_out): out has the input's dt and the convolved x, B, C
+    rounded to the input dtype; state_out [b, W-1, CH] (forward only, else None)."""
+    c = _Call(seq)
+    b, L, H, P = seq.x.shape
+    G = seq.B.shape[2]
+    CH = conv_channels(seq)
+    weight = np.ascontiguousarray(weight, np.float32)
+    W = weight.shape[1]
+    assert weight.shape == (CH, W)
+    bias = None if bias is None else np.ascontiguousarray(bias, np.float32)
+    dt_np = np.uint16 if seq.dtype == 1 else np.float32
+    out = ConvSeq(np.zeros_like(c.x), c.dt, np.zeros_like(c.B), np.zeros_like(c.C), seq.dtype)
+    o = _Seq(_ptr(out.x), _ptr(out.dt), _ptr(out.B), _ptr(out.C))
+    si = None if state_in is None else _in(state_in, seq.dtype)
+    so = np.zeros((b, W - 1, CH), dtype=dt_np) if (want_state and not reverse) else None
+    rc = _load().oracle_conv(ctypes.byref(_dims(seq, G)), L, W, act, 1 if reverse else 0,
+                             _ptr(weight), _ptr(bias), _ptr(si), ctypes.byref(c.s), ctypes.byref(o),
+                             _ptr(so), nthreads)
+    if rc:
+        raise ValueError("oracle_conv rejected its arguments")
+    return out, so
+
+
+def block_step_conv(h_prefix, conv_state, fwd, rev, conv_fwd, conv_rev, A, D, heads=None,
+                    nthreads=0, A_rev=None, D_rev=None):
+    """Block step on raw (pre-convolution) inputs: the forward branch's x, B, C are
+    convolved causally from the cached conv state, the reverse branch's anti-causally inside
+    the block, then the block step of eqs. (11)-(13). conv_fwd / conv_rev: (weight, bias,
+    act). Returns (y, y_fwd, y_rev)."""
+    pf, _ = conv(fwd, *conv_fwd, reverse=False, state_in=conv_state, want_state=False, nthreads=nthreads)
+    pr, _ = conv(rev, *conv_rev, reverse=True, nthreads=nthreads)
+    return block_step(h_prefix, pf, pr, A, D, heads=heads, nthreads=nthreads, A_rev=A_rev, D_rev=D_rev)
+
+
+def commit_conv(h, conv_state, clean, conv_fwd, A, D, want_y=False, heads=None, nthreads=0):
+    """Commit on raw inputs: convolve the clean block from the conv state, advance the SSM
+    state over it, and advance the conv state. Returns (h_new, conv_state_new, y or None)."""
+    pc, so = conv(clean, *conv_fwd, reverse=False, state_in=conv_state, nthreads=nthreads)
+    hn, y = commit(h, pc, A, D, want_y=want_y, heads=heads, nthreads=nthreads)
+    return hn, so, y

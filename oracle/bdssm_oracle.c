@@ -287,3 +287,111 @@ int oracle_commit(const oracle_dims *d, int64_t T, const oracle_seq *clean, cons
     }
     return 0;
 }
+
+/*
+ * Convolution state (the Mamba cache holds "convolution and selective-SSM state", per the
+ * cache discussion of "Training Hybrid Block Diffusion Language Models with Partial
+ * Bidirectionality"). Reading of what the pages leave open, following the Mamba-2 layer:
+ * before the scan, the x, B and C inputs (channels ordered x [H*P], then B [G*N], then C
+ * [G*N]: per token, the rows of the three arrays) pass through a depthwise convolution of
+ * width W <= 4 with a per-channel bias and then an activation (identity or SiLU). The
+ * result is an activation of the input dtype, so it is rounded to that dtype
+ * (round-to-nearest-even) before the scan reads it. dt is not convolved.
+ *
+ *  forward (causal), from the conv state: out_t = bias + sum_k w[k] u_{t-(W-1)+k}, where
+ *      u_t for t < 0 is row W-1+t of the conv state (the W-1 raw rows before the segment;
+ *      zero when there is none) and the raw input otherwise;
+ *  reverse (anti-causal, inside the block only): out_t = bias + sum_k w[k] u_{t+(W-1)-k}
+ *      with u_t = 0 past the block's end - the causal convolution of the reversed block
+ *      from a zero history, read back in natural order (eq. (12) gives the reverse branch
+ *      no state).
+ * The conv state after a forward segment is its extended input's last W-1 raw rows.
+ *
+ * conv state layout: [b][W-1][H*P + 2*G*N], input dtype. w: [H*P + 2*G*N][W] float32,
+ * bias: [H*P + 2*G*N] float32 or NULL. act: 0 identity, 1 SiLU (v / (1 + exp(-v))).
+ */
+static void put(void *p, int dtype, int64_t i, double v)
+{
+    if (dtype == 0) {
+        ((float *)p)[i] = (float)v;
+        return;
+    }
+    /* bfloat16: 8 significant bits, ties to even, straight from float64 */
+    double r = v;
+    if (v != 0.0 && isfinite(v)) {
+        int e;
+        frexp(v, &e);
+        int qe = e - 8;
+        if (qe < -133)
+            qe = -133; /* bfloat16 subnormal quantum */
+        r = ldexp(nearbyint(ldexp(v, -qe)), qe);
+    }
+    const float f = (float)r; /* exact */
+    uint32_t bits;
+    memcpy(&bits, &f, sizeof bits);
+    ((uint16_t *)p)[i] = (uint16_t)(bits >> 16);
+}
+
+/* channel c of token row `tok` of a sequence (x, then B, then C) */
+static double chan(const oracle_dims *d, const oracle_seq *s, int64_t tok, int64_t c)
+{
+    const int64_t HP = (int64_t)d->nheads * d->headdim, GN = (int64_t)d->ngroups * d->d_state;
+    if (c < HP)
+        return val(s->x, d->in_dtype, tok * HP + c);
+    if (c < HP + GN)
+        return val(s->B, d->in_dtype, tok * GN + (c - HP));
+    return val(s->C, d->in_dtype, tok * GN + (c - HP - GN));
+}
+
+static void put_chan(const oracle_dims *d, const oracle_seq *s, int64_t tok, int64_t c, double v)
+{
+    const int64_t HP = (int64_t)d->nheads * d->headdim, GN = (int64_t)d->ngroups * d->d_state;
+    if (c < HP)
+        put((void *)s->x, d->in_dtype, tok * HP + c, v);
+    else if (c < HP + GN)
+        put((void *)s->B, d->in_dtype, tok * GN + (c - HP), v);
+    else
+        put((void *)s->C, d->in_dtype, tok * GN + (c - HP - GN), v);
+}
+
+int oracle_conv(const oracle_dims *d, int64_t len, int32_t width, int32_t act, int32_t reverse,
+                const float *w, const float *bias, const void *state_in, const oracle_seq *raw,
+                const oracle_seq *out, void *state_out, int nthreads)
+{
+    if (check(d) || len < 1 || width < 1 || width > 4 || (act != 0 && act != 1) || !w || !raw ||
+        !out || (reverse && (state_in || state_out)))
+        return 1;
+    set_threads(nthreads);
+    const int dty = d->in_dtype;
+    const int64_t CH = (int64_t)d->nheads * d->headdim + 2 * (int64_t)d->ngroups * d->d_state;
+    const int64_t total = (int64_t)d->batch * CH;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < total; ++i) {
+        const int64_t b = i / CH, c = i % CH;
+        /* the raw input extended by W-1 rows of history (forward) or of zeros (reverse) */
+        double *u = malloc(sizeof(double) * (size_t)(len + width - 1));
+        for (int k = 0; k < width - 1; ++k) {
+            const int64_t hist = reverse ? len + width - 1 - 1 - k : k;
+            u[hist] = (!reverse && state_in) ? val(state_in, dty, (b * (width - 1) + k) * CH + c) : 0.0;
+        }
+        const int64_t off = reverse ? 0 : width - 1;
+        for (int64_t t = 0; t < len; ++t)
+            u[off + t] = chan(d, raw, b * len + t, c);
+        for (int64_t t = 0; t < len; ++t) {
+            double v = bias ? (double)bias[c] : 0.0;
+            for (int k = 0; k < width; ++k) {
+                /* forward: u_{t-(W-1)+k} sits at index t+k; reverse: u_{t+(W-1)-k} at t+W-1-k */
+                const int64_t at = reverse ? t + width - 1 - k : t + k;
+                v += (double)w[c * width + k] * u[at];
+            }
+            if (act == 1)
+                v = v / (1.0 + exp(-v));
+            put_chan(d, out, b * len + t, c, v);
+        }
+        if (state_out)
+            for (int k = 0; k < width - 1; ++k)
+                put(state_out, dty, (b * (width - 1) + k) * CH + c, u[len + k]);
+        free(u);
+    }
+    return 0;
+}

@@ -310,6 +310,174 @@ def test_head_subset_matches_full():
 
 
 # ------------------------------------------------------------ planted mistakes
+
+# ---------------------------------------------------------------- convolution state
+def raw_channels(seq):
+    """[b, L, CH] float64 view of a segment's x, B, C channels (x, then B, then C)."""
+    x, _, B, C = dec(seq)
+    b, L = x.shape[:2]
+    return np.concatenate([x.reshape(b, L, -1), B.reshape(b, L, -1), C.reshape(b, L, -1)], axis=2)
+
+
+def conv_reference(u, w, bias, act, reverse, hist=None):
+    """Depthwise convolution by shifted slices of a padded array (numpy), then the
+    activation (SiLU via scipy's logistic function); float64, not rounded."""
+    from scipy.special import expit
+    b, L, CH = u.shape
+    W = w.shape[1]
+    pad = np.zeros((b, W - 1, CH)) if hist is None else hist
+    ext = np.concatenate([u, pad], axis=1) if reverse else np.concatenate([pad, u], axis=1)
+    out = np.zeros((b, L, CH)) + (0.0 if bias is None else bias.astype(np.float64))
+    for k in range(W):
+        # forward: w[k] meets u_{t-(W-1)+k}; reverse: w[k] meets u_{t+(W-1)-k}
+        sl = ext[:, W - 1 - k:W - 1 - k + L] if reverse else ext[:, k:k + L]
+        out = out + w[:, k].astype(np.float64) * sl
+    return out * expit(out) if act == 1 else out
+
+
+def rounded(v, dtype):
+    return bf16_bits_to_f32(round_bf16_bits(v)).astype(np.float64) if dtype == BF16 else \
+        v.astype(np.float32).astype(np.float64)
+
+
+def conv_weights(rng, CH, W):
+    bound = 1.0 / np.sqrt(W)
+    return (rng.uniform(-bound, bound, (CH, W)).astype(np.float32),
+            rng.uniform(-bound, bound, CH).astype(np.float32))
+
+
+def state_f64(a, dtype):
+    return bf16_bits_to_f32(a).astype(np.float64) if dtype == BF16 else np.asarray(a, np.float64)
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("reverse", [False, True])
+def test_conv_matches_shifted_slices(dtype, reverse):
+    """oracle_conv == the convolution written as shifted slices of a padded array, with a
+    conv-state history (forward) or zeros past the block's end (reverse), SiLU, rounded
+    to the input dtype; the new conv state is the extended input's last W-1 raw rows."""
+    rng = np.random.default_rng(21)
+    b, L, H, P, N, G, W = 2, 13, 4, 3, 5, 2, 4
+    seq = rand_seq(rng, b, L, H, P, N, G, dtype)
+    CH = H * P + 2 * G * N
+    w, bias = conv_weights(rng, CH, W)
+    hist_raw = rng.standard_normal((b, W - 1, CH))
+    hist = round_bf16_bits(hist_raw) if dtype == BF16 else hist_raw.astype(np.float32)
+    out, so = oracle.conv(seq, w, bias, 1, reverse=reverse, state_in=None if reverse else hist)
+    u = raw_channels(seq)
+    ref = conv_reference(u, w, bias, 1, reverse, None if reverse else state_f64(hist, dtype))
+    got = raw_channels(out)
+    want = rounded(ref, dtype)
+    # the activation's exp may differ by an ulp between libm and scipy: at most one output
+    # ulp apart, and almost always equal
+    ulp = 2.0 ** -7 if dtype == BF16 else 2.0 ** -23
+    assert np.all(np.abs(got - want) <= ulp * np.abs(want) + 1e-300)
+    assert np.mean(got != want) < 1e-3
+    assert np.array_equal(out.dt, seq.dt)            # dt is not convolved
+    if reverse:
+        assert so is None
+    else:
+        ext = np.concatenate([state_f64(hist, dtype), u], axis=1)
+        assert np.array_equal(state_f64(so, dtype), ext[:, -(W - 1):])
+
+
+def test_conv_identity_shift_and_flip():
+    rng = np.random.default_rng(22)
+    b, L, H, P, N, G = 1, 9, 2, 4, 3, 1
+    seq = rand_seq(rng, b, L, H, P, N, G, BF16)
+    CH = H * P + 2 * G * N
+    # width 1, weight 1, no bias, identity: the raw input, bit for bit
+    out, so = oracle.conv(seq, np.ones((CH, 1), np.float32), None, 0)
+    for a, r in zip((out.x, out.B, out.C), (seq.x, seq.B, seq.C)):
+        assert np.array_equal(a, r)
+    assert so.shape == (b, 0, CH)
+    # a unit tap on the oldest position delays by W-1 tokens, reading the conv state first
+    W = 4
+    w = np.zeros((CH, W), np.float32)
+    w[:, 0] = 1.0
+    hist = round_bf16_bits(rng.standard_normal((b, W - 1, CH)))
+    out, _ = oracle.conv(seq, w, None, 0, state_in=hist)
+    ext = np.concatenate([state_f64(hist, BF16), raw_channels(seq)], axis=1)
+    assert np.array_equal(raw_channels(out), ext[:, :L])
+    # reverse: the same tap reads W-1 tokens ahead, zero past the end
+    out, _ = oracle.conv(seq, w, None, 0, reverse=True)
+    u = raw_channels(seq)
+    assert np.array_equal(raw_channels(out)[:, :L - 3], u[:, 3:])
+    assert np.all(raw_channels(out)[:, L - 3:] == 0)
+    # reverse == flip . forward from a zero history . flip
+    w, bias = conv_weights(rng, CH, W)
+    fl = Seq(*(np.ascontiguousarray(a[:, ::-1]) for a in (seq.x, seq.dt, seq.B, seq.C)), BF16)
+    o_r, _ = oracle.conv(seq, w, bias, 1, reverse=True)
+    o_f, _ = oracle.conv(fl, w, bias, 1, state_in=None)
+    assert np.array_equal(raw_channels(o_r), raw_channels(o_f)[:, ::-1])
+
+
+def test_conv_state_chains_and_silu_values():
+    rng = np.random.default_rng(23)
+    b, H, P, N, G, W = 2, 2, 4, 3, 1, 4
+    U = rand_seq(rng, b, 7, H, P, N, G, BF16)
+    V = rand_seq(rng, b, 2, H, P, N, G, BF16)   # shorter than the history
+    X = rand_seq(rng, b, 5, H, P, N, G, BF16)
+    CH = H * P + 2 * G * N
+    w, bias = conv_weights(rng, CH, W)
+    cat = Seq(*(np.concatenate(z, axis=1) for z in zip((U.x, U.dt, U.B, U.C), (V.x, V.dt, V.B, V.C),
+                                                        (X.x, X.dt, X.B, X.C))), BF16)
+    full, s_full = oracle.conv(cat, w, bias, 1)
+    s = None
+    outs = []
+    for piece in (U, V, X):
+        o, s = oracle.conv(piece, w, bias, 1, state_in=s)
+        outs.append(raw_channels(o))
+    assert np.array_equal(np.concatenate(outs, axis=1), raw_channels(full))
+    assert np.array_equal(s, s_full)
+    # SiLU closed form: width 1, unit weight, no bias
+    vals = np.array([-4.0, -1.0, -0.25, 0.0, 0.5, 1.0, 3.0], np.float32)
+    one = Seq(vals.reshape(1, 7, 1, 1), np.full((1, 7, 1), 0.01, np.float32),
+              np.zeros((1, 7, 1, 1), np.float32), np.zeros((1, 7, 1, 1), np.float32), F32)
+    o, _ = oracle.conv(one, np.ones((3, 1), np.float32), None, 1)
+    want = np.array([float(v) / (1.0 + np.exp(-float(v))) for v in vals]).astype(np.float32)
+    assert np.array_equal(o.x.ravel(), want)
+    assert o.x.ravel()[3] == 0.0
+
+
+def test_block_step_and_commit_with_conv():
+    """With a width-1 identity convolution the conv variants are the plain calls; with a
+    real one they are the plain calls on the convolved inputs, and the commit's conv state
+    is the block's last W-1 raw rows."""
+    rng = np.random.default_rng(24)
+    b, T, H, P, N, G = 2, 12, 4, 3, 5, 2
+    fwd = rand_seq(rng, b, T, H, P, N, G)
+    rev = rand_seq(rng, b, T, H, P, N, G)
+    A, D = rand_params(rng, H)
+    h0 = 0.3 * rng.standard_normal((b, H, N, P))
+    CH = H * P + 2 * G * N
+    ident = (np.ones((CH, 1), np.float32), None, 0)
+    y0 = oracle.block_step(h0, fwd, rev, A, D)[0]
+    y1 = oracle.block_step_conv(h0, np.zeros((b, 0, CH), np.float32), fwd, rev, ident, ident, A, D)[0]
+    assert np.array_equal(y0, y1)
+    W = 4
+    cf, cr = conv_weights(rng, CH, W), conv_weights(rng, CH, W)
+    hist = rng.standard_normal((b, W - 1, CH)).astype(np.float32)
+    y, _, _ = oracle.block_step_conv(h0, hist, fwd, rev, cf + (1,), cr + (1,), A, D)
+    # the quadratic form on inputs convolved by the numpy reference
+    def convolved(seq, wb, reverse, hs):
+        v = conv_reference(raw_channels(seq), wb[0], wb[1], 1, reverse, hs)
+        v = v.astype(np.float32)
+        HP, GN = H * P, G * N
+        return Seq(v[..., :HP].reshape(b, T, H, P).copy(), seq.dt, v[..., HP:HP + GN].reshape(b, T, G, N).copy(),
+                   v[..., HP + GN:].reshape(b, T, G, N).copy(), F32)
+    pf = convolved(fwd, cf, False, hist.astype(np.float64))
+    pr = convolved(rev, cr, True, None)
+    qf, _ = quad_forward(pf, A, D, h0, with_D=False)
+    qr = quad_reverse(pr, A)
+    expect = qf + qr + D[None, None, :, None] * dec(pf)[0]
+    assert rel(y, expect) < 1e-6                      # float32 rounding of the convolved inputs
+    hn, s_new, _ = oracle.commit_conv(h0, hist, fwd, cf + (1,), A, D)
+    assert np.array_equal(s_new, raw_channels(fwd)[:, -(W - 1):].astype(np.float32))
+    _, _, h_ref = oracle.scan(pf, A, D, chunk=T, h_init=h0)
+    assert rel(hn, h_ref) < 1e-12
+
+
 PLANTS = {
     "dropped dt on the input term": ("const double w = dt * val(in->B", "const double w = val(in->B"),
     "decay applied after the input": ("row[p] = alpha * row[p] + w * xv[p];",
@@ -325,6 +493,13 @@ PLANTS = {
     "C and B swapped in the forward output": (
         "acc += val(in->C, dty, (tok * G + g) * N + n) * S",
         "acc += val(in->B, dty, (tok * G + g) * N + n) * S"),
+    "forward convolution taps reversed": ("const int64_t at = reverse ? t + width - 1 - k : t + k;",
+                                          "const int64_t at = reverse ? t + width - 1 - k : t + width - 1 - k;"),
+    "reverse convolution reads causally": ("const int64_t at = reverse ? t + width - 1 - k : t + k;",
+                                           "const int64_t at = t + k;"),
+    "conv state ignored": ("(!reverse && state_in) ?", "(0 && state_in) ?"),
+    "conv state not advanced": ("u[len + k]);", "u[k]);"),
+    "activation dropped": ("v = v / (1.0 + exp(-v));", "v = v * 1.0;"),
 }
 
 
@@ -348,7 +523,11 @@ def test_planted_mistake_is_caught(tmp_path, monkeypatch, name):
     failed = []
     for test in (test_golden_hand_worked, lambda: test_scan_matches_quadratic_form(F32, 2),
                  lambda: test_block_step_matches_quadratic_form(2),
-                 test_block_step_separate_reverse_params):
+                 test_block_step_separate_reverse_params,
+                 lambda: test_conv_matches_shifted_slices(BF16, False),
+                 lambda: test_conv_matches_shifted_slices(F32, True),
+                 test_conv_identity_shift_and_flip, test_conv_state_chains_and_silu_values,
+                 test_block_step_and_commit_with_conv):
         try:
             test()
         except AssertionError:
