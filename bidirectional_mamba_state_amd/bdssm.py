@@ -20,7 +20,8 @@ F32, BF16 = 0, 1
 EXPORTS = ("bdssm_abi_version", "bdssm_status_str", "bdssm_prefix_scan_workspace",
            "bdssm_prefix_scan", "bdssm_block_step", "bdssm_block_step_ex", "bdssm_commit",
            "bdssm_decode_graph_create",
-           "bdssm_decode_graph_launch", "bdssm_decode_graph_destroy")
+           "bdssm_decode_graph_launch", "bdssm_decode_graph_destroy",
+           "bdssm_conv_workspace", "bdssm_conv", "bdssm_block_step_conv", "bdssm_commit_conv")
 
 
 class BdssmError(RuntimeError):
@@ -39,6 +40,11 @@ class Dims(ctypes.Structure):
 class SeqPtrs(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("dt", ctypes.c_void_p),
                 ("B", ctypes.c_void_p), ("C", ctypes.c_void_p)]
+
+
+class ConvParams(ctypes.Structure):
+    _fields_ = [("width", ctypes.c_int32), ("activation", ctypes.c_int32),
+                ("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p)]
 
 
 _lib = None
@@ -73,6 +79,16 @@ def load():
         lib.bdssm_decode_graph_launch.argtypes = [V, V]
         lib.bdssm_decode_graph_destroy.restype = None
         lib.bdssm_decode_graph_destroy.argtypes = [V]
+        lib.bdssm_conv_workspace.restype = SZ
+        lib.bdssm_conv_workspace.argtypes = [P(Dims), I64]
+        lib.bdssm_conv.restype = ctypes.c_int
+        lib.bdssm_conv.argtypes = [P(Dims), I64, P(ConvParams), I32, V, P(SeqPtrs), P(SeqPtrs), V, V]
+        lib.bdssm_block_step_conv.restype = ctypes.c_int
+        lib.bdssm_block_step_conv.argtypes = [P(Dims), I32, P(ConvParams), P(ConvParams), V, V,
+                                              P(SeqPtrs), P(SeqPtrs), V, V, V, V, V, V, SZ, V]
+        lib.bdssm_commit_conv.restype = ctypes.c_int
+        lib.bdssm_commit_conv.argtypes = [P(Dims), I32, P(ConvParams), P(SeqPtrs), V, V, V, V, V,
+                                          V, SZ, V]
         _lib = lib
     return _lib
 
@@ -162,6 +178,43 @@ def commit(d, block_len, clean, A, D, h, y=None, stream=None):
     """bdssm_commit. clean = (x, dt, B, C) tensors (C may be None when y is None)."""
     _check(load().bdssm_commit(ctypes.byref(d), block_len, _byref(_seq(clean)), _ptr(A), _ptr(D),
                                _ptr(h), _ptr(y), _stream(stream)))
+
+
+def conv_params(weight, bias, activation, width=None):
+    """A bdssm_conv_params for weight [CH, W] and bias [CH] (or None) device tensors."""
+    w = int(weight.shape[1]) if width is None else width
+    return ConvParams(w, activation, _ptr(weight), _ptr(bias))
+
+
+def conv_workspace(d, length):
+    return load().bdssm_conv_workspace(ctypes.byref(d), length)
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def conv(d, length, params, reverse, state_in, raw, out, state_out, stream=None):
+    """bdssm_conv. raw, out = (x, dt, B, C) tensors (dt unused, may be None)."""
+    _check(load().bdssm_conv(ctypes.byref(d), length, ctypes.byref(params), int(reverse), _ptr(state_in),
+                             _byref(_seq(raw)), _byref(_seq(out)), _ptr(state_out), _stream(stream)))
+
+
+def block_step_conv(d, block_len, conv_fwd, conv_rev, h_prefix, conv_state, fwd, rev, A, D, y,
+                    workspace, A_rev=None, D_rev=None, stream=None):
+    """bdssm_block_step_conv: fwd, rev are raw (unconvolved) inputs."""
+    _check(load().bdssm_block_step_conv(ctypes.byref(d), block_len, ctypes.byref(conv_fwd),
+                                        ctypes.byref(conv_rev), _ptr(h_prefix), _ptr(conv_state),
+                                        _byref(_seq(fwd)), _byref(_seq(rev)), _ptr(A), _ptr(D),
+                                        _ptr(A_rev), _ptr(D_rev), _ptr(y), _ptr(workspace),
+                                        _nbytes(workspace), _stream(stream)))
+
+
+def commit_conv(d, block_len, params, clean, A, D, h, conv_state, workspace, y=None, stream=None):
+    """bdssm_commit_conv: advances h and the conv state in place over raw clean inputs."""
+    _check(load().bdssm_commit_conv(ctypes.byref(d), block_len, ctypes.byref(params), _byref(_seq(clean)),
+                                    _ptr(A), _ptr(D), _ptr(h), _ptr(conv_state), _ptr(y), _ptr(workspace),
+                                    _nbytes(workspace), _stream(stream)))
 
 
 class DecodeGraph:

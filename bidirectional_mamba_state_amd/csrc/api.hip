@@ -153,6 +153,150 @@ void override_block_plan(const Shape &s, int *hpw, int *ps)
     }
 }
 
+// Validates a block step and fills its kernel arguments (nothing is launched).
+bdssm_status prepare_block_step(const bdssm_dims *dims, int32_t block_len, const float *h_prefix,
+                                const bdssm_seq *fwd, const bdssm_seq *rev, const float *A,
+                                const float *D, const float *A_rev, const float *D_rev, void *y,
+                                BlockArgs *out)
+{
+    Shape s;
+    bdssm_status rc = check_dims(dims, &s);
+    if (rc != BDSSM_OK)
+        return rc;
+    if (block_len < 0)
+        return BDSSM_ERR_SHAPE;
+    if (block_len > 256)
+        return BDSSM_ERR_UNSUPPORTED;
+    if (!h_prefix || !A || !D || !A_rev || !y)
+        return BDSSM_ERR_NULL;
+    SeqRanges qf{}, qr{};
+    if ((rc = check_seq(fwd, s, block_len, true, &qf)) != BDSSM_OK)
+        return rc;
+    if ((rc = check_seq(rev, s, block_len, true, &qr)) != BDSSM_OK)
+        return rc;
+    if (!aligned(h_prefix) || !aligned(A) || !aligned(D) || !aligned(A_rev) || !aligned(D_rev) ||
+        !aligned(y))
+        return BDSSM_ERR_ALIGN;
+    const int64_t NP = static_cast<int64_t>(s.N) * s.P;
+    const Range ry = rng(y, static_cast<int64_t>(s.b) * block_len * s.H * s.P * elt(s.y_dt));
+    if (hits(ry, qf) || hits(ry, qr) || overlap(ry, rng(h_prefix, static_cast<int64_t>(s.b) * s.H * NP * 4)) ||
+        overlap(ry, rng(A, s.H * 4)) || overlap(ry, rng(D, s.H * 4)) || overlap(ry, rng(A_rev, s.H * 4)) ||
+        overlap(ry, rng(D_rev, s.H * 4)))
+        return BDSSM_ERR_ALIAS;
+    *out = BlockArgs{s, block_len, h_prefix, Seq{fwd->x, fwd->dt, fwd->B, fwd->C},
+                     Seq{rev->x, rev->dt, rev->B, rev->C}, A, D, y, A_rev, D_rev};
+    return BDSSM_OK;
+}
+
+bdssm_status launch_block_step(const BlockArgs &a, hipStream_t st)
+{
+    if (block_mfma_supported(a.s, a.T)) {
+        int hpw, ps;
+        block_mfma_plan(a.s, &hpw, &ps);
+        override_block_plan(a.s, &hpw, &ps);
+        return launched(launch_block_step_mfma(a, hpw, ps, st));
+    }
+    return launched(launch_block_step_valu(a, st));
+}
+
+// Validates a commit (nothing is launched).
+bdssm_status prepare_commit(const bdssm_dims *dims, int32_t block_len, const bdssm_seq *clean,
+                            const float *A, const float *D, float *h, void *y, Shape *out)
+{
+    Shape s;
+    bdssm_status rc = check_dims(dims, &s);
+    if (rc != BDSSM_OK)
+        return rc;
+    if (block_len < 0)
+        return BDSSM_ERR_SHAPE;
+    if (block_len > 256)
+        return BDSSM_ERR_UNSUPPORTED;
+    if (!A || !D || !h)
+        return BDSSM_ERR_NULL;
+    SeqRanges q{};
+    if ((rc = check_seq(clean, s, block_len, y != nullptr, &q)) != BDSSM_OK)
+        return rc;
+    if (!aligned(A) || !aligned(D) || !aligned(h) || !aligned(y))
+        return BDSSM_ERR_ALIGN;
+    const int64_t NP = static_cast<int64_t>(s.N) * s.P;
+    const Range rh = rng(h, static_cast<int64_t>(s.b) * s.H * NP * 4);
+    const Range ry = rng(y, static_cast<int64_t>(s.b) * block_len * s.H * s.P * elt(s.y_dt));
+    for (Range o : {rh, ry}) {
+        if (hits(o, q) || overlap(o, rng(A, s.H * 4)) || overlap(o, rng(D, s.H * 4)))
+            return BDSSM_ERR_ALIAS;
+    }
+    if (overlap(rh, ry))
+        return BDSSM_ERR_ALIAS;
+    *out = s;
+    return BDSSM_OK;
+}
+
+bdssm_status launch_commit(const Shape &s, int32_t block_len, const Seq &seq, const float *A, const float *D,
+                           float *h, void *y, hipStream_t st)
+{
+    // a commit is a prefix scan of the block from h, in place: on the matrix-core prefix
+    // path, one segment per (stream, head) (no workspace)
+    if (prefix_mfma_supported(s, 64))
+        return launched(run_prefix_mfma(s, block_len, 64, seq, A, D, h, y, nullptr, h, nullptr, st, true));
+    ForwardArgs f{s, block_len, block_len, 1, seq, A, D, h, nullptr, y, h, nullptr};
+    return launched(launch_forward_valu(f, st));
+}
+
+// ---- convolution state
+struct ConvRanges {
+    Range w, b;
+};
+
+bdssm_status check_conv(const bdssm_conv_params *c, const Shape &s, ConvRanges *out)
+{
+    if (!c || !c->weight)
+        return BDSSM_ERR_NULL;
+    if (c->width < 1 || c->width > 4 || (c->activation != 0 && c->activation != 1))
+        return BDSSM_ERR_UNSUPPORTED;
+    if ((s.H * s.P) % 8 != 0 || (s.G * s.N) % 8 != 0)
+        return BDSSM_ERR_UNSUPPORTED;
+    if (!aligned(c->weight) || !aligned(c->bias))
+        return BDSSM_ERR_ALIGN;
+    const int64_t ch = static_cast<int64_t>(s.H) * s.P + 2 * static_cast<int64_t>(s.G) * s.N;
+    out->w = rng(c->weight, ch * c->width * 4);
+    out->b = rng(c->bias, ch * 4);
+    return BDSSM_OK;
+}
+
+int64_t conv_state_bytes(const Shape &s, int width)
+{
+    const int64_t ch = static_cast<int64_t>(s.H) * s.P + 2 * static_cast<int64_t>(s.G) * s.N;
+    return static_cast<int64_t>(s.b) * (width - 1) * ch * elt(s.in_dt);
+}
+
+// x, B and C of a segment (dt not needed) with their byte ranges
+bdssm_status check_xbc(const bdssm_seq *q, const Shape &s, int64_t len, SeqRanges *out)
+{
+    if (!q || !q->x || !q->B || !q->C)
+        return BDSSM_ERR_NULL;
+    if (!aligned(q->x) || !aligned(q->B) || !aligned(q->C))
+        return BDSSM_ERR_ALIGN;
+    const int64_t e = elt(s.in_dt), tok = static_cast<int64_t>(s.b) * len;
+    out->x = rng(q->x, tok * s.H * s.P * e);
+    out->dt = rng(nullptr, 0);
+    out->B = rng(q->B, tok * s.G * s.N * e);
+    out->C = rng(q->C, tok * s.G * s.N * e);
+    return BDSSM_OK;
+}
+
+// one convolved copy of x, B, C in a workspace: offsets of B and C, total bytes
+struct ConvCopy {
+    size_t B, C, total;
+};
+
+ConvCopy conv_copy_bytes(const Shape &s, int64_t len)
+{
+    auto r256 = [](int64_t v) { return static_cast<size_t>((v + 255) / 256 * 256); };
+    const int64_t e = elt(s.in_dt), tok = static_cast<int64_t>(s.b) * len;
+    const size_t xb = r256(tok * s.H * s.P * e), bb = r256(tok * s.G * s.N * e);
+    return ConvCopy{xb, xb + bb, xb + 2 * bb};
+}
+
 }  // namespace
 
 extern "C" {
@@ -314,45 +458,90 @@ bdssm_status bdssm_block_step_ex(const bdssm_dims *dims, int32_t block_len,
                                  const bdssm_seq *rev, const float *A, const float *D,
                                  const float *A_rev, const float *D_rev, void *y, void *stream)
 {
-    Shape s;
-    bdssm_status rc = check_dims(dims, &s);
-    if (rc != BDSSM_OK)
+    BlockArgs a{};
+    const bdssm_status rc = prepare_block_step(dims, block_len, h_prefix, fwd, rev, A, D, A_rev, D_rev, y, &a);
+    if (rc != BDSSM_OK || a.s.b == 0 || block_len == 0)
         return rc;
-    if (block_len < 0)
-        return BDSSM_ERR_SHAPE;
-    if (block_len > 256)
-        return BDSSM_ERR_UNSUPPORTED;
-    if (!h_prefix || !A || !D || !A_rev || !y)
-        return BDSSM_ERR_NULL;
-    SeqRanges qf{}, qr{};
-    if ((rc = check_seq(fwd, s, block_len, true, &qf)) != BDSSM_OK)
-        return rc;
-    if ((rc = check_seq(rev, s, block_len, true, &qr)) != BDSSM_OK)
-        return rc;
-    if (!aligned(h_prefix) || !aligned(A) || !aligned(D) || !aligned(A_rev) || !aligned(D_rev) ||
-        !aligned(y))
-        return BDSSM_ERR_ALIGN;
-    const int64_t NP = static_cast<int64_t>(s.N) * s.P;
-    const Range ry = rng(y, static_cast<int64_t>(s.b) * block_len * s.H * s.P * elt(s.y_dt));
-    if (hits(ry, qf) || hits(ry, qr) || overlap(ry, rng(h_prefix, static_cast<int64_t>(s.b) * s.H * NP * 4)) ||
-        overlap(ry, rng(A, s.H * 4)) || overlap(ry, rng(D, s.H * 4)) || overlap(ry, rng(A_rev, s.H * 4)) ||
-        overlap(ry, rng(D_rev, s.H * 4)))
-        return BDSSM_ERR_ALIAS;
-    if (s.b == 0 || block_len == 0)
-        return BDSSM_OK;
-    BlockArgs a{s, block_len, h_prefix, Seq{fwd->x, fwd->dt, fwd->B, fwd->C},
-                Seq{rev->x, rev->dt, rev->B, rev->C}, A, D, y, A_rev, D_rev};
-    if (block_mfma_supported(s, block_len)) {
-        int hpw, ps;
-        block_mfma_plan(s, &hpw, &ps);
-        override_block_plan(s, &hpw, &ps);
-        return launched(launch_block_step_mfma(a, hpw, ps, static_cast<hipStream_t>(stream)));
-    }
-    return launched(launch_block_step_valu(a, static_cast<hipStream_t>(stream)));
+    return launch_block_step(a, static_cast<hipStream_t>(stream));
 }
 
 bdssm_status bdssm_commit(const bdssm_dims *dims, int32_t block_len, const bdssm_seq *clean,
                           const float *A, const float *D, float *h, void *y, void *stream)
+{
+    Shape s;
+    const bdssm_status rc = prepare_commit(dims, block_len, clean, A, D, h, y, &s);
+    if (rc != BDSSM_OK || s.b == 0 || block_len == 0)
+        return rc;
+    return launch_commit(s, block_len, Seq{clean->x, clean->dt, clean->B, clean->C}, A, D, h, y,
+                         static_cast<hipStream_t>(stream));
+}
+
+size_t bdssm_conv_workspace(const bdssm_dims *dims, int64_t len)
+{
+    Shape s;
+    if (check_dims(dims, &s) != BDSSM_OK || len < 0)
+        return SIZE_MAX;
+    return conv_copy_bytes(s, len).total;
+}
+
+bdssm_status bdssm_conv(const bdssm_dims *dims, int64_t len, const bdssm_conv_params *conv,
+                        int32_t reverse, const void *state_in, const bdssm_seq *raw,
+                        const bdssm_seq *out, void *state_out, void *stream)
+{
+    Shape s;
+    bdssm_status rc = check_dims(dims, &s);
+    if (rc != BDSSM_OK)
+        return rc;
+    if (len < 0 || (reverse != 0 && reverse != 1))
+        return BDSSM_ERR_SHAPE;
+    if (reverse && (state_in || state_out))
+        return BDSSM_ERR_SHAPE;
+    ConvRanges cr{};
+    if ((rc = check_conv(conv, s, &cr)) != BDSSM_OK)
+        return rc;
+    SeqRanges qr{}, qo{};
+    if ((rc = check_xbc(raw, s, len, &qr)) != BDSSM_OK || (rc = check_xbc(out, s, len, &qo)) != BDSSM_OK)
+        return rc;
+    if (!aligned(state_in) || !aligned(state_out))
+        return BDSSM_ERR_ALIGN;
+    const int64_t sb = conv_state_bytes(s, conv->width);
+    const Range rsi = rng(state_in, sb), rso = rng(state_out, sb);
+    if (overlap(qo.x, qo.B) || overlap(qo.x, qo.C) || overlap(qo.B, qo.C))
+        return BDSSM_ERR_ALIAS;
+    for (Range o : {qo.x, qo.B, qo.C}) {
+        if (hits(o, qr) || overlap(o, cr.w) || overlap(o, cr.b) || overlap(o, rsi) || overlap(o, rso))
+            return BDSSM_ERR_ALIAS;
+    }
+    if (hits(rso, qr) || overlap(rso, cr.w) || overlap(rso, cr.b) || (overlap(rso, rsi) && state_out != state_in))
+        return BDSSM_ERR_ALIAS;
+    if (s.b == 0 || len == 0) {
+        // no tokens: the history is unchanged
+        if (state_out && state_out != state_in && sb > 0) {
+            if (state_in)
+                return launched(launch_copy_f32(static_cast<float *>(state_out),
+                                                static_cast<const float *>(state_in), sb / 4,
+                                                static_cast<hipStream_t>(stream)));
+            return launched(launch_fill_f32(static_cast<float *>(state_out), 0.f, sb / 4,
+                                            static_cast<hipStream_t>(stream)));
+        }
+        return BDSSM_OK;
+    }
+    ConvArgs a{};
+    a.s = s;
+    a.len = len;
+    a.act = conv->activation;
+    a.q[0] = ConvSeqArgs{raw->x, raw->B, raw->C, const_cast<void *>(out->x), const_cast<void *>(out->B),
+                         const_cast<void *>(out->C), conv->weight, conv->bias, state_in, state_out, reverse};
+    return launched(launch_conv(a, conv->width, 1, static_cast<hipStream_t>(stream)));
+}
+
+bdssm_status bdssm_block_step_conv(const bdssm_dims *dims, int32_t block_len,
+                                   const bdssm_conv_params *conv_fwd,
+                                   const bdssm_conv_params *conv_rev, const float *h_prefix,
+                                   const void *conv_state, const bdssm_seq *fwd,
+                                   const bdssm_seq *rev, const float *A, const float *D,
+                                   const float *A_rev, const float *D_rev, void *y,
+                                   void *workspace, size_t workspace_bytes, void *stream)
 {
     Shape s;
     bdssm_status rc = check_dims(dims, &s);
@@ -362,32 +551,128 @@ bdssm_status bdssm_commit(const bdssm_dims *dims, int32_t block_len, const bdssm
         return BDSSM_ERR_SHAPE;
     if (block_len > 256)
         return BDSSM_ERR_UNSUPPORTED;
-    if (!A || !D || !h)
-        return BDSSM_ERR_NULL;
-    SeqRanges q{};
-    if ((rc = check_seq(clean, s, block_len, y != nullptr, &q)) != BDSSM_OK)
+    ConvRanges cf{}, cr{};
+    if ((rc = check_conv(conv_fwd, s, &cf)) != BDSSM_OK || (rc = check_conv(conv_rev, s, &cr)) != BDSSM_OK)
         return rc;
-    if (!aligned(A) || !aligned(D) || !aligned(h) || !aligned(y))
+    if (conv_fwd->width > 1 && !conv_state)
+        return BDSSM_ERR_NULL;
+    SeqRanges qf{}, qr{};
+    if ((rc = check_seq(fwd, s, block_len, true, &qf)) != BDSSM_OK ||
+        (rc = check_seq(rev, s, block_len, true, &qr)) != BDSSM_OK)
+        return rc;
+    if (!aligned(conv_state) || !aligned(workspace))
         return BDSSM_ERR_ALIGN;
-    const int64_t NP = static_cast<int64_t>(s.N) * s.P;
-    const Range rh = rng(h, static_cast<int64_t>(s.b) * s.H * NP * 4);
+    const ConvCopy cc = conv_copy_bytes(s, block_len);
+    if (block_len > 0 && s.b > 0 && (!workspace || workspace_bytes < 2 * cc.total))
+        return BDSSM_ERR_WORKSPACE;
+    const Range rws = rng(workspace, static_cast<int64_t>(2 * cc.total));
+    const Range rcs = rng(conv_state, conv_fwd->width > 1 ? conv_state_bytes(s, conv_fwd->width) : 0);
+    if (hits(rws, qf) || hits(rws, qr) || overlap(rws, cf.w) || overlap(rws, cf.b) || overlap(rws, cr.w) ||
+        overlap(rws, cr.b) || overlap(rws, rcs))
+        return BDSSM_ERR_ALIAS;
+    // the block step reads the convolved x, B, C from the workspace and the raw dt
+    char *w0 = static_cast<char *>(workspace);
+    char *w1 = w0 + cc.total;
+    const bdssm_seq pf{w0, fwd->dt, w0 + cc.B, w0 + cc.C};
+    const bdssm_seq pr{w1, rev->dt, w1 + cc.B, w1 + cc.C};
+    BlockArgs a{};
+    if ((rc = prepare_block_step(dims, block_len, h_prefix, &pf, &pr, A, D, A_rev ? A_rev : A, D_rev, y, &a)) !=
+        BDSSM_OK)
+        return rc;
     const Range ry = rng(y, static_cast<int64_t>(s.b) * block_len * s.H * s.P * elt(s.y_dt));
-    for (Range o : {rh, ry}) {
-        if (hits(o, q) || overlap(o, rng(A, s.H * 4)) || overlap(o, rng(D, s.H * 4)))
-            return BDSSM_ERR_ALIAS;
-    }
-    if (overlap(rh, ry))
+    if (hits(ry, qf) || hits(ry, qr) || overlap(ry, rws) || overlap(ry, rcs) || overlap(ry, cf.w) ||
+        overlap(ry, cf.b) || overlap(ry, cr.w) || overlap(ry, cr.b))
         return BDSSM_ERR_ALIAS;
     if (s.b == 0 || block_len == 0)
         return BDSSM_OK;
-    const Seq seq{clean->x, clean->dt, clean->B, clean->C};
-    // a commit is a prefix scan of the block from h, in place: on the matrix-core prefix
-    // path, one segment per (stream, head) (no workspace)
-    if (prefix_mfma_supported(s, 64))
-        return launched(run_prefix_mfma(s, block_len, 64, seq, A, D, h, y, nullptr, h, nullptr,
-                                        static_cast<hipStream_t>(stream), true));
-    ForwardArgs f{s, block_len, block_len, 1, seq, A, D, h, nullptr, y, h, nullptr};
-    return launched(launch_forward_valu(f, static_cast<hipStream_t>(stream)));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (conv_fwd->width == conv_rev->width && conv_fwd->activation == conv_rev->activation) {
+        // both directions in one launch
+        ConvArgs ca{};
+        ca.s = s;
+        ca.len = block_len;
+        ca.act = conv_fwd->activation;
+        ca.q[0] = ConvSeqArgs{fwd->x, fwd->B, fwd->C, w0, w0 + cc.B, w0 + cc.C, conv_fwd->weight,
+                              conv_fwd->bias, conv_fwd->width > 1 ? conv_state : nullptr, nullptr, 0};
+        ca.q[1] = ConvSeqArgs{rev->x, rev->B, rev->C, w1, w1 + cc.B, w1 + cc.C, conv_rev->weight,
+                              conv_rev->bias, nullptr, nullptr, 1};
+        if ((rc = launched(launch_conv(ca, conv_fwd->width, 2, st))) != BDSSM_OK)
+            return rc;
+    } else {
+        for (int d = 0; d < 2; ++d) {
+            const bdssm_conv_params *cp = d ? conv_rev : conv_fwd;
+            const bdssm_seq *in = d ? rev : fwd;
+            char *w = d ? w1 : w0;
+            ConvArgs ca{};
+            ca.s = s;
+            ca.len = block_len;
+            ca.act = cp->activation;
+            ca.q[0] = ConvSeqArgs{in->x, in->B, in->C, w, w + cc.B, w + cc.C, cp->weight, cp->bias,
+                                  (d == 0 && cp->width > 1) ? conv_state : nullptr, nullptr, d};
+            if ((rc = launched(launch_conv(ca, cp->width, 1, st))) != BDSSM_OK)
+                return rc;
+        }
+    }
+    return launch_block_step(a, st);
+}
+
+bdssm_status bdssm_commit_conv(const bdssm_dims *dims, int32_t block_len,
+                               const bdssm_conv_params *conv, const bdssm_seq *clean,
+                               const float *A, const float *D, float *h, void *conv_state,
+                               void *y, void *workspace, size_t workspace_bytes, void *stream)
+{
+    Shape s;
+    bdssm_status rc = check_dims(dims, &s);
+    if (rc != BDSSM_OK)
+        return rc;
+    if (block_len < 0)
+        return BDSSM_ERR_SHAPE;
+    if (block_len > 256)
+        return BDSSM_ERR_UNSUPPORTED;
+    ConvRanges cr{};
+    if ((rc = check_conv(conv, s, &cr)) != BDSSM_OK)
+        return rc;
+    if (conv->width > 1 && !conv_state)
+        return BDSSM_ERR_NULL;
+    SeqRanges q{};
+    if ((rc = check_seq(clean, s, block_len, true, &q)) != BDSSM_OK)
+        return rc;
+    if (!aligned(conv_state) || !aligned(workspace))
+        return BDSSM_ERR_ALIGN;
+    const ConvCopy cc = conv_copy_bytes(s, block_len);
+    if (block_len > 0 && s.b > 0 && (!workspace || workspace_bytes < cc.total))
+        return BDSSM_ERR_WORKSPACE;
+    const Range rws = rng(workspace, static_cast<int64_t>(cc.total));
+    const Range rcs = rng(conv_state, conv->width > 1 ? conv_state_bytes(s, conv->width) : 0);
+    const Range rh = rng(h, static_cast<int64_t>(s.b) * s.H * s.N * s.P * 4);
+    const Range ry = rng(y, static_cast<int64_t>(s.b) * block_len * s.H * s.P * elt(s.y_dt));
+    for (Range o : {rws, rcs}) {
+        if (hits(o, q) || overlap(o, cr.w) || overlap(o, cr.b) || overlap(o, rh) || overlap(o, ry) ||
+            overlap(o, rng(A, s.H * 4)) || overlap(o, rng(D, s.H * 4)))
+            return BDSSM_ERR_ALIAS;
+    }
+    if (overlap(rws, rcs))
+        return BDSSM_ERR_ALIAS;
+    char *w0 = static_cast<char *>(workspace);
+    const bdssm_seq pc{w0, clean->dt, w0 + cc.B, w0 + cc.C};
+    Shape s2;
+    if ((rc = prepare_commit(dims, block_len, &pc, A, D, h, y, &s2)) != BDSSM_OK)
+        return rc;
+    if (hits(rh, q) || hits(ry, q))
+        return BDSSM_ERR_ALIAS;
+    if (s.b == 0 || block_len == 0)
+        return BDSSM_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    ConvArgs ca{};
+    ca.s = s;
+    ca.len = block_len;
+    ca.act = conv->activation;
+    void *cs = conv->width > 1 ? conv_state : nullptr;
+    ca.q[0] = ConvSeqArgs{clean->x, clean->B, clean->C, w0, w0 + cc.B, w0 + cc.C, conv->weight, conv->bias,
+                          cs, cs, 0};
+    if ((rc = launched(launch_conv(ca, conv->width, 1, st))) != BDSSM_OK)
+        return rc;
+    return launch_commit(s, block_len, Seq{pc.x, pc.dt, pc.B, pc.C}, A, D, h, y, st);
 }
 
 }  // extern "C"

@@ -53,6 +53,25 @@ struct BlockArgs {
     const float *D_rev;  // skip term of the reverse input, or NULL for none
 };
 
+// Depthwise convolution of one token segment's x, B, C channels (see conv.hip)
+struct ConvSeqArgs {
+    const void *x, *B, *C;  // raw inputs
+    void *ox, *oB, *oC;     // convolved outputs (same layouts and dtype)
+    const float *w;         // [CH][W] taps, CH = H*P + 2*G*N
+    const float *bias;      // [CH] or NULL
+    const void *state_in;   // [b][W-1][CH] history before the segment, or NULL (zeros); forward only
+    void *state_out;        // [b][W-1][CH] new history, or NULL; forward only
+    int reverse;            // 0 causal, 1 anti-causal with zeros past the end
+};
+
+struct ConvArgs {
+    Shape s;
+    int64_t len;
+    int act;   // 0 identity, 1 SiLU
+    int nrun;  // token runs per channel group (set by launch_conv)
+    ConvSeqArgs q[2];
+};
+
 struct PrefixPlan {
     int seg_sub;       // 64-token sub-chunks per segment
     int nseg;          // segments per stream
@@ -75,6 +94,7 @@ hipError_t launch_block_step_mfma(const BlockArgs &a, int hpw, int ps, hipStream
 hipError_t launch_forward_valu(const ForwardArgs &a, hipStream_t st);
 hipError_t launch_block_step_valu(const BlockArgs &a, hipStream_t st);
 hipError_t launch_state_pass(const PassArgs &a, hipStream_t st);
+hipError_t launch_conv(ConvArgs a, int width, int nseq, hipStream_t st);
 hipError_t launch_copy_f32(float *dst, const float *src, int64_t n, hipStream_t st);
 hipError_t launch_fill_f32(float *dst, float v, int64_t n, hipStream_t st);
 

@@ -165,6 +165,84 @@ bdssm_status bdssm_commit(const bdssm_dims *dims, int32_t block_len, const bdssm
                           const float *A, const float *D, float *h, void *y, void *stream);
 
 /*
+ * Convolution state. A Mamba layer's cache holds convolution state as well as the SSM
+ * state (the cache discussion of "Training Hybrid Block Diffusion Language Models with
+ * Partial Bidirectionality"); the pages leave the convolution itself open, and these calls
+ * take the Mamba-2 layer's: before the scan, each of the CH = H*P + 2*G*N channels of a
+ * token (x [H][P], then B [G][N], then C [G][N]) is convolved with its own `width` taps,
+ * a bias is added and an activation applied, and the result, rounded to the input dtype,
+ * is what the scan reads. dt is not convolved.
+ *   forward (causal):   out_t = bias + sum_{k<W} w[k] u_{t-(W-1)+k}, where u_t for t < 0
+ *                       comes from the conv state, the W-1 raw (unconvolved) rows that
+ *                       precede the segment;
+ *   reverse (anti-causal, the block's reverse branch, which has no state, eq. (12)):
+ *                       out_t = bias + sum_{k<W} w[k] u_{t+(W-1)-k}, with u_t = 0 past the
+ *                       segment's end (the causal convolution of the reversed block).
+ * The conv state after a forward segment is the last W-1 rows of the raw input extended by
+ * the previous state. Conv state layout: [b][W-1][CH] in dims->in_dtype.
+ */
+typedef struct {
+    int32_t width;       /* W, 1..4 */
+    int32_t activation;  /* 0 identity, 1 SiLU (v / (1 + exp(-v))) */
+    const float *weight; /* [CH][W] float32, taps w[c][k] */
+    const float *bias;   /* [CH] float32, or NULL for none */
+} bdssm_conv_params;
+
+/* Bytes of one convolved copy of x, B and C for `len` tokens (each part 256-byte aligned in
+ * the buffer): bdssm_block_step_conv needs two, bdssm_commit_conv one. SIZE_MAX for
+ * invalid dims or len < 0. */
+size_t bdssm_conv_workspace(const bdssm_dims *dims, int64_t len);
+
+/*
+ * The convolution of one segment of `len` tokens: out.{x,B,C} <- act(conv(raw.{x,B,C})).
+ *   reverse    0 forward (causal), 1 reverse (anti-causal)
+ *   state_in   forward: [b][W-1][CH] history before the segment, or NULL for zeros (the
+ *              start of a sequence); must be NULL when reverse
+ *   raw, out   x, B, C are used (dt is ignored and may be NULL); out must not overlap raw,
+ *              the parameters or the states
+ *   state_out  forward: [b][W-1][CH] receives the new history, or NULL; it may be the same
+ *              pointer as state_in (updated in place) but must not otherwise overlap
+ *              anything; must be NULL when reverse
+ * A prefix is convolved with this call (forward, state_in NULL, state_out = the cache's
+ * conv state) before bdssm_prefix_scan reads it.
+ */
+bdssm_status bdssm_conv(const bdssm_dims *dims, int64_t len, const bdssm_conv_params *conv,
+                        int32_t reverse, const void *state_in, const bdssm_seq *raw,
+                        const bdssm_seq *out, void *state_out, void *stream);
+
+/*
+ * Block step on unconvolved inputs: the forward branch's x, B, C are convolved causally from
+ * the cached conv state (conv_fwd), the reverse branch's anti-causally inside the block
+ * (conv_rev, its own parameters; pass conv_fwd's for shared ones), both in one launch into
+ * the workspace, then bdssm_block_step_ex runs on the convolved inputs with the raw dt.
+ *   conv_state  [b][W_fwd-1][CH] in in_dtype, read only (NULL when W_fwd = 1)
+ *   A_rev       as in bdssm_block_step_ex; NULL means A
+ *   workspace   at least 2 * bdssm_conv_workspace(dims, block_len) bytes; must not overlap
+ *               anything else
+ * Everything else as bdssm_block_step_ex.
+ */
+bdssm_status bdssm_block_step_conv(const bdssm_dims *dims, int32_t block_len,
+                                   const bdssm_conv_params *conv_fwd,
+                                   const bdssm_conv_params *conv_rev, const float *h_prefix,
+                                   const void *conv_state, const bdssm_seq *fwd,
+                                   const bdssm_seq *rev, const float *A, const float *D,
+                                   const float *A_rev, const float *D_rev, void *y,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Commit on unconvolved inputs: the clean block is convolved causally from the conv state
+ * into the workspace, the conv state is advanced in place, then bdssm_commit advances h.
+ *   conv_state  [b][W-1][CH] in in_dtype, read then overwritten (NULL when W = 1)
+ *   workspace   at least bdssm_conv_workspace(dims, block_len) bytes
+ * Everything else as bdssm_commit, except that clean->C is always required (its raw rows
+ * enter the conv state).
+ */
+bdssm_status bdssm_commit_conv(const bdssm_dims *dims, int32_t block_len,
+                               const bdssm_conv_params *conv, const bdssm_seq *clean,
+                               const float *A, const float *D, float *h, void *conv_state,
+                               void *y, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Decode loop of one active block as a HIP graph: `steps` calls of bdssm_block_step (step
  * k reads fwd[k], rev[k] and writes y[k], all from the cached state h), followed, when
  * clean is not NULL, by bdssm_commit(clean, h, y_commit). This is the static-shape block

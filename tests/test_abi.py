@@ -180,3 +180,63 @@ def test_block_step_ex_argument_checks():
     assert call(D_rev=FAKE + 8) == bdssm.ERR_ALIGN
     assert call(A_rev=FAKE + (1 << 24)) == bdssm.ERR_ALIAS   # y on top of A_rev
     assert call(D_rev=FAKE + (1 << 24)) == bdssm.ERR_ALIAS   # y on top of D_rev
+
+
+def test_conv_argument_checks():
+    """bdssm_conv, bdssm_block_step_conv, bdssm_commit_conv: argument errors are reported
+    before anything is launched; the workspace query's size."""
+    lib = bdssm.load()
+    d = bdssm.dims(1, 4, 16, 16, 1, bdssm.BF16, bdssm.F32)   # CH = 64 + 32 = 96
+    # one convolved copy of 10 tokens: x 1280 B, B and C 320 B each, 256-byte aligned parts
+    assert bdssm.conv_workspace(d, 10) == 1280 + 512 + 512
+    assert bdssm.conv_workspace(d, -1) == ctypes.c_size_t(-1).value
+    base = 1 << 32
+    raw = seq(base, None, base + (1 << 20), base + (2 << 20))
+    out = seq(base + (3 << 20), None, base + (4 << 20), base + (5 << 20))
+    W = base + (6 << 20)
+    st = base + (7 << 20)
+
+    def conv(cp=None, reverse=0, si=st, so=st, r=raw, o=out, length=10):
+        cp = bdssm.ConvParams(4, 1, W, None) if cp is None else cp
+        return lib.bdssm_conv(ctypes.byref(d), length, ctypes.byref(cp), reverse, si, ctypes.byref(r),
+                              ctypes.byref(o), so, None)
+    assert lib.bdssm_conv(ctypes.byref(d), 10, None, 0, None, ctypes.byref(raw), ctypes.byref(out), None,
+                          None) == bdssm.ERR_NULL
+    assert conv(bdssm.ConvParams(5, 1, W, None)) == bdssm.ERR_UNSUPPORTED
+    assert conv(bdssm.ConvParams(0, 1, W, None)) == bdssm.ERR_UNSUPPORTED
+    assert conv(bdssm.ConvParams(4, 2, W, None)) == bdssm.ERR_UNSUPPORTED
+    assert conv(bdssm.ConvParams(4, 1, None, None)) == bdssm.ERR_NULL
+    assert conv(bdssm.ConvParams(4, 1, W + 4, None)) == bdssm.ERR_ALIGN
+    assert conv(reverse=1) == bdssm.ERR_SHAPE               # no state for the reverse branch
+    assert conv(length=-1) == bdssm.ERR_SHAPE
+    assert conv(si=st + 8) == bdssm.ERR_ALIGN
+    assert conv(so=st + 16) == bdssm.ERR_ALIAS               # partial overlap of the two states
+    assert conv(o=seq(base + 64, None, base + (4 << 20), base + (5 << 20))) == bdssm.ERR_ALIAS  # out on raw
+    assert conv(o=seq(base + (3 << 20), None, None, base + (5 << 20))) == bdssm.ERR_NULL
+    assert conv(so=W) == bdssm.ERR_ALIAS                     # state on the weights
+    # block step with conv
+    f = seq(base, base + (8 << 20), base + (1 << 20), base + (2 << 20))
+    r = seq(base + (9 << 20), base + (10 << 20), base + (11 << 20), base + (12 << 20))
+    cp = bdssm.ConvParams(4, 1, W, None)
+    ws = base + (16 << 20)
+    need = 2 * bdssm.conv_workspace(d, 10)
+
+    def step(cs=st, wsp=ws, wsb=need, y=base + (20 << 20)):
+        return lib.bdssm_block_step_conv(ctypes.byref(d), 10, ctypes.byref(cp), ctypes.byref(cp),
+                                         base + (24 << 20), cs, ctypes.byref(f), ctypes.byref(r), FAKE,
+                                         FAKE + 256, None, None, y, wsp, wsb, None)
+    assert step(cs=None) == bdssm.ERR_NULL                   # width 4 needs the conv state
+    assert step(wsb=need - 1) == bdssm.ERR_WORKSPACE
+    assert step(wsp=None) == bdssm.ERR_WORKSPACE
+    assert step(wsp=base + (1 << 20)) == bdssm.ERR_ALIAS     # workspace on an input
+    assert step(y=ws) == bdssm.ERR_ALIAS                      # y on the workspace
+    assert step(y=base + (1 << 20)) == bdssm.ERR_ALIAS       # y on a raw input
+    # commit with conv: C is required (it enters the conv state)
+    cl = seq(base, base + (8 << 20), base + (1 << 20), None)
+    assert lib.bdssm_commit_conv(ctypes.byref(d), 10, ctypes.byref(cp), ctypes.byref(cl), FAKE, FAKE + 256,
+                                 base + (24 << 20), st, None, ws, need, None) == bdssm.ERR_NULL
+    cl = seq(base, base + (8 << 20), base + (1 << 20), base + (2 << 20))
+    assert lib.bdssm_commit_conv(ctypes.byref(d), 10, ctypes.byref(cp), ctypes.byref(cl), FAKE, FAKE + 256,
+                                 base + (24 << 20), st, None, ws, 16, None) == bdssm.ERR_WORKSPACE
+    assert lib.bdssm_commit_conv(ctypes.byref(d), 10, ctypes.byref(cp), ctypes.byref(cl), FAKE, FAKE + 256,
+                                 base + (24 << 20), base + 32, None, ws, need, None) == bdssm.ERR_ALIAS
