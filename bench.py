@@ -295,10 +295,64 @@ def main():
                            "active_tokens_per_s": round(S * b * T / (blk_us * 1e-6), 1)}
 
     if not args.no_secondary:
+        out["conv_state"] = conv_workloads(torch, bdssm, cfg, inputs, d, h, steps, Ad, Dd, y_blk, pre, L,
+                                           avg_us["block_step"])
         out["secondary"] = secondary(torch, np, bdssm, configs, inputs)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(np, cfg, A, D, pre_np, steps_np, clean_np)
     print(json.dumps(out), flush=True)
+
+
+def conv_bytes(b, H, P, N, G, L, W, in_bytes, state):
+    ch = H * P + 2 * G * N
+    return 2 * b * L * ch * in_bytes + ch * (W + 1) * 4 + (2 * b * (W - 1) * ch * in_bytes if state else 0)
+
+
+def conv_workloads(torch, bdssm, cfg, inputs, d, h, steps, Ad, Dd, y_blk, pre, L, plain_step_us, reps=20):
+    """The convolution state at the 700M shape (width 4, SiLU): the 64 block steps through
+    bdssm_block_step_conv (both directions' convolutions in one launch, then the block step),
+    captured in one graph like the main step, and the forward convolution of the 8192-token
+    prefix that writes the conv state (HBM-bound)."""
+    b, H, P, N, G, T = cfg.batch, cfg.nheads, cfg.headdim, cfg.d_state, cfg.ngroups, cfg.block_len
+    W = 4
+    ch = H * P + 2 * G * N
+    wf, bf = (torch.from_numpy(a).cuda() for a in inputs.conv_params(cfg, W, inputs.FWD))
+    wr, br = (torch.from_numpy(a).cuda() for a in inputs.conv_params(cfg, W, inputs.REV))
+    cpf, cpr = bdssm.conv_params(wf, bf, 1), bdssm.conv_params(wr, br, 1)
+    cs = torch.zeros((b, W - 1, ch), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(2 * bdssm.conv_workspace(d, T), dtype=torch.uint8, device="cuda")
+    S = len(steps)
+
+    def run_steps():
+        for s in range(S):
+            f, r = steps[s]
+            bdssm.block_step_conv(d, T, cpf, cpr, h, cs, f, r, Ad, Dd, y_blk[s], ws)
+
+    g = capture(torch, run_steps)
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    for _ in range(reps):
+        tm.run("k", g.replay)
+    torch.cuda.synchronize()
+    step_us = tm.avg_us("k") / S
+    post = tuple(torch.empty_like(t) for t in pre)
+    cso = torch.empty_like(cs)
+    tm = Timer(torch)
+    for i in range(reps + 3):
+        (tm if i >= 3 else Timer(torch)).run("c", lambda: bdssm.conv(d, L, cpf, False, None, pre, post, cso))
+    torch.cuda.synchronize()
+    conv_us = tm.avg_us("c")
+    nb = conv_bytes(b, H, P, N, G, L, W, 2, True)
+    return {"block_step_conv": {"workload": "64 block steps (T=32) on unconvolved inputs, width-4 SiLU "
+                                            "convolution of x, B, C per direction, 700M shape, one graph",
+                                "us_per_step": round(step_us, 3), "plain_block_step_us": round(plain_step_us, 3),
+                                "active_tokens_per_s": round(b * T / (step_us * 1e-6), 1)},
+            "prefix_conv": {"workload": "forward convolution of an 8192-token prefix (x, B, C; width 4, "
+                                        "SiLU) writing the conv state, 700M shape, bf16",
+                            "avg_us": round(conv_us, 3), "alg_bytes": nb,
+                            "roofline": make_roofline("hbm", nb, conv_us, None)}}
 
 
 def secondary(torch, np, bdssm, configs, inputs, reps=20):
