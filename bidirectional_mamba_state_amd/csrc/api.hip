@@ -188,8 +188,22 @@ bdssm_status prepare_block_step(const bdssm_dims *dims, int32_t block_len, const
     return BDSSM_OK;
 }
 
+// Small batches (fewer (stream, head) pairs than fill the GPU with one workgroup per CU)
+// take the latency-ordered kernel, one wavefront per (row block, column block, head);
+// BDSSM_BLOCK_LAT=0 or 1 forces the choice where both kernels apply.
+bool use_block_lat(const Shape &s, int T)
+{
+    if (!block_lat_supported(s, T))
+        return false;
+    if (const char *e = getenv("BDSSM_BLOCK_LAT"))
+        return atoi(e) != 0;
+    return static_cast<int64_t>(s.b) * s.H < 512;
+}
+
 bdssm_status launch_block_step(const BlockArgs &a, hipStream_t st)
 {
+    if (use_block_lat(a.s, a.T))
+        return launched(launch_block_step_lat(a, st));
     if (block_mfma_supported(a.s, a.T)) {
         int hpw, ps;
         block_mfma_plan(a.s, &hpw, &ps);

@@ -260,9 +260,11 @@ def test_commit_chain_equals_prefix_scan():
     assert within(rel(h, ho), TOL_BF16, "commit chain vs oracle")
 
 
-@pytest.mark.parametrize("T", [32, 128])
+@pytest.mark.parametrize("T", [17, 32, 64, 128])
 def test_block_step_launch_shapes(monkeypatch, T):
-    """Every (heads per workgroup, column split) launch shape gives the oracle's result."""
+    """Both block-step kernels give the oracle's result: the bandwidth kernel at every
+    (heads per workgroup, column split) launch shape, and the latency kernel (one wavefront
+    per row block, column block and head; T <= 32) with float32 and bfloat16 y."""
     rng = np.random.default_rng(100 + T)
     from test_oracle_pins import rand_seq
     b, H, G = 3, 12, 2        # 6 heads per group
@@ -274,15 +276,25 @@ def test_block_step_launch_shapes(monkeypatch, T):
     yo, _, _ = oracle.block_step(h, fwd, rev, A, D)
     Dz = np.zeros_like(D)
     yzo, _, _ = oracle.block_step(h, fwd, rev, A, Dz)
-    for hpw in (1, 2, 3, 6):
-        for ps in (1, 2, 4):
-            monkeypatch.setenv("BDSSM_BLOCK_HPW", str(hpw))
-            monkeypatch.setenv("BDSSM_BLOCK_PS", str(ps))
-            _case(f"launch shape T={T} hpw={hpw} ps={ps}")
-            y = gpu_block_step(h, fwd, rev, A, D)
-            yz = gpu_block_step(h, fwd, rev, A, Dz)
-            assert within(rel(y, yo), TOL_BF16, f"y hpw={hpw} ps={ps}")
-            assert within(rel(yz, yzo), TOL_BF16, f"y - D x hpw={hpw} ps={ps}")
+    shapes = [(hpw, ps) for hpw in (1, 2, 3, 6) for ps in (1, 2, 4)] if T in (32, 128) else [(1, 4), (6, 1)]
+    monkeypatch.setenv("BDSSM_BLOCK_LAT", "0")
+    for hpw, ps in shapes:
+        monkeypatch.setenv("BDSSM_BLOCK_HPW", str(hpw))
+        monkeypatch.setenv("BDSSM_BLOCK_PS", str(ps))
+        _case(f"launch shape T={T} hpw={hpw} ps={ps}")
+        y = gpu_block_step(h, fwd, rev, A, D)
+        yz = gpu_block_step(h, fwd, rev, A, Dz)
+        assert within(rel(y, yo), TOL_BF16, f"y hpw={hpw} ps={ps}")
+        assert within(rel(yz, yzo), TOL_BF16, f"y - D x hpw={hpw} ps={ps}")
+    if T <= 32:
+        monkeypatch.setenv("BDSSM_BLOCK_LAT", "1")
+        for y_dtype in (bdssm.F32, bdssm.BF16):
+            _case(f"latency kernel T={T} y_dtype={y_dtype}")
+            y = gpu_block_step(h, fwd, rev, A, D, y_dtype)
+            yz = gpu_block_step(h, fwd, rev, A, Dz, y_dtype)
+            assert within(rel(y, yo), TOL_BF16, "y, latency kernel")
+            assert within(rel(yz, yzo), TOL_BF16, "y - D x, latency kernel")
+            assert within(max_head_rel(yz, yzo, 2), 4 * TOL_BF16, "y - D x, latency kernel, worst head")
 
 
 def test_config4_running_set_shape():
