@@ -11,7 +11,9 @@
 //   state:   h <- exp(c_63) h + sum_s B_s [exp(c_63 - c_s) dt_s x_s]^T
 //   output:  y_t = exp(c_t) C_t . h_in + sum_{s<=t} exp(c_t - c_s) dt_s (C_t . B_s) x_s + D x_t
 // Outputs are computed transposed (y^T = h^T C^T + X^T M^T) so that a lane holds four
-// consecutive columns of one token. The C B^T scores are shared by the workgroup's heads.
+// consecutive columns of one token. The causal C B^T score tiles and their decay weights do
+// not depend on the columns: the four wavefronts compute a share each and exchange the
+// weighted tiles M through LDS.
 // B, C and x are staged in LDS in the fragment-major order of mfma_tiles.h (an operand
 // fragment is one contiguous 512-byte read per wavefront); operands whose contraction runs
 // over tokens are read from the same tiles with the gfx950 transposing LDS load
@@ -87,6 +89,10 @@ struct Lds {
     __bf16 hT[FULL ? 4 * HPW : 1][FULL ? 2 : 1][FULL ? 16 * kN : 8];
     float tab[2][HPW][NTAB][SC];  // decay tables of sub-chunks k and k+1 (by parity)
     float tot[2][HPW];
+    // FULL: the decay-weighted causal score tiles M[t][s] of the sub-chunk (row block tb,
+    // column block sb <= tb; tile tb(tb+1)/2 + sb), each stored as the 64 lanes' accumulator
+    // values in lane order, so that a reader lane fetches the 8 bytes it needs contiguously
+    __bf16 Mt[FULL ? 10 : 1][256];
 };
 
 
@@ -294,111 +300,104 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
                 xf[hh][m] = tr_frag<kP>(L.X[hh], 32 * m, p0, q, r16);
 
         if constexpr (FULL && WITHY) {
+            static_assert(HPW == 1, "outputs are computed one head per workgroup");
             // y rows of this sub-chunk; rows past the end fall outside the buffer range and
             // their stores are dropped by the hardware
             const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
                 static_cast<Ty *>(a.y) + (tok0 + t0) * rowX, 0, nvalid * rowX * static_cast<int>(sizeof(Ty)),
                 0x00020000);
+            const float(*tbl)[SC] = L.tab[k & 1][0];
+            // (1) the ten causal score tiles S[tb][sb] = B_s . C_t are shared by the four
+            // wavefronts: wavefront w computes tiles w, w+4, w+8, weights them with the
+            // decays (factored below the diagonal 32-token pair, per element on it) and
+            // stores them for all
 #pragma unroll
-            for (int hh = 0; hh < HPW; ++hh) {
-                const float(*tbl)[SC] = L.tab[k & 1][hh];
-                // state entering the sub-chunk as y^T operands (rows p, contraction over n in
-                // the order of two stacked accumulator tiles), from this wavefront's LDS copy
-                const __bf16 *hTh = L.hT[wave * HPW + hh][0], *hTl = L.hT[wave * HPW + hh][1];
-                // Groups of NRB row blocks. Per group, scores S[tb][sb] = B_s . C_t (s in block
-                // sb <= tb, t in block tb) and y^T[p][t] = sum_n h[n][p] C[t][n]: each C
-                // fragment is read once, and the products of one 32-wide slice of n are
-                // independent.
-                constexpr int NRB = 2;
+            for (int r = 0; r < 3; ++r) {
+                const int tau = wave + 4 * r;
+                if (tau < 10) {  // uniform over the wavefront
+                    const int tb = tau >= 6 ? 3 : tau >= 3 ? 2 : tau >= 1 ? 1 : 0;
+                    const int sb = tau - tb * (tb + 1) / 2;
+                    f32x4 S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int half = 0; half < 4 / NRB; ++half) {
-                f32x4 S[NRB][4], acc[NRB];
-#pragma unroll
-                for (int u = 0; u < NRB; ++u) {
-                    acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int sb = 0; sb < 4; ++sb)
-                        S[u][sb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                }
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const bf16x8 hfh = frag<kN>(hTh, 0, m, q, r16), hfl = frag<kN>(hTl, 0, m, q, r16);
-                    bf16x8 bf[4];
-#pragma unroll
-                    for (int sb = 0; sb < NRB * half + NRB; ++sb)
-                        bf[sb] = frag<kN>(L.B, sb, m, q, r16);
-#pragma unroll
-                    for (int u = 0; u < NRB; ++u) {
-                        const int tb = NRB * half + u;
-                        const bf16x8 cf = frag<kN>(L.C, tb, m, q, r16);
-#pragma unroll
-                        for (int sb = 0; sb <= tb; ++sb)
-                            S[u][sb] = mfma(bf[sb], cf, S[u][sb]);
-                        acc[u] = mfma(hfh, cf, acc[u]);
-                        acc[u] = mfma(hfl, cf, acc[u]);
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < NRB; ++u) {
-                    const int tb = NRB * half + u;
-                    const int t = 16 * tb + r16, md = tb >> 1;
+                    for (int m = 0; m < 4; ++m)
+                        S = mfma(frag<kN>(L.B, sb, m, q, r16), frag<kN>(L.C, tb, m, q, r16), S);
+                    // lane (t, q) holds S[s = 16 sb + 4q + j][t]
+                    const int t = 16 * tb + r16, mp = sb >> 1, s0 = 16 * sb + 4 * q;
                     const float ct = tbl[TAB_C][t];
-                    acc[u] *= tbl[TAB_EF][t];
-                    // ---- + sum_{s<=t} M[t][s] x_s, per 32-token pair
-#pragma unroll
-                    for (int m = 0; m <= md; ++m) {
-                        float mv[8];
-                        if (m < md) {  // pair wholly below the row block: factored decay
-                            const float rowf = __builtin_amdgcn_exp2f(ct - tbl[TAB_C][32 * m + 31]);
-                            const float4 c0 = *reinterpret_cast<const float4 *>(&tbl[TAB_COL][32 * m + 4 * q]);
-                            const float4 c1 = *reinterpret_cast<const float4 *>(&tbl[TAB_COL][32 * m + 16 + 4 * q]);
-                            const float cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-#pragma unroll
-                            for (int e = 0; e < 8; ++e)
-                                mv[e] = (e < 4 ? S[u][2 * m][e] : S[u][2 * m + 1][e & 3]) * cw[e] * rowf;
-                        } else {  // the pair holding the row block: per element, masked to s <= t
-                            const float4 l0 = *reinterpret_cast<const float4 *>(&tbl[TAB_LG][32 * m + 4 * q]);
-                            const float4 l1 = *reinterpret_cast<const float4 *>(&tbl[TAB_LG][32 * m + 16 + 4 * q]);
-                            const float lg[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                const int s = 32 * m + (e < 4 ? 0 : 16) + 4 * q + (e & 3);
-                                const float sv = e < 4 ? S[u][2 * m][e] : S[u][2 * m + 1][e & 3];
-                                mv[e] = s <= t ? sv * __builtin_amdgcn_exp2f(ct + lg[e]) : 0.f;
-                            }
-                        }
-                        bf16x8 mf;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            mf[e] = static_cast<__bf16>(mv[e]);
-                        acc[u] = mfma(xf[hh][m], mf, acc[u]);
-                    }
-                    // ---- + D x_t; lane holds y[t][p0 + 4q .. p0 + 4q + 3]
-                    {
-                        const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(&L.X[hh][f8_off<kP>(t, p0 + 4 * q)]);
-                        float o[4];
+                    float mv[4];
+                    if (mp < (tb >> 1)) {  // pair wholly below the row block
+                        const float rowf = __builtin_amdgcn_exp2f(ct - tbl[TAB_C][32 * mp + 31]);
+                        const float4 cw = *reinterpret_cast<const float4 *>(&tbl[TAB_COL][s0]);
+                        mv[0] = S[0] * cw.x * rowf;
+                        mv[1] = S[1] * cw.y * rowf;
+                        mv[2] = S[2] * cw.z * rowf;
+                        mv[3] = S[3] * cw.w * rowf;
+                    } else {  // the pair holding the row block: masked to s <= t
+                        const float4 lg = *reinterpret_cast<const float4 *>(&tbl[TAB_LG][s0]);
+                        const float l4[4] = {lg.x, lg.y, lg.z, lg.w};
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
-                            o[j] = fmaf(Dh[hh], bf2f(xv[j]), acc[u][j]);
-                        const int off = ((t * H + h0 + hh) * kP + p0 + 4 * q) * static_cast<int>(sizeof(Ty));
-                        if constexpr (sizeof(Ty) == 2) {
-                            bf16x4 ov;
-#pragma unroll
-                            for (int j = 0; j < 4; ++j)
-                                ov[j] = static_cast<__bf16>(o[j]);
-                            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2i32, ov), yr, off, 0, 0);
-                        } else {
-                            __builtin_amdgcn_raw_buffer_store_b128(
-                                v4i32{__float_as_int(o[0]), __float_as_int(o[1]), __float_as_int(o[2]), __float_as_int(o[3])},
-                                yr, off, 0, 0);
-                        }
+                            mv[j] = s0 + j <= t ? S[j] * __builtin_amdgcn_exp2f(ct + l4[j]) : 0.f;
                     }
+                    bf16x4 mb;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        mb[j] = static_cast<__bf16>(mv[j]);
+                    *reinterpret_cast<bf16x4 *>(&L.Mt[tau][4 * lane]) = mb;
                 }
-                __builtin_amdgcn_sched_barrier(0);  // one group at a time
+            }
+            // (2) the state entering the sub-chunk: y^T[p][t] = sum_n h[n][p] C[t][n], from this
+            // wavefront's hi/lo copy of its columns (rows p, contraction over n in the order
+            // of two stacked accumulator tiles)
+            const __bf16 *hTh = L.hT[wave][0], *hTl = L.hT[wave][1];
+            f32x4 acc[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+                acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const bf16x8 hfh = frag<kN>(hTh, 0, m, q, r16), hfl = frag<kN>(hTl, 0, m, q, r16);
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    const bf16x8 cf = frag<kN>(L.C, tb, m, q, r16);
+                    acc[tb] = mfma(hfh, cf, acc[tb]);
+                    acc[tb] = mfma(hfl, cf, acc[tb]);
+                }
+            }
+            __syncthreads();  // (A2) the weighted score tiles are stored
+            // (3) + sum_{s<=t} M[t][s] x_s per 32-token pair, + D x_t; the lane holds
+            // y[t][p0 + 4q .. p0 + 4q + 3]
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                const int t = 16 * tb + r16, md = tb >> 1;
+                acc[tb] *= tbl[TAB_EF][t];
+#pragma unroll
+                for (int m = 0; m <= md; ++m) {
+                    const int lo = tb * (tb + 1) / 2 + 2 * m;  // tile (tb, 2m); (tb, 2m+1) follows
+                    const bf16x4 m0 = *reinterpret_cast<const bf16x4 *>(&L.Mt[lo][4 * lane]);
+                    const bf16x4 m1 = 2 * m + 1 <= tb ? *reinterpret_cast<const bf16x4 *>(&L.Mt[lo + 1][4 * lane])
+                                                      : bf16x4{};
+                    acc[tb] = mfma(xf[0][m], cat(m0, m1), acc[tb]);
+                }
+                const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(&L.X[0][f8_off<kP>(t, p0 + 4 * q)]);
+                float o[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    o[j] = fmaf(Dh[0], bf2f(xv[j]), acc[tb][j]);
+                const int off = ((t * H + h0) * kP + p0 + 4 * q) * static_cast<int>(sizeof(Ty));
+                if constexpr (sizeof(Ty) == 2) {
+                    bf16x4 ov;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        ov[j] = static_cast<__bf16>(o[j]);
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2i32, ov), yr, off, 0, 0);
+                } else {
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        v4i32{__float_as_int(o[0]), __float_as_int(o[1]), __float_as_int(o[2]), __float_as_int(o[3])},
+                        yr, off, 0, 0);
                 }
             }
         }
-
 
         // ---- state: h <- exp(c_63) h + B^T (w o x), w_s = exp(c_63 - c_s) dt_s
 #pragma unroll
