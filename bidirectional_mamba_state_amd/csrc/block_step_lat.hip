@@ -111,7 +111,14 @@ __global__ __launch_bounds__(64) void k_block_lat(BlockArgs a)
     __shared__ __attribute__((aligned(16))) float tab[NTAB][TP];
 
     const int T = a.T, H = a.s.H, G = a.s.G;
-    const int wid = blockIdx.x;
+    // The hardware deals workgroup ids round-robin over the 8 XCDs. The 8 wavefronts of one
+    // (stream, head) read the same state and x lines (each a quarter row), so they are given
+    // ids that land on one XCD and share its L2: logical id = position within the XCD's
+    // consecutive range.
+    const int nwg = gridDim.x;
+    int wid = blockIdx.x;
+    if ((nwg & 7) == 0)
+        wid = (wid & 7) * (nwg >> 3) + (wid >> 3);
     const int tb = wid % NB;
     const int pblk = (wid / NB) % (kP / 16);
     const int h = (wid / (NB * (kP / 16))) % H;
