@@ -7,9 +7,10 @@
 // wavefront is its own workgroup and owns one 16-token row block, one 16-column block and
 // one head, and everything it needs goes from global memory straight into registers in the
 // layout the matrix cores read:
-//   - the cached state as the B operand of C . h, which runs on the float32 matrix cores
-//     (v_mfma_f32_16x16x4f32, so the state is used at full precision): lane (column p,
-//     quarter q) loads h[32k + 8q + e][p] as single dwords;
+//   - the cached state as the B operand of C . h: lane (column p, quarter q) loads
+//     h[32k + 8q + e][p], e = 0..7, as single dwords -- eight consecutive contraction
+//     indices of its column, the bf16 operand layout as loaded -- and splits it into bf16
+//     hi + lo parts in registers (two products, ~16 significant bits);
 //   - x of both directions as the B operand of M X: 8-byte row pieces transposed 4 x 4
 //     (16-bit) across lanes with DPP, giving each lane the tokens of its slots
 //     (4q + e, 16 + 4q + e) in its column; the same registers give D x;
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(64) void k_block_lat(BlockArgs a)
         for (int kk = 0; kk < 4; ++kk)
             bfr[ut][kk] = ld_b128(fwd ? rBf : rBr, (srow * rowBC + 32 * kk + 8 * q) * 2);
     }
-    // the cached state as B operands of the float32 product: h[32kk + 8q + e][p]
+    // the cached state as B operands of the state product: h[32kk + 8q + e][p]
     float hv[4][8];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
@@ -232,18 +233,18 @@ __global__ __launch_bounds__(64) void k_block_lat(BlockArgs a)
         S[ut] = acc;
     }
 
-    // ---- eq. (11), cached-state term: C_t . h on the float32 matrix cores (v_mfma 16x16x4:
-    // lane (row t, k = q) gives C[t][32kk + 8q + e], lane (column p, k = q) h[32kk + 8q + e][p]),
-    // four independent chains
-    f32x4 hc[4];
+    // ---- eq. (11), cached-state term: C_t . (h_hi + h_lo). The dword loads gave each lane
+    // h[32kk + 8q + e][p], e = 0..7: the B operand layout of the bf16 product as loaded, so
+    // the state is split in registers; two independent chains
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc_lo = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-        hc[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            hc[kk] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf2f(cfw[kk][e]), hv[kk][e], hc[kk], 0, 0, 0);
+        bf16x8 hi, lo;
+        split8(hv[kk], hi, lo);
+        acc = mfma(cfw[kk], hi, acc);
+        acc_lo = mfma(cfw[kk], lo, acc_lo);
     }
-    f32x4 acc = (hc[0] + hc[1]) + (hc[2] + hc[3]);
+    acc += acc_lo;
     __syncthreads();  // the tables (one wavefront: a wavefront barrier)
     {
         const float4 e4 = *reinterpret_cast<const float4 *>(&tab[TAB_EF][tb * 16 + 4 * q]);
