@@ -194,7 +194,7 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
             st.cq[u] = *reinterpret_cast<const uint4 *>(Cg + (t0 + row) * rowBC + c16 * 8);
         }
     };
-    auto load_stage = [&](int k) {  // all but C
+    auto load_b = [&](int k) {
         const int64_t t0 = seg_t0 + static_cast<int64_t>(k) * SC;
         const int last = static_cast<int>(min<int64_t>(SC, len - t0)) - 1;
 #pragma unroll
@@ -202,12 +202,20 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
             const int it = tid + 256 * u, row = min(16 * (it >> 8) + (it & 15), last), c16 = (it >> 4) & 15;
             st.bq[u] = *reinterpret_cast<const uint4 *>(Bg + (t0 + row) * rowBC + c16 * 8);
         }
+    };
+    auto load_x = [&](int k) {
+        const int64_t t0 = seg_t0 + static_cast<int64_t>(k) * SC;
+        const int last = static_cast<int>(min<int64_t>(SC, len - t0)) - 1;
 #pragma unroll
         for (int u = 0; u < XPT; ++u) {
             const int it = tid + 256 * u, c = (it >> 4) % (8 * HPW);
             const int row = min(16 * ((it >> 4) / (8 * HPW)) + (it & 15), last);
             st.xq[u] = *reinterpret_cast<const uint4 *>(xg + (t0 + row) * rowX + c * 8);
         }
+    };
+    auto load_stage = [&](int k) {  // all but C
+        load_b(k);
+        load_x(k);
     };
     // dt two sub-chunks ahead of the stage (clamped to the segment's last sub-chunk)
     auto load_dt = [&](int k) {
@@ -273,21 +281,35 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
     load_dt(0);
     if (FULL)
         load_c(0);
+    __bf16 dt1;  // dt of sub-chunk 1, loaded with the first stage
+    {
+        const int64_t t1 = seg_t0 + SC * static_cast<int64_t>(min(1, nsub - 1));
+        dt1 = dtg[(t1 + min<int64_t>(lane, len - t1 - 1)) * H + th];
+    }
     publish_state();
     store_stage(0);
     tables(0);
-    load_dt(min(1, nsub - 1));
+    st.dt = dt1;
+    if (nsub > 1)
+        tables(1);
     for (int k = 0; k < nsub; ++k) {
         const int64_t t0 = seg_t0 + static_cast<int64_t>(k) * SC;
         const int nvalid = static_cast<int>(min<int64_t>(SC, len - t0));
         __syncthreads();  // (A) sub-chunk k staged, its tables written
-        if (k + 1 < nsub)
-            tables(k + 1);  // other buffer; visible after barrier (B)
         if (FULL && a.chunk_states && k > 0)
             emit_chunk_state(k - 1);
-        load_stage(min(k + 1, nsub - 1));  // in flight during sub-chunk k
-        if (FULL)
-            load_c(min(k + 1, nsub - 1));
+        // the loads of sub-chunk k+1, in flight during sub-chunk k. With outputs they are
+        // spread over the first phases (B and dt here, C after the score tiles, x after the
+        // state product) rather than queued all at once behind the barrier; all of them
+        // precede the y stores, so that waiting for them never waits for a store.
+        const int kn = min(k + 1, nsub - 1);
+        if constexpr (FULL && WITHY) {
+            load_b(kn);
+        } else {
+            load_stage(kn);
+            if (FULL)
+                load_c(kn);
+        }
         load_dt(min(k + 2, nsub - 1));
         __builtin_amdgcn_sched_barrier(0);  // keep the loads here, ahead of the compute
 
@@ -346,6 +368,7 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
                     *reinterpret_cast<bf16x4 *>(&L.Mt[tau][4 * lane]) = mb;
                 }
             }
+            load_c(kn);
             // (2) the state entering the sub-chunk: y^T[p][t] = sum_n h[n][p] C[t][n], from this
             // wavefront's hi/lo copy of its columns (rows p, contraction over n in the order
             // of two stacked accumulator tiles)
@@ -364,6 +387,7 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
                     acc[tb] = mfma(hfl, cf, acc[tb]);
                 }
             }
+            load_x(kn);
             __syncthreads();  // (A2) the weighted score tiles are stored
             // (3) + sum_{s<=t} M[t][s] x_s per 32-token pair, + D x_t; the lane holds
             // y[t][p0 + 4q .. p0 + 4q + 3]
@@ -438,6 +462,11 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
         // unconditional, so that no path reaches the loop head with loads in flight (after
         // the last sub-chunk it stages data nobody reads)
         store_stage(k + 1);
+        // tables of sub-chunk k+2 (its dt was loaded with the stage of k+1, whose wait just
+        // passed; at the top of the loop the wait would cover the y stores as well) into the
+        // buffer sub-chunk k has finished with; visible after the next barrier (A)
+        if (k + 2 < nsub)
+            tables(k + 2);
     }
     if (FULL && a.chunk_states)
         emit_chunk_state(nsub - 1);
