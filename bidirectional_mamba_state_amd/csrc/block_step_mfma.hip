@@ -57,6 +57,30 @@ __device__ __forceinline__ uint4 sel4(bool ok, uint4 v) { return ok ? v : make_u
 __device__ __forceinline__ void store_out(float *p, float v) { *p = v; }
 __device__ __forceinline__ void store_out(__bf16 *p, float v) { *p = static_cast<__bf16>(v); }
 
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_move(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, false));
+}
+
+// inclusive sum over the 64 lanes: shifts by 1, 2, 4, 8 inside rows of 16 lanes, then the
+// last lane of each row is added to the rows after it
+__device__ __forceinline__ float wave_inclusive_sum(float v)
+{
+    v += dpp_move<0x111, 0xf>(v);
+    v += dpp_move<0x112, 0xf>(v);
+    v += dpp_move<0x114, 0xf>(v);
+    v += dpp_move<0x118, 0xf>(v);
+    v += dpp_move<0x142, 0xa>(v);
+    v += dpp_move<0x143, 0xc>(v);
+    return v;
+}
+
+__device__ __forceinline__ float lane_value(float v, int l)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
 template <int NB, int PS>
 struct Geo {
     static constexpr int TP = NB * 16;        // padded block length
@@ -144,7 +168,7 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
     const float *hp = a.h_prefix + static_cast<int64_t>(b) * H * (kN * kP) + pbase;
     Ty *y = static_cast<Ty *>(a.y) + tok0 * rowX + pbase;
 
-    auto load_stage = [&](Stage<SPT, XPT> &st, int h) {
+    auto load_state = [&](Stage<SPT, XPT> &st, int h) {
         const float *hs = hp + h * (kN * kP);
 #pragma unroll
         for (int k = 0; k < SPT; ++k) {
@@ -156,6 +180,8 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
                     st.s[k][r] = *reinterpret_cast<const float2 *>(hs + (n8 + r) * kP + 2 * p2);
             }
         }
+    };
+    auto load_x = [&](Stage<SPT, XPT> &st, int h) {  // x, dt and the head's parameters
 #pragma unroll
         for (int k = 0; k < XPT; ++k) {
             const int i = tid + k * THREADS;
@@ -178,6 +204,10 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
         st.D = a.D[h];
         st.Ar = a.A_rev[h];
         st.Dr = a.D_rev ? a.D_rev[h] : 0.f;
+    };
+    auto load_stage = [&](Stage<SPT, XPT> &st, int h) {
+        load_state(st, h);
+        load_x(st, h);
     };
 
     auto store_stage = [&](const Stage<SPT, XPT> &st, int buf) {
@@ -240,20 +270,24 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
             const float Aw = wave == 0 ? st.A : st.Ar;  // the reverse scan has its own decay
             const float a0 = d0 * Aw, a1 = d1 * Aw;
             const float loc = a0 + a1;
-            float inc = loc;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float up = __shfl_up(inc, off, 64);
-                if (lane >= off)
-                    inc += up;
-            }
+            const float inc = wave_inclusive_sum(loc);
             const float excl = inc - loc;
-            const float total = __shfl(inc, 63, 64);
+            const float total = lane_value(inc, 63);
             // forward: c_t inclusive prefix sum; reference at the pair's last token
             // reverse: r_t inclusive suffix sum; reference at the pair's first token
             const float c0 = wave == 0 ? (excl + a0) * kLog2e : (total - excl) * kLog2e;
             const float c1 = wave == 0 ? (excl + loc) * kLog2e : (total - excl - a0) * kLog2e;
-            const float ref = wave == 0 ? __shfl(c1, lane | 15, 64) : __shfl(c0, lane & ~15, 64);
+            // the pair's last token (forward: lane 16k+15) or first token (reverse: lane 16k);
+            // the readlanes as separate statements (inside a conditional expression they
+            // would become branches), then a per-lane choice
+            const int row = lane >> 4;
+            const float f15 = lane_value(c1, 15), f31 = lane_value(c1, 31), f47 = lane_value(c1, 47),
+                        f63 = lane_value(c1, 63);
+            const float g00 = lane_value(c0, 0), g16 = lane_value(c0, 16), g32 = lane_value(c0, 32),
+                        g48 = lane_value(c0, 48);
+            const float reff = row == 0 ? f15 : row == 1 ? f31 : row == 2 ? f47 : f63;
+            const float refr = row == 0 ? g00 : row == 1 ? g16 : row == 2 ? g32 : g48;
+            const float ref = wave == 0 ? reff : refr;
             if (t0 < TP) {
                 float *cc = tab[buf][wave == 0 ? TAB_CF : TAB_CR];
                 float *lg = tab[buf][wave == 0 ? TAB_LGF : TAB_LGR];
@@ -328,6 +362,11 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
                 acc[pb] = mfma(cfw[kk], ld16(&hlo[pc * HS + 32 * kk + 8 * q]), acc[pb]);
             }
         }
+        // the rest of the next head's loads (its state was issued after the last barrier):
+        // spread out rather than queued all at once behind the barrier, and still ahead of
+        // this head's y stores
+        if (hh >= 1 && hh + 1 < hpw)
+            load_x(stage, h + 1);
         {
             const float4 e4 = *reinterpret_cast<const float4 *>(&ef[tb * 16 + 4 * q]);
 #pragma unroll
@@ -459,7 +498,7 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
             store_stage(stage, cur ^ 1);
         __syncthreads();
         if (hh + 2 < hpw)
-            load_stage(stage, h + 2);
+            load_state(stage, h + 2);
     }
 }
 
