@@ -21,12 +21,14 @@
 //     lane); x of both directions is read once and stored transposed in LDS;
 //   - the next head's state and x are already being loaded into registers while this
 //     head computes (software pipelining across the head loop);
-//   - each wavefront accumulates C.(h_hi + h_lo) on the matrix cores, scales rows by
-//     exp(c_t), builds the decay-masked A operands M = S o exp2(..) o dt from its register
-//     tiles, accumulates M X for both directions, adds D x and writes y once.
+//   - each wavefront accumulates y^T = (h_hi + h_lo)^T C^T on the matrix cores, scales by
+//     exp(c_t), builds the decay-masked operands M = S o exp2(..) o dt from its register
+//     tiles, accumulates X^T M^T for both directions, adds D x and writes y once. The
+//     outputs are transposed so that a lane holds four consecutive columns of one token
+//     and stores them as one 8-byte (bf16) or 16-byte (fp32) piece.
 // The k-index of the M X products is permuted (lane slots j = 0..3 take s-block 2m, slots
-// 4..7 s-block 2m+1) so that the score tiles' accumulator layout is directly the A-operand
-// layout; the X operand uses the same permutation.
+// 4..7 s-block 2m+1) so that the score tiles' accumulator layout is directly the operand
+// layout of M^T; the X operand uses the same permutation.
 #include "internal.h"
 
 namespace bdssm {
@@ -54,8 +56,18 @@ __device__ __forceinline__ float bf2f(__bf16 v) { return static_cast<float>(v); 
 __device__ __forceinline__ bf16x8 sel8(bool ok, bf16x8 v) { return ok ? v : bf16x8{}; }
 __device__ __forceinline__ uint4 sel4(bool ok, uint4 v) { return ok ? v : make_uint4(0, 0, 0, 0); }
 
-__device__ __forceinline__ void store_out(float *p, float v) { *p = v; }
-__device__ __forceinline__ void store_out(__bf16 *p, float v) { *p = static_cast<__bf16>(v); }
+__device__ __forceinline__ void store4(float *p, const float (&v)[4])
+{
+    *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store4(__bf16 *p, const float (&v)[4])
+{
+    bf16x4 b;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        b[j] = static_cast<__bf16>(v[j]);
+    *reinterpret_cast<bf16x4 *>(p) = b;
+}
 
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ float dpp_move(float x)
@@ -92,10 +104,9 @@ struct Geo {
     static constexpr int THREADS = 64 * UNITS;
     static constexpr int YW = PBW * 16;       // columns of a unit's output tile
     // LDS row strides (bf16 elements): transposed state [PW][HS] (16-byte operand reads),
-    // transposed x [PW][XS] (8-byte operand reads), output tile [16][YS]
+    // transposed x [PW][XS] (8-byte operand reads)
     static constexpr int HS = kN + 8;
     static constexpr int XS = TP + 4;
-    static constexpr int YS = YW + 8;
     // global-load items: state = 8 rows x 2 columns, x = 4 tokens x 8 columns
     static constexpr int SITEMS = (kN / 8) * (PW / 2);
     static constexpr int XITEMS = (TP / 4) * (PW / 8);  // per direction
@@ -123,10 +134,8 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
 {
     using Gm = Geo<NB, PS>;
     constexpr int TP = Gm::TP, PW = Gm::PW, PBW = Gm::PBW, PGRP = Gm::PGRP, THREADS = Gm::THREADS,
-                  HS = Gm::HS, XS = Gm::XS, YS = Gm::YS, YW = Gm::YW, SITEMS = Gm::SITEMS,
+                  HS = Gm::HS, XS = Gm::XS, YW = Gm::YW, SITEMS = Gm::SITEMS,
                   XITEMS = Gm::XITEMS, SPT = Gm::SPT, XPT = Gm::XPT, UNITS = Gm::UNITS;
-    // bf16 outputs leave through a per-wavefront LDS tile as 16-byte row stores
-    constexpr bool YSTAGE = sizeof(Ty) == 2;
     // two buffers: the next head is staged while the current one is being computed
     __shared__ __attribute__((aligned(16))) __bf16 hT_hi[2][PW * HS];
     __shared__ __attribute__((aligned(16))) __bf16 hT_lo[2][PW * HS];
@@ -134,7 +143,6 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
     __shared__ __attribute__((aligned(16))) __bf16 XTr[2][PW * XS];
     __shared__ __attribute__((aligned(16))) float tab[2][NTAB][TP];
     __shared__ float hd[2], hdr[2];  // D and the reverse skip weight of the head in each buffer
-    __shared__ __attribute__((aligned(16))) __bf16 ybuf[YSTAGE ? UNITS * 16 * YS : 8];
 
     // Workgroups sharing a stream (and so its B, C) go to the same XCD: the hardware
     // deals linear workgroup ids round-robin over the 8 XCDs.
@@ -358,8 +366,8 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
 #pragma unroll
             for (int pb = 0; pb < PBW; ++pb) {
                 const int pc = (pgrp * PBW + pb) * 16 + r16;
-                acc[pb] = mfma(cfw[kk], ld16(&hhi[pc * HS + 32 * kk + 8 * q]), acc[pb]);
-                acc[pb] = mfma(cfw[kk], ld16(&hlo[pc * HS + 32 * kk + 8 * q]), acc[pb]);
+                acc[pb] = mfma(ld16(&hhi[pc * HS + 32 * kk + 8 * q]), cfw[kk], acc[pb]);
+                acc[pb] = mfma(ld16(&hlo[pc * HS + 32 * kk + 8 * q]), cfw[kk], acc[pb]);
             }
         }
         // the rest of the next head's loads (its state was issued after the last barrier):
@@ -368,14 +376,10 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
         if (hh >= 1 && hh + 1 < hpw)
             load_x(stage, h + 1);
         {
-            const float4 e4 = *reinterpret_cast<const float4 *>(&ef[tb * 16 + 4 * q]);
+            const float et = ef[t];  // exp(c_t) of this lane's token
 #pragma unroll
-            for (int pb = 0; pb < PBW; ++pb) {
-                acc[pb][0] *= e4.x;
-                acc[pb][1] *= e4.y;
-                acc[pb][2] *= e4.z;
-                acc[pb][3] *= e4.w;
-            }
+            for (int pb = 0; pb < PBW; ++pb)
+                acc[pb] *= et;
         }
         auto mx = [&](const bf16x8 &af, const __bf16 *XT, int m) {
 #pragma unroll
@@ -384,7 +388,7 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
                 const __bf16 *xp = &XT[pc * XS + 32 * m + 4 * q];
                 const bf16x4 lo4 = *reinterpret_cast<const bf16x4 *>(xp);
                 const bf16x4 hi4 = *reinterpret_cast<const bf16x4 *>(xp + 16);
-                acc[pb] = mfma(af, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7), acc[pb]);
+                acc[pb] = mfma(__builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7), af, acc[pb]);
             }
         };
         // eq. (11), inside the block (s <= t). Pairs wholly below the row block use the
@@ -451,46 +455,23 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
                 mx(af, xtr, m);
             }
         }
-        // eq. (13) + D x, written once: the lane holds rows tb*16 + 4q + j of column pc
+        // eq. (13) + D x, written once: the lane holds y[t][pcb + 4q .. pcb + 4q + 3] of each
+        // 16-column block pcb and leaves it as one 8-byte (bf16) or 16-byte (fp32) store
         // (+ D_rev x_rev when the reverse direction has its own skip term)
         const float Dh = hd[cur], Dr = hdr[cur];
         const bool with_dr = a.D_rev != nullptr;
-        auto skip = [&](int pc, int tr, float v) {
-            v = fmaf(Dh, bf2f(xtf[pc * XS + tr]), v);
-            return with_dr ? fmaf(Dr, bf2f(xtr[pc * XS + tr]), v) : v;
-        };
         Ty *yh = y + h * kP + pgrp * YW;
-        if constexpr (YSTAGE) {
-            __bf16 *yt = &ybuf[wave * 16 * YS];
 #pragma unroll
-            for (int pb = 0; pb < PBW; ++pb) {
-                const int pc = (pgrp * PBW + pb) * 16 + r16;
+        for (int pb = 0; pb < PBW; ++pb) {
+            const int pcb = (pgrp * PBW + pb) * 16 + 4 * q;
+            float o[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int tr = tb * 16 + 4 * q + j;
-                    yt[(4 * q + j) * YS + pb * 16 + r16] = static_cast<__bf16>(skip(pc, tr, acc[pb][j]));
-                }
+            for (int j = 0; j < 4; ++j) {
+                float v = fmaf(Dh, bf2f(xtf[(pcb + j) * XS + t]), acc[pb][j]);
+                o[j] = with_dr ? fmaf(Dr, bf2f(xtr[(pcb + j) * XS + t]), v) : v;
             }
-            // the wavefront reads back its own tile: rows of YW bf16 in 16-byte pieces
-            constexpr int CPR = YW / 8, CHUNKS = 16 * CPR;
-#pragma unroll
-            for (int c0 = 0; c0 < CHUNKS; c0 += 64) {
-                const int c = c0 + lane, row = c / CPR, col = (c % CPR) * 8;
-                if ((CHUNKS % 64 == 0 || c < CHUNKS) && tb * 16 + row < T)
-                    *reinterpret_cast<uint4 *>(yh + (tb * 16 + row) * rowX + col) =
-                        *reinterpret_cast<const uint4 *>(&yt[row * YS + col]);
-            }
-        } else {
-#pragma unroll
-            for (int pb = 0; pb < PBW; ++pb) {
-                const int pc = (pgrp * PBW + pb) * 16 + r16;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int tr = tb * 16 + 4 * q + j;
-                    if (tr < T)
-                        store_out(yh + tr * rowX + pb * 16 + r16, skip(pc, tr, acc[pb][j]));
-                }
-            }
+            if (t < T)
+                store4(yh + t * rowX + pb * 16 + 4 * q, o);
         }
         // stage the next head into the other buffer (its previous contents were last read
         // before the barrier that ended the previous head), then sync, then prefetch
