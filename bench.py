@@ -317,6 +317,7 @@ def main():
         out["conv_state"] = conv_workloads(torch, bdssm, cfg, inputs, d, h, steps, Ad, Dd, y_blk, pre, L,
                                            avg_us["block_step"])
         out["secondary"] = secondary(torch, np, bdssm, configs, inputs)
+        out["extra"] = extra(torch, np, bdssm, configs, inputs)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(np, cfg, A, D, pre_np, steps_np, clean_np)
     print(json.dumps(out), flush=True)
@@ -374,6 +375,105 @@ def conv_workloads(torch, bdssm, cfg, inputs, d, h, steps, Ad, Dd, y_blk, pre, L
                             "roofline": make_roofline("hbm", nb, conv_us, None)}}
 
 
+def prefix_flops_causal(b, H, P, N, G, L, Q):
+    """As prefix_flops, counting only the causal half (s <= t) of the quadratic products."""
+    nch = -(-L // Q)
+    hpg = H // G
+    tri = Q * (Q + 1) / 2
+    per = 2 * tri * N / hpg + 2 * tri * P + 2 * Q * N * P + 2 * Q * N * P
+    return b * nch * H * per
+
+
+def graph_us(torch, fn, reps=10, warm=2):
+    """Average time of fn() captured as one HIP graph, replayed `reps` times (HIP events)."""
+    g = capture(torch, fn)
+    for _ in range(warm):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return 1e3 * e0.elapsed_time(e1) / reps
+
+
+def extra(torch, np, bdssm, configs, inputs):
+    """The remaining figures of the measurement plan: the block step as a single launch
+    (median of 20 after 5 warm-ups), with every buffer cold (rotation over more than the
+    256 MiB last-level cache) and cache-resident, at configs 0 and 3; the commit chain."""
+    res = {}
+    c1 = configs.get(1)
+    b, H, P, N, G, T = c1.batch, c1.nheads, c1.headdim, c1.d_state, c1.ngroups, c1.block_len
+    A, D = inputs.params(c1)
+    Ad, Dd = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
+    d = bdssm.dims(b, H, P, N, G, c1.in_dtype, bdssm.BF16)
+    f = bdssm.seq_to_device(inputs.block(c1, 0, 0, inputs.FWD))
+    r = bdssm.seq_to_device(inputs.block(c1, 0, 0, inputs.REV))
+    h = torch.randn((b, H, N, P), device="cuda") * 0.05
+    y = torch.empty((b, T, H, P), dtype=torch.bfloat16, device="cuda")
+    ts = []
+    for i in range(25):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        bdssm.block_step(d, T, h, f, r, Ad, Dd, y)
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= 5:
+            ts.append(1e3 * e0.elapsed_time(e1))
+    res["block_step_single_launch"] = {"workload": "700M shape, T=32, one launch between synchronizations",
+                                       "median_us": round(float(np.median(ts)), 3)}
+    # cold: 256 sets of (state, inputs, y), about 540 MB, one launch each; warm: one set
+    nset = 256
+    sets = []
+    for k in range(nset):
+        sets.append((torch.randn((b, H, N, P), device="cuda") * 0.05,
+                     tuple(t.clone() for t in f), tuple(t.clone() for t in r),
+                     torch.empty_like(y)))
+    cold = graph_us(torch, lambda: [bdssm.block_step(d, T, hh, ff, rr, Ad, Dd, yy) for hh, ff, rr, yy in sets]) / nset
+    warm = graph_us(torch, lambda: [bdssm.block_step(d, T, h, f, r, Ad, Dd, y) for _ in range(nset)]) / nset
+    nb = block_step_bytes(b, H, P, N, G, T, 2, 2)
+    res["block_step_cold_warm"] = {"workload": "700M shape, T=32, 256 launches in one graph",
+                                   "cold_us": round(cold, 3), "warm_us": round(warm, 3),
+                                   "rotation_bytes": nset * nb}
+    del sets
+    # configs 3 and 0: 64 (resp. 4) steps with distinct inputs in one graph
+    for ci in (3, 0):
+        c = configs.get(ci)
+        b, H, P, N, G, T = c.batch, c.nheads, c.headdim, c.d_state, c.ngroups, c.block_len
+        A, D = inputs.params(c)
+        Ad3, Dd3 = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
+        yd = bdssm.BF16 if c.in_dtype == 1 else bdssm.F32
+        d3 = bdssm.dims(b, H, P, N, G, c.in_dtype, yd)
+        S = c.steps_per_block
+        st = [(bdssm.seq_to_device(inputs.block(c, 0, k, inputs.FWD)), bdssm.seq_to_device(inputs.block(c, 0, k, inputs.REV)))
+              for k in range(S)]
+        hh = torch.randn((b, H, N, P), device="cuda") * 0.05
+        ys = [torch.empty((b, T, H, P), dtype=torch.bfloat16 if yd == bdssm.BF16 else torch.float32, device="cuda")
+              for _ in range(S)]
+        us = graph_us(torch, lambda: [bdssm.block_step(d3, T, hh, ff, rr, Ad3, Dd3, yy) for (ff, rr), yy in zip(st, ys)]) / S
+        ib = 2 if c.in_dtype == 1 else 4
+        nb = block_step_bytes(b, H, P, N, G, T, ib, ib)
+        res[f"block_step_config{ci}"] = {"workload": c.name, "us_per_step": round(us, 3),
+                                         "active_tokens_per_s": round(b * T / (us * 1e-6), 1),
+                                         "hbm_frac": round(nb / (us * 1e-6) / HBM_PEAK, 4), "alg_bytes": nb}
+    # commit chain, config 2: 2048 commits of 32 tokens over the 65,536-token prefix
+    c2 = configs.get(2)
+    b, H, P, N, G, L, T = c2.batch, c2.nheads, c2.headdim, c2.d_state, c2.ngroups, c2.prefix_len, c2.commit_len
+    A, D = inputs.params(c2)
+    Ad2, Dd2 = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
+    d2 = bdssm.dims(b, H, P, N, G, c2.in_dtype, bdssm.BF16)
+    pre = bdssm.seq_to_device(inputs.prefix(c2))
+    blocks = [tuple(t[:, k * T:(k + 1) * T].contiguous() for t in pre) for k in range(L // T)]
+    hc = torch.zeros((b, H, N, P), device="cuda")
+    us = graph_us(torch, lambda: [bdssm.commit(d2, T, blk, Ad2, Dd2, hc) for blk in blocks], reps=3, warm=1)
+    res["commit_chain_config2"] = {"workload": "2,048 commits of 32 tokens (350M shape), one graph",
+                                   "us_per_commit": round(us / len(blocks), 3),
+                                   "tokens_per_s": round(L / (us * 1e-6), 1)}
+    return res
+
+
 def secondary(torch, np, bdssm, configs, inputs, reps=20):
     res = []
     # 64-stream running set: T = 128, fp32 state per stream (values do not affect timing;
@@ -421,6 +521,7 @@ def secondary(torch, np, bdssm, configs, inputs, reps=20):
     res.append({"workload": "prefix scan, 350M shape, 65,536 tokens, chunk 256, bf16 y + fp32 chunk states",
                 "avg_us": round(us, 3), "prefix_tokens_per_s": round(b * L / (us * 1e-6), 1),
                 "roofline": make_roofline("mfma", fl, us, traffic_for("prefix_scan_c2")),
+                "mfma_frac_causal_count": round(prefix_flops_causal(b, H, P, N, G, L, Q) / (us * 1e-6) / MFMA_BF16_PEAK, 4),
                 "hbm_frac": round(nb / (us * 1e-6) / HBM_PEAK, 4), "alg_bytes": nb, "flops": fl})
     return res
 
