@@ -3,26 +3,28 @@
 // matrix form of the Mamba-2 scan), laid out for latency instead of bandwidth.
 //
 // With few (stream, head) pairs a launch has about one wavefront per SIMD, and its time is
-// the length of one wavefront's chain of dependent steps, not the bytes it moves. So each
-// wavefront is its own workgroup and owns one 16-token row block, one 16-column block and
-// one head, and everything it needs goes from global memory straight into registers in the
-// layout the matrix cores read:
-//   - the cached state as the B operand of C . h: lane (column p, quarter q) loads
-//     h[32k + 8q + e][p], e = 0..7, as single dwords -- eight consecutive contraction
-//     indices of its column, the bf16 operand layout as loaded -- and splits it into bf16
-//     hi + lo parts in registers (two products, ~16 significant bits);
-//   - x of both directions as the B operand of M X: 8-byte row pieces transposed 4 x 4
-//     (16-bit) across lanes with DPP, giving each lane the tokens of its slots
-//     (4q + e, 16 + 4q + e) in its column; the same registers give D x;
-//   - the C B^T score tiles as in the bandwidth kernel (B rows as A, C rows as B operand).
-// The cumulative log-decays of both directions are a 64-lane DPP scan in the same
-// wavefront, shared through a small wavefront-private LDS table. There is no workgroup
-// barrier, no state or x staging through LDS, and y leaves straight from the accumulators.
-// Loads and stores go through range-checked buffer resources over the stream's T tokens, so
-// rows past T read as zero and their stores are dropped, with no clamping or masking code
-// (at about one wavefront per SIMD, every vector instruction is on the critical path). All
-// loads are issued before the first use, fewer than a wavefront can have in flight (63), so
-// the wavefront waits for memory once.
+// the length of one wavefront's chain of dependent steps, not the bytes it moves. A
+// workgroup owns one (head, 16-token row block) and its four wavefronts one 16-column
+// block each. What dominates that chain is getting the inputs in: a load whose 64 lanes
+// touch 16 rows for 64 bytes each costs the L1 several times what the same bytes cost in
+// whole 128-byte lines, and the matrix-core operand layouts are of that first kind. So
+// every input the workgroup needs -- the B and C rows of its score tiles, the cached fp32
+// state of the head and x of both directions -- is copied once, in whole lines, straight
+// into LDS (gfx950 buffer loads to LDS, no registers on the way; 19 loads per wavefront,
+// each wavefront a quarter of each tile), with the 16-byte pieces of each row permuted
+// so that the operand reads that follow are free of bank conflicts:
+//   - B and C rows as A/B operands of the C B^T score tiles (16-byte reads);
+//   - the state as the B operand of C . h: lane (column p, quarter q) reads h[32k + 8q + e][p],
+//     e = 0..7, and splits it into bf16 hi + lo parts in registers (two products, ~16
+//     significant bits);
+//   - x as the B operand of M X by transposing reads (gfx950 ds_read_b64_tr_b16), giving
+//     each lane the tokens of its slots (4q + e, 16 + 4q + e) in its column; the same
+//     registers give D x.
+// The cumulative log-decays of both directions are a 64-lane DPP scan that every wavefront
+// computes for itself into its own small table. One workgroup barrier (after the copies);
+// y leaves straight from the accumulators. Loads and stores go through range-checked
+// buffer resources over the stream's T tokens, so rows past T read as zero and their
+// stores are dropped (LDS rows past T are cleared in a branch taken only for short blocks).
 #include "internal.h"
 #include "mfma_tiles.h"
 
@@ -62,36 +64,33 @@ __device__ __forceinline__ uint32_t quad_move(uint32_t x)
     return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, 0xf, 0xf, false));
 }
 
-// 4 x 4 transpose of 16-bit values inside each group of four lanes. Lane i holds row i as
-// two dwords (columns 0,1 | 2,3, the lower column in the lower half) and receives column i
-// as rows 0,1 | 2,3. First lanes i^2 swap the dword with the other column pair, then lanes
-// i^1 swap the 16-bit halves of the other column; v_perm with per-lane selectors puts the
-// four rows in order.
-__device__ __forceinline__ uint2 quad_transpose16(uint2 v, int i)
-{
-    const bool b0 = i & 1, b1 = i & 2;
-    const uint32_t keep = b1 ? v.y : v.x, send = b1 ? v.x : v.y;
-    const uint32_t oth = quad_move<0x4E>(send);  // quad_perm 2,3,0,1: row i^2, same columns
-    // column 2*b1 + b0 of rows (i, i^2) is kept, the other column of them is sent to lane i^1
-    const uint32_t kept = __builtin_amdgcn_perm(oth, keep, b0 ? 0x07060302u : 0x05040100u);
-    const uint32_t snd = __builtin_amdgcn_perm(oth, keep, b0 ? 0x05040100u : 0x07060302u);
-    const uint32_t rcv = quad_move<0xB1>(snd);  // quad_perm 1,0,3,2: rows (i^1, i^3)
-    // rows (2m, 2m+1): from (kept.lo, rcv.lo) when m == b1, (kept.hi, rcv.hi) otherwise,
-    // with the two swapped when b0 is set
-    const uint32_t L = __builtin_amdgcn_perm(rcv, kept, b0 ? 0x01000504u : 0x05040100u);
-    const uint32_t Hh = __builtin_amdgcn_perm(rcv, kept, b0 ? 0x03020706u : 0x07060302u);
-    return make_uint2(b1 ? Hh : L, b1 ? L : Hh);
-}
-
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes)
 {
     // raw buffer with range checking: loads past `bytes` return zero, stores are dropped
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), 0x00020000);
 }
 
-__device__ __forceinline__ bf16x8 ld_b128(__amdgpu_buffer_rsrc_t r, int off)
+// Copies one 1 KB piece of global memory into LDS without passing through registers
+// (gfx950 buffer_load ... lds): lane l's 16 bytes from byte offset `off` land at
+// dst + 16 l. Bytes past the buffer's range read as zero.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *dst, int off)
 {
-    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, off, 0, 0, 0);
+}
+
+// LDS tiles, each filled by whole-line copies (a load that touches few lines in full costs
+// the L1 several times less than one that touches many in part), with the 16-byte pieces
+// of a row permuted (an XOR of the piece index) so that the operand reads below fall in
+// distinct banks:
+//   row block: 16 rows of N = 128 bf16 (B or C), piece c of row r at slot c ^ r;
+//   state:     N x P fp32, piece c (4 columns) of row n at slot c ^ 4 ((n / 8) % 4);
+//   x:         T x P bf16 per direction, piece c (8 columns) of row t at slot c ^ 2 (t % 4).
+constexpr int kRowBlk = 16 * 128;
+
+// Operand fragment of row r16 of a row block: n = 32 kk + 8 q .. +7
+__device__ __forceinline__ bf16x8 rows_frag(const __bf16 *blk, int kk, int q, int r16)
+{
+    return *reinterpret_cast<const bf16x8 *>(blk + 8 * (16 * r16 + ((4 * kk + q) ^ r16)));
 }
 
 __device__ __forceinline__ void store_y(__amdgpu_buffer_rsrc_t r, int off, float v)
@@ -106,26 +105,29 @@ __device__ __forceinline__ void store_y_bf16(__amdgpu_buffer_rsrc_t r, int off, 
 enum { TAB_CF, TAB_CR, TAB_LGF, TAB_LGR, TAB_COLF, TAB_COLR, TAB_EF, NTAB };
 
 template <typename Ty>
-__global__ __launch_bounds__(64) void k_block_lat(BlockArgs a)
+__global__ __launch_bounds__(256) void k_block_lat(BlockArgs a)
 {
     constexpr int NB = 2, TP = 32;  // one 32-token pair: two 16-token row blocks
-    __shared__ __attribute__((aligned(16))) float tab[NTAB][TP];
+    // C rows of the row block (forward, reverse), then B rows of its three score tiles
+    __shared__ __attribute__((aligned(16))) __bf16 rows[NB + 3][kRowBlk];
+    __shared__ __attribute__((aligned(16))) float hst[kN * kP];        // the cached state
+    __shared__ __attribute__((aligned(16))) __bf16 xs[2][TP * kP];      // x, both directions
+    __shared__ __attribute__((aligned(16))) float tab[4][NTAB][TP];     // per wavefront
 
     const int T = a.T, H = a.s.H, G = a.s.G;
-    // The hardware deals workgroup ids round-robin over the 8 XCDs. The 8 wavefronts of one
-    // (stream, head) read the same state and x lines (each a quarter row), so they are given
-    // ids that land on one XCD and share its L2: logical id = position within the XCD's
-    // consecutive range.
-    const int nwg = gridDim.x;
+    // workgroup = (head, row block), grid.y = stream. The hardware deals workgroup ids
+    // round-robin over the 8 XCDs; the two row blocks of a head read the same state and x,
+    // so they get consecutive logical ids within one XCD's range and share its L2.
+    const int nx = gridDim.x;
     int wid = blockIdx.x;
-    if ((nwg & 7) == 0)
-        wid = (wid & 7) * (nwg >> 3) + (wid >> 3);
-    const int tb = wid % NB;
-    const int pblk = (wid / NB) % (kP / 16);
-    const int h = (wid / (NB * (kP / 16))) % H;
-    const int b = wid / (NB * (kP / 16) * H);
-    const int g = h / (H / G);
-    const int lane = threadIdx.x, q = lane >> 4, r16 = lane & 15, i4 = lane & 3;
+    if ((nx & 7) == 0)
+        wid = (wid & 7) * (nx >> 3) + (wid >> 3);
+    const int tb = wid & 1, h = wid >> 1, b = blockIdx.y;
+    const int g = G == 1 ? 0 : h / (H / G);
+    // wavefront = 16-column block of the outputs (uniform, so that LDS copy addresses are
+    // scalar)
+    const int pblk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, q = lane >> 4, r16 = lane & 15;
     const int t = tb * 16 + r16;  // this lane's row as an A operand
     const int p = pblk * 16 + r16;
 
@@ -147,38 +149,26 @@ __global__ __launch_bounds__(64) void k_block_lat(BlockArgs a)
     const auto rDr = rsrc(static_cast<const __bf16 *>(a.rev.dt) + tok0 * H + h, dt_bytes);
     const auto rH = rsrc(a.h_prefix + (static_cast<int64_t>(b) * H + h) * (kN * kP), kN * kP * 4);
 
-    // ---- every load of the wavefront (60, fewer than a wavefront can have in flight),
-    // issued before any of them is used
-    bf16x8 cfw[4], crv[4];
+    // ---- the workgroup's inputs, each byte copied once, in whole lines, straight into
+    // LDS: this wavefront copies a quarter of each tile (19 loads in all)
+    auto row0_of = [&](int i) {  // first row of row block i
+        return i < 2 ? tb * 16 : (i - 2 <= tb ? i - 2 : i - 3) * 16;
+    };
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        cfw[kk] = ld_b128(rCf, (t * rowBC + 32 * kk + 8 * q) * 2);
-        crv[kk] = ld_b128(rCr, (t * rowBC + 32 * kk + 8 * q) * 2);
+    for (int i = 0; i < NB + 3; ++i) {  // quarter pblk: rows 4 pblk .. 4 pblk + 3
+        const auto r = i == 0 ? rCf : i == 1 ? rCr : (i - 2 <= tb ? rBf : rBr);
+        const int rl = 4 * pblk + (lane >> 4), piece = (lane & 15) ^ rl;
+        dma16(r, &rows[i][4 * pblk * 128], ((row0_of(i) + rl) * rowBC + 8 * piece) * 2);
     }
-    bf16x8 bfr[NB + 1][4];
 #pragma unroll
-    for (int ut = 0; ut <= NB; ++ut) {
-        const bool fwd = ut <= tb;
-        const int srow = (fwd ? ut : ut - 1) * 16 + r16;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            bfr[ut][kk] = ld_b128(fwd ? rBf : rBr, (srow * rowBC + 32 * kk + 8 * q) * 2);
+    for (int m = 0; m < 8; ++m) {  // state rows 32 pblk + 4 m .. +3
+        const int n = 32 * pblk + 4 * m + (lane >> 4), c = (lane & 15) ^ (4 * ((n >> 3) & 3));
+        dma16(rH, &hst[(32 * pblk + 4 * m) * kP], (n * kP + 4 * c) * 4);
     }
-    // the cached state as B operands of the state product: h[32kk + 8q + e][p]
-    float hv[4][8];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            hv[kk][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rH, ((32 * kk + 8 * q + e) * kP + p) * 4, 0, 0));
-    // x: lane 4c + i loads columns 4c .. 4c+3 of token 4q + i (and 16 + 4q + i); a 16-bit
-    // 4 x 4 transpose in each group of four lanes gives tokens 4q .. 4q+3 of its own column
-    uint2 xl[2][2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int off = ((16 * u + 4 * q + i4) * rowX + pblk * 16 + (r16 & ~3)) * 2;
-        xl[0][u] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rXf, off, 0, 0));
-        xl[1][u] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rXr, off, 0, 0));
+    for (int d = 0; d < 2; ++d) {  // x rows 8 pblk .. 8 pblk + 7 of each direction
+        const int tr = 8 * pblk + (lane >> 3), c = (lane & 7) ^ (2 * (tr & 3));
+        dma16(d ? rXr : rXf, &xs[d][8 * pblk * kP], (tr * rowX + 8 * c) * 2);
     }
     const int t0 = 2 * lane, t1 = t0 + 1;
     const unsigned short df0 = __builtin_amdgcn_raw_buffer_load_b16(rDf, t0 * H * 2, 0, 0);
@@ -188,7 +178,9 @@ __global__ __launch_bounds__(64) void k_block_lat(BlockArgs a)
     const float Ah = a.A[h], Dh = a.D[h], Ar = a.A_rev[h];
     const float Dr = a.D_rev ? a.D_rev[h] : 0.f;
 
-    // ---- decay tables of both directions (lane l holds tokens 2l and 2l+1; dt past T is 0)
+    // ---- decay tables of both directions (lane l holds tokens 2l and 2l+1; dt past T is 0),
+    // computed by every wavefront into its own table
+    float(*tb_)[TP] = tab[pblk];
     {
         const float f0 = __uint_as_float(static_cast<uint32_t>(df0) << 16);
         const float f1 = __uint_as_float(static_cast<uint32_t>(df1) << 16);
@@ -204,24 +196,46 @@ __global__ __launch_bounds__(64) void k_block_lat(BlockArgs a)
         const float r0 = (totr - exclr) * kLog2e, r1 = (totr - exclr - b0) * kLog2e;
         const float reff = lane_value(c1, 15), refr = lane_value(r0, 0);
         if (t0 < TP) {
-            tab[TAB_CF][t0] = c0;
-            tab[TAB_CF][t1] = c1;
-            tab[TAB_CR][t0] = r0;
-            tab[TAB_CR][t1] = r1;
-            tab[TAB_LGF][t0] = __builtin_amdgcn_logf(f0) - c0;
-            tab[TAB_LGF][t1] = __builtin_amdgcn_logf(f1) - c1;
-            tab[TAB_LGR][t0] = __builtin_amdgcn_logf(g0) - r0;
-            tab[TAB_LGR][t1] = __builtin_amdgcn_logf(g1) - r1;
-            tab[TAB_COLF][t0] = __builtin_amdgcn_exp2f(reff - c0) * f0;
-            tab[TAB_COLF][t1] = __builtin_amdgcn_exp2f(reff - c1) * f1;
-            tab[TAB_COLR][t0] = __builtin_amdgcn_exp2f(refr - r0) * g0;
-            tab[TAB_COLR][t1] = __builtin_amdgcn_exp2f(refr - r1) * g1;
-            tab[TAB_EF][t0] = __builtin_amdgcn_exp2f(c0);
-            tab[TAB_EF][t1] = __builtin_amdgcn_exp2f(c1);
+            tb_[TAB_CF][t0] = c0;
+            tb_[TAB_CF][t1] = c1;
+            tb_[TAB_CR][t0] = r0;
+            tb_[TAB_CR][t1] = r1;
+            tb_[TAB_LGF][t0] = __builtin_amdgcn_logf(f0) - c0;
+            tb_[TAB_LGF][t1] = __builtin_amdgcn_logf(f1) - c1;
+            tb_[TAB_LGR][t0] = __builtin_amdgcn_logf(g0) - r0;
+            tb_[TAB_LGR][t1] = __builtin_amdgcn_logf(g1) - r1;
+            tb_[TAB_COLF][t0] = __builtin_amdgcn_exp2f(reff - c0) * f0;
+            tb_[TAB_COLF][t1] = __builtin_amdgcn_exp2f(reff - c1) * f1;
+            tb_[TAB_COLR][t0] = __builtin_amdgcn_exp2f(refr - r0) * g0;
+            tb_[TAB_COLR][t1] = __builtin_amdgcn_exp2f(refr - r1) * g1;
+            tb_[TAB_EF][t0] = __builtin_amdgcn_exp2f(c0);
+            tb_[TAB_EF][t1] = __builtin_amdgcn_exp2f(c1);
         }
     }
+    if (T < TP) {
+        // rows past T: whatever the copies left in LDS there is replaced by zeros, each
+        // wavefront in the pieces it copied (the wait orders these writes after its copies)
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        const uint4 z = make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < NB + 3; ++i)
+            if (row0_of(i) + 4 * pblk + (lane >> 4) >= T)
+                *reinterpret_cast<uint4 *>(&rows[i][4 * pblk * 128 + 8 * lane]) = z;
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+            if (8 * pblk + (lane >> 3) >= T)
+                *reinterpret_cast<uint4 *>(&xs[d][8 * pblk * kP + 8 * lane]) = z;
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's copies have landed
+    __syncthreads();                      // and so have everyone's
 
     // ---- score tiles of the row block: S[t = tb*16 + r16][s = sb*16 + 4q + j]
+    bf16x8 cfw[4], crv[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        cfw[kk] = rows_frag(rows[0], kk, q, r16);
+        crv[kk] = rows_frag(rows[1], kk, q, r16);
+    }
     f32x4 S[NB + 1];
 #pragma unroll
     for (int ut = 0; ut <= NB; ++ut) {
@@ -229,40 +243,53 @@ __global__ __launch_bounds__(64) void k_block_lat(BlockArgs a)
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
-            acc = mfma(bfr[ut][kk], fwd ? cfw[kk] : crv[kk], acc);
+            acc = mfma(rows_frag(rows[2 + ut], kk, q, r16), fwd ? cfw[kk] : crv[kk], acc);
         S[ut] = acc;
     }
 
-    // ---- eq. (11), cached-state term: C_t . (h_hi + h_lo). The dword loads gave each lane
-    // h[32kk + 8q + e][p], e = 0..7: the B operand layout of the bf16 product as loaded, so
-    // the state is split in registers; two independent chains
+    // ---- eq. (11), cached-state term: C_t . (h_hi + h_lo), the B operand of column p being
+    // h[32kk + 8q + e][p], e = 0..7, split into bf16 halves in registers; two independent chains
     f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc_lo = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
+        // row n = 32kk + 8q + e, piece p/4 at slot (p/4) ^ 4q: column p sits at 16 (pblk ^ q) + r16
+        const float *hp = &hst[(32 * kk + 8 * q) * kP + 16 * (pblk ^ q) + r16];
+        float hv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            hv[e] = hp[e * kP];
         bf16x8 hi, lo;
-        split8(hv[kk], hi, lo);
+        split8(hv, hi, lo);
         acc = mfma(cfw[kk], hi, acc);
         acc_lo = mfma(cfw[kk], lo, acc_lo);
     }
     acc += acc_lo;
-    __syncthreads();  // the tables (one wavefront: a wavefront barrier)
     {
-        const float4 e4 = *reinterpret_cast<const float4 *>(&tab[TAB_EF][tb * 16 + 4 * q]);
+        const float4 e4 = *reinterpret_cast<const float4 *>(&tb_[TAB_EF][tb * 16 + 4 * q]);
         acc[0] *= e4.x;
         acc[1] *= e4.y;
         acc[2] *= e4.z;
         acc[3] *= e4.w;
     }
-    // x operands: slots 0..3 tokens 4q + j, slots 4..7 tokens 16 + 4q + j, column p
-    const uint2 f0 = quad_transpose16(xl[0][0], i4), f1 = quad_transpose16(xl[0][1], i4);
-    const uint2 v0 = quad_transpose16(xl[1][0], i4), v1 = quad_transpose16(xl[1][1], i4);
-    const bf16x8 xvf = __builtin_bit_cast(bf16x8, make_uint4(f0.x, f0.y, f1.x, f1.y));
-    const bf16x8 xvr = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+    // x operands: slots 0..3 tokens 4q + j, slots 4..7 tokens 16 + 4q + j, column p, by
+    // transposing reads (lane r16 addresses row 4q + r16/4, columns 16 pblk + 4 (r16 % 4) ..)
+    bf16x8 xv[2];
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+        bf16x4 half[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int tr = 16 * u + 4 * q + (r16 >> 2), col = 16 * pblk + 4 * (r16 & 3);
+            half[u] = tr_read(&xs[d][tr * kP + 8 * ((col >> 3) ^ (2 * (tr & 3))) + (col & 7)]);
+        }
+        xv[d] = cat(half[0], half[1]);
+    }
+    const bf16x8 xvf = xv[0], xvr = xv[1];
     // eq. (11), inside the block (s <= t), exp2 per element on the diagonal pair
     {
-        const float ctf = tab[TAB_CF][t];
-        const float4 l0 = *reinterpret_cast<const float4 *>(&tab[TAB_LGF][4 * q]);
-        const float4 l1 = *reinterpret_cast<const float4 *>(&tab[TAB_LGF][16 + 4 * q]);
+        const float ctf = tb_[TAB_CF][t];
+        const float4 l0 = *reinterpret_cast<const float4 *>(&tb_[TAB_LGF][4 * q]);
+        const float4 l1 = *reinterpret_cast<const float4 *>(&tb_[TAB_LGF][16 + 4 * q]);
         const float lg[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
         const bool hi_ok = 1 <= tb;
         bf16x8 af;
@@ -277,9 +304,9 @@ __global__ __launch_bounds__(64) void k_block_lat(BlockArgs a)
     }
     // eq. (12), reverse inside the block (s >= t)
     {
-        const float ctr = tab[TAB_CR][t];
-        const float4 l0 = *reinterpret_cast<const float4 *>(&tab[TAB_LGR][4 * q]);
-        const float4 l1 = *reinterpret_cast<const float4 *>(&tab[TAB_LGR][16 + 4 * q]);
+        const float ctr = tb_[TAB_CR][t];
+        const float4 l0 = *reinterpret_cast<const float4 *>(&tb_[TAB_LGR][4 * q]);
+        const float4 l1 = *reinterpret_cast<const float4 *>(&tb_[TAB_LGR][16 + 4 * q]);
         const float lg[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
         const bool lo_ok = 0 >= tb;
         bf16x8 af;
@@ -316,8 +343,8 @@ __global__ __launch_bounds__(64) void k_block_lat(BlockArgs a)
 template <typename Ty>
 hipError_t launch_ty(const BlockArgs &a, hipStream_t st)
 {
-    const int64_t nwg = static_cast<int64_t>(a.s.b) * a.s.H * (kP / 16) * 2;
-    k_block_lat<Ty><<<dim3(static_cast<unsigned>(nwg)), dim3(64), 0, st>>>(a);
+    // one workgroup per (head, row block), grid.y = stream
+    k_block_lat<Ty><<<dim3(static_cast<unsigned>(a.s.H * 2), static_cast<unsigned>(a.s.b)), dim3(256), 0, st>>>(a);
     return hipGetLastError();
 }
 
