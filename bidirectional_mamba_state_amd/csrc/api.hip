@@ -189,8 +189,9 @@ bdssm_status prepare_block_step(const bdssm_dims *dims, int32_t block_len, const
 }
 
 // Small batches (fewer (stream, head) pairs than fill the GPU with one workgroup per CU)
-// take the latency-ordered kernel, one wavefront per (row block, column block, head);
-// BDSSM_BLOCK_LAT=0 or 1 forces the choice where both kernels apply.
+// take the latency-ordered kernel, one workgroup per (head, row block, column part);
+// BDSSM_BLOCK_LAT=0 or 1 forces the choice where both kernels apply, and
+// BDSSM_BLOCK_LAT_WPG=2 or 4 its wavefronts per workgroup.
 bool use_block_lat(const Shape &s, int T)
 {
     if (!block_lat_supported(s, T))
@@ -202,8 +203,10 @@ bool use_block_lat(const Shape &s, int T)
 
 bdssm_status launch_block_step(const BlockArgs &a, hipStream_t st)
 {
-    if (use_block_lat(a.s, a.T))
-        return launched(launch_block_step_lat(a, st));
+    if (use_block_lat(a.s, a.T)) {
+        const char *e = getenv("BDSSM_BLOCK_LAT_WPG");
+        return launched(launch_block_step_lat(a, e ? atoi(e) : 0, st));
+    }
     if (block_mfma_supported(a.s, a.T)) {
         int hpw, ps;
         block_mfma_plan(a.s, &hpw, &ps);

@@ -83,7 +83,9 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *dst, int o
 // of a row permuted (an XOR of the piece index) so that the operand reads below fall in
 // distinct banks:
 //   row block: 16 rows of N = 128 bf16 (B or C), piece c of row r at slot c ^ r;
-//   state:     N x P fp32, piece c (4 columns) of row n at slot c ^ 4 ((n / 8) % 4);
+//   state:     N x (the workgroup's 32 or 64 columns) fp32; with 32, row n at LDS row
+//              n ^ ((n / 16) % 2) and piece c (4 columns) at slot c ^ 4 ((n / 8) % 2); with
+//              64, row n in place and piece c at slot c ^ 4 ((n / 8) % 4);
 //   x:         T x P bf16 per direction, piece c (8 columns) of row t at slot c ^ 2 (t % 4).
 constexpr int kRowBlk = 16 * 128;
 
@@ -104,29 +106,33 @@ __device__ __forceinline__ void store_y_bf16(__amdgpu_buffer_rsrc_t r, int off, 
 
 enum { TAB_CF, TAB_CR, TAB_LGF, TAB_LGR, TAB_COLF, TAB_COLR, TAB_EF, NTAB };
 
-template <typename Ty>
-__global__ __launch_bounds__(256) void k_block_lat(BlockArgs a)
+// WPG wavefronts per workgroup (2 or 4), each owning one 16-column block of the outputs
+template <typename Ty, int WPG>
+__global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
 {
     constexpr int NB = 2, TP = 32;  // one 32-token pair: two 16-token row blocks
+    constexpr int CW = 16 * WPG;    // the workgroup's columns
+    constexpr int NPH = kP / CW;    // column parts of a head
     // C rows of the row block (forward, reverse), then B rows of its three score tiles
     __shared__ __attribute__((aligned(16))) __bf16 rows[NB + 3][kRowBlk];
-    __shared__ __attribute__((aligned(16))) float hst[kN * kP];        // the cached state
+    __shared__ __attribute__((aligned(16))) float hst[kN * CW];        // the state, CW columns
     __shared__ __attribute__((aligned(16))) __bf16 xs[2][TP * kP];      // x, both directions
-    __shared__ __attribute__((aligned(16))) float tab[4][NTAB][TP];     // per wavefront
+    __shared__ __attribute__((aligned(16))) float tab[WPG][NTAB][TP];   // per wavefront
 
     const int T = a.T, H = a.s.H, G = a.s.G;
-    // workgroup = (head, row block), grid.y = stream. The hardware deals workgroup ids
-    // round-robin over the 8 XCDs; the two row blocks of a head read the same state and x,
-    // so they get consecutive logical ids within one XCD's range and share its L2.
+    // workgroup = (head, row block, column part), grid.y = stream. The hardware deals
+    // workgroup ids round-robin over the 8 XCDs; the workgroups of a head read the same B, C
+    // and x, so they get consecutive logical ids within one XCD's range and share its L2.
     const int nx = gridDim.x;
     int wid = blockIdx.x;
     if ((nx & 7) == 0)
         wid = (wid & 7) * (nx >> 3) + (wid >> 3);
-    const int tb = wid & 1, h = wid >> 1, b = blockIdx.y;
+    const int ph = wid % NPH, tb = (wid / NPH) & 1, h = wid / (2 * NPH), b = blockIdx.y;
     const int g = G == 1 ? 0 : h / (H / G);
-    // wavefront = 16-column block of the outputs (uniform, so that LDS copy addresses are
-    // scalar)
-    const int pblk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // wavefront w = 16-column block WPG ph + w of the outputs (uniform, so that LDS copy
+    // addresses are scalar)
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int pblk = WPG * ph + w;
     const int lane = threadIdx.x & 63, q = lane >> 4, r16 = lane & 15;
     const int t = tb * 16 + r16;  // this lane's row as an A operand
     const int p = pblk * 16 + r16;
@@ -150,26 +156,36 @@ __global__ __launch_bounds__(256) void k_block_lat(BlockArgs a)
     const auto rH = rsrc(a.h_prefix + (static_cast<int64_t>(b) * H + h) * (kN * kP), kN * kP * 4);
 
     // ---- the workgroup's inputs, each byte copied once, in whole lines, straight into
-    // LDS: this wavefront copies a quarter of each tile (19 loads in all)
+    // LDS: each wavefront copies 1/WPG of each tile (40/WPG + 8 loads, 4 more for dt)
+    constexpr int JPW = 4 / WPG;  // 1 KB pieces per wavefront of a row block or an x tile
     auto row0_of = [&](int i) {  // first row of row block i
         return i < 2 ? tb * 16 : (i - 2 <= tb ? i - 2 : i - 3) * 16;
     };
 #pragma unroll
-    for (int i = 0; i < NB + 3; ++i) {  // quarter pblk: rows 4 pblk .. 4 pblk + 3
-        const auto r = i == 0 ? rCf : i == 1 ? rCr : (i - 2 <= tb ? rBf : rBr);
-        const int rl = 4 * pblk + (lane >> 4), piece = (lane & 15) ^ rl;
-        dma16(r, &rows[i][4 * pblk * 128], ((row0_of(i) + rl) * rowBC + 8 * piece) * 2);
+    for (int i = 0; i < NB + 3; ++i)  // rows 4 j .. 4 j + 3 of each row block
+#pragma unroll
+        for (int j = JPW * w; j < JPW * w + JPW; ++j) {
+            const auto r = i == 0 ? rCf : i == 1 ? rCr : (i - 2 <= tb ? rBf : rBr);
+            const int rl = 4 * j + (lane >> 4), piece = (lane & 15) ^ rl;
+            dma16(r, &rows[i][4 * j * 128], ((row0_of(i) + rl) * rowBC + 8 * piece) * 2);
+        }
+#pragma unroll
+    for (int m = 8 * w; m < 8 * w + 8; ++m) {  // LDS state rows 8 m .. 8 m + 7 (32 columns)
+        if constexpr (WPG == 2) {              // or 4 m .. 4 m + 3 (64 columns)
+            const int lr = 8 * m + (lane >> 3), n = lr ^ ((lr >> 4) & 1), c = (lane & 7) ^ (4 * ((n >> 3) & 1));
+            dma16(rH, &hst[8 * m * CW], (n * kP + CW * ph + 4 * c) * 4);
+        } else {
+            const int n = 4 * m + (lane >> 4), c = (lane & 15) ^ (4 * ((n >> 3) & 3));
+            dma16(rH, &hst[4 * m * CW], (n * kP + 4 * c) * 4);
+        }
     }
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {  // state rows 32 pblk + 4 m .. +3
-        const int n = 32 * pblk + 4 * m + (lane >> 4), c = (lane & 15) ^ (4 * ((n >> 3) & 3));
-        dma16(rH, &hst[(32 * pblk + 4 * m) * kP], (n * kP + 4 * c) * 4);
-    }
+    for (int d = 0; d < 2; ++d)  // x rows 8 j .. 8 j + 7 of each direction
 #pragma unroll
-    for (int d = 0; d < 2; ++d) {  // x rows 8 pblk .. 8 pblk + 7 of each direction
-        const int tr = 8 * pblk + (lane >> 3), c = (lane & 7) ^ (2 * (tr & 3));
-        dma16(d ? rXr : rXf, &xs[d][8 * pblk * kP], (tr * rowX + 8 * c) * 2);
-    }
+        for (int j = JPW * w; j < JPW * w + JPW; ++j) {
+            const int tr = 8 * j + (lane >> 3), c = (lane & 7) ^ (2 * (tr & 3));
+            dma16(d ? rXr : rXf, &xs[d][8 * j * kP], (tr * rowX + 8 * c) * 2);
+        }
     const int t0 = 2 * lane, t1 = t0 + 1;
     const unsigned short df0 = __builtin_amdgcn_raw_buffer_load_b16(rDf, t0 * H * 2, 0, 0);
     const unsigned short df1 = __builtin_amdgcn_raw_buffer_load_b16(rDf, t1 * H * 2, 0, 0);
@@ -180,7 +196,7 @@ __global__ __launch_bounds__(256) void k_block_lat(BlockArgs a)
 
     // ---- decay tables of both directions (lane l holds tokens 2l and 2l+1; dt past T is 0),
     // computed by every wavefront into its own table
-    float(*tb_)[TP] = tab[pblk];
+    float(*tb_)[TP] = tab[w];
     {
         const float f0 = __uint_as_float(static_cast<uint32_t>(df0) << 16);
         const float f1 = __uint_as_float(static_cast<uint32_t>(df1) << 16);
@@ -219,12 +235,16 @@ __global__ __launch_bounds__(256) void k_block_lat(BlockArgs a)
         const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < NB + 3; ++i)
-            if (row0_of(i) + 4 * pblk + (lane >> 4) >= T)
-                *reinterpret_cast<uint4 *>(&rows[i][4 * pblk * 128 + 8 * lane]) = z;
+#pragma unroll
+            for (int j = JPW * w; j < JPW * w + JPW; ++j)
+                if (row0_of(i) + 4 * j + (lane >> 4) >= T)
+                    *reinterpret_cast<uint4 *>(&rows[i][4 * j * 128 + 8 * lane]) = z;
 #pragma unroll
         for (int d = 0; d < 2; ++d)
-            if (8 * pblk + (lane >> 3) >= T)
-                *reinterpret_cast<uint4 *>(&xs[d][8 * pblk * kP + 8 * lane]) = z;
+#pragma unroll
+            for (int j = JPW * w; j < JPW * w + JPW; ++j)
+                if (8 * j + (lane >> 3) >= T)
+                    *reinterpret_cast<uint4 *>(&xs[d][8 * j * kP + 8 * lane]) = z;
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's copies have landed
     __syncthreads();                      // and so have everyone's
@@ -250,14 +270,20 @@ __global__ __launch_bounds__(256) void k_block_lat(BlockArgs a)
     // ---- eq. (11), cached-state term: C_t . (h_hi + h_lo), the B operand of column p being
     // h[32kk + 8q + e][p], e = 0..7, split into bf16 halves in registers; two independent chains
     f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc_lo = {0.f, 0.f, 0.f, 0.f};
+    // 32 columns: row n = 32kk + 8q + e sits at LDS row 32kk + 8q + (e ^ (q / 2)), and local
+    // column 16 w + r16 (piece 4 w + r16 / 4) at slot (4 w + r16 / 4) ^ 4 (q % 2), i.e. at
+    // 16 (w ^ (q % 2)) + r16. 64 columns: row n in place, column 16 w + r16 at 16 (w ^ q) + r16.
+    const float *hq = WPG == 2 ? &hst[8 * q * CW + 16 * (w ^ (q & 1)) + r16] : &hst[8 * q * CW + 16 * (w ^ q) + r16];
+    const int sw = WPG == 2 ? (q >> 1) * CW : 0;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-        // row n = 32kk + 8q + e, piece p/4 at slot (p/4) ^ 4q: column p sits at 16 (pblk ^ q) + r16
-        const float *hp = &hst[(32 * kk + 8 * q) * kP + 16 * (pblk ^ q) + r16];
+        const float *hp = hq + 32 * kk * CW;
         float hv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            hv[e] = hp[e * kP];
+        for (int e = 0; e < 8; e += 2) {
+            hv[e] = hp[e * CW + sw];
+            hv[e + 1] = hp[(e + 1) * CW - sw];
+        }
         bf16x8 hi, lo;
         split8(hv, hi, lo);
         acc = mfma(cfw[kk], hi, acc);
@@ -341,10 +367,18 @@ __global__ __launch_bounds__(256) void k_block_lat(BlockArgs a)
 }
 
 template <typename Ty>
-hipError_t launch_ty(const BlockArgs &a, hipStream_t st)
+hipError_t launch_ty(const BlockArgs &a, int wpg, hipStream_t st)
 {
-    // one workgroup per (head, row block), grid.y = stream
-    k_block_lat<Ty><<<dim3(static_cast<unsigned>(a.s.H * 2), static_cast<unsigned>(a.s.b)), dim3(256), 0, st>>>(a);
+    // one workgroup per (head, row block, column part), grid.y = stream: two wavefronts (32
+    // columns) when that many workgroups still get a compute unit each, else four
+    const int64_t pairs = static_cast<int64_t>(a.s.b) * a.s.H;
+    if (wpg != 2 && wpg != 4)
+        wpg = pairs * 4 <= device_cus() ? 2 : 4;
+    if (wpg == 2) {
+        k_block_lat<Ty, 2><<<dim3(static_cast<unsigned>(a.s.H * 4), static_cast<unsigned>(a.s.b)), dim3(128), 0, st>>>(a);
+    } else {
+        k_block_lat<Ty, 4><<<dim3(static_cast<unsigned>(a.s.H * 2), static_cast<unsigned>(a.s.b)), dim3(256), 0, st>>>(a);
+    }
     return hipGetLastError();
 }
 
@@ -357,9 +391,9 @@ bool block_lat_supported(const Shape &s, int T)
     return s.in_dt == 1 && s.N == kN && s.P == kP && T >= 1 && T <= 32;
 }
 
-hipError_t launch_block_step_lat(const BlockArgs &a, hipStream_t st)
+hipError_t launch_block_step_lat(const BlockArgs &a, int wpg, hipStream_t st)
 {
-    return a.s.y_dt ? launch_ty<__bf16>(a, st) : launch_ty<float>(a, st);
+    return a.s.y_dt ? launch_ty<__bf16>(a, wpg, st) : launch_ty<float>(a, wpg, st);
 }
 
 }  // namespace bdssm

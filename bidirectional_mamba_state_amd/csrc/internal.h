@@ -92,7 +92,7 @@ bool block_mfma_supported(const Shape &s, int T);
 void block_mfma_plan(const Shape &s, int *hpw, int *ps);
 hipError_t launch_block_step_mfma(const BlockArgs &a, int hpw, int ps, hipStream_t st);
 bool block_lat_supported(const Shape &s, int T);
-hipError_t launch_block_step_lat(const BlockArgs &a, hipStream_t st);
+hipError_t launch_block_step_lat(const BlockArgs &a, int wpg, hipStream_t st);  // wpg 2, 4 or 0 (chosen)
 hipError_t launch_forward_valu(const ForwardArgs &a, hipStream_t st);
 hipError_t launch_block_step_valu(const BlockArgs &a, hipStream_t st);
 hipError_t launch_state_pass(const PassArgs &a, hipStream_t st);

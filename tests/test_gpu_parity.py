@@ -263,8 +263,9 @@ def test_commit_chain_equals_prefix_scan():
 @pytest.mark.parametrize("T", [17, 32, 64, 128])
 def test_block_step_launch_shapes(monkeypatch, T):
     """Both block-step kernels give the oracle's result: the bandwidth kernel at every
-    (heads per workgroup, column split) launch shape, and the latency kernel (one wavefront
-    per row block, column block and head; T <= 32) with float32 and bfloat16 y."""
+    (heads per workgroup, column split) launch shape, and the latency kernel (one workgroup
+    per head, row block and column part, of 2 or 4 wavefronts; T <= 32) with float32 and
+    bfloat16 y."""
     rng = np.random.default_rng(100 + T)
     from test_oracle_pins import rand_seq
     b, H, G = 3, 12, 2        # 6 heads per group
@@ -288,8 +289,9 @@ def test_block_step_launch_shapes(monkeypatch, T):
         assert within(rel(yz, yzo), TOL_BF16, f"y - D x hpw={hpw} ps={ps}")
     if T <= 32:
         monkeypatch.setenv("BDSSM_BLOCK_LAT", "1")
-        for y_dtype in (bdssm.F32, bdssm.BF16):
-            _case(f"latency kernel T={T} y_dtype={y_dtype}")
+        for wpg, y_dtype in ((2, bdssm.F32), (2, bdssm.BF16), (4, bdssm.F32), (4, bdssm.BF16)):
+            monkeypatch.setenv("BDSSM_BLOCK_LAT_WPG", str(wpg))
+            _case(f"latency kernel T={T} wavefronts per workgroup {wpg} y_dtype={y_dtype}")
             y = gpu_block_step(h, fwd, rev, A, D, y_dtype)
             yz = gpu_block_step(h, fwd, rev, A, Dz, y_dtype)
             assert within(rel(y, yo), TOL_BF16, "y, latency kernel")
