@@ -21,8 +21,10 @@
 //     each lane the tokens of its slots (4q + e, 16 + 4q + e) in its column; the same
 //     registers give D x.
 // The cumulative log-decays of both directions are a 64-lane DPP scan that every wavefront
-// computes for itself into its own small table. One workgroup barrier (after the copies);
-// y leaves straight from the accumulators. Loads and stores go through range-checked
+// computes for itself into its own small table. The copies are issued in the order of use,
+// the state last: after a barrier for B, C and x the score tiles and M X run while the
+// state still arrives, and a second barrier precedes C . h; y leaves straight from the
+// accumulators. Loads and stores go through range-checked
 // buffer resources over the stream's T tokens, so rows past T read as zero and their
 // stores are dropped (LDS rows past T are cleared in a branch taken only for short blocks).
 #include "internal.h"
@@ -88,6 +90,20 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *dst, int o
 //              64, row n in place and piece c at slot c ^ 4 ((n / 8) % 4);
 //   x:         T x P bf16 per direction, piece c (8 columns) of row t at slot c ^ 2 (t % 4).
 constexpr int kRowBlk = 16 * 128;
+
+// Workgroup barrier over LDS filled by this workgroup's copies and writes: waits until at
+// most INFLIGHT of this wavefront's loads are outstanding and its LDS writes are done, then
+// synchronizes. (A memory fence here would wait for every load, copies to LDS included.)
+template <int INFLIGHT>
+__device__ __forceinline__ void lds_barrier()
+{
+    static_assert(INFLIGHT >= 0 && INFLIGHT < 64, "vmcnt range");
+    __builtin_amdgcn_sched_barrier(0);
+    // vmcnt(INFLIGHT) (bits 3:0 and 15:14), expcnt unchanged (7), lgkmcnt(0)
+    __builtin_amdgcn_s_waitcnt((INFLIGHT & 15) | ((INFLIGHT >> 4) << 14) | 0x0070);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+}
 
 // Operand fragment of row r16 of a row block: n = 32 kk + 8 q .. +7
 __device__ __forceinline__ bf16x8 rows_frag(const __bf16 *blk, int kk, int q, int r16)
@@ -156,8 +172,17 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
     const auto rH = rsrc(a.h_prefix + (static_cast<int64_t>(b) * H + h) * (kN * kP), kN * kP * 4);
 
     // ---- the workgroup's inputs, each byte copied once, in whole lines, straight into
-    // LDS: each wavefront copies 1/WPG of each tile (40/WPG + 8 loads, 4 more for dt)
+    // LDS: each wavefront copies 1/WPG of each tile (40/WPG + 8 loads after 4 for dt), in the
+    // order they are used -- dt (decay tables), B and C (score tiles), x (M X), and the state
+    // (C . h) last, so that the first products overlap the state's arrival
     constexpr int JPW = 4 / WPG;  // 1 KB pieces per wavefront of a row block or an x tile
+    const int t0 = 2 * lane, t1 = t0 + 1;
+    const unsigned short df0 = __builtin_amdgcn_raw_buffer_load_b16(rDf, t0 * H * 2, 0, 0);
+    const unsigned short df1 = __builtin_amdgcn_raw_buffer_load_b16(rDf, t1 * H * 2, 0, 0);
+    const unsigned short dr0 = __builtin_amdgcn_raw_buffer_load_b16(rDr, t0 * H * 2, 0, 0);
+    const unsigned short dr1 = __builtin_amdgcn_raw_buffer_load_b16(rDr, t1 * H * 2, 0, 0);
+    const float Ah = a.A[h], Dh = a.D[h], Ar = a.A_rev[h];
+    const float Dr = a.D_rev ? a.D_rev[h] : 0.f;
     auto row0_of = [&](int i) {  // first row of row block i
         return i < 2 ? tb * 16 : (i - 2 <= tb ? i - 2 : i - 3) * 16;
     };
@@ -170,8 +195,16 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
             dma16(r, &rows[i][4 * j * 128], ((row0_of(i) + rl) * rowBC + 8 * piece) * 2);
         }
 #pragma unroll
-    for (int m = 8 * w; m < 8 * w + 8; ++m) {  // LDS state rows 8 m .. 8 m + 7 (32 columns)
-        if constexpr (WPG == 2) {              // or 4 m .. 4 m + 3 (64 columns)
+    for (int d = 0; d < 2; ++d)  // x rows 8 j .. 8 j + 7 of each direction
+#pragma unroll
+        for (int j = JPW * w; j < JPW * w + JPW; ++j) {
+            const int tr = 8 * j + (lane >> 3), c = (lane & 7) ^ (2 * (tr & 3));
+            dma16(d ? rXr : rXf, &xs[d][8 * j * kP], (tr * rowX + 8 * c) * 2);
+        }
+    constexpr int NSTATE = 8;  // state copies per wavefront, the last loads issued
+#pragma unroll
+    for (int m = NSTATE * w; m < NSTATE * w + NSTATE; ++m) {  // LDS state rows 8 m .. 8 m + 7
+        if constexpr (WPG == 2) {                              // (32 columns) or 4 m .. 4 m + 3
             const int lr = 8 * m + (lane >> 3), n = lr ^ ((lr >> 4) & 1), c = (lane & 7) ^ (4 * ((n >> 3) & 1));
             dma16(rH, &hst[8 * m * CW], (n * kP + CW * ph + 4 * c) * 4);
         } else {
@@ -179,20 +212,6 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
             dma16(rH, &hst[4 * m * CW], (n * kP + 4 * c) * 4);
         }
     }
-#pragma unroll
-    for (int d = 0; d < 2; ++d)  // x rows 8 j .. 8 j + 7 of each direction
-#pragma unroll
-        for (int j = JPW * w; j < JPW * w + JPW; ++j) {
-            const int tr = 8 * j + (lane >> 3), c = (lane & 7) ^ (2 * (tr & 3));
-            dma16(d ? rXr : rXf, &xs[d][8 * j * kP], (tr * rowX + 8 * c) * 2);
-        }
-    const int t0 = 2 * lane, t1 = t0 + 1;
-    const unsigned short df0 = __builtin_amdgcn_raw_buffer_load_b16(rDf, t0 * H * 2, 0, 0);
-    const unsigned short df1 = __builtin_amdgcn_raw_buffer_load_b16(rDf, t1 * H * 2, 0, 0);
-    const unsigned short dr0 = __builtin_amdgcn_raw_buffer_load_b16(rDr, t0 * H * 2, 0, 0);
-    const unsigned short dr1 = __builtin_amdgcn_raw_buffer_load_b16(rDr, t1 * H * 2, 0, 0);
-    const float Ah = a.A[h], Dh = a.D[h], Ar = a.A_rev[h];
-    const float Dr = a.D_rev ? a.D_rev[h] : 0.f;
 
     // ---- decay tables of both directions (lane l holds tokens 2l and 2l+1; dt past T is 0),
     // computed by every wavefront into its own table
@@ -228,10 +247,11 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
             tb_[TAB_EF][t1] = __builtin_amdgcn_exp2f(c1);
         }
     }
+    // B, C and x of this wavefront have landed once at most its state copies are in flight
+    __builtin_amdgcn_s_waitcnt(0x0F70 | NSTATE);  // vmcnt(NSTATE)
     if (T < TP) {
         // rows past T: whatever the copies left in LDS there is replaced by zeros, each
-        // wavefront in the pieces it copied (the wait orders these writes after its copies)
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        // wavefront in the pieces it copied (after the wait above)
         const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < NB + 3; ++i)
@@ -246,8 +266,7 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
                 if (8 * j + (lane >> 3) >= T)
                     *reinterpret_cast<uint4 *>(&xs[d][8 * j * kP + 8 * lane]) = z;
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's copies have landed
-    __syncthreads();                      // and so have everyone's
+    lds_barrier<NSTATE>();  // (1) everyone's B, C and x
 
     // ---- score tiles of the row block: S[t = tb*16 + r16][s = sb*16 + 4q + j]
     bf16x8 cfw[4], crv[4];
@@ -267,6 +286,56 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
         S[ut] = acc;
     }
 
+    // x operands: slots 0..3 tokens 4q + j, slots 4..7 tokens 16 + 4q + j, column p, by
+    // transposing reads (lane r16 addresses row 4q + r16/4, columns 16 pblk + 4 (r16 % 4) ..)
+    bf16x8 xv[2];
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+        bf16x4 half[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int tr = 16 * u + 4 * q + (r16 >> 2), col = 16 * pblk + 4 * (r16 & 3);
+            half[u] = tr_read(&xs[d][tr * kP + 8 * ((col >> 3) ^ (2 * (tr & 3))) + (col & 7)]);
+        }
+        xv[d] = cat(half[0], half[1]);
+    }
+    const bf16x8 xvf = xv[0], xvr = xv[1];
+    f32x4 acc_x = {0.f, 0.f, 0.f, 0.f};
+    // eq. (11), inside the block (s <= t), exp2 per element on the diagonal pair
+    {
+        const float ctf = tb_[TAB_CF][t];
+        const float4 l0 = *reinterpret_cast<const float4 *>(&tb_[TAB_LGF][4 * q]);
+        const float4 l1 = *reinterpret_cast<const float4 *>(&tb_[TAB_LGF][16 + 4 * q]);
+        const float lg[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+        const bool hi_ok = 1 <= tb;
+        bf16x8 af;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int s = (j < 4 ? 0 : 16) + 4 * q + (j & 3);
+            const float sv = j < 4 ? S[0][j] : (hi_ok ? S[1][j & 3] : 0.f);
+            const float w = __builtin_amdgcn_exp2f(ctf + lg[j]);
+            af[j] = static_cast<__bf16>(s <= t ? sv * w : 0.f);
+        }
+        acc_x = mfma(af, xvf, acc_x);
+    }
+    // eq. (12), reverse inside the block (s >= t)
+    {
+        const float ctr = tb_[TAB_CR][t];
+        const float4 l0 = *reinterpret_cast<const float4 *>(&tb_[TAB_LGR][4 * q]);
+        const float4 l1 = *reinterpret_cast<const float4 *>(&tb_[TAB_LGR][16 + 4 * q]);
+        const float lg[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+        const bool lo_ok = 0 >= tb;
+        bf16x8 af;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int s = (j < 4 ? 0 : 16) + 4 * q + (j & 3);
+            const float sv = j < 4 ? (lo_ok ? S[1][j] : 0.f) : S[2][j & 3];
+            const float w = __builtin_amdgcn_exp2f(ctr + lg[j]);
+            af[j] = static_cast<__bf16>(s >= t ? sv * w : 0.f);
+        }
+        acc_x = mfma(af, xvr, acc_x);
+    }
+    lds_barrier<0>();  // (2) everyone's state
     // ---- eq. (11), cached-state term: C_t . (h_hi + h_lo), the B operand of column p being
     // h[32kk + 8q + e][p], e = 0..7, split into bf16 halves in registers; two independent chains
     f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc_lo = {0.f, 0.f, 0.f, 0.f};
@@ -289,61 +358,12 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
         acc = mfma(cfw[kk], hi, acc);
         acc_lo = mfma(cfw[kk], lo, acc_lo);
     }
-    acc += acc_lo;
     {
         const float4 e4 = *reinterpret_cast<const float4 *>(&tb_[TAB_EF][tb * 16 + 4 * q]);
-        acc[0] *= e4.x;
-        acc[1] *= e4.y;
-        acc[2] *= e4.z;
-        acc[3] *= e4.w;
-    }
-    // x operands: slots 0..3 tokens 4q + j, slots 4..7 tokens 16 + 4q + j, column p, by
-    // transposing reads (lane r16 addresses row 4q + r16/4, columns 16 pblk + 4 (r16 % 4) ..)
-    bf16x8 xv[2];
-#pragma unroll
-    for (int d = 0; d < 2; ++d) {
-        bf16x4 half[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int tr = 16 * u + 4 * q + (r16 >> 2), col = 16 * pblk + 4 * (r16 & 3);
-            half[u] = tr_read(&xs[d][tr * kP + 8 * ((col >> 3) ^ (2 * (tr & 3))) + (col & 7)]);
-        }
-        xv[d] = cat(half[0], half[1]);
-    }
-    const bf16x8 xvf = xv[0], xvr = xv[1];
-    // eq. (11), inside the block (s <= t), exp2 per element on the diagonal pair
-    {
-        const float ctf = tb_[TAB_CF][t];
-        const float4 l0 = *reinterpret_cast<const float4 *>(&tb_[TAB_LGF][4 * q]);
-        const float4 l1 = *reinterpret_cast<const float4 *>(&tb_[TAB_LGF][16 + 4 * q]);
-        const float lg[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-        const bool hi_ok = 1 <= tb;
-        bf16x8 af;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int s = (j < 4 ? 0 : 16) + 4 * q + (j & 3);
-            const float sv = j < 4 ? S[0][j] : (hi_ok ? S[1][j & 3] : 0.f);
-            const float w = __builtin_amdgcn_exp2f(ctf + lg[j]);
-            af[j] = static_cast<__bf16>(s <= t ? sv * w : 0.f);
-        }
-        acc = mfma(af, xvf, acc);
-    }
-    // eq. (12), reverse inside the block (s >= t)
-    {
-        const float ctr = tb_[TAB_CR][t];
-        const float4 l0 = *reinterpret_cast<const float4 *>(&tb_[TAB_LGR][4 * q]);
-        const float4 l1 = *reinterpret_cast<const float4 *>(&tb_[TAB_LGR][16 + 4 * q]);
-        const float lg[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-        const bool lo_ok = 0 >= tb;
-        bf16x8 af;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int s = (j < 4 ? 0 : 16) + 4 * q + (j & 3);
-            const float sv = j < 4 ? (lo_ok ? S[1][j] : 0.f) : S[2][j & 3];
-            const float w = __builtin_amdgcn_exp2f(ctr + lg[j]);
-            af[j] = static_cast<__bf16>(s >= t ? sv * w : 0.f);
-        }
-        acc = mfma(af, xvr, acc);
+        acc[0] = fmaf(acc[0] + acc_lo[0], e4.x, acc_x[0]);
+        acc[1] = fmaf(acc[1] + acc_lo[1], e4.y, acc_x[1]);
+        acc[2] = fmaf(acc[2] + acc_lo[2], e4.z, acc_x[2]);
+        acc[3] = fmaf(acc[3] + acc_lo[3], e4.w, acc_x[3]);
     }
     // ---- eq. (13) + D x (+ D_rev x_rev), written once: rows tb*16 + 4q + j, column p. The
     // x of those rows are slots (tb & 1) * 4 + j of the operands. Rows past T fall outside
