@@ -3,9 +3,10 @@
 One step = one pass of the whole hot path over one decoding block of the 700M-shape
 layer (48 heads x 64, d_state 128, ngroups 1, batch 1, bf16 inputs, fp32 state):
   1. bdssm_prefix_scan over the 8192-token prefix (y in bf16, final state),
-  2. 64 denoising steps of bdssm_block_step (T = 32, distinct fwd/rev inputs per step)
-     against that cached state,
-  3. bdssm_commit of the block's clean inputs.
+  2. bdssm_state_ops: that cached state in the block step's operand form,
+  3. 64 denoising steps of bdssm_block_step_ops (T = 32, distinct fwd/rev inputs per step)
+     against it,
+  4. bdssm_commit of the block's clean inputs.
 value = active (denoised) tokens per second = steps * 64 * 32 / wall time.
 
 Per-kernel times come from HIP events recorded on the launch stream around every call in
@@ -16,6 +17,7 @@ with per-chunk states (matrix-core-bound). The CPU baseline times the float64 or
 the host on one whole step of the same workload.
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -186,6 +188,7 @@ def main():
     clean_np = inputs.block(cfg, 0, 0, inputs.CLEAN)
     clean = bdssm.seq_to_device(clean_np)
     h = torch.empty((b, H, N, P), device="cuda")
+    h_ops = torch.empty(bdssm.state_ops_bytes(d), dtype=torch.uint8, device="cuda")
     y_pre = torch.empty((b, L, H, P), dtype=torch.bfloat16, device="cuda")
     y_blk = [torch.empty((b, T, H, P), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
     wsb = bdssm.prefix_scan_workspace(d, L, Q, True, False)
@@ -194,7 +197,15 @@ def main():
     def run_prefix():
         bdssm.prefix_scan(d, L, Q, pre, Ad, Dd, None, y_pre, None, h, ws, wsb)
 
+    def run_state_ops():
+        bdssm.state_ops(d, h, h_ops)
+
     def run_blocks():
+        for s in range(S):
+            f, r = steps[s]
+            bdssm.block_step_ops(d, T, h_ops, f, r, Ad, Dd, y_blk[s])
+
+    def run_blocks_fp32_state():
         for s in range(S):
             f, r = steps[s]
             bdssm.block_step(d, T, h, f, r, Ad, Dd, y_blk[s])
@@ -202,22 +213,22 @@ def main():
     def run_commit():
         bdssm.commit(d, T, clean, Ad, Dd, h)
 
+    parts = (("prefix_scan", run_prefix), ("state_ops", run_state_ops), ("block_step", run_blocks),
+             ("commit", run_commit))
     for _ in range(args.warmup):
-        run_prefix()
-        run_blocks()
-        run_commit()
+        for _, fn in parts:
+            fn()
     torch.cuda.synchronize()
 
-    # A step is one HIP graph replay of the whole path (prefix scan, the 64 block steps, the
-    # commit), so launch overhead is off the clock, as in the pages' own graph-captured
-    # decoding measurements; `value` and `ms_per_step` time exactly K replays. The parts are
-    # then timed on their own: the same work as three graphs (prefix scan; the 64 block steps;
-    # the commit), with HIP events between the replays on the launch stream; the block-step
-    # average includes the gaps between the 64 back-to-back launches of its graph.
+    # A step is one HIP graph replay of the whole path (prefix scan, operand form of the
+    # state, the 64 block steps, the commit), so launch overhead is off the clock, as in the
+    # pages' own graph-captured decoding measurements; `value` and `ms_per_step` time exactly
+    # K replays. The parts are then timed on their own: the same work as one graph per part,
+    # with HIP events between the replays on the launch stream; the block-step average
+    # includes the gaps between the 64 back-to-back launches of its graph.
     def run_all():
-        run_prefix()
-        run_blocks()
-        run_commit()
+        for _, fn in parts:
+            fn()
 
     whole = capture(torch, run_all)
     for _ in range(2):
@@ -235,35 +246,39 @@ def main():
     gpu_ms_per_step = e_all[0].elapsed_time(e_all[1]) / args.steps
     del whole
 
-    graphs = [capture(torch, fn) for fn in (run_prefix, run_blocks, run_commit)]
+    graphs = [capture(torch, fn) for _, fn in parts]
+    names = [k for k, _ in parts]
     ev = []
     torch.cuda.synchronize()
     for i in range(args.steps):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)]
         e[0].record()
         for g, en in zip(graphs, e[1:]):
             g.replay()
             en.record()
         ev.append(e)
     torch.cuda.synchronize()
-    per_step = {"prefix_scan": 1, "block_step": S, "commit": 1}
-    part_ms = {k: sum(e[j].elapsed_time(e[j + 1]) for e in ev) / args.steps
-               for j, k in enumerate(("prefix_scan", "block_step", "commit"))}
-    parts_ms = sum(e[0].elapsed_time(e[3]) for e in ev) / args.steps
+    per_step = {"prefix_scan": 1, "state_ops": 1, "block_step": S, "commit": 1}
+    part_ms = {k: sum(e[j].elapsed_time(e[j + 1]) for e in ev) / args.steps for j, k in enumerate(names)}
+    parts_ms = sum(e[0].elapsed_time(e[len(parts)]) for e in ev) / args.steps
     avg_us = {k: 1e3 * part_ms[k] / per_step[k] for k in part_ms}
-    timing = ("one HIP graph replay per step (prefix scan, 64 block steps, commit); per-part times "
-              "from the same work as three graphs with HIP events between them on the launch stream")
+    del graphs
+    fp32_state_us = graph_us(torch, run_blocks_fp32_state) / S
+    timing = ("one HIP graph replay per step (prefix scan, state operand form, 64 block steps, commit); "
+              "per-part times from the same work as one graph per part with HIP events between them on "
+              "the launch stream")
     ms_per_step = 1e3 * wall / args.steps
     active = args.steps * S * b * T
     value = active / wall
 
     ib, yb = 2, 2
     k_bytes = {"block_step": block_step_bytes(b, H, P, N, G, T, ib, yb),
+               "state_ops": 2 * b * H * N * P * 4,
                "commit": commit_bytes(b, H, P, N, G, T, ib),
                "prefix_scan": prefix_bytes(b, H, P, N, G, L, Q, ib, yb, False)}
     pf = prefix_flops(b, H, P, N, G, L, Q)
     breakdown = {}
-    for k in ("prefix_scan", "block_step", "commit"):
+    for k in names:
         us = avg_us[k]
         breakdown[k] = {"launches_per_step": per_step[k], "avg_us": round(us, 3),
                         "share_of_step": round(part_ms[k] / parts_ms, 4),
@@ -272,6 +287,7 @@ def main():
     breakdown["prefix_scan"]["tokens_per_s"] = round(b * L / (avg_us["prefix_scan"] * 1e-6), 1)
     breakdown["prefix_scan"]["mfma_frac"] = round(pf / (avg_us["prefix_scan"] * 1e-6) / MFMA_BF16_PEAK, 5)
     breakdown["block_step"]["active_tokens_per_s"] = round(b * T / (avg_us["block_step"] * 1e-6), 1)
+    breakdown["block_step"]["from_fp32_state_us"] = round(fp32_state_us, 3)
     dom = max(part_ms, key=part_ms.get)
     if dom == "prefix_scan":
         roof = make_roofline("mfma", pf, avg_us[dom], traffic_for(dom))
@@ -288,14 +304,16 @@ def main():
            "data": "synthetic (seeded; random-init layer parameters)",
            "config": {"workload": "700M-shape Mamba-2 layer, 48 heads x 64, d_state 128, ngroups 1, "
                                   "batch 1, bf16 inputs, fp32 state: 8192-token prefix scan + "
-                                  "64 block steps (T=32) + commit per step",
+                                  "state operand form + 64 block steps (T=32) + commit per step",
                       "global_batch": b, "seq_len": L, "block_len": T, "steps_per_block": S,
                       "parallelism": "none (1 GPU)"},
            "roofline": roof, "breakdown": breakdown}
 
-    # the same 64 block steps + commit through the library's decode-loop graph (one HIP
-    # graph recorded by bdssm_decode_graph_create), timed per replay
-    dg = bdssm.DecodeGraph(d, T, h, [f for f, _ in steps], [r for _, r in steps], Ad, Dd, y_blk, clean)
+    # the same 64 block steps + commit (+ the operand form of the advanced state) through the
+    # library's decode-loop graph (one HIP graph recorded by bdssm_decode_graph_create),
+    # timed per replay
+    dg = bdssm.DecodeGraph(d, T, h, [f for f, _ in steps], [r for _, r in steps], Ad, Dd, y_blk, clean,
+                           h_ops=h_ops)
     for _ in range(2):
         dg.launch()
     torch.cuda.synchronize()
@@ -308,14 +326,15 @@ def main():
     torch.cuda.synchronize()
     blk_us = 1e3 * e0.elapsed_time(e1) / reps
     dg.close()
-    out["decode_graph"] = {"workload": "bdssm_decode_graph: 64 block steps (T=32) + commit of one block, "
-                                       "700M shape, replayed back to back",
-                           "us_per_block": round(blk_us, 2), "us_per_launch": round(blk_us / (S + 1), 3),
+    out["decode_graph"] = {"workload": "bdssm_decode_graph: 64 block steps (T=32) + commit of one block "
+                                       "+ operand form of the advanced state, 700M shape, replayed back "
+                                       "to back",
+                           "us_per_block": round(blk_us, 2), "us_per_launch": round(blk_us / (S + 2), 3),
                            "active_tokens_per_s": round(S * b * T / (blk_us * 1e-6), 1)}
 
     if not args.no_secondary:
         out["conv_state"] = conv_workloads(torch, bdssm, cfg, inputs, d, h, steps, Ad, Dd, y_blk, pre, L,
-                                           avg_us["block_step"])
+                                           fp32_state_us)
         out["secondary"] = secondary(torch, np, bdssm, configs, inputs)
         out["extra"] = extra(torch, np, bdssm, configs, inputs)
     if not args.no_cpu_baseline:
@@ -411,30 +430,36 @@ def extra(torch, np, bdssm, configs, inputs):
     d = bdssm.dims(b, H, P, N, G, c1.in_dtype, bdssm.BF16)
     f = bdssm.seq_to_device(inputs.block(c1, 0, 0, inputs.FWD))
     r = bdssm.seq_to_device(inputs.block(c1, 0, 0, inputs.REV))
-    h = torch.randn((b, H, N, P), device="cuda") * 0.05
+    def ops_of(dd, hh):
+        o = torch.empty(bdssm.state_ops_bytes(dd), dtype=torch.uint8, device="cuda")
+        bdssm.state_ops(dd, hh, o)
+        return o
+
+    h = ops_of(d, torch.randn((b, H, N, P), device="cuda") * 0.05)
     y = torch.empty((b, T, H, P), dtype=torch.bfloat16, device="cuda")
     ts = []
     for i in range(25):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        bdssm.block_step(d, T, h, f, r, Ad, Dd, y)
+        bdssm.block_step_ops(d, T, h, f, r, Ad, Dd, y)
         e1.record()
         torch.cuda.synchronize()
         if i >= 5:
             ts.append(1e3 * e0.elapsed_time(e1))
-    res["block_step_single_launch"] = {"workload": "700M shape, T=32, one launch between synchronizations",
+    res["block_step_single_launch"] = {"workload": "700M shape, T=32, state in operand form, one launch "
+                                                   "between synchronizations",
                                        "median_us": round(float(np.median(ts)), 3)}
     # cold: 256 sets of (state, inputs, y), about 540 MB, one launch each; warm: one set
     nset = 256
     sets = []
     for k in range(nset):
-        sets.append((torch.randn((b, H, N, P), device="cuda") * 0.05,
+        sets.append((ops_of(d, torch.randn((b, H, N, P), device="cuda") * 0.05),
                      tuple(t.clone() for t in f), tuple(t.clone() for t in r),
                      torch.empty_like(y)))
-    cold = graph_us(torch, lambda: [bdssm.block_step(d, T, hh, ff, rr, Ad, Dd, yy) for hh, ff, rr, yy in sets]) / nset
-    warm = graph_us(torch, lambda: [bdssm.block_step(d, T, h, f, r, Ad, Dd, y) for _ in range(nset)]) / nset
+    cold = graph_us(torch, lambda: [bdssm.block_step_ops(d, T, hh, ff, rr, Ad, Dd, yy) for hh, ff, rr, yy in sets]) / nset
+    warm = graph_us(torch, lambda: [bdssm.block_step_ops(d, T, h, f, r, Ad, Dd, y) for _ in range(nset)]) / nset
     nb = block_step_bytes(b, H, P, N, G, T, 2, 2)
-    res["block_step_cold_warm"] = {"workload": "700M shape, T=32, 256 launches in one graph",
+    res["block_step_cold_warm"] = {"workload": "700M shape, T=32, state in operand form, 256 launches in one graph",
                                    "cold_us": round(cold, 3), "warm_us": round(warm, 3),
                                    "rotation_bytes": nset * nb}
     del sets
@@ -452,7 +477,13 @@ def extra(torch, np, bdssm, configs, inputs):
         hh = torch.randn((b, H, N, P), device="cuda") * 0.05
         ys = [torch.empty((b, T, H, P), dtype=torch.bfloat16 if yd == bdssm.BF16 else torch.float32, device="cuda")
               for _ in range(S)]
-        us = graph_us(torch, lambda: [bdssm.block_step(d3, T, hh, ff, rr, Ad3, Dd3, yy) for (ff, rr), yy in zip(st, ys)]) / S
+        if bdssm.state_ops_bytes(d3) != ctypes.c_size_t(-1).value and c.in_dtype == 1:
+            ho = ops_of(d3, hh)   # the operand form where the shape has one
+            us = graph_us(torch, lambda: [bdssm.block_step_ops(d3, T, ho, ff, rr, Ad3, Dd3, yy)
+                                          for (ff, rr), yy in zip(st, ys)]) / S
+        else:
+            us = graph_us(torch, lambda: [bdssm.block_step(d3, T, hh, ff, rr, Ad3, Dd3, yy)
+                                          for (ff, rr), yy in zip(st, ys)]) / S
         ib = 2 if c.in_dtype == 1 else 4
         nb = block_step_bytes(b, H, P, N, G, T, ib, ib)
         res[f"block_step_config{ci}"] = {"workload": c.name, "us_per_step": round(us, 3),

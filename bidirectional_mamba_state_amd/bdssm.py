@@ -21,7 +21,8 @@ EXPORTS = ("bdssm_abi_version", "bdssm_status_str", "bdssm_prefix_scan_workspace
            "bdssm_prefix_scan", "bdssm_block_step", "bdssm_block_step_ex", "bdssm_commit",
            "bdssm_decode_graph_create",
            "bdssm_decode_graph_launch", "bdssm_decode_graph_destroy",
-           "bdssm_conv_workspace", "bdssm_conv", "bdssm_block_step_conv", "bdssm_commit_conv")
+           "bdssm_conv_workspace", "bdssm_conv", "bdssm_block_step_conv", "bdssm_commit_conv",
+           "bdssm_state_ops_bytes", "bdssm_state_ops", "bdssm_block_step_ops")
 
 
 class BdssmError(RuntimeError):
@@ -73,7 +74,13 @@ def load():
         lib.bdssm_commit.restype = ctypes.c_int
         lib.bdssm_commit.argtypes = [P(Dims), I32, P(SeqPtrs), V, V, V, V, V]
         lib.bdssm_decode_graph_create.restype = ctypes.c_int
-        lib.bdssm_decode_graph_create.argtypes = [P(Dims), I32, I32, V, P(SeqPtrs), P(SeqPtrs), V, V,
+        lib.bdssm_state_ops_bytes.restype = SZ
+        lib.bdssm_state_ops_bytes.argtypes = [P(Dims)]
+        lib.bdssm_state_ops.restype = ctypes.c_int
+        lib.bdssm_state_ops.argtypes = [P(Dims), V, V, V]
+        lib.bdssm_block_step_ops.restype = ctypes.c_int
+        lib.bdssm_block_step_ops.argtypes = [P(Dims), I32, V, P(SeqPtrs), P(SeqPtrs), V, V, V, V, V, V]
+        lib.bdssm_decode_graph_create.argtypes = [P(Dims), I32, I32, V, V, P(SeqPtrs), P(SeqPtrs), V, V,
                                                   P(V), P(SeqPtrs), V, V, P(V)]
         lib.bdssm_decode_graph_launch.restype = ctypes.c_int
         lib.bdssm_decode_graph_launch.argtypes = [V, V]
@@ -174,6 +181,24 @@ def block_step_ex(d, block_len, h_prefix, fwd, rev, A, D, A_rev, D_rev, y, strea
                                       _ptr(y), _stream(stream)))
 
 
+def state_ops_bytes(d):
+    """bdssm_state_ops_bytes (SIZE_MAX for invalid or unsupported dims)."""
+    return load().bdssm_state_ops_bytes(ctypes.byref(d))
+
+
+def state_ops(d, h, ops, stream=None):
+    """bdssm_state_ops: the cached state h in operand form, into ops."""
+    _check(load().bdssm_state_ops(ctypes.byref(d), _ptr(h), _ptr(ops), _stream(stream)))
+
+
+def block_step_ops(d, block_len, h_ops, fwd, rev, A, D, y, A_rev=None, D_rev=None, stream=None):
+    """bdssm_block_step_ops: block step from the state in operand form (A_rev None = A)."""
+    _check(load().bdssm_block_step_ops(ctypes.byref(d), block_len, _ptr(h_ops), _byref(_seq(fwd)),
+                                       _byref(_seq(rev)), _ptr(A), _ptr(D),
+                                       _ptr(A if A_rev is None else A_rev), _ptr(D_rev), _ptr(y),
+                                       _stream(stream)))
+
+
 def commit(d, block_len, clean, A, D, h, y=None, stream=None):
     """bdssm_commit. clean = (x, dt, B, C) tensors (C may be None when y is None)."""
     _check(load().bdssm_commit(ctypes.byref(d), block_len, _byref(_seq(clean)), _ptr(A), _ptr(D),
@@ -221,19 +246,20 @@ class DecodeGraph:
     """bdssm_decode_graph_*: the steps of one active block and its commit, recorded once
     and replayed with launch(). Keeps references to the tensors whose addresses it holds."""
 
-    def __init__(self, d, block_len, h, fwd_steps, rev_steps, A, D, ys, clean=None, y_commit=None):
+    def __init__(self, d, block_len, h, fwd_steps, rev_steps, A, D, ys, clean=None, y_commit=None,
+                 h_ops=None):
         import torch
         steps = len(ys)
         if len(fwd_steps) != steps or len(rev_steps) != steps:
             raise ValueError("one fwd, rev and y per step")
-        self._keep = (h, fwd_steps, rev_steps, A, D, ys, clean, y_commit)
+        self._keep = (h, h_ops, fwd_steps, rev_steps, A, D, ys, clean, y_commit)
         fw = (SeqPtrs * max(steps, 1))(*[_seq(s) for s in fwd_steps])
         rv = (SeqPtrs * max(steps, 1))(*[_seq(s) for s in rev_steps])
         yp = (ctypes.c_void_p * max(steps, 1))(*[_ptr(t) for t in ys])
         # record on a side stream: the legacy default stream cannot be captured
         side = torch.cuda.Stream()
         handle = ctypes.c_void_p()
-        rc = load().bdssm_decode_graph_create(ctypes.byref(d), block_len, steps, _ptr(h), fw, rv,
+        rc = load().bdssm_decode_graph_create(ctypes.byref(d), block_len, steps, _ptr(h), _ptr(h_ops), fw, rv,
                                               _ptr(A), _ptr(D), yp, _byref(_seq(clean)),
                                               _ptr(y_commit), side.cuda_stream, ctypes.byref(handle))
         _check(rc)

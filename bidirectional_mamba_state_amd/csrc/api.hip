@@ -482,6 +482,53 @@ bdssm_status bdssm_block_step_ex(const bdssm_dims *dims, int32_t block_len,
     return launch_block_step(a, static_cast<hipStream_t>(stream));
 }
 
+size_t bdssm_state_ops_bytes(const bdssm_dims *dims)
+{
+    Shape s;
+    if (check_dims(dims, &s) != BDSSM_OK || s.N != 128 || s.P != 64)
+        return SIZE_MAX;
+    return static_cast<size_t>(s.b) * s.H * s.N * s.P * 4;
+}
+
+bdssm_status bdssm_state_ops(const bdssm_dims *dims, const float *h, void *ops, void *stream)
+{
+    Shape s;
+    const bdssm_status rc = check_dims(dims, &s);
+    if (rc != BDSSM_OK)
+        return rc;
+    if (s.N != 128 || s.P != 64)
+        return BDSSM_ERR_UNSUPPORTED;
+    if (!h || !ops)
+        return BDSSM_ERR_NULL;
+    if (!aligned(h) || !aligned(ops))
+        return BDSSM_ERR_ALIGN;
+    const int64_t bytes = static_cast<int64_t>(s.b) * s.H * s.N * s.P * 4;
+    if (overlap(rng(ops, bytes), rng(h, bytes)))
+        return BDSSM_ERR_ALIAS;
+    return launched(launch_state_ops(h, ops, static_cast<int64_t>(s.b) * s.H, static_cast<hipStream_t>(stream)));
+}
+
+bdssm_status bdssm_block_step_ops(const bdssm_dims *dims, int32_t block_len, const void *h_ops,
+                                  const bdssm_seq *fwd, const bdssm_seq *rev, const float *A,
+                                  const float *D, const float *A_rev, const float *D_rev, void *y,
+                                  void *stream)
+{
+    BlockArgs a{};
+    // the operand form has the float32 state's size, so the same validation applies
+    const bdssm_status rc = prepare_block_step(dims, block_len, static_cast<const float *>(h_ops), fwd, rev, A, D,
+                                               A_rev, D_rev, y, &a);
+    if (rc != BDSSM_OK)
+        return rc;
+    if (a.s.b == 0 || block_len == 0)
+        return BDSSM_OK;
+    if (!block_lat_supported(a.s, block_len))
+        return BDSSM_ERR_UNSUPPORTED;
+    a.h_ops = h_ops;
+    a.h_prefix = nullptr;
+    const char *e = getenv("BDSSM_BLOCK_LAT_WPG");
+    return launched(launch_block_step_lat(a, e ? atoi(e) : 0, static_cast<hipStream_t>(stream)));
+}
+
 bdssm_status bdssm_commit(const bdssm_dims *dims, int32_t block_len, const bdssm_seq *clean,
                           const float *A, const float *D, float *h, void *y, void *stream)
 {

@@ -88,7 +88,9 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *dst, int o
 //   state:     N x (the workgroup's 32 or 64 columns) fp32; with 32, row n at LDS row
 //              n ^ ((n / 16) % 2) and piece c (4 columns) at slot c ^ 4 ((n / 8) % 2); with
 //              64, row n in place and piece c at slot c ^ 4 ((n / 8) % 4);
-//   x:         T x P bf16 per direction, piece c (8 columns) of row t at slot c ^ 2 (t % 4).
+//   x:         T x P bf16 per direction, piece c (8 columns) of row t at slot c ^ 2 (t % 4);
+//   state in operand form (OPS): [hi, lo][N/8][the workgroup's columns][8] bf16 as stored,
+//              a lane's operand one 16-byte read, consecutive lanes consecutive pieces.
 constexpr int kRowBlk = 16 * 128;
 
 // Workgroup barrier over LDS filled by this workgroup's copies and writes: waits until at
@@ -122,8 +124,9 @@ __device__ __forceinline__ void store_y_bf16(__amdgpu_buffer_rsrc_t r, int off, 
 
 enum { TAB_CF, TAB_CR, TAB_LGF, TAB_LGR, TAB_COLF, TAB_COLR, TAB_EF, NTAB };
 
-// WPG wavefronts per workgroup (2 or 4), each owning one 16-column block of the outputs
-template <typename Ty, int WPG>
+// WPG wavefronts per workgroup (2 or 4), each owning one 16-column block of the outputs;
+// OPS: the cached state comes in operand form (k_state_ops) instead of as float32
+template <typename Ty, int WPG, bool OPS>
 __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
 {
     constexpr int NB = 2, TP = 32;  // one 32-token pair: two 16-token row blocks
@@ -132,6 +135,7 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
     // C rows of the row block (forward, reverse), then B rows of its three score tiles
     __shared__ __attribute__((aligned(16))) __bf16 rows[NB + 3][kRowBlk];
     __shared__ __attribute__((aligned(16))) float hst[kN * CW];        // the state, CW columns
+    __bf16 *const hops = reinterpret_cast<__bf16 *>(hst);               // ... in operand form
     __shared__ __attribute__((aligned(16))) __bf16 xs[2][TP * kP];      // x, both directions
     __shared__ __attribute__((aligned(16))) float tab[WPG][NTAB][TP];   // per wavefront
 
@@ -169,7 +173,9 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
     const int64_t dt_bytes = (static_cast<int64_t>(T - 1) * H + 1) * 2;
     const auto rDf = rsrc(static_cast<const __bf16 *>(a.fwd.dt) + tok0 * H + h, dt_bytes);
     const auto rDr = rsrc(static_cast<const __bf16 *>(a.rev.dt) + tok0 * H + h, dt_bytes);
-    const auto rH = rsrc(a.h_prefix + (static_cast<int64_t>(b) * H + h) * (kN * kP), kN * kP * 4);
+    const int64_t bh = static_cast<int64_t>(b) * H + h;
+    const auto rH = OPS ? rsrc(static_cast<const __bf16 *>(a.h_ops) + bh * (2 * kN * kP), 2 * kN * kP * 2)
+                        : rsrc(a.h_prefix + bh * (kN * kP), kN * kP * 4);
 
     // ---- the workgroup's inputs, each byte copied once, in whole lines, straight into
     // LDS: each wavefront copies 1/WPG of each tile (40/WPG + 8 loads after 4 for dt), in the
@@ -204,7 +210,11 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
     constexpr int NSTATE = 8;  // state copies per wavefront, the last loads issued
 #pragma unroll
     for (int m = NSTATE * w; m < NSTATE * w + NSTATE; ++m) {  // LDS state rows 8 m .. 8 m + 7
-        if constexpr (WPG == 2) {                              // (32 columns) or 4 m .. 4 m + 3
+        if constexpr (OPS) {  // operand rows (hi/lo, n/8) RPC m .. RPC m + RPC - 1, CW pieces each
+            constexpr int RPC = 64 / CW;
+            const int row = RPC * m + lane / CW, col = lane % CW;
+            dma16(rH, &hops[RPC * m * CW * 8], (row * kP + CW * ph + col) * 16);
+        } else if constexpr (WPG == 2) {                       // (32 columns) or 4 m .. 4 m + 3
             const int lr = 8 * m + (lane >> 3), n = lr ^ ((lr >> 4) & 1), c = (lane & 7) ^ (4 * ((n >> 3) & 1));
             dma16(rH, &hst[8 * m * CW], (n * kP + CW * ph + 4 * c) * 4);
         } else {
@@ -339,6 +349,15 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
     // ---- eq. (11), cached-state term: C_t . (h_hi + h_lo), the B operand of column p being
     // h[32kk + 8q + e][p], e = 0..7, split into bf16 halves in registers; two independent chains
     f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc_lo = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (OPS) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const bf16x8 hi = *reinterpret_cast<const bf16x8 *>(&hops[((4 * kk + q) * CW + 16 * w + r16) * 8]);
+            const bf16x8 lo = *reinterpret_cast<const bf16x8 *>(&hops[((16 + 4 * kk + q) * CW + 16 * w + r16) * 8]);
+            acc = mfma(cfw[kk], hi, acc);
+            acc_lo = mfma(cfw[kk], lo, acc_lo);
+        }
+    } else {
     // 32 columns: row n = 32kk + 8q + e sits at LDS row 32kk + 8q + (e ^ (q / 2)), and local
     // column 16 w + r16 (piece 4 w + r16 / 4) at slot (4 w + r16 / 4) ^ 4 (q % 2), i.e. at
     // 16 (w ^ (q % 2)) + r16. 64 columns: row n in place, column 16 w + r16 at 16 (w ^ q) + r16.
@@ -357,6 +376,7 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
         split8(hv, hi, lo);
         acc = mfma(cfw[kk], hi, acc);
         acc_lo = mfma(cfw[kk], lo, acc_lo);
+    }
     }
     {
         const float4 e4 = *reinterpret_cast<const float4 *>(&tb_[TAB_EF][tb * 16 + 4 * q]);
@@ -394,12 +414,35 @@ hipError_t launch_ty(const BlockArgs &a, int wpg, hipStream_t st)
     const int64_t pairs = static_cast<int64_t>(a.s.b) * a.s.H;
     if (wpg != 2 && wpg != 4)
         wpg = pairs * 4 <= device_cus() ? 2 : 4;
-    if (wpg == 2) {
-        k_block_lat<Ty, 2><<<dim3(static_cast<unsigned>(a.s.H * 4), static_cast<unsigned>(a.s.b)), dim3(128), 0, st>>>(a);
-    } else {
-        k_block_lat<Ty, 4><<<dim3(static_cast<unsigned>(a.s.H * 2), static_cast<unsigned>(a.s.b)), dim3(256), 0, st>>>(a);
-    }
+    const dim3 g2(static_cast<unsigned>(a.s.H * 4), static_cast<unsigned>(a.s.b));
+    const dim3 g4(static_cast<unsigned>(a.s.H * 2), static_cast<unsigned>(a.s.b));
+    if (wpg == 2)
+        a.h_ops ? k_block_lat<Ty, 2, true><<<g2, dim3(128), 0, st>>>(a) : k_block_lat<Ty, 2, false><<<g2, dim3(128), 0, st>>>(a);
+    else
+        a.h_ops ? k_block_lat<Ty, 4, true><<<g4, dim3(256), 0, st>>>(a) : k_block_lat<Ty, 4, false><<<g4, dim3(256), 0, st>>>(a);
     return hipGetLastError();
+}
+
+// Operand form of cached states: thread (state, n/8, p) reads h[8 (n/8) + e][p], e = 0..7,
+// and writes its bf16 hi and lo parts as two 16-byte pieces (the split the block step would
+// otherwise make on every call, in the same arithmetic)
+__global__ __launch_bounds__(256) void k_state_ops(const float *__restrict__ h, __bf16 *__restrict__ ops, int64_t nbh)
+{
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= nbh * (kN / 8) * kP)
+        return;
+    const int p = static_cast<int>(i % kP), n8 = static_cast<int>((i / kP) % (kN / 8));
+    const int64_t bh = i / (kP * (kN / 8));
+    const float *src = h + bh * (kN * kP) + 8 * n8 * kP + p;
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        f[e] = src[e * kP];
+    bf16x8 hi, lo;
+    split8(f, hi, lo);
+    __bf16 *dst = ops + bh * (2 * kN * kP) + (static_cast<int64_t>(n8) * kP + p) * 8;
+    *reinterpret_cast<bf16x8 *>(dst) = hi;
+    *reinterpret_cast<bf16x8 *>(dst + kN * kP) = lo;
 }
 
 }  // namespace
@@ -414,6 +457,15 @@ bool block_lat_supported(const Shape &s, int T)
 hipError_t launch_block_step_lat(const BlockArgs &a, int wpg, hipStream_t st)
 {
     return a.s.y_dt ? launch_ty<__bf16>(a, wpg, st) : launch_ty<float>(a, wpg, st);
+}
+
+hipError_t launch_state_ops(const float *h, void *ops, int64_t nbh, hipStream_t st)
+{
+    const int64_t n = nbh * (kN / 8) * kP;
+    if (n == 0)
+        return hipSuccess;
+    k_state_ops<<<dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st>>>(h, static_cast<__bf16 *>(ops), nbh);
+    return hipGetLastError();
 }
 
 }  // namespace bdssm

@@ -12,7 +12,7 @@ struct bdssm_decode_graph {
 };
 
 extern "C" bdssm_status bdssm_decode_graph_create(const bdssm_dims *dims, int32_t block_len, int32_t steps,
-                                                  float *h, const bdssm_seq *fwd, const bdssm_seq *rev,
+                                                  float *h, void *h_ops, const bdssm_seq *fwd, const bdssm_seq *rev,
                                                   const float *A, const float *D, void *const *y,
                                                   const bdssm_seq *clean, void *y_commit, void *stream,
                                                   bdssm_decode_graph **out)
@@ -35,9 +35,13 @@ extern "C" bdssm_status bdssm_decode_graph_create(const bdssm_dims *dims, int32_
     // record the calls; on the first failure end the capture and drop what was recorded
     bdssm_status rc = BDSSM_OK;
     for (int32_t k = 0; k < steps && rc == BDSSM_OK; ++k)
-        rc = bdssm_block_step(dims, block_len, h, &fwd[k], &rev[k], A, D, y[k], stream);
-    if (rc == BDSSM_OK && clean)
+        rc = h_ops ? bdssm_block_step_ops(dims, block_len, h_ops, &fwd[k], &rev[k], A, D, A, nullptr, y[k], stream)
+                   : bdssm_block_step(dims, block_len, h, &fwd[k], &rev[k], A, D, y[k], stream);
+    if (rc == BDSSM_OK && clean) {
         rc = bdssm_commit(dims, block_len, clean, A, D, h, y_commit, stream);
+        if (rc == BDSSM_OK && h_ops)  // the next block's steps read the advanced state
+            rc = bdssm_state_ops(dims, h, h_ops, stream);
+    }
     hipGraph_t graph = nullptr;
     const hipError_t ce = hipStreamEndCapture(st, &graph);
     if (rc != BDSSM_OK || ce != hipSuccess) {

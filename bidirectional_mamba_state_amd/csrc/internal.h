@@ -51,6 +51,8 @@ struct BlockArgs {
     void *y;
     const float *A_rev;  // decay of the reverse scan (A when the directions share it)
     const float *D_rev;  // skip term of the reverse input, or NULL for none
+    const void *h_ops;   // the cached state in operand form (launch_state_ops), read instead
+                         // of h_prefix when not NULL (small-batch kernel only)
 };
 
 // Depthwise convolution of one token segment's x, B, C channels (see conv.hip)
@@ -93,6 +95,9 @@ void block_mfma_plan(const Shape &s, int *hpw, int *ps);
 hipError_t launch_block_step_mfma(const BlockArgs &a, int hpw, int ps, hipStream_t st);
 bool block_lat_supported(const Shape &s, int T);
 hipError_t launch_block_step_lat(const BlockArgs &a, int wpg, hipStream_t st);  // wpg 2, 4 or 0 (chosen)
+// Operand form of nbh cached states [nbh][N][P] float32 (N = 128, P = 64): the bf16 pair
+// hi = bf16(S), lo = bf16(S - hi) as [nbh][2][N/8][P][8]
+hipError_t launch_state_ops(const float *h, void *ops, int64_t nbh, hipStream_t st);
 hipError_t launch_forward_valu(const ForwardArgs &a, hipStream_t st);
 hipError_t launch_block_step_valu(const BlockArgs &a, hipStream_t st);
 hipError_t launch_state_pass(const PassArgs &a, hipStream_t st);

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define BDSSM_ABI_VERSION 1
+#define BDSSM_ABI_VERSION 2
 
 typedef enum {
     BDSSM_OK = 0,
@@ -165,6 +165,39 @@ bdssm_status bdssm_commit(const bdssm_dims *dims, int32_t block_len, const bdssm
                           const float *A, const float *D, float *h, void *y, void *stream);
 
 /*
+ * Cached state in operand form. The cached state is read by every denoising step of a
+ * block and changes only when a block is committed (eqs. (9)-(11): s_k is fixed while
+ * block k is denoised), so the re-encoding the block step's matrix-core product needs can
+ * be made once per cached state instead of once per step. The operand form of a float32
+ * state S is the bf16 pair hi = bf16(S), lo = bf16(S - hi) (round to nearest even; together
+ * about 16 significant bits, the same pair bdssm_block_step forms from S on every call), laid
+ * out as
+ *     ops [b][H][2 (hi, lo)][N/8][P][8] bf16,  ops[..][k][n/8][p][n%8] = k-part of S[n][p],
+ * which has the size of the float32 state. Supported for (d_state, headdim) = (128, 64).
+ *
+ * bdssm_state_ops_bytes: bytes of ops for these dims; SIZE_MAX for invalid or unsupported
+ * dims.
+ * bdssm_state_ops: writes ops from h [b][H][N][P] float32 (read only); ops must not overlap
+ * h. Errors: BDSSM_ERR_NULL, BDSSM_ERR_UNSUPPORTED (other d_state/headdim), BDSSM_ERR_ALIGN,
+ * BDSSM_ERR_ALIAS.
+ */
+size_t bdssm_state_ops_bytes(const bdssm_dims *dims);
+bdssm_status bdssm_state_ops(const bdssm_dims *dims, const float *h, void *ops, void *stream);
+
+/*
+ * Block step from the cached state in operand form: bdssm_block_step_ex with the state
+ * given as h_ops, made by bdssm_state_ops from h_prefix. Its y is bitwise that of
+ * bdssm_block_step_ex on h_prefix wherever the latter runs its small-batch kernel (bf16
+ * inputs, d_state 128, headdim 64, block_len <= 32, batch * nheads < 512), and this call
+ * always runs that kernel. Errors as bdssm_block_step_ex, with BDSSM_ERR_UNSUPPORTED for
+ * other dtypes, shapes or block_len > 32; y must not overlap h_ops.
+ */
+bdssm_status bdssm_block_step_ops(const bdssm_dims *dims, int32_t block_len, const void *h_ops,
+                                  const bdssm_seq *fwd, const bdssm_seq *rev, const float *A,
+                                  const float *D, const float *A_rev, const float *D_rev, void *y,
+                                  void *stream);
+
+/*
  * Convolution state. A Mamba layer's cache holds convolution state as well as the SSM
  * state (the cache discussion of "Training Hybrid Block Diffusion Language Models with
  * Partial Bidirectionality"); the pages leave the convolution itself open, and these calls
@@ -250,6 +283,10 @@ bdssm_status bdssm_commit_conv(const bdssm_dims *dims, int32_t block_len,
  *   fwd, rev   host arrays of `steps` input descriptors (device pointers)
  *   y          host array of `steps` device output pointers, [b][T][H][P] in y_dtype
  *   h          [b][H][N][P] float32: read by every step, then advanced by the commit
+ *   h_ops      NULL, or the cached state in operand form (bdssm_state_ops of h, made by the
+ *              caller before the first replay): the steps then read it (bdssm_block_step_ops)
+ *              and the commit is followed by bdssm_state_ops(h -> h_ops), so that it holds
+ *              the advanced state for the next replay
  *   clean      the commit's inputs, or NULL for steps only; y_commit as in bdssm_commit
  *   stream     the stream the calls are recorded on; must not be NULL (the legacy default
  *              stream cannot be captured). Nothing runs during creation.
@@ -263,7 +300,8 @@ bdssm_status bdssm_commit_conv(const bdssm_dims *dims, int32_t block_len,
  */
 typedef struct bdssm_decode_graph bdssm_decode_graph;
 bdssm_status bdssm_decode_graph_create(const bdssm_dims *dims, int32_t block_len, int32_t steps,
-                                       float *h, const bdssm_seq *fwd, const bdssm_seq *rev,
+                                       float *h, void *h_ops, const bdssm_seq *fwd,
+                                       const bdssm_seq *rev,
                                        const float *A, const float *D, void *const *y,
                                        const bdssm_seq *clean, void *y_commit, void *stream,
                                        bdssm_decode_graph **out);

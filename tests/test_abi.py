@@ -24,7 +24,7 @@ def test_library_exports_every_declared_symbol():
     assert syms == sorted(bdssm.EXPORTS)
     for s in syms:
         assert hasattr(lib, s), s
-    assert bdssm.abi_version() == 1
+    assert bdssm.abi_version() == 2
     for st in range(8):
         assert bdssm.status_str(st).startswith("BDSSM_")
     assert "unknown" in bdssm.status_str(99)
@@ -151,17 +151,17 @@ def test_decode_graph_argument_checks():
     ys = (ctypes.c_void_p * 2)(FAKE + (1 << 24), FAKE + (1 << 25))
     create = lib.bdssm_decode_graph_create
     # NULL stream (the legacy default stream cannot be captured); out is cleared
-    assert create(ctypes.byref(d), 16, 2, FAKE, f, f, FAKE, FAKE, ys, None, None, None,
+    assert create(ctypes.byref(d), 16, 2, FAKE, None, f, f, FAKE, FAKE, ys, None, None, None,
                   ctypes.byref(out)) == bdssm.ERR_NULL
     assert out.value is None
-    assert create(None, 16, 2, FAKE, f, f, FAKE, FAKE, ys, None, None, FAKE, ctypes.byref(out)) == bdssm.ERR_NULL
-    assert create(ctypes.byref(d), 16, 2, FAKE, f, f, FAKE, FAKE, ys, None, None, FAKE, None) == bdssm.ERR_NULL
-    assert create(ctypes.byref(d), 16, -1, FAKE, f, f, FAKE, FAKE, ys, None, None, FAKE,
+    assert create(None, 16, 2, FAKE, None, f, f, FAKE, FAKE, ys, None, None, FAKE, ctypes.byref(out)) == bdssm.ERR_NULL
+    assert create(ctypes.byref(d), 16, 2, FAKE, None, f, f, FAKE, FAKE, ys, None, None, FAKE, None) == bdssm.ERR_NULL
+    assert create(ctypes.byref(d), 16, -1, FAKE, None, f, f, FAKE, FAKE, ys, None, None, FAKE,
                   ctypes.byref(out)) == bdssm.ERR_SHAPE
-    assert create(ctypes.byref(d), 16, 2, FAKE, None, f, FAKE, FAKE, ys, None, None, FAKE,
+    assert create(ctypes.byref(d), 16, 2, FAKE, None, None, f, FAKE, FAKE, ys, None, None, FAKE,
                   ctypes.byref(out)) == bdssm.ERR_NULL
     # no steps and no commit: nothing to record
-    assert create(ctypes.byref(d), 16, 0, FAKE, None, None, FAKE, FAKE, None, None, None, FAKE,
+    assert create(ctypes.byref(d), 16, 0, FAKE, None, None, None, FAKE, FAKE, None, None, None, FAKE,
                   ctypes.byref(out)) == bdssm.ERR_NULL
     assert lib.bdssm_decode_graph_launch(None, None) == bdssm.ERR_NULL
     lib.bdssm_decode_graph_destroy(None)
@@ -240,3 +240,33 @@ def test_conv_argument_checks():
                                  base + (24 << 20), st, None, ws, 16, None) == bdssm.ERR_WORKSPACE
     assert lib.bdssm_commit_conv(ctypes.byref(d), 10, ctypes.byref(cp), ctypes.byref(cl), FAKE, FAKE + 256,
                                  base + (24 << 20), base + 32, None, ws, need, None) == bdssm.ERR_ALIAS
+
+
+def test_state_ops_argument_checks():
+    """bdssm_state_ops_bytes, bdssm_state_ops, bdssm_block_step_ops: sizes, and argument
+    errors reported before anything is launched."""
+    lib = bdssm.load()
+    d = bdssm.dims(2, 4, 64, 128, 1, bdssm.BF16, bdssm.F32)
+    nbytes = 2 * 4 * 128 * 64 * 4
+    assert bdssm.state_ops_bytes(d) == nbytes
+    assert bdssm.state_ops_bytes(good()) == ctypes.c_size_t(-1).value      # (16, 16): unsupported
+    assert bdssm.state_ops_bytes(bdssm.dims(1, 4, 64, 128, 3, bdssm.BF16)) == ctypes.c_size_t(-1).value
+    h, ops = FAKE, FAKE + (1 << 24)
+    st = lib.bdssm_state_ops
+    assert st(ctypes.byref(d), None, ops, None) == bdssm.ERR_NULL
+    assert st(ctypes.byref(d), h, None, None) == bdssm.ERR_NULL
+    assert st(ctypes.byref(good()), h, ops, None) == bdssm.ERR_UNSUPPORTED
+    assert st(ctypes.byref(d), h + 8, ops, None) == bdssm.ERR_ALIGN
+    assert st(ctypes.byref(d), h, h + nbytes - 16, None) == bdssm.ERR_ALIAS
+    f, r = seq(), seq()
+
+    def step(dd=d, T=32, h_ops=ops, y=FAKE + (1 << 26), A_rev=FAKE):
+        return lib.bdssm_block_step_ops(ctypes.byref(dd), T, h_ops, ctypes.byref(f), ctypes.byref(r),
+                                        FAKE, FAKE, A_rev, None, y, None)
+    assert step(h_ops=None) == bdssm.ERR_NULL
+    assert step(A_rev=None) == bdssm.ERR_NULL
+    assert step(y=ops + 1024) == bdssm.ERR_ALIAS                       # y on top of the state
+    assert step(T=33) == bdssm.ERR_UNSUPPORTED                         # longer than the kernel's blocks
+    assert step(dd=bdssm.dims(2, 4, 64, 128, 1, bdssm.F32)) == bdssm.ERR_UNSUPPORTED   # fp32 inputs
+    assert step(T=-1) == bdssm.ERR_SHAPE
+    assert step(T=0) == bdssm.OK                                       # nothing to do

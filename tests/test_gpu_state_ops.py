@@ -1,0 +1,140 @@
+"""The cached state in operand form (bdssm_state_ops) and the block step that reads it
+(bdssm_block_step_ops): the encoding is exactly the bf16 hi/lo pair its definition states,
+and the block step from it gives bitwise the y of bdssm_block_step_ex from the float32 state
+(the small-batch kernel forms the same pair on every call), hence the oracle's y."""
+import numpy as np
+import pytest
+
+import oracle
+from bidirectional_mamba_state_amd import bdssm, configs, inputs
+from harness import TOL_BF16, f32_round, rel, within
+
+pytestmark = pytest.mark.gpu
+
+
+def _expected_ops(h):
+    """[b][H][N][P] float32 -> [b][H][2][N/8][P][8] uint16: hi = bf16(h), lo = bf16(h - hi),
+    both rounded to nearest even (h - hi is exact in float32)."""
+    h = np.asarray(h, np.float32)
+    hi = inputs.round_bf16_bits(h.astype(np.float64))
+    lo = inputs.round_bf16_bits(h.astype(np.float64) - inputs.bf16_bits_to_f32(hi).astype(np.float64))
+    b, H, N, P = h.shape
+    both = np.stack([hi, lo], axis=2)                         # [b][H][2][N][P]
+    return both.reshape(b, H, 2, N // 8, 8, P).transpose(0, 1, 2, 3, 5, 4).copy()
+
+
+def test_state_ops_encoding():
+    import torch
+    rng = np.random.default_rng(11)
+    b, H, N, P = 2, 4, 128, 64
+    h = (rng.standard_normal((b, H, N, P)) * np.exp(rng.uniform(-20, 20, (b, H, N, P)))).astype(np.float32)
+    # special values: zeros, exact bf16 values (lo = 0), halfway cases that round to even
+    h[0, 0, 0, :8] = 0.0
+    h[0, 0, 1, :8] = -0.0
+    h[0, 0, 2, :8] = np.float32(1.5)
+    h[0, 0, 3, :8] = np.array([0x3F808000, 0x3F818000, 0xBF808000, 0x3F80FFFF] * 2, np.uint32).view(np.float32)
+    print(f"[case] state ops encoding b={b} H={H}", flush=True)
+    d = bdssm.dims(b, H, P, N, 1, bdssm.BF16, bdssm.F32)
+    hd = torch.from_numpy(h).cuda()
+    ops = torch.full((bdssm.state_ops_bytes(d) // 2,), -1, dtype=torch.int16, device="cuda")
+    bdssm.state_ops(d, hd, ops)
+    torch.cuda.synchronize()
+    got = ops.cpu().numpy().view(np.uint16).reshape(b, H, 2, N // 8, P, 8)
+    want = _expected_ops(h)
+    assert np.array_equal(got, want), int((got != want).sum())
+    assert torch.equal(hd.cpu(), torch.from_numpy(h))          # the state is read only
+
+
+def _case_inputs(b, H, G, T, seed):
+    from test_oracle_pins import rand_seq
+    rng = np.random.default_rng(seed)
+    fwd = rand_seq(rng, b, T, H, 64, 128, G, 1)
+    rev = rand_seq(rng, b, T, H, 64, 128, G, 1)
+    A = (-np.exp(rng.uniform(0, np.log(16), H))).astype(np.float32)
+    Ar = (-np.exp(rng.uniform(0, np.log(16), H))).astype(np.float32)
+    D = rng.standard_normal(H).astype(np.float32)
+    Dr = rng.standard_normal(H).astype(np.float32)
+    h = f32_round(rng.standard_normal((b, H, 128, 64)) * 0.1)
+    return fwd, rev, A, D, Ar, Dr, h
+
+
+@pytest.mark.parametrize("b,H,G,T", [(1, 48, 1, 32), (3, 12, 2, 17), (3, 12, 2, 32), (2, 40, 8, 1)])
+def test_block_step_ops_bitwise(monkeypatch, b, H, G, T):
+    import torch
+    fwd, rev, A, D, Ar, Dr, h = _case_inputs(b, H, G, T, 1000 + 7 * H + T)
+    tf, tr = bdssm.seq_to_device(fwd), bdssm.seq_to_device(rev)
+    Ad, Dd, Ard, Drd = (torch.from_numpy(v).cuda() for v in (A, D, Ar, Dr))
+    hd = torch.from_numpy(h.astype(np.float32)).cuda()
+    d32 = bdssm.dims(b, H, 64, 128, G, bdssm.BF16, bdssm.F32)
+    ops = torch.empty(bdssm.state_ops_bytes(d32), dtype=torch.uint8, device="cuda")
+    bdssm.state_ops(d32, hd, ops)
+    monkeypatch.setenv("BDSSM_BLOCK_LAT", "1")
+    for wpg in (2, 4):
+        monkeypatch.setenv("BDSSM_BLOCK_LAT_WPG", str(wpg))
+        for y_dt, tdt in ((bdssm.F32, torch.float32), (bdssm.BF16, torch.bfloat16)):
+            for sep in (False, True):
+                print(f"[case] block step ops b={b} H={H} G={G} T={T} wpg={wpg} y={y_dt} separate={sep}", flush=True)
+                d = bdssm.dims(b, H, 64, 128, G, bdssm.BF16, y_dt)
+                y_ref = torch.full((b, T, H, 64), 7.0, dtype=tdt, device="cuda")
+                y_ops = torch.full((b, T, H, 64), -7.0, dtype=tdt, device="cuda")
+                A_rev, D_rev = (Ard, Drd) if sep else (Ad, None)
+                bdssm.block_step_ex(d, T, hd, tf, tr, Ad, Dd, A_rev, D_rev, y_ref)
+                bdssm.block_step_ops(d, T, ops, tf, tr, Ad, Dd, y_ops, A_rev=A_rev, D_rev=D_rev)
+                torch.cuda.synchronize()
+                assert torch.equal(y_ops, y_ref)
+    yo, _, _ = oracle.block_step(h, fwd, rev, A, D)
+    assert within(rel(y_ops.float().cpu().numpy(), oracle.block_step(h, fwd, rev, A, D, A_rev=Ar, D_rev=Dr)[0]),
+                  TOL_BF16, "block step ops, separate reverse parameters, bf16 y")
+    y32 = torch.empty((b, T, H, 64), device="cuda")
+    bdssm.block_step_ops(d32, T, ops, tf, tr, Ad, Dd, y32)
+    torch.cuda.synchronize()
+    assert within(rel(y32.cpu().numpy(), yo), TOL_BF16, "block step ops vs oracle")
+
+
+def test_decode_graph_with_state_ops():
+    """The decode graph on the operand form: its steps equal eager bdssm_block_step_ops
+    calls, its commit advances h, and it leaves h_ops = state_ops(advanced h), replay after
+    replay."""
+    import torch
+    cfg = configs.get(1)
+    A, D = inputs.params(cfg)
+    H, P, N, T, steps = cfg.nheads, cfg.headdim, cfg.d_state, cfg.block_len, 3
+    print(f"[case] decode graph with state ops: {steps} steps + commit, 48 heads, T={T}", flush=True)
+    rng = np.random.default_rng(8)
+    h0 = f32_round(rng.standard_normal((1, H, N, P)) * 0.05)
+    fwd = [bdssm.seq_to_device(inputs.block(cfg, 0, k, inputs.FWD)) for k in range(steps)]
+    rev = [bdssm.seq_to_device(inputs.block(cfg, 0, k, inputs.REV)) for k in range(steps)]
+    clean = bdssm.seq_to_device(inputs.block(cfg, 0, 0, inputs.CLEAN))
+    d = bdssm.dims(1, H, P, N, 1, cfg.in_dtype, bdssm.F32)
+    Ad, Dd = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
+    h_init = torch.from_numpy(h0.astype(np.float32)).cuda()
+    nb = bdssm.state_ops_bytes(d)
+
+    h_e = h_init.clone()
+    ops_e = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    bdssm.state_ops(d, h_e, ops_e)
+    y_e = [torch.empty((1, T, H, P), device="cuda") for _ in range(steps)]
+    for k in range(steps):
+        bdssm.block_step_ops(d, T, ops_e, fwd[k], rev[k], Ad, Dd, y_e[k])
+    bdssm.commit(d, T, clean, Ad, Dd, h_e)
+    bdssm.state_ops(d, h_e, ops_e)
+    torch.cuda.synchronize()
+
+    h_g = h_init.clone()
+    ops_g = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    y_g = [torch.empty((1, T, H, P), device="cuda") for _ in range(steps)]
+    g = bdssm.DecodeGraph(d, T, h_g, fwd, rev, Ad, Dd, y_g, clean, None, h_ops=ops_g)
+    try:
+        for replay in range(3):
+            h_g.copy_(h_init)
+            bdssm.state_ops(d, h_g, ops_g)
+            for t in y_g:
+                t.zero_()
+            g.launch()
+            torch.cuda.synchronize()
+            for k in range(steps):
+                assert torch.equal(y_g[k], y_e[k]), (replay, k)
+            assert torch.equal(h_g, h_e), replay
+            assert torch.equal(ops_g, ops_e), replay
+    finally:
+        g.close()
