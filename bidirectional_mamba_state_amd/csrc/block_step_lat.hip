@@ -27,6 +27,8 @@
 // accumulators. Loads and stores go through range-checked
 // buffer resources over the stream's T tokens, so rows past T read as zero and their
 // stores are dropped (LDS rows past T are cleared in a branch taken only for short blocks).
+#include <type_traits>
+
 #include "internal.h"
 #include "mfma_tiles.h"
 
@@ -113,14 +115,8 @@ __device__ __forceinline__ bf16x8 rows_frag(const __bf16 *blk, int kk, int q, in
     return *reinterpret_cast<const bf16x8 *>(blk + 8 * (16 * r16 + ((4 * kk + q) ^ r16)));
 }
 
-__device__ __forceinline__ void store_y(__amdgpu_buffer_rsrc_t r, int off, float v)
-{
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
-}
-__device__ __forceinline__ void store_y_bf16(__amdgpu_buffer_rsrc_t r, int off, float v)
-{
-    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, static_cast<__bf16>(v)), r, off, 0, 0);
-}
+typedef uint32_t v2u32 __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
 
 enum { TAB_CF, TAB_CR, TAB_LGF, TAB_LGR, TAB_COLF, TAB_COLR, TAB_EF, NTAB };
 
@@ -137,7 +133,7 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
     __shared__ __attribute__((aligned(16))) float hst[kN * CW];        // the state, CW columns
     __bf16 *const hops = reinterpret_cast<__bf16 *>(hst);               // ... in operand form
     __shared__ __attribute__((aligned(16))) __bf16 xs[2][TP * kP];      // x, both directions
-    __shared__ __attribute__((aligned(16))) float tab[WPG][NTAB][TP];   // per wavefront
+    __shared__ __attribute__((aligned(16))) float tab[NTAB][TP];        // decay tables
 
     const int T = a.T, H = a.s.H, G = a.s.G;
     // workgroup = (head, row block, column part), grid.y = stream. The hardware deals
@@ -178,59 +174,90 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
                         : rsrc(a.h_prefix + bh * (kN * kP), kN * kP * 4);
 
     // ---- the workgroup's inputs, each byte copied once, in whole lines, straight into
-    // LDS: each wavefront copies 1/WPG of each tile (40/WPG + 8 loads after 4 for dt), in the
-    // order they are used -- dt (decay tables), B and C (score tiles), x (M X), and the state
-    // (C . h) last, so that the first products overlap the state's arrival
-    constexpr int JPW = 4 / WPG;  // 1 KB pieces per wavefront of a row block or an x tile
-    const int t0 = 2 * lane, t1 = t0 + 1;
-    const unsigned short df0 = __builtin_amdgcn_raw_buffer_load_b16(rDf, t0 * H * 2, 0, 0);
-    const unsigned short df1 = __builtin_amdgcn_raw_buffer_load_b16(rDf, t1 * H * 2, 0, 0);
-    const unsigned short dr0 = __builtin_amdgcn_raw_buffer_load_b16(rDr, t0 * H * 2, 0, 0);
-    const unsigned short dr1 = __builtin_amdgcn_raw_buffer_load_b16(rDr, t1 * H * 2, 0, 0);
-    const float Ah = a.A[h], Dh = a.D[h], Ar = a.A_rev[h];
-    const float Dr = a.D_rev ? a.D_rev[h] : 0.f;
+    // LDS, in the order of use: B and C (score tiles), x (M X), the state (C . h) last, so
+    // that the first products overlap the state's arrival. The 28 pieces of B, C and x
+    // (1 KB each) are dealt to all wavefronts but the last, which loads dt and builds the
+    // decay tables for the workgroup meanwhile (with two wavefronts, it copies x); every
+    // wavefront then copies its eighth (WPG = 2) or quarter (4) of the state.
+    constexpr int TW = WPG - 1;  // the wavefront that builds the tables
+    constexpr int NSTATE = 8;    // state copies per wavefront, its last loads
     auto row0_of = [&](int i) {  // first row of row block i
         return i < 2 ? tb * 16 : (i - 2 <= tb ? i - 2 : i - 3) * 16;
     };
-#pragma unroll
-    for (int i = 0; i < NB + 3; ++i)  // rows 4 j .. 4 j + 3 of each row block
-#pragma unroll
-        for (int j = JPW * w; j < JPW * w + JPW; ++j) {
+    // piece k < 20: rows 4 (k % 4) .. +3 of row block k / 4; k < 28: x rows 8 (k % 4) .. +7 of
+    // direction (k - 20) / 4. Rows past T: zeroed in LDS after the copy has landed.
+    auto copy_piece = [&](int k) {
+        if (k < 20) {
+            const int i = k / 4, j = k % 4;
             const auto r = i == 0 ? rCf : i == 1 ? rCr : (i - 2 <= tb ? rBf : rBr);
             const int rl = 4 * j + (lane >> 4), piece = (lane & 15) ^ rl;
             dma16(r, &rows[i][4 * j * 128], ((row0_of(i) + rl) * rowBC + 8 * piece) * 2);
-        }
-#pragma unroll
-    for (int d = 0; d < 2; ++d)  // x rows 8 j .. 8 j + 7 of each direction
-#pragma unroll
-        for (int j = JPW * w; j < JPW * w + JPW; ++j) {
+        } else {
+            const int d = (k - 20) / 4, j = (k - 20) % 4;
             const int tr = 8 * j + (lane >> 3), c = (lane & 7) ^ (2 * (tr & 3));
             dma16(d ? rXr : rXf, &xs[d][8 * j * kP], (tr * rowX + 8 * c) * 2);
         }
-    constexpr int NSTATE = 8;  // state copies per wavefront, the last loads issued
-#pragma unroll
-    for (int m = NSTATE * w; m < NSTATE * w + NSTATE; ++m) {  // LDS state rows 8 m .. 8 m + 7
-        if constexpr (OPS) {  // operand rows (hi/lo, n/8) RPC m .. RPC m + RPC - 1, CW pieces each
-            constexpr int RPC = 64 / CW;
-            const int row = RPC * m + lane / CW, col = lane % CW;
-            dma16(rH, &hops[RPC * m * CW * 8], (row * kP + CW * ph + col) * 16);
-        } else if constexpr (WPG == 2) {                       // (32 columns) or 4 m .. 4 m + 3
-            const int lr = 8 * m + (lane >> 3), n = lr ^ ((lr >> 4) & 1), c = (lane & 7) ^ (4 * ((n >> 3) & 1));
-            dma16(rH, &hst[8 * m * CW], (n * kP + CW * ph + 4 * c) * 4);
+    };
+    auto clear_piece = [&](int k) {
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        if (k < 20) {
+            const int i = k / 4, j = k % 4;
+            if (row0_of(i) + 4 * j + (lane >> 4) >= T)
+                *reinterpret_cast<uint4 *>(&rows[i][4 * j * 128 + 8 * lane]) = z;
         } else {
-            const int n = 4 * m + (lane >> 4), c = (lane & 15) ^ (4 * ((n >> 3) & 3));
-            dma16(rH, &hst[4 * m * CW], (n * kP + 4 * c) * 4);
+            const int d = (k - 20) / 4, j = (k - 20) % 4;
+            if (8 * j + (lane >> 3) >= T)
+                *reinterpret_cast<uint4 *>(&xs[d][8 * j * kP + 8 * lane]) = z;
         }
-    }
+    };
+    // pieces [lo, hi) of wavefront W: WPG = 2: B and C | x; WPG = 4: half of B and C each
+    // for 0 and 1, x for 2, none for 3
+    auto for_pieces = [&](auto W, auto fn) {
+        constexpr int w_ = decltype(W)::value;
+        constexpr int lo = WPG == 2 ? (w_ == 0 ? 0 : 20) : (w_ < 2 ? 10 * w_ : w_ == 2 ? 20 : 28);
+        constexpr int hi = WPG == 2 ? (w_ == 0 ? 20 : 28) : (w_ < 2 ? 10 * w_ + 10 : 28);
+#pragma unroll
+        for (int k = lo; k < hi; ++k)
+            fn(k);
+    };
+    auto by_wave = [&](auto fn) {  // fn(integral_constant<w>) for this wavefront's w
+        if (w == 0)
+            fn(std::integral_constant<int, 0>{});
+        else if (w == 1)
+            fn(std::integral_constant<int, 1>{});
+        else if (WPG == 4 && w == 2)
+            fn(std::integral_constant<int, 2>{});
+        else if (WPG == 4)
+            fn(std::integral_constant<int, 3>{});
+    };
+    const int t0 = 2 * lane, t1 = t0 + 1;
+    const float Ah = a.A[h], Dh = a.D[h], Ar = a.A_rev[h];
+    const float Dr = a.D_rev ? a.D_rev[h] : 0.f;
+    auto copy_state = [&]() {  // this wavefront's NSTATE state pieces
+#pragma unroll
+        for (int m = NSTATE * w; m < NSTATE * w + NSTATE; ++m) {  // LDS state rows 8 m .. 8 m + 7
+            if constexpr (OPS) {  // operand rows (hi/lo, n/8) RPC m .. RPC m + RPC - 1, CW pieces each
+                constexpr int RPC = 64 / CW;
+                const int row = RPC * m + lane / CW, col = lane % CW;
+                dma16(rH, &hops[RPC * m * CW * 8], (row * kP + CW * ph + col) * 16);
+            } else if constexpr (WPG == 2) {                       // (32 columns) or 4 m .. 4 m + 3
+                const int lr = 8 * m + (lane >> 3), n = lr ^ ((lr >> 4) & 1), c = (lane & 7) ^ (4 * ((n >> 3) & 1));
+                dma16(rH, &hst[8 * m * CW], (n * kP + CW * ph + 4 * c) * 4);
+            } else {
+                const int n = 4 * m + (lane >> 4), c = (lane & 15) ^ (4 * ((n >> 3) & 3));
+                dma16(rH, &hst[4 * m * CW], (n * kP + 4 * c) * 4);
+            }
+        }
+    };
 
     // ---- decay tables of both directions (lane l holds tokens 2l and 2l+1; dt past T is 0),
-    // computed by every wavefront into its own table
-    float(*tb_)[TP] = tab[w];
-    {
-        const float f0 = __uint_as_float(static_cast<uint32_t>(df0) << 16);
-        const float f1 = __uint_as_float(static_cast<uint32_t>(df1) << 16);
-        const float g0 = __uint_as_float(static_cast<uint32_t>(dr0) << 16);
-        const float g1 = __uint_as_float(static_cast<uint32_t>(dr1) << 16);
+    // built once for the workgroup
+    float(*tb_)[TP] = tab;
+    auto build_tables = [&](const unsigned short (&dt4)[4]) {  // dt of tokens t0, t1 (fwd, rev)
+        const float f0 = __uint_as_float(static_cast<uint32_t>(dt4[0]) << 16);
+        const float f1 = __uint_as_float(static_cast<uint32_t>(dt4[1]) << 16);
+        const float g0 = __uint_as_float(static_cast<uint32_t>(dt4[2]) << 16);
+        const float g1 = __uint_as_float(static_cast<uint32_t>(dt4[3]) << 16);
         // forward: c_t inclusive prefix sum; reference at the pair's last token (lane 15)
         const float a0 = f0 * Ah, a1 = f1 * Ah, loc = a0 + a1;
         const float inc = wave_inclusive_sum(loc), excl = inc - loc;
@@ -256,27 +283,29 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
             tb_[TAB_EF][t0] = __builtin_amdgcn_exp2f(c0);
             tb_[TAB_EF][t1] = __builtin_amdgcn_exp2f(c1);
         }
-    }
-    // B, C and x of this wavefront have landed once at most its state copies are in flight
-    __builtin_amdgcn_s_waitcnt(0x0F70 | NSTATE);  // vmcnt(NSTATE)
-    if (T < TP) {
-        // rows past T: whatever the copies left in LDS there is replaced by zeros, each
-        // wavefront in the pieces it copied (after the wait above)
-        const uint4 z = make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < NB + 3; ++i)
-#pragma unroll
-            for (int j = JPW * w; j < JPW * w + JPW; ++j)
-                if (row0_of(i) + 4 * j + (lane >> 4) >= T)
-                    *reinterpret_cast<uint4 *>(&rows[i][4 * j * 128 + 8 * lane]) = z;
-#pragma unroll
-        for (int d = 0; d < 2; ++d)
-#pragma unroll
-            for (int j = JPW * w; j < JPW * w + JPW; ++j)
-                if (8 * j + (lane >> 3) >= T)
-                    *reinterpret_cast<uint4 *>(&xs[d][8 * j * kP + 8 * lane]) = z;
-    }
-    lds_barrier<NSTATE>();  // (1) everyone's B, C and x
+    };
+    // each wavefront's prologue, specialized per wavefront so that every wait counts exactly
+    // the loads it must (and no wavefront holds loads it does not use): the table wavefront
+    // loads dt first; then its B, C or x pieces; then (table wavefront) the tables; then its
+    // state pieces. Its pieces have landed once at most the state copies are in flight.
+    by_wave([&](auto W) {
+        constexpr bool table_wave = decltype(W)::value == TW;
+        unsigned short dt4[4] = {0, 0, 0, 0};
+        if constexpr (table_wave) {
+            dt4[0] = __builtin_amdgcn_raw_buffer_load_b16(rDf, t0 * H * 2, 0, 0);
+            dt4[1] = __builtin_amdgcn_raw_buffer_load_b16(rDf, t1 * H * 2, 0, 0);
+            dt4[2] = __builtin_amdgcn_raw_buffer_load_b16(rDr, t0 * H * 2, 0, 0);
+            dt4[3] = __builtin_amdgcn_raw_buffer_load_b16(rDr, t1 * H * 2, 0, 0);
+        }
+        for_pieces(W, copy_piece);
+        if constexpr (table_wave)
+            build_tables(dt4);
+        copy_state();
+        __builtin_amdgcn_s_waitcnt(0x0F70 | NSTATE);  // vmcnt(NSTATE)
+        if (T < TP)  // rows past T: whatever the copies left in LDS there is replaced by zeros
+            for_pieces(W, clear_piece);
+    });
+    lds_barrier<NSTATE>();  // (1) everyone's B, C and x, and the tables
 
     // ---- score tiles of the row block: S[t = tb*16 + r16][s = sb*16 + 4q + j]
     bf16x8 cfw[4], crv[4];
@@ -326,7 +355,7 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
             const float w = __builtin_amdgcn_exp2f(ctf + lg[j]);
             af[j] = static_cast<__bf16>(s <= t ? sv * w : 0.f);
         }
-        acc_x = mfma(af, xvf, acc_x);
+        acc_x = mfma(xvf, af, acc_x);
     }
     // eq. (12), reverse inside the block (s >= t)
     {
@@ -343,7 +372,7 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
             const float w = __builtin_amdgcn_exp2f(ctr + lg[j]);
             af[j] = static_cast<__bf16>(s >= t ? sv * w : 0.f);
         }
-        acc_x = mfma(af, xvr, acc_x);
+        acc_x = mfma(xvr, af, acc_x);
     }
     lds_barrier<0>();  // (2) everyone's state
     // ---- eq. (11), cached-state term: C_t . (h_hi + h_lo), the B operand of column p being
@@ -354,8 +383,8 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
         for (int kk = 0; kk < 4; ++kk) {
             const bf16x8 hi = *reinterpret_cast<const bf16x8 *>(&hops[((4 * kk + q) * CW + 16 * w + r16) * 8]);
             const bf16x8 lo = *reinterpret_cast<const bf16x8 *>(&hops[((16 + 4 * kk + q) * CW + 16 * w + r16) * 8]);
-            acc = mfma(cfw[kk], hi, acc);
-            acc_lo = mfma(cfw[kk], lo, acc_lo);
+            acc = mfma(hi, cfw[kk], acc);
+            acc_lo = mfma(lo, cfw[kk], acc_lo);
         }
     } else {
     // 32 columns: row n = 32kk + 8q + e sits at LDS row 32kk + 8q + (e ^ (q / 2)), and local
@@ -374,35 +403,50 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
         }
         bf16x8 hi, lo;
         split8(hv, hi, lo);
-        acc = mfma(cfw[kk], hi, acc);
-        acc_lo = mfma(cfw[kk], lo, acc_lo);
+        acc = mfma(hi, cfw[kk], acc);
+        acc_lo = mfma(lo, cfw[kk], acc_lo);
     }
     }
+    // The products were taken with the state and x as A operands, so the accumulators hold
+    // y^T: lane (token t = 16 tb + r16, quarter q) has columns p0 .. p0+3 of its token.
+    const int p0 = 16 * pblk + 4 * q;
     {
-        const float4 e4 = *reinterpret_cast<const float4 *>(&tb_[TAB_EF][tb * 16 + 4 * q]);
-        acc[0] = fmaf(acc[0] + acc_lo[0], e4.x, acc_x[0]);
-        acc[1] = fmaf(acc[1] + acc_lo[1], e4.y, acc_x[1]);
-        acc[2] = fmaf(acc[2] + acc_lo[2], e4.z, acc_x[2]);
-        acc[3] = fmaf(acc[3] + acc_lo[3], e4.w, acc_x[3]);
-    }
-    // ---- eq. (13) + D x (+ D_rev x_rev), written once: rows tb*16 + 4q + j, column p. The
-    // x of those rows are slots (tb & 1) * 4 + j of the operands. Rows past T fall outside
-    // the output buffer's range and are dropped.
-    const auto rY = rsrc(static_cast<Ty *>(a.y) + x0, (static_cast<int64_t>(T - 1) * rowX + kP) * sizeof(Ty));
-    const bool with_dr = a.D_rev != nullptr;
-    const bool odd = tb & 1;
+        const float ef = tb_[TAB_EF][t];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int tr = tb * 16 + 4 * q + j;
-        const float xa = bf2f(xvf[j]), xb = bf2f(xvf[4 + j]);
-        const float ra = bf2f(xvr[j]), rb = bf2f(xvr[4 + j]);
-        float v = fmaf(Dh, odd ? xb : xa, acc[j]);
-        if (with_dr)
-            v = fmaf(Dr, odd ? rb : ra, v);
-        if constexpr (sizeof(Ty) == 2)
-            store_y_bf16(rY, (tr * rowX + p) * 2, v);
-        else
-            store_y(rY, (tr * rowX + p) * 4, v);
+        for (int j = 0; j < 4; ++j)
+            acc[j] = fmaf(acc[j] + acc_lo[j], ef, acc_x[j]);
+    }
+    // ---- eq. (13) + D x (+ D_rev x_rev), written once: token t, columns p0 .. p0+3, one 8-
+    // (bf16) or 16-byte (float32) store. Rows past T fall outside the output buffer's range
+    // and are dropped.
+    auto x4 = [&](int d) {  // x[t][p0 .. p0+3] of direction d, from the LDS tile
+        return *reinterpret_cast<const bf16x4 *>(&xs[d][t * kP + 8 * ((p0 >> 3) ^ (2 * (t & 3))) + (p0 & 7)]);
+    };
+    float o[4];
+    {
+        const bf16x4 xf = x4(0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            o[j] = fmaf(Dh, bf2f(xf[j]), acc[j]);
+    }
+    if (a.D_rev) {
+        const bf16x4 xr = x4(1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            o[j] = fmaf(Dr, bf2f(xr[j]), o[j]);
+    }
+    const auto rY = rsrc(static_cast<Ty *>(a.y) + x0, (static_cast<int64_t>(T - 1) * rowX + kP) * sizeof(Ty));
+    const int off = (t * rowX + p0) * static_cast<int>(sizeof(Ty));
+    if constexpr (sizeof(Ty) == 2) {
+        bf16x4 ov;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            ov[j] = static_cast<__bf16>(o[j]);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32, ov), rY, off, 0, 0);
+    } else {
+        __builtin_amdgcn_raw_buffer_store_b128(
+            v4u32{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])}, rY,
+            off, 0, 0);
     }
 }
 
