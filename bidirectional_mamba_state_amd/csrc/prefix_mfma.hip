@@ -28,6 +28,7 @@
 // The fp32 states and the weighted x~ operand are split into bf16 hi + lo parts, so that
 // products against them keep ~16 significant bits; B, C and x are exact in bf16.
 #include <algorithm>
+#include <type_traits>
 
 #include "internal.h"
 #include "mfma_tiles.h"
@@ -504,6 +505,303 @@ __global__ __launch_bounds__(256) void k_seg_scan(float *buf, const float *tot, 
         h_out[(static_cast<int64_t>(b) * H + h) * NP + e] = v;
 }
 
+// State-only pass (segment end states, and the commit): h <- exp(c_63) h + B^T (w o x) per
+// 64-token sub-chunk, w_s = exp(c_63 - c_s) dt_s, with the state in the MFMA accumulators of
+// wavefront w (columns 16w .. 16w+15) as in k_scan. Its time per sub-chunk is the staging of
+// B and x (24 KB per head), so they are copied straight into LDS (gfx950 buffer loads to
+// LDS, no registers on the way) in whole 128-byte lines, two sub-chunks ahead into three
+// buffers, and read by transposing reads. One head per workgroup (with two, the operands
+// do not fit the registers beside the states; those launches keep k_scan).
+// The compiler waits for a copy before an LDS read only when it cannot tell that the two
+// touch different buffers; it can when each buffer is its own LDS array, the loop is
+// unrolled by NBUF (buffer choice known at compile time) and its body has no branch. So:
+// the loop runs whole groups of NBUF sub-chunks (the rest after it), every wavefront builds
+// its own copy of the decay tables (no wavefront-dependent branch), the staging buffers
+// are cleared once before the first copy instead of per sub-chunk (rows past the stream's
+// end then hold zeros or an earlier sub-chunk's finite inputs, and weigh 0), and the
+// barriers are bare (a memory fence would wait for every copy). Tile layouts, 16-byte
+// pieces of a row permuted so that a transposing read (4 rows x 32 bytes per 16 lanes)
+// falls in distinct banks:
+//   B: 64 rows x 128 bf16, piece c of row t at slot c ^ 2 (t % 4);
+//   x: 64 rows x 64 bf16 per head, piece c of row t at slot c ^ 2 (t % 4).
+__global__ __launch_bounds__(256, 2) void k_state(ScanArgs a)
+{
+    constexpr int HPW = 1, NBUF = 3;
+    __shared__ __attribute__((aligned(16))) __bf16 sB0[SC * kN];
+    __shared__ __attribute__((aligned(16))) __bf16 sB1[SC * kN];
+    __shared__ __attribute__((aligned(16))) __bf16 sB2[SC * kN];
+    __shared__ __attribute__((aligned(16))) __bf16 sX0[HPW][SC * kP];
+    __shared__ __attribute__((aligned(16))) __bf16 sX1[HPW][SC * kP];
+    __shared__ __attribute__((aligned(16))) __bf16 sX2[HPW][SC * kP];
+    // per wavefront: TAB_W and the total log-decay of sub-chunks k, k+1, k+2 (by k % 3)
+    __shared__ __attribute__((aligned(16))) float sW[3][4][HPW][SC];
+    __shared__ float sTot[3][4][HPW];
+    auto bufB = [&](auto ph) -> __bf16 * {
+        if constexpr (decltype(ph)::value == 0)
+            return sB0;
+        else if constexpr (decltype(ph)::value == 1)
+            return sB1;
+        else
+            return sB2;
+    };
+    auto bufX = [&](auto ph, int hh) -> __bf16 * {
+        if constexpr (decltype(ph)::value == 0)
+            return sX0[hh];
+        else if constexpr (decltype(ph)::value == 1)
+            return sX1[hh];
+        else
+            return sX2[hh];
+    };
+
+    // workgroups of one segment (all heads of a stream) go to the same XCD
+    const int nwg = gridDim.x;
+    int lid = blockIdx.x;
+    if ((nwg & 7) == 0)
+        lid = (lid & 7) * (nwg >> 3) + (lid >> 3);
+    const int H = a.s.H, G = a.s.G, NGRP = H / HPW;
+    const int h0 = (lid % NGRP) * HPW;
+    const int sg = (lid / NGRP) % a.nseg;
+    const int b = lid / (NGRP * a.nseg);
+    const int g = h0 / (H / G);
+    const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int p0 = 16 * wave;  // this wavefront's state columns
+
+    const int64_t len = a.len;
+    const int64_t seg_t0 = static_cast<int64_t>(sg) * a.seg_sub * SC;
+    const int nsub = static_cast<int>(min<int64_t>(a.seg_sub, (len - seg_t0 + SC - 1) / SC));
+    const int rowBC = G * kN, rowX = H * kP;
+    const int64_t tok0 = static_cast<int64_t>(b) * len;
+    const int64_t NP = static_cast<int64_t>(kN) * kP;
+    const __bf16 *Bg = static_cast<const __bf16 *>(a.in.B) + tok0 * rowBC + g * kN;
+    const __bf16 *xg = static_cast<const __bf16 *>(a.in.x) + tok0 * rowX + h0 * kP;
+    const __bf16 *dtg = static_cast<const __bf16 *>(a.in.dt) + tok0 * H + h0;
+    // range-checked buffers over the tokens of one sub-chunk (based at its first token, so
+    // that offsets stay small however long the stream): rows past the stream's end read as
+    // zero
+    const auto mk = [](const void *base, int64_t bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), 0x00020000);
+    };
+    float Ah[HPW];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh)
+        Ah[hh] = a.A[h0 + hh];
+
+    // ---- copies of sub-chunk k into buffer PH = k % NBUF: B in 16 pieces of 1 KB (4 rows),
+    // x in 8 per head (8 rows); wavefront w takes B pieces w + 4u (u < 4) and x pieces
+    // w + 4 (u - 4) (u >= 4)
+    constexpr int NPW = 4 + 2 * HPW;  // pieces per wavefront
+    auto piece_B = [&](int u) { return wave + 4 * u; };
+    auto piece_X = [&](int u) { return wave + 4 * (u - 4); };  // head px / 8, rows 8 (px % 8) ..
+    auto copy = [&](auto PH, int k) {
+        const int kk = min(k, nsub - 1);  // past the segment: the last sub-chunk again (unused)
+        const int64_t t0 = seg_t0 + static_cast<int64_t>(kk) * SC;
+        const int nrows = static_cast<int>(min<int64_t>(SC, len - t0));
+        const auto rB = mk(Bg + t0 * rowBC, ((nrows - 1) * rowBC + kN) * 2);
+        const auto rX = mk(xg + t0 * rowX, ((nrows - 1) * rowX + HPW * kP) * 2);
+#pragma unroll
+        for (int u = 0; u < NPW; ++u) {
+            if (u < 4) {
+                const int pc = piece_B(u), row = 4 * pc + (lane >> 4), c = (lane & 15) ^ (2 * (row & 3));
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rB, (__attribute__((address_space(3))) void *)(bufB(PH) + 4 * pc * kN), 16,
+                    (row * rowBC + 8 * c) * 2, 0, 0, 0);
+            } else {
+                const int px = piece_X(u), hh = px >> 3, row = 8 * (px & 7) + (lane >> 3);
+                const int c = (lane & 7) ^ (2 * (row & 3));
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rX, (__attribute__((address_space(3))) void *)(bufX(PH, hh) + 8 * (px & 7) * kP), 16,
+                    (row * rowX + hh * kP + 8 * c) * 2, 0, 0, 0);
+            }
+        }
+    };
+    auto clear = [&](auto PH) {  // this wavefront's pieces of buffer PH
+        const uint4 z = make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < NPW; ++u) {
+            if (u < 4) {
+                *reinterpret_cast<uint4 *>(bufB(PH) + 4 * piece_B(u) * kN + 8 * lane) = z;
+            } else {
+                const int px = piece_X(u);
+                *reinterpret_cast<uint4 *>(bufX(PH, px >> 3) + 8 * (px & 7) * kP + 8 * lane) = z;
+            }
+        }
+    };
+    // dt of sub-chunk k, token `lane`, every head of the workgroup (zero past the stream's
+    // end; k past the segment: its last sub-chunk again)
+    auto load_dt = [&](int k, unsigned short (&d)[HPW]) {
+        const int kk = min(k, nsub - 1);
+        const int64_t t0 = seg_t0 + static_cast<int64_t>(kk) * SC;
+        const int nrows = static_cast<int>(min<int64_t>(SC, len - t0));
+        const auto rD = mk(dtg + t0 * H, ((nrows - 1) * H + HPW) * 2);
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh)
+            d[hh] = __builtin_amdgcn_raw_buffer_load_b16(rD, (lane * H + hh) * 2, 0, 0);
+    };
+    // TAB_W and the total log-decay of sub-chunk k into this wavefront's own tables
+    auto tables = [&](int k, const unsigned short (&dbits)[HPW]) {
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) {
+            const float d = __uint_as_float(static_cast<uint32_t>(dbits[hh]) << 16);
+            const float inc = wave_inclusive_sum(d * Ah[hh]);
+            const float c = inc * kLog2e;
+            const float clast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 63));
+            sW[k % 3][wave][hh][lane] = __builtin_amdgcn_exp2f(clast - c) * d;
+            sTot[k % 3][wave][hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inc), 63));
+        }
+    };
+    // bare barrier: waits until at most N of this wavefront's loads are outstanding and its
+    // LDS writes are done, then synchronizes
+    auto barrier = [&](auto N) {
+        constexpr int n = decltype(N)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0070);  // vmcnt(n), lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    f32x4 hs[HPW][8];  // hs[hh][i] holds h[16 i + 4 q + j][p0 + r16] of head h0 + hh
+    float seg_tot[HPW];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh)
+        seg_tot[hh] = 0.f;
+    // one sub-chunk k, in buffer PH = k % NBUF
+    auto step = [&](auto PH, int k) {
+        constexpr int ph = decltype(PH)::value, phn = (ph + NBUF - 1) % NBUF;
+        // this wavefront's copies of k have landed once at most those issued after them are
+        // in flight: dt of k+1 and the copies of k+1
+        barrier(std::integral_constant<int, NPW + HPW>{});
+        unsigned short dn[HPW];
+        {
+            // every operand of the sub-chunk into registers first: B^T (contraction over tokens
+            // 32 ks + 4q + e and 32 ks + 16 + 4q + e, rows n = 16 i + r16) and x~ (columns
+            // p0 + r16) by transposing reads (lane r16 addresses row 4q + r16/4, columns
+            // 4 (r16 % 4) .. of a 16-column block), and the weights
+            bf16x8 bt[2][8], xf[HPW][2];
+            float wv[HPW][2][8];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int tr = 32 * ks + 4 * q + (r16 >> 2), sw = 2 * (tr & 3);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int col = 16 * i + 4 * (r16 & 3);
+                    const __bf16 *p = bufB(PH) + tr * kN + 8 * ((col >> 3) ^ sw) + (col & 7);
+                    bt[ks][i] = cat(tr_read(p), tr_read(p + 16 * kN));
+                }
+#pragma unroll
+                for (int hh = 0; hh < HPW; ++hh) {
+                    const int col = p0 + 4 * (r16 & 3);
+                    const __bf16 *px = bufX(PH, hh) + tr * kP + 8 * ((col >> 3) ^ sw) + (col & 7);
+                    xf[hh][ks] = cat(tr_read(px), tr_read(px + 16 * kP));
+                    const float4 w0 = *reinterpret_cast<const float4 *>(&sW[k % 3][wave][hh][32 * ks + 4 * q]);
+                    const float4 w1 = *reinterpret_cast<const float4 *>(&sW[k % 3][wave][hh][32 * ks + 16 + 4 * q]);
+                    wv[hh][ks][0] = w0.x, wv[hh][ks][1] = w0.y, wv[hh][ks][2] = w0.z, wv[hh][ks][3] = w0.w;
+                    wv[hh][ks][4] = w1.x, wv[hh][ks][5] = w1.y, wv[hh][ks][6] = w1.z, wv[hh][ks][7] = w1.w;
+                }
+            }
+            float tot[HPW];
+#pragma unroll
+            for (int hh = 0; hh < HPW; ++hh)
+                tot[hh] = sTot[k % 3][wave][hh];
+            // then sub-chunk k + NBUF - 1 into the buffer k - 1 has left, its dt first (the
+            // compiler may make the reads above wait for the copies of k+1, but not for these)
+            load_dt(k + 2, dn);
+            copy(std::integral_constant<int, phn>{}, k + NBUF - 1);
+
+            // state: h <- exp(c_63) h + B^T (w o x)
+#pragma unroll
+            for (int hh = 0; hh < HPW; ++hh) {
+                seg_tot[hh] += tot[hh];
+                const float alpha = __expf(tot[hh]);
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    hs[hh][i] *= alpha;
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+                for (int hh = 0; hh < HPW; ++hh) {
+                    float xw[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        xw[e] = bf2f(xf[hh][ks][e]) * wv[hh][ks][e];
+                    bf16x8 xhi, xlo;
+                    split8(xw, xhi, xlo);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        hs[hh][i] = mfma(bt[ks][i], xhi, hs[hh][i]);
+                        hs[hh][i] = mfma(bt[ks][i], xlo, hs[hh][i]);
+                    }
+                }
+            }
+        }
+        // tables of sub-chunk k+2 into the table buffer k-1 has left
+        tables(k + 2, dn);
+    };
+
+    // ---- prologue: clear this wavefront's staging pieces, put sub-chunks 0 .. NBUF-2 in
+    // flight (each dt ahead of the copies after it, so that waiting for it never waits for
+    // them), load the entering state, build the tables of 0 and 1, and let everything land
+    // once, so that the waits in the loop can be counted exactly
+    clear(std::integral_constant<int, 0>{});
+    clear(std::integral_constant<int, 1>{});
+    clear(std::integral_constant<int, 2>{});
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the clears precede the copies
+    {
+        unsigned short d0[HPW], d1[HPW];
+        load_dt(0, d0);
+        copy(std::integral_constant<int, 0>{}, 0);
+        load_dt(1, d1);
+        copy(std::integral_constant<int, 1>{}, 1);
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                hs[hh][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (a.h_in) {
+                const float *hin = a.h_in + ((static_cast<int64_t>(b) * a.nseg + sg) * H + h0 + hh) * NP;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        hs[hh][i][j] = hin[(16 * i + 4 * q + j) * kP + p0 + r16];
+            }
+        }
+        tables(0, d0);
+        tables(1, d1);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    }
+    int k = 0;
+    for (; k + NBUF <= nsub; k += NBUF) {  // whole groups: a body with no branch
+        step(std::integral_constant<int, 0>{}, k);
+        step(std::integral_constant<int, 1>{}, k + 1);
+        step(std::integral_constant<int, 2>{}, k + 2);
+    }
+    if (k < nsub)
+        step(std::integral_constant<int, 0>{}, k);
+    if (k + 1 < nsub)
+        step(std::integral_constant<int, 1>{}, k + 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // no copy outlives the workgroup
+
+    // ---- end of the segment
+    if (a.h_end) {
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) {
+            float *base = a.h_end + ((static_cast<int64_t>(b) * a.nseg + sg) * H + h0 + hh) * NP;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    base[(16 * i + 4 * q + j) * kP + p0 + r16] = hs[hh][i][j];
+        }
+    }
+    if (a.tot && tid == 0) {
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh)
+            a.tot[(static_cast<int64_t>(b) * a.nseg + sg) * H + h0 + hh] = seg_tot[hh];
+    }
+}
+
 template <bool FULL, int HPW, typename Ty>
 hipError_t launch_scan(const ScanArgs &a, hipStream_t st)
 {
@@ -521,11 +819,14 @@ hipError_t launch_scan(const ScanArgs &a, hipStream_t st)
 template <bool FULL, typename Ty>
 hipError_t launch_scan_hpw(const ScanArgs &a, int hpw, hipStream_t st)
 {
-    if constexpr (!FULL) {
+    if constexpr (!FULL) {  // the state-only pass
         if (hpw == 2)
             return launch_scan<FULL, 2, Ty>(a, st);
+        k_state<<<dim3(static_cast<unsigned>(a.s.b * a.nseg * a.s.H)), dim3(256), 0, st>>>(a);
+        return hipGetLastError();
+    } else {
+        return launch_scan<FULL, 1, Ty>(a, st);
     }
-    return launch_scan<FULL, 1, Ty>(a, st);
 }
 
 // Heads per workgroup: as many as the pass allows (shared B/C staging and scores), but
