@@ -86,8 +86,6 @@ struct Lds {
     __bf16 B[SC * kN];
     __bf16 C[FULL ? SC * kN : 8];
     __bf16 X[HPW][SC * kP];
-    // FULL: each wavefront's state columns as bf16 hi and lo rows [p][n] (private to it)
-    __bf16 hT[FULL ? 4 * HPW : 1][FULL ? 2 : 1][FULL ? 16 * kN : 8];
     float tab[2][HPW][NTAB][SC];  // decay tables of sub-chunks k and k+1 (by parity)
     float tot[2][HPW];
     // FULL: the decay-weighted causal score tiles M[t][s] of the sub-chunk (row block tb,
@@ -149,23 +147,6 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
                     hs[hh][i][j] = hin[(16 * i + 4 * q + j) * kP + p0 + r16];
         }
     }
-    auto publish_state = [&]() {  // hs -> this wavefront's hi/lo rows in LDS (FULL only)
-        if constexpr (FULL && WITHY) {
-#pragma unroll
-            for (int hh = 0; hh < HPW; ++hh)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    bf16x4 hi, lo;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        hi[j] = static_cast<__bf16>(hs[hh][i][j]);
-                        lo[j] = static_cast<__bf16>(hs[hh][i][j] - bf2f(hi[j]));
-                    }
-                    *reinterpret_cast<bf16x4 *>(&L.hT[wave * HPW + hh][0][f8_off<kN>(r16, 16 * i + 4 * q)]) = hi;
-                    *reinterpret_cast<bf16x4 *>(&L.hT[wave * HPW + hh][1][f8_off<kN>(r16, 16 * i + 4 * q)]) = lo;
-                }
-        }
-    };
     auto store_state = [&](float *base) {  // base: [HPW heads][N][P] with head stride NP
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh)
@@ -287,7 +268,6 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
         const int64_t t1 = seg_t0 + SC * static_cast<int64_t>(min(1, nsub - 1));
         dt1 = dtg[(t1 + min<int64_t>(lane, len - t1 - 1)) * H + th];
     }
-    publish_state();
     store_stage(0);
     tables(0);
     st.dt = dt1;
@@ -370,17 +350,24 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
                 }
             }
             load_c(kn);
-            // (2) the state entering the sub-chunk: y^T[p][t] = sum_n h[n][p] C[t][n], from this
-            // wavefront's hi/lo copy of its columns (rows p, contraction over n in the order
-            // of two stacked accumulator tiles)
-            const __bf16 *hTh = L.hT[wave][0], *hTl = L.hT[wave][1];
+            // (2) the state entering the sub-chunk: y^T[p][t] = sum_n h[n][p] C[t][n]. The
+            // state accumulators are the A operand as they stand: lane (p, q) holds
+            // h[16 i + 4q + j][p], so tiles 2m and 2m+1 give it rows 32m + 4q + j and
+            // 32m + 16 + 4q + j, the contraction order of the operand fragments; they are
+            // split into bf16 hi + lo here
             f32x4 acc[4];
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb)
                 acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                const bf16x8 hfh = frag<kN>(hTh, 0, m, q, r16), hfl = frag<kN>(hTl, 0, m, q, r16);
+                bf16x8 hfh, hfl;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float v = hs[0][2 * m + (e >> 2)][e & 3];
+                    hfh[e] = static_cast<__bf16>(v);
+                    hfl[e] = static_cast<__bf16>(v - bf2f(hfh[e]));
+                }
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) {
                     const bf16x8 cf = frag<kN>(L.C, tb, m, q, r16);
@@ -458,7 +445,6 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
                 }
             }
         }
-        publish_state();  // private to the wavefront: no barrier needed before its next use
         __syncthreads();  // (B) every LDS read for sub-chunk k is done
         // unconditional, so that no path reaches the loop head with loads in flight (after
         // the last sub-chunk it stages data nobody reads)
