@@ -507,28 +507,37 @@ def extra(torch, np, bdssm, configs, inputs):
 
 def secondary(torch, np, bdssm, configs, inputs, reps=20):
     res = []
-    # 64-stream running set: T = 128, fp32 state per stream (values do not affect timing;
-    # the state is drawn at random, inputs from the seeded generator)
+    # 64-stream running set: T = 128, the cached fp32 state per stream in operand form (made
+    # once per commit, i.e. once per 16 steps of this workload; its time is reported beside);
+    # values do not affect timing: the state is drawn at random, inputs from the seeded
+    # generator
     c4 = configs.get(4)
     b, H, P, N, G, T = c4.batch, c4.nheads, c4.headdim, c4.d_state, c4.ngroups, c4.block_len
     A, D = inputs.params(c4)
     Ad, Dd = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
     d = bdssm.dims(b, H, P, N, G, c4.in_dtype, bdssm.BF16)
     h = torch.randn((b, H, N, P), device="cuda") * 0.05
+    ops = torch.empty(bdssm.state_ops_bytes(d), dtype=torch.uint8, device="cuda")
+    bdssm.state_ops(d, h, ops)
     f = bdssm.seq_to_device(inputs.block(c4, 0, 0, inputs.FWD))
     r = bdssm.seq_to_device(inputs.block(c4, 0, 0, inputs.REV))
     y = torch.empty((b, T, H, P), dtype=torch.bfloat16, device="cuda")
     tm = Timer(torch)
-    for i in range(reps + 3):
-        (tm if i >= 3 else Timer(torch)).run("k", lambda: bdssm.block_step(d, T, h, f, r, Ad, Dd, y))
+    for name, fn in (("k", lambda: bdssm.block_step_ops(d, T, ops, f, r, Ad, Dd, y)),
+                     ("f32", lambda: bdssm.block_step(d, T, h, f, r, Ad, Dd, y)),
+                     ("ops", lambda: bdssm.state_ops(d, h, ops))):
+        for i in range(reps + 3):  # each kernel back to back with itself
+            (tm if i >= 3 else Timer(torch)).run(name, fn)
     torch.cuda.synchronize()
     us = tm.avg_us("k")
     nb = block_step_bytes(b, H, P, N, G, T, 2, 2)
-    res.append({"workload": "block step, 700M shape x 64 streams, running set T=128, bf16 in/out",
+    res.append({"workload": "block step, 700M shape x 64 streams, running set T=128, bf16 in/out, "
+                            "cached state in operand form",
                 "avg_us": round(us, 3), "active_tokens_per_s": round(b * T / (us * 1e-6), 1),
                 "roofline": make_roofline("hbm", nb, us, traffic_for("block_step_c4")),
-                "alg_bytes": nb})
-    del h, f, r, y
+                "alg_bytes": nb, "from_fp32_state_us": round(tm.avg_us("f32"), 3),
+                "state_ops_us": round(tm.avg_us("ops"), 3)})
+    del h, ops, f, r, y
     # 350M prefix: 65,536 tokens, chunk 256, bf16 y + fp32 chunk states
     c2 = configs.get(2)
     b, H, P, N, G, L, Q = c2.batch, c2.nheads, c2.headdim, c2.d_state, c2.ngroups, c2.prefix_len, c2.chunk

@@ -7,7 +7,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libbdssm.so")
-SOURCES = ["api.hip", "scan_valu.hip", "block_step_mfma.hip", "block_step_lat.hip", "prefix_mfma.hip", "graph.hip", "conv.hip"]
+SOURCES = ["api.hip", "scan_valu.hip", "block_step_mfma.hip", "block_step_lat.hip", "block_step_bw.hip", "prefix_mfma.hip", "graph.hip", "conv.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -521,12 +521,18 @@ bdssm_status bdssm_block_step_ops(const bdssm_dims *dims, int32_t block_len, con
         return rc;
     if (a.s.b == 0 || block_len == 0)
         return BDSSM_OK;
-    if (!block_lat_supported(a.s, block_len))
-        return BDSSM_ERR_UNSUPPORTED;
     a.h_ops = h_ops;
     a.h_prefix = nullptr;
-    const char *e = getenv("BDSSM_BLOCK_LAT_WPG");
-    return launched(launch_block_step_lat(a, e ? atoi(e) : 0, static_cast<hipStream_t>(stream)));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (use_block_lat(a.s, block_len)) {
+        const char *e = getenv("BDSSM_BLOCK_LAT_WPG");
+        return launched(launch_block_step_lat(a, e ? atoi(e) : 0, st));
+    }
+    if (!block_bw_supported(a.s, block_len))
+        return BDSSM_ERR_UNSUPPORTED;
+    int hpw = block_bw_plan(a.s), ps = 1;
+    override_block_plan(a.s, &hpw, &ps);
+    return launched(launch_block_step_bw(a, hpw, st));
 }
 
 bdssm_status bdssm_commit(const bdssm_dims *dims, int32_t block_len, const bdssm_seq *clean,

@@ -95,6 +95,10 @@ void block_mfma_plan(const Shape &s, int *hpw, int *ps);
 hipError_t launch_block_step_mfma(const BlockArgs &a, int hpw, int ps, hipStream_t st);
 bool block_lat_supported(const Shape &s, int T);
 hipError_t launch_block_step_lat(const BlockArgs &a, int wpg, hipStream_t st);  // wpg 2, 4 or 0 (chosen)
+// many (stream, head) pairs, state in operand form (a.h_ops): hpw heads per workgroup
+bool block_bw_supported(const Shape &s, int T);
+int block_bw_plan(const Shape &s);
+hipError_t launch_block_step_bw(const BlockArgs &a, int hpw, hipStream_t st);
 // Operand form of nbh cached states [nbh][N][P] float32 (N = 128, P = 64): the bf16 pair
 // hi = bf16(S), lo = bf16(S - hi) as [nbh][2][N/8][P][8]
 hipError_t launch_state_ops(const float *h, void *ops, int64_t nbh, hipStream_t st);

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define BDSSM_ABI_VERSION 2
+#define BDSSM_ABI_VERSION 3
 
 typedef enum {
     BDSSM_OK = 0,
@@ -186,11 +186,13 @@ bdssm_status bdssm_state_ops(const bdssm_dims *dims, const float *h, void *ops, 
 
 /*
  * Block step from the cached state in operand form: bdssm_block_step_ex with the state
- * given as h_ops, made by bdssm_state_ops from h_prefix. Its y is bitwise that of
- * bdssm_block_step_ex on h_prefix wherever the latter runs its small-batch kernel (bf16
- * inputs, d_state 128, headdim 64, block_len <= 32, batch * nheads < 512), and this call
- * always runs that kernel. Errors as bdssm_block_step_ex, with BDSSM_ERR_UNSUPPORTED for
- * other dtypes, shapes or block_len > 32; y must not overlap h_ops.
+ * given as h_ops, made by bdssm_state_ops from h_prefix. For block_len <= 32 and
+ * batch * nheads < 512 it runs the small-batch kernel of bdssm_block_step_ex and its y is
+ * bitwise that call's on h_prefix; otherwise (block_len <= 128) a kernel that copies the
+ * operand-form state and x straight into LDS, whose y agrees with bdssm_block_step_ex up to
+ * rounding (the same bounds against the exact result). Errors as bdssm_block_step_ex, with
+ * BDSSM_ERR_UNSUPPORTED for inputs other than bf16, (d_state, headdim) other than
+ * (128, 64), or block_len > 128; y must not overlap h_ops.
  */
 bdssm_status bdssm_block_step_ops(const bdssm_dims *dims, int32_t block_len, const void *h_ops,
                                   const bdssm_seq *fwd, const bdssm_seq *rev, const float *A,

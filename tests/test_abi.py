@@ -24,7 +24,7 @@ def test_library_exports_every_declared_symbol():
     assert syms == sorted(bdssm.EXPORTS)
     for s in syms:
         assert hasattr(lib, s), s
-    assert bdssm.abi_version() == 2
+    assert bdssm.abi_version() == 3
     for st in range(8):
         assert bdssm.status_str(st).startswith("BDSSM_")
     assert "unknown" in bdssm.status_str(99)
@@ -266,7 +266,7 @@ def test_state_ops_argument_checks():
     assert step(h_ops=None) == bdssm.ERR_NULL
     assert step(A_rev=None) == bdssm.ERR_NULL
     assert step(y=ops + 1024) == bdssm.ERR_ALIAS                       # y on top of the state
-    assert step(T=33) == bdssm.ERR_UNSUPPORTED                         # longer than the kernel's blocks
+    assert step(T=129) == bdssm.ERR_UNSUPPORTED                        # longer than the kernels' blocks
     assert step(dd=bdssm.dims(2, 4, 64, 128, 1, bdssm.F32)) == bdssm.ERR_UNSUPPORTED   # fp32 inputs
     assert step(T=-1) == bdssm.ERR_SHAPE
     assert step(T=0) == bdssm.OK                                       # nothing to do

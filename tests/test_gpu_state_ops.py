@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 from bidirectional_mamba_state_amd import bdssm, configs, inputs
-from harness import TOL_BF16, f32_round, rel, within
+from harness import TOL_BF16, f32_round, max_head_rel, rel, within
 
 pytestmark = pytest.mark.gpu
 
@@ -138,3 +138,86 @@ def test_decode_graph_with_state_ops():
             assert torch.equal(ops_g, ops_e), replay
     finally:
         g.close()
+
+
+@pytest.mark.parametrize("b,H,G,T,lat_off,hpws", [
+    (12, 48, 1, 128, False, (1, 2, 3, 6)),   # 576 (stream, head) pairs: the bandwidth kernel
+    (2, 12, 2, 77, False, (1, 2, 3, 6)),     # T > 32: 8 row blocks, ragged
+    (3, 8, 2, 40, False, (1, 2, 4)),         # 4 row blocks, ragged
+    (16, 32, 1, 32, False, (1, 2, 4)),       # 512 pairs, T = 32: 2 row blocks
+    (2, 16, 4, 5, True, (1, 2)),             # 2 row blocks, mostly past T
+])
+def test_block_step_ops_bandwidth_kernel(monkeypatch, b, H, G, T, lat_off, hpws):
+    """bdssm_block_step_ops where it runs the kernel that copies the operand-form state and x
+    into LDS: y matches the oracle for float32 and bf16 y, with and without separate reverse
+    parameters, also with D = 0 (the scan terms alone), and does not depend on how many
+    heads a workgroup walks (bitwise)."""
+    import torch
+    fwd, rev, A, D, Ar, Dr, h = _case_inputs(b, H, G, T, 2000 + 7 * H + T)
+    tf, tr = bdssm.seq_to_device(fwd), bdssm.seq_to_device(rev)
+    Ad, Dd, Ard, Drd = (torch.from_numpy(v).cuda() for v in (A, D, Ar, Dr))
+    Dz = torch.zeros_like(Dd)
+    hd = torch.from_numpy(h.astype(np.float32)).cuda()
+    d32 = bdssm.dims(b, H, 64, 128, G, bdssm.BF16, bdssm.F32)
+    ops = torch.empty(bdssm.state_ops_bytes(d32), dtype=torch.uint8, device="cuda")
+    bdssm.state_ops(d32, hd, ops)
+    if lat_off:
+        monkeypatch.setenv("BDSSM_BLOCK_LAT", "0")
+    want = {
+        (False, False): oracle.block_step(h, fwd, rev, A, D)[0],
+        (False, True): oracle.block_step(h, fwd, rev, A, np.zeros_like(D))[0],
+        (True, False): oracle.block_step(h, fwd, rev, A, D, A_rev=Ar, D_rev=Dr)[0],
+    }
+    for y_dt, tdt in ((bdssm.F32, torch.float32), (bdssm.BF16, torch.bfloat16)):
+        d = bdssm.dims(b, H, 64, 128, G, bdssm.BF16, y_dt)
+        for sep, dz in ((False, False), (False, True), (True, False)):
+            first = None
+            for hpw in hpws:
+                monkeypatch.setenv("BDSSM_BLOCK_HPW", str(hpw))
+                print(f"[case] block step ops (bandwidth) b={b} H={H} G={G} T={T} hpw={hpw} y={y_dt} "
+                      f"separate={sep} D=0:{dz}", flush=True)
+                y = torch.full((b, T, H, 64), float("nan"), dtype=tdt, device="cuda")
+                A_rev, D_rev = (Ard, Drd) if sep else (Ad, None)
+                bdssm.block_step_ops(d, T, ops, tf, tr, Ad, Dz if dz else Dd, y, A_rev=A_rev, D_rev=D_rev)
+                torch.cuda.synchronize()
+                if first is None:
+                    first = y.clone()
+                    assert within(rel(y.float().cpu().numpy(), want[(sep, dz)]), TOL_BF16,
+                                  f"block step ops (bandwidth), y={y_dt}, separate={sep}, D=0:{dz}")
+                else:
+                    assert torch.equal(y, first), f"heads per workgroup {hpw} changed y"
+    assert torch.equal(hd.cpu(), torch.from_numpy(h.astype(np.float32)))  # the state is read only
+
+
+def test_config4_ops_running_set():
+    """64 streams x 48 heads, T = 128, in the launch configuration the benchmark times: the
+    operand form of cached states from a 1024-token prefix per stream, one block step from
+    it; oracle on streams {0, 31, 63} (y with and without D x)."""
+    import torch
+    from harness import gpu_prefix, streams_of
+    cfg = configs.get(4)
+    A, D = inputs.params(cfg)
+    b, H, P, N, G, T = cfg.batch, cfg.nheads, cfg.headdim, cfg.d_state, cfg.ngroups, cfg.block_len
+    pre = inputs.prefix(cfg, length=1024)
+    print("[case] c4 prefix for the cached states", flush=True)
+    _, _, h = gpu_prefix(pre, A, D, cfg.chunk, want_y=False, want_cs=False)
+    fwd = inputs.block(cfg, 0, 0, inputs.FWD)
+    rev = inputs.block(cfg, 0, 0, inputs.REV)
+    tf, tr = bdssm.seq_to_device(fwd), bdssm.seq_to_device(rev)
+    hd = torch.from_numpy(np.asarray(h, np.float32)).cuda()
+    d = bdssm.dims(b, H, P, N, G, cfg.in_dtype, bdssm.BF16)
+    ops = torch.empty(bdssm.state_ops_bytes(d), dtype=torch.uint8, device="cuda")
+    bdssm.state_ops(d, hd, ops)
+    Ad = torch.from_numpy(A).cuda()
+    sample = [0, 31, 63]
+    hs = np.asarray(h, np.float64)[sample]
+    fs, rs = streams_of(fwd, sample), streams_of(rev, sample)
+    for Dv, label in ((D, "y"), (np.zeros_like(D), "y - D x")):
+        print(f"[case] c4 block step ops, {label}", flush=True)
+        y = torch.empty((b, T, H, P), dtype=torch.bfloat16, device="cuda")
+        bdssm.block_step_ops(d, T, ops, tf, tr, Ad, torch.from_numpy(Dv).cuda(), y)
+        torch.cuda.synchronize()
+        yo, _, _ = oracle.block_step(hs, fs, rs, A, Dv)
+        yg = y.float().cpu().numpy()[sample]
+        assert within(rel(yg, yo), TOL_BF16, f"c4 block step ops, {label} (sampled streams)")
+        assert within(max_head_rel(yg, yo, 2), 4 * TOL_BF16, f"c4 block step ops, {label}, worst head")
