@@ -151,7 +151,6 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
     const int pblk = WPG * ph + w;
     const int lane = threadIdx.x & 63, q = lane >> 4, r16 = lane & 15;
     const int t = tb * 16 + r16;  // this lane's row as an A operand
-    const int p = pblk * 16 + r16;
 
     // range-checked buffers over this stream's T tokens: rows past T read as zero
     const int64_t tok0 = static_cast<int64_t>(b) * T;

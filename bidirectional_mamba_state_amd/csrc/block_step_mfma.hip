@@ -135,7 +135,7 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
     using Gm = Geo<NB, PS>;
     constexpr int TP = Gm::TP, PW = Gm::PW, PBW = Gm::PBW, PGRP = Gm::PGRP, THREADS = Gm::THREADS,
                   HS = Gm::HS, XS = Gm::XS, YW = Gm::YW, SITEMS = Gm::SITEMS,
-                  XITEMS = Gm::XITEMS, SPT = Gm::SPT, XPT = Gm::XPT, UNITS = Gm::UNITS;
+                  XITEMS = Gm::XITEMS, SPT = Gm::SPT, XPT = Gm::XPT;
     // two buffers: the next head is staged while the current one is being computed
     __shared__ __attribute__((aligned(16))) __bf16 hT_hi[2][PW * HS];
     __shared__ __attribute__((aligned(16))) __bf16 hT_lo[2][PW * HS];
