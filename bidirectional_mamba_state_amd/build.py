@@ -13,6 +13,7 @@ ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Wall", "-Wno-unused-command-line-argument",
+    "-Wl,--no-undefined",  # a missing symbol (e.g. a kernel's launch stub) fails the build
     # packed float32 vector instructions stay off: the compiler must not form them
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),

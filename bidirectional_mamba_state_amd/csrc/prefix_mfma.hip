@@ -32,6 +32,7 @@
 
 #include "internal.h"
 #include "mfma_tiles.h"
+#include "wave_ops.h"
 
 namespace bdssm {
 namespace {
@@ -788,13 +789,416 @@ __global__ __launch_bounds__(256, 2) void k_state(ScanArgs a)
     }
 }
 
+// ---- FULL pass with outputs, one head per workgroup, inputs copied straight into LDS
+//
+// The same computation as k_scan<true, true, 1> (and bitwise the same state walk as
+// k_state), with B, C and x copied into LDS by buffer loads to LDS in whole lines instead of
+// through registers: B and x of sub-chunk k+1 are copied at the start of sub-chunk k into
+// the other of two buffers; C, read only before the mid-sub-chunk barrier, has one buffer
+// and its next copy is issued right after that barrier. 71.5 KB of LDS: two workgroups per
+// CU. B and C rows (256 bytes) hold piece c of row r at slot c ^ swz(r), which keeps three
+// read patterns free of bank conflicts: 16-byte operand reads of 16 consecutive rows (score
+// tiles), transposing reads of 4 rows x 16 columns per 16 lanes (B in the state update) and
+// 8-byte reads of the permuted contraction order (C in the state product); x rows
+// (128 bytes) hold piece c of row t at slot c ^ 2 (t % 4), as in k_state.
+__device__ __forceinline__ int swz(int r)
+{
+    return ((r & 3) << 2) | ((r & 4) >> 1) | ((r >> 3) & 1);
+}
+
+// (the body is a device function template with one kernel per output type: a kernel
+// template built from generic lambdas loses its host-side launch stub in this compiler)
+template <typename Ty>
+__device__ __forceinline__ void full_pass(const ScanArgs &a)
+{
+    __shared__ __attribute__((aligned(16))) __bf16 sB0[SC * kN];
+    __shared__ __attribute__((aligned(16))) __bf16 sB1[SC * kN];
+    __shared__ __attribute__((aligned(16))) __bf16 sC[SC * kN];
+    __shared__ __attribute__((aligned(16))) __bf16 sX0[SC * kP];
+    __shared__ __attribute__((aligned(16))) __bf16 sX1[SC * kP];
+    __shared__ __attribute__((aligned(16))) float sT[2][NTAB][SC];  // decay tables by parity
+    __shared__ float sTot[2];
+    // the decay-weighted causal score tiles M (row block tb, column block sb <= tb: tile
+    // tb (tb + 1) / 2 + sb), each as the 64 lanes' accumulator values in lane order
+    __shared__ __attribute__((aligned(16))) __bf16 sM[10][256];
+    auto bufB = [&](auto ph) -> __bf16 * {
+        if constexpr (decltype(ph)::value == 0)
+            return sB0;
+        else
+            return sB1;
+    };
+    auto bufX = [&](auto ph) -> __bf16 * {
+        if constexpr (decltype(ph)::value == 0)
+            return sX0;
+        else
+            return sX1;
+    };
+
+    // workgroups of one segment (all heads of a stream) go to the same XCD
+    const int nwg = gridDim.x;
+    int lid = blockIdx.x;
+    if ((nwg & 7) == 0)
+        lid = (lid & 7) * (nwg >> 3) + (lid >> 3);
+    const int H = a.s.H, G = a.s.G;
+    const int h0 = lid % H;
+    const int sg = (lid / H) % a.nseg;
+    const int b = lid / (H * a.nseg);
+    const int g = h0 / (H / G);
+    const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    const int64_t len = a.len;
+    const int64_t seg_t0 = static_cast<int64_t>(sg) * a.seg_sub * SC;
+    const int nsub = static_cast<int>(min<int64_t>(a.seg_sub, (len - seg_t0 + SC - 1) / SC));
+    const int64_t nsub_all = (len + SC - 1) / SC;
+    const int rowBC = G * kN, rowX = H * kP;
+    const int64_t tok0 = static_cast<int64_t>(b) * len;
+    const int64_t NP = static_cast<int64_t>(kN) * kP;
+    const __bf16 *Bg = static_cast<const __bf16 *>(a.in.B) + tok0 * rowBC + g * kN;
+    const __bf16 *Cg = static_cast<const __bf16 *>(a.in.C) + tok0 * rowBC + g * kN;
+    const __bf16 *xg = static_cast<const __bf16 *>(a.in.x) + tok0 * rowX + h0 * kP;
+    const __bf16 *dtg = static_cast<const __bf16 *>(a.in.dt) + tok0 * H + h0;
+    const float Ah = a.A[h0], Dh = a.D[h0];
+    const auto mk = [](const void *base, int64_t bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), 0x00020000);
+    };
+    // rows of sub-chunk k of the segment; 0 past the segment (its copies then move nothing)
+    auto rows_of = [&](int k) {
+        const int64_t t0 = seg_t0 + static_cast<int64_t>(k) * SC;
+        return k < nsub ? static_cast<int>(min<int64_t>(SC, len - t0)) : 0;
+    };
+
+    // ---- copies of sub-chunk k (range-checked buffers based at its first token: rows past
+    // the stream's end read as zero or land nothing). B, C: 16 pieces of 4 rows, wavefront w
+    // takes w + 4u; x: 8 pieces of 8 rows, w + 4u.
+    auto copy_rows = [&](const __bf16 *base, __bf16 *dst, int k) {
+        const int64_t t0 = seg_t0 + static_cast<int64_t>(k) * SC;
+        const int nrows = rows_of(k);
+        const auto r = mk(base + t0 * rowBC, nrows > 0 ? ((nrows - 1) * rowBC + kN) * 2 : 0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int pc = wave + 4 * u, row = 4 * pc + (lane >> 4), c = (lane & 15) ^ swz(row);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(dst + 4 * pc * kN),
+                                                     16, (row * rowBC + 8 * c) * 2, 0, 0, 0);
+        }
+    };
+    auto copy_x = [&](__bf16 *dst, int k) {
+        const int64_t t0 = seg_t0 + static_cast<int64_t>(k) * SC;
+        const int nrows = rows_of(k);
+        const auto r = mk(xg + t0 * rowX, nrows > 0 ? ((nrows - 1) * rowX + kP) * 2 : 0);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int px = wave + 4 * u, row = 8 * px + (lane >> 3), c = (lane & 7) ^ (2 * (row & 3));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(dst + 8 * px * kP),
+                                                     16, (row * rowX + 8 * c) * 2, 0, 0, 0);
+        }
+    };
+    // dt of sub-chunk k, token `lane` (zero past the end)
+    auto load_dt = [&](int k) {
+        const int64_t t0 = seg_t0 + static_cast<int64_t>(k) * SC;
+        const int nrows = rows_of(k);
+        const auto r = mk(dtg + t0 * H, nrows > 0 ? ((nrows - 1) * H + 1) * 2 : 0);
+        return __builtin_amdgcn_raw_buffer_load_b16(r, lane * H * 2, 0, 0);
+    };
+    // cumulative log2-decays of a sub-chunk from its dt, into table buffer PH
+    auto tables = [&](auto PH, unsigned short dbits) {
+        const float d = __uint_as_float(static_cast<uint32_t>(dbits) << 16);
+        const float inc = wave_inclusive_sum(d * Ah);
+        const float c = inc * kLog2e;
+        const float c31 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 31));
+        const float clast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 63));
+        const float ref = lane < 32 ? c31 : clast;  // end of this token's 32-token pair
+        float(*tb)[SC] = sT[decltype(PH)::value];
+        tb[TAB_C][lane] = c;
+        tb[TAB_EF][lane] = __builtin_amdgcn_exp2f(c);
+        tb[TAB_LG][lane] = __builtin_amdgcn_logf(d) - c;
+        tb[TAB_COL][lane] = __builtin_amdgcn_exp2f(ref - c) * d;
+        tb[TAB_W][lane] = __builtin_amdgcn_exp2f(clast - c) * d;
+        sTot[decltype(PH)::value] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inc), 63));
+    };
+
+    // ---- operand reads
+    // B or C rows 16 blk + r16, contraction n = 32 m + 8 q .. +7 (score tiles)
+    auto row_frag = [&](const __bf16 *T, int blk, int m) {
+        const int row = 16 * blk + r16;
+        return *reinterpret_cast<const bf16x8 *>(T + row * kN + 8 * ((4 * m + q) ^ swz(row)));
+    };
+    // C rows 16 tb + r16, contraction n = 32 m + 4 q + e and 32 m + 16 + 4 q + e (state product)
+    auto c_frag = [&](int tb, int m) {
+        const int row = 16 * tb + r16, sw = swz(row);
+        const __bf16 *p = sC + row * kN + 4 * (q & 1);
+        return cat(*reinterpret_cast<const bf16x4 *>(p + 8 * ((4 * m + (q >> 1)) ^ sw)),
+                   *reinterpret_cast<const bf16x4 *>(p + 8 * ((4 * m + 2 + (q >> 1)) ^ sw)));
+    };
+    // B^T: lane (r16, q) gets B[32 ks + 4 q + e][16 i + r16] and B[32 ks + 16 + 4 q + e][..]
+    auto bt_frag = [&](const __bf16 *T, int ks, int i) {
+        const int tr = 32 * ks + 4 * q + (r16 >> 2), col = 16 * i + 4 * (r16 & 3);
+        const __bf16 *p = T + tr * kN + 8 * ((col >> 3) ^ swz(tr)) + (col & 7);
+        const __bf16 *p16 = T + (tr + 16) * kN + 8 * ((col >> 3) ^ swz(tr + 16)) + (col & 7);
+        return cat(tr_read(p), tr_read(p16));
+    };
+    // x~: lane (r16, q) gets x[32 m + 4 q + e][p0 + r16] and x[32 m + 16 + 4 q + e][..]
+    auto x_frag = [&](const __bf16 *X, int m, int p0) {
+        const int tr = 32 * m + 4 * q + (r16 >> 2), col = p0 + 4 * (r16 & 3), sw = 2 * (tr & 3);
+        const __bf16 *p = X + tr * kP + 8 * ((col >> 3) ^ sw) + (col & 7);
+        return cat(tr_read(p), tr_read(p + 16 * kP));
+    };
+
+    f32x4 hs[8];  // hs[i] holds h[16 i + 4 q + j][p0 + r16]
+    auto store_state = [&](float *base, int p0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                base[(16 * i + 4 * q + j) * kP + p0 + r16] = hs[i][j];
+    };
+    auto emit_chunk_state = [&](int k, int p0) {  // state after sub-chunk k, at chunk ends and the end
+        const int64_t gsub = seg_t0 / SC + k;
+        if ((gsub + 1) % a.chunk_sub == 0 || gsub == nsub_all - 1) {
+            const int64_t c = gsub / a.chunk_sub;
+            store_state(a.chunk_states + ((static_cast<int64_t>(b) * a.nch + c) * H + h0) * NP, p0);
+        }
+    };
+
+    // wavefront W owns state columns 16 W .. 16 W + 15 and score tiles W, W + 4, W + 8;
+    // wavefront 0 builds the decay tables. Everything below is specialized per wavefront.
+    auto body = [&](auto Wc) {
+        constexpr int W = decltype(Wc)::value;
+        constexpr int p0 = 16 * W;
+
+        // one sub-chunk k, in buffers PH = k % 2
+        auto step = [&](auto PH, int k) {
+            constexpr int ph = decltype(PH)::value;
+            using PN = std::integral_constant<int, 1 - ph>;
+            const int64_t t0 = seg_t0 + static_cast<int64_t>(k) * SC;
+            const int nvalid = rows_of(k);
+            // (A) the copies of k have landed (only the four y stores of k-1 may still be in
+            // flight) and its tables are written
+            workgroup_lds_barrier<4>();
+            if (a.chunk_states && k > 0)
+                emit_chunk_state(k - 1, p0);
+            bf16x8 xf[2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+                xf[m] = x_frag(bufX(PH), m, p0);
+            __builtin_amdgcn_sched_barrier(0);
+            unsigned short dn = 0;
+            if constexpr (W == 0)
+                dn = load_dt(k + 1);
+            copy_rows(Bg, bufB(PN{}), k + 1);
+            copy_x(bufX(PN{}), k + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            const __amdgpu_buffer_rsrc_t yr =
+                mk(static_cast<Ty *>(a.y) + (tok0 + t0) * rowX, static_cast<int64_t>(nvalid) * rowX * sizeof(Ty));
+            const float(*tbl)[SC] = sT[ph];
+            // (1) this wavefront's score tiles S[tb][sb] = B_s . C_t, decay-weighted (factored
+            // below the diagonal 32-token pair, per element on it), stored for all
+#pragma unroll
+            for (int rr = 0; rr < 3; ++rr) {
+                const int tau = W + 4 * rr;
+                if (tau < 10) {
+                    const int tb = tau >= 6 ? 3 : tau >= 3 ? 2 : tau >= 1 ? 1 : 0;
+                    const int sb = tau - tb * (tb + 1) / 2;
+                    f32x4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+                        S = mfma(row_frag(bufB(PH), sb, m), row_frag(sC, tb, m), S);
+                    // lane (t, q) holds S[s = 16 sb + 4q + j][t]
+                    const int t = 16 * tb + r16, mp = sb >> 1, s0 = 16 * sb + 4 * q;
+                    const float ct = tbl[TAB_C][t];
+                    float mv[4];
+                    if (mp < (tb >> 1)) {  // pair wholly below the row block
+                        const float rowf = __builtin_amdgcn_exp2f(ct - tbl[TAB_C][32 * mp + 31]);
+                        const float4 cw = *reinterpret_cast<const float4 *>(&tbl[TAB_COL][s0]);
+                        mv[0] = S[0] * cw.x * rowf;
+                        mv[1] = S[1] * cw.y * rowf;
+                        mv[2] = S[2] * cw.z * rowf;
+                        mv[3] = S[3] * cw.w * rowf;
+                    } else {  // the pair holding the row block: masked to s <= t
+                        const float4 lg = *reinterpret_cast<const float4 *>(&tbl[TAB_LG][s0]);
+                        const float l4[4] = {lg.x, lg.y, lg.z, lg.w};
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            mv[j] = s0 + j <= t ? S[j] * __builtin_amdgcn_exp2f(ct + l4[j]) : 0.f;
+                    }
+                    bf16x4 mb;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        mb[j] = static_cast<__bf16>(mv[j]);
+                    *reinterpret_cast<bf16x4 *>(&sM[tau][4 * lane]) = mb;
+                }
+            }
+            // (2) the state entering the sub-chunk: y^T[p][t] = sum_n h[n][p] C[t][n], the
+            // state accumulators split into bf16 hi + lo as the A operand
+            f32x4 acc[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+                acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                bf16x8 hfh, hfl;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float v = hs[2 * m + (e >> 2)][e & 3];
+                    hfh[e] = static_cast<__bf16>(v);
+                    hfl[e] = static_cast<__bf16>(v - bf2f(hfh[e]));
+                }
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    const bf16x8 cf = c_frag(tb, m);
+                    acc[tb] = mfma(hfh, cf, acc[tb]);
+                    acc[tb] = mfma(hfl, cf, acc[tb]);
+                }
+            }
+            workgroup_lds_barrier<63>();  // (A2) the weighted tiles are stored; C is free
+            copy_rows(Cg, sC, k + 1);
+            // the copies stay ahead of the y stores: barrier (A) counts on exactly four
+            // operations after them
+            __builtin_amdgcn_sched_barrier(0);
+            // (3) + sum_{s<=t} M[t][s] x_s per 32-token pair, + D x_t; the lane holds
+            // y[t][p0 + 4q .. p0 + 4q + 3]
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                const int t = 16 * tb + r16, md = tb >> 1;
+                acc[tb] *= tbl[TAB_EF][t];
+#pragma unroll
+                for (int m = 0; m <= md; ++m) {
+                    const int lo = tb * (tb + 1) / 2 + 2 * m;  // tile (tb, 2m); (tb, 2m+1) follows
+                    const bf16x4 m0 = *reinterpret_cast<const bf16x4 *>(&sM[lo][4 * lane]);
+                    const bf16x4 m1 =
+                        2 * m + 1 <= tb ? *reinterpret_cast<const bf16x4 *>(&sM[lo + 1][4 * lane]) : bf16x4{};
+                    acc[tb] = mfma(xf[m], cat(m0, m1), acc[tb]);
+                }
+                const int pc = p0 + 4 * q;
+                const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(
+                    bufX(PH) + t * kP + 8 * ((pc >> 3) ^ (2 * (t & 3))) + (pc & 7));
+                float o[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    o[j] = fmaf(Dh, bf2f(xv[j]), acc[tb][j]);
+                const int off = ((t * H + h0) * kP + pc) * static_cast<int>(sizeof(Ty));
+                if constexpr (sizeof(Ty) == 2) {
+                    bf16x4 ov;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        ov[j] = static_cast<__bf16>(o[j]);
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2i32, ov), yr, off, 0, 0);
+                } else {
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        v4i32{__float_as_int(o[0]), __float_as_int(o[1]), __float_as_int(o[2]), __float_as_int(o[3])},
+                        yr, off, 0, 0);
+                }
+            }
+            // (4) state: h <- exp(c_63) h + B^T (w o x), w_s = exp(c_63 - c_s) dt_s (the same
+            // arithmetic as k_state, so that the walk is bitwise the state-only pass's)
+            {
+                const float tot = sTot[ph];
+                const float alpha = __expf(tot);
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    hs[i] *= alpha;
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                bf16x8 bt[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    bt[i] = bt_frag(bufB(PH), ks, i);
+                const float4 w0 = *reinterpret_cast<const float4 *>(&tbl[TAB_W][32 * ks + 4 * q]);
+                const float4 w1 = *reinterpret_cast<const float4 *>(&tbl[TAB_W][32 * ks + 16 + 4 * q]);
+                const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+                float xw[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    xw[e] = bf2f(xf[ks][e]) * wv[e];
+                bf16x8 xhi, xlo;
+                split8(xw, xhi, xlo);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    hs[i] = mfma(bt[i], xhi, hs[i]);
+                    hs[i] = mfma(bt[i], xlo, hs[i]);
+                }
+            }
+            workgroup_lds_barrier<63>();  // (B) every LDS read for sub-chunk k is done
+            if constexpr (W == 0)
+                tables(PN{}, dn);  // sub-chunk k+1, into the table buffer k-1 has left
+        };
+
+        // ---- prologue: clear the staging buffers when the stream ends inside a sub-chunk
+        // (rows past its end must hold finite values: they are weighted 0), put sub-chunk 0
+        // in flight, load the entering state, build the tables of 0, let everything land
+        if (len % SC != 0) {
+            const uint4 z = make_uint4(0, 0, 0, 0);
+            for (int i = tid; i < SC * kN / 8; i += 256) {
+                *reinterpret_cast<uint4 *>(sB0 + 8 * i) = z;
+                *reinterpret_cast<uint4 *>(sB1 + 8 * i) = z;
+                *reinterpret_cast<uint4 *>(sC + 8 * i) = z;
+            }
+            for (int i = tid; i < SC * kP / 8; i += 256) {
+                *reinterpret_cast<uint4 *>(sX0 + 8 * i) = z;
+                *reinterpret_cast<uint4 *>(sX1 + 8 * i) = z;
+            }
+            workgroup_lds_barrier<63>();
+        }
+        unsigned short d0 = 0;
+        if constexpr (W == 0)
+            d0 = load_dt(0);
+        copy_rows(Bg, sB0, 0);
+        copy_rows(Cg, sC, 0);
+        copy_x(sX0, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            hs[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (a.h_in) {
+            const float *hin = a.h_in + ((static_cast<int64_t>(b) * a.nseg + sg) * H + h0) * NP;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    hs[i][j] = hin[(16 * i + 4 * q + j) * kP + p0 + r16];
+        }
+        if constexpr (W == 0)
+            tables(std::integral_constant<int, 0>{}, d0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        int k = 0;
+        for (; k + 2 <= nsub; k += 2) {  // pairs of sub-chunks: a body with no branch
+            step(std::integral_constant<int, 0>{}, k);
+            step(std::integral_constant<int, 1>{}, k + 1);
+        }
+        if (k < nsub)
+            step(std::integral_constant<int, 0>{}, k);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // no copy outlives the workgroup
+        if (a.chunk_states)
+            emit_chunk_state(nsub - 1, p0);
+        if (a.h_last && sg == a.nseg - 1)
+            store_state(a.h_last + (static_cast<int64_t>(b) * H + h0) * NP, p0);
+    };
+    switch (wave) {
+    case 0: body(std::integral_constant<int, 0>{}); break;
+    case 1: body(std::integral_constant<int, 1>{}); break;
+    case 2: body(std::integral_constant<int, 2>{}); break;
+    default: body(std::integral_constant<int, 3>{}); break;
+    }
+}
+
+__global__ __launch_bounds__(256, 2) void k_full_bf16(ScanArgs a) { full_pass<__bf16>(a); }
+__global__ __launch_bounds__(256, 2) void k_full_f32(ScanArgs a) { full_pass<float>(a); }
+
 template <bool FULL, int HPW, typename Ty>
 hipError_t launch_scan(const ScanArgs &a, hipStream_t st)
 {
     const int nwg = a.s.b * a.nseg * (a.s.H / HPW);
     if constexpr (FULL) {
         if (a.y) {
-            k_scan<true, true, HPW, Ty><<<dim3(nwg), dim3(256), 0, st>>>(a);
+            static const bool regs = getenv("BDSSM_PREFIX_REG_STAGING") != nullptr;  // the register-staged kernel
+            if (HPW == 1 && !regs) {
+                if constexpr (sizeof(Ty) == 2)
+                    k_full_bf16<<<dim3(nwg), dim3(256), 0, st>>>(a);
+                else
+                    k_full_f32<<<dim3(nwg), dim3(256), 0, st>>>(a);
+            } else {
+                k_scan<true, true, HPW, Ty><<<dim3(nwg), dim3(256), 0, st>>>(a);
+            }
             return hipGetLastError();
         }
     }
