@@ -14,17 +14,20 @@
 // consecutive columns of one token. The causal C B^T score tiles and their decay weights do
 // not depend on the columns: the four wavefronts compute a share each and exchange the
 // weighted tiles M through LDS.
-// B, C and x are staged in LDS in the fragment-major order of mfma_tiles.h (an operand
-// fragment is one contiguous 512-byte read per wavefront); operands whose contraction runs
-// over tokens are read from the same tiles with the gfx950 transposing LDS load
-// (ds_read_b64_tr_b16), which that order keeps free of bank conflicts.
+// Operands whose contraction runs over tokens are read with the gfx950 transposing LDS load
+// (ds_read_b64_tr_b16) from tiles laid out to keep those reads free of bank conflicts.
 //
-// Two modes:
+// Passes:
 //   STATE  from h_init (or zero): only the state recurrence; writes the segment's end
 //          state and its total log-decay (used by the segment scan, or as h_out).
-//   FULL   from the state entering the segment: also y, the chunk states (the state after
-//          every chunk of Q tokens, and after the last token) and, for the stream's last
-//          segment, the final state.
+//          k_state (one head per workgroup, inputs copied straight into LDS) or k_scan<false,
+//          2> (two heads per workgroup, inputs staged through registers).
+//   FULL   from the state entering the segment: also y (k_full_*, inputs copied straight
+//          into LDS), or only the chunk states (k_scan<true, 1>): the state after every
+//          chunk of Q tokens and after the last token, and, for the stream's last segment,
+//          the final state.
+// k_scan stages B and x through registers into the fragment-major order of mfma_tiles.h
+// (an operand fragment is one contiguous 512-byte read per wavefront).
 // The fp32 states and the weighted x~ operand are split into bf16 hi + lo parts, so that
 // products against them keep ~16 significant bits; B, C and x are exact in bf16.
 #include <algorithm>
@@ -82,24 +85,19 @@ struct ScanArgs {
     float *chunk_states; // FULL: [b][nch][H][N][P], or NULL
 };
 
-template <bool FULL, int HPW>
+template <int HPW>
 struct Lds {
     __bf16 B[SC * kN];
-    __bf16 C[FULL ? SC * kN : 8];
     __bf16 X[HPW][SC * kP];
     float tab[2][HPW][NTAB][SC];  // decay tables of sub-chunks k and k+1 (by parity)
     float tot[2][HPW];
-    // FULL: the decay-weighted causal score tiles M[t][s] of the sub-chunk (row block tb,
-    // column block sb <= tb; tile tb(tb+1)/2 + sb), each stored as the 64 lanes' accumulator
-    // values in lane order, so that a reader lane fetches the 8 bytes it needs contiguously
-    __bf16 Mt[FULL ? 10 : 1][256];
 };
 
 
-template <bool FULL, bool WITHY, int HPW, typename Ty>
+template <bool FULL, int HPW>
 __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
 {
-    __shared__ __attribute__((aligned(16))) Lds<FULL, HPW> L;
+    __shared__ __attribute__((aligned(16))) Lds<HPW> L;
 
     // workgroups of one segment (all heads of a stream) go to the same XCD
     const int nwg = gridDim.x;
@@ -121,16 +119,11 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
     const int rowBC = G * kN, rowX = H * kP;
     const int64_t tok0 = static_cast<int64_t>(b) * len;
     const __bf16 *Bg = static_cast<const __bf16 *>(a.in.B) + tok0 * rowBC + g * kN;
-    const __bf16 *Cg = static_cast<const __bf16 *>(a.in.C) + tok0 * rowBC + g * kN;
     const __bf16 *xg = static_cast<const __bf16 *>(a.in.x) + tok0 * rowX + h0 * kP;
     const __bf16 *dtg = static_cast<const __bf16 *>(a.in.dt) + tok0 * H + h0;
     const int64_t NP = static_cast<int64_t>(kN) * kP;
     const int th = min(wave, HPW - 1);  // head whose dt this wavefront stages
     const float Ath = a.A[h0 + th];
-    float Dh[HPW];
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh)
-        Dh[hh] = a.D[h0 + hh];
 
     // ---- states: hs[hh][i] holds h[16 i + 4 q + j][p0 + r16] of head h0 + hh
     f32x4 hs[HPW][8];
@@ -163,20 +156,10 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
     constexpr int XPT = SC * kP * HPW / 8 / 256;  // uint4 per thread for x: 2 HPW
     struct Stage {
         uint4 bq[BPT];
-        uint4 cq[FULL ? BPT : 1];
         uint4 xq[XPT];
         __bf16 dt;  // dt of sub-chunk k+2, token `lane`, head h0 + min(wave, HPW-1)
     } st;
     // rows past the end are clamped here and zeroed at store time
-    auto load_c = [&](int k) {
-        const int64_t t0 = seg_t0 + static_cast<int64_t>(k) * SC;
-        const int last = static_cast<int>(min<int64_t>(SC, len - t0)) - 1;
-#pragma unroll
-        for (int u = 0; u < BPT; ++u) {
-            const int it = tid + 256 * u, row = min(16 * (it >> 8) + (it & 15), last), c16 = (it >> 4) & 15;
-            st.cq[u] = *reinterpret_cast<const uint4 *>(Cg + (t0 + row) * rowBC + c16 * 8);
-        }
-    };
     auto load_b = [&](int k) {
         const int64_t t0 = seg_t0 + static_cast<int64_t>(k) * SC;
         const int last = static_cast<int>(min<int64_t>(SC, len - t0)) - 1;
@@ -196,7 +179,7 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
             st.xq[u] = *reinterpret_cast<const uint4 *>(xg + (t0 + row) * rowX + c * 8);
         }
     };
-    auto load_stage = [&](int k) {  // all but C
+    auto load_stage = [&](int k) {
         load_b(k);
         load_x(k);
     };
@@ -213,8 +196,6 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
         for (int u = 0; u < BPT; ++u) {
             const int it = tid + 256 * u, row = 16 * (it >> 8) + (it & 15), c16 = (it >> 4) & 15;
             put16<kN>(L.B, row, c16 * 8, sel4(row < nvalid, st.bq[u]));
-            if (FULL)
-                put16<kN>(L.C, row, c16 * 8, sel4(row < nvalid, st.cq[u]));
         }
 #pragma unroll
         for (int u = 0; u < XPT; ++u) {
@@ -223,8 +204,8 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
             put16<kP>(L.X[c >> 3], row, (c & 7) * 8, sel4(row < nvalid, st.xq[u]));
         }
     };
-    // cumulative log2-decays of sub-chunk k for head h0 + wave (wavefronts below HPW), one
-    // token per lane, from the dt in st.dt; into table buffer k % 2
+    // the state update's weights of sub-chunk k for head h0 + wave (wavefronts below HPW),
+    // one token per lane, from the dt in st.dt; into table buffer k % 2
     auto tables = [&](int k) {
         if (wave < HPW) {
             const int64_t t0 = seg_t0 + static_cast<int64_t>(k) * SC;
@@ -232,15 +213,8 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
             const float d = lane < nvalid ? bf2f(st.dt) : 0.f;
             const float inc = wave_inclusive_sum(d * Ath);
             const float c = inc * kLog2e;
-            const float c31 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 31));
             const float clast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 63));
-            const float ref = lane < 32 ? c31 : clast;  // end of this token's 32-token pair
-            float(*tb)[SC] = L.tab[k & 1][wave];
-            tb[TAB_C][lane] = c;
-            tb[TAB_EF][lane] = __builtin_amdgcn_exp2f(c);
-            tb[TAB_LG][lane] = __builtin_amdgcn_logf(d) - c;
-            tb[TAB_COL][lane] = __builtin_amdgcn_exp2f(ref - c) * d;
-            tb[TAB_W][lane] = __builtin_amdgcn_exp2f(clast - c) * d;
+            L.tab[k & 1][wave][TAB_W][lane] = __builtin_amdgcn_exp2f(clast - c) * d;
             if (lane == 63)
                 L.tot[k & 1][wave] = inc;
         }
@@ -257,13 +231,8 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
             store_state(a.chunk_states + ((static_cast<int64_t>(b) * a.nch + c) * H + h0) * NP);
         }
     };
-    // The loads for sub-chunk k+1 are issued once the chunk-state stores of sub-chunk k-1
-    // are out, and only the (branch-free) y stores of sub-chunk k follow them before their
-    // use, so that waiting for them never waits for a store issued after them.
     load_stage(0);
     load_dt(0);
-    if (FULL)
-        load_c(0);
     __bf16 dt1;  // dt of sub-chunk 1, loaded with the first stage
     {
         const int64_t t1 = seg_t0 + SC * static_cast<int64_t>(min(1, nsub - 1));
@@ -275,23 +244,12 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
     if (nsub > 1)
         tables(1);
     for (int k = 0; k < nsub; ++k) {
-        const int64_t t0 = seg_t0 + static_cast<int64_t>(k) * SC;
-        const int nvalid = static_cast<int>(min<int64_t>(SC, len - t0));
         __syncthreads();  // (A) sub-chunk k staged, its tables written
         if (FULL && a.chunk_states && k > 0)
             emit_chunk_state(k - 1);
-        // the loads of sub-chunk k+1, in flight during sub-chunk k. With outputs they are
-        // spread over the first phases (B and dt here, C after the score tiles, x after the
-        // state product) rather than queued all at once behind the barrier; all of them
-        // precede the y stores, so that waiting for them never waits for a store.
+        // the loads of sub-chunk k+1, in flight during sub-chunk k
         const int kn = min(k + 1, nsub - 1);
-        if constexpr (FULL && WITHY) {
-            load_b(kn);
-        } else {
-            load_stage(kn);
-            if (FULL)
-                load_c(kn);
-        }
+        load_stage(kn);
         load_dt(min(k + 2, nsub - 1));
         __builtin_amdgcn_sched_barrier(0);  // keep the loads here, ahead of the compute
 
@@ -302,115 +260,6 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
 #pragma unroll
             for (int m = 0; m < 2; ++m)
                 xf[hh][m] = tr_frag<kP>(L.X[hh], 32 * m, p0, q, r16);
-
-        if constexpr (FULL && WITHY) {
-            static_assert(HPW == 1, "outputs are computed one head per workgroup");
-            // y rows of this sub-chunk; rows past the end fall outside the buffer range and
-            // their stores are dropped by the hardware
-            const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
-                static_cast<Ty *>(a.y) + (tok0 + t0) * rowX, 0, nvalid * rowX * static_cast<int>(sizeof(Ty)),
-                0x00020000);
-            const float(*tbl)[SC] = L.tab[k & 1][0];
-            // (1) the ten causal score tiles S[tb][sb] = B_s . C_t are shared by the four
-            // wavefronts: wavefront w computes tiles w, w+4, w+8, weights them with the
-            // decays (factored below the diagonal 32-token pair, per element on it) and
-            // stores them for all
-#pragma unroll
-            for (int r = 0; r < 3; ++r) {
-                const int tau = wave + 4 * r;
-                if (tau < 10) {  // uniform over the wavefront
-                    const int tb = tau >= 6 ? 3 : tau >= 3 ? 2 : tau >= 1 ? 1 : 0;
-                    const int sb = tau - tb * (tb + 1) / 2;
-                    f32x4 S = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int m = 0; m < 4; ++m)
-                        S = mfma(frag<kN>(L.B, sb, m, q, r16), frag<kN>(L.C, tb, m, q, r16), S);
-                    // lane (t, q) holds S[s = 16 sb + 4q + j][t]
-                    const int t = 16 * tb + r16, mp = sb >> 1, s0 = 16 * sb + 4 * q;
-                    const float ct = tbl[TAB_C][t];
-                    float mv[4];
-                    if (mp < (tb >> 1)) {  // pair wholly below the row block
-                        const float rowf = __builtin_amdgcn_exp2f(ct - tbl[TAB_C][32 * mp + 31]);
-                        const float4 cw = *reinterpret_cast<const float4 *>(&tbl[TAB_COL][s0]);
-                        mv[0] = S[0] * cw.x * rowf;
-                        mv[1] = S[1] * cw.y * rowf;
-                        mv[2] = S[2] * cw.z * rowf;
-                        mv[3] = S[3] * cw.w * rowf;
-                    } else {  // the pair holding the row block: masked to s <= t
-                        const float4 lg = *reinterpret_cast<const float4 *>(&tbl[TAB_LG][s0]);
-                        const float l4[4] = {lg.x, lg.y, lg.z, lg.w};
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            mv[j] = s0 + j <= t ? S[j] * __builtin_amdgcn_exp2f(ct + l4[j]) : 0.f;
-                    }
-                    bf16x4 mb;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        mb[j] = static_cast<__bf16>(mv[j]);
-                    *reinterpret_cast<bf16x4 *>(&L.Mt[tau][4 * lane]) = mb;
-                }
-            }
-            load_c(kn);
-            // (2) the state entering the sub-chunk: y^T[p][t] = sum_n h[n][p] C[t][n]. The
-            // state accumulators are the A operand as they stand: lane (p, q) holds
-            // h[16 i + 4q + j][p], so tiles 2m and 2m+1 give it rows 32m + 4q + j and
-            // 32m + 16 + 4q + j, the contraction order of the operand fragments; they are
-            // split into bf16 hi + lo here
-            f32x4 acc[4];
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
-                acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                bf16x8 hfh, hfl;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float v = hs[0][2 * m + (e >> 2)][e & 3];
-                    hfh[e] = static_cast<__bf16>(v);
-                    hfl[e] = static_cast<__bf16>(v - bf2f(hfh[e]));
-                }
-#pragma unroll
-                for (int tb = 0; tb < 4; ++tb) {
-                    const bf16x8 cf = frag<kN>(L.C, tb, m, q, r16);
-                    acc[tb] = mfma(hfh, cf, acc[tb]);
-                    acc[tb] = mfma(hfl, cf, acc[tb]);
-                }
-            }
-            load_x(kn);
-            __syncthreads();  // (A2) the weighted score tiles are stored
-            // (3) + sum_{s<=t} M[t][s] x_s per 32-token pair, + D x_t; the lane holds
-            // y[t][p0 + 4q .. p0 + 4q + 3]
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                const int t = 16 * tb + r16, md = tb >> 1;
-                acc[tb] *= tbl[TAB_EF][t];
-#pragma unroll
-                for (int m = 0; m <= md; ++m) {
-                    const int lo = tb * (tb + 1) / 2 + 2 * m;  // tile (tb, 2m); (tb, 2m+1) follows
-                    const bf16x4 m0 = *reinterpret_cast<const bf16x4 *>(&L.Mt[lo][4 * lane]);
-                    const bf16x4 m1 = 2 * m + 1 <= tb ? *reinterpret_cast<const bf16x4 *>(&L.Mt[lo + 1][4 * lane])
-                                                      : bf16x4{};
-                    acc[tb] = mfma(xf[0][m], cat(m0, m1), acc[tb]);
-                }
-                const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(&L.X[0][f8_off<kP>(t, p0 + 4 * q)]);
-                float o[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    o[j] = fmaf(Dh[0], bf2f(xv[j]), acc[tb][j]);
-                const int off = ((t * H + h0) * kP + p0 + 4 * q) * static_cast<int>(sizeof(Ty));
-                if constexpr (sizeof(Ty) == 2) {
-                    bf16x4 ov;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        ov[j] = static_cast<__bf16>(o[j]);
-                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2i32, ov), yr, off, 0, 0);
-                } else {
-                    __builtin_amdgcn_raw_buffer_store_b128(
-                        v4i32{__float_as_int(o[0]), __float_as_int(o[1]), __float_as_int(o[2]), __float_as_int(o[3])},
-                        yr, off, 0, 0);
-                }
-            }
-        }
 
         // ---- state: h <- exp(c_63) h + B^T (w o x), w_s = exp(c_63 - c_s) dt_s
 #pragma unroll
@@ -1189,20 +1038,16 @@ hipError_t launch_scan(const ScanArgs &a, hipStream_t st)
 {
     const int nwg = a.s.b * a.nseg * (a.s.H / HPW);
     if constexpr (FULL) {
+        static_assert(HPW == 1, "the full pass runs one head per workgroup");
         if (a.y) {
-            static const bool regs = getenv("BDSSM_PREFIX_REG_STAGING") != nullptr;  // the register-staged kernel
-            if (HPW == 1 && !regs) {
-                if constexpr (sizeof(Ty) == 2)
-                    k_full_bf16<<<dim3(nwg), dim3(256), 0, st>>>(a);
-                else
-                    k_full_f32<<<dim3(nwg), dim3(256), 0, st>>>(a);
-            } else {
-                k_scan<true, true, HPW, Ty><<<dim3(nwg), dim3(256), 0, st>>>(a);
-            }
+            if constexpr (sizeof(Ty) == 2)
+                k_full_bf16<<<dim3(nwg), dim3(256), 0, st>>>(a);
+            else
+                k_full_f32<<<dim3(nwg), dim3(256), 0, st>>>(a);
             return hipGetLastError();
         }
     }
-    k_scan<FULL, false, HPW, Ty><<<dim3(nwg), dim3(256), 0, st>>>(a);
+    k_scan<FULL, HPW><<<dim3(nwg), dim3(256), 0, st>>>(a);
     return hipGetLastError();
 }
 
