@@ -31,56 +31,13 @@
 
 #include "internal.h"
 #include "mfma_tiles.h"
+#include "wave_ops.h"
 
 namespace bdssm {
 namespace {
 
 constexpr int kN = 128, kP = 64;
 constexpr float kLog2e = 1.4426950408889634f;
-
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_move(float x)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, false));
-}
-
-// inclusive sum over the 64 lanes: shifts by 1, 2, 4, 8 inside rows of 16 lanes, then the
-// last lane of each row is added to the rows after it
-__device__ __forceinline__ float wave_inclusive_sum(float v)
-{
-    v += dpp_move<0x111, 0xf>(v);
-    v += dpp_move<0x112, 0xf>(v);
-    v += dpp_move<0x114, 0xf>(v);
-    v += dpp_move<0x118, 0xf>(v);
-    v += dpp_move<0x142, 0xa>(v);
-    v += dpp_move<0x143, 0xc>(v);
-    return v;
-}
-
-__device__ __forceinline__ float lane_value(float v, int l)
-{
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t quad_move(uint32_t x)
-{
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, 0xf, 0xf, false));
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes)
-{
-    // raw buffer with range checking: loads past `bytes` return zero, stores are dropped
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), 0x00020000);
-}
-
-// Copies one 1 KB piece of global memory into LDS without passing through registers
-// (gfx950 buffer_load ... lds): lane l's 16 bytes from byte offset `off` land at
-// dst + 16 l. Bytes past the buffer's range read as zero.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *dst, int off)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, off, 0, 0, 0);
-}
 
 // LDS tiles, each filled by whole-line copies (a load that touches few lines in full costs
 // the L1 several times less than one that touches many in part), with the 16-byte pieces
@@ -95,28 +52,11 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *dst, int o
 //              a lane's operand one 16-byte read, consecutive lanes consecutive pieces.
 constexpr int kRowBlk = 16 * 128;
 
-// Workgroup barrier over LDS filled by this workgroup's copies and writes: waits until at
-// most INFLIGHT of this wavefront's loads are outstanding and its LDS writes are done, then
-// synchronizes. (A memory fence here would wait for every load, copies to LDS included.)
-template <int INFLIGHT>
-__device__ __forceinline__ void lds_barrier()
-{
-    static_assert(INFLIGHT >= 0 && INFLIGHT < 64, "vmcnt range");
-    __builtin_amdgcn_sched_barrier(0);
-    // vmcnt(INFLIGHT) (bits 3:0 and 15:14), expcnt unchanged (7), lgkmcnt(0)
-    __builtin_amdgcn_s_waitcnt((INFLIGHT & 15) | ((INFLIGHT >> 4) << 14) | 0x0070);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-}
-
 // Operand fragment of row r16 of a row block: n = 32 kk + 8 q .. +7
 __device__ __forceinline__ bf16x8 rows_frag(const __bf16 *blk, int kk, int q, int r16)
 {
     return *reinterpret_cast<const bf16x8 *>(blk + 8 * (16 * r16 + ((4 * kk + q) ^ r16)));
 }
-
-typedef uint32_t v2u32 __attribute__((ext_vector_type(2)));
-typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
 
 enum { TAB_CF, TAB_CR, TAB_LGF, TAB_LGR, TAB_COLF, TAB_COLR, TAB_EF, NTAB };
 
@@ -157,20 +97,20 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
     const int rowBC = G * kN, rowX = H * kP;
     const int64_t bc_bytes = (static_cast<int64_t>(T - 1) * rowBC + kN) * 2;
     const int64_t bc0 = tok0 * rowBC + g * kN;
-    const auto rBf = rsrc(static_cast<const __bf16 *>(a.fwd.B) + bc0, bc_bytes);
-    const auto rCf = rsrc(static_cast<const __bf16 *>(a.fwd.C) + bc0, bc_bytes);
-    const auto rBr = rsrc(static_cast<const __bf16 *>(a.rev.B) + bc0, bc_bytes);
-    const auto rCr = rsrc(static_cast<const __bf16 *>(a.rev.C) + bc0, bc_bytes);
+    const auto rBf = buffer_range(static_cast<const __bf16 *>(a.fwd.B) + bc0, bc_bytes);
+    const auto rCf = buffer_range(static_cast<const __bf16 *>(a.fwd.C) + bc0, bc_bytes);
+    const auto rBr = buffer_range(static_cast<const __bf16 *>(a.rev.B) + bc0, bc_bytes);
+    const auto rCr = buffer_range(static_cast<const __bf16 *>(a.rev.C) + bc0, bc_bytes);
     const int64_t x0 = tok0 * rowX + h * kP;
     const int64_t x_bytes = (static_cast<int64_t>(T - 1) * rowX + kP) * 2;
-    const auto rXf = rsrc(static_cast<const __bf16 *>(a.fwd.x) + x0, x_bytes);
-    const auto rXr = rsrc(static_cast<const __bf16 *>(a.rev.x) + x0, x_bytes);
+    const auto rXf = buffer_range(static_cast<const __bf16 *>(a.fwd.x) + x0, x_bytes);
+    const auto rXr = buffer_range(static_cast<const __bf16 *>(a.rev.x) + x0, x_bytes);
     const int64_t dt_bytes = (static_cast<int64_t>(T - 1) * H + 1) * 2;
-    const auto rDf = rsrc(static_cast<const __bf16 *>(a.fwd.dt) + tok0 * H + h, dt_bytes);
-    const auto rDr = rsrc(static_cast<const __bf16 *>(a.rev.dt) + tok0 * H + h, dt_bytes);
+    const auto rDf = buffer_range(static_cast<const __bf16 *>(a.fwd.dt) + tok0 * H + h, dt_bytes);
+    const auto rDr = buffer_range(static_cast<const __bf16 *>(a.rev.dt) + tok0 * H + h, dt_bytes);
     const int64_t bh = static_cast<int64_t>(b) * H + h;
-    const auto rH = OPS ? rsrc(static_cast<const __bf16 *>(a.h_ops) + bh * (2 * kN * kP), 2 * kN * kP * 2)
-                        : rsrc(a.h_prefix + bh * (kN * kP), kN * kP * 4);
+    const auto rH = OPS ? buffer_range(static_cast<const __bf16 *>(a.h_ops) + bh * (2 * kN * kP), 2 * kN * kP * 2)
+                        : buffer_range(a.h_prefix + bh * (kN * kP), kN * kP * 4);
 
     // ---- the workgroup's inputs, each byte copied once, in whole lines, straight into
     // LDS, in the order of use: B and C (score tiles), x (M X), the state (C . h) last, so
@@ -190,11 +130,11 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
             const int i = k / 4, j = k % 4;
             const auto r = i == 0 ? rCf : i == 1 ? rCr : (i - 2 <= tb ? rBf : rBr);
             const int rl = 4 * j + (lane >> 4), piece = (lane & 15) ^ rl;
-            dma16(r, &rows[i][4 * j * 128], ((row0_of(i) + rl) * rowBC + 8 * piece) * 2);
+            copy_to_lds(r, &rows[i][4 * j * 128], ((row0_of(i) + rl) * rowBC + 8 * piece) * 2);
         } else {
             const int d = (k - 20) / 4, j = (k - 20) % 4;
             const int tr = 8 * j + (lane >> 3), c = (lane & 7) ^ (2 * (tr & 3));
-            dma16(d ? rXr : rXf, &xs[d][8 * j * kP], (tr * rowX + 8 * c) * 2);
+            copy_to_lds(d ? rXr : rXf, &xs[d][8 * j * kP], (tr * rowX + 8 * c) * 2);
         }
     };
     auto clear_piece = [&](int k) {
@@ -238,13 +178,13 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
             if constexpr (OPS) {  // operand rows (hi/lo, n/8) RPC m .. RPC m + RPC - 1, CW pieces each
                 constexpr int RPC = 64 / CW;
                 const int row = RPC * m + lane / CW, col = lane % CW;
-                dma16(rH, &hops[RPC * m * CW * 8], (row * kP + CW * ph + col) * 16);
+                copy_to_lds(rH, &hops[RPC * m * CW * 8], (row * kP + CW * ph + col) * 16);
             } else if constexpr (WPG == 2) {                       // (32 columns) or 4 m .. 4 m + 3
                 const int lr = 8 * m + (lane >> 3), n = lr ^ ((lr >> 4) & 1), c = (lane & 7) ^ (4 * ((n >> 3) & 1));
-                dma16(rH, &hst[8 * m * CW], (n * kP + CW * ph + 4 * c) * 4);
+                copy_to_lds(rH, &hst[8 * m * CW], (n * kP + CW * ph + 4 * c) * 4);
             } else {
                 const int n = 4 * m + (lane >> 4), c = (lane & 15) ^ (4 * ((n >> 3) & 3));
-                dma16(rH, &hst[4 * m * CW], (n * kP + 4 * c) * 4);
+                copy_to_lds(rH, &hst[4 * m * CW], (n * kP + 4 * c) * 4);
             }
         }
     };
@@ -259,13 +199,13 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
         const float g1 = __uint_as_float(static_cast<uint32_t>(dt4[3]) << 16);
         // forward: c_t inclusive prefix sum; reference at the pair's last token (lane 15)
         const float a0 = f0 * Ah, a1 = f1 * Ah, loc = a0 + a1;
-        const float inc = wave_inclusive_sum(loc), excl = inc - loc;
+        const float inc = wave_prefix_sum(loc), excl = inc - loc;
         const float c0 = (excl + a0) * kLog2e, c1 = (excl + loc) * kLog2e;
         // reverse: r_t inclusive suffix sum; reference at the pair's first token (lane 0)
         const float b0 = g0 * Ar, b1 = g1 * Ar, locr = b0 + b1;
-        const float incr = wave_inclusive_sum(locr), exclr = incr - locr, totr = lane_value(incr, 63);
+        const float incr = wave_prefix_sum(locr), exclr = incr - locr, totr = wave_lane(incr, 63);
         const float r0 = (totr - exclr) * kLog2e, r1 = (totr - exclr - b0) * kLog2e;
-        const float reff = lane_value(c1, 15), refr = lane_value(r0, 0);
+        const float reff = wave_lane(c1, 15), refr = wave_lane(r0, 0);
         if (t0 < TP) {
             tb_[TAB_CF][t0] = c0;
             tb_[TAB_CF][t1] = c1;
@@ -304,7 +244,7 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
         if (T < TP)  // rows past T: whatever the copies left in LDS there is replaced by zeros
             for_pieces(W, clear_piece);
     });
-    lds_barrier<NSTATE>();  // (1) everyone's B, C and x, and the tables
+    workgroup_lds_barrier<NSTATE>();  // (1) everyone's B, C and x, and the tables
 
     // ---- score tiles of the row block: S[t = tb*16 + r16][s = sb*16 + 4q + j]
     bf16x8 cfw[4], crv[4];
@@ -373,7 +313,7 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
         }
         acc_x = mfma(xvr, af, acc_x);
     }
-    lds_barrier<0>();  // (2) everyone's state
+    workgroup_lds_barrier<0>();  // (2) everyone's state
     // ---- eq. (11), cached-state term: C_t . (h_hi + h_lo), the B operand of column p being
     // h[32kk + 8q + e][p], e = 0..7, split into bf16 halves in registers; two independent chains
     f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc_lo = {0.f, 0.f, 0.f, 0.f};
@@ -434,7 +374,7 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
         for (int j = 0; j < 4; ++j)
             o[j] = fmaf(Dr, bf2f(xr[j]), o[j]);
     }
-    const auto rY = rsrc(static_cast<Ty *>(a.y) + x0, (static_cast<int64_t>(T - 1) * rowX + kP) * sizeof(Ty));
+    const auto rY = buffer_range(static_cast<Ty *>(a.y) + x0, (static_cast<int64_t>(T - 1) * rowX + kP) * sizeof(Ty));
     const int off = (t * rowX + p0) * static_cast<int>(sizeof(Ty));
     if constexpr (sizeof(Ty) == 2) {
         bf16x4 ov;

@@ -30,6 +30,7 @@
 // 4..7 s-block 2m+1) so that the score tiles' accumulator layout is directly the operand
 // layout of M^T; the X operand uses the same permutation.
 #include "internal.h"
+#include "wave_ops.h"
 
 namespace bdssm {
 namespace {
@@ -67,30 +68,6 @@ __device__ __forceinline__ void store4(__bf16 *p, const float (&v)[4])
     for (int j = 0; j < 4; ++j)
         b[j] = static_cast<__bf16>(v[j]);
     *reinterpret_cast<bf16x4 *>(p) = b;
-}
-
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_move(float x)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, false));
-}
-
-// inclusive sum over the 64 lanes: shifts by 1, 2, 4, 8 inside rows of 16 lanes, then the
-// last lane of each row is added to the rows after it
-__device__ __forceinline__ float wave_inclusive_sum(float v)
-{
-    v += dpp_move<0x111, 0xf>(v);
-    v += dpp_move<0x112, 0xf>(v);
-    v += dpp_move<0x114, 0xf>(v);
-    v += dpp_move<0x118, 0xf>(v);
-    v += dpp_move<0x142, 0xa>(v);
-    v += dpp_move<0x143, 0xc>(v);
-    return v;
-}
-
-__device__ __forceinline__ float lane_value(float v, int l)
-{
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
 template <int NB, int PS>
@@ -278,9 +255,9 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
             const float Aw = wave == 0 ? st.A : st.Ar;  // the reverse scan has its own decay
             const float a0 = d0 * Aw, a1 = d1 * Aw;
             const float loc = a0 + a1;
-            const float inc = wave_inclusive_sum(loc);
+            const float inc = wave_prefix_sum(loc);
             const float excl = inc - loc;
-            const float total = lane_value(inc, 63);
+            const float total = wave_lane(inc, 63);
             // forward: c_t inclusive prefix sum; reference at the pair's last token
             // reverse: r_t inclusive suffix sum; reference at the pair's first token
             const float c0 = wave == 0 ? (excl + a0) * kLog2e : (total - excl) * kLog2e;
@@ -289,10 +266,10 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
             // the readlanes as separate statements (inside a conditional expression they
             // would become branches), then a per-lane choice
             const int row = lane >> 4;
-            const float f15 = lane_value(c1, 15), f31 = lane_value(c1, 31), f47 = lane_value(c1, 47),
-                        f63 = lane_value(c1, 63);
-            const float g00 = lane_value(c0, 0), g16 = lane_value(c0, 16), g32 = lane_value(c0, 32),
-                        g48 = lane_value(c0, 48);
+            const float f15 = wave_lane(c1, 15), f31 = wave_lane(c1, 31), f47 = wave_lane(c1, 47),
+                        f63 = wave_lane(c1, 63);
+            const float g00 = wave_lane(c0, 0), g16 = wave_lane(c0, 16), g32 = wave_lane(c0, 32),
+                        g48 = wave_lane(c0, 48);
             const float reff = row == 0 ? f15 : row == 1 ? f31 : row == 2 ? f47 : f63;
             const float refr = row == 0 ? g00 : row == 1 ? g16 : row == 2 ? g32 : g48;
             const float ref = wave == 0 ? reff : refr;

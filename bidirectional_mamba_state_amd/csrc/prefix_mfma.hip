@@ -48,26 +48,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 enum { TAB_C, TAB_EF, TAB_LG, TAB_COL, TAB_W, NTAB };
 
-// DPP move of x from another lane (lanes with no source, or outside ROW_MASK, read 0)
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_move(float x)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, false));
-}
-
-// Inclusive sum over the 64 lanes of a wavefront: shifts by 1, 2, 4, 8 within rows of 16,
-// then the last lane of each row is added to the rows after it.
-__device__ __forceinline__ float wave_inclusive_sum(float v)
-{
-    v += dpp_move<0x111, 0xf>(v);  // row_shr:1
-    v += dpp_move<0x112, 0xf>(v);  // row_shr:2
-    v += dpp_move<0x114, 0xf>(v);  // row_shr:4
-    v += dpp_move<0x118, 0xf>(v);  // row_shr:8
-    v += dpp_move<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
-    v += dpp_move<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
-    return v;
-}
-
 struct ScanArgs {
     Shape s;
     int64_t len;         // tokens per stream
@@ -211,7 +191,7 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
             const int64_t t0 = seg_t0 + static_cast<int64_t>(k) * SC;
             const int nvalid = static_cast<int>(min<int64_t>(SC, len - t0));
             const float d = lane < nvalid ? bf2f(st.dt) : 0.f;
-            const float inc = wave_inclusive_sum(d * Ath);
+            const float inc = wave_prefix_sum(d * Ath);
             const float c = inc * kLog2e;
             const float clast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 63));
             L.tab[k & 1][wave][TAB_W][lane] = __builtin_amdgcn_exp2f(clast - c) * d;
@@ -415,9 +395,7 @@ __global__ __launch_bounds__(256, 2) void k_state(ScanArgs a)
     // range-checked buffers over the tokens of one sub-chunk (based at its first token, so
     // that offsets stay small however long the stream): rows past the stream's end read as
     // zero
-    const auto mk = [](const void *base, int64_t bytes) {
-        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), 0x00020000);
-    };
+    const auto mk = buffer_range;
     float Ah[HPW];
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh)
@@ -479,21 +457,12 @@ __global__ __launch_bounds__(256, 2) void k_state(ScanArgs a)
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh) {
             const float d = __uint_as_float(static_cast<uint32_t>(dbits[hh]) << 16);
-            const float inc = wave_inclusive_sum(d * Ah[hh]);
+            const float inc = wave_prefix_sum(d * Ah[hh]);
             const float c = inc * kLog2e;
             const float clast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 63));
             sW[k % 3][wave][hh][lane] = __builtin_amdgcn_exp2f(clast - c) * d;
             sTot[k % 3][wave][hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inc), 63));
         }
-    };
-    // bare barrier: waits until at most N of this wavefront's loads are outstanding and its
-    // LDS writes are done, then synchronizes
-    auto barrier = [&](auto N) {
-        constexpr int n = decltype(N)::value;
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0070);  // vmcnt(n), lgkmcnt(0)
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
     };
 
     f32x4 hs[HPW][8];  // hs[hh][i] holds h[16 i + 4 q + j][p0 + r16] of head h0 + hh
@@ -506,7 +475,7 @@ __global__ __launch_bounds__(256, 2) void k_state(ScanArgs a)
         constexpr int ph = decltype(PH)::value, phn = (ph + NBUF - 1) % NBUF;
         // this wavefront's copies of k have landed once at most those issued after them are
         // in flight: dt of k+1 and the copies of k+1
-        barrier(std::integral_constant<int, NPW + HPW>{});
+        workgroup_lds_barrier<NPW + HPW>();
         unsigned short dn[HPW];
         {
             // every operand of the sub-chunk into registers first: B^T (contraction over tokens
@@ -708,9 +677,7 @@ __device__ __forceinline__ void full_pass(const ScanArgs &a)
     const __bf16 *xg = static_cast<const __bf16 *>(a.in.x) + tok0 * rowX + h0 * kP;
     const __bf16 *dtg = static_cast<const __bf16 *>(a.in.dt) + tok0 * H + h0;
     const float Ah = a.A[h0], Dh = a.D[h0];
-    const auto mk = [](const void *base, int64_t bytes) {
-        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), 0x00020000);
-    };
+    const auto mk = buffer_range;
     // rows of sub-chunk k of the segment; 0 past the segment (its copies then move nothing)
     auto rows_of = [&](int k) {
         const int64_t t0 = seg_t0 + static_cast<int64_t>(k) * SC;
@@ -752,7 +719,7 @@ __device__ __forceinline__ void full_pass(const ScanArgs &a)
     // cumulative log2-decays of a sub-chunk from its dt, into table buffer PH
     auto tables = [&](auto PH, unsigned short dbits) {
         const float d = __uint_as_float(static_cast<uint32_t>(dbits) << 16);
-        const float inc = wave_inclusive_sum(d * Ah);
+        const float inc = wave_prefix_sum(d * Ah);
         const float c = inc * kLog2e;
         const float c31 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 31));
         const float clast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 63));
