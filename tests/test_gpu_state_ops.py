@@ -91,21 +91,25 @@ def test_block_step_ops_bitwise(monkeypatch, b, H, G, T):
     assert within(rel(y32.cpu().numpy(), yo), TOL_BF16, "block step ops vs oracle")
 
 
-def test_decode_graph_with_state_ops():
+@pytest.mark.parametrize("cfg_index,steps", [(1, 3), (4, 2)])
+def test_decode_graph_with_state_ops(cfg_index, steps):
     """The decode graph on the operand form: its steps equal eager bdssm_block_step_ops
     calls, its commit advances h, and it leaves h_ops = state_ops(advanced h), replay after
-    replay."""
+    replay (700M shape: one stream, T = 32, the small-batch kernel; 64 streams, T = 128,
+    the bandwidth kernel)."""
     import torch
-    cfg = configs.get(1)
+    cfg = configs.get(cfg_index)
     A, D = inputs.params(cfg)
-    H, P, N, T, steps = cfg.nheads, cfg.headdim, cfg.d_state, cfg.block_len, 3
-    print(f"[case] decode graph with state ops: {steps} steps + commit, 48 heads, T={T}", flush=True)
+    b, H, P, N, T = cfg.batch, cfg.nheads, cfg.headdim, cfg.d_state, cfg.block_len
+    print(f"[case] decode graph with state ops: config {cfg_index}, {b} streams, {steps} steps + commit, "
+          f"{H} heads, T={T}", flush=True)
     rng = np.random.default_rng(8)
-    h0 = f32_round(rng.standard_normal((1, H, N, P)) * 0.05)
+    h0 = f32_round(rng.standard_normal((b, H, N, P)) * 0.05)
     fwd = [bdssm.seq_to_device(inputs.block(cfg, 0, k, inputs.FWD)) for k in range(steps)]
     rev = [bdssm.seq_to_device(inputs.block(cfg, 0, k, inputs.REV)) for k in range(steps)]
-    clean = bdssm.seq_to_device(inputs.block(cfg, 0, 0, inputs.CLEAN))
-    d = bdssm.dims(1, H, P, N, 1, cfg.in_dtype, bdssm.F32)
+    # the graph commits block_len tokens (config 4's own commits take the oldest 32)
+    clean = bdssm.seq_to_device(inputs.block(cfg, 0, 0, inputs.CLEAN, length=T))
+    d = bdssm.dims(b, H, P, N, cfg.ngroups, cfg.in_dtype, bdssm.F32)
     Ad, Dd = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
     h_init = torch.from_numpy(h0.astype(np.float32)).cuda()
     nb = bdssm.state_ops_bytes(d)
@@ -113,7 +117,7 @@ def test_decode_graph_with_state_ops():
     h_e = h_init.clone()
     ops_e = torch.empty(nb, dtype=torch.uint8, device="cuda")
     bdssm.state_ops(d, h_e, ops_e)
-    y_e = [torch.empty((1, T, H, P), device="cuda") for _ in range(steps)]
+    y_e = [torch.empty((b, T, H, P), device="cuda") for _ in range(steps)]
     for k in range(steps):
         bdssm.block_step_ops(d, T, ops_e, fwd[k], rev[k], Ad, Dd, y_e[k])
     bdssm.commit(d, T, clean, Ad, Dd, h_e)
@@ -122,7 +126,7 @@ def test_decode_graph_with_state_ops():
 
     h_g = h_init.clone()
     ops_g = torch.empty(nb, dtype=torch.uint8, device="cuda")
-    y_g = [torch.empty((1, T, H, P), device="cuda") for _ in range(steps)]
+    y_g = [torch.empty((b, T, H, P), device="cuda") for _ in range(steps)]
     g = bdssm.DecodeGraph(d, T, h_g, fwd, rev, Ad, Dd, y_g, clean, None, h_ops=ops_g)
     try:
         for replay in range(3):
