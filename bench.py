@@ -114,6 +114,11 @@ def prefix_bytes(b, H, P, N, G, L, Q, in_bytes, y_bytes, chunk_states):
     return io + b * H * N * P * 4 + (b * nch * H * N * P * 4 if chunk_states else 0)
 
 
+def prefix_state_bytes(b, H, P, N, G, L, in_bytes):
+    """State-only prefix scan: x, dt and B read once, the final state written once, A and D."""
+    return b * L * (H * P + G * N + H) * in_bytes + b * H * N * P * 4 + 2 * H * 4
+
+
 def prefix_flops(b, H, P, N, G, L, Q):
     """Dense matrix-form flops of the chunked scan: per chunk and head, C.B^T (shared by
     the H/G heads of a group), the masked (Q x Q)(Q x P) product, the chunk state
@@ -421,7 +426,8 @@ def graph_us(torch, fn, reps=10, warm=2):
 def extra(torch, np, bdssm, configs, inputs):
     """The remaining figures of the measurement plan: the block step as a single launch
     (median of 20 after 5 warm-ups), with every buffer cold (rotation over more than the
-    256 MiB last-level cache) and cache-resident, at configs 0 and 3; the commit chain."""
+    256 MiB last-level cache) and cache-resident, at configs 0 and 3; the state-only prefix
+    builds of configs 3 and 4; the commit chain."""
     res = {}
     c1 = configs.get(1)
     b, H, P, N, G, T = c1.batch, c1.nheads, c1.headdim, c1.d_state, c1.ngroups, c1.block_len
@@ -489,6 +495,41 @@ def extra(torch, np, bdssm, configs, inputs):
         res[f"block_step_config{ci}"] = {"workload": c.name, "us_per_step": round(us, 3),
                                          "active_tokens_per_s": round(b * T / (us * 1e-6), 1),
                                          "hbm_frac": round(nb / (us * 1e-6) / HBM_PEAK, 4), "alg_bytes": nb}
+    # state-only prefix builds of configs 3 and 4 (the long-context cache: 262,144 tokens x
+    # 80 heads; the running set's caches: 64 streams x 32,768 tokens x 48 heads). Inputs of
+    # the configs' shapes and distributions drawn on the device (values do not change the
+    # time; the seeded host generator would take minutes at 3-14 GB)
+    for ci in (3, 4):
+        c = configs.get(ci)
+        b, H, P, N, G, L, Q = c.batch, c.nheads, c.headdim, c.d_state, c.ngroups, c.prefix_len, c.chunk
+        A, D = inputs.params(c)
+        Adv, Ddv = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(ci)
+        x = torch.empty((b, L, H, P), dtype=torch.bfloat16, device="cuda")
+        for k in range(b):  # one stream at a time keeps the float32 temporary small
+            x[k] = torch.randn((L, H, P), device="cuda", generator=gen).to(torch.bfloat16)
+        Bv = (0.25 * torch.randn((b, L, G, N), device="cuda", generator=gen)).to(torch.bfloat16)
+        dt = torch.nn.functional.softplus(torch.randn((b, L, H), device="cuda", generator=gen) - 4.0)
+        dt = dt.clamp(1e-3, 0.1).to(torch.bfloat16)
+        dv = bdssm.dims(b, H, P, N, G, 1, bdssm.BF16)
+        hv = torch.empty((b, H, N, P), device="cuda")
+        wsb = bdssm.prefix_scan_workspace(dv, L, Q, False, False)
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+        seq = (x, dt, Bv, None)
+        tm = Timer(torch)
+        for i in range(7):
+            (tm if i >= 2 else Timer(torch)).run("p", lambda: bdssm.prefix_scan(dv, L, Q, seq, Adv, Ddv, None, None,
+                                                                                 None, hv, ws, wsb))
+        torch.cuda.synchronize()
+        us = tm.avg_us("p")
+        nb = prefix_state_bytes(b, H, P, N, G, L, 2)
+        res[f"prefix_build_config{ci}"] = {"workload": f"state-only prefix scan, {c.name}, {b} x {L} tokens",
+                                           "avg_us": round(us, 1), "prefix_tokens_per_s": round(b * L / (us * 1e-6), 1),
+                                           "hbm_frac": round(nb / (us * 1e-6) / HBM_PEAK, 4), "alg_bytes": nb,
+                                           "data": "device-generated, same shapes and distributions"}
+        del x, Bv, dt, hv, ws, seq
+        torch.cuda.empty_cache()
     # commit chain, config 2: 2048 commits of 32 tokens over the 65,536-token prefix
     c2 = configs.get(2)
     b, H, P, N, G, L, T = c2.batch, c2.nheads, c2.headdim, c2.d_state, c2.ngroups, c2.prefix_len, c2.commit_len
