@@ -30,32 +30,21 @@
 // 4..7 s-block 2m+1) so that the score tiles' accumulator layout is directly the operand
 // layout of M^T; the X operand uses the same permutation.
 #include "internal.h"
+#include "mfma_tiles.h"
 #include "wave_ops.h"
 
 namespace bdssm {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
 constexpr int kN = 128, kP = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
 __device__ __forceinline__ bf16x8 ld16(const void *p) { return *static_cast<const bf16x8 *>(p); }
 
-__device__ __forceinline__ float bf2f(__bf16 v) { return static_cast<float>(v); }
-
-// Guarded loads without branches: the address is clamped to a valid row and the value
-// replaced by zero afterwards, so that all loads of a phase can be in flight together
-// (a branch around a load makes the compiler wait for every outstanding load).
-__device__ __forceinline__ bf16x8 sel8(bool ok, bf16x8 v) { return ok ? v : bf16x8{}; }
-__device__ __forceinline__ uint4 sel4(bool ok, uint4 v) { return ok ? v : make_uint4(0, 0, 0, 0); }
+// Guarded loads without branches (sel8, sel4 of mfma_tiles.h): the address is clamped to a
+// valid row and the value replaced by zero afterwards, so that all loads of a phase can be
+// in flight together (a branch around a load makes the compiler wait for every outstanding
+// load).
 
 __device__ __forceinline__ void store4(float *p, const float (&v)[4])
 {
@@ -203,14 +192,12 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
                 const int p2 = i % (PW / 2), n8 = (i / (PW / 2)) * 8;
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
-                    bf16x8 hi, lo;
+                    float f[8];
 #pragma unroll
-                    for (int r = 0; r < 8; ++r) {
-                        const float f = c ? st.s[k][r].y : st.s[k][r].x;
-                        const __bf16 fh = static_cast<__bf16>(f);
-                        hi[r] = fh;
-                        lo[r] = static_cast<__bf16>(f - bf2f(fh));
-                    }
+                    for (int r = 0; r < 8; ++r)
+                        f[r] = c ? st.s[k][r].y : st.s[k][r].x;
+                    bf16x8 hi, lo;
+                    split8(f, hi, lo);
                     *reinterpret_cast<bf16x8 *>(&hT_hi[buf][(2 * p2 + c) * HS + n8]) = hi;
                     *reinterpret_cast<bf16x8 *>(&hT_lo[buf][(2 * p2 + c) * HS + n8]) = lo;
                 }

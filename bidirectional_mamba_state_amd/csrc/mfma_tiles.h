@@ -30,14 +30,26 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 lo, bf16x4 hi)
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// fp32 values as bf16 hi + lo parts (about 16 significant bits together)
+// fp32 values as bf16 hi + lo parts (about 16 significant bits together): hi = bf16(f),
+// lo = bf16(f - hi), both rounded to nearest even. Written on pairs so that each conversion
+// instruction packs two values and the hi parts come back to float32 from the packed word
+// (a shift or a mask, exact), instead of being converted a second time one by one.
 __device__ __forceinline__ void split8(const float (&f)[8], bf16x8 &hi, bf16x8 &lo)
 {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 hw, lw;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        hi[e] = static_cast<__bf16>(f[e]);
-        lo[e] = static_cast<__bf16>(f[e] - bf2f(hi[e]));
+    for (int k = 0; k < 4; ++k) {
+        const f32x2 v = {f[2 * k], f[2 * k + 1]};
+        const uint32_t p = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+        const f32x2 r = {f[2 * k] - __uint_as_float(p << 16), f[2 * k + 1] - __uint_as_float(p & 0xffff0000u)};
+        hw[k] = p;
+        lw[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
     }
+    hi = __builtin_bit_cast(bf16x8, hw);
+    lo = __builtin_bit_cast(bf16x8, lw);
 }
 
 // Transposing LDS read (gfx950 ds_read_b64_tr_b16): in each 16-lane group, lanes 4r .. 4r+3

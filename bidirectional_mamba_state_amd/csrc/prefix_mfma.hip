@@ -852,13 +852,10 @@ __device__ __forceinline__ void full_pass(const ScanArgs &a)
                 acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
+                const float hv[8] = {hs[2 * m][0], hs[2 * m][1], hs[2 * m][2], hs[2 * m][3],
+                                     hs[2 * m + 1][0], hs[2 * m + 1][1], hs[2 * m + 1][2], hs[2 * m + 1][3]};
                 bf16x8 hfh, hfl;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float v = hs[2 * m + (e >> 2)][e & 3];
-                    hfh[e] = static_cast<__bf16>(v);
-                    hfl[e] = static_cast<__bf16>(v - bf2f(hfh[e]));
-                }
+                split8(hv, hfh, hfl);
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) {
                     const bf16x8 cf = c_frag(tb, m);
