@@ -286,15 +286,15 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
         const float4 l1 = *reinterpret_cast<const float4 *>(&tb_[TAB_LGF][16 + 4 * q]);
         const float lg[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
         const bool hi_ok = 1 <= tb;
-        bf16x8 af;
+        float mv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int s = (j < 4 ? 0 : 16) + 4 * q + (j & 3);
             const float sv = j < 4 ? S[0][j] : (hi_ok ? S[1][j & 3] : 0.f);
             const float w = __builtin_amdgcn_exp2f(ctf + lg[j]);
-            af[j] = static_cast<__bf16>(s <= t ? sv * w : 0.f);
+            mv[j] = s <= t ? sv * w : 0.f;
         }
-        acc_x = mfma(xvf, af, acc_x);
+        acc_x = mfma(xvf, to_bf16x8(mv), acc_x);
     }
     // eq. (12), reverse inside the block (s >= t)
     {
@@ -303,16 +303,19 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
         const float4 l1 = *reinterpret_cast<const float4 *>(&tb_[TAB_LGR][16 + 4 * q]);
         const float lg[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
         const bool lo_ok = 0 >= tb;
-        bf16x8 af;
+        float mv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int s = (j < 4 ? 0 : 16) + 4 * q + (j & 3);
             const float sv = j < 4 ? (lo_ok ? S[1][j] : 0.f) : S[2][j & 3];
             const float w = __builtin_amdgcn_exp2f(ctr + lg[j]);
-            af[j] = static_cast<__bf16>(s >= t ? sv * w : 0.f);
+            mv[j] = s >= t ? sv * w : 0.f;
         }
-        acc_x = mfma(xvr, af, acc_x);
+        acc_x = mfma(xvr, to_bf16x8(mv), acc_x);
     }
+    // both products are done before the barrier: left to itself the compiler sinks the second
+    // one (and its operand) below it, onto the path that waits for the state
+    asm volatile("" ::"v"(acc_x));
     workgroup_lds_barrier<0>();  // (2) everyone's state
     // ---- eq. (11), cached-state term: C_t . (h_hi + h_lo), the B operand of column p being
     // h[32kk + 8q + e][p], e = 0..7, split into bf16 halves in registers; two independent chains

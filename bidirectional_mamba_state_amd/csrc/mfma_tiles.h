@@ -52,6 +52,19 @@ __device__ __forceinline__ void split8(const float (&f)[8], bf16x8 &hi, bf16x8 &
     lo = __builtin_bit_cast(bf16x8, lw);
 }
 
+// eight floats as bf16 (round to nearest even), converted two per instruction
+__device__ __forceinline__ bf16x8 to_bf16x8(const float (&f)[8])
+{
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 w;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        w[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{f[2 * k], f[2 * k + 1]}), bf16x2));
+    return __builtin_bit_cast(bf16x8, w);
+}
+
 // Transposing LDS read (gfx950 ds_read_b64_tr_b16): in each 16-lane group, lanes 4r .. 4r+3
 // address row r (four consecutive elements each) and lane j receives column j of the four
 // rows.
