@@ -304,7 +304,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4, 
             const float ctf = cf[t];
 #pragma unroll
             for (int m = 0; m <= MD; ++m) {
-                bf16x8 af;
+                float mv[8];
                 if (m < MD) {
                     const float rowf = __builtin_amdgcn_exp2f(ctf - cf[32 * m + 31]);
                     const float4 c0 = *reinterpret_cast<const float4 *>(&colf[32 * m + 4 * q]);
@@ -312,7 +312,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4, 
                     const float cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
                     for (int j = 0; j < 8; ++j)
-                        af[j] = static_cast<__bf16>((j < 4 ? S[2 * m][j] : S[2 * m + 1][j & 3]) * cw[j] * rowf);
+                        mv[j] = (j < 4 ? S[2 * m][j] : S[2 * m + 1][j & 3]) * cw[j] * rowf;
                 } else {
                     const float4 l0 = *reinterpret_cast<const float4 *>(&lgf[32 * m + 4 * q]);
                     const float4 l1 = *reinterpret_cast<const float4 *>(&lgf[32 * m + 16 + 4 * q]);
@@ -323,17 +323,17 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4, 
                         const int s = 32 * m + (j < 4 ? 0 : 16) + 4 * q + (j & 3);
                         const float sv = j < 4 ? S[2 * m][j] : (hi_ok ? S[2 * m + 1][j & 3] : 0.f);
                         const float wgt = __builtin_amdgcn_exp2f(ctf + lg[j]);
-                        af[j] = static_cast<__bf16>(s <= t ? sv * wgt : 0.f);
+                        mv[j] = s <= t ? sv * wgt : 0.f;
                     }
                 }
-                mx(af, xs0, m);
+                mx(to_bf16x8(mv), xs0, m);
             }
             // eq. (12), reverse inside the block (s >= t); pairs wholly above the row block
             // use the factored decay with the reference at the pair's first token
             const float ctr = cr[t];
 #pragma unroll
             for (int m = MD; m < NB / 2; ++m) {
-                bf16x8 af;
+                float mv[8];
                 if (m > MD) {
                     const float rowr = __builtin_amdgcn_exp2f(ctr - cr[32 * m]);
                     const float4 c0 = *reinterpret_cast<const float4 *>(&colr[32 * m + 4 * q]);
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4, 
                     const float cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
                     for (int j = 0; j < 8; ++j)
-                        af[j] = static_cast<__bf16>((j < 4 ? S[2 * m + 1][j] : S[2 * m + 2][j & 3]) * cw[j] * rowr);
+                        mv[j] = (j < 4 ? S[2 * m + 1][j] : S[2 * m + 2][j & 3]) * cw[j] * rowr;
                 } else {
                     const float4 l0 = *reinterpret_cast<const float4 *>(&lgr[32 * m + 4 * q]);
                     const float4 l1 = *reinterpret_cast<const float4 *>(&lgr[32 * m + 16 + 4 * q]);
@@ -352,10 +352,10 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4, 
                         const int s = 32 * m + (j < 4 ? 0 : 16) + 4 * q + (j & 3);
                         const float sv = j < 4 ? (lo_ok ? S[2 * m + 1][j] : 0.f) : S[2 * m + 2][j & 3];
                         const float wgt = __builtin_amdgcn_exp2f(ctr + lg[j]);
-                        af[j] = static_cast<__bf16>(s >= t ? sv * wgt : 0.f);
+                        mv[j] = s >= t ? sv * wgt : 0.f;
                     }
                 }
-                mx(af, xs1, m);
+                mx(to_bf16x8(mv), xs1, m);
             }
             // the next head's decay tables (its inputs were loaded before the state copies)
             if constexpr (table_wave)

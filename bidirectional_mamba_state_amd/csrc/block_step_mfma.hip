@@ -367,25 +367,25 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
                 const float4 c0 = *reinterpret_cast<const float4 *>(&colf[32 * m + 4 * q]);
                 const float4 c1 = *reinterpret_cast<const float4 *>(&colf[32 * m + 16 + 4 * q]);
                 const float cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-                bf16x8 af;
+                float mv[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
-                    af[j] = static_cast<__bf16>((j < 4 ? S[2 * m][j] : S[2 * m + 1][j & 3]) * cw[j] * rowf);
-                mx(af, xtf, m);
+                    mv[j] = (j < 4 ? S[2 * m][j] : S[2 * m + 1][j & 3]) * cw[j] * rowf;
+                mx(to_bf16x8(mv), xtf, m);
             } else if (m == md) {
                 const float4 l0 = *reinterpret_cast<const float4 *>(&lgf[32 * m + 4 * q]);
                 const float4 l1 = *reinterpret_cast<const float4 *>(&lgf[32 * m + 16 + 4 * q]);
                 const float lg[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
                 const bool hi_ok = 2 * m + 1 <= tb;
-                bf16x8 af;
+                float mv[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int s = 32 * m + (j < 4 ? 0 : 16) + 4 * q + (j & 3);
                     const float sv = j < 4 ? S[2 * m][j] : (hi_ok ? S[2 * m + 1][j & 3] : 0.f);
                     const float w = __builtin_amdgcn_exp2f(ctf + lg[j]);
-                    af[j] = static_cast<__bf16>(s <= t ? sv * w : 0.f);
+                    mv[j] = s <= t ? sv * w : 0.f;
                 }
-                mx(af, xtf, m);
+                mx(to_bf16x8(mv), xtf, m);
             }
         }
         // eq. (12), reverse inside the block (s >= t); pairs wholly above the row block use
@@ -398,25 +398,25 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
                 const float4 c0 = *reinterpret_cast<const float4 *>(&colr[32 * m + 4 * q]);
                 const float4 c1 = *reinterpret_cast<const float4 *>(&colr[32 * m + 16 + 4 * q]);
                 const float cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-                bf16x8 af;
+                float mv[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
-                    af[j] = static_cast<__bf16>((j < 4 ? S[2 * m + 1][j] : S[2 * m + 2][j & 3]) * cw[j] * rowr);
-                mx(af, xtr, m);
+                    mv[j] = (j < 4 ? S[2 * m + 1][j] : S[2 * m + 2][j & 3]) * cw[j] * rowr;
+                mx(to_bf16x8(mv), xtr, m);
             } else if (m == md) {
                 const float4 l0 = *reinterpret_cast<const float4 *>(&lgr[32 * m + 4 * q]);
                 const float4 l1 = *reinterpret_cast<const float4 *>(&lgr[32 * m + 16 + 4 * q]);
                 const float lg[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
                 const bool lo_ok = 2 * m >= tb;
-                bf16x8 af;
+                float mv[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int s = 32 * m + (j < 4 ? 0 : 16) + 4 * q + (j & 3);
                     const float sv = j < 4 ? (lo_ok ? S[2 * m + 1][j] : 0.f) : S[2 * m + 2][j & 3];
                     const float w = __builtin_amdgcn_exp2f(ctr + lg[j]);
-                    af[j] = static_cast<__bf16>(s >= t ? sv * w : 0.f);
+                    mv[j] = s >= t ? sv * w : 0.f;
                 }
-                mx(af, xtr, m);
+                mx(to_bf16x8(mv), xtr, m);
             }
         }
         // eq. (13) + D x, written once: the lane holds y[t][pcb + 4q .. pcb + 4q + 3] of each
