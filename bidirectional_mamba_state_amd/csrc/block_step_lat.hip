@@ -75,14 +75,18 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
     __shared__ __attribute__((aligned(16))) __bf16 xs[2][TP * kP];      // x, both directions
     __shared__ __attribute__((aligned(16))) float tab[NTAB][TP];        // decay tables
 
+    // every kernel argument the first copies need, loaded in one round: left to itself the
+    // compiler loads some of them behind the index arithmetic's branches, a round trip each
+    asm volatile("" ::"s"(a.T), "s"(a.s.H), "s"(a.s.G), "s"(a.fwd.x), "s"(a.fwd.dt), "s"(a.fwd.B), "s"(a.fwd.C),
+                 "s"(a.rev.x), "s"(a.rev.dt), "s"(a.rev.B), "s"(a.rev.C), "s"(OPS ? a.h_ops : a.h_prefix),
+                 "s"(gridDim.x));
     const int T = a.T, H = a.s.H, G = a.s.G;
     // workgroup = (head, row block, column part), grid.y = stream. The hardware deals
     // workgroup ids round-robin over the 8 XCDs; the workgroups of a head read the same B, C
     // and x, so they get consecutive logical ids within one XCD's range and share its L2.
     const int nx = gridDim.x;
-    int wid = blockIdx.x;
-    if ((nx & 7) == 0)
-        wid = (wid & 7) * (nx >> 3) + (wid >> 3);
+    const int wid = (nx & 7) == 0 ? static_cast<int>((blockIdx.x & 7) * (nx >> 3) + (blockIdx.x >> 3))
+                                  : static_cast<int>(blockIdx.x);
     const int ph = wid % NPH, tb = (wid / NPH) & 1, h = wid / (2 * NPH), b = blockIdx.y;
     const int g = G == 1 ? 0 : h / (H / G);
     // wavefront w = 16-column block WPG ph + w of the outputs (uniform, so that LDS copy
@@ -170,8 +174,18 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
             fn(std::integral_constant<int, 3>{});
     };
     const int t0 = 2 * lane, t1 = t0 + 1;
-    const float Ah = a.A[h], Dh = a.D[h], Ar = a.A_rev[h];
-    const float Dr = a.D_rev ? a.D_rev[h] : 0.f;
+    // the head's decays and skip weights, read by vector loads issued first in each
+    // wavefront's prologue: as scalar loads, the wait that the first copies need for the
+    // kernel arguments would also wait for them
+    float Ah = 0.f, Dh = 0.f, Ar = 0.f, Dr = 0.f;
+    auto load_params = [&](bool decays) {
+        Dh = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_range(a.D, H * 4), h * 4, 0, 0));
+        Dr = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_range(a.D_rev, a.D_rev ? H * 4 : 0), h * 4, 0, 0));
+        if (decays) {
+            Ah = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_range(a.A, H * 4), h * 4, 0, 0));
+            Ar = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_range(a.A_rev, H * 4), h * 4, 0, 0));
+        }
+    };
     auto copy_state = [&]() {  // this wavefront's NSTATE state pieces
 #pragma unroll
         for (int m = NSTATE * w; m < NSTATE * w + NSTATE; ++m) {  // LDS state rows 8 m .. 8 m + 7
@@ -230,6 +244,7 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
     by_wave([&](auto W) {
         constexpr bool table_wave = decltype(W)::value == TW;
         unsigned short dt4[4] = {0, 0, 0, 0};
+        load_params(table_wave);
         if constexpr (table_wave) {
             dt4[0] = __builtin_amdgcn_raw_buffer_load_b16(rDf, t0 * H * 2, 0, 0);
             dt4[1] = __builtin_amdgcn_raw_buffer_load_b16(rDf, t1 * H * 2, 0, 0);
