@@ -270,3 +270,13 @@ def test_state_ops_argument_checks():
     assert step(dd=bdssm.dims(2, 4, 64, 128, 1, bdssm.F32)) == bdssm.ERR_UNSUPPORTED   # fp32 inputs
     assert step(T=-1) == bdssm.ERR_SHAPE
     assert step(T=0) == bdssm.OK                                       # nothing to do
+
+
+def test_missing_library_raises(monkeypatch):
+    # no fallback path: without the built library every call raises
+    monkeypatch.setattr(bdssm, "_lib", None)
+    monkeypatch.setattr(bdssm, "LIB_PATH", os.path.join(ROOT, "no_such_dir", "libbdssm.so"))
+    with pytest.raises(OSError, match="not built"):
+        bdssm.abi_version()
+    with pytest.raises(OSError, match="not built"):
+        bdssm.load()
