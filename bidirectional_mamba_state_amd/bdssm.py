@@ -22,7 +22,8 @@ EXPORTS = ("bdssm_abi_version", "bdssm_status_str", "bdssm_prefix_scan_workspace
            "bdssm_decode_graph_create",
            "bdssm_decode_graph_launch", "bdssm_decode_graph_destroy",
            "bdssm_conv_workspace", "bdssm_conv", "bdssm_block_step_conv", "bdssm_commit_conv",
-           "bdssm_state_ops_bytes", "bdssm_state_ops", "bdssm_block_step_ops")
+           "bdssm_state_ops_bytes", "bdssm_state_ops", "bdssm_block_step_ops",
+           "bdssm_set_launch_override")
 
 
 class BdssmError(RuntimeError):
@@ -41,6 +42,11 @@ class Dims(ctypes.Structure):
 class SeqPtrs(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("dt", ctypes.c_void_p),
                 ("B", ctypes.c_void_p), ("C", ctypes.c_void_p)]
+
+
+class LaunchOverride(ctypes.Structure):
+    _fields_ = [("block_kernel", ctypes.c_int32), ("lat_waves", ctypes.c_int32),
+                ("bw_heads", ctypes.c_int32), ("bw_splits", ctypes.c_int32)]
 
 
 class ConvParams(ctypes.Structure):
@@ -96,6 +102,8 @@ def load():
         lib.bdssm_commit_conv.restype = ctypes.c_int
         lib.bdssm_commit_conv.argtypes = [P(Dims), I32, P(ConvParams), P(SeqPtrs), V, V, V, V, V,
                                           V, SZ, V]
+        lib.bdssm_set_launch_override.restype = ctypes.c_int
+        lib.bdssm_set_launch_override.argtypes = [P(LaunchOverride)]
         _lib = lib
     return _lib
 
@@ -197,6 +205,16 @@ def block_step_ops(d, block_len, h_ops, fwd, rev, A, D, y, A_rev=None, D_rev=Non
                                        _byref(_seq(rev)), _ptr(A), _ptr(D),
                                        _ptr(A if A_rev is None else A_rev), _ptr(D_rev), _ptr(y),
                                        _stream(stream)))
+
+
+KERNEL_AUTO, KERNEL_SMALL_BATCH, KERNEL_BANDWIDTH = 0, 1, 2
+
+
+def set_launch_override(block_kernel=0, lat_waves=0, bw_heads=0, bw_splits=0):
+    """bdssm_set_launch_override (tests and launch-shape sweeps only): pins the block-step
+    kernel and its launch shape for later calls; all zeros = automatic."""
+    o = LaunchOverride(block_kernel, lat_waves, bw_heads, bw_splits)
+    _check(load().bdssm_set_launch_override(ctypes.byref(o)))
 
 
 def commit(d, block_len, clean, A, D, h, y=None, stream=None):

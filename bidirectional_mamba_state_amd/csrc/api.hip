@@ -136,21 +136,21 @@ Plan plan_prefix(const Shape &s, int64_t len, int32_t chunk, bool with_y, bool w
 
 bdssm_status launched(hipError_t e) { return e == hipSuccess ? BDSSM_OK : BDSSM_ERR_HIP; }
 
-// Tuning knobs for launch-shape sweeps: BDSSM_BLOCK_HPW (heads per workgroup, must divide
-// the heads of a group) and BDSSM_BLOCK_PS (column splits: 1, 2 or 4). Invalid values are
-// ignored.
+// Launch-shape override (bdssm_set_launch_override; tests and launch-shape sweeps only):
+// block kernel choice, small-batch wavefronts per workgroup, bandwidth-kernel heads per
+// workgroup and column splits; 0 = automatic. Read with relaxed atomic loads once per call.
+int g_override[4];
+int override_of(int i) { return __atomic_load_n(&g_override[i], __ATOMIC_RELAXED); }
+enum { OV_KERNEL, OV_LAT_WAVES, OV_BW_HEADS, OV_BW_SPLITS };
+
 void override_block_plan(const Shape &s, int *hpw, int *ps)
 {
-    if (const char *e = getenv("BDSSM_BLOCK_HPW")) {
-        const int v = atoi(e);
-        if (v >= 1 && (s.H / s.G) % v == 0)
-            *hpw = v;
-    }
-    if (const char *e = getenv("BDSSM_BLOCK_PS")) {
-        const int v = atoi(e);
-        if (v == 1 || v == 2 || v == 4)
-            *ps = v;
-    }
+    const int v = override_of(OV_BW_HEADS);
+    if (v >= 1 && (s.H / s.G) % v == 0)
+        *hpw = v;
+    const int p = override_of(OV_BW_SPLITS);
+    if (p == 1 || p == 2 || p == 4)
+        *ps = p;
 }
 
 // Validates a block step and fills its kernel arguments (nothing is launched).
@@ -189,23 +189,22 @@ bdssm_status prepare_block_step(const bdssm_dims *dims, int32_t block_len, const
 }
 
 // Small batches (fewer (stream, head) pairs than fill the GPU with one workgroup per CU)
-// take the latency-ordered kernel, one workgroup per (head, row block, column part);
-// BDSSM_BLOCK_LAT=0 or 1 forces the choice where both kernels apply, and
-// BDSSM_BLOCK_LAT_WPG=2 or 4 its wavefronts per workgroup.
+// take the latency-ordered kernel, one workgroup per (head, row block, column part); the
+// launch-shape override can force either kernel where both apply.
 bool use_block_lat(const Shape &s, int T)
 {
     if (!block_lat_supported(s, T))
         return false;
-    if (const char *e = getenv("BDSSM_BLOCK_LAT"))
-        return atoi(e) != 0;
+    const int k = override_of(OV_KERNEL);
+    if (k != 0)
+        return k == 1;
     return static_cast<int64_t>(s.b) * s.H < 512;
 }
 
 bdssm_status launch_block_step(const BlockArgs &a, hipStream_t st)
 {
     if (use_block_lat(a.s, a.T)) {
-        const char *e = getenv("BDSSM_BLOCK_LAT_WPG");
-        return launched(launch_block_step_lat(a, e ? atoi(e) : 0, st));
+        return launched(launch_block_step_lat(a, override_of(OV_LAT_WAVES), st));
     }
     if (block_mfma_supported(a.s, a.T)) {
         int hpw, ps;
@@ -482,6 +481,20 @@ bdssm_status bdssm_block_step_ex(const bdssm_dims *dims, int32_t block_len,
     return launch_block_step(a, static_cast<hipStream_t>(stream));
 }
 
+bdssm_status bdssm_set_launch_override(const bdssm_launch_override *o)
+{
+    const bdssm_launch_override z{0, 0, 0, 0};
+    const bdssm_launch_override &v = o ? *o : z;
+    if (v.block_kernel < 0 || v.block_kernel > 2 || (v.lat_waves != 0 && v.lat_waves != 2 && v.lat_waves != 4) ||
+        v.bw_heads < 0 || (v.bw_splits != 0 && v.bw_splits != 1 && v.bw_splits != 2 && v.bw_splits != 4))
+        return BDSSM_ERR_UNSUPPORTED;
+    __atomic_store_n(&g_override[OV_KERNEL], v.block_kernel, __ATOMIC_RELAXED);
+    __atomic_store_n(&g_override[OV_LAT_WAVES], v.lat_waves, __ATOMIC_RELAXED);
+    __atomic_store_n(&g_override[OV_BW_HEADS], v.bw_heads, __ATOMIC_RELAXED);
+    __atomic_store_n(&g_override[OV_BW_SPLITS], v.bw_splits, __ATOMIC_RELAXED);
+    return BDSSM_OK;
+}
+
 size_t bdssm_state_ops_bytes(const bdssm_dims *dims)
 {
     Shape s;
@@ -525,8 +538,7 @@ bdssm_status bdssm_block_step_ops(const bdssm_dims *dims, int32_t block_len, con
     a.h_prefix = nullptr;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     if (use_block_lat(a.s, block_len)) {
-        const char *e = getenv("BDSSM_BLOCK_LAT_WPG");
-        return launched(launch_block_step_lat(a, e ? atoi(e) : 0, st));
+        return launched(launch_block_step_lat(a, override_of(OV_LAT_WAVES), st));
     }
     if (!block_bw_supported(a.s, block_len))
         return BDSSM_ERR_UNSUPPORTED;

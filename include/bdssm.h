@@ -315,6 +315,31 @@ bdssm_status bdssm_decode_graph_launch(const bdssm_decode_graph *graph, void *st
 /* Frees the graph (NULL is ignored). Replays already enqueued are not affected. */
 void bdssm_decode_graph_destroy(bdssm_decode_graph *graph);
 
+/*
+ * Launch-shape override, for tests and launch-shape sweeps only (not for the hot path).
+ * Several kernels implement the block step, each one in full and each checked against the
+ * same bounds; the library picks one per call from the shapes. This call pins that choice
+ * for every later call in the process until it is called again (NULL or all zeros =
+ * automatic). Values are read once per call; a change racing with calls on other threads
+ * applies to each of them either entirely or not at all.
+ *   block_kernel  0 automatic; 1 the small-batch kernel (used where it applies:
+ *                 block_len <= 32, bf16 inputs, (d_state, headdim) = (128, 64));
+ *                 2 the bandwidth kernels
+ *   lat_waves     small-batch kernel: wavefronts per workgroup, 2 or 4 (0 automatic)
+ *   bw_heads      bandwidth kernels: heads per workgroup; ignored unless it divides H/G
+ *                 (0 automatic)
+ *   bw_splits     bandwidth kernel from the float32 state: column splits, 1, 2 or 4
+ *                 (0 automatic)
+ * Errors: BDSSM_ERR_UNSUPPORTED for values outside these sets (nothing is changed).
+ */
+typedef struct {
+    int32_t block_kernel;
+    int32_t lat_waves;
+    int32_t bw_heads;
+    int32_t bw_splits;
+} bdssm_launch_override;
+bdssm_status bdssm_set_launch_override(const bdssm_launch_override *o);
+
 #ifdef __cplusplus
 }
 #endif

@@ -280,3 +280,19 @@ def test_missing_library_raises(monkeypatch):
         bdssm.abi_version()
     with pytest.raises(OSError, match="not built"):
         bdssm.load()
+
+
+def test_launch_override_validation():
+    """bdssm_set_launch_override accepts the documented values only, and NULL resets."""
+    lib = bdssm.load()
+    bad = [(3, 0, 0, 0), (-1, 0, 0, 0), (0, 3, 0, 0), (0, 1, 0, 0), (0, 0, -2, 0), (0, 0, 0, 3)]
+    for v in bad:
+        o = bdssm.LaunchOverride(*v)
+        assert lib.bdssm_set_launch_override(ctypes.byref(o)) == bdssm.ERR_UNSUPPORTED, v
+    for v in [(1, 2, 0, 0), (2, 4, 6, 2), (0, 0, 0, 4)]:
+        o = bdssm.LaunchOverride(*v)
+        assert lib.bdssm_set_launch_override(ctypes.byref(o)) == bdssm.OK, v
+    assert lib.bdssm_set_launch_override(None) == bdssm.OK
+    bdssm.set_launch_override()
+    with pytest.raises(bdssm.BdssmError):
+        bdssm.set_launch_override(lat_waves=5)

@@ -261,7 +261,7 @@ def test_commit_chain_equals_prefix_scan():
 
 
 @pytest.mark.parametrize("T", [17, 32, 64, 128])
-def test_block_step_launch_shapes(monkeypatch, T):
+def test_block_step_launch_shapes(launch_override, T):
     """Both block-step kernels give the oracle's result: the bandwidth kernel at every
     (heads per workgroup, column split) launch shape, and the latency kernel (one workgroup
     per head, row block and column part, of 2 or 4 wavefronts; T <= 32) with float32 and
@@ -278,19 +278,16 @@ def test_block_step_launch_shapes(monkeypatch, T):
     Dz = np.zeros_like(D)
     yzo, _, _ = oracle.block_step(h, fwd, rev, A, Dz)
     shapes = [(hpw, ps) for hpw in (1, 2, 3, 6) for ps in (1, 2, 4)] if T in (32, 128) else [(1, 4), (6, 1)]
-    monkeypatch.setenv("BDSSM_BLOCK_LAT", "0")
     for hpw, ps in shapes:
-        monkeypatch.setenv("BDSSM_BLOCK_HPW", str(hpw))
-        monkeypatch.setenv("BDSSM_BLOCK_PS", str(ps))
+        launch_override(block_kernel=bdssm.KERNEL_BANDWIDTH, bw_heads=hpw, bw_splits=ps)
         _case(f"launch shape T={T} hpw={hpw} ps={ps}")
         y = gpu_block_step(h, fwd, rev, A, D)
         yz = gpu_block_step(h, fwd, rev, A, Dz)
         assert within(rel(y, yo), TOL_BF16, f"y hpw={hpw} ps={ps}")
         assert within(rel(yz, yzo), TOL_BF16, f"y - D x hpw={hpw} ps={ps}")
     if T <= 32:
-        monkeypatch.setenv("BDSSM_BLOCK_LAT", "1")
         for wpg, y_dtype in ((2, bdssm.F32), (2, bdssm.BF16), (4, bdssm.F32), (4, bdssm.BF16)):
-            monkeypatch.setenv("BDSSM_BLOCK_LAT_WPG", str(wpg))
+            launch_override(block_kernel=bdssm.KERNEL_SMALL_BATCH, lat_waves=wpg)
             _case(f"latency kernel T={T} wavefronts per workgroup {wpg} y_dtype={y_dtype}")
             y = gpu_block_step(h, fwd, rev, A, D, y_dtype)
             yz = gpu_block_step(h, fwd, rev, A, Dz, y_dtype)

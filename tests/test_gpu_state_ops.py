@@ -59,7 +59,7 @@ def _case_inputs(b, H, G, T, seed):
 
 
 @pytest.mark.parametrize("b,H,G,T", [(1, 48, 1, 32), (3, 12, 2, 17), (3, 12, 2, 32), (2, 40, 8, 1)])
-def test_block_step_ops_bitwise(monkeypatch, b, H, G, T):
+def test_block_step_ops_bitwise(launch_override, b, H, G, T):
     import torch
     fwd, rev, A, D, Ar, Dr, h = _case_inputs(b, H, G, T, 1000 + 7 * H + T)
     tf, tr = bdssm.seq_to_device(fwd), bdssm.seq_to_device(rev)
@@ -68,9 +68,8 @@ def test_block_step_ops_bitwise(monkeypatch, b, H, G, T):
     d32 = bdssm.dims(b, H, 64, 128, G, bdssm.BF16, bdssm.F32)
     ops = torch.empty(bdssm.state_ops_bytes(d32), dtype=torch.uint8, device="cuda")
     bdssm.state_ops(d32, hd, ops)
-    monkeypatch.setenv("BDSSM_BLOCK_LAT", "1")
     for wpg in (2, 4):
-        monkeypatch.setenv("BDSSM_BLOCK_LAT_WPG", str(wpg))
+        launch_override(block_kernel=bdssm.KERNEL_SMALL_BATCH, lat_waves=wpg)
         for y_dt, tdt in ((bdssm.F32, torch.float32), (bdssm.BF16, torch.bfloat16)):
             for sep in (False, True):
                 print(f"[case] block step ops b={b} H={H} G={G} T={T} wpg={wpg} y={y_dt} separate={sep}", flush=True)
@@ -151,7 +150,7 @@ def test_decode_graph_with_state_ops(cfg_index, steps):
     (16, 32, 1, 32, False, (1, 2, 4)),       # 512 pairs, T = 32: 2 row blocks
     (2, 16, 4, 5, True, (1, 2)),             # 2 row blocks, mostly past T
 ])
-def test_block_step_ops_bandwidth_kernel(monkeypatch, b, H, G, T, lat_off, hpws):
+def test_block_step_ops_bandwidth_kernel(launch_override, b, H, G, T, lat_off, hpws):
     """bdssm_block_step_ops where it runs the kernel that copies the operand-form state and x
     into LDS: y matches the oracle for float32 and bf16 y, with and without separate reverse
     parameters, also with D = 0 (the scan terms alone), and does not depend on how many
@@ -165,8 +164,7 @@ def test_block_step_ops_bandwidth_kernel(monkeypatch, b, H, G, T, lat_off, hpws)
     d32 = bdssm.dims(b, H, 64, 128, G, bdssm.BF16, bdssm.F32)
     ops = torch.empty(bdssm.state_ops_bytes(d32), dtype=torch.uint8, device="cuda")
     bdssm.state_ops(d32, hd, ops)
-    if lat_off:
-        monkeypatch.setenv("BDSSM_BLOCK_LAT", "0")
+    kernel = bdssm.KERNEL_BANDWIDTH if lat_off else bdssm.KERNEL_AUTO
     want = {
         (False, False): oracle.block_step(h, fwd, rev, A, D)[0],
         (False, True): oracle.block_step(h, fwd, rev, A, np.zeros_like(D))[0],
@@ -177,7 +175,7 @@ def test_block_step_ops_bandwidth_kernel(monkeypatch, b, H, G, T, lat_off, hpws)
         for sep, dz in ((False, False), (False, True), (True, False)):
             first = None
             for hpw in hpws:
-                monkeypatch.setenv("BDSSM_BLOCK_HPW", str(hpw))
+                launch_override(block_kernel=kernel, bw_heads=hpw)
                 print(f"[case] block step ops (bandwidth) b={b} H={H} G={G} T={T} hpw={hpw} y={y_dt} "
                       f"separate={sep} D=0:{dz}", flush=True)
                 y = torch.full((b, T, H, 64), float("nan"), dtype=tdt, device="cuda")
