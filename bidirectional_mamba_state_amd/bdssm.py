@@ -13,7 +13,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbdssm.so")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_ALIAS, ERR_WORKSPACE, ERR_HIP = range(8)
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_ALIAS, ERR_WORKSPACE, ERR_HIP, ERR_SCRATCH = range(9)
+STATIC_SCRATCH_BYTES = 64 << 20
 F32, BF16 = 0, 1
 
 # every symbol include/bdssm.h declares
@@ -23,7 +24,7 @@ EXPORTS = ("bdssm_abi_version", "bdssm_status_str", "bdssm_prefix_scan_workspace
            "bdssm_decode_graph_launch", "bdssm_decode_graph_destroy",
            "bdssm_conv_workspace", "bdssm_conv", "bdssm_block_step_conv", "bdssm_commit_conv",
            "bdssm_state_ops_bytes", "bdssm_state_ops", "bdssm_block_step_ops",
-           "bdssm_set_launch_override")
+           "bdssm_set_launch_override", "bdssm_prefix_scan_static")
 
 
 class BdssmError(RuntimeError):
@@ -102,6 +103,8 @@ def load():
         lib.bdssm_commit_conv.restype = ctypes.c_int
         lib.bdssm_commit_conv.argtypes = [P(Dims), I32, P(ConvParams), P(SeqPtrs), V, V, V, V, V,
                                           V, SZ, V]
+        lib.bdssm_prefix_scan_static.restype = ctypes.c_int
+        lib.bdssm_prefix_scan_static.argtypes = [P(Dims), I64, I32, P(SeqPtrs), V, V, V, V, V, V, V]
         lib.bdssm_set_launch_override.restype = ctypes.c_int
         lib.bdssm_set_launch_override.argtypes = [P(LaunchOverride)]
         _lib = lib
@@ -173,6 +176,14 @@ def prefix_scan(d, length, chunk, seq, A, D, h_init, y, chunk_states, h_out,
                                     _ptr(D), _ptr(h_init), _ptr(y), _ptr(chunk_states),
                                     _ptr(h_out), _ptr(workspace), workspace_bytes,
                                     _stream(stream)))
+
+
+def prefix_scan_static(d, length, chunk, seq, A, D, h_init, y, chunk_states, h_out, stream=None):
+    """bdssm_prefix_scan_static: bdssm_prefix_scan with its workspace taken from the
+    library's static scratch buffer (no workspace argument, nothing allocated)."""
+    _check(load().bdssm_prefix_scan_static(ctypes.byref(d), length, chunk, _byref(_seq(seq)), _ptr(A),
+                                           _ptr(D), _ptr(h_init), _ptr(y), _ptr(chunk_states),
+                                           _ptr(h_out), _stream(stream)))
 
 
 def block_step(d, block_len, h_prefix, fwd, rev, A, D, y, stream=None):

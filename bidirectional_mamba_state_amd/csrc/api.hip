@@ -313,45 +313,40 @@ ConvCopy conv_copy_bytes(const Shape &s, int64_t len)
     return ConvCopy{xb, xb + bb, xb + 2 * bb};
 }
 
-}  // namespace
+// ---- the static scratch buffer of bdssm_prefix_scan_static: device memory the library
+// holds for callers that cannot allocate. Each GPU has its own copy at its own address; in
+// host code the array's name is only a stand-in, so the address is taken per device with
+// hipGetSymbolAddress (with that device current, on the first call there) and only that
+// address is passed to kernels.
+constexpr size_t kStaticScratchBytes = BDSSM_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
-extern "C" {
-
-int bdssm_abi_version(void) { return BDSSM_ABI_VERSION; }
-
-const char *bdssm_status_str(int status)
+bdssm_status static_scratch_ptr(void **out)
 {
-    switch (status) {
-    case BDSSM_OK: return "BDSSM_OK";
-    case BDSSM_ERR_NULL: return "BDSSM_ERR_NULL: a required pointer is NULL";
-    case BDSSM_ERR_SHAPE: return "BDSSM_ERR_SHAPE: invalid or inconsistent sizes";
-    case BDSSM_ERR_UNSUPPORTED: return "BDSSM_ERR_UNSUPPORTED: no kernel for this shape, chunk or dtype";
-    case BDSSM_ERR_ALIGN: return "BDSSM_ERR_ALIGN: a pointer is not 16-byte aligned";
-    case BDSSM_ERR_ALIAS: return "BDSSM_ERR_ALIAS: an output overlaps an input";
-    case BDSSM_ERR_WORKSPACE: return "BDSSM_ERR_WORKSPACE: workspace missing or too small";
-    case BDSSM_ERR_HIP: return "BDSSM_ERR_HIP: the HIP runtime reported a launch error";
-    default: return "unknown bdssm status";
+    static void *cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return BDSSM_ERR_HIP;
     }
+    void *p = __atomic_load_n(&cache[dev], __ATOMIC_ACQUIRE);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return BDSSM_ERR_HIP;
+        }
+        __atomic_store_n(&cache[dev], p, __ATOMIC_RELEASE);
+    }
+    *out = p;
+    return BDSSM_OK;
 }
 
-size_t bdssm_prefix_scan_workspace(const bdssm_dims *dims, int64_t len, int32_t chunk,
-                                   int32_t with_y, int32_t with_chunk_states)
-{
-    Shape s;
-    if (check_dims(dims, &s) != BDSSM_OK || len < 0 || !chunk_ok(chunk))
-        return SIZE_MAX;
-    if (len == 0 || s.b == 0)
-        return 0;
-    if (prefix_mfma_supported(s, chunk))
-        return prefix_mfma_plan(s, len, chunk, with_y || with_chunk_states).ws_bytes;
-    return plan_prefix(s, len, chunk, with_y != 0, with_chunk_states != 0).ws_bytes;
-}
-
-bdssm_status bdssm_prefix_scan(const bdssm_dims *dims, int64_t len, int32_t chunk,
-                               const bdssm_seq *in, const float *A, const float *D,
-                               const float *h_init, void *y, float *chunk_states,
-                               float *h_out, void *workspace, size_t workspace_bytes,
-                               void *stream)
+// bdssm_prefix_scan and bdssm_prefix_scan_static: with static_scratch the workspace comes
+// from the library's static device buffer instead of the caller.
+bdssm_status prefix_scan_impl(const bdssm_dims *dims, int64_t len, int32_t chunk, const bdssm_seq *in,
+                              const float *A, const float *D, const float *h_init, void *y,
+                              float *chunk_states, float *h_out, void *workspace, size_t workspace_bytes,
+                              bool static_scratch, void *stream)
 {
     Shape s;
     bdssm_status rc = check_dims(dims, &s);
@@ -399,6 +394,22 @@ bdssm_status bdssm_prefix_scan(const bdssm_dims *dims, int64_t len, int32_t chun
 
     const bool with_y = y != nullptr, with_cs = chunk_states != nullptr;
     const Seq seq{in->x, in->dt, in->B, in->C};
+    if (static_scratch) {
+        // the plan's workspace from the static buffer (nothing to clear: every byte a kernel
+        // reads from it is written earlier in the same call)
+        const size_t need = prefix_mfma_supported(s, chunk)
+                                ? prefix_mfma_plan(s, len, chunk, with_y || with_cs).ws_bytes
+                                : plan_prefix(s, len, chunk, with_y, with_cs).ws_bytes;
+        workspace = nullptr;
+        workspace_bytes = 0;
+        if (need > 0) {
+            if (need > kStaticScratchBytes)
+                return BDSSM_ERR_SCRATCH;
+            if ((rc = static_scratch_ptr(&workspace)) != BDSSM_OK)
+                return rc;
+            workspace_bytes = kStaticScratchBytes;
+        }
+    }
     if (prefix_mfma_supported(s, chunk)) {
         const PrefixPlan mp = prefix_mfma_plan(s, len, chunk, with_y || with_cs);
         if (mp.ws_bytes > 0) {
@@ -459,6 +470,61 @@ bdssm_status bdssm_prefix_scan(const bdssm_dims *dims, int64_t len, int32_t chun
             return rc;
     }
     return BDSSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bdssm_abi_version(void) { return BDSSM_ABI_VERSION; }
+
+const char *bdssm_status_str(int status)
+{
+    switch (status) {
+    case BDSSM_OK: return "BDSSM_OK";
+    case BDSSM_ERR_NULL: return "BDSSM_ERR_NULL: a required pointer is NULL";
+    case BDSSM_ERR_SHAPE: return "BDSSM_ERR_SHAPE: invalid or inconsistent sizes";
+    case BDSSM_ERR_UNSUPPORTED: return "BDSSM_ERR_UNSUPPORTED: no kernel for this shape, chunk or dtype";
+    case BDSSM_ERR_ALIGN: return "BDSSM_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case BDSSM_ERR_ALIAS: return "BDSSM_ERR_ALIAS: an output overlaps an input";
+    case BDSSM_ERR_WORKSPACE: return "BDSSM_ERR_WORKSPACE: workspace missing or too small";
+    case BDSSM_ERR_HIP: return "BDSSM_ERR_HIP: the HIP runtime reported a launch error";
+    case BDSSM_ERR_SCRATCH:
+        return "BDSSM_ERR_SCRATCH: the call needs more workspace than the library's static scratch buffer holds";
+    default: return "unknown bdssm status";
+    }
+}
+
+size_t bdssm_prefix_scan_workspace(const bdssm_dims *dims, int64_t len, int32_t chunk,
+                                   int32_t with_y, int32_t with_chunk_states)
+{
+    Shape s;
+    if (check_dims(dims, &s) != BDSSM_OK || len < 0 || !chunk_ok(chunk))
+        return SIZE_MAX;
+    if (len == 0 || s.b == 0)
+        return 0;
+    if (prefix_mfma_supported(s, chunk))
+        return prefix_mfma_plan(s, len, chunk, with_y || with_chunk_states).ws_bytes;
+    return plan_prefix(s, len, chunk, with_y != 0, with_chunk_states != 0).ws_bytes;
+}
+
+bdssm_status bdssm_prefix_scan(const bdssm_dims *dims, int64_t len, int32_t chunk,
+                               const bdssm_seq *in, const float *A, const float *D,
+                               const float *h_init, void *y, float *chunk_states,
+                               float *h_out, void *workspace, size_t workspace_bytes,
+                               void *stream)
+{
+    return prefix_scan_impl(dims, len, chunk, in, A, D, h_init, y, chunk_states, h_out, workspace,
+                            workspace_bytes, false, stream);
+}
+
+bdssm_status bdssm_prefix_scan_static(const bdssm_dims *dims, int64_t len, int32_t chunk,
+                                      const bdssm_seq *in, const float *A, const float *D,
+                                      const float *h_init, void *y, float *chunk_states,
+                                      float *h_out, void *stream)
+{
+    return prefix_scan_impl(dims, len, chunk, in, A, D, h_init, y, chunk_states, h_out, nullptr, 0, true,
+                            stream);
 }
 
 bdssm_status bdssm_block_step(const bdssm_dims *dims, int32_t block_len,

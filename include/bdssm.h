@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define BDSSM_ABI_VERSION 3
+#define BDSSM_ABI_VERSION 4
 
 typedef enum {
     BDSSM_OK = 0,
@@ -70,7 +70,9 @@ typedef enum {
     BDSSM_ERR_ALIGN = 4,       /* a base pointer is not 16-byte aligned */
     BDSSM_ERR_ALIAS = 5,       /* an output overlaps an input it must not overlap */
     BDSSM_ERR_WORKSPACE = 6,   /* workspace missing or smaller than the query returned */
-    BDSSM_ERR_HIP = 7          /* the HIP runtime reported an error at launch */
+    BDSSM_ERR_HIP = 7,         /* the HIP runtime reported an error at launch */
+    BDSSM_ERR_SCRATCH = 8      /* bdssm_prefix_scan_static: more workspace needed than the
+                                  static scratch buffer holds */
 } bdssm_status;
 
 typedef enum { BDSSM_F32 = 0, BDSSM_BF16 = 1 } bdssm_dtype;
@@ -123,6 +125,29 @@ bdssm_status bdssm_prefix_scan(const bdssm_dims *dims, int64_t len, int32_t chun
                                const float *h_init, void *y, float *chunk_states,
                                float *h_out, void *workspace, size_t workspace_bytes,
                                void *stream);
+
+/*
+ * Prefix scan that allocates nothing and takes no workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): bdssm_prefix_scan, bitwise, with the workspace it would need taken
+ * from a scratch buffer the library keeps in device memory -- a static array of
+ * BDSSM_STATIC_SCRATCH_BYTES (64 MiB) per GPU, held from the library's first use of that
+ * GPU until the process ends. Every call on one GPU shares that GPU's buffer and it keeps
+ * the last call's contents (each call writes all it reads), so calls that overlap in time
+ * on one GPU -- on different streams, or from different threads -- race and give wrong
+ * results; calls in order on one stream are safe. On the matrix-core path (bf16 inputs,
+ * (d_state, headdim) = (128, 64), chunk >= 64) the largest plan needs about 32 MiB on a
+ * 256-CU MI355X, whatever the sizes; other paths need bdssm_prefix_scan_workspace bytes.
+ * Arguments, layouts, ownership and errors as bdssm_prefix_scan, plus:
+ *   BDSSM_ERR_SCRATCH  the call would need more than BDSSM_STATIC_SCRATCH_BYTES of workspace
+ *                      (rejected before anything is launched)
+ *   BDSSM_ERR_HIP      the buffer's device address could not be obtained
+ */
+#define BDSSM_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+bdssm_status bdssm_prefix_scan_static(const bdssm_dims *dims, int64_t len, int32_t chunk,
+                                      const bdssm_seq *in, const float *A, const float *D,
+                                      const float *h_init, void *y, float *chunk_states,
+                                      float *h_out, void *stream);
 
 /*
  * Block step: eqs. (11)-(13), one denoising step of the active block of T = block_len

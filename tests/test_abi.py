@@ -24,8 +24,8 @@ def test_library_exports_every_declared_symbol():
     assert syms == sorted(bdssm.EXPORTS)
     for s in syms:
         assert hasattr(lib, s), s
-    assert bdssm.abi_version() == 3
-    for st in range(8):
+    assert bdssm.abi_version() == 4
+    for st in range(9):
         assert bdssm.status_str(st).startswith("BDSSM_")
     assert "unknown" in bdssm.status_str(99)
 
@@ -296,3 +296,23 @@ def test_launch_override_validation():
     bdssm.set_launch_override()
     with pytest.raises(bdssm.BdssmError):
         bdssm.set_launch_override(lat_waves=5)
+
+
+def test_prefix_scan_static_rejects_oversized_plans():
+    """bdssm_prefix_scan_static refuses, before any launch, a call whose plan needs more
+    workspace than the static scratch buffer holds (float32 inputs: the chunk-local states
+    of every chunk live in the workspace, 1 KiB each at d_state = headdim = 16)."""
+    lib = bdssm.load()
+    d = bdssm.dims(1, 64, 16, 16, 1, bdssm.F32, bdssm.F32)
+    L, chunk = 1 << 20, 16
+    need = bdssm.prefix_scan_workspace(d, L, chunk, True, False)
+    assert need > bdssm.STATIC_SCRATCH_BYTES
+    x, y = 1 << 40, 1 << 42   # far apart: no range overlaps, nothing dereferenced
+    s = bdssm.SeqPtrs(x, x + (1 << 38), x + (2 << 38), x + (3 << 38))
+    rc = lib.bdssm_prefix_scan_static(ctypes.byref(d), L, chunk, ctypes.byref(s), FAKE, FAKE + 4096, None,
+                                      y, None, FAKE + 8192, None)
+    assert rc == bdssm.ERR_SCRATCH
+    assert "static scratch" in bdssm.status_str(rc)
+    # the usual validation comes first
+    assert lib.bdssm_prefix_scan_static(None, L, chunk, ctypes.byref(s), FAKE, FAKE, None, y, None,
+                                        FAKE + 8192, None) == bdssm.ERR_NULL
