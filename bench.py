@@ -1,23 +1,31 @@
 """Benchmark of the bidirectional Mamba state hot path on one MI355X.
 
-One step = one pass of the whole hot path over one decoding block of the 700M-shape
-layer (48 heads x 64, d_state 128, ngroups 1, batch 1, bf16 inputs, fp32 state):
-  1. bdssm_prefix_scan over the 8192-token prefix (y in bf16, final state),
-  2. bdssm_state_ops: that cached state in the block step's operand form,
-  3. 64 denoising steps of bdssm_block_step_ops (T = 32, distinct fwd/rev inputs per step)
-     against it,
-  4. bdssm_commit of the block's clean inputs.
-value = active (denoised) tokens per second = steps * 64 * 32 / wall time.
+Headline workload: the 64-stream running set of the 700M-shape layer (48 heads x 64,
+d_state 128, ngroups 1, bf16 inputs, fp32 state). Each stream has its own cached state,
+built by a state-only prefix scan over its own 32,768 tokens. One step is one block cycle
+of the running set:
+  1. bdssm_state_ops: the cached states in the block step's operand form (after the last
+     commit),
+  2. 16 denoising steps of bdssm_block_step_ops over the running set of four 32-token blocks
+     (T = 128, distinct fwd/rev inputs per step),
+  3. bdssm_commit of the oldest 32-token block of every stream (its clean inputs).
+The step is captured as one HIP graph and replayed; value = active (denoised) tokens per
+second = 16 * 64 * 128 per step / wall time. The 64 x 32,768-token prefix build is timed as
+its own part (once per context, not per block).
 
-Per-kernel times come from HIP events recorded on the launch stream around every call in
-the timed region. The roofline object describes the kernel with the largest share of the
-step. Two more workloads are timed the same way and reported under "secondary": the
-64-stream running-set block step (T = 128, HBM-bound) and the 65,536-token prefix scan
-with per-chunk states (matrix-core-bound). The CPU baseline times the float64 oracle on
-the host on one whole step of the same workload.
+The parts are also timed on their own (each as its own graph, warmed before timing, median
+over replays), and the dominant kernel's launches one by one with HIP events on the launch
+stream: the roofline object describes that kernel. Secondary lines: the 700M batch-1 block
+cycle (prefix + 64 steps + commit), the 65,536-token prefix scan with chunk states (the
+matrix-core target), the long-context builds, the decode graph, the convolution state. The
+CPU baseline times the float64 oracle on the host on a bounded sample of the headline step.
+
+Inputs are seeded synthetic draws with the workload's distributions (x ~ N(0,1);
+B, C ~ N(0,1/16); dt = softplus(N(-4,1)) clipped to [1e-3, 0.1]; rounded to bf16), drawn on
+the device for the multi-GB tensors and by the seeded host generator elsewhere; values do
+not change the time.
 """
 import argparse
-import ctypes
 import hashlib
 import json
 import os
@@ -36,12 +44,12 @@ METRIC = "block-step active tokens/s + HBM GB/s; prefix-scan tokens/s + MFMA uti
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--secondary-only", action="store_true",
-                    help="only the 64-stream block step and the 65,536-token prefix scan")
+    ap.add_argument("--only", choices=("headline", "c1", "c2prefix", "builds"),
+                    help="run one workload only (for profiler runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -61,27 +69,10 @@ def src_hash():
     return h.hexdigest()[:16]
 
 
-class Timer:
-    """HIP events around launches on the current stream; durations read after sync."""
-
-    def __init__(self, torch):
-        self.torch = torch
-        self.pairs = {}
-
-    def run(self, name, fn):
-        t = self.torch
-        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
-        a.record()
-        fn()
-        b.record()
-        self.pairs.setdefault(name, []).append((a, b))
-
-    def avg_us(self, name):
-        ps = self.pairs.get(name, [])
-        return 1e3 * sum(a.elapsed_time(b) for a, b in ps) / len(ps) if ps else 0.0
-
-    def total_us(self, name):
-        return self.avg_us(name) * len(self.pairs.get(name, []))
+def median(v):
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
 
 
 def capture(torch, fn):
@@ -98,6 +89,47 @@ def capture(torch, fn):
     return g
 
 
+def warmed(torch, g, warm=2):
+    for _ in range(warm):
+        g.replay()
+    torch.cuda.synchronize()
+    return g
+
+
+def replay_times_us(torch, g, reps):
+    """Per-replay durations (HIP events on the current stream), after the caller warmed g."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        g.replay()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    return [1e3 * ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+
+
+def launch_times_us(torch, fns, reps=1):
+    """Durations of individual launches enqueued back to back on the current stream, one HIP
+    event between each: per fn, the list over reps."""
+    out = [[] for _ in fns]
+    for _ in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+        ev[0].record()
+        for i, fn in enumerate(fns):
+            fn()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        for i in range(len(fns)):
+            out[i].append(1e3 * ev[i].elapsed_time(ev[i + 1]))
+    return out
+
+
+def graph_us(torch, fn, reps=10, warm=2):
+    """Median time of fn() captured as one HIP graph, warmed, replayed `reps` times."""
+    g = warmed(torch, capture(torch, fn), warm)
+    return median(replay_times_us(torch, g, reps))
+
+
+# ---------------------------------------------------------------- algorithmic work
 def block_step_bytes(b, H, P, N, G, T, in_bytes, y_bytes):
     state = b * H * N * P * 4
     inputs = 2 * b * T * (H * P + H + 2 * G * N) * in_bytes + 2 * H * 4
@@ -106,6 +138,10 @@ def block_step_bytes(b, H, P, N, G, T, in_bytes, y_bytes):
 
 def commit_bytes(b, H, P, N, G, T, in_bytes):
     return 2 * b * H * N * P * 4 + b * T * (H * P + H + G * N) * in_bytes + 2 * H * 4
+
+
+def state_ops_bytes(b, H, P, N):
+    return 2 * b * H * N * P * 4
 
 
 def prefix_bytes(b, H, P, N, G, L, Q, in_bytes, y_bytes, chunk_states):
@@ -126,6 +162,15 @@ def prefix_flops(b, H, P, N, G, L, Q):
     nch = -(-L // Q)
     hpg = H // G
     per = 2 * Q * Q * N / hpg + 2 * Q * Q * P + 2 * Q * N * P + 2 * Q * N * P
+    return b * nch * H * per
+
+
+def prefix_flops_causal(b, H, P, N, G, L, Q):
+    """As prefix_flops, counting only the causal half (s <= t) of the quadratic products."""
+    nch = -(-L // Q)
+    hpg = H // G
+    tri = Q * (Q + 1) / 2
+    per = 2 * tri * N / hpg + 2 * tri * P + 2 * Q * N * P + 2 * Q * N * P
     return b * nch * H * per
 
 
@@ -153,6 +198,442 @@ def traffic_for(kernel):
     return e.get("bytes_per_launch")
 
 
+# ---------------------------------------------------------------- inputs on the device
+def dev_seq(torch, gen, b, L, H, P, G, N, with_c=True, chunk_streams=4):
+    """Seeded draws of one segment on the device with the workload's distributions, rounded
+    to bf16 (torch's conversion rounds to nearest even); drawn a few streams at a time so
+    that the float32 temporaries stay small."""
+    bf = torch.bfloat16
+    x = torch.empty((b, L, H, P), dtype=bf, device="cuda")
+    dt = torch.empty((b, L, H), dtype=bf, device="cuda")
+    B = torch.empty((b, L, G, N), dtype=bf, device="cuda")
+    C = torch.empty((b, L, G, N), dtype=bf, device="cuda") if with_c else None
+    for s0 in range(0, b, chunk_streams):
+        s1 = min(b, s0 + chunk_streams)
+        n = s1 - s0
+        x[s0:s1] = torch.randn((n, L, H, P), device="cuda", generator=gen).to(bf)
+        z = torch.randn((n, L, H), device="cuda", generator=gen) - 4.0
+        dt[s0:s1] = torch.nn.functional.softplus(z).clamp(1e-3, 0.1).to(bf)
+        B[s0:s1] = (0.25 * torch.randn((n, L, G, N), device="cuda", generator=gen)).to(bf)
+        if with_c:
+            C[s0:s1] = (0.25 * torch.randn((n, L, G, N), device="cuda", generator=gen)).to(bf)
+    return (x, dt, B, C)
+
+
+# ---------------------------------------------------------------- headline: config 4
+def headline(args, torch, np, bdssm, configs, inputs):
+    cfg = configs.get(4)
+    b, H, P, N, G, L, Q = cfg.batch, cfg.nheads, cfg.headdim, cfg.d_state, cfg.ngroups, cfg.prefix_len, cfg.chunk
+    T, S, TC = cfg.block_len, cfg.steps_per_block, cfg.commit_len
+    A, D = inputs.params(cfg)
+    Ad, Dd = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
+    d = bdssm.dims(b, H, P, N, G, cfg.in_dtype, bdssm.BF16)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4)
+
+    # the cached states: a state-only prefix scan over each stream's 32,768 tokens
+    print("[bench] headline: drawing the 64 x 32,768-token prefixes on the device", file=sys.stderr, flush=True)
+    pre = dev_seq(torch, gen, b, L, H, P, G, N, with_c=False)
+    h = torch.empty((b, H, N, P), device="cuda")
+    wsb = bdssm.prefix_scan_workspace(d, L, Q, False, False)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+
+    def run_prefix():
+        bdssm.prefix_scan(d, L, Q, pre, Ad, Dd, None, None, None, h, ws, wsb)
+
+    run_prefix()
+    torch.cuda.synchronize()
+    pre_us = median(launch_times_us(torch, [run_prefix], reps=5)[0])
+    pre_nb = prefix_state_bytes(b, H, P, N, G, L, 2)
+    h0 = h.clone()
+    del pre
+    torch.cuda.empty_cache()
+
+    print("[bench] headline: drawing the running set's inputs", file=sys.stderr, flush=True)
+    steps = [(dev_seq(torch, gen, b, T, H, P, G, N), dev_seq(torch, gen, b, T, H, P, G, N)) for _ in range(S)]
+    clean = dev_seq(torch, gen, b, TC, H, P, G, N, with_c=False)
+    ops = torch.empty(bdssm.state_ops_bytes(d), dtype=torch.uint8, device="cuda")
+    ys = [torch.empty((b, T, H, P), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
+
+    def run_ops():
+        bdssm.state_ops(d, h, ops)
+
+    step_fns = [(lambda f=f, r=r, y=y: bdssm.block_step_ops(d, T, ops, f, r, Ad, Dd, y))
+                for (f, r), y in zip(steps, ys)]
+
+    def run_steps():
+        for fn in step_fns:
+            fn()
+
+    def run_commit():
+        bdssm.commit(d, TC, clean, Ad, Dd, h)
+
+    parts = (("state_ops", run_ops, 1), ("block_step", run_steps, S), ("commit", run_commit, 1))
+
+    def run_all():
+        for _, fn, _ in parts:
+            fn()
+
+    for _ in range(args.warmup):
+        run_all()
+    torch.cuda.synchronize()
+
+    # the step: one graph replay; exactly K replays on the clock
+    whole = warmed(torch, capture(torch, run_all))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        whole.replay()
+        print(f"[bench] step {i + 1}/{args.steps}", file=sys.stderr, flush=True)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms_per_step = e0.elapsed_time(e1) / args.steps
+    step_med_us = median(replay_times_us(torch, whole, args.steps))
+    del whole
+
+    # the parts, each as its own warmed graph (median over replays)
+    part_us = {}
+    for name, fn, _ in parts:
+        g = warmed(torch, capture(torch, fn))
+        part_us[name] = median(replay_times_us(torch, g, max(args.steps, 5)))
+        del g
+    parts_sum = sum(part_us.values())
+    if any(v > 1.02 * step_med_us for v in part_us.values()):
+        print(f"[bench] inconsistent timing: a part exceeds the whole step ({part_us} vs {step_med_us:.1f} us)",
+              file=sys.stderr, flush=True)
+        sys.exit(3)
+
+    # the dominant kernel's launches one by one (HIP events on the launch stream)
+    per_launch = launch_times_us(torch, step_fns, reps=3)
+    blk_us = median([t for v in per_launch for t in v])
+    ops_us = median(launch_times_us(torch, [run_ops], reps=9)[0])
+    h.copy_(h0)
+    commit_us = median(launch_times_us(torch, [run_commit], reps=9)[0])
+    h.copy_(h0)
+
+    nb_step = block_step_bytes(b, H, P, N, G, T, 2, 2)
+    nb_ops = state_ops_bytes(b, H, P, N)
+    nb_commit = commit_bytes(b, H, P, N, G, TC, 2)
+    nb_all = S * nb_step + nb_ops + nb_commit
+    ms_per_step = 1e3 * wall / args.steps
+    active = S * b * T
+    breakdown = {
+        "state_ops": {"launches_per_step": 1, "graph_us": round(part_us["state_ops"], 3),
+                      "launch_us": round(ops_us, 3), "alg_bytes": nb_ops,
+                      "hbm_frac": round(nb_ops / (ops_us * 1e-6) / HBM_PEAK, 4)},
+        "block_step": {"launches_per_step": S, "graph_us": round(part_us["block_step"], 3),
+                       "launch_us": round(blk_us, 3), "alg_bytes": nb_step,
+                       "hbm_frac": round(nb_step / (blk_us * 1e-6) / HBM_PEAK, 4),
+                       "active_tokens_per_s": round(b * T / (blk_us * 1e-6), 1)},
+        "commit": {"launches_per_step": 1, "graph_us": round(part_us["commit"], 3),
+                   "launch_us": round(commit_us, 3), "alg_bytes": nb_commit,
+                   "hbm_frac": round(nb_commit / (commit_us * 1e-6) / HBM_PEAK, 4)},
+        "parts_sum_us": round(parts_sum, 3), "step_median_us": round(step_med_us, 3),
+    }
+    shares = {"state_ops": ops_us, "block_step": S * blk_us, "commit": commit_us}
+    dom = max(shares, key=shares.get)
+    work = {"state_ops": nb_ops, "block_step": nb_step, "commit": nb_commit}[dom]
+    avg = {"state_ops": ops_us, "block_step": blk_us, "commit": commit_us}[dom]
+    kname = {"state_ops": "k_state_ops", "block_step": "k_block_bw", "commit": "k_state"}[dom]
+    roof = make_roofline("hbm", work, avg, traffic_for({"block_step": "block_step_c4"}.get(dom, dom)))
+    roof.update({"kernel": kname, "part": dom, "work_per_launch": work, "avg_launch_us": round(avg, 3),
+                 "launches_per_step": S if dom == "block_step" else 1})
+    out = {"metric": METRIC, "value": round(active / (wall / args.steps), 1), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+           "gpu_ms_per_step": round(gpu_ms_per_step, 4),
+           "timing": "one HIP graph replay per step (operand form of the cached states, 16 block steps, commit "
+                     "of the oldest block); exactly `steps` replays on the clock; parts timed as their own warmed "
+                     "graphs and the kernels launch by launch with HIP events on the launch stream",
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded device draws with the workload's distributions; random-init layer parameters)",
+           "config": {"workload": "running set of 64 independent streams, 700M-shape Mamba-2 layer (48 heads x 64, "
+                                  "d_state 128, ngroups 1), bf16 inputs, fp32 cached state per stream built from "
+                                  "32,768 prefix tokens; one step = operand form of the 64 cached states + 16 "
+                                  "block steps of the 4 x 32 = 128-token window + commit of the oldest 32 tokens",
+                      "global_batch": b, "seq_len": L, "block_len": T, "steps_per_block": S, "commit_len": TC,
+                      "parallelism": "none (1 GPU)"},
+           "roofline": roof, "breakdown": breakdown,
+           "step_hbm_frac": round(nb_all / (step_med_us * 1e-6) / HBM_PEAK, 4), "step_alg_bytes": nb_all,
+           "prefix_build": {"workload": "state-only prefix scan building the 64 cached states, 64 x 32,768 tokens",
+                            "avg_us": round(pre_us, 1), "prefix_tokens_per_s": round(b * L / (pre_us * 1e-6), 1),
+                            "alg_bytes": pre_nb,
+                            "roofline": make_roofline("hbm", pre_nb, pre_us, traffic_for("prefix_build_c4"))}}
+    del steps, clean, ys, ops, h, h0, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------- config 1: batch-1 block cycle
+def config1(args, torch, np, bdssm, configs, inputs):
+    """The 700M batch-1 block cycle as one graph: the 8192-token prefix scan (bf16 y), the
+    operand form, 64 block steps (T = 32), the commit; parts as warmed graphs."""
+    cfg = configs.get(1)
+    b, H, P, N, G, L, Q, T = (cfg.batch, cfg.nheads, cfg.headdim, cfg.d_state, cfg.ngroups,
+                              cfg.prefix_len, cfg.chunk, cfg.block_len)
+    S = cfg.steps_per_block
+    A, D = inputs.params(cfg)
+    d = bdssm.dims(b, H, P, N, G, cfg.in_dtype, bdssm.BF16)
+    Ad, Dd = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
+    pre = bdssm.seq_to_device(inputs.prefix(cfg))
+    steps = [(bdssm.seq_to_device(inputs.block(cfg, 0, s, inputs.FWD)),
+              bdssm.seq_to_device(inputs.block(cfg, 0, s, inputs.REV))) for s in range(S)]
+    clean = bdssm.seq_to_device(inputs.block(cfg, 0, 0, inputs.CLEAN))
+    h = torch.empty((b, H, N, P), device="cuda")
+    h_ops = torch.empty(bdssm.state_ops_bytes(d), dtype=torch.uint8, device="cuda")
+    y_pre = torch.empty((b, L, H, P), dtype=torch.bfloat16, device="cuda")
+    y_blk = [torch.empty((b, T, H, P), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
+    wsb = bdssm.prefix_scan_workspace(d, L, Q, True, False)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+
+    def run_prefix():
+        bdssm.prefix_scan(d, L, Q, pre, Ad, Dd, None, y_pre, None, h, ws, wsb)
+
+    def run_ops():
+        bdssm.state_ops(d, h, h_ops)
+
+    def run_blocks():
+        for s in range(S):
+            f, r = steps[s]
+            bdssm.block_step_ops(d, T, h_ops, f, r, Ad, Dd, y_blk[s])
+
+    def run_blocks_fp32():
+        for s in range(S):
+            f, r = steps[s]
+            bdssm.block_step(d, T, h, f, r, Ad, Dd, y_blk[s])
+
+    def run_commit():
+        bdssm.commit(d, T, clean, Ad, Dd, h)
+
+    parts = (("prefix_scan", run_prefix, 1), ("state_ops", run_ops, 1), ("block_step", run_blocks, S),
+             ("commit", run_commit, 1))
+
+    def run_all():
+        for _, fn, _ in parts:
+            fn()
+
+    for _ in range(2):
+        run_all()
+    whole = warmed(torch, capture(torch, run_all))
+    step_us = median(replay_times_us(torch, whole, 20))
+    del whole
+    res = {"workload": "700M shape, batch 1: 8192-token prefix scan (bf16 y) + operand form + 64 block steps "
+                       "(T=32) + commit, one graph", "step_us": round(step_us, 2),
+           "active_tokens_per_s": round(S * b * T / (step_us * 1e-6), 1)}
+    for name, fn, n in parts:
+        us = graph_us(torch, fn, reps=20)
+        if us > 1.02 * step_us:
+            print(f"[bench] inconsistent timing: config 1 {name} {us:.1f} us > step {step_us:.1f} us",
+                  file=sys.stderr, flush=True)
+            sys.exit(3)
+        res[name + "_us"] = round(us / n, 3)
+    nb = block_step_bytes(b, H, P, N, G, T, 2, 2)
+    res["block_step_hbm_frac"] = round(nb / (res["block_step_us"] * 1e-6) / HBM_PEAK, 4)
+    res["block_step_from_fp32_state_us"] = round(graph_us(torch, run_blocks_fp32, reps=20) / S, 3)
+    pf = prefix_flops(b, H, P, N, G, L, Q)
+    res["prefix_mfma_frac"] = round(pf / (res["prefix_scan_us"] * 1e-6) / MFMA_BF16_PEAK, 4)
+    res["prefix_mfma_frac_causal"] = round(prefix_flops_causal(b, H, P, N, G, L, Q) /
+                                           (res["prefix_scan_us"] * 1e-6) / MFMA_BF16_PEAK, 4)
+    # the same block through the library's decode graph (64 steps + commit + operand form)
+    dg = bdssm.DecodeGraph(d, T, h, [f for f, _ in steps], [r for _, r in steps], Ad, Dd, y_blk, clean,
+                           h_ops=h_ops)
+    for _ in range(2):
+        dg.launch()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        dg.launch()
+    e1.record()
+    torch.cuda.synchronize()
+    dg.close()
+    res["decode_graph_us_per_block"] = round(1e3 * e0.elapsed_time(e1) / 20, 2)
+    # a single launch between synchronizations
+    ts = []
+    for i in range(25):
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        bdssm.block_step_ops(d, T, h_ops, steps[0][0], steps[0][1], Ad, Dd, y_blk[0])
+        a1.record()
+        torch.cuda.synchronize()
+        if i >= 5:
+            ts.append(1e3 * a0.elapsed_time(a1))
+    res["block_step_single_launch_us"] = round(median(ts), 3)
+    return res
+
+
+# ---------------------------------------------------------------- config 2: prefix scan
+def config2_prefix(torch, np, bdssm, configs, inputs, reps=10):
+    c2 = configs.get(2)
+    b, H, P, N, G, L, Q = c2.batch, c2.nheads, c2.headdim, c2.d_state, c2.ngroups, c2.prefix_len, c2.chunk
+    A, D = inputs.params(c2)
+    Ad, Dd = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
+    d = bdssm.dims(b, H, P, N, G, c2.in_dtype, bdssm.BF16)
+    pre = bdssm.seq_to_device(inputs.prefix(c2))
+    y = torch.empty((b, L, H, P), dtype=torch.bfloat16, device="cuda")
+    cs = torch.empty((b, -(-L // Q), H, N, P), device="cuda")
+    ho = torch.empty((b, H, N, P), device="cuda")
+    wsb = bdssm.prefix_scan_workspace(d, L, Q, True, True)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    fn = lambda: bdssm.prefix_scan(d, L, Q, pre, Ad, Dd, None, y, cs, ho, ws, wsb)
+    fn()
+    torch.cuda.synchronize()
+    us = median(launch_times_us(torch, [fn], reps=reps)[0])
+    fl = prefix_flops(b, H, P, N, G, L, Q)
+    nb = prefix_bytes(b, H, P, N, G, L, Q, 2, 2, True)
+    return {"workload": "prefix scan, 350M shape (32 heads x 64, d_state 128), 65,536 tokens, chunk 256, bf16 y + "
+                        "fp32 chunk states", "avg_us": round(us, 3),
+            "prefix_tokens_per_s": round(b * L / (us * 1e-6), 1),
+            "roofline": make_roofline("mfma", fl, us, traffic_for("prefix_scan_c2")),
+            "mfma_frac_causal_count": round(prefix_flops_causal(b, H, P, N, G, L, Q) / (us * 1e-6) / MFMA_BF16_PEAK, 4),
+            "hbm_frac": round(nb / (us * 1e-6) / HBM_PEAK, 4), "alg_bytes": nb, "flops_dense": fl,
+            "flops_causal": prefix_flops_causal(b, H, P, N, G, L, Q)}
+
+
+def builds(torch, np, bdssm, configs, inputs):
+    """The state-only prefix build of the long-context cache (262,144 tokens x 80 heads, 8
+    groups) and the config-2 commit chain."""
+    res = {}
+    c = configs.get(3)
+    b, H, P, N, G, L, Q = c.batch, c.nheads, c.headdim, c.d_state, c.ngroups, c.prefix_len, c.chunk
+    A, D = inputs.params(c)
+    Adv, Ddv = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(3)
+    seq = dev_seq(torch, gen, b, L, H, P, G, N, with_c=False, chunk_streams=1)
+    dv = bdssm.dims(b, H, P, N, G, 1, bdssm.BF16)
+    hv = torch.empty((b, H, N, P), device="cuda")
+    wsb = bdssm.prefix_scan_workspace(dv, L, Q, False, False)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    fn = lambda: bdssm.prefix_scan(dv, L, Q, seq, Adv, Ddv, None, None, None, hv, ws, wsb)
+    fn()
+    torch.cuda.synchronize()
+    us = median(launch_times_us(torch, [fn], reps=7)[0])
+    nb = prefix_state_bytes(b, H, P, N, G, L, 2)
+    res["prefix_build_config3"] = {"workload": "state-only prefix scan, 3B shape (80 heads x 64, 8 groups), "
+                                               "262,144 tokens", "avg_us": round(us, 1),
+                                   "prefix_tokens_per_s": round(b * L / (us * 1e-6), 1),
+                                   "roofline": make_roofline("hbm", nb, us, traffic_for("prefix_build_c3")),
+                                   "alg_bytes": nb}
+    del seq, hv, ws
+    # the block step of the 3B shape (64 steps with distinct inputs in one graph)
+    T, S = c.block_len, c.steps_per_block
+    d3 = bdssm.dims(b, H, P, N, G, 1, bdssm.BF16)
+    st = [(dev_seq(torch, gen, b, T, H, P, G, N), dev_seq(torch, gen, b, T, H, P, G, N)) for _ in range(S)]
+    hh = torch.randn((b, H, N, P), device="cuda", generator=gen) * 0.05
+    ho = torch.empty(bdssm.state_ops_bytes(d3), dtype=torch.uint8, device="cuda")
+    bdssm.state_ops(d3, hh, ho)
+    ys = [torch.empty((b, T, H, P), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
+    us = graph_us(torch, lambda: [bdssm.block_step_ops(d3, T, ho, f, r, Adv, Ddv, y) for (f, r), y in zip(st, ys)]) / S
+    nb = block_step_bytes(b, H, P, N, G, T, 2, 2)
+    res["block_step_config3"] = {"workload": "block step, 3B shape, T=32, 64 distinct inputs in one graph",
+                                 "us_per_step": round(us, 3), "active_tokens_per_s": round(b * T / (us * 1e-6), 1),
+                                 "hbm_frac": round(nb / (us * 1e-6) / HBM_PEAK, 4), "alg_bytes": nb}
+    # commit chain, config 2: 2048 commits of 32 tokens over the 65,536-token prefix
+    c2 = configs.get(2)
+    b, H, P, N, G, L, T = c2.batch, c2.nheads, c2.headdim, c2.d_state, c2.ngroups, c2.prefix_len, c2.commit_len
+    A, D = inputs.params(c2)
+    Ad2, Dd2 = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
+    d2 = bdssm.dims(b, H, P, N, G, c2.in_dtype, bdssm.BF16)
+    pre = dev_seq(torch, gen, b, L, H, P, G, N, with_c=False)
+    blocks = [tuple(None if t is None else t[:, k * T:(k + 1) * T].contiguous() for t in pre) for k in range(L // T)]
+    hc = torch.zeros((b, H, N, P), device="cuda")
+    us = graph_us(torch, lambda: [bdssm.commit(d2, T, blk, Ad2, Dd2, hc) for blk in blocks], reps=3, warm=1)
+    res["commit_chain_config2"] = {"workload": "2,048 commits of 32 tokens (350M shape), one graph",
+                                   "us_per_commit": round(us / len(blocks), 3),
+                                   "tokens_per_s": round(L / (us * 1e-6), 1)}
+    return res
+
+
+def conv_workloads(torch, bdssm, configs, inputs, reps=20):
+    """The convolution state at the 700M shape (width 4, SiLU): 64 block steps through
+    bdssm_block_step_conv in one graph, and the forward convolution of the 8192-token prefix
+    that writes the conv state (HBM-bound)."""
+    cfg = configs.get(1)
+    b, H, P, N, G, T, L = cfg.batch, cfg.nheads, cfg.headdim, cfg.d_state, cfg.ngroups, cfg.block_len, cfg.prefix_len
+    W = 4
+    ch = H * P + 2 * G * N
+    A, D = inputs.params(cfg)
+    Ad, Dd = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
+    d = bdssm.dims(b, H, P, N, G, cfg.in_dtype, bdssm.BF16)
+    wf, bf = (torch.from_numpy(a).cuda() for a in inputs.conv_params(cfg, W, inputs.FWD))
+    wr, br = (torch.from_numpy(a).cuda() for a in inputs.conv_params(cfg, W, inputs.REV))
+    cpf, cpr = bdssm.conv_params(wf, bf, 1), bdssm.conv_params(wr, br, 1)
+    cs = torch.zeros((b, W - 1, ch), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(2 * bdssm.conv_workspace(d, T), dtype=torch.uint8, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    S = cfg.steps_per_block
+    steps = [(dev_seq(torch, gen, b, T, H, P, G, N), dev_seq(torch, gen, b, T, H, P, G, N)) for _ in range(S)]
+    h = torch.randn((b, H, N, P), device="cuda", generator=gen) * 0.05
+    ys = [torch.empty((b, T, H, P), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
+    step_us = graph_us(torch, lambda: [bdssm.block_step_conv(d, T, cpf, cpr, h, cs, f, r, Ad, Dd, y, ws)
+                                       for (f, r), y in zip(steps, ys)], reps=reps) / S
+    pre = dev_seq(torch, gen, b, L, H, P, G, N)
+    post = tuple(torch.empty_like(t) for t in pre)
+    cso = torch.empty_like(cs)
+    fn = lambda: bdssm.conv(d, L, cpf, False, None, pre, post, cso)
+    fn()
+    torch.cuda.synchronize()
+    conv_us = median(launch_times_us(torch, [fn], reps=reps)[0])
+    nb = 2 * b * L * ch * 2 + ch * (W + 1) * 4 + 2 * b * (W - 1) * ch * 2
+    return {"block_step_conv": {"workload": "64 block steps (T=32) on unconvolved inputs, width-4 SiLU "
+                                            "convolution of x, B, C per direction, 700M shape, one graph",
+                                "us_per_step": round(step_us, 3),
+                                "active_tokens_per_s": round(b * T / (step_us * 1e-6), 1)},
+            "prefix_conv": {"workload": "forward convolution of an 8192-token prefix (x, B, C; width 4, SiLU) "
+                                        "writing the conv state, 700M shape, bf16",
+                            "avg_us": round(conv_us, 3), "alg_bytes": nb,
+                            "roofline": make_roofline("hbm", nb, conv_us, None)}}
+
+
+# ---------------------------------------------------------------- CPU baseline
+def cpu_baseline(np, configs, inputs):
+    """The float64 oracle on the host cores, on a bounded sample of the headline step: the
+    16 block steps of the running set (T = 128) and the oldest-block commit, for 4 streams on
+    one thread and for all 64 streams on all threads (threads over (stream, head) pairs).
+    Each figure is active tokens of the sample per second of host time."""
+    import oracle
+    cfg = configs.get(4)
+    A, D = inputs.params(cfg)
+    H, P, N = cfg.nheads, cfg.headdim, cfg.d_state
+    S = cfg.steps_per_block
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = os.cpu_count() or 1
+    all_threads = max(1, min(oracle.max_threads(), affinity))
+
+    def run(nstreams, nthreads):
+        streams = list(range(nstreams))
+        rng = np.random.default_rng(5)
+        h = rng.standard_normal((nstreams, H, N, P)) * 0.05
+        steps = [(inputs.block(cfg, 0, s, inputs.FWD, streams=streams),
+                  inputs.block(cfg, 0, s, inputs.REV, streams=streams)) for s in range(S)]
+        clean = inputs.block(cfg, 0, 0, inputs.CLEAN, streams=streams)
+        t0 = time.perf_counter()
+        for f, r in steps:
+            oracle.block_step(h, f, r, A, D, nthreads=nthreads)
+        oracle.commit(h, clean, A, D, nthreads=nthreads)
+        wall = time.perf_counter() - t0
+        return nstreams * S * cfg.block_len / wall, wall
+
+    few = 4
+    one, w1 = run(few, 1)
+    many_streams = cfg.batch
+    allv, wall_all = run(many_streams, all_threads)
+    return {"value": round(allv, 2), "unit": "tokens/s", "cores": all_threads, "kind": "oracle",
+            "sample": f"the headline step's 16 block steps (T=128) + oldest-block commit for {many_streams} of the "
+                      f"64 streams on {all_threads} threads ({wall_all:.1f} s of host time); rate = active tokens "
+                      "of the sample per second",
+            "single_thread": {"value": round(one, 2), "unit": "tokens/s", "cores": 1,
+                              "sample": f"the same for {few} streams on 1 thread ({w1:.1f} s)"},
+            "host_cpus_in_affinity_mask": affinity, "host_cpu_count": os.cpu_count(),
+            "openmp_max_threads": oracle.max_threads()}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -176,452 +657,24 @@ def main():
         return
 
     bdssm.load()
-    if args.secondary_only:
-        print(json.dumps({"secondary": secondary(torch, np, bdssm, configs, inputs)}), flush=True)
+    if args.only:
+        fn = {"headline": lambda: headline(args, torch, np, bdssm, configs, inputs),
+              "c1": lambda: config1(args, torch, np, bdssm, configs, inputs),
+              "c2prefix": lambda: config2_prefix(torch, np, bdssm, configs, inputs),
+              "builds": lambda: builds(torch, np, bdssm, configs, inputs)}.get(args.only)
+        print(json.dumps({args.only: fn()}), flush=True)
         return
-    cfg = configs.get(1)
-    b, H, P, N, G, L, Q, T = (cfg.batch, cfg.nheads, cfg.headdim, cfg.d_state, cfg.ngroups,
-                              cfg.prefix_len, cfg.chunk, cfg.block_len)
-    S = cfg.steps_per_block
-    A, D = inputs.params(cfg)
-    d = bdssm.dims(b, H, P, N, G, cfg.in_dtype, bdssm.BF16)
-    Ad, Dd = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
-    pre_np = inputs.prefix(cfg)
-    pre = bdssm.seq_to_device(pre_np)
-    steps_np = [(inputs.block(cfg, 0, s, inputs.FWD), inputs.block(cfg, 0, s, inputs.REV)) for s in range(S)]
-    steps = [(bdssm.seq_to_device(f), bdssm.seq_to_device(r)) for f, r in steps_np]
-    clean_np = inputs.block(cfg, 0, 0, inputs.CLEAN)
-    clean = bdssm.seq_to_device(clean_np)
-    h = torch.empty((b, H, N, P), device="cuda")
-    h_ops = torch.empty(bdssm.state_ops_bytes(d), dtype=torch.uint8, device="cuda")
-    y_pre = torch.empty((b, L, H, P), dtype=torch.bfloat16, device="cuda")
-    y_blk = [torch.empty((b, T, H, P), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
-    wsb = bdssm.prefix_scan_workspace(d, L, Q, True, False)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
-
-    def run_prefix():
-        bdssm.prefix_scan(d, L, Q, pre, Ad, Dd, None, y_pre, None, h, ws, wsb)
-
-    def run_state_ops():
-        bdssm.state_ops(d, h, h_ops)
-
-    def run_blocks():
-        for s in range(S):
-            f, r = steps[s]
-            bdssm.block_step_ops(d, T, h_ops, f, r, Ad, Dd, y_blk[s])
-
-    def run_blocks_fp32_state():
-        for s in range(S):
-            f, r = steps[s]
-            bdssm.block_step(d, T, h, f, r, Ad, Dd, y_blk[s])
-
-    def run_commit():
-        bdssm.commit(d, T, clean, Ad, Dd, h)
-
-    parts = (("prefix_scan", run_prefix), ("state_ops", run_state_ops), ("block_step", run_blocks),
-             ("commit", run_commit))
-    for _ in range(args.warmup):
-        for _, fn in parts:
-            fn()
-    torch.cuda.synchronize()
-
-    # A step is one HIP graph replay of the whole path (prefix scan, operand form of the
-    # state, the 64 block steps, the commit), so launch overhead is off the clock, as in the
-    # pages' own graph-captured decoding measurements; `value` and `ms_per_step` time exactly
-    # K replays. The parts are then timed on their own: the same work as one graph per part,
-    # with HIP events between the replays on the launch stream; the block-step average
-    # includes the gaps between the 64 back-to-back launches of its graph.
-    def run_all():
-        for _, fn in parts:
-            fn()
-
-    whole = capture(torch, run_all)
-    for _ in range(2):
-        whole.replay()
-    torch.cuda.synchronize()
-    e_all = [torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-    t0 = time.perf_counter()
-    e_all[0].record()
-    for i in range(args.steps):
-        whole.replay()
-        print(f"[bench] step {i + 1}/{args.steps}", file=sys.stderr, flush=True)
-    e_all[1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms_per_step = e_all[0].elapsed_time(e_all[1]) / args.steps
-    del whole
-
-    graphs = [capture(torch, fn) for _, fn in parts]
-    names = [k for k, _ in parts]
-    ev = []
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)]
-        e[0].record()
-        for g, en in zip(graphs, e[1:]):
-            g.replay()
-            en.record()
-        ev.append(e)
-    torch.cuda.synchronize()
-    per_step = {"prefix_scan": 1, "state_ops": 1, "block_step": S, "commit": 1}
-    part_ms = {k: sum(e[j].elapsed_time(e[j + 1]) for e in ev) / args.steps for j, k in enumerate(names)}
-    parts_ms = sum(e[0].elapsed_time(e[len(parts)]) for e in ev) / args.steps
-    avg_us = {k: 1e3 * part_ms[k] / per_step[k] for k in part_ms}
-    del graphs
-    fp32_state_us = graph_us(torch, run_blocks_fp32_state) / S
-    timing = ("one HIP graph replay per step (prefix scan, state operand form, 64 block steps, commit); "
-              "per-part times from the same work as one graph per part with HIP events between them on "
-              "the launch stream")
-    ms_per_step = 1e3 * wall / args.steps
-    active = args.steps * S * b * T
-    value = active / wall
-
-    ib, yb = 2, 2
-    k_bytes = {"block_step": block_step_bytes(b, H, P, N, G, T, ib, yb),
-               "state_ops": 2 * b * H * N * P * 4,
-               "commit": commit_bytes(b, H, P, N, G, T, ib),
-               "prefix_scan": prefix_bytes(b, H, P, N, G, L, Q, ib, yb, False)}
-    pf = prefix_flops(b, H, P, N, G, L, Q)
-    breakdown = {}
-    for k in names:
-        us = avg_us[k]
-        breakdown[k] = {"launches_per_step": per_step[k], "avg_us": round(us, 3),
-                        "share_of_step": round(part_ms[k] / parts_ms, 4),
-                        "alg_bytes": k_bytes[k],
-                        "hbm_frac": round(k_bytes[k] / (us * 1e-6) / HBM_PEAK, 4)}
-    breakdown["prefix_scan"]["tokens_per_s"] = round(b * L / (avg_us["prefix_scan"] * 1e-6), 1)
-    breakdown["prefix_scan"]["mfma_frac"] = round(pf / (avg_us["prefix_scan"] * 1e-6) / MFMA_BF16_PEAK, 5)
-    breakdown["block_step"]["active_tokens_per_s"] = round(b * T / (avg_us["block_step"] * 1e-6), 1)
-    breakdown["block_step"]["from_fp32_state_us"] = round(fp32_state_us, 3)
-    dom = max(part_ms, key=part_ms.get)
-    if dom == "prefix_scan":
-        roof = make_roofline("mfma", pf, avg_us[dom], traffic_for(dom))
-    else:
-        roof = make_roofline("hbm", k_bytes[dom], avg_us[dom], traffic_for(dom))
-    roof["kernel"] = dom
-    roof["work_per_launch"] = pf if dom == "prefix_scan" else k_bytes[dom]
-
-    out = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-           "gpu_ms_per_step": round(gpu_ms_per_step, 4),
-           "timing": timing,
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-           "data": "synthetic (seeded; random-init layer parameters)",
-           "config": {"workload": "700M-shape Mamba-2 layer, 48 heads x 64, d_state 128, ngroups 1, "
-                                  "batch 1, bf16 inputs, fp32 state: 8192-token prefix scan + "
-                                  "state operand form + 64 block steps (T=32) + commit per step",
-                      "global_batch": b, "seq_len": L, "block_len": T, "steps_per_block": S,
-                      "parallelism": "none (1 GPU)"},
-           "roofline": roof, "breakdown": breakdown}
-
-    # the same 64 block steps + commit (+ the operand form of the advanced state) through the
-    # library's decode-loop graph (one HIP graph recorded by bdssm_decode_graph_create),
-    # timed per replay
-    dg = bdssm.DecodeGraph(d, T, h, [f for f, _ in steps], [r for _, r in steps], Ad, Dd, y_blk, clean,
-                           h_ops=h_ops)
-    for _ in range(2):
-        dg.launch()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 20
-    e0.record()
-    for _ in range(reps):
-        dg.launch()
-    e1.record()
-    torch.cuda.synchronize()
-    blk_us = 1e3 * e0.elapsed_time(e1) / reps
-    dg.close()
-    out["decode_graph"] = {"workload": "bdssm_decode_graph: 64 block steps (T=32) + commit of one block "
-                                       "+ operand form of the advanced state, 700M shape, replayed back "
-                                       "to back",
-                           "us_per_block": round(blk_us, 2), "us_per_launch": round(blk_us / (S + 2), 3),
-                           "active_tokens_per_s": round(S * b * T / (blk_us * 1e-6), 1)}
-
+    out = headline(args, torch, np, bdssm, configs, inputs)
     if not args.no_secondary:
-        out["conv_state"] = conv_workloads(torch, bdssm, cfg, inputs, d, h, steps, Ad, Dd, y_blk, pre, L,
-                                           fp32_state_us)
-        out["secondary"] = secondary(torch, np, bdssm, configs, inputs)
-        out["extra"] = extra(torch, np, bdssm, configs, inputs)
+        print("[bench] secondary workloads", file=sys.stderr, flush=True)
+        out["secondary"] = {"config1_block_cycle": config1(args, torch, np, bdssm, configs, inputs),
+                            "config2_prefix_scan": config2_prefix(torch, np, bdssm, configs, inputs)}
+        out["secondary"].update(builds(torch, np, bdssm, configs, inputs))
+        out["secondary"]["conv_state"] = conv_workloads(torch, bdssm, configs, inputs)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(np, cfg, A, D, pre_np, steps_np, clean_np)
+        print("[bench] CPU baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(np, configs, inputs)
     print(json.dumps(out), flush=True)
-
-
-def conv_bytes(b, H, P, N, G, L, W, in_bytes, state):
-    ch = H * P + 2 * G * N
-    return 2 * b * L * ch * in_bytes + ch * (W + 1) * 4 + (2 * b * (W - 1) * ch * in_bytes if state else 0)
-
-
-def conv_workloads(torch, bdssm, cfg, inputs, d, h, steps, Ad, Dd, y_blk, pre, L, plain_step_us, reps=20):
-    """The convolution state at the 700M shape (width 4, SiLU): the 64 block steps through
-    bdssm_block_step_conv (both directions' convolutions in one launch, then the block step),
-    captured in one graph like the main step, and the forward convolution of the 8192-token
-    prefix that writes the conv state (HBM-bound)."""
-    b, H, P, N, G, T = cfg.batch, cfg.nheads, cfg.headdim, cfg.d_state, cfg.ngroups, cfg.block_len
-    W = 4
-    ch = H * P + 2 * G * N
-    wf, bf = (torch.from_numpy(a).cuda() for a in inputs.conv_params(cfg, W, inputs.FWD))
-    wr, br = (torch.from_numpy(a).cuda() for a in inputs.conv_params(cfg, W, inputs.REV))
-    cpf, cpr = bdssm.conv_params(wf, bf, 1), bdssm.conv_params(wr, br, 1)
-    cs = torch.zeros((b, W - 1, ch), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(2 * bdssm.conv_workspace(d, T), dtype=torch.uint8, device="cuda")
-    S = len(steps)
-
-    def run_steps():
-        for s in range(S):
-            f, r = steps[s]
-            bdssm.block_step_conv(d, T, cpf, cpr, h, cs, f, r, Ad, Dd, y_blk[s], ws)
-
-    g = capture(torch, run_steps)
-    for _ in range(2):
-        g.replay()
-    torch.cuda.synchronize()
-    tm = Timer(torch)
-    for _ in range(reps):
-        tm.run("k", g.replay)
-    torch.cuda.synchronize()
-    step_us = tm.avg_us("k") / S
-    post = tuple(torch.empty_like(t) for t in pre)
-    cso = torch.empty_like(cs)
-    tm = Timer(torch)
-    for i in range(reps + 3):
-        (tm if i >= 3 else Timer(torch)).run("c", lambda: bdssm.conv(d, L, cpf, False, None, pre, post, cso))
-    torch.cuda.synchronize()
-    conv_us = tm.avg_us("c")
-    nb = conv_bytes(b, H, P, N, G, L, W, 2, True)
-    return {"block_step_conv": {"workload": "64 block steps (T=32) on unconvolved inputs, width-4 SiLU "
-                                            "convolution of x, B, C per direction, 700M shape, one graph",
-                                "us_per_step": round(step_us, 3), "plain_block_step_us": round(plain_step_us, 3),
-                                "active_tokens_per_s": round(b * T / (step_us * 1e-6), 1)},
-            "prefix_conv": {"workload": "forward convolution of an 8192-token prefix (x, B, C; width 4, "
-                                        "SiLU) writing the conv state, 700M shape, bf16",
-                            "avg_us": round(conv_us, 3), "alg_bytes": nb,
-                            "roofline": make_roofline("hbm", nb, conv_us, None)}}
-
-
-def prefix_flops_causal(b, H, P, N, G, L, Q):
-    """As prefix_flops, counting only the causal half (s <= t) of the quadratic products."""
-    nch = -(-L // Q)
-    hpg = H // G
-    tri = Q * (Q + 1) / 2
-    per = 2 * tri * N / hpg + 2 * tri * P + 2 * Q * N * P + 2 * Q * N * P
-    return b * nch * H * per
-
-
-def graph_us(torch, fn, reps=10, warm=2):
-    """Average time of fn() captured as one HIP graph, replayed `reps` times (HIP events)."""
-    g = capture(torch, fn)
-    for _ in range(warm):
-        g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return 1e3 * e0.elapsed_time(e1) / reps
-
-
-def extra(torch, np, bdssm, configs, inputs):
-    """The remaining figures of the measurement plan: the block step as a single launch
-    (median of 20 after 5 warm-ups), with every buffer cold (rotation over more than the
-    256 MiB last-level cache) and cache-resident, at configs 0 and 3; the state-only prefix
-    builds of configs 3 and 4; the commit chain."""
-    res = {}
-    c1 = configs.get(1)
-    b, H, P, N, G, T = c1.batch, c1.nheads, c1.headdim, c1.d_state, c1.ngroups, c1.block_len
-    A, D = inputs.params(c1)
-    Ad, Dd = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
-    d = bdssm.dims(b, H, P, N, G, c1.in_dtype, bdssm.BF16)
-    f = bdssm.seq_to_device(inputs.block(c1, 0, 0, inputs.FWD))
-    r = bdssm.seq_to_device(inputs.block(c1, 0, 0, inputs.REV))
-    def ops_of(dd, hh):
-        o = torch.empty(bdssm.state_ops_bytes(dd), dtype=torch.uint8, device="cuda")
-        bdssm.state_ops(dd, hh, o)
-        return o
-
-    h = ops_of(d, torch.randn((b, H, N, P), device="cuda") * 0.05)
-    y = torch.empty((b, T, H, P), dtype=torch.bfloat16, device="cuda")
-    ts = []
-    for i in range(25):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        bdssm.block_step_ops(d, T, h, f, r, Ad, Dd, y)
-        e1.record()
-        torch.cuda.synchronize()
-        if i >= 5:
-            ts.append(1e3 * e0.elapsed_time(e1))
-    res["block_step_single_launch"] = {"workload": "700M shape, T=32, state in operand form, one launch "
-                                                   "between synchronizations",
-                                       "median_us": round(float(np.median(ts)), 3)}
-    # cold: 256 sets of (state, inputs, y), about 540 MB, one launch each; warm: one set
-    nset = 256
-    sets = []
-    for k in range(nset):
-        sets.append((ops_of(d, torch.randn((b, H, N, P), device="cuda") * 0.05),
-                     tuple(t.clone() for t in f), tuple(t.clone() for t in r),
-                     torch.empty_like(y)))
-    cold = graph_us(torch, lambda: [bdssm.block_step_ops(d, T, hh, ff, rr, Ad, Dd, yy) for hh, ff, rr, yy in sets]) / nset
-    warm = graph_us(torch, lambda: [bdssm.block_step_ops(d, T, h, f, r, Ad, Dd, y) for _ in range(nset)]) / nset
-    nb = block_step_bytes(b, H, P, N, G, T, 2, 2)
-    res["block_step_cold_warm"] = {"workload": "700M shape, T=32, state in operand form, 256 launches in one graph",
-                                   "cold_us": round(cold, 3), "warm_us": round(warm, 3),
-                                   "rotation_bytes": nset * nb}
-    del sets
-    # configs 3 and 0: 64 (resp. 4) steps with distinct inputs in one graph
-    for ci in (3, 0):
-        c = configs.get(ci)
-        b, H, P, N, G, T = c.batch, c.nheads, c.headdim, c.d_state, c.ngroups, c.block_len
-        A, D = inputs.params(c)
-        Ad3, Dd3 = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
-        yd = bdssm.BF16 if c.in_dtype == 1 else bdssm.F32
-        d3 = bdssm.dims(b, H, P, N, G, c.in_dtype, yd)
-        S = c.steps_per_block
-        st = [(bdssm.seq_to_device(inputs.block(c, 0, k, inputs.FWD)), bdssm.seq_to_device(inputs.block(c, 0, k, inputs.REV)))
-              for k in range(S)]
-        hh = torch.randn((b, H, N, P), device="cuda") * 0.05
-        ys = [torch.empty((b, T, H, P), dtype=torch.bfloat16 if yd == bdssm.BF16 else torch.float32, device="cuda")
-              for _ in range(S)]
-        if bdssm.state_ops_bytes(d3) != ctypes.c_size_t(-1).value and c.in_dtype == 1:
-            ho = ops_of(d3, hh)   # the operand form where the shape has one
-            us = graph_us(torch, lambda: [bdssm.block_step_ops(d3, T, ho, ff, rr, Ad3, Dd3, yy)
-                                          for (ff, rr), yy in zip(st, ys)]) / S
-        else:
-            us = graph_us(torch, lambda: [bdssm.block_step(d3, T, hh, ff, rr, Ad3, Dd3, yy)
-                                          for (ff, rr), yy in zip(st, ys)]) / S
-        ib = 2 if c.in_dtype == 1 else 4
-        nb = block_step_bytes(b, H, P, N, G, T, ib, ib)
-        res[f"block_step_config{ci}"] = {"workload": c.name, "us_per_step": round(us, 3),
-                                         "active_tokens_per_s": round(b * T / (us * 1e-6), 1),
-                                         "hbm_frac": round(nb / (us * 1e-6) / HBM_PEAK, 4), "alg_bytes": nb}
-    # state-only prefix builds of configs 3 and 4 (the long-context cache: 262,144 tokens x
-    # 80 heads; the running set's caches: 64 streams x 32,768 tokens x 48 heads). Inputs of
-    # the configs' shapes and distributions drawn on the device (values do not change the
-    # time; the seeded host generator would take minutes at 3-14 GB)
-    for ci in (3, 4):
-        c = configs.get(ci)
-        b, H, P, N, G, L, Q = c.batch, c.nheads, c.headdim, c.d_state, c.ngroups, c.prefix_len, c.chunk
-        A, D = inputs.params(c)
-        Adv, Ddv = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
-        gen = torch.Generator(device="cuda")
-        gen.manual_seed(ci)
-        x = torch.empty((b, L, H, P), dtype=torch.bfloat16, device="cuda")
-        for k in range(b):  # one stream at a time keeps the float32 temporary small
-            x[k] = torch.randn((L, H, P), device="cuda", generator=gen).to(torch.bfloat16)
-        Bv = (0.25 * torch.randn((b, L, G, N), device="cuda", generator=gen)).to(torch.bfloat16)
-        dt = torch.nn.functional.softplus(torch.randn((b, L, H), device="cuda", generator=gen) - 4.0)
-        dt = dt.clamp(1e-3, 0.1).to(torch.bfloat16)
-        dv = bdssm.dims(b, H, P, N, G, 1, bdssm.BF16)
-        hv = torch.empty((b, H, N, P), device="cuda")
-        wsb = bdssm.prefix_scan_workspace(dv, L, Q, False, False)
-        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
-        seq = (x, dt, Bv, None)
-        tm = Timer(torch)
-        for i in range(7):
-            (tm if i >= 2 else Timer(torch)).run("p", lambda: bdssm.prefix_scan(dv, L, Q, seq, Adv, Ddv, None, None,
-                                                                                 None, hv, ws, wsb))
-        torch.cuda.synchronize()
-        us = tm.avg_us("p")
-        nb = prefix_state_bytes(b, H, P, N, G, L, 2)
-        res[f"prefix_build_config{ci}"] = {"workload": f"state-only prefix scan, {c.name}, {b} x {L} tokens",
-                                           "avg_us": round(us, 1), "prefix_tokens_per_s": round(b * L / (us * 1e-6), 1),
-                                           "hbm_frac": round(nb / (us * 1e-6) / HBM_PEAK, 4), "alg_bytes": nb,
-                                           "data": "device-generated, same shapes and distributions"}
-        del x, Bv, dt, hv, ws, seq
-        torch.cuda.empty_cache()
-    # commit chain, config 2: 2048 commits of 32 tokens over the 65,536-token prefix
-    c2 = configs.get(2)
-    b, H, P, N, G, L, T = c2.batch, c2.nheads, c2.headdim, c2.d_state, c2.ngroups, c2.prefix_len, c2.commit_len
-    A, D = inputs.params(c2)
-    Ad2, Dd2 = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
-    d2 = bdssm.dims(b, H, P, N, G, c2.in_dtype, bdssm.BF16)
-    pre = bdssm.seq_to_device(inputs.prefix(c2))
-    blocks = [tuple(t[:, k * T:(k + 1) * T].contiguous() for t in pre) for k in range(L // T)]
-    hc = torch.zeros((b, H, N, P), device="cuda")
-    us = graph_us(torch, lambda: [bdssm.commit(d2, T, blk, Ad2, Dd2, hc) for blk in blocks], reps=3, warm=1)
-    res["commit_chain_config2"] = {"workload": "2,048 commits of 32 tokens (350M shape), one graph",
-                                   "us_per_commit": round(us / len(blocks), 3),
-                                   "tokens_per_s": round(L / (us * 1e-6), 1)}
-    return res
-
-
-def secondary(torch, np, bdssm, configs, inputs, reps=20):
-    res = []
-    # 64-stream running set: T = 128, the cached fp32 state per stream in operand form (made
-    # once per commit, i.e. once per 16 steps of this workload; its time is reported beside);
-    # values do not affect timing: the state is drawn at random, inputs from the seeded
-    # generator
-    c4 = configs.get(4)
-    b, H, P, N, G, T = c4.batch, c4.nheads, c4.headdim, c4.d_state, c4.ngroups, c4.block_len
-    A, D = inputs.params(c4)
-    Ad, Dd = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
-    d = bdssm.dims(b, H, P, N, G, c4.in_dtype, bdssm.BF16)
-    h = torch.randn((b, H, N, P), device="cuda") * 0.05
-    ops = torch.empty(bdssm.state_ops_bytes(d), dtype=torch.uint8, device="cuda")
-    bdssm.state_ops(d, h, ops)
-    f = bdssm.seq_to_device(inputs.block(c4, 0, 0, inputs.FWD))
-    r = bdssm.seq_to_device(inputs.block(c4, 0, 0, inputs.REV))
-    y = torch.empty((b, T, H, P), dtype=torch.bfloat16, device="cuda")
-    tm = Timer(torch)
-    for name, fn in (("k", lambda: bdssm.block_step_ops(d, T, ops, f, r, Ad, Dd, y)),
-                     ("f32", lambda: bdssm.block_step(d, T, h, f, r, Ad, Dd, y)),
-                     ("ops", lambda: bdssm.state_ops(d, h, ops))):
-        for i in range(reps + 3):  # each kernel back to back with itself
-            (tm if i >= 3 else Timer(torch)).run(name, fn)
-    torch.cuda.synchronize()
-    us = tm.avg_us("k")
-    nb = block_step_bytes(b, H, P, N, G, T, 2, 2)
-    res.append({"workload": "block step, 700M shape x 64 streams, running set T=128, bf16 in/out, "
-                            "cached state in operand form",
-                "avg_us": round(us, 3), "active_tokens_per_s": round(b * T / (us * 1e-6), 1),
-                "roofline": make_roofline("hbm", nb, us, traffic_for("block_step_c4")),
-                "alg_bytes": nb, "from_fp32_state_us": round(tm.avg_us("f32"), 3),
-                "state_ops_us": round(tm.avg_us("ops"), 3)})
-    del h, ops, f, r, y
-    # 350M prefix: 65,536 tokens, chunk 256, bf16 y + fp32 chunk states
-    c2 = configs.get(2)
-    b, H, P, N, G, L, Q = c2.batch, c2.nheads, c2.headdim, c2.d_state, c2.ngroups, c2.prefix_len, c2.chunk
-    A, D = inputs.params(c2)
-    Ad, Dd = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
-    d = bdssm.dims(b, H, P, N, G, c2.in_dtype, bdssm.BF16)
-    pre = bdssm.seq_to_device(inputs.prefix(c2))
-    y = torch.empty((b, L, H, P), dtype=torch.bfloat16, device="cuda")
-    cs = torch.empty((b, -(-L // Q), H, N, P), device="cuda")
-    ho = torch.empty((b, H, N, P), device="cuda")
-    wsb = bdssm.prefix_scan_workspace(d, L, Q, True, True)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
-    tm = Timer(torch)
-    for i in range(8):
-        (tm if i >= 2 else Timer(torch)).run(
-            "k", lambda: bdssm.prefix_scan(d, L, Q, pre, Ad, Dd, None, y, cs, ho, ws, wsb))
-    torch.cuda.synchronize()
-    us = tm.avg_us("k")
-    fl = prefix_flops(b, H, P, N, G, L, Q)
-    nb = prefix_bytes(b, H, P, N, G, L, Q, 2, 2, True)
-    res.append({"workload": "prefix scan, 350M shape, 65,536 tokens, chunk 256, bf16 y + fp32 chunk states",
-                "avg_us": round(us, 3), "prefix_tokens_per_s": round(b * L / (us * 1e-6), 1),
-                "roofline": make_roofline("mfma", fl, us, traffic_for("prefix_scan_c2")),
-                "mfma_frac_causal_count": round(prefix_flops_causal(b, H, P, N, G, L, Q) / (us * 1e-6) / MFMA_BF16_PEAK, 4),
-                "hbm_frac": round(nb / (us * 1e-6) / HBM_PEAK, 4), "alg_bytes": nb, "flops": fl})
-    return res
-
-
-def cpu_baseline(np, cfg, A, D, pre_np, steps_np, clean_np):
-    """The float64 oracle on the host cores, one whole step of the same workload."""
-    import oracle
-    threads = oracle.max_threads()
-    t0 = time.perf_counter()
-    _, _, h = oracle.scan(pre_np, A, D, cfg.chunk, want_y=True, want_chunk_states=False)
-    hf = h.astype(np.float32).astype(np.float64)
-    for f, r in steps_np:
-        oracle.block_step(hf, f, r, A, D)
-    oracle.commit(hf, clean_np, A, D)
-    wall = time.perf_counter() - t0
-    active = cfg.steps_per_block * cfg.batch * cfg.block_len
-    return {"value": round(active / wall, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "one whole step (8192-token prefix scan with y, 64 block steps, commit) of the "
-                      f"same workload; {wall:.2f} s of host time"}
 
 
 if __name__ == "__main__":
