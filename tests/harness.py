@@ -113,3 +113,35 @@ def streams_of(seq, idx):
 
 def f32_round(a):
     return np.asarray(a, np.float64).astype(np.float32).astype(np.float64)
+
+
+def device_draw(gen, b, L, H, P, G, N, dtype_bits=True):
+    """Seeded device draws of one segment with the workload's distributions (x ~ N(0,1);
+    B, C ~ N(0,1/16); dt = softplus(N(-4,1)) clipped to [1e-3, 0.1]), rounded to bf16: the
+    streams the oracle does not check, at sizes the host generator would take minutes for."""
+    t = torch()
+    bf = t.bfloat16
+    x = t.empty((b, L, H, P), dtype=bf, device="cuda")
+    dt = t.empty((b, L, H), dtype=bf, device="cuda")
+    B = t.empty((b, L, G, N), dtype=bf, device="cuda")
+    C = t.empty((b, L, G, N), dtype=bf, device="cuda")
+    for s in range(b):
+        x[s] = t.randn((L, H, P), device="cuda", generator=gen).to(bf)
+        dt[s] = t.nn.functional.softplus(t.randn((L, H), device="cuda", generator=gen) - 4.0).clamp(1e-3, 0.1).to(bf)
+        B[s] = (0.25 * t.randn((L, G, N), device="cuda", generator=gen)).to(bf)
+        C[s] = (0.25 * t.randn((L, G, N), device="cuda", generator=gen)).to(bf)
+    return (x, dt, B, C)
+
+
+def mixed_seq(cfg, gen, segment, step, direction, length, sample):
+    """All cfg.batch streams of one segment on the device: the sampled streams from the
+    seeded host generator (returned as an inputs.Seq for the oracle), the others drawn on the
+    device. Streams are independent, so the sampled ones check the full-batch launch."""
+    from bidirectional_mamba_state_amd import inputs
+    host = inputs.segment(cfg, segment, step, direction, length, streams=sample)
+    dev = device_draw(gen, cfg.batch, length, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.d_state)
+    hd = bdssm.seq_to_device(host)
+    for i, s in enumerate(sample):
+        for full, part in zip(dev, hd):
+            full[s] = part[i]
+    return dev, host

@@ -86,39 +86,64 @@ def test_config0_tiny_fp32_full_path():
         h = f32_round(_check_commit(h, inputs.block(cfg, k, 0, inputs.CLEAN), A, D, label=f"c0 block {k}"))
 
 
-def test_config1_700m():
+def test_config1_700m_four_blocks():
+    """The 700M batch-1 plan: the 8192-token prefix scan (y and state), then four blocks of
+    64 denoising steps each followed by a commit. Every step of block 0 and the last step of
+    blocks 1-3 are checked (y, and y - D x on the first and last step of each block), and
+    every post-commit state; the oracle continues from the GPU's float32 state, as the next
+    block's steps do."""
     cfg = configs.get(1)
     A, D = inputs.params(cfg)
     pre = inputs.prefix(cfg)
     h = f32_round(_check_prefix(pre, A, D, cfg.chunk, want_cs=False, label="c1"))
-    for step in (0, 1, cfg.steps_per_block - 1):
-        fwd = inputs.block(cfg, 0, step, inputs.FWD)
-        rev = inputs.block(cfg, 0, step, inputs.REV)
-        _check_block(h, fwd, rev, A, D, label=f"c1 step {step}")
-    _check_block(h, inputs.block(cfg, 0, 0, inputs.FWD), inputs.block(cfg, 0, 0, inputs.REV), A, D,
-                 y_dtype=bdssm.BF16, label="c1 bf16 y")
-    _check_commit(h, inputs.block(cfg, 0, 0, inputs.CLEAN), A, D, label="c1")
+    S = cfg.steps_per_block
+    for k in range(cfg.n_blocks):
+        for step in (range(S) if k == 0 else (S - 1,)):
+            fwd = inputs.block(cfg, k, step, inputs.FWD)
+            rev = inputs.block(cfg, k, step, inputs.REV)
+            if step in (0, S - 1):
+                _check_block(h, fwd, rev, A, D, label=f"c1 block {k} step {step}")
+            else:
+                _case(f"block_step c1 block {k} step {step}")
+                y = gpu_block_step(h, fwd, rev, A, D)
+                yo, _, _ = oracle.block_step(h, fwd, rev, A, D)
+                assert within(rel(y, yo), TOL_BF16, "block y")
+        if k == 0:
+            _check_block(h, inputs.block(cfg, 0, 0, inputs.FWD), inputs.block(cfg, 0, 0, inputs.REV), A, D,
+                         y_dtype=bdssm.BF16, label="c1 bf16 y")
+        h = f32_round(_check_commit(h, inputs.block(cfg, k, 0, inputs.CLEAN), A, D, label=f"c1 block {k}"))
 
 
-def test_config2_prefix_chunk_states_sampled_heads():
+def test_config2_prefix_chunk_states_all_heads():
     cfg = configs.get(2)
     A, D = inputs.params(cfg)
     pre = inputs.prefix(cfg)
-    h = _check_prefix(pre, A, D, cfg.chunk, heads=(0, 17, 31), label="c2")
+    h = _check_prefix(pre, A, D, cfg.chunk, label="c2 (all 32 heads)")
     _check_commit(f32_round(h), inputs.block(cfg, 0, 0, inputs.CLEAN), A, D, label="c2")
 
 
 def test_config3_long_context_grouped():
+    """The 3B long-context plan: the 262,144-token state-only prefix (all 80 heads, 8
+    groups of 10), then 64 denoising steps (each checked; y - D x on the first and last) and
+    the commit."""
     cfg = configs.get(3)
     A, D = inputs.params(cfg)
     pre = inputs.prefix(cfg)
-    # state-only prefix; heads sampled from different groups (10 heads per group)
-    h = _check_prefix(pre, A, D, cfg.chunk, want_y=False, want_cs=False, heads=(0, 29, 79),
-                      label="c3")
+    h = _check_prefix(pre, A, D, cfg.chunk, want_y=False, want_cs=False, label="c3 (all 80 heads)")
+    del pre
     hf = f32_round(h)
-    fwd = inputs.block(cfg, 0, 0, inputs.FWD)
-    rev = inputs.block(cfg, 0, 0, inputs.REV)
-    _check_block(hf, fwd, rev, A, D, heads=(0, 29, 79), label="c3")
+    S = cfg.steps_per_block
+    for step in range(S):
+        fwd = inputs.block(cfg, 0, step, inputs.FWD)
+        rev = inputs.block(cfg, 0, step, inputs.REV)
+        if step in (0, S - 1):
+            _check_block(hf, fwd, rev, A, D, label=f"c3 step {step}")
+        else:
+            _case(f"block_step c3 step {step}")
+            y = gpu_block_step(hf, fwd, rev, A, D)
+            yo, _, _ = oracle.block_step(hf, fwd, rev, A, D)
+            assert within(rel(y, yo), TOL_BF16, "block y")
+    _check_commit(hf, inputs.block(cfg, 0, 0, inputs.CLEAN), A, D, label="c3")
 
 
 # ------------------------------------------------------------------ edge cases
