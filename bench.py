@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--only", choices=("headline", "c1", "c2prefix", "builds"),
+    ap.add_argument("--only", choices=("headline", "c1", "c2prefix", "builds", "fullwindow"),
                     help="run one workload only (for profiler runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
@@ -464,6 +464,40 @@ def config1(args, torch, np, bdssm, configs, inputs):
     return res
 
 
+# ---------------------------------------------------------------- full-window comparison
+def full_window_c1(torch, np, bdssm, configs, inputs, block_step_us=None, reps=10):
+    """The system the method replaces, timed beside the block step: one denoising step of a
+    full-window bidirectional Mamba layer (bdssm_full_window) over the 700M shape's window of
+    8192 prefix tokens plus the 32-token block (both directions from zero, every token's
+    output), against one block step from the cached state."""
+    cfg = configs.get(1)
+    b, H, P, N, G, Q = cfg.batch, cfg.nheads, cfg.headdim, cfg.d_state, cfg.ngroups, cfg.chunk
+    L = cfg.prefix_len + cfg.block_len
+    A, D = inputs.params(cfg)
+    Ad, Dd = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
+    d = bdssm.dims(b, H, P, N, G, cfg.in_dtype, bdssm.BF16)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(13)
+    fwd = dev_seq(torch, gen, b, L, H, P, G, N)
+    rev = dev_seq(torch, gen, b, L, H, P, G, N)
+    y = torch.empty((b, L, H, P), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(max(bdssm.full_window_workspace(d, L, Q), 1), dtype=torch.uint8, device="cuda")
+    fn = lambda: bdssm.full_window(d, L, Q, fwd, rev, Ad, Dd, None, None, y, ws)
+    fn()
+    torch.cuda.synchronize()
+    us = median(launch_times_us(torch, [fn], reps=reps)[0])
+    nb = 2 * prefix_bytes(b, H, P, N, G, L, Q, 2, 2, False) + b * L * H * P * 2
+    out = {"workload": "full-window bidirectional scan (both directions from zero over 8192 prefix + 32 block "
+                       "tokens, all outputs, bf16 y), 700M shape, batch 1: one denoising step of the "
+                       "comparison system", "avg_us": round(us, 2), "window_tokens": L,
+           "hbm_frac": round(nb / (us * 1e-6) / HBM_PEAK, 4), "alg_bytes": nb,
+           "mfma_frac": round(2 * prefix_flops(b, H, P, N, G, L, Q) / (us * 1e-6) / MFMA_BF16_PEAK, 4)}
+    if block_step_us:
+        out["block_step_us"] = block_step_us
+        out["full_window_over_block_step"] = round(us / block_step_us, 1)
+    return out
+
+
 # ---------------------------------------------------------------- config 2: prefix scan
 def config2_prefix(torch, np, bdssm, configs, inputs, reps=10):
     c2 = configs.get(2)
@@ -661,14 +695,18 @@ def main():
         fn = {"headline": lambda: headline(args, torch, np, bdssm, configs, inputs),
               "c1": lambda: config1(args, torch, np, bdssm, configs, inputs),
               "c2prefix": lambda: config2_prefix(torch, np, bdssm, configs, inputs),
-              "builds": lambda: builds(torch, np, bdssm, configs, inputs)}.get(args.only)
+              "builds": lambda: builds(torch, np, bdssm, configs, inputs),
+              "fullwindow": lambda: full_window_c1(torch, np, bdssm, configs, inputs)}.get(args.only)
         print(json.dumps({args.only: fn()}), flush=True)
         return
     out = headline(args, torch, np, bdssm, configs, inputs)
     if not args.no_secondary:
         print("[bench] secondary workloads", file=sys.stderr, flush=True)
-        out["secondary"] = {"config1_block_cycle": config1(args, torch, np, bdssm, configs, inputs),
-                            "config2_prefix_scan": config2_prefix(torch, np, bdssm, configs, inputs)}
+        c1 = config1(args, torch, np, bdssm, configs, inputs)
+        out["secondary"] = {"config1_block_cycle": c1,
+                            "config2_prefix_scan": config2_prefix(torch, np, bdssm, configs, inputs),
+                            "full_window_config1": full_window_c1(torch, np, bdssm, configs, inputs,
+                                                                  c1["block_step_us"])}
         out["secondary"].update(builds(torch, np, bdssm, configs, inputs))
         out["secondary"]["conv_state"] = conv_workloads(torch, bdssm, configs, inputs)
     if not args.no_cpu_baseline:

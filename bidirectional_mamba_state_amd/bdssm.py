@@ -24,7 +24,8 @@ EXPORTS = ("bdssm_abi_version", "bdssm_status_str", "bdssm_prefix_scan_workspace
            "bdssm_decode_graph_launch", "bdssm_decode_graph_destroy",
            "bdssm_conv_workspace", "bdssm_conv", "bdssm_block_step_conv", "bdssm_commit_conv",
            "bdssm_state_ops_bytes", "bdssm_state_ops", "bdssm_block_step_ops",
-           "bdssm_set_launch_override", "bdssm_prefix_scan_static")
+           "bdssm_set_launch_override", "bdssm_prefix_scan_static",
+           "bdssm_full_window_workspace", "bdssm_full_window")
 
 
 class BdssmError(RuntimeError):
@@ -105,6 +106,10 @@ def load():
                                           V, SZ, V]
         lib.bdssm_prefix_scan_static.restype = ctypes.c_int
         lib.bdssm_prefix_scan_static.argtypes = [P(Dims), I64, I32, P(SeqPtrs), V, V, V, V, V, V, V]
+        lib.bdssm_full_window_workspace.restype = SZ
+        lib.bdssm_full_window_workspace.argtypes = [P(Dims), I64, I32]
+        lib.bdssm_full_window.restype = ctypes.c_int
+        lib.bdssm_full_window.argtypes = [P(Dims), I64, I32, P(SeqPtrs), P(SeqPtrs), V, V, V, V, V, V, SZ, V]
         lib.bdssm_set_launch_override.restype = ctypes.c_int
         lib.bdssm_set_launch_override.argtypes = [P(LaunchOverride)]
         _lib = lib
@@ -184,6 +189,18 @@ def prefix_scan_static(d, length, chunk, seq, A, D, h_init, y, chunk_states, h_o
     _check(load().bdssm_prefix_scan_static(ctypes.byref(d), length, chunk, _byref(_seq(seq)), _ptr(A),
                                            _ptr(D), _ptr(h_init), _ptr(y), _ptr(chunk_states),
                                            _ptr(h_out), _stream(stream)))
+
+
+def full_window_workspace(d, length, chunk):
+    return load().bdssm_full_window_workspace(ctypes.byref(d), length, chunk)
+
+
+def full_window(d, length, chunk, fwd, rev, A, D, A_rev, D_rev, y, workspace=None, stream=None):
+    """bdssm_full_window: forward and reverse scans over the whole window from zero states
+    (A_rev None = A; D_rev None = no reverse skip term)."""
+    _check(load().bdssm_full_window(ctypes.byref(d), length, chunk, _byref(_seq(fwd)), _byref(_seq(rev)),
+                                    _ptr(A), _ptr(D), _ptr(A if A_rev is None else A_rev), _ptr(D_rev),
+                                    _ptr(y), _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def block_step(d, block_len, h_prefix, fwd, rev, A, D, y, stream=None):

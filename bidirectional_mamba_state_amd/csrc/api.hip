@@ -341,6 +341,55 @@ bdssm_status static_scratch_ptr(void **out)
     return BDSSM_OK;
 }
 
+// The vector-ALU prefix scan of plan p (workspace already checked). rev: the tokens in
+// reverse order, outputs added to y (y required, no chunk states, h_out may be NULL).
+bdssm_status run_prefix_valu(const Shape &s, int64_t len, const Plan &p, const Seq &seq, const float *A,
+                             const float *D, const float *h_init, void *y, float *chunk_states, float *h_out,
+                             void *workspace, bool rev, hipStream_t st)
+{
+    const bool with_y = y != nullptr, with_cs = chunk_states != nullptr;
+    const int64_t NP = static_cast<int64_t>(s.N) * s.P;
+    const int r = rev ? 1 : 0;
+    bdssm_status rc;
+    if (!with_y && !with_cs && p.nseg == 1) {
+        // one pass per (stream, head), from h_init straight to h_out (in place is safe:
+        // each workgroup reads its whole state before it writes any of it)
+        ForwardArgs f{s, len, static_cast<int>(p.seg_len), 1, seq, A, D, h_init, nullptr,
+                      nullptr, h_out, nullptr, r};
+        return launched(launch_forward_valu(f, st));
+    }
+
+    float *decay = static_cast<float *>(workspace);
+    float *states = with_cs ? chunk_states
+                            : reinterpret_cast<float *>(static_cast<char *>(workspace) + p.decay_bytes);
+    // 1. chunk-local states (from zero) and decay sums
+    ForwardArgs f1{s, len, static_cast<int>(p.seg_len), p.nseg, seq, A, D, nullptr, nullptr,
+                   nullptr, states, decay, r};
+    if ((rc = launched(launch_forward_valu(f1, st))) != BDSSM_OK)
+        return rc;
+    // 2. pass states across segments. With y, h_init must survive until pass 3 reads it,
+    //    so h_out is written afterwards from the last chunk state.
+    PassArgs pa{s, p.nseg, h_init, states, decay, (with_y || with_cs) ? 1 : 0,
+                with_y ? nullptr : h_out};
+    if ((rc = launched(launch_state_pass(pa, st))) != BDSSM_OK)
+        return rc;
+    if (!with_y)
+        return BDSSM_OK;
+    // 3. outputs: each chunk recomputed from the state entering it
+    ForwardArgs f3{s, len, static_cast<int>(p.seg_len), p.nseg, seq, A, D, h_init, states,
+                   y, nullptr, nullptr, r};
+    if ((rc = launched(launch_forward_valu(f3, st))) != BDSSM_OK)
+        return rc;
+    for (int b = 0; h_out && b < s.b; ++b) {
+        rc = launched(launch_copy_f32(h_out + static_cast<int64_t>(b) * s.H * NP,
+                                      states + (static_cast<int64_t>(b) * p.nseg + p.nseg - 1) * s.H * NP,
+                                      s.H * NP, st));
+        if (rc != BDSSM_OK)
+            return rc;
+    }
+    return BDSSM_OK;
+}
+
 // bdssm_prefix_scan and bdssm_prefix_scan_static: with static_scratch the workspace comes
 // from the library's static device buffer instead of the caller.
 bdssm_status prefix_scan_impl(const bdssm_dims *dims, int64_t len, int32_t chunk, const bdssm_seq *in,
@@ -433,43 +482,7 @@ bdssm_status prefix_scan_impl(const bdssm_dims *dims, int64_t len, int32_t chunk
             return BDSSM_ERR_ALIAS;
     }
 
-    if (!with_y && !with_cs && p.nseg == 1) {
-        // one pass per (stream, head), from h_init straight to h_out (in place is safe:
-        // each workgroup reads its whole state before it writes any of it)
-        ForwardArgs f{s, len, static_cast<int>(p.seg_len), 1, seq, A, D, h_init, nullptr,
-                      nullptr, h_out, nullptr};
-        return launched(launch_forward_valu(f, st));
-    }
-
-    float *decay = static_cast<float *>(workspace);
-    float *states = with_cs ? chunk_states
-                            : reinterpret_cast<float *>(static_cast<char *>(workspace) + p.decay_bytes);
-    // 1. chunk-local states (from zero) and decay sums
-    ForwardArgs f1{s, len, static_cast<int>(p.seg_len), p.nseg, seq, A, D, nullptr, nullptr,
-                   nullptr, states, decay};
-    if ((rc = launched(launch_forward_valu(f1, st))) != BDSSM_OK)
-        return rc;
-    // 2. pass states across segments. With y, h_init must survive until pass 3 reads it,
-    //    so h_out is written afterwards from the last chunk state.
-    PassArgs pa{s, p.nseg, h_init, states, decay, (with_y || with_cs) ? 1 : 0,
-                with_y ? nullptr : h_out};
-    if ((rc = launched(launch_state_pass(pa, st))) != BDSSM_OK)
-        return rc;
-    if (!with_y)
-        return BDSSM_OK;
-    // 3. outputs: each chunk recomputed from the state entering it
-    ForwardArgs f3{s, len, static_cast<int>(p.seg_len), p.nseg, seq, A, D, h_init, states,
-                   y, nullptr, nullptr};
-    if ((rc = launched(launch_forward_valu(f3, st))) != BDSSM_OK)
-        return rc;
-    for (int b = 0; b < s.b; ++b) {
-        rc = launched(launch_copy_f32(h_out + static_cast<int64_t>(b) * s.H * NP,
-                                      states + (static_cast<int64_t>(b) * p.nseg + p.nseg - 1) * s.H * NP,
-                                      s.H * NP, st));
-        if (rc != BDSSM_OK)
-            return rc;
-    }
-    return BDSSM_OK;
+    return run_prefix_valu(s, len, p, seq, A, D, h_init, y, chunk_states, h_out, workspace, false, st);
 }
 
 }  // namespace
@@ -525,6 +538,72 @@ bdssm_status bdssm_prefix_scan_static(const bdssm_dims *dims, int64_t len, int32
 {
     return prefix_scan_impl(dims, len, chunk, in, A, D, h_init, y, chunk_states, h_out, nullptr, 0, true,
                             stream);
+}
+
+size_t bdssm_full_window_workspace(const bdssm_dims *dims, int64_t len, int32_t chunk)
+{
+    // both directions run the prefix scan's plan with outputs, one after the other, in the
+    // same workspace
+    return bdssm_prefix_scan_workspace(dims, len, chunk, 1, 0);
+}
+
+bdssm_status bdssm_full_window(const bdssm_dims *dims, int64_t len, int32_t chunk, const bdssm_seq *fwd,
+                               const bdssm_seq *rev, const float *A, const float *D, const float *A_rev,
+                               const float *D_rev, void *y, void *workspace, size_t workspace_bytes,
+                               void *stream)
+{
+    Shape s;
+    bdssm_status rc = check_dims(dims, &s);
+    if (rc != BDSSM_OK)
+        return rc;
+    if (len < 0)
+        return BDSSM_ERR_SHAPE;
+    if (!chunk_ok(chunk))
+        return BDSSM_ERR_UNSUPPORTED;
+    if (!A || !D || !A_rev || !y)
+        return BDSSM_ERR_NULL;
+    SeqRanges qf{}, qr{};
+    if ((rc = check_seq(fwd, s, len, true, &qf)) != BDSSM_OK || (rc = check_seq(rev, s, len, true, &qr)) != BDSSM_OK)
+        return rc;
+    if (!aligned(A) || !aligned(D) || !aligned(A_rev) || !aligned(D_rev) || !aligned(y) || !aligned(workspace))
+        return BDSSM_ERR_ALIGN;
+    const Range ry = rng(y, static_cast<int64_t>(s.b) * len * s.H * s.P * elt(s.y_dt));
+    const Range rp[4] = {rng(A, s.H * 4), rng(D, s.H * 4), rng(A_rev, s.H * 4), rng(D_rev, s.H * 4)};
+    if (hits(ry, qf) || hits(ry, qr))
+        return BDSSM_ERR_ALIAS;
+    for (const Range &r : rp)
+        if (overlap(ry, r))
+            return BDSSM_ERR_ALIAS;
+    if (s.b == 0 || len == 0)
+        return BDSSM_OK;
+    const bool mfma = prefix_mfma_supported(s, chunk);
+    const size_t need = mfma ? prefix_mfma_plan(s, len, chunk, true).ws_bytes
+                             : plan_prefix(s, len, chunk, true, false).ws_bytes;
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return BDSSM_ERR_WORKSPACE;
+        const Range rws = rng(workspace, static_cast<int64_t>(need));
+        if (hits(rws, qf) || hits(rws, qr) || overlap(rws, ry))
+            return BDSSM_ERR_ALIAS;
+        for (const Range &r : rp)
+            if (overlap(rws, r))
+                return BDSSM_ERR_ALIAS;
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const Seq sf{fwd->x, fwd->dt, fwd->B, fwd->C}, sr{rev->x, rev->dt, rev->B, rev->C};
+    if (mfma) {
+        // forward from zero over the window (writes y, with D x), then the reverse scan from
+        // zero at the window's end (adds its outputs, with D_rev x_rev when given)
+        if ((rc = launched(run_prefix_mfma(s, len, chunk, sf, A, D, nullptr, y, nullptr, nullptr, workspace, st)))
+            != BDSSM_OK)
+            return rc;
+        return launched(run_prefix_mfma(s, len, chunk, sr, A_rev, D_rev, nullptr, y, nullptr, nullptr, workspace,
+                                        st, false, true));
+    }
+    const Plan p = plan_prefix(s, len, chunk, true, false);
+    if ((rc = run_prefix_valu(s, len, p, sf, A, D, nullptr, y, nullptr, nullptr, workspace, false, st)) != BDSSM_OK)
+        return rc;
+    return run_prefix_valu(s, len, p, sr, A_rev, D_rev, nullptr, y, nullptr, nullptr, workspace, true, st);
 }
 
 bdssm_status bdssm_block_step(const bdssm_dims *dims, int32_t block_len,

@@ -29,6 +29,8 @@ struct ForwardArgs {
     void *y;                   // [b][len][H][P] in s.y_dt, with D x; NULL = no output
     float *state_out;          // final state of each segment, [b][nseg][H][N][P]; NULL = none
     float *decay_out;          // sum over the segment of dt*A, [b][nseg][H]; NULL = none
+    int rev = 0;               // scan token len-1-t at position t, and add the outputs to y
+                               // (D may then be NULL: no skip term)
 };
 
 // Inter-chunk state passing: h_c = exp(decay_c) h_{c-1} + local_c, in place over `states`.
@@ -87,9 +89,12 @@ bool prefix_mfma_supported(const Shape &s, int chunk);
 // full: y or chunk states are wanted; single_segment: one segment per (stream, head), no
 // workspace (used by commits)
 PrefixPlan prefix_mfma_plan(const Shape &s, int64_t len, int chunk, bool full, bool single_segment = false);
+// rev: scan from the last token to the first and add the outputs to y (y required, no chunk
+// states; h_out may be NULL when y is given); D may then be NULL (no skip term)
 hipError_t run_prefix_mfma(const Shape &s, int64_t len, int chunk, const Seq &in, const float *A,
                            const float *D, const float *h_init, void *y, float *chunk_states,
-                           float *h_out, void *ws, hipStream_t st, bool single_segment = false);
+                           float *h_out, void *ws, hipStream_t st, bool single_segment = false,
+                           bool rev = false);
 bool block_mfma_supported(const Shape &s, int T);
 void block_mfma_plan(const Shape &s, int *hpw, int *ps);
 hipError_t launch_block_step_mfma(const BlockArgs &a, int hpw, int ps, hipStream_t st);

@@ -26,6 +26,11 @@
 //          into LDS), or only the chunk states (k_scan<true, 1>): the state after every
 //          chunk of Q tokens and after the last token, and, for the stream's last segment,
 //          the final state.
+// Reverse order (REV): k_state and the full pass also scan a sequence from its last token
+// to its first (token t of the scan is token len - 1 - t of the stream), reading the same
+// layouts: row r of a sub-chunk holding scan positions t0 .. t0 + n - 1 is stream token
+// (len - t0 - n) + (n - 1 - r). The full pass then adds its outputs to y instead of writing
+// them (the reverse half of a full-window bidirectional scan, whose forward half wrote y).
 // k_scan stages B and x through registers into the fragment-major order of mfma_tiles.h
 // (an operand fragment is one contiguous 512-byte read per wavefront).
 // The fp32 states and the weighted x~ operand are split into bf16 hi + lo parts, so that
@@ -300,6 +305,26 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
     }
 }
 
+// Token mapping of the reverse order: the stream token held by the first memory row of the
+// sub-chunk at scan position t0 with nrows valid rows, and the memory row of its scan row
+// `row` (rows past the valid ones map past any buffer range). Identities in natural order.
+template <bool REV>
+__device__ __forceinline__ int64_t first_token(int64_t len, int64_t t0, int nrows)
+{
+    if constexpr (REV)
+        return max<int64_t>(len - t0 - nrows, 0);
+    else
+        return t0;
+}
+template <bool REV>
+__device__ __forceinline__ int mem_row(int row, int nrows)
+{
+    if constexpr (REV)
+        return row < nrows ? nrows - 1 - row : SC;
+    else
+        return row;
+}
+
 // Segment scan, one thread per state element: the end states of segments started from
 // zero become the states entering each segment (in place), and the final state.
 __global__ __launch_bounds__(256) void k_seg_scan(float *buf, const float *tot, int nseg, int H,
@@ -340,7 +365,10 @@ __global__ __launch_bounds__(256) void k_seg_scan(float *buf, const float *tot, 
 // falls in distinct banks:
 //   B: 64 rows x 128 bf16, piece c of row t at slot c ^ 2 (t % 4);
 //   x: 64 rows x 64 bf16 per head, piece c of row t at slot c ^ 2 (t % 4).
-__global__ __launch_bounds__(256, 2) void k_state(ScanArgs a)
+// (the body is a device function template with one kernel per scan order: a kernel template
+// built from generic lambdas loses its host-side launch stub in this compiler)
+template <bool REV>
+__device__ __forceinline__ void state_pass(const ScanArgs &a)
 {
     constexpr int HPW = 1, NBUF = 3;
     __shared__ __attribute__((aligned(16))) __bf16 sB0[SC * kN];
@@ -411,21 +439,22 @@ __global__ __launch_bounds__(256, 2) void k_state(ScanArgs a)
         const int kk = min(k, nsub - 1);  // past the segment: the last sub-chunk again (unused)
         const int64_t t0 = seg_t0 + static_cast<int64_t>(kk) * SC;
         const int nrows = static_cast<int>(min<int64_t>(SC, len - t0));
-        const auto rB = mk(Bg + t0 * rowBC, ((nrows - 1) * rowBC + kN) * 2);
-        const auto rX = mk(xg + t0 * rowX, ((nrows - 1) * rowX + HPW * kP) * 2);
+        const int64_t f0 = first_token<REV>(len, t0, nrows);
+        const auto rB = mk(Bg + f0 * rowBC, ((nrows - 1) * rowBC + kN) * 2);
+        const auto rX = mk(xg + f0 * rowX, ((nrows - 1) * rowX + HPW * kP) * 2);
 #pragma unroll
         for (int u = 0; u < NPW; ++u) {
             if (u < 4) {
                 const int pc = piece_B(u), row = 4 * pc + (lane >> 4), c = (lane & 15) ^ (2 * (row & 3));
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     rB, (__attribute__((address_space(3))) void *)(bufB(PH) + 4 * pc * kN), 16,
-                    (row * rowBC + 8 * c) * 2, 0, 0, 0);
+                    (mem_row<REV>(row, nrows) * rowBC + 8 * c) * 2, 0, 0, 0);
             } else {
                 const int px = piece_X(u), hh = px >> 3, row = 8 * (px & 7) + (lane >> 3);
                 const int c = (lane & 7) ^ (2 * (row & 3));
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     rX, (__attribute__((address_space(3))) void *)(bufX(PH, hh) + 8 * (px & 7) * kP), 16,
-                    (row * rowX + hh * kP + 8 * c) * 2, 0, 0, 0);
+                    (mem_row<REV>(row, nrows) * rowX + hh * kP + 8 * c) * 2, 0, 0, 0);
             }
         }
     };
@@ -447,10 +476,10 @@ __global__ __launch_bounds__(256, 2) void k_state(ScanArgs a)
         const int kk = min(k, nsub - 1);
         const int64_t t0 = seg_t0 + static_cast<int64_t>(kk) * SC;
         const int nrows = static_cast<int>(min<int64_t>(SC, len - t0));
-        const auto rD = mk(dtg + t0 * H, ((nrows - 1) * H + HPW) * 2);
+        const auto rD = mk(dtg + first_token<REV>(len, t0, nrows) * H, ((nrows - 1) * H + HPW) * 2);
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh)
-            d[hh] = __builtin_amdgcn_raw_buffer_load_b16(rD, (lane * H + hh) * 2, 0, 0);
+            d[hh] = __builtin_amdgcn_raw_buffer_load_b16(rD, (mem_row<REV>(lane, nrows) * H + hh) * 2, 0, 0);
     };
     // TAB_W and the total log-decay of sub-chunk k into this wavefront's own tables
     auto tables = [&](int k, const unsigned short (&dbits)[HPW]) {
@@ -607,6 +636,9 @@ __global__ __launch_bounds__(256, 2) void k_state(ScanArgs a)
     }
 }
 
+__global__ __launch_bounds__(256, 2) void k_state(ScanArgs a) { state_pass<false>(a); }
+__global__ __launch_bounds__(256, 2) void k_state_rev(ScanArgs a) { state_pass<true>(a); }
+
 // ---- FULL pass with outputs, one head per workgroup, inputs copied straight into LDS
 //
 // The same computation as k_scan<true, true, 1> (and bitwise the same state walk as
@@ -626,7 +658,7 @@ __device__ __forceinline__ int swz(int r)
 
 // (the body is a device function template with one kernel per output type: a kernel
 // template built from generic lambdas loses its host-side launch stub in this compiler)
-template <typename Ty>
+template <typename Ty, bool REV>
 __device__ __forceinline__ void full_pass(const ScanArgs &a)
 {
     __shared__ __attribute__((aligned(16))) __bf16 sB0[SC * kN];
@@ -676,7 +708,7 @@ __device__ __forceinline__ void full_pass(const ScanArgs &a)
     const __bf16 *Cg = static_cast<const __bf16 *>(a.in.C) + tok0 * rowBC + g * kN;
     const __bf16 *xg = static_cast<const __bf16 *>(a.in.x) + tok0 * rowX + h0 * kP;
     const __bf16 *dtg = static_cast<const __bf16 *>(a.in.dt) + tok0 * H + h0;
-    const float Ah = a.A[h0], Dh = a.D[h0];
+    const float Ah = a.A[h0], Dh = (!REV || a.D) ? a.D[h0] : 0.f;
     const auto mk = buffer_range;
     // rows of sub-chunk k of the segment; 0 past the segment (its copies then move nothing)
     auto rows_of = [&](int k) {
@@ -690,31 +722,31 @@ __device__ __forceinline__ void full_pass(const ScanArgs &a)
     auto copy_rows = [&](const __bf16 *base, __bf16 *dst, int k) {
         const int64_t t0 = seg_t0 + static_cast<int64_t>(k) * SC;
         const int nrows = rows_of(k);
-        const auto r = mk(base + t0 * rowBC, nrows > 0 ? ((nrows - 1) * rowBC + kN) * 2 : 0);
+        const auto r = mk(base + first_token<REV>(len, t0, nrows) * rowBC, nrows > 0 ? ((nrows - 1) * rowBC + kN) * 2 : 0);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int pc = wave + 4 * u, row = 4 * pc + (lane >> 4), c = (lane & 15) ^ swz(row);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(dst + 4 * pc * kN),
-                                                     16, (row * rowBC + 8 * c) * 2, 0, 0, 0);
+                                                     16, (mem_row<REV>(row, nrows) * rowBC + 8 * c) * 2, 0, 0, 0);
         }
     };
     auto copy_x = [&](__bf16 *dst, int k) {
         const int64_t t0 = seg_t0 + static_cast<int64_t>(k) * SC;
         const int nrows = rows_of(k);
-        const auto r = mk(xg + t0 * rowX, nrows > 0 ? ((nrows - 1) * rowX + kP) * 2 : 0);
+        const auto r = mk(xg + first_token<REV>(len, t0, nrows) * rowX, nrows > 0 ? ((nrows - 1) * rowX + kP) * 2 : 0);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int px = wave + 4 * u, row = 8 * px + (lane >> 3), c = (lane & 7) ^ (2 * (row & 3));
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(dst + 8 * px * kP),
-                                                     16, (row * rowX + 8 * c) * 2, 0, 0, 0);
+                                                     16, (mem_row<REV>(row, nrows) * rowX + 8 * c) * 2, 0, 0, 0);
         }
     };
     // dt of sub-chunk k, token `lane` (zero past the end)
     auto load_dt = [&](int k) {
         const int64_t t0 = seg_t0 + static_cast<int64_t>(k) * SC;
         const int nrows = rows_of(k);
-        const auto r = mk(dtg + t0 * H, nrows > 0 ? ((nrows - 1) * H + 1) * 2 : 0);
-        return __builtin_amdgcn_raw_buffer_load_b16(r, lane * H * 2, 0, 0);
+        const auto r = mk(dtg + first_token<REV>(len, t0, nrows) * H, nrows > 0 ? ((nrows - 1) * H + 1) * 2 : 0);
+        return __builtin_amdgcn_raw_buffer_load_b16(r, mem_row<REV>(lane, nrows) * H * 2, 0, 0);
     };
     // cumulative log2-decays of a sub-chunk from its dt, into table buffer PH
     auto tables = [&](auto PH, unsigned short dbits) {
@@ -797,6 +829,33 @@ __device__ __forceinline__ void full_pass(const ScanArgs &a)
 #pragma unroll
             for (int m = 0; m < 2; ++m)
                 xf[m] = x_frag(bufX(PH), m, p0);
+            auto y_res = [&]() {
+                return mk(static_cast<Ty *>(a.y) + (tok0 + first_token<REV>(len, t0, nvalid)) * rowX,
+                          static_cast<int64_t>(nvalid) * rowX * sizeof(Ty));
+            };
+            auto y_off = [&](int tb) {
+                const int row = mem_row<REV>(16 * tb + r16, nvalid);
+                return ((row * H + h0) * kP + p0 + 4 * q) * static_cast<int>(sizeof(Ty));
+            };
+            // REV: the forward half's outputs of this wavefront's columns, loaded ahead of the
+            // copies so that waiting for them never waits for a copy
+            f32x4 yprev[4];
+            __amdgpu_buffer_rsrc_t yr;
+            if constexpr (REV) {
+                yr = y_res();
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    if constexpr (sizeof(Ty) == 2) {
+                        const bf16x4 v =
+                            __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(yr, y_off(tb), 0, 0));
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            yprev[tb][j] = bf2f(v[j]);
+                    } else {
+                        yprev[tb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(yr, y_off(tb), 0, 0));
+                    }
+                }
+            }
             __builtin_amdgcn_sched_barrier(0);
             unsigned short dn = 0;
             if constexpr (W == 0)
@@ -804,8 +863,8 @@ __device__ __forceinline__ void full_pass(const ScanArgs &a)
             copy_rows(Bg, bufB(PN{}), k + 1);
             copy_x(bufX(PN{}), k + 1);
             __builtin_amdgcn_sched_barrier(0);
-            const __amdgpu_buffer_rsrc_t yr =
-                mk(static_cast<Ty *>(a.y) + (tok0 + t0) * rowX, static_cast<int64_t>(nvalid) * rowX * sizeof(Ty));
+            if constexpr (!REV)
+                yr = y_res();
             const float(*tbl)[SC] = sT[ph];
             // (1) this wavefront's score tiles S[tb][sb] = B_s . C_t, decay-weighted (factored
             // below the diagonal 32-token pair, per element on it), stored for all
@@ -889,7 +948,12 @@ __device__ __forceinline__ void full_pass(const ScanArgs &a)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     o[j] = fmaf(Dh, bf2f(xv[j]), acc[tb][j]);
-                const int off = ((t * H + h0) * kP + pc) * static_cast<int>(sizeof(Ty));
+                if constexpr (REV) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        o[j] += yprev[tb][j];
+                }
+                const int off = y_off(tb);
                 if constexpr (sizeof(Ty) == 2) {
                     bf16x4 ov;
 #pragma unroll
@@ -994,37 +1058,52 @@ __device__ __forceinline__ void full_pass(const ScanArgs &a)
     }
 }
 
-__global__ __launch_bounds__(256, 2) void k_full_bf16(ScanArgs a) { full_pass<__bf16>(a); }
-__global__ __launch_bounds__(256, 2) void k_full_f32(ScanArgs a) { full_pass<float>(a); }
+__global__ __launch_bounds__(256, 2) void k_full_bf16(ScanArgs a) { full_pass<__bf16, false>(a); }
+__global__ __launch_bounds__(256, 2) void k_full_f32(ScanArgs a) { full_pass<float, false>(a); }
+__global__ __launch_bounds__(256, 2) void k_full_bf16_rev(ScanArgs a) { full_pass<__bf16, true>(a); }
+__global__ __launch_bounds__(256, 2) void k_full_f32_rev(ScanArgs a) { full_pass<float, true>(a); }
 
 template <bool FULL, int HPW, typename Ty>
-hipError_t launch_scan(const ScanArgs &a, hipStream_t st)
+hipError_t launch_scan(const ScanArgs &a, bool rev, hipStream_t st)
 {
     const int nwg = a.s.b * a.nseg * (a.s.H / HPW);
     if constexpr (FULL) {
         static_assert(HPW == 1, "the full pass runs one head per workgroup");
         if (a.y) {
-            if constexpr (sizeof(Ty) == 2)
-                k_full_bf16<<<dim3(nwg), dim3(256), 0, st>>>(a);
-            else
-                k_full_f32<<<dim3(nwg), dim3(256), 0, st>>>(a);
+            if constexpr (sizeof(Ty) == 2) {
+                if (rev)
+                    k_full_bf16_rev<<<dim3(nwg), dim3(256), 0, st>>>(a);
+                else
+                    k_full_bf16<<<dim3(nwg), dim3(256), 0, st>>>(a);
+            } else {
+                if (rev)
+                    k_full_f32_rev<<<dim3(nwg), dim3(256), 0, st>>>(a);
+                else
+                    k_full_f32<<<dim3(nwg), dim3(256), 0, st>>>(a);
+            }
             return hipGetLastError();
         }
     }
+    if (rev)  // the reverse order exists for the passes with y only
+        return hipErrorInvalidValue;
     k_scan<FULL, HPW><<<dim3(nwg), dim3(256), 0, st>>>(a);
     return hipGetLastError();
 }
 
 template <bool FULL, typename Ty>
-hipError_t launch_scan_hpw(const ScanArgs &a, int hpw, hipStream_t st)
+hipError_t launch_scan_hpw(const ScanArgs &a, int hpw, bool rev, hipStream_t st)
 {
     if constexpr (!FULL) {  // the state-only pass
         if (hpw == 2)
-            return launch_scan<FULL, 2, Ty>(a, st);
-        k_state<<<dim3(static_cast<unsigned>(a.s.b * a.nseg * a.s.H)), dim3(256), 0, st>>>(a);
+            return launch_scan<FULL, 2, Ty>(a, rev, st);
+        const dim3 grid(static_cast<unsigned>(a.s.b * a.nseg * a.s.H));
+        if (rev)
+            k_state_rev<<<grid, dim3(256), 0, st>>>(a);
+        else
+            k_state<<<grid, dim3(256), 0, st>>>(a);
         return hipGetLastError();
     } else {
-        return launch_scan<FULL, 1, Ty>(a, st);
+        return launch_scan<FULL, 1, Ty>(a, rev, st);
     }
 }
 
@@ -1073,12 +1152,14 @@ PrefixPlan prefix_mfma_plan(const Shape &s, int64_t len, int chunk, bool full, b
 
 hipError_t run_prefix_mfma(const Shape &s, int64_t len, int chunk, const Seq &in, const float *A,
                            const float *D, const float *h_init, void *y, float *chunk_states,
-                           float *h_out, void *ws, hipStream_t st, bool single_segment)
+                           float *h_out, void *ws, hipStream_t st, bool single_segment, bool rev)
 {
     const bool full = y || chunk_states;
+    if (rev && (!y || chunk_states))  // reverse order: y accumulated, nothing else
+        return hipErrorInvalidValue;
     const PrefixPlan p = prefix_mfma_plan(s, len, chunk, full, single_segment);
     const int hpw_full = pick_hpw(s, true, single_segment);
-    const int hpw_state = pick_hpw(s, false, single_segment || p.nseg == 1);
+    const int hpw_state = rev ? 1 : pick_hpw(s, false, single_segment || p.nseg == 1);
     ScanArgs a{};
     a.s = s;
     a.len = len;
@@ -1093,8 +1174,8 @@ hipError_t run_prefix_mfma(const Shape &s, int64_t len, int chunk, const Seq &in
         a.y = y;
         a.chunk_states = chunk_states;
         a.h_last = h_out;
-        return s.y_dt ? launch_scan_hpw<true, __bf16>(a, hpw_full, st)
-                      : launch_scan_hpw<true, float>(a, hpw_full, st);
+        return s.y_dt ? launch_scan_hpw<true, __bf16>(a, hpw_full, rev, st)
+                      : launch_scan_hpw<true, float>(a, hpw_full, rev, st);
     };
     if (p.nseg == 1) {
         // one segment per (stream, head): a single pass from h_init straight to h_out
@@ -1103,7 +1184,7 @@ hipError_t run_prefix_mfma(const Shape &s, int64_t len, int chunk, const Seq &in
         if (full)
             return run_full();
         a.h_end = h_out;
-        return launch_scan_hpw<false, float>(a, hpw_state, st);
+        return launch_scan_hpw<false, float>(a, hpw_state, rev, st);
     }
     hipError_t e;
     float *tot = static_cast<float *>(ws);
@@ -1112,7 +1193,7 @@ hipError_t run_prefix_mfma(const Shape &s, int64_t len, int chunk, const Seq &in
     a.h_in = nullptr;
     a.h_end = segs;
     a.tot = tot;
-    if ((e = launch_scan_hpw<false, float>(a, hpw_state, st)) != hipSuccess)
+    if ((e = launch_scan_hpw<false, float>(a, hpw_state, rev, st)) != hipSuccess)
         return e;
     // 2. states entering each segment (in place); the final state when nothing else follows
     {

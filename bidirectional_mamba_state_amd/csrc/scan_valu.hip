@@ -36,6 +36,8 @@ __device__ __forceinline__ uint16_t to_bf16(float v)
 }
 __device__ __forceinline__ void store_y(float *p, int64_t i, float v) { p[i] = v; }
 __device__ __forceinline__ void store_y(uint16_t *p, int64_t i, float v) { p[i] = to_bf16(v); }
+__device__ __forceinline__ float load_y(const float *p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float load_y(const uint16_t *p, int64_t i) { return load_in(p, i); }
 
 template <int N, int P>
 struct Lay {
@@ -70,7 +72,9 @@ __device__ __forceinline__ float token(float (&S)[NPT], const Tin *Bt, const Tin
     return part;
 }
 
-// Forward recurrence over one segment of one (stream, head). grid = (nseg, H, b).
+// Forward recurrence over one segment of one (stream, head). grid = (nseg, H, b). With
+// a.rev the scan runs over the tokens in reverse (position t is token len - 1 - t) and adds
+// its outputs to y.
 template <typename Tin, typename Ty, int N, int P, bool WANT_Y>
 __global__ __launch_bounds__(kThreads) void k_forward(ForwardArgs a)
 {
@@ -99,10 +103,10 @@ __global__ __launch_bounds__(kThreads) void k_forward(ForwardArgs a)
     const Tin *Cm = static_cast<const Tin *>(a.in.C);
     Ty *y = static_cast<Ty *>(a.y);
     const float Ah = a.A[h];
-    const float Dh = a.D[h];
+    const float Dh = a.D ? a.D[h] : 0.f;
     float dsum = 0.f;
     for (int64_t t = t0; t < t1; ++t) {
-        const int64_t tok = static_cast<int64_t>(b) * a.len + t;
+        const int64_t tok = static_cast<int64_t>(b) * a.len + (a.rev ? a.len - 1 - t : t);
         const float dtv = load_in(dt, tok * H + h);
         const float la = dtv * Ah;
         dsum += la;
@@ -112,8 +116,11 @@ __global__ __launch_bounds__(kThreads) void k_forward(ForwardArgs a)
         float part = token<Tin, L::R, L::NPT, WANT_Y>(S, Bm + bc, WANT_Y ? Cm + bc : nullptr, alpha, dtv * xv, r);
         if (WANT_Y) {
             part = reduce_lanes<L::R>(part);
-            if (r == 0)
-                store_y(y, (tok * H + h) * P + p, fmaf(Dh, xv, part));
+            if (r == 0) {
+                const int64_t o = (tok * H + h) * P + p;
+                const float v = fmaf(Dh, xv, part);
+                store_y(y, o, a.rev ? v + load_y(y, o) : v);
+            }
         }
     }
     if (a.state_out) {

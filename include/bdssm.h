@@ -180,6 +180,36 @@ bdssm_status bdssm_block_step_ex(const bdssm_dims *dims, int32_t block_len,
                                  const float *A_rev, const float *D_rev, void *y, void *stream);
 
 /*
+ * Full-window bidirectional scan: the system the block-local method is compared against, a
+ * fully bidirectional Mamba layer over the whole sequence ("DiffuApriel", Sec. 3.2, eqs.
+ * (4)-(6): a forward and a backward scan, each with its own parameters, summed; the
+ * full-sequence bidirectional baselines of "Training Hybrid Block Diffusion Language Models
+ * with Partial Bidirectionality", whose directionality discussion explains why their reverse
+ * states cannot be cached). Over one window of len tokens -- the prefix and the active block
+ * together -- with nothing cached:
+ *   y_t = C_t . S_t             (forward scan from a zero state at token 0, over fwd)
+ *       + C'_t . R_t            (reverse scan from a zero state past token len-1, over rev,
+ *                                decaying with A_rev)
+ *       + D[h] * x_fwd[t] (+ D_rev[h] * x_rev[t] when D_rev is given)
+ * for every token of the window. Since the reverse states of prefix tokens depend on the
+ * active block, a full-window model recomputes all of this on every denoising step; on the
+ * block's own tokens the result equals bdssm_block_step from the prefix's state.
+ *   fwd, rev        the two directions' inputs, len tokens each, natural token order
+ *   A, D            [H] float32; A_rev [H] float32, required (pass A for a shared decay);
+ *                   D_rev [H] float32 or NULL
+ *   y               [b][len][H][P] in dims->y_dtype, written (forward half) then added to
+ *                   (reverse half, so bf16 y is rounded twice); must not overlap any input
+ *   chunk, workspace  as in bdssm_prefix_scan (bdssm_full_window_workspace bytes; both
+ *                   directions use the same workspace in turn)
+ * Errors as bdssm_prefix_scan.
+ */
+size_t bdssm_full_window_workspace(const bdssm_dims *dims, int64_t len, int32_t chunk);
+bdssm_status bdssm_full_window(const bdssm_dims *dims, int64_t len, int32_t chunk, const bdssm_seq *fwd,
+                               const bdssm_seq *rev, const float *A, const float *D, const float *A_rev,
+                               const float *D_rev, void *y, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/*
  * Commit: the clean forward pass over a finalized block of T = block_len tokens that
  * extends the cache, S <- F_fwd(clean; S), in place on h.
  *   clean  the block's clean inputs; clean->C may be NULL when y is NULL

@@ -58,13 +58,15 @@ def _load():
         lib.oracle_block_step_ex.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int64, P,
                                              ctypes.POINTER(_Seq), ctypes.POINTER(_Seq),
                                              P, P, P, P, P, P, P, P, ctypes.c_int]
+        lib.oracle_full_window.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int64, ctypes.POINTER(_Seq),
+                                           ctypes.POINTER(_Seq), P, P, P, P, P, P, ctypes.c_int]
         lib.oracle_commit.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int64,
                                       ctypes.POINTER(_Seq), P, P, P, P, P, ctypes.c_int]
         lib.oracle_conv.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int64, ctypes.c_int32,
                                     ctypes.c_int32, ctypes.c_int32, P, P, P,
                                     ctypes.POINTER(_Seq), ctypes.POINTER(_Seq), P, ctypes.c_int]
         for f in (lib.oracle_scan, lib.oracle_block_step, lib.oracle_block_step_ex, lib.oracle_commit,
-                  lib.oracle_conv):
+                  lib.oracle_conv, lib.oracle_full_window):
             f.restype = ctypes.c_int
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -164,6 +166,26 @@ def block_step(h_prefix, fwd, rev, A, D, heads=None, nthreads=0, A_rev=None, D_r
     if rc:
         raise ValueError("oracle_block_step rejected its arguments")
     return y, yf, yr
+
+
+def full_window(fwd, rev, A, D, A_rev=None, D_rev=None, heads=None, nthreads=0):
+    """Full-window bidirectional scan (oracle_full_window): forward from zero over the whole
+    window of fwd, reverse from zero at its end over rev (decay A_rev, default A), plus
+    D x_fwd (and D_rev x_rev). Returns y [b, len, H, P] float64."""
+    cf, cr = _Call(fwd), _Call(rev)
+    b, L, H, P = fwd.x.shape
+    G = fwd.B.shape[2]
+    y = np.zeros((b, L, H, P))
+    A = np.ascontiguousarray(A, np.float32)
+    D = np.ascontiguousarray(D, np.float32)
+    Ar = None if A_rev is None else np.ascontiguousarray(A_rev, np.float32)
+    Dr = None if D_rev is None else np.ascontiguousarray(D_rev, np.float32)
+    m = _mask(heads, H)
+    rc = _load().oracle_full_window(ctypes.byref(_dims(fwd, G)), L, ctypes.byref(cf.s), ctypes.byref(cr.s),
+                                    _ptr(A), _ptr(D), _ptr(Ar), _ptr(Dr), _ptr(y), _ptr(m), nthreads)
+    if rc:
+        raise ValueError("oracle_full_window rejected its arguments")
+    return y
 
 
 def commit(h, clean, A, D, want_y=False, heads=None, nthreads=0):

@@ -267,6 +267,33 @@ int oracle_block_step(const oracle_dims *d, int64_t T, const double *h_prefix,
                                 head_mask, nthreads);
 }
 
+/*
+ * Full-window bidirectional scan: the system the block-local method replaces -- a fully
+ * bidirectional Mamba layer over the whole sequence ("DiffuApriel", Sec. 3.2, eqs. (4)-(6):
+ * forward and backward scans with their own parameters, summed; the full-sequence
+ * baselines of the BDLM page, whose reverse states depend on the active tokens and so cannot
+ * be cached). Over one window of len tokens (prefix and active block together) nothing is
+ * cached: the forward scan starts from a zero state at token 0 and the reverse scan from a
+ * zero state past token len-1, and y = y_fwd + y_rev + D x_fwd (+ D_rev x_rev). That is
+ * exactly the block step's pair of scans (eqs. (11)-(13)) taken over the whole window with
+ * a zero cached state, which is how it is computed here.
+ */
+int oracle_full_window(const oracle_dims *d, int64_t len, const oracle_seq *fwd, const oracle_seq *rev,
+                       const float *A, const float *D, const float *A_rev, const float *D_rev, double *y,
+                       const int8_t *head_mask, int nthreads)
+{
+    if (check(d) || len < 1)
+        return 1;
+    const int64_t n = (int64_t)d->batch * d->nheads * d->d_state * d->headdim;
+    double *zero = calloc((size_t)n, sizeof(double));
+    if (!zero)
+        return 1;
+    const int rc = oracle_block_step_ex(d, len, zero, fwd, rev, A, D, A_rev, D_rev, y, NULL, NULL, head_mask,
+                                        nthreads);
+    free(zero);
+    return rc;
+}
+
 /* Commit: the clean forward pass over a finalized block, advancing h in place.
  * y (with D) is optional. */
 int oracle_commit(const oracle_dims *d, int64_t T, const oracle_seq *clean, const float *A,

@@ -316,3 +316,38 @@ def test_prefix_scan_static_rejects_oversized_plans():
     # the usual validation comes first
     assert lib.bdssm_prefix_scan_static(None, L, chunk, ctypes.byref(s), FAKE, FAKE, None, y, None,
                                         FAKE + 8192, None) == bdssm.ERR_NULL
+
+
+def test_full_window_validation():
+    """bdssm_full_window validates before any launch: NULL pointers, shapes, chunks, aliasing
+    of y with the inputs, and the workspace (the prefix scan's with outputs)."""
+    lib = bdssm.load()
+    d = bdssm.dims(1, 4, 64, 128, 1, bdssm.BF16, bdssm.F32)
+    L = 4096
+    need = lib.bdssm_full_window_workspace(ctypes.byref(d), L, 256)
+    assert need == bdssm.prefix_scan_workspace(d, L, 256, True, False) and need > 0
+    base = 1 << 40
+    f = bdssm.SeqPtrs(base, base + (1 << 36), base + (2 << 36), base + (3 << 36))
+    r = bdssm.SeqPtrs(base + (4 << 36), base + (5 << 36), base + (6 << 36), base + (7 << 36))
+    y = base + (8 << 36)
+    ws = base + (9 << 36)
+
+    def call(dd=d, length=L, chunk=256, fw=f, rv=r, A=FAKE, D=FAKE + 256, Ar=FAKE + 512, Dr=None, yy=y, w=ws,
+             wb=need):
+        return lib.bdssm_full_window(None if dd is None else ctypes.byref(dd), length, chunk,
+                                     None if fw is None else ctypes.byref(fw), None if rv is None else ctypes.byref(rv),
+                                     A, D, Ar, Dr, yy, w, wb, None)
+
+    assert call(dd=None) == bdssm.ERR_NULL
+    assert call(fw=None) == bdssm.ERR_NULL
+    assert call(rv=bdssm.SeqPtrs(base, base, base, None)) == bdssm.ERR_NULL     # C is needed
+    assert call(Ar=None) == bdssm.ERR_NULL
+    assert call(yy=None) == bdssm.ERR_NULL
+    assert call(length=-1) == bdssm.ERR_SHAPE
+    assert call(chunk=48) == bdssm.ERR_UNSUPPORTED
+    assert call(yy=y + 2) == bdssm.ERR_ALIGN
+    assert call(yy=f.x) == bdssm.ERR_ALIAS                                     # y over an input
+    assert call(w=None, wb=0) == bdssm.ERR_WORKSPACE
+    assert call(wb=need - 1) == bdssm.ERR_WORKSPACE
+    assert call(w=r.B) == bdssm.ERR_ALIAS                                      # workspace over an input
+    assert call(length=0) == bdssm.OK                                          # nothing to do

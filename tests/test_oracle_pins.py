@@ -206,6 +206,64 @@ def test_reverse_is_flipped_forward():
     assert rel(y, yr) < 1e-14                   # zero forward input and state: y = y_rev
 
 
+@pytest.mark.parametrize("G", [1, 2])
+def test_full_window_matches_quadratic_form(G):
+    """The full-window bidirectional scan against the dual form over the whole window: the
+    causal sum from a zero state at the start, the anti-causal sum from a zero state past the
+    end (with the reverse decay), and both skip terms."""
+    rng = np.random.default_rng(31 + G)
+    b, L, H, P, N = 2, 37, 4, 3, 5
+    fwd = rand_seq(rng, b, L, H, P, N, G)
+    rev = rand_seq(rng, b, L, H, P, N, G)
+    A, D = rand_params(rng, H)
+    Ar, Dr = rand_params(rng, H)
+    y = oracle.full_window(fwd, rev, A, D, A_rev=Ar, D_rev=Dr)
+    qf, _ = quad_forward(fwd, A, D, np.zeros((b, H, N, P)), with_D=False)
+    qr = quad_reverse(rev, Ar)
+    xf, xr = dec(fwd)[0], dec(rev)[0]
+    assert rel(y, qf + qr + D[None, None, :, None] * xf + Dr[None, None, :, None] * xr) < 1e-12
+    y2 = oracle.full_window(fwd, rev, A, D)
+    assert rel(y2, qf + quad_reverse(rev, A) + D[None, None, :, None] * xf) < 1e-12
+
+
+def test_full_window_reverse_is_flipped_forward_scan():
+    """With no forward input, the full window's output is the forward scan of the flipped
+    reverse inputs, flipped back."""
+    rng = np.random.default_rng(33)
+    b, L, H, P, N, G = 2, 50, 3, 4, 6, 1
+    rev = rand_seq(rng, b, L, H, P, N, G)
+    zero_fwd = Seq(np.zeros_like(rev.x), rev.dt, rev.B, rev.C, rev.dtype)
+    A, _ = rand_params(rng, H)
+    y = oracle.full_window(zero_fwd, rev, A, np.zeros(H, np.float32))
+    flip = Seq(*(np.ascontiguousarray(a[:, ::-1]) for a in (rev.x, rev.dt, rev.B, rev.C)), rev.dtype)
+    yflip, _, _ = oracle.scan(flip, A, np.zeros(H, np.float32), chunk=16, want_chunk_states=False)
+    assert rel(y, yflip[:, ::-1]) < 1e-13
+
+
+def test_full_window_on_the_block_equals_the_block_step():
+    """On the active block's tokens, the full-window scan over prefix || block equals the
+    block step from the prefix's state: the forward scan carries the prefix in its state and
+    the reverse scan reaches the block's tokens before any prefix token. On prefix tokens it
+    does not equal the prefix scan's outputs: their reverse states depend on the block."""
+    rng = np.random.default_rng(34)
+    b, L, T, H, P, N, G = 2, 45, 13, 4, 3, 5, 2
+    pre = rand_seq(rng, b, L, H, P, N, G)
+    pre_rev = rand_seq(rng, b, L, H, P, N, G)
+    fwd = rand_seq(rng, b, T, H, P, N, G)
+    rev = rand_seq(rng, b, T, H, P, N, G)
+    A, D = rand_params(rng, H)
+    cat = lambda u, v: Seq(*(np.concatenate([p, q], axis=1) for p, q in zip((u.x, u.dt, u.B, u.C),
+                                                                             (v.x, v.dt, v.B, v.C))), u.dtype)
+    y = oracle.full_window(cat(pre, fwd), cat(pre_rev, rev), A, D)
+    _, _, h = oracle.scan(pre, A, D, chunk=16, want_y=False, want_chunk_states=False)
+    yb, _, _ = oracle.block_step(h, fwd, rev, A, D)
+    assert rel(y[:, L:], yb) < 1e-12
+    # the prefix tokens' outputs change with the block's reverse inputs
+    rev2 = Seq(rev.x * np.float32(2), rev.dt, rev.B, rev.C, rev.dtype)
+    y2 = oracle.full_window(cat(pre, fwd), cat(pre_rev, rev2), A, D)
+    assert rel(y2[:, :L], y[:, :L]) > 1e-6
+
+
 def test_scan_associativity_and_commit_chain():
     rng = np.random.default_rng(4)
     b, H, P, N, G = 2, 4, 3, 4, 2
@@ -500,6 +558,8 @@ PLANTS = {
     "conv state ignored": ("(!reverse && state_in) ?", "(0 && state_in) ?"),
     "conv state not advanced": ("u[len + k]);", "u[k]);"),
     "activation dropped": ("v = v / (1.0 + exp(-v));", "v = v * 1.0;"),
+    "full window drops the reverse parameters": ("zero, fwd, rev, A, D, A_rev, D_rev, y,",
+                                                 "zero, fwd, rev, A, D, NULL, NULL, y,"),
 }
 
 
@@ -527,7 +587,7 @@ def test_planted_mistake_is_caught(tmp_path, monkeypatch, name):
                  lambda: test_conv_matches_shifted_slices(BF16, False),
                  lambda: test_conv_matches_shifted_slices(F32, True),
                  test_conv_identity_shift_and_flip, test_conv_state_chains_and_silu_values,
-                 test_block_step_and_commit_with_conv):
+                 test_block_step_and_commit_with_conv, lambda: test_full_window_matches_quadratic_form(2)):
         try:
             test()
         except AssertionError:
