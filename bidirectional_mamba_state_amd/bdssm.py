@@ -25,7 +25,9 @@ EXPORTS = ("bdssm_abi_version", "bdssm_status_str", "bdssm_prefix_scan_workspace
            "bdssm_conv_workspace", "bdssm_conv", "bdssm_block_step_conv", "bdssm_commit_conv",
            "bdssm_state_ops_bytes", "bdssm_state_ops", "bdssm_block_step_ops",
            "bdssm_set_launch_override", "bdssm_prefix_scan_static",
-           "bdssm_full_window_workspace", "bdssm_full_window")
+           "bdssm_full_window_workspace", "bdssm_full_window",
+           "bdssm_state_bf16_bytes", "bdssm_state_bf16", "bdssm_block_step_variant")
+STATE_F32, STATE_OPS, STATE_BF16 = 0, 1, 2
 
 
 class BdssmError(RuntimeError):
@@ -49,6 +51,11 @@ class SeqPtrs(ctypes.Structure):
 class LaunchOverride(ctypes.Structure):
     _fields_ = [("block_kernel", ctypes.c_int32), ("lat_waves", ctypes.c_int32),
                 ("bw_heads", ctypes.c_int32), ("bw_splits", ctypes.c_int32)]
+
+
+class StepParams(ctypes.Structure):
+    _fields_ = [("A", ctypes.c_void_p), ("D", ctypes.c_void_p), ("A_rev", ctypes.c_void_p),
+                ("D_rev", ctypes.c_void_p), ("skip_per_channel", ctypes.c_int32)]
 
 
 class ConvParams(ctypes.Structure):
@@ -110,6 +117,12 @@ def load():
         lib.bdssm_full_window_workspace.argtypes = [P(Dims), I64, I32]
         lib.bdssm_full_window.restype = ctypes.c_int
         lib.bdssm_full_window.argtypes = [P(Dims), I64, I32, P(SeqPtrs), P(SeqPtrs), V, V, V, V, V, V, SZ, V]
+        lib.bdssm_state_bf16_bytes.restype = SZ
+        lib.bdssm_state_bf16_bytes.argtypes = [P(Dims)]
+        lib.bdssm_state_bf16.restype = ctypes.c_int
+        lib.bdssm_state_bf16.argtypes = [P(Dims), V, V, V]
+        lib.bdssm_block_step_variant.restype = ctypes.c_int
+        lib.bdssm_block_step_variant.argtypes = [P(Dims), I32, V, I32, P(SeqPtrs), P(SeqPtrs), P(StepParams), V, V]
         lib.bdssm_set_launch_override.restype = ctypes.c_int
         lib.bdssm_set_launch_override.argtypes = [P(LaunchOverride)]
         _lib = lib
@@ -243,6 +256,25 @@ def set_launch_override(block_kernel=0, lat_waves=0, bw_heads=0, bw_splits=0):
     kernel and its launch shape for later calls; all zeros = automatic."""
     o = LaunchOverride(block_kernel, lat_waves, bw_heads, bw_splits)
     _check(load().bdssm_set_launch_override(ctypes.byref(o)))
+
+
+def state_bf16_bytes(d):
+    """bdssm_state_bf16_bytes (SIZE_MAX for invalid or unsupported dims)."""
+    return load().bdssm_state_bf16_bytes(ctypes.byref(d))
+
+
+def state_bf16(d, h, out, stream=None):
+    """bdssm_state_bf16: the bf16 copy of the cached state h, into out."""
+    _check(load().bdssm_state_bf16(ctypes.byref(d), _ptr(h), _ptr(out), _stream(stream)))
+
+
+def block_step_variant(d, block_len, state, state_form, fwd, rev, A, D, y, A_rev=None, D_rev=None,
+                       skip_per_channel=False, stream=None):
+    """bdssm_block_step_variant: the state as float32, operand form or bf16 (state_form), skip
+    weights per head or per channel."""
+    prm = StepParams(_ptr(A), _ptr(D), _ptr(A_rev), _ptr(D_rev), int(skip_per_channel))
+    _check(load().bdssm_block_step_variant(ctypes.byref(d), block_len, _ptr(state), state_form, _byref(_seq(fwd)),
+                                           _byref(_seq(rev)), ctypes.byref(prm), _ptr(y), _stream(stream)))
 
 
 def commit(d, block_len, clean, A, D, h, y=None, stream=None):

@@ -154,10 +154,12 @@ void override_block_plan(const Shape &s, int *hpw, int *ps)
 }
 
 // Validates a block step and fills its kernel arguments (nothing is launched).
+// state_elt: bytes per state element as stored (4: float32 or operand form, 2: bf16);
+// dch: skip weights per head and channel ([H][P]).
 bdssm_status prepare_block_step(const bdssm_dims *dims, int32_t block_len, const float *h_prefix,
                                 const bdssm_seq *fwd, const bdssm_seq *rev, const float *A,
                                 const float *D, const float *A_rev, const float *D_rev, void *y,
-                                BlockArgs *out)
+                                BlockArgs *out, int state_elt = 4, bool dch = false)
 {
     Shape s;
     bdssm_status rc = check_dims(dims, &s);
@@ -178,13 +180,16 @@ bdssm_status prepare_block_step(const bdssm_dims *dims, int32_t block_len, const
         !aligned(y))
         return BDSSM_ERR_ALIGN;
     const int64_t NP = static_cast<int64_t>(s.N) * s.P;
+    const int64_t dbytes = (dch ? static_cast<int64_t>(s.H) * s.P : s.H) * 4;
     const Range ry = rng(y, static_cast<int64_t>(s.b) * block_len * s.H * s.P * elt(s.y_dt));
-    if (hits(ry, qf) || hits(ry, qr) || overlap(ry, rng(h_prefix, static_cast<int64_t>(s.b) * s.H * NP * 4)) ||
-        overlap(ry, rng(A, s.H * 4)) || overlap(ry, rng(D, s.H * 4)) || overlap(ry, rng(A_rev, s.H * 4)) ||
-        overlap(ry, rng(D_rev, s.H * 4)))
+    if (hits(ry, qf) || hits(ry, qr) ||
+        overlap(ry, rng(h_prefix, static_cast<int64_t>(s.b) * s.H * NP * state_elt)) ||
+        overlap(ry, rng(A, s.H * 4)) || overlap(ry, rng(D, dbytes)) || overlap(ry, rng(A_rev, s.H * 4)) ||
+        overlap(ry, rng(D_rev, dbytes)))
         return BDSSM_ERR_ALIAS;
     *out = BlockArgs{s, block_len, h_prefix, Seq{fwd->x, fwd->dt, fwd->B, fwd->C},
                      Seq{rev->x, rev->dt, rev->B, rev->C}, A, D, y, A_rev, D_rev};
+    out->d_per_channel = dch ? 1 : 0;
     return BDSSM_OK;
 }
 
@@ -690,6 +695,78 @@ bdssm_status bdssm_block_step_ops(const bdssm_dims *dims, int32_t block_len, con
     int hpw = block_bw_plan(a.s), ps = 1;
     override_block_plan(a.s, &hpw, &ps);
     return launched(launch_block_step_bw(a, hpw, st));
+}
+
+size_t bdssm_state_bf16_bytes(const bdssm_dims *dims)
+{
+    Shape s;
+    if (check_dims(dims, &s) != BDSSM_OK || s.N % 8 != 0)
+        return SIZE_MAX;
+    return static_cast<size_t>(s.b) * s.H * s.N * s.P * 2;
+}
+
+bdssm_status bdssm_state_bf16(const bdssm_dims *dims, const float *h, void *out, void *stream)
+{
+    Shape s;
+    const bdssm_status rc = check_dims(dims, &s);
+    if (rc != BDSSM_OK)
+        return rc;
+    if (s.N % 8 != 0)
+        return BDSSM_ERR_UNSUPPORTED;
+    if (!h || !out)
+        return BDSSM_ERR_NULL;
+    if (!aligned(h) || !aligned(out))
+        return BDSSM_ERR_ALIGN;
+    const int64_t n = static_cast<int64_t>(s.b) * s.H * s.N * s.P;
+    if (overlap(rng(out, n * 2), rng(h, n * 4)))
+        return BDSSM_ERR_ALIAS;
+    if (n == 0)
+        return BDSSM_OK;
+    return launched(launch_state_bf16(h, out, static_cast<int64_t>(s.b) * s.H, s.N, s.P,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+bdssm_status bdssm_block_step_variant(const bdssm_dims *dims, int32_t block_len, const void *state,
+                                      int32_t state_form, const bdssm_seq *fwd, const bdssm_seq *rev,
+                                      const bdssm_step_params *params, void *y, void *stream)
+{
+    if (!params)
+        return BDSSM_ERR_NULL;
+    if (state_form != BDSSM_STATE_F32 && state_form != BDSSM_STATE_OPS && state_form != BDSSM_STATE_BF16)
+        return BDSSM_ERR_UNSUPPORTED;
+    if (params->skip_per_channel != 0 && params->skip_per_channel != 1)
+        return BDSSM_ERR_UNSUPPORTED;
+    const bool dch = params->skip_per_channel != 0;
+    const float *A_rev = params->A_rev ? params->A_rev : params->A;
+    BlockArgs a{};
+    const bdssm_status rc = prepare_block_step(dims, block_len, static_cast<const float *>(state), fwd, rev,
+                                               params->A, params->D, A_rev, params->D_rev, y, &a,
+                                               state_form == BDSSM_STATE_BF16 ? 2 : 4, dch);
+    if (rc != BDSSM_OK)
+        return rc;
+    const Shape &s = a.s;
+    const bool mc = s.in_dt == 1 && s.N == 128 && s.P == 64;  // the matrix-core kernels' shapes
+    if (state_form == BDSSM_STATE_OPS && (!mc || block_len > 128))
+        return BDSSM_ERR_UNSUPPORTED;
+    if (state_form == BDSSM_STATE_BF16 && s.N % 8 != 0)
+        return BDSSM_ERR_UNSUPPORTED;
+    if (s.b == 0 || block_len == 0)
+        return BDSSM_OK;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (state_form == BDSSM_STATE_F32)
+        return launch_block_step(a, st);
+    a.h_ops = state;
+    a.h_prefix = nullptr;
+    a.ops_hi_only = state_form == BDSSM_STATE_BF16 ? 1 : 0;
+    if (use_block_lat(s, block_len))
+        return launched(launch_block_step_lat(a, override_of(OV_LAT_WAVES), st));
+    if (mc && block_bw_supported(s, block_len)) {
+        int hpw = block_bw_plan(s), ps = 1;
+        override_block_plan(s, &hpw, &ps);
+        return launched(launch_block_step_bw(a, hpw, st));
+    }
+    // the bf16 state on the vector-ALU kernel (float32 inputs, other shapes, T > 128)
+    return launched(launch_block_step_valu(a, st));
 }
 
 bdssm_status bdssm_commit(const bdssm_dims *dims, int32_t block_len, const bdssm_seq *clean,

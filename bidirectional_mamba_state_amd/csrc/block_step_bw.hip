@@ -36,22 +36,26 @@ constexpr int kOpsElems = 2 * kN * kP;  // one head's state in operand form, bf1
 enum { TAB_CF, TAB_CR, TAB_LGF, TAB_LGR, TAB_COLF, TAB_COLR, TAB_EF, NTAB };
 
 // two workgroups per CU: four wavefronts per SIMD, 128 registers each
-template <int NB, typename Ty>
+// HI_ONLY: the cached state is its bf16 hi part only (the bf16 cached state): half the state
+// copies, one state product instead of two. DCH: skip weights per head and channel.
+template <int NB, typename Ty, bool HI_ONLY, bool DCH>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_block_bw(BlockArgs a, int hpw, int n_hg)
 {
+    constexpr int kStateElems = HI_ONLY ? kOpsElems / 2 : kOpsElems;  // one head's state in HBM
     constexpr int TP = 16 * NB;         // padded block length
     constexpr int PBW = NB / 2;         // 16-column blocks per wavefront (4, 2, 1)
     constexpr int PGRP = 4 / PBW;       // column groups per row block
     static_assert(NB * PGRP == kWaves, "one wavefront per (row block, column group)");
     constexpr int XPD = TP / 8;         // 1 KB x copies per direction (8 rows each)
     constexpr int NX = 2 * XPD / kWaves;               // per wavefront
-    constexpr int NS = kOpsElems * 2 / 1024 / kWaves;  // state copies per wavefront (4)
+    constexpr int NS = kStateElems * 2 / 1024 / kWaves;  // state copies per wavefront (4, or 2)
 
     __shared__ __attribute__((aligned(16))) __bf16 hop[kOpsElems];  // the head's state
     __shared__ __attribute__((aligned(16))) __bf16 xs0[TP * kP];    // x, forward
     __shared__ __attribute__((aligned(16))) __bf16 xs1[TP * kP];    // x, reverse
     __shared__ __attribute__((aligned(16))) float tab[2][NTAB][TP]; // decay tables, two heads
     __shared__ float skip[2][2];                                     // D, D_rev of those heads
+    __shared__ __attribute__((aligned(16))) float skipc[DCH ? 2 : 1][2][DCH ? kP : 1];  // DCH: per channel
 
     // Workgroups of one stream (and so of its B, C) go to the same XCD: the hardware deals
     // linear workgroup ids round-robin over the 8 XCDs.
@@ -80,8 +84,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4, 
     const int64_t dt_bytes = static_cast<int64_t>(T) * H * 2;
     const auto rDf = buffer_range(static_cast<const __bf16 *>(a.fwd.dt) + tok0 * H, dt_bytes);
     const auto rDr = buffer_range(static_cast<const __bf16 *>(a.rev.dt) + tok0 * H, dt_bytes);
-    const auto rH = buffer_range(static_cast<const __bf16 *>(a.h_ops) + (static_cast<int64_t>(b) * H + h0) * kOpsElems,
-                                 static_cast<int64_t>(hpw) * kOpsElems * 2);
+    const auto rH = buffer_range(static_cast<const __bf16 *>(a.h_ops) + (static_cast<int64_t>(b) * H + h0) * kStateElems,
+                                 static_cast<int64_t>(hpw) * kStateElems * 2);
     const auto rY = buffer_range(static_cast<Ty *>(a.y) + tok0 * rowX, static_cast<int64_t>(T) * rowX * sizeof(Ty));
 
     // ---- copies into LDS. State: this wavefront's NS pieces of head h0 + hh, in place
@@ -92,7 +96,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4, 
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
             const int k = w * NS + i;
-            copy_to_lds(rH, &hop[k * 512], (hh * kOpsElems + k * 512 + 8 * lane) * 2);
+            copy_to_lds(rH, &hop[k * 512], (hh * kStateElems + k * 512 + 8 * lane) * 2);
         }
     };
     auto copy_x = [&](int h, int skip_bytes) {
@@ -110,15 +114,22 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4, 
     // nothing else (memory operations complete in order).
     struct Head {
         unsigned short d0, d1;  // dt of tokens 2 lane, 2 lane + 1
-        float A, D;             // decay and skip weight of the direction (D_rev: 0 if none)
+        float A, D;             // decay and skip weight of the direction (D_rev: 0 if none);
+                                // DCH: the skip weight of column `lane`
     };
     auto load_head = [&](int dir, int h, Head &hd) {
         const auto r = dir ? rDr : rDf;
         hd.d0 = __builtin_amdgcn_raw_buffer_load_b16(r, (2 * lane * H + h) * 2, 0, 0);
         hd.d1 = __builtin_amdgcn_raw_buffer_load_b16(r, ((2 * lane + 1) * H + h) * 2, 0, 0);
         hd.A = dir ? a.A_rev[h] : a.A[h];  // the reverse scan has its own decay
-        const float dv = (dir && a.D_rev ? a.D_rev : a.D)[h];
-        hd.D = dir && !a.D_rev ? 0.f : dv;
+        if constexpr (DCH) {
+            const float *dsrc = dir ? a.D_rev : a.D;
+            hd.D = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                 buffer_range(dsrc, dsrc ? H * kP * 4 : 0), (h * kP + lane) * 4, 0, 0));
+        } else {
+            const float dv = (dir && a.D_rev ? a.D_rev : a.D)[h];
+            hd.D = dir && !a.D_rev ? 0.f : dv;
+        }
         __builtin_amdgcn_sched_barrier(0);  // all of them ahead of the copies that follow
     };
     auto build_tables = [&](int dir, int buf, const Head &hd) {
@@ -153,7 +164,10 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4, 
                 tab[buf][TAB_EF][t1] = __builtin_amdgcn_exp2f(c1);
             }
         }
-        skip[buf][dir] = hd.D;  // every lane (a branch would delay the load to here)
+        if constexpr (DCH)
+            skipc[buf][dir][lane] = hd.D;
+        else
+            skip[buf][dir] = hd.D;  // every lane (a branch would delay the load to here)
     };
 
     // Rows past T: their copies read past the range and may leave the LDS rows as they
@@ -275,9 +289,11 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4, 
                 for (int pb = 0; pb < PBW; ++pb) {
                     const int pc = (pgrp * PBW + pb) * 16 + r16;
                     const bf16x8 hi = *reinterpret_cast<const bf16x8 *>(&hop[((4 * kk + q) * kP + pc) * 8]);
-                    const bf16x8 lo = *reinterpret_cast<const bf16x8 *>(&hop[((16 + 4 * kk + q) * kP + pc) * 8]);
                     acc[pb] = mfma(hi, cfw[kk], acc[pb]);
-                    acc[pb] = mfma(lo, cfw[kk], acc[pb]);
+                    if constexpr (!HI_ONLY) {
+                        const bf16x8 lo = *reinterpret_cast<const bf16x8 *>(&hop[((16 + 4 * kk + q) * kP + pc) * 8]);
+                        acc[pb] = mfma(lo, cfw[kk], acc[pb]);
+                    }
                 }
             }
             workgroup_lds_barrier<63>();  // everyone's state reads are done
@@ -371,10 +387,18 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4, 
                 const bf16x4 xf = *reinterpret_cast<const bf16x4 *>(&xs0[xo]);
                 const bf16x4 xr = *reinterpret_cast<const bf16x4 *>(&xs1[xo]);
                 float o[4];
+                if constexpr (DCH) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float v = fmaf(Dh, bf2f(xf[j]), acc[pb][j]);
-                    o[j] = with_dr ? fmaf(Dr, bf2f(xr[j]), v) : v;
+                    for (int j = 0; j < 4; ++j) {
+                        const float v = fmaf(skipc[cur][0][p0 + j], bf2f(xf[j]), acc[pb][j]);
+                        o[j] = with_dr ? fmaf(skipc[cur][1][p0 + j], bf2f(xr[j]), v) : v;
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float v = fmaf(Dh, bf2f(xf[j]), acc[pb][j]);
+                        o[j] = with_dr ? fmaf(Dr, bf2f(xr[j]), v) : v;
+                    }
                 }
                 const int off = (t * rowX + h * kP + p0) * static_cast<int>(sizeof(Ty));
                 if constexpr (sizeof(Ty) == 2) {
@@ -413,7 +437,13 @@ hipError_t launch_nb(const BlockArgs &a, int hpw, hipStream_t st)
 {
     const int n_hg = a.s.H / hpw;
     const int nwg = a.s.b * n_hg;
-    k_block_bw<NB, Ty><<<dim3(nwg), dim3(64 * kWaves), 0, st>>>(a, hpw, n_hg);
+    const dim3 grid(nwg), block(64 * kWaves);
+    if (a.ops_hi_only)
+        a.d_per_channel ? k_block_bw<NB, Ty, true, true><<<grid, block, 0, st>>>(a, hpw, n_hg)
+                        : k_block_bw<NB, Ty, true, false><<<grid, block, 0, st>>>(a, hpw, n_hg);
+    else
+        a.d_per_channel ? k_block_bw<NB, Ty, false, true><<<grid, block, 0, st>>>(a, hpw, n_hg)
+                        : k_block_bw<NB, Ty, false, false><<<grid, block, 0, st>>>(a, hpw, n_hg);
     return hipGetLastError();
 }
 

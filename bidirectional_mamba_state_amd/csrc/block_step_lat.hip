@@ -61,10 +61,14 @@ __device__ __forceinline__ bf16x8 rows_frag(const __bf16 *blk, int kk, int q, in
 enum { TAB_CF, TAB_CR, TAB_LGF, TAB_LGR, TAB_COLF, TAB_COLR, TAB_EF, NTAB };
 
 // WPG wavefronts per workgroup (2 or 4), each owning one 16-column block of the outputs;
-// OPS: the cached state comes in operand form (k_state_ops) instead of as float32
-template <typename Ty, int WPG, bool OPS>
+// FORM: the cached state as float32 (0), in operand form (1, k_state_ops) or as its bf16 hi
+// part only (2, the bf16 cached state: half the bytes, one product instead of two);
+// DCH: skip weights per head and channel ([H][P]) instead of per head
+enum { FORM_F32 = 0, FORM_OPS = 1, FORM_BF16 = 2 };
+template <typename Ty, int WPG, int FORM, bool DCH>
 __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
 {
+    constexpr bool OPS = FORM != FORM_F32;
     constexpr int NB = 2, TP = 32;  // one 32-token pair: two 16-token row blocks
     constexpr int CW = 16 * WPG;    // the workgroup's columns
     constexpr int NPH = kP / CW;    // column parts of a head
@@ -113,7 +117,9 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
     const auto rDf = buffer_range(static_cast<const __bf16 *>(a.fwd.dt) + tok0 * H + h, dt_bytes);
     const auto rDr = buffer_range(static_cast<const __bf16 *>(a.rev.dt) + tok0 * H + h, dt_bytes);
     const int64_t bh = static_cast<int64_t>(b) * H + h;
-    const auto rH = OPS ? buffer_range(static_cast<const __bf16 *>(a.h_ops) + bh * (2 * kN * kP), 2 * kN * kP * 2)
+    constexpr int OPS_PARTS = FORM == FORM_BF16 ? 1 : 2;  // bf16 halves per state element
+    const auto rH = OPS ? buffer_range(static_cast<const __bf16 *>(a.h_ops) + bh * (OPS_PARTS * kN * kP),
+                                       OPS_PARTS * kN * kP * 2)
                         : buffer_range(a.h_prefix + bh * (kN * kP), kN * kP * 4);
 
     // ---- the workgroup's inputs, each byte copied once, in whole lines, straight into
@@ -123,7 +129,7 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
     // decay tables for the workgroup meanwhile (with two wavefronts, it copies x); every
     // wavefront then copies its eighth (WPG = 2) or quarter (4) of the state.
     constexpr int TW = WPG - 1;  // the wavefront that builds the tables
-    constexpr int NSTATE = 8;    // state copies per wavefront, its last loads
+    constexpr int NSTATE = FORM == FORM_BF16 ? 4 : 8;  // state copies per wavefront, its last loads
     auto row0_of = [&](int i) {  // first row of row block i
         return i < 2 ? tb * 16 : (i - 2 <= tb ? i - 2 : i - 3) * 16;
     };
@@ -178,9 +184,18 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
     // wavefront's prologue: as scalar loads, the wait that the first copies need for the
     // kernel arguments would also wait for them
     float Ah = 0.f, Dh = 0.f, Ar = 0.f, Dr = 0.f;
+    f32x4 Dc = {0.f, 0.f, 0.f, 0.f}, Drc = {0.f, 0.f, 0.f, 0.f};  // DCH: this lane's four columns
     auto load_params = [&](bool decays) {
-        Dh = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_range(a.D, H * 4), h * 4, 0, 0));
-        Dr = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_range(a.D_rev, a.D_rev ? H * 4 : 0), h * 4, 0, 0));
+        if constexpr (DCH) {
+            const int pc = 16 * pblk + 4 * q;
+            Dc = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(buffer_range(a.D, H * kP * 4),
+                                                                                 (h * kP + pc) * 4, 0, 0));
+            Drc = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                buffer_range(a.D_rev, a.D_rev ? H * kP * 4 : 0), (h * kP + pc) * 4, 0, 0));
+        } else {
+            Dh = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_range(a.D, H * 4), h * 4, 0, 0));
+            Dr = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_range(a.D_rev, a.D_rev ? H * 4 : 0), h * 4, 0, 0));
+        }
         if (decays) {
             Ah = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_range(a.A, H * 4), h * 4, 0, 0));
             Ar = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_range(a.A_rev, H * 4), h * 4, 0, 0));
@@ -339,9 +354,11 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const bf16x8 hi = *reinterpret_cast<const bf16x8 *>(&hops[((4 * kk + q) * CW + 16 * w + r16) * 8]);
-            const bf16x8 lo = *reinterpret_cast<const bf16x8 *>(&hops[((16 + 4 * kk + q) * CW + 16 * w + r16) * 8]);
             acc = mfma(hi, cfw[kk], acc);
-            acc_lo = mfma(lo, cfw[kk], acc_lo);
+            if constexpr (FORM == FORM_OPS) {
+                const bf16x8 lo = *reinterpret_cast<const bf16x8 *>(&hops[((16 + 4 * kk + q) * CW + 16 * w + r16) * 8]);
+                acc_lo = mfma(lo, cfw[kk], acc_lo);
+            }
         }
     } else {
     // 32 columns: row n = 32kk + 8q + e sits at LDS row 32kk + 8q + (e ^ (q / 2)), and local
@@ -384,13 +401,13 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
         const bf16x4 xf = x4(0);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            o[j] = fmaf(Dh, bf2f(xf[j]), acc[j]);
+            o[j] = fmaf(DCH ? Dc[j] : Dh, bf2f(xf[j]), acc[j]);
     }
     if (a.D_rev) {
         const bf16x4 xr = x4(1);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            o[j] = fmaf(Dr, bf2f(xr[j]), o[j]);
+            o[j] = fmaf(DCH ? Drc[j] : Dr, bf2f(xr[j]), o[j]);
     }
     const auto rY = buffer_range(static_cast<Ty *>(a.y) + x0, (static_cast<int64_t>(T - 1) * rowX + kP) * sizeof(Ty));
     const int off = (t * rowX + p0) * static_cast<int>(sizeof(Ty));
@@ -417,10 +434,30 @@ hipError_t launch_ty(const BlockArgs &a, int wpg, hipStream_t st)
         wpg = pairs * 4 <= device_cus() ? 2 : 4;
     const dim3 g2(static_cast<unsigned>(a.s.H * 4), static_cast<unsigned>(a.s.b));
     const dim3 g4(static_cast<unsigned>(a.s.H * 2), static_cast<unsigned>(a.s.b));
+    const int form = !a.h_ops ? FORM_F32 : a.ops_hi_only ? FORM_BF16 : FORM_OPS;
+    auto go = [&](auto W, auto F, auto C) {
+        constexpr int wpg_ = decltype(W)::value;
+        k_block_lat<Ty, wpg_, decltype(F)::value, decltype(C)::value>
+            <<<wpg_ == 2 ? g2 : g4, dim3(64 * wpg_), 0, st>>>(a);
+    };
+    auto by_form = [&](auto W, auto C) {
+        if (form == FORM_F32)
+            go(W, std::integral_constant<int, FORM_F32>{}, C);
+        else if (form == FORM_OPS)
+            go(W, std::integral_constant<int, FORM_OPS>{}, C);
+        else
+            go(W, std::integral_constant<int, FORM_BF16>{}, C);
+    };
+    auto by_dch = [&](auto W) {
+        if (a.d_per_channel)
+            by_form(W, std::true_type{});
+        else
+            by_form(W, std::false_type{});
+    };
     if (wpg == 2)
-        a.h_ops ? k_block_lat<Ty, 2, true><<<g2, dim3(128), 0, st>>>(a) : k_block_lat<Ty, 2, false><<<g2, dim3(128), 0, st>>>(a);
+        by_dch(std::integral_constant<int, 2>{});
     else
-        a.h_ops ? k_block_lat<Ty, 4, true><<<g4, dim3(256), 0, st>>>(a) : k_block_lat<Ty, 4, false><<<g4, dim3(256), 0, st>>>(a);
+        by_dch(std::integral_constant<int, 4>{});
     return hipGetLastError();
 }
 

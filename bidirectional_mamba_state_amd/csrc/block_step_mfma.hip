@@ -95,7 +95,8 @@ struct Stage {
 // per-head decay tables (log2 units), one set per LDS buffer
 enum { TAB_CF, TAB_CR, TAB_LGF, TAB_LGR, TAB_COLF, TAB_COLR, TAB_EF, NTAB };
 
-template <int NB, int PS, typename Ty>
+// DCH: skip weights per head and channel ([H][P], read where the outputs are formed)
+template <int NB, int PS, typename Ty, bool DCH>
 __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockArgs a, int hpw, int n_hg)
 {
     using Gm = Geo<NB, PS>;
@@ -429,10 +430,23 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
         for (int pb = 0; pb < PBW; ++pb) {
             const int pcb = (pgrp * PBW + pb) * 16 + 4 * q;
             float o[4];
+            float d4[4] = {Dh, Dh, Dh, Dh}, r4[4] = {Dr, Dr, Dr, Dr};
+            if constexpr (DCH) {
+                const float4 dv = *reinterpret_cast<const float4 *>(a.D + h * kP + pbase + pcb);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    d4[j] = (&dv.x)[j];
+                if (with_dr) {
+                    const float4 rv = *reinterpret_cast<const float4 *>(a.D_rev + h * kP + pbase + pcb);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        r4[j] = (&rv.x)[j];
+                }
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                float v = fmaf(Dh, bf2f(xtf[(pcb + j) * XS + t]), acc[pb][j]);
-                o[j] = with_dr ? fmaf(Dr, bf2f(xtr[(pcb + j) * XS + t]), v) : v;
+                float v = fmaf(d4[j], bf2f(xtf[(pcb + j) * XS + t]), acc[pb][j]);
+                o[j] = with_dr ? fmaf(r4[j], bf2f(xtr[(pcb + j) * XS + t]), v) : v;
             }
             if (t < T)
                 store4(yh + t * rowX + pb * 16 + 4 * q, o);
@@ -452,7 +466,10 @@ hipError_t launch_nb(const BlockArgs &a, int hpw, hipStream_t st)
 {
     const int n_hg = a.s.H / hpw;
     const int nwg = a.s.b * n_hg * PS;
-    k_block_mfma<NB, PS, Ty><<<dim3(nwg), dim3(Geo<NB, PS>::THREADS), 0, st>>>(a, hpw, n_hg);
+    if (a.d_per_channel)
+        k_block_mfma<NB, PS, Ty, true><<<dim3(nwg), dim3(Geo<NB, PS>::THREADS), 0, st>>>(a, hpw, n_hg);
+    else
+        k_block_mfma<NB, PS, Ty, false><<<dim3(nwg), dim3(Geo<NB, PS>::THREADS), 0, st>>>(a, hpw, n_hg);
     return hipGetLastError();
 }
 

@@ -54,7 +54,10 @@ struct BlockArgs {
     const float *A_rev;  // decay of the reverse scan (A when the directions share it)
     const float *D_rev;  // skip term of the reverse input, or NULL for none
     const void *h_ops;   // the cached state in operand form (launch_state_ops), read instead
-                         // of h_prefix when not NULL (small-batch kernel only)
+                         // of h_prefix when not NULL
+    int ops_hi_only = 0;    // h_ops holds only the hi parts: the bf16 cached state
+                            // [b][H][N/8][P][8] (launch_state_bf16)
+    int d_per_channel = 0;  // D and D_rev are [H][P] skip weights instead of [H]
 };
 
 // Depthwise convolution of one token segment's x, B, C channels (see conv.hip)
@@ -107,6 +110,9 @@ hipError_t launch_block_step_bw(const BlockArgs &a, int hpw, hipStream_t st);
 // Operand form of nbh cached states [nbh][N][P] float32 (N = 128, P = 64): the bf16 pair
 // hi = bf16(S), lo = bf16(S - hi) as [nbh][2][N/8][P][8]
 hipError_t launch_state_ops(const float *h, void *ops, int64_t nbh, hipStream_t st);
+// bf16 copy of nbh cached states [nbh][N][P] float32 (N % 8 == 0): bf16(S) rounded to nearest
+// even, as [nbh][N/8][P][8] (the hi part of the operand form)
+hipError_t launch_state_bf16(const float *h, void *out, int64_t nbh, int N, int P, hipStream_t st);
 hipError_t launch_forward_valu(const ForwardArgs &a, hipStream_t st);
 hipError_t launch_block_step_valu(const BlockArgs &a, hipStream_t st);
 hipError_t launch_state_pass(const PassArgs &a, hipStream_t st);

@@ -147,10 +147,19 @@ __global__ __launch_bounds__(kThreads) void k_block_step(BlockArgs a)
     const float Ah = a.A[h], Ahr = a.A_rev[h];
 
     float S[L::NPT];
-    const float *hp = a.h_prefix + (static_cast<int64_t>(b) * H + h) * NP;
+    if (a.h_prefix) {
+        const float *hp = a.h_prefix + (static_cast<int64_t>(b) * H + h) * NP;
 #pragma unroll
-    for (int k = 0; k < L::NPT; ++k)
-        S[k] = hp[static_cast<int64_t>(r + k * L::R) * P + p];
+        for (int k = 0; k < L::NPT; ++k)
+            S[k] = hp[static_cast<int64_t>(r + k * L::R) * P + p];
+    } else {  // the bf16 cached state, [N/8][P][8]: element (n, p) at (n/8 P + p) 8 + n % 8
+        const uint16_t *hb = static_cast<const uint16_t *>(a.h_ops) + (static_cast<int64_t>(b) * H + h) * NP;
+#pragma unroll
+        for (int k = 0; k < L::NPT; ++k) {
+            const int n = r + k * L::R;
+            S[k] = load_in(hb, ((n >> 3) * P + p) * 8 + (n & 7));
+        }
+    }
 
     {   // eq. (11): forward continuation of the cached state
         const Tin *x = static_cast<const Tin *>(a.fwd.x);
@@ -194,16 +203,34 @@ __global__ __launch_bounds__(kThreads) void k_block_step(BlockArgs a)
     const Tin *xf = static_cast<const Tin *>(a.fwd.x);
     const Tin *xr = static_cast<const Tin *>(a.rev.x);
     Ty *y = static_cast<Ty *>(a.y);
-    const float Dh = a.D[h];
-    const float Dr = a.D_rev ? a.D_rev[h] : 0.f;
     for (int i = tid; i < T * P; i += kThreads) {
         const int t = i / P, pp = i % P;
         const int64_t o = ((static_cast<int64_t>(b) * T + t) * H + h) * P + pp;
-        float v = fmaf(Dh, load_in(xf, o), ybuf[i]);
+        const int wi = a.d_per_channel ? h * P + pp : h;  // skip weight per head or per channel
+        float v = fmaf(a.D[wi], load_in(xf, o), ybuf[i]);
         if (a.D_rev)
-            v = fmaf(Dr, load_in(xr, o), v);
+            v = fmaf(a.D_rev[wi], load_in(xr, o), v);
         store_y(y, o, v);
     }
+}
+
+// bf16 copy of cached states: thread (state, n/8, p) reads h[8 (n/8) + e][p], e = 0..7, and
+// writes bf16(h) (round to nearest even) as one 16-byte piece of [N/8][P][8]
+__global__ __launch_bounds__(kThreads) void k_state_bf16(const float *__restrict__ h, uint16_t *__restrict__ out,
+                                                         int64_t nbh, int N, int P)
+{
+    const int64_t per = static_cast<int64_t>(N / 8) * P;
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (i >= nbh * per)
+        return;
+    const int64_t st = i / per;
+    const int n8 = static_cast<int>((i % per) / P), p = static_cast<int>(i % P);
+    const float *src = h + st * N * P + static_cast<int64_t>(8 * n8) * P + p;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2)
+        w[e / 2] = static_cast<uint32_t>(to_bf16(src[e * P])) | (static_cast<uint32_t>(to_bf16(src[(e + 1) * P])) << 16);
+    *reinterpret_cast<uint4 *>(out + st * N * P + (static_cast<int64_t>(n8) * P + p) * 8) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 // Inter-chunk state passing, one thread per state element. grid = (ceil(NP/256), H, b).
@@ -296,6 +323,14 @@ hipError_t launch_state_pass(const PassArgs &a, hipStream_t st)
     const int64_t NP = static_cast<int64_t>(a.s.N) * a.s.P;
     dim3 grid(static_cast<unsigned>((NP + kThreads - 1) / kThreads), a.s.H, a.s.b);
     k_state_pass<<<grid, kThreads, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_state_bf16(const float *h, void *out, int64_t nbh, int N, int P, hipStream_t st)
+{
+    const int64_t n = nbh * (N / 8) * P;
+    k_state_bf16<<<static_cast<unsigned>((n + kThreads - 1) / kThreads), kThreads, 0, st>>>(
+        h, static_cast<uint16_t *>(out), nbh, N, P);
     return hipGetLastError();
 }
 

@@ -255,6 +255,50 @@ bdssm_status bdssm_block_step_ops(const bdssm_dims *dims, int32_t block_len, con
                                   void *stream);
 
 /*
+ * bf16 cached state. The block step reads the whole cached state on every denoising step,
+ * so its bytes bound the step at large batch; a bf16 copy halves them at the cost of
+ * rounding the state once (relative error 2^-9 per element). The bf16 state of a float32
+ * state S is bf16(S), rounded to nearest even -- the operand form's hi part -- laid out as
+ *     [b][H][N/8][P][8] bf16,  element (n, p) of a head at index (n/8 * P + p) * 8 + n % 8,
+ * made once per cached state (after the prefix scan or a commit, which keep the float32
+ * state as the master copy). Supported for d_state a multiple of 8.
+ * bdssm_state_bf16_bytes: bytes of the bf16 state; SIZE_MAX for invalid or unsupported dims.
+ * bdssm_state_bf16: writes it from h [b][H][N][P] float32 (read only); out must not overlap
+ * h. Errors: BDSSM_ERR_NULL, BDSSM_ERR_UNSUPPORTED, BDSSM_ERR_ALIGN, BDSSM_ERR_ALIAS.
+ */
+size_t bdssm_state_bf16_bytes(const bdssm_dims *dims);
+bdssm_status bdssm_state_bf16(const bdssm_dims *dims, const float *h, void *out, void *stream);
+
+/*
+ * Block step with every variant of the layer's parameters and of the cached state's form.
+ * The reverse scan of eq. (12) has its own parameters (theta_rev): its decay A_rev and its
+ * own skip weight D_rev; the skip weights may also be one per channel of x ([H][P], the
+ * Mamba-2 layer's per-channel option) instead of one per head:
+ *   y_t = C_t . S_t + C'_t . R_t + D (.) x_fwd[t] (+ D_rev (.) x_rev[t])
+ * with (.) the per-head scalar or the per-channel product.
+ *   state       the cached state in the form state_form:
+ *                 BDSSM_STATE_F32   float32 [b][H][N][P] (as bdssm_block_step)
+ *                 BDSSM_STATE_OPS   operand form (bdssm_state_ops; bf16 inputs, (d_state,
+ *                                   headdim) = (128, 64), block_len <= 128 only)
+ *                 BDSSM_STATE_BF16  bf16 state (bdssm_state_bf16)
+ *               read only, never written
+ *   params      A [H] required; D [H] (or [H][P]) required; A_rev [H] or NULL (= A);
+ *               D_rev [H] (or [H][P]) or NULL (none); skip_per_channel 0 or 1
+ * With the float32 state and per-head weights this is bdssm_block_step_ex, bitwise; with
+ * the operand form, bdssm_block_step_ops. Errors as bdssm_block_step_ex, plus
+ * BDSSM_ERR_UNSUPPORTED for an unknown state form or skip layout, or the operand form outside
+ * its shapes. y must not overlap the state or any parameter.
+ */
+enum { BDSSM_STATE_F32 = 0, BDSSM_STATE_OPS = 1, BDSSM_STATE_BF16 = 2 };
+typedef struct {
+    const float *A, *D, *A_rev, *D_rev;
+    int32_t skip_per_channel;
+} bdssm_step_params;
+bdssm_status bdssm_block_step_variant(const bdssm_dims *dims, int32_t block_len, const void *state,
+                                      int32_t state_form, const bdssm_seq *fwd, const bdssm_seq *rev,
+                                      const bdssm_step_params *params, void *y, void *stream);
+
+/*
  * Convolution state. A Mamba layer's cache holds convolution state as well as the SSM
  * state (the cache discussion of "Training Hybrid Block Diffusion Language Models with
  * Partial Bidirectionality"); the pages leave the convolution itself open, and these calls

@@ -58,6 +58,9 @@ def _load():
         lib.oracle_block_step_ex.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int64, P,
                                              ctypes.POINTER(_Seq), ctypes.POINTER(_Seq),
                                              P, P, P, P, P, P, P, P, ctypes.c_int]
+        lib.oracle_block_step_dch.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int64, P,
+                                              ctypes.POINTER(_Seq), ctypes.POINTER(_Seq),
+                                              P, P, P, P, P, P, ctypes.c_int]
         lib.oracle_full_window.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int64, ctypes.POINTER(_Seq),
                                            ctypes.POINTER(_Seq), P, P, P, P, P, P, ctypes.c_int]
         lib.oracle_commit.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int64,
@@ -66,7 +69,7 @@ def _load():
                                     ctypes.c_int32, ctypes.c_int32, P, P, P,
                                     ctypes.POINTER(_Seq), ctypes.POINTER(_Seq), P, ctypes.c_int]
         for f in (lib.oracle_scan, lib.oracle_block_step, lib.oracle_block_step_ex, lib.oracle_commit,
-                  lib.oracle_conv, lib.oracle_full_window):
+                  lib.oracle_conv, lib.oracle_full_window, lib.oracle_block_step_dch):
             f.restype = ctypes.c_int
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -166,6 +169,29 @@ def block_step(h_prefix, fwd, rev, A, D, heads=None, nthreads=0, A_rev=None, D_r
     if rc:
         raise ValueError("oracle_block_step rejected its arguments")
     return y, yf, yr
+
+
+def block_step_per_channel(h_prefix, fwd, rev, A, D, A_rev=None, D_rev=None, heads=None, nthreads=0):
+    """Block step with skip weights per head and channel (oracle_block_step_dch): D and D_rev
+    (optional) are [H, P]. Returns y [b, T, H, P] float64."""
+    cf, cr = _Call(fwd), _Call(rev)
+    b, T, H, P = fwd.x.shape
+    G = fwd.B.shape[2]
+    y = np.zeros((b, T, H, P))
+    hp = _f64(h_prefix)
+    A = np.ascontiguousarray(A, np.float32)
+    D = np.ascontiguousarray(D, np.float32)
+    assert D.shape == (H, P)
+    Ar = None if A_rev is None else np.ascontiguousarray(A_rev, np.float32)
+    Dr = None if D_rev is None else np.ascontiguousarray(D_rev, np.float32)
+    assert Dr is None or Dr.shape == (H, P)
+    m = _mask(heads, H)
+    rc = _load().oracle_block_step_dch(ctypes.byref(_dims(fwd, G)), T, _ptr(hp), ctypes.byref(cf.s),
+                                       ctypes.byref(cr.s), _ptr(A), _ptr(D), _ptr(Ar), _ptr(Dr), _ptr(y),
+                                       _ptr(m), nthreads)
+    if rc:
+        raise ValueError("oracle_block_step_dch rejected its arguments")
+    return y
 
 
 def full_window(fwd, rev, A, D, A_rev=None, D_rev=None, heads=None, nthreads=0):

@@ -172,11 +172,14 @@ int oracle_scan(const oracle_dims *d, int64_t len, int64_t chunk, const oracle_s
 }
 
 /* Block step (eqs. 11-13). h_prefix is read only. y = y_fwd + y_rev + D x_fwd.
- * y_fwd and y_rev (without D) are optional extra outputs. */
-int oracle_block_step_ex(const oracle_dims *d, int64_t T, const double *h_prefix,
-                         const oracle_seq *fwd, const oracle_seq *rev, const float *A,
-                         const float *D, const float *A_rev, const float *D_rev, double *y,
-                         double *y_fwd, double *y_rev, const int8_t *head_mask, int nthreads)
+ * y_fwd and y_rev (without D) are optional extra outputs. The skip weights D (and D_rev) are
+ * one per head, [H], or with skip_per_channel one per head and channel, [H][P] (the Mamba-2
+ * layer's option of a skip weight per channel of x). */
+static int block_step_impl(const oracle_dims *d, int64_t T, const double *h_prefix,
+                           const oracle_seq *fwd, const oracle_seq *rev, const float *A,
+                           const float *D, const float *A_rev, const float *D_rev,
+                           int skip_per_channel, double *y, double *y_fwd, double *y_rev,
+                           const int8_t *head_mask, int nthreads)
 {
     if (check(d) || T < 1 || !h_prefix || !fwd || !rev || !A || !D || !y)
         return 1;
@@ -241,9 +244,10 @@ int oracle_block_step_ex(const oracle_dims *d, int64_t T, const double *h_prefix
             const int64_t tok = (int64_t)b * T + t;
             for (int p = 0; p < P; ++p) {
                 const int64_t o = (tok * H + h) * P + p;
-                y[o] = yf[t * P + p] + yr[t * P + p] + (double)D[h] * val(fwd->x, dty, o);
+                const int64_t w = skip_per_channel ? (int64_t)h * P + p : h;
+                y[o] = yf[t * P + p] + yr[t * P + p] + (double)D[w] * val(fwd->x, dty, o);
                 if (D_rev)
-                    y[o] += (double)D_rev[h] * val(rev->x, dty, o);
+                    y[o] += (double)D_rev[w] * val(rev->x, dty, o);
                 if (y_fwd)
                     y_fwd[o] = yf[t * P + p];
                 if (y_rev)
@@ -256,6 +260,26 @@ int oracle_block_step_ex(const oracle_dims *d, int64_t T, const double *h_prefix
         free(xv);
     }
     return 0;
+}
+
+int oracle_block_step_ex(const oracle_dims *d, int64_t T, const double *h_prefix,
+                         const oracle_seq *fwd, const oracle_seq *rev, const float *A,
+                         const float *D, const float *A_rev, const float *D_rev, double *y,
+                         double *y_fwd, double *y_rev, const int8_t *head_mask, int nthreads)
+{
+    return block_step_impl(d, T, h_prefix, fwd, rev, A, D, A_rev, D_rev, 0, y, y_fwd, y_rev, head_mask,
+                           nthreads);
+}
+
+/* The block step with skip weights per head and channel: D and D_rev (when given) are
+ * [H][P]. */
+int oracle_block_step_dch(const oracle_dims *d, int64_t T, const double *h_prefix,
+                          const oracle_seq *fwd, const oracle_seq *rev, const float *A,
+                          const float *D, const float *A_rev, const float *D_rev, double *y,
+                          const int8_t *head_mask, int nthreads)
+{
+    return block_step_impl(d, T, h_prefix, fwd, rev, A, D, A_rev, D_rev, 1, y, NULL, NULL, head_mask,
+                           nthreads);
 }
 
 int oracle_block_step(const oracle_dims *d, int64_t T, const double *h_prefix,

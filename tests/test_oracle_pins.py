@@ -193,6 +193,29 @@ def test_block_step_separate_reverse_params():
     assert np.array_equal(y0, y1)
 
 
+def test_block_step_per_channel_skip():
+    """Skip weights per head and channel: the dual form with D[h][p] x[t][p] (and
+    D_rev[h][p] x_rev[t][p]); with every channel of a head equal to D[h] it is the
+    per-head step exactly."""
+    rng = np.random.default_rng(14)
+    b, T, H, P, N, G = 2, 24, 4, 3, 5, 2
+    fwd = rand_seq(rng, b, T, H, P, N, G)
+    rev = rand_seq(rng, b, T, H, P, N, G)
+    A, D = rand_params(rng, H)
+    Ar, Dr = rand_params(rng, H)
+    Dc = rng.standard_normal((H, P)).astype(np.float32)
+    Drc = rng.standard_normal((H, P)).astype(np.float32)
+    h0 = 0.3 * rng.standard_normal((b, H, N, P))
+    y = oracle.block_step_per_channel(h0, fwd, rev, A, Dc, A_rev=Ar, D_rev=Drc)
+    qf, _ = quad_forward(fwd, A, D, h0, with_D=False)
+    qr = quad_reverse(rev, Ar)
+    xf, xr = dec(fwd)[0], dec(rev)[0]
+    assert rel(y, qf + qr + Dc[None, None] * xf + Drc[None, None] * xr) < 1e-12
+    y1 = oracle.block_step_per_channel(h0, fwd, rev, A, np.repeat(D[:, None], P, 1))
+    y0, _, _ = oracle.block_step(h0, fwd, rev, A, D)
+    assert np.array_equal(y0, y1)
+
+
 def test_reverse_is_flipped_forward():
     rng = np.random.default_rng(3)
     b, T, H, P, N, G = 1, 20, 2, 4, 3, 1
@@ -543,11 +566,11 @@ PLANTS = {
     "reverse uses the forward dt": ("const double dt = val(rev->dt", "const double dt = val(fwd->dt"),
     "wrong group index": ("const int g = h / (H / G);\n    const int dty",
                           "const int g = h % G;\n    const int dty"),
-    "D applied twice in the block step": ("(double)D[h] * val(fwd->x, dty, o);",
-                                          "2.0 * (double)D[h] * val(fwd->x, dty, o);"),
+    "D applied twice in the block step": ("(double)D[w] * val(fwd->x, dty, o);",
+                                          "2.0 * (double)D[w] * val(fwd->x, dty, o);"),
     "reverse scan decays with the forward A": ("exp(dt * Ar[h])", "exp(dt * A[h])"),
-    "reverse skip term on the forward input": ("(double)D_rev[h] * val(rev->x, dty, o)",
-                                               "(double)D_rev[h] * val(fwd->x, dty, o)"),
+    "reverse skip term on the forward input": ("(double)D_rev[w] * val(rev->x, dty, o)",
+                                               "(double)D_rev[w] * val(fwd->x, dty, o)"),
     "C and B swapped in the forward output": (
         "acc += val(in->C, dty, (tok * G + g) * N + n) * S",
         "acc += val(in->B, dty, (tok * G + g) * N + n) * S"),
@@ -558,6 +581,8 @@ PLANTS = {
     "conv state ignored": ("(!reverse && state_in) ?", "(0 && state_in) ?"),
     "conv state not advanced": ("u[len + k]);", "u[k]);"),
     "activation dropped": ("v = v / (1.0 + exp(-v));", "v = v * 1.0;"),
+    "per-channel skip weight read per head": ("const int64_t w = skip_per_channel ? (int64_t)h * P + p : h;",
+                                              "const int64_t w = skip_per_channel ? (int64_t)h * P : h;"),
     "full window drops the reverse parameters": ("zero, fwd, rev, A, D, A_rev, D_rev, y,",
                                                  "zero, fwd, rev, A, D, NULL, NULL, y,"),
 }
@@ -587,7 +612,8 @@ def test_planted_mistake_is_caught(tmp_path, monkeypatch, name):
                  lambda: test_conv_matches_shifted_slices(BF16, False),
                  lambda: test_conv_matches_shifted_slices(F32, True),
                  test_conv_identity_shift_and_flip, test_conv_state_chains_and_silu_values,
-                 test_block_step_and_commit_with_conv, lambda: test_full_window_matches_quadratic_form(2)):
+                 test_block_step_and_commit_with_conv, lambda: test_full_window_matches_quadratic_form(2),
+                 test_block_step_per_channel_skip):
         try:
             test()
         except AssertionError:
