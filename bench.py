@@ -4,14 +4,15 @@ Headline workload: the 64-stream running set of the 700M-shape layer (48 heads x
 d_state 128, ngroups 1, bf16 inputs, fp32 state). Each stream has its own cached state,
 built by a state-only prefix scan over its own 32,768 tokens. One step is one block cycle
 of the running set:
-  1. bdssm_state_ops: the cached states in the block step's operand form (after the last
-     commit),
-  2. 16 denoising steps of bdssm_block_step_ops over the running set of four 32-token blocks
-     (T = 128, distinct fwd/rev inputs per step),
-  3. bdssm_commit of the oldest 32-token block of every stream (its clean inputs).
+  1. 16 denoising steps of bdssm_block_step_ops over the running set of four 32-token blocks
+     (T = 128, distinct fwd/rev inputs per step), from the cached states in operand form,
+  2. bdssm_commit_refresh of the oldest 32-token block of every stream (its clean inputs):
+     the states advance and their operand form for the next cycle's steps is written in the
+     same pass.
 The step is captured as one HIP graph and replayed; value = active (denoised) tokens per
-second = 16 * 64 * 128 per step / wall time. The 64 x 32,768-token prefix build is timed as
-its own part (once per context, not per block).
+second = 16 * 64 * 128 per step / wall time. The 64 x 32,768-token prefix build (and the
+first operand form of its states) is timed as its own part: once per context, not per
+block.
 
 The parts are also timed on their own (each as its own graph, warmed before timing, median
 over replays), and the dominant kernel's launches one by one with HIP events on the launch
@@ -258,6 +259,7 @@ def headline(args, torch, np, bdssm, configs, inputs):
     def run_ops():
         bdssm.state_ops(d, h, ops)
 
+    run_ops()  # the first cycle's operand form (with the prefix build, once per context)
     step_fns = [(lambda f=f, r=r, y=y: bdssm.block_step_ops(d, T, ops, f, r, Ad, Dd, y))
                 for (f, r), y in zip(steps, ys)]
 
@@ -266,9 +268,9 @@ def headline(args, torch, np, bdssm, configs, inputs):
             fn()
 
     def run_commit():
-        bdssm.commit(d, TC, clean, Ad, Dd, h)
+        bdssm.commit_refresh(d, TC, clean, Ad, Dd, h, ops, bdssm.STATE_OPS)
 
-    parts = (("state_ops", run_ops, 1), ("block_step", run_steps, S), ("commit", run_commit, 1))
+    parts = (("block_step", run_steps, S), ("commit_refresh", run_commit, 1))
 
     def run_all():
         for _, fn, _ in parts:
@@ -313,46 +315,47 @@ def headline(args, torch, np, bdssm, configs, inputs):
     h.copy_(h0)
     commit_us = median(launch_times_us(torch, [run_commit], reps=9)[0])
     h.copy_(h0)
+    plain_commit_us = median(launch_times_us(torch, [lambda: bdssm.commit(d, TC, clean, Ad, Dd, h)], reps=9)[0])
+    h.copy_(h0)
 
     nb_step = block_step_bytes(b, H, P, N, G, T, 2, 2)
     nb_ops = state_ops_bytes(b, H, P, N)
-    nb_commit = commit_bytes(b, H, P, N, G, TC, 2)
-    nb_all = S * nb_step + nb_ops + nb_commit
+    nb_commit = commit_bytes(b, H, P, N, G, TC, 2) + nb_ops // 2   # + the operand form written
+    nb_all = S * nb_step + nb_commit
     ms_per_step = 1e3 * wall / args.steps
     active = S * b * T
     breakdown = {
-        "state_ops": {"launches_per_step": 1, "graph_us": round(part_us["state_ops"], 3),
-                      "launch_us": round(ops_us, 3), "alg_bytes": nb_ops,
-                      "hbm_frac": round(nb_ops / (ops_us * 1e-6) / HBM_PEAK, 4)},
         "block_step": {"launches_per_step": S, "graph_us": round(part_us["block_step"], 3),
                        "launch_us": round(blk_us, 3), "alg_bytes": nb_step,
                        "hbm_frac": round(nb_step / (blk_us * 1e-6) / HBM_PEAK, 4),
                        "active_tokens_per_s": round(b * T / (blk_us * 1e-6), 1)},
-        "commit": {"launches_per_step": 1, "graph_us": round(part_us["commit"], 3),
-                   "launch_us": round(commit_us, 3), "alg_bytes": nb_commit,
-                   "hbm_frac": round(nb_commit / (commit_us * 1e-6) / HBM_PEAK, 4)},
+        "commit_refresh": {"launches_per_step": 1, "graph_us": round(part_us["commit_refresh"], 3),
+                           "launch_us": round(commit_us, 3), "alg_bytes": nb_commit,
+                           "hbm_frac": round(nb_commit / (commit_us * 1e-6) / HBM_PEAK, 4),
+                           "commit_alone_us": round(plain_commit_us, 3),
+                           "operand_form_alone_us": round(ops_us, 3)},
         "parts_sum_us": round(parts_sum, 3), "step_median_us": round(step_med_us, 3),
     }
-    shares = {"state_ops": ops_us, "block_step": S * blk_us, "commit": commit_us}
+    shares = {"block_step": S * blk_us, "commit_refresh": commit_us}
     dom = max(shares, key=shares.get)
-    work = {"state_ops": nb_ops, "block_step": nb_step, "commit": nb_commit}[dom]
-    avg = {"state_ops": ops_us, "block_step": blk_us, "commit": commit_us}[dom]
-    kname = {"state_ops": "k_state_ops", "block_step": "k_block_bw", "commit": "k_state"}[dom]
+    work = {"block_step": nb_step, "commit_refresh": nb_commit}[dom]
+    avg = {"block_step": blk_us, "commit_refresh": commit_us}[dom]
+    kname = {"block_step": "k_block_bw", "commit_refresh": "k_scan (state pass, two heads per workgroup)"}[dom]
     roof = make_roofline("hbm", work, avg, traffic_for({"block_step": "block_step_c4"}.get(dom, dom)))
     roof.update({"kernel": kname, "part": dom, "work_per_launch": work, "avg_launch_us": round(avg, 3),
                  "launches_per_step": S if dom == "block_step" else 1})
     out = {"metric": METRIC, "value": round(active / (wall / args.steps), 1), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
            "gpu_ms_per_step": round(gpu_ms_per_step, 4),
-           "timing": "one HIP graph replay per step (operand form of the cached states, 16 block steps, commit "
-                     "of the oldest block); exactly `steps` replays on the clock; parts timed as their own warmed "
-                     "graphs and the kernels launch by launch with HIP events on the launch stream",
+           "timing": "one HIP graph replay per step (16 block steps, commit of the oldest block with the operand "
+                     "form refreshed in the same pass); exactly `steps` replays on the clock; parts timed as their "
+                     "own warmed graphs and the kernels launch by launch with HIP events on the launch stream",
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded device draws with the workload's distributions; random-init layer parameters)",
            "config": {"workload": "running set of 64 independent streams, 700M-shape Mamba-2 layer (48 heads x 64, "
                                   "d_state 128, ngroups 1), bf16 inputs, fp32 cached state per stream built from "
-                                  "32,768 prefix tokens; one step = operand form of the 64 cached states + 16 "
-                                  "block steps of the 4 x 32 = 128-token window + commit of the oldest 32 tokens",
+                                  "32,768 prefix tokens; one step = 16 block steps of the 4 x 32 = 128-token window "
+                                  "+ commit of the oldest 32 tokens (refreshing the states' operand form)",
                       "global_batch": b, "seq_len": L, "block_len": T, "steps_per_block": S, "commit_len": TC,
                       "parallelism": "none (1 GPU)"},
            "roofline": roof, "breakdown": breakdown,
@@ -368,8 +371,10 @@ def headline(args, torch, np, bdssm, configs, inputs):
 
 # ---------------------------------------------------------------- config 1: batch-1 block cycle
 def config1(args, torch, np, bdssm, configs, inputs):
-    """The 700M batch-1 block cycle as one graph: the 8192-token prefix scan (bf16 y), the
-    operand form, 64 block steps (T = 32), the commit; parts as warmed graphs."""
+    """The 700M batch-1 decode: a block cycle as one graph -- 64 block steps (T = 32) from the
+    cached state in operand form, then the commit that refreshes it -- with the parts as
+    warmed graphs; the 8192-token prefix scan (bf16 y) that builds the first cached state,
+    once per context, timed on its own."""
     cfg = configs.get(1)
     b, H, P, N, G, L, Q, T = (cfg.batch, cfg.nheads, cfg.headdim, cfg.d_state, cfg.ngroups,
                               cfg.prefix_len, cfg.chunk, cfg.block_len)
@@ -391,9 +396,6 @@ def config1(args, torch, np, bdssm, configs, inputs):
     def run_prefix():
         bdssm.prefix_scan(d, L, Q, pre, Ad, Dd, None, y_pre, None, h, ws, wsb)
 
-    def run_ops():
-        bdssm.state_ops(d, h, h_ops)
-
     def run_blocks():
         for s in range(S):
             f, r = steps[s]
@@ -405,10 +407,11 @@ def config1(args, torch, np, bdssm, configs, inputs):
             bdssm.block_step(d, T, h, f, r, Ad, Dd, y_blk[s])
 
     def run_commit():
-        bdssm.commit(d, T, clean, Ad, Dd, h)
+        bdssm.commit_refresh(d, T, clean, Ad, Dd, h, h_ops, bdssm.STATE_OPS)
 
-    parts = (("prefix_scan", run_prefix, 1), ("state_ops", run_ops, 1), ("block_step", run_blocks, S),
-             ("commit", run_commit, 1))
+    run_prefix()
+    bdssm.state_ops(d, h, h_ops)
+    parts = (("block_step", run_blocks, S), ("commit_refresh", run_commit, 1))
 
     def run_all():
         for _, fn, _ in parts:
@@ -419,16 +422,17 @@ def config1(args, torch, np, bdssm, configs, inputs):
     whole = warmed(torch, capture(torch, run_all))
     step_us = median(replay_times_us(torch, whole, 20))
     del whole
-    res = {"workload": "700M shape, batch 1: 8192-token prefix scan (bf16 y) + operand form + 64 block steps "
-                       "(T=32) + commit, one graph", "step_us": round(step_us, 2),
-           "active_tokens_per_s": round(S * b * T / (step_us * 1e-6), 1)}
+    res = {"workload": "700M shape, batch 1: block cycle of 64 block steps (T=32) + commit refreshing the operand "
+                       "form, one graph; the 8192-token prefix scan (bf16 y) timed on its own",
+           "cycle_us": round(step_us, 2), "active_tokens_per_s": round(S * b * T / (step_us * 1e-6), 1)}
     for name, fn, n in parts:
         us = graph_us(torch, fn, reps=20)
         if us > 1.02 * step_us:
-            print(f"[bench] inconsistent timing: config 1 {name} {us:.1f} us > step {step_us:.1f} us",
+            print(f"[bench] inconsistent timing: config 1 {name} {us:.1f} us > cycle {step_us:.1f} us",
                   file=sys.stderr, flush=True)
             sys.exit(3)
         res[name + "_us"] = round(us / n, 3)
+    res["prefix_scan_us"] = round(graph_us(torch, run_prefix, reps=20), 3)
     nb = block_step_bytes(b, H, P, N, G, T, 2, 2)
     res["block_step_hbm_frac"] = round(nb / (res["block_step_us"] * 1e-6) / HBM_PEAK, 4)
     res["block_step_from_fp32_state_us"] = round(graph_us(torch, run_blocks_fp32, reps=20) / S, 3)

@@ -26,7 +26,8 @@ EXPORTS = ("bdssm_abi_version", "bdssm_status_str", "bdssm_prefix_scan_workspace
            "bdssm_state_ops_bytes", "bdssm_state_ops", "bdssm_block_step_ops",
            "bdssm_set_launch_override", "bdssm_prefix_scan_static",
            "bdssm_full_window_workspace", "bdssm_full_window",
-           "bdssm_state_bf16_bytes", "bdssm_state_bf16", "bdssm_block_step_variant")
+           "bdssm_state_bf16_bytes", "bdssm_state_bf16", "bdssm_block_step_variant",
+           "bdssm_commit_refresh")
 STATE_F32, STATE_OPS, STATE_BF16 = 0, 1, 2
 
 
@@ -123,6 +124,8 @@ def load():
         lib.bdssm_state_bf16.argtypes = [P(Dims), V, V, V]
         lib.bdssm_block_step_variant.restype = ctypes.c_int
         lib.bdssm_block_step_variant.argtypes = [P(Dims), I32, V, I32, P(SeqPtrs), P(SeqPtrs), P(StepParams), V, V]
+        lib.bdssm_commit_refresh.restype = ctypes.c_int
+        lib.bdssm_commit_refresh.argtypes = [P(Dims), I32, P(SeqPtrs), V, V, V, V, I32, V, V]
         lib.bdssm_set_launch_override.restype = ctypes.c_int
         lib.bdssm_set_launch_override.argtypes = [P(LaunchOverride)]
         _lib = lib
@@ -281,6 +284,13 @@ def commit(d, block_len, clean, A, D, h, y=None, stream=None):
     """bdssm_commit. clean = (x, dt, B, C) tensors (C may be None when y is None)."""
     _check(load().bdssm_commit(ctypes.byref(d), block_len, _byref(_seq(clean)), _ptr(A), _ptr(D),
                                _ptr(h), _ptr(y), _stream(stream)))
+
+
+def commit_refresh(d, block_len, clean, A, D, h, state_copy, state_form=STATE_OPS, y=None, stream=None):
+    """bdssm_commit_refresh: the commit, with the block step's copy of the advanced state
+    (operand form or bf16) written in the same pass."""
+    _check(load().bdssm_commit_refresh(ctypes.byref(d), block_len, _byref(_seq(clean)), _ptr(A), _ptr(D), _ptr(h),
+                                       _ptr(state_copy), state_form, _ptr(y), _stream(stream)))
 
 
 def conv_params(weight, bias, activation, width=None):

@@ -780,6 +780,48 @@ bdssm_status bdssm_commit(const bdssm_dims *dims, int32_t block_len, const bdssm
                          static_cast<hipStream_t>(stream));
 }
 
+bdssm_status bdssm_commit_refresh(const bdssm_dims *dims, int32_t block_len, const bdssm_seq *clean,
+                                  const float *A, const float *D, float *h, void *state_copy,
+                                  int32_t state_form, void *y, void *stream)
+{
+    Shape s;
+    bdssm_status rc = prepare_commit(dims, block_len, clean, A, D, h, y, &s);
+    if (rc != BDSSM_OK)
+        return rc;
+    if (state_form != BDSSM_STATE_OPS && state_form != BDSSM_STATE_BF16)
+        return BDSSM_ERR_UNSUPPORTED;
+    if (state_form == BDSSM_STATE_OPS && (s.N != 128 || s.P != 64))
+        return BDSSM_ERR_UNSUPPORTED;
+    if (state_form == BDSSM_STATE_BF16 && s.N % 8 != 0)
+        return BDSSM_ERR_UNSUPPORTED;
+    if (!state_copy)
+        return BDSSM_ERR_NULL;
+    if (!aligned(state_copy))
+        return BDSSM_ERR_ALIGN;
+    const int64_t n = static_cast<int64_t>(s.b) * s.H * s.N * s.P;
+    const Range rc_copy = rng(state_copy, n * (state_form == BDSSM_STATE_OPS ? 4 : 2));
+    SeqRanges q{};
+    (void)check_seq(clean, s, block_len, y != nullptr, &q);
+    if (hits(rc_copy, q) || overlap(rc_copy, rng(h, n * 4)) || overlap(rc_copy, rng(A, s.H * 4)) ||
+        overlap(rc_copy, rng(D, s.H * 4)) ||
+        overlap(rc_copy, rng(y, static_cast<int64_t>(s.b) * block_len * s.H * s.P * elt(s.y_dt))))
+        return BDSSM_ERR_ALIAS;
+    if (s.b == 0)
+        return BDSSM_OK;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool hi_only = state_form == BDSSM_STATE_BF16;
+    if (block_len > 0 && !y && prefix_mfma_supported(s, 64)) {
+        // one pass: the commit's state walk writes the advanced state and its encoded copy
+        return launched(run_prefix_mfma(s, block_len, 64, Seq{clean->x, clean->dt, clean->B, clean->C}, A, D, h,
+                                        nullptr, nullptr, h, nullptr, st, true, false, state_copy, hi_only));
+    }
+    if (block_len > 0 && (rc = launch_commit(s, block_len, Seq{clean->x, clean->dt, clean->B, clean->C}, A, D, h,
+                                             y, st)) != BDSSM_OK)
+        return rc;
+    return launched(hi_only ? launch_state_bf16(h, state_copy, static_cast<int64_t>(s.b) * s.H, s.N, s.P, st)
+                            : launch_state_ops(h, state_copy, static_cast<int64_t>(s.b) * s.H, st));
+}
+
 size_t bdssm_conv_workspace(const bdssm_dims *dims, int64_t len)
 {
     Shape s;

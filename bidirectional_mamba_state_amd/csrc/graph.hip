@@ -38,9 +38,9 @@ extern "C" bdssm_status bdssm_decode_graph_create(const bdssm_dims *dims, int32_
         rc = h_ops ? bdssm_block_step_ops(dims, block_len, h_ops, &fwd[k], &rev[k], A, D, A, nullptr, y[k], stream)
                    : bdssm_block_step(dims, block_len, h, &fwd[k], &rev[k], A, D, y[k], stream);
     if (rc == BDSSM_OK && clean) {
-        rc = bdssm_commit(dims, block_len, clean, A, D, h, y_commit, stream);
-        if (rc == BDSSM_OK && h_ops)  // the next block's steps read the advanced state
-            rc = bdssm_state_ops(dims, h, h_ops, stream);
+        // the next block's steps read the advanced state: with h_ops, the commit refreshes it
+        rc = h_ops ? bdssm_commit_refresh(dims, block_len, clean, A, D, h, h_ops, BDSSM_STATE_OPS, y_commit, stream)
+                   : bdssm_commit(dims, block_len, clean, A, D, h, y_commit, stream);
     }
     hipGraph_t graph = nullptr;
     const hipError_t ce = hipStreamEndCapture(st, &graph);

@@ -94,10 +94,12 @@ bool prefix_mfma_supported(const Shape &s, int chunk);
 PrefixPlan prefix_mfma_plan(const Shape &s, int64_t len, int chunk, bool full, bool single_segment = false);
 // rev: scan from the last token to the first and add the outputs to y (y required, no chunk
 // states; h_out may be NULL when y is given); D may then be NULL (no skip term)
+// enc (single segment, state only): h_out also written encoded for the block step, as the
+// operand form or (enc_hi_only) the bf16 state
 hipError_t run_prefix_mfma(const Shape &s, int64_t len, int chunk, const Seq &in, const float *A,
                            const float *D, const float *h_init, void *y, float *chunk_states,
                            float *h_out, void *ws, hipStream_t st, bool single_segment = false,
-                           bool rev = false);
+                           bool rev = false, void *enc = nullptr, bool enc_hi_only = false);
 bool block_mfma_supported(const Shape &s, int T);
 void block_mfma_plan(const Shape &s, int *hpw, int *ps);
 hipError_t launch_block_step_mfma(const BlockArgs &a, int hpw, int ps, hipStream_t st);

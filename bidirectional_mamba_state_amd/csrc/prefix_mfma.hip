@@ -68,7 +68,29 @@ struct ScanArgs {
     float *tot;          // STATE: natural-log decay of each segment [b][nseg][H], or NULL
     void *y;             // FULL: [b][len][H][P] in s.y_dt, or NULL
     float *chunk_states; // FULL: [b][nch][H][N][P], or NULL
+    void *enc;           // STATE, single segment: the end state also encoded for the block
+                         // step ([b][H][2][N/8][P][8] operand form, or [b][H][N/8][P][8] bf16),
+                         // or NULL
+    int enc_hi_only;     // enc holds only the hi parts (the bf16 state)
 };
+
+// A lane's four accumulator values, rows n0 .. n0+3 (n0 % 4 == 0) of column p of one head's
+// state, encoded for the block step: hi = bf16(S) and lo = bf16(S - hi), both rounded to
+// nearest even (the same parts the operand-form pass makes), each four contiguous elements
+// of [N/8][P][8]; with hi_only just the hi parts.
+__device__ __forceinline__ void store_encoded4(__bf16 *head, bool hi_only, int n0, int p, f32x4 v)
+{
+    bf16x4 hi, lo;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        hi[j] = static_cast<__bf16>(v[j]);
+        lo[j] = static_cast<__bf16>(v[j] - static_cast<float>(hi[j]));
+    }
+    const int o = ((n0 >> 3) * kP + p) * 8 + (n0 & 7);
+    *reinterpret_cast<bf16x4 *>(head + o) = hi;
+    if (!hi_only)
+        *reinterpret_cast<bf16x4 *>(head + kN * kP + o) = lo;
+}
 
 template <int HPW>
 struct Lds {
@@ -296,6 +318,15 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
     // ---- end of the segment
     if (!FULL && a.h_end)
         store_state(a.h_end + ((static_cast<int64_t>(b) * a.nseg + sg) * H + h0) * NP);
+    if (!FULL && a.enc) {  // single segment: the end state is the stream's new state
+        const int64_t per = a.enc_hi_only ? NP : 2 * NP;
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                store_encoded4(static_cast<__bf16 *>(a.enc) + (static_cast<int64_t>(b) * H + h0 + hh) * per,
+                               a.enc_hi_only, 16 * i + 4 * q, p0 + r16, hs[hh][i]);
+    }
     if (FULL && a.h_last && sg == a.nseg - 1)
         store_state(a.h_last + (static_cast<int64_t>(b) * H + h0) * NP);
     if (!FULL && a.tot && tid == 0) {
@@ -628,6 +659,15 @@ __device__ __forceinline__ void state_pass(const ScanArgs &a)
                 for (int j = 0; j < 4; ++j)
                     base[(16 * i + 4 * q + j) * kP + p0 + r16] = hs[hh][i][j];
         }
+    }
+    if (a.enc) {  // single segment: the end state is the stream's new state
+        const int64_t per = a.enc_hi_only ? NP : 2 * NP;
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                store_encoded4(static_cast<__bf16 *>(a.enc) + (static_cast<int64_t>(b) * H + h0 + hh) * per,
+                               a.enc_hi_only, 16 * i + 4 * q, p0 + r16, hs[hh][i]);
     }
     if (a.tot && tid == 0) {
 #pragma unroll
@@ -1152,10 +1192,13 @@ PrefixPlan prefix_mfma_plan(const Shape &s, int64_t len, int chunk, bool full, b
 
 hipError_t run_prefix_mfma(const Shape &s, int64_t len, int chunk, const Seq &in, const float *A,
                            const float *D, const float *h_init, void *y, float *chunk_states,
-                           float *h_out, void *ws, hipStream_t st, bool single_segment, bool rev)
+                           float *h_out, void *ws, hipStream_t st, bool single_segment, bool rev,
+                           void *enc, bool enc_hi_only)
 {
     const bool full = y || chunk_states;
     if (rev && (!y || chunk_states))  // reverse order: y accumulated, nothing else
+        return hipErrorInvalidValue;
+    if (enc && (full || !single_segment))  // the encoded copy comes from a single state pass
         return hipErrorInvalidValue;
     const PrefixPlan p = prefix_mfma_plan(s, len, chunk, full, single_segment);
     const int hpw_full = pick_hpw(s, true, single_segment);
@@ -1170,6 +1213,8 @@ hipError_t run_prefix_mfma(const Shape &s, int64_t len, int chunk, const Seq &in
     a.in = in;
     a.A = A;
     a.D = D;
+    a.enc = enc;
+    a.enc_hi_only = enc_hi_only ? 1 : 0;
     auto run_full = [&]() {
         a.y = y;
         a.chunk_states = chunk_states;

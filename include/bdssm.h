@@ -299,6 +299,24 @@ bdssm_status bdssm_block_step_variant(const bdssm_dims *dims, int32_t block_len,
                                       const bdssm_step_params *params, void *y, void *stream);
 
 /*
+ * Commit with the block step's copy of the state refreshed in the same pass: bdssm_commit,
+ * then state_copy <- the advanced state in the form state_form (BDSSM_STATE_OPS: the operand
+ * form of bdssm_state_ops; BDSSM_STATE_BF16: the bf16 state of bdssm_state_bf16), bitwise
+ * those calls' results. The cached state changes only at a commit (eqs. (9)-(11)), so this
+ * is the one place a decode loop needs to re-encode it; with bf16 inputs, (d_state,
+ * headdim) = (128, 64) and y == NULL one launch does both (the state walk writes both from
+ * its registers), else a commit and an encoding launch.
+ *   state_copy  [b][H][2][N/8][P][8] or [b][H][N/8][P][8] bf16; must not overlap h, y or
+ *               any input
+ * With block_len = 0 the state is unchanged and only the copy is written. Errors as
+ * bdssm_commit, plus BDSSM_ERR_UNSUPPORTED for a state form other than those two, or the
+ * operand form outside its shape.
+ */
+bdssm_status bdssm_commit_refresh(const bdssm_dims *dims, int32_t block_len, const bdssm_seq *clean,
+                                  const float *A, const float *D, float *h, void *state_copy,
+                                  int32_t state_form, void *y, void *stream);
+
+/*
  * Convolution state. A Mamba layer's cache holds convolution state as well as the SSM
  * state (the cache discussion of "Training Hybrid Block Diffusion Language Models with
  * Partial Bidirectionality"); the pages leave the convolution itself open, and these calls

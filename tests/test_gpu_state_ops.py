@@ -223,3 +223,70 @@ def test_config4_ops_running_set():
         yg = y.float().cpu().numpy()[sample]
         assert within(rel(yg, yo), TOL_BF16, f"c4 block step ops, {label} (sampled streams)")
         assert within(max_head_rel(yg, yo, 2), 4 * TOL_BF16, f"c4 block step ops, {label}, worst head")
+
+
+@pytest.mark.parametrize("b,H,G,T,form,with_y", [
+    (1, 48, 1, 32, bdssm.STATE_OPS, False),     # 700M shape: one head per workgroup
+    (64, 48, 1, 32, bdssm.STATE_OPS, False),    # running set: two heads per workgroup
+    (64, 48, 1, 32, bdssm.STATE_BF16, False),
+    (2, 12, 2, 77, bdssm.STATE_BF16, False),    # ragged block
+    (1, 48, 1, 32, bdssm.STATE_OPS, True),      # with y: a commit and an encoding launch
+    (2, 12, 2, 0, bdssm.STATE_OPS, False),      # no tokens: the copy only
+])
+def test_commit_refresh_bitwise(b, H, G, T, form, with_y):
+    """bdssm_commit_refresh gives bitwise the state of bdssm_commit and the copy of
+    bdssm_state_ops / bdssm_state_bf16 of that state."""
+    import torch
+    from test_oracle_pins import rand_seq
+    rng = np.random.default_rng(300 + b + T)
+    clean = rand_seq(rng, b, max(T, 1), H, 64, 128, G, 1)
+    if T == 0:
+        clean = inputs.Seq(*(np.ascontiguousarray(a[:, :0]) for a in (clean.x, clean.dt, clean.B, clean.C)), 1)
+    A = (-np.exp(rng.uniform(0, np.log(16), H))).astype(np.float32)
+    D = rng.standard_normal(H).astype(np.float32)
+    h0 = (rng.standard_normal((b, H, 128, 64)) * 0.1).astype(np.float32)
+    d = bdssm.dims(b, H, 64, 128, G, bdssm.BF16, bdssm.F32)
+    print(f"[case] commit refresh b={b} H={H} G={G} T={T} form={form} y={with_y}", flush=True)
+    cd = bdssm.seq_to_device(clean) if T > 0 else tuple(torch.empty(16, device="cuda") for _ in range(4))
+    Ad, Dd = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
+    nbytes = bdssm.state_ops_bytes(d) if form == bdssm.STATE_OPS else bdssm.state_bf16_bytes(d)
+    h1 = torch.from_numpy(h0).cuda()
+    c1 = torch.full((nbytes,), 0xAB, dtype=torch.uint8, device="cuda")
+    y1 = torch.empty((b, T, H, 64), device="cuda") if with_y else None
+    bdssm.commit_refresh(d, T, cd, Ad, Dd, h1, c1, form, y1)
+    h2 = torch.from_numpy(h0).cuda()
+    c2 = torch.zeros((nbytes,), dtype=torch.uint8, device="cuda")
+    y2 = torch.empty((b, T, H, 64), device="cuda") if with_y else None
+    bdssm.commit(d, T, cd, Ad, Dd, h2, y2)
+    (bdssm.state_ops if form == bdssm.STATE_OPS else bdssm.state_bf16)(d, h2, c2)
+    torch.cuda.synchronize()
+    assert torch.equal(h1, h2)
+    assert torch.equal(c1, c2)
+    if with_y:
+        assert torch.equal(y1, y2)
+
+
+def test_commit_refresh_vector_alu_shape():
+    """The tiny fp32 shape: the commit, then the bf16 copy (two launches), bitwise."""
+    import torch
+    from test_oracle_pins import rand_seq
+    rng = np.random.default_rng(310)
+    b, H, G, T = 2, 4, 1, 16
+    clean = rand_seq(rng, b, T, H, 16, 16, G, 0)
+    A = (-np.exp(rng.uniform(0, np.log(16), H))).astype(np.float32)
+    D = rng.standard_normal(H).astype(np.float32)
+    h0 = (rng.standard_normal((b, H, 16, 16)) * 0.1).astype(np.float32)
+    d = bdssm.dims(b, H, 16, 16, G, bdssm.F32, bdssm.F32)
+    print("[case] commit refresh, fp32 inputs, d_state 16", flush=True)
+    cd = bdssm.seq_to_device(clean)
+    Ad, Dd = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
+    h1, h2 = torch.from_numpy(h0).cuda(), torch.from_numpy(h0).cuda()
+    c1 = torch.empty(bdssm.state_bf16_bytes(d), dtype=torch.uint8, device="cuda")
+    c2 = torch.empty_like(c1)
+    bdssm.commit_refresh(d, T, cd, Ad, Dd, h1, c1, bdssm.STATE_BF16)
+    bdssm.commit(d, T, cd, Ad, Dd, h2)
+    bdssm.state_bf16(d, h2, c2)
+    torch.cuda.synchronize()
+    assert torch.equal(h1, h2) and torch.equal(c1, c2)
+    with pytest.raises(bdssm.BdssmError):
+        bdssm.commit_refresh(d, T, cd, Ad, Dd, h1, c1, bdssm.STATE_OPS)   # no operand form at this shape
