@@ -82,6 +82,7 @@ struct ConvArgs {
 struct PrefixPlan {
     int seg_sub;       // 64-token sub-chunks per segment
     int nseg;          // segments per stream
+    int hpw_state;     // heads per workgroup of the state-only pass (1, 2 or 4)
     size_t tot_bytes;  // workspace bytes for segment decays (256-byte rounded)
     size_t ws_bytes;   // total workspace bytes (0 for a single segment)
 };

@@ -20,13 +20,13 @@
 // Passes:
 //   STATE  from h_init (or zero): only the state recurrence; writes the segment's end
 //          state and its total log-decay (used by the segment scan, or as h_out).
-//          k_state (one head per workgroup, inputs copied straight into LDS) or k_scan<false,
-//          2> (two heads per workgroup, inputs staged through registers).
+//          k_fold*: the end state as a weighted sum of the segment's tokens, walked from
+//          its last sub-chunk to its first, 1, 2 or 4 heads of a B/C group per workgroup.
 //   FULL   from the state entering the segment: also y (k_full_*, inputs copied straight
-//          into LDS), or only the chunk states (k_scan<true, 1>): the state after every
-//          chunk of Q tokens and after the last token, and, for the stream's last segment,
-//          the final state.
-// Reverse order (REV): k_state and the full pass also scan a sequence from its last token
+//          into LDS), or only the chunk states (k_scan<1>): the state after every chunk of
+//          Q tokens and after the last token, and, for the stream's last segment, the final
+//          state.
+// Reverse order (REV): k_fold and the full pass also scan a sequence from its last token
 // to its first (token t of the scan is token len - 1 - t of the stream), reading the same
 // layouts: row r of a sub-chunk holding scan positions t0 .. t0 + n - 1 is stream token
 // (len - t0 - n) + (n - 1 - r). The full pass then adds its outputs to y instead of writing
@@ -37,6 +37,7 @@
 // products against them keep ~16 significant bits; B, C and x are exact in bf16.
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 #include "internal.h"
 #include "mfma_tiles.h"
@@ -101,7 +102,7 @@ struct Lds {
 };
 
 
-template <bool FULL, int HPW>
+template <int HPW>
 __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
 {
     __shared__ __attribute__((aligned(16))) Lds<HPW> L;
@@ -252,7 +253,7 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
         tables(1);
     for (int k = 0; k < nsub; ++k) {
         __syncthreads();  // (A) sub-chunk k staged, its tables written
-        if (FULL && a.chunk_states && k > 0)
+        if (a.chunk_states && k > 0)
             emit_chunk_state(k - 1);
         // the loads of sub-chunk k+1, in flight during sub-chunk k
         const int kn = min(k + 1, nsub - 1);
@@ -312,28 +313,12 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
         if (k + 2 < nsub)
             tables(k + 2);
     }
-    if (FULL && a.chunk_states)
+    if (a.chunk_states)
         emit_chunk_state(nsub - 1);
 
     // ---- end of the segment
-    if (!FULL && a.h_end)
-        store_state(a.h_end + ((static_cast<int64_t>(b) * a.nseg + sg) * H + h0) * NP);
-    if (!FULL && a.enc) {  // single segment: the end state is the stream's new state
-        const int64_t per = a.enc_hi_only ? NP : 2 * NP;
-#pragma unroll
-        for (int hh = 0; hh < HPW; ++hh)
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                store_encoded4(static_cast<__bf16 *>(a.enc) + (static_cast<int64_t>(b) * H + h0 + hh) * per,
-                               a.enc_hi_only, 16 * i + 4 * q, p0 + r16, hs[hh][i]);
-    }
-    if (FULL && a.h_last && sg == a.nseg - 1)
+    if (a.h_last && sg == a.nseg - 1)
         store_state(a.h_last + (static_cast<int64_t>(b) * H + h0) * NP);
-    if (!FULL && a.tot && tid == 0) {
-#pragma unroll
-        for (int hh = 0; hh < HPW; ++hh)
-            a.tot[(static_cast<int64_t>(b) * a.nseg + sg) * H + h0 + hh] = seg_tot[hh];
-    }
 }
 
 // Token mapping of the reverse order: the stream token held by the first memory row of the
@@ -377,58 +362,103 @@ __global__ __launch_bounds__(256) void k_seg_scan(float *buf, const float *tot, 
         h_out[(static_cast<int64_t>(b) * H + h) * NP + e] = v;
 }
 
-// State-only pass (segment end states, and the commit): h <- exp(c_63) h + B^T (w o x) per
-// 64-token sub-chunk, w_s = exp(c_63 - c_s) dt_s, with the state in the MFMA accumulators of
-// wavefront w (columns 16w .. 16w+15) as in k_scan. Its time per sub-chunk is the staging of
-// B and x (24 KB per head), so they are copied straight into LDS (gfx950 buffer loads to
-// LDS, no registers on the way) in whole 128-byte lines, two sub-chunks ahead into three
-// buffers, and read by transposing reads. One head per workgroup (with two, the operands
-// do not fit the registers beside the states; those launches keep k_scan).
-// The compiler waits for a copy before an LDS read only when it cannot tell that the two
-// touch different buffers; it can when each buffer is its own LDS array, the loop is
-// unrolled by NBUF (buffer choice known at compile time) and its body has no branch. So:
-// the loop runs whole groups of NBUF sub-chunks (the rest after it), every wavefront builds
-// its own copy of the decay tables (no wavefront-dependent branch), the staging buffers
-// are cleared once before the first copy instead of per sub-chunk (rows past the stream's
-// end then hold zeros or an earlier sub-chunk's finite inputs, and weigh 0), and the
-// barriers are bare (a memory fence would wait for every copy). Tile layouts, 16-byte
-// pieces of a row permuted so that a transposing read (4 rows x 32 bytes per 16 lanes)
-// falls in distinct banks:
-//   B: 64 rows x 128 bf16, piece c of row t at slot c ^ 2 (t % 4);
-//   x: 64 rows x 64 bf16 per head, piece c of row t at slot c ^ 2 (t % 4).
-// (the body is a device function template with one kernel per scan order: a kernel template
-// built from generic lambdas loses its host-side launch stub in this compiler)
-template <bool REV>
-__device__ __forceinline__ void state_pass(const ScanArgs &a)
+
+// ---- State-only pass as a weighted sum (segment end states, state-only scans, commits)
+//
+// The end state of a segment is a weighted sum over its tokens,
+//   h_end = exp(R) h_in + sum_t exp(sum_{u > t} a_u) dt_t B_t x_t^T,   a_u = dt_u A, R = sum_u a_u,
+// so the segment can be walked from its last sub-chunk to its first with R, the log-decay of
+// everything after the current sub-chunk, carried as one number per head: a token's weight is
+// then exp2(R + c_63 - c_t) dt_t (c the sub-chunk's inclusive cumulative log2-decay) and the
+// state accumulators are never rescaled. Weights of tokens far from the end underflow to zero,
+// as their true weights do. Rounding differs from the forward walk of the full pass (sums in
+// another order, weights relative to the segment's end).
+//
+// A workgroup owns HPW heads of one B/C group, in 4 HS wavefronts: wavefront w holds columns
+// 16 (w % 4) .. +15 of the HPW / HS heads hb = (w / 4) HPW / HS .. (all 128 rows), so the B^T
+// operand it reads serves all its heads and the staged B the whole workgroup. B and the heads'
+// x are copied into LDS by buffer loads to LDS in whole lines, NBUF - 1 sub-chunks ahead into
+// NBUF buffers. What keeps the matrix cores busy:
+//  - no wait for copies in flight: the compiler makes an LDS read wait for the copies it
+//    cannot tell apart from it, so each buffer is its own LDS array, the loop is unrolled by
+//    NBUF (buffer choice known at compile time) with no branch on the copies' path, and every
+//    read address is one step from its array (offsets precomputed, opaque to the optimizer)
+//    so that the read keeps its attribution to that array;
+//  - the copies of a step are spread over its products: a copy issued while the memory queue
+//    is full stalls its wavefront, and with it the wavefront's share of the matrix core;
+//  - two wavefronts per SIMD (HS = 2 for 2 and 4 heads), operands read per contraction block;
+//  - the token weights of step j + 1 are computed at the end of step j by one wavefront per
+//    head and published by the barrier, outside the step's critical path;
+//  - tile layouts free of LDS bank conflicts for 32-lane transposing reads (swz_b, swz_x).
+
+// f(integral_constant<int, 0>), .. f(integral_constant<int, N - 1>), in order
+template <int N, typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>)
 {
-    constexpr int HPW = 1, NBUF = 3;
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
+
+// v unchanged, but opaque to the optimizer (an empty asm statement that may change it)
+__device__ __forceinline__ int opaque_int(int v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// Piece permutations of the fold pass's tiles: a transposing read of 32 lanes covers 8
+// consecutive rows x 32 bytes, and each 16-byte piece c of row t sits at slot c ^ swz(t) so
+// that those 256 bytes fall in distinct banks: B rows (256 bytes, one bank period) need 8
+// distinct piece pairs; x rows (128 bytes, two rows per period) need distinct pairs among the
+// even rows and among the odd ones.
+__device__ __forceinline__ int swz_b(int t) { return 2 * (t & 7); }
+__device__ __forceinline__ int swz_x(int t) { return 2 * ((t >> 1) & 3); }
+
+template <int HPW, int HS, int NBUF, bool REV>
+__device__ __forceinline__ void fold_pass(const ScanArgs &a)
+{
+    static_assert(NBUF == 3 || NBUF == 4, "three or four staging buffers");
+    static_assert(HPW % HS == 0, "heads split evenly over the wavefront groups");
+    constexpr int WPG = 4 * HS, HW = HPW / HS;  // wavefronts per workgroup, heads per wavefront
+    constexpr int B3 = NBUF > 3 ? SC * kN : 8, X3 = NBUF > 3 ? SC * kP : 8;  // (a stub when unused)
     __shared__ __attribute__((aligned(16))) __bf16 sB0[SC * kN];
     __shared__ __attribute__((aligned(16))) __bf16 sB1[SC * kN];
     __shared__ __attribute__((aligned(16))) __bf16 sB2[SC * kN];
+    __shared__ __attribute__((aligned(16))) __bf16 sB3[B3];
     __shared__ __attribute__((aligned(16))) __bf16 sX0[HPW][SC * kP];
     __shared__ __attribute__((aligned(16))) __bf16 sX1[HPW][SC * kP];
     __shared__ __attribute__((aligned(16))) __bf16 sX2[HPW][SC * kP];
-    // per wavefront: TAB_W and the total log-decay of sub-chunks k, k+1, k+2 (by k % 3)
-    __shared__ __attribute__((aligned(16))) float sW[3][4][HPW][SC];
-    __shared__ float sTot[3][4][HPW];
+    __shared__ __attribute__((aligned(16))) __bf16 sX3[HPW][X3];
+    // token weights of walk steps j (by j % 2), per head: written by wavefront hh of head hh
+    // at the end of the step before, read by every wavefront of the head after the barrier
+    __shared__ __attribute__((aligned(16))) float sW[2][HPW][SC];
+    __shared__ float sR[HPW];  // each head's log2-decay over the segment
     auto bufB = [&](auto ph) -> __bf16 * {
         if constexpr (decltype(ph)::value == 0)
             return sB0;
         else if constexpr (decltype(ph)::value == 1)
             return sB1;
-        else
+        else if constexpr (decltype(ph)::value == 2)
             return sB2;
-    };
-    auto bufX = [&](auto ph, int hh) -> __bf16 * {
-        if constexpr (decltype(ph)::value == 0)
-            return sX0[hh];
-        else if constexpr (decltype(ph)::value == 1)
-            return sX1[hh];
         else
-            return sX2[hh];
+            return sB3;
+    };
+    auto bufX = [&](auto ph) -> __bf16 * {  // the HPW heads' tiles, one after the other
+        if constexpr (decltype(ph)::value == 0)
+            return &sX0[0][0];
+        else if constexpr (decltype(ph)::value == 1)
+            return &sX1[0][0];
+        else if constexpr (decltype(ph)::value == 2)
+            return &sX2[0][0];
+        else
+            return &sX3[0][0];
     };
 
-    // workgroups of one segment (all heads of a stream) go to the same XCD
+    // workgroups of one segment (all head groups of a stream) go to the same XCD
     const int nwg = gridDim.x;
     int lid = blockIdx.x;
     if ((nwg & 7) == 0)
@@ -440,7 +470,8 @@ __device__ __forceinline__ void state_pass(const ScanArgs &a)
     const int g = h0 / (H / G);
     const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int p0 = 16 * wave;  // this wavefront's state columns
+    const int p0 = 16 * (wave & 3);  // this wavefront's state columns
+    const int hb = (wave >> 2) * HW;  // and its first head (of h0 + hb .. h0 + hb + HW - 1)
 
     const int64_t len = a.len;
     const int64_t seg_t0 = static_cast<int64_t>(sg) * a.seg_sub * SC;
@@ -451,238 +482,274 @@ __device__ __forceinline__ void state_pass(const ScanArgs &a)
     const __bf16 *Bg = static_cast<const __bf16 *>(a.in.B) + tok0 * rowBC + g * kN;
     const __bf16 *xg = static_cast<const __bf16 *>(a.in.x) + tok0 * rowX + h0 * kP;
     const __bf16 *dtg = static_cast<const __bf16 *>(a.in.dt) + tok0 * H + h0;
-    // range-checked buffers over the tokens of one sub-chunk (based at its first token, so
-    // that offsets stay small however long the stream): rows past the stream's end read as
-    // zero
-    const auto mk = buffer_range;
-    float Ah[HPW];
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh)
-        Ah[hh] = a.A[h0 + hh];
+    // range-checked buffer over [base, base + bytes), both the same in every lane: built from
+    // lane 0's values, so that the descriptor is known to be uniform and stays in scalar
+    // registers
+    auto mk = [](const void *base, int bytes) {
+        const uint64_t p = reinterpret_cast<uint64_t>(base);
+        const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p));
+        const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32));
+        return buffer_range(reinterpret_cast<const void *>((static_cast<uint64_t>(hi) << 32) | lo),
+                            __builtin_amdgcn_readfirstlane(bytes));
+    };
+    // wavefront w < HPW computes the token weights of head h0 + w; every wavefront loads the
+    // dt of head h0 + w % HPW (the same number of loads in every wavefront keeps the waits
+    // of the barriers exact)
+    const int hd = wave % HPW;
+    const float Aw = a.A[h0 + hd] * kLog2e;  // A in log2 units
 
-    // ---- copies of sub-chunk k into buffer PH = k % NBUF: B in 16 pieces of 1 KB (4 rows),
-    // x in 8 per head (8 rows); wavefront w takes B pieces w + 4u (u < 4) and x pieces
-    // w + 4 (u - 4) (u >= 4)
-    constexpr int NPW = 4 + 2 * HPW;  // pieces per wavefront
-    auto piece_B = [&](int u) { return wave + 4 * u; };
-    auto piece_X = [&](int u) { return wave + 4 * (u - 4); };  // head px / 8, rows 8 (px % 8) ..
-    auto copy = [&](auto PH, int k) {
-        const int kk = min(k, nsub - 1);  // past the segment: the last sub-chunk again (unused)
-        const int64_t t0 = seg_t0 + static_cast<int64_t>(kk) * SC;
+    // walk step j handles the segment's sub-chunk nsub - 1 - j; a step past the segment
+    // (issued ahead, never used) gets empty ranges, so its copies and dt loads read nothing
+    auto sub_of = [&](int j) { return max(nsub - 1 - j, 0); };
+    // copies of walk step j into buffer PH: B in 16 pieces of 1 KB (4 rows), x in 8 per head
+    // (8 rows); wavefront w takes pieces w, w + WPG, ... of the 16 + 8 HPW
+    constexpr int NPIECE = 16 + 8 * HPW, NPW = NPIECE / WPG;
+    static_assert(NPIECE % WPG == 0 && 16 % WPG == 0, "pieces split evenly");
+    struct Ranges {
+        __amdgpu_buffer_rsrc_t rB, rX;
+        int nrows;
+    };
+    auto ranges = [&](int j) {
+        const int64_t t0 = seg_t0 + static_cast<int64_t>(sub_of(j)) * SC;
         const int nrows = static_cast<int>(min<int64_t>(SC, len - t0));
         const int64_t f0 = first_token<REV>(len, t0, nrows);
-        const auto rB = mk(Bg + f0 * rowBC, ((nrows - 1) * rowBC + kN) * 2);
-        const auto rX = mk(xg + f0 * rowX, ((nrows - 1) * rowX + HPW * kP) * 2);
+        const bool live = j < nsub;
+        return Ranges{mk(Bg + f0 * rowBC, live ? ((nrows - 1) * rowBC + kN) * 2 : 0),
+                      mk(xg + f0 * rowX, live ? ((nrows - 1) * rowX + HPW * kP) * 2 : 0), nrows};
+    };
+    // this wavefront's pieces U0 .. U1 - 1 of walk step j's copies (ranges from ranges(j))
+    auto copy_part = [&](auto PH, auto U0, auto U1, const Ranges &g) {
+        const auto rB = g.rB;
+        const auto rX = g.rX;
+        const int nrows = g.nrows;
 #pragma unroll
-        for (int u = 0; u < NPW; ++u) {
-            if (u < 4) {
-                const int pc = piece_B(u), row = 4 * pc + (lane >> 4), c = (lane & 15) ^ (2 * (row & 3));
+        for (int u = decltype(U0)::value; u < decltype(U1)::value; ++u) {
+            const int pc = wave + WPG * u;  // a B piece exactly when u < 16 / WPG
+            if (u < 16 / WPG) {
+                const int row = 4 * pc + (lane >> 4), c = (lane & 15) ^ swz_b(row);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     rB, (__attribute__((address_space(3))) void *)(bufB(PH) + 4 * pc * kN), 16,
                     (mem_row<REV>(row, nrows) * rowBC + 8 * c) * 2, 0, 0, 0);
             } else {
-                const int px = piece_X(u), hh = px >> 3, row = 8 * (px & 7) + (lane >> 3);
-                const int c = (lane & 7) ^ (2 * (row & 3));
+                const int px = pc - 16, hh = px >> 3, row = 8 * (px & 7) + (lane >> 3);
+                const int c = (lane & 7) ^ swz_x(row);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rX, (__attribute__((address_space(3))) void *)(bufX(PH, hh) + 8 * (px & 7) * kP), 16,
+                    rX, (__attribute__((address_space(3))) void *)(bufX(PH) + hh * SC * kP + 8 * (px & 7) * kP), 16,
                     (mem_row<REV>(row, nrows) * rowX + hh * kP + 8 * c) * 2, 0, 0, 0);
             }
         }
+    };
+    auto copy = [&](auto PH, int j) {
+        copy_part(PH, std::integral_constant<int, 0>{}, std::integral_constant<int, NPW>{}, ranges(j));
     };
     auto clear = [&](auto PH) {  // this wavefront's pieces of buffer PH
         const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int u = 0; u < NPW; ++u) {
-            if (u < 4) {
-                *reinterpret_cast<uint4 *>(bufB(PH) + 4 * piece_B(u) * kN + 8 * lane) = z;
+            const int pc = wave + WPG * u;
+            if (u < 16 / WPG) {
+                *reinterpret_cast<uint4 *>(bufB(PH) + 4 * pc * kN + 8 * lane) = z;
             } else {
-                const int px = piece_X(u);
-                *reinterpret_cast<uint4 *>(bufX(PH, px >> 3) + 8 * (px & 7) * kP + 8 * lane) = z;
+                const int px = pc - 16;
+                *reinterpret_cast<uint4 *>(bufX(PH) + (px >> 3) * SC * kP + 8 * (px & 7) * kP + 8 * lane) = z;
             }
         }
     };
-    // dt of sub-chunk k, token `lane`, every head of the workgroup (zero past the stream's
-    // end; k past the segment: its last sub-chunk again)
-    auto load_dt = [&](int k, unsigned short (&d)[HPW]) {
-        const int kk = min(k, nsub - 1);
-        const int64_t t0 = seg_t0 + static_cast<int64_t>(kk) * SC;
+    // dt of walk step j, token `lane`, head h0 + hd (zero past the stream's end)
+    auto load_dt = [&](int j, unsigned short &d) {
+        const int64_t t0 = seg_t0 + static_cast<int64_t>(sub_of(j)) * SC;
         const int nrows = static_cast<int>(min<int64_t>(SC, len - t0));
-        const auto rD = mk(dtg + first_token<REV>(len, t0, nrows) * H, ((nrows - 1) * H + HPW) * 2);
-#pragma unroll
-        for (int hh = 0; hh < HPW; ++hh)
-            d[hh] = __builtin_amdgcn_raw_buffer_load_b16(rD, (mem_row<REV>(lane, nrows) * H + hh) * 2, 0, 0);
+        const auto rD = mk(dtg + first_token<REV>(len, t0, nrows) * H, j < nsub ? ((nrows - 1) * H + HPW) * 2 : 0);
+        d = __builtin_amdgcn_raw_buffer_load_b16(rD, (mem_row<REV>(lane, nrows) * H + hd) * 2, 0, 0);
     };
-    // TAB_W and the total log-decay of sub-chunk k into this wavefront's own tables
-    auto tables = [&](int k, const unsigned short (&dbits)[HPW]) {
+
+    f32x4 acc[HW][8];  // acc[hh][i] holds h[16 i + 4 q + e][p0 + r16] of head h0 + hb + hh
 #pragma unroll
-        for (int hh = 0; hh < HPW; ++hh) {
-            const float d = __uint_as_float(static_cast<uint32_t>(dbits[hh]) << 16);
-            const float inc = wave_prefix_sum(d * Ah[hh]);
-            const float c = inc * kLog2e;
-            const float clast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 63));
-            sW[k % 3][wave][hh][lane] = __builtin_amdgcn_exp2f(clast - c) * d;
-            sTot[k % 3][wave][hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inc), 63));
+    for (int hh = 0; hh < HW; ++hh)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            acc[hh][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float R = 0.f;  // head h0 + hd: log2-decay of the tokens after the weighted sub-chunks
+    // weights of walk step j into sW[j % 2][hd] (wavefronts w < HPW): exp2(R + c_63 - c_t) dt_t,
+    // lane t
+    auto weights = [&](int j, unsigned short dbits) {
+        if (wave < HPW) {
+            const float d = __uint_as_float(static_cast<uint32_t>(dbits) << 16);
+            const float c = wave_prefix_sum(d * Aw);
+            const float clast = wave_lane(c, 63);
+            sW[j & 1][hd][lane] = __builtin_amdgcn_exp2f(R + (clast - c)) * d;
+            R += clast;
         }
     };
 
-    f32x4 hs[HPW][8];  // hs[hh][i] holds h[16 i + 4 q + j][p0 + r16] of head h0 + hh
-    float seg_tot[HPW];
+    // element offsets of this lane's transposing reads in a buffer, for contraction block ks
+    // (tokens 32 ks + 4 q + e and, 16 rows on, 32 ks + 16 + 4 q + e): B^T rows 16 i + r16 and
+    // x columns p0 + r16. Each is made opaque to the optimizer once, here: a read's address is
+    // then one step from its LDS array, which keeps the compiler's attribution of the read to
+    // that array (needed to tell it from the copies in flight) within its search depth.
+    int offB[2][8], offX[2][HW];
 #pragma unroll
-    for (int hh = 0; hh < HPW; ++hh)
-        seg_tot[hh] = 0.f;
-    // one sub-chunk k, in buffer PH = k % NBUF
-    auto step = [&](auto PH, int k) {
+    for (int ks = 0; ks < 2; ++ks) {
+        const int tr = 32 * ks + 4 * q + (r16 >> 2);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int col = 16 * i + 4 * (r16 & 3);
+            offB[ks][i] = opaque_int(tr * kN + 8 * ((col >> 3) ^ swz_b(tr)) + (col & 7));
+        }
+        const int col = p0 + 4 * (r16 & 3);
+#pragma unroll
+        for (int hh = 0; hh < HW; ++hh)
+            offX[ks][hh] = opaque_int((hb + hh) * SC * kP + tr * kP + 8 * ((col >> 3) ^ swz_x(tr)) + (col & 7));
+    }
+
+    // dt of walk steps j .. j + NBUF - 2, by j % NBUF
+    unsigned short dts[NBUF];
+    // one walk step j, in buffer PH = j % NBUF, with its dt in dts[PH] (loaded NBUF - 1 steps
+    // before); loads the dt of step j + NBUF - 1 into the slot the previous step has left
+    auto step = [&](auto PH, int j) {
         constexpr int ph = decltype(PH)::value, phn = (ph + NBUF - 1) % NBUF;
-        // this wavefront's copies of k have landed once at most those issued after them are
-        // in flight: dt of k+1 and the copies of k+1
-        workgroup_lds_barrier<NPW + HPW>();
-        unsigned short dn[HPW];
-        {
-            // every operand of the sub-chunk into registers first: B^T (contraction over tokens
-            // 32 ks + 4q + e and 32 ks + 16 + 4q + e, rows n = 16 i + r16) and x~ (columns
-            // p0 + r16) by transposing reads (lane r16 addresses row 4q + r16/4, columns
-            // 4 (r16 % 4) .. of a 16-column block), and the weights
-            bf16x8 bt[2][8], xf[HPW][2];
-            float wv[HPW][2][8];
+        constexpr int phw = (ph + 1) % NBUF;  // the dt slot of step j + 1
+        unsigned short &dn = dts[phn];
+        // this wavefront's copies of j have landed once at most those issued after them are in
+        // flight: the dt and copies of j + 1 .. j + NBUF - 2; the weights of j are in sW
+        workgroup_lds_barrier<(NBUF - 2) * (1 + NPW)>();
+        // then walk step j + NBUF - 1 into the buffer j - 1 has left, its dt first, the copies
+        // spread over the products below (a copy issued while the memory queue is full stalls
+        // the wavefront, and with it its matrix core)
+        load_dt(j + NBUF - 1, dn);
+        const Ranges g = ranges(j + NBUF - 1);
+        constexpr int NG = 2 * HW;  // product groups (ks, hh)
+        static_for<2>([&](auto KS) {
+            constexpr int ks = decltype(KS)::value;
+            // the operands of contraction block ks (tokens 32 ks + 4 q + e and 32 ks + 16 + 4 q
+            // + e): B^T (rows 16 i + r16) and x (columns p0 + r16) by transposing reads, and the
+            // tokens' weights (a read may follow copies already issued: its address is known to
+            // lie in another LDS array)
+            bf16x8 bt[8], xf[HW];
+            float wv[HW][8];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const int tr = 32 * ks + 4 * q + (r16 >> 2), sw = 2 * (tr & 3);
+            for (int hh = 0; hh < HW; ++hh) {
+                const float4 w0 = *reinterpret_cast<const float4 *>(&sW[j & 1][hb + hh][32 * ks + 4 * q]);
+                const float4 w1 = *reinterpret_cast<const float4 *>(&sW[j & 1][hb + hh][32 * ks + 16 + 4 * q]);
+                wv[hh][0] = w0.x, wv[hh][1] = w0.y, wv[hh][2] = w0.z, wv[hh][3] = w0.w;
+                wv[hh][4] = w1.x, wv[hh][5] = w1.y, wv[hh][6] = w1.z, wv[hh][7] = w1.w;
+                const __bf16 *px = bufX(PH) + offX[ks][hh];
+                xf[hh] = cat(tr_read(px), tr_read(px + 16 * kP));
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const __bf16 *p = bufB(PH) + offB[ks][i];
+                bt[i] = cat(tr_read(p), tr_read(p + 16 * kN));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // h += B^T x~ with x~ = w o x split into bf16 hi + lo
+            static_for<HW>([&](auto HH) {
+                constexpr int hh = decltype(HH)::value, gi = ks * HW + hh;
+                copy_part(std::integral_constant<int, phn>{}, std::integral_constant<int, gi * NPW / NG>{},
+                          std::integral_constant<int, (gi + 1) * NPW / NG>{}, g);
+                __builtin_amdgcn_sched_barrier(0);
+                float xw[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    xw[e] = bf2f(xf[hh][e]) * wv[hh][e];
+                bf16x8 xhi, xlo;
+                split8(xw, xhi, xlo);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const int col = 16 * i + 4 * (r16 & 3);
-                    const __bf16 *p = bufB(PH) + tr * kN + 8 * ((col >> 3) ^ sw) + (col & 7);
-                    bt[ks][i] = cat(tr_read(p), tr_read(p + 16 * kN));
+                    acc[hh][i] = mfma(bt[i], xhi, acc[hh][i]);
+                    acc[hh][i] = mfma(bt[i], xlo, acc[hh][i]);
                 }
-#pragma unroll
-                for (int hh = 0; hh < HPW; ++hh) {
-                    const int col = p0 + 4 * (r16 & 3);
-                    const __bf16 *px = bufX(PH, hh) + tr * kP + 8 * ((col >> 3) ^ sw) + (col & 7);
-                    xf[hh][ks] = cat(tr_read(px), tr_read(px + 16 * kP));
-                    const float4 w0 = *reinterpret_cast<const float4 *>(&sW[k % 3][wave][hh][32 * ks + 4 * q]);
-                    const float4 w1 = *reinterpret_cast<const float4 *>(&sW[k % 3][wave][hh][32 * ks + 16 + 4 * q]);
-                    wv[hh][ks][0] = w0.x, wv[hh][ks][1] = w0.y, wv[hh][ks][2] = w0.z, wv[hh][ks][3] = w0.w;
-                    wv[hh][ks][4] = w1.x, wv[hh][ks][5] = w1.y, wv[hh][ks][6] = w1.z, wv[hh][ks][7] = w1.w;
-                }
-            }
-            float tot[HPW];
-#pragma unroll
-            for (int hh = 0; hh < HPW; ++hh)
-                tot[hh] = sTot[k % 3][wave][hh];
-            // then sub-chunk k + NBUF - 1 into the buffer k - 1 has left, its dt first (the
-            // compiler may make the reads above wait for the copies of k+1, but not for these)
-            load_dt(k + 2, dn);
-            copy(std::integral_constant<int, phn>{}, k + NBUF - 1);
-
-            // state: h <- exp(c_63) h + B^T (w o x)
-#pragma unroll
-            for (int hh = 0; hh < HPW; ++hh) {
-                seg_tot[hh] += tot[hh];
-                const float alpha = __expf(tot[hh]);
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    hs[hh][i] *= alpha;
-            }
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-                for (int hh = 0; hh < HPW; ++hh) {
-                    float xw[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        xw[e] = bf2f(xf[hh][ks][e]) * wv[hh][ks][e];
-                    bf16x8 xhi, xlo;
-                    split8(xw, xhi, xlo);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        hs[hh][i] = mfma(bt[ks][i], xhi, hs[hh][i]);
-                        hs[hh][i] = mfma(bt[ks][i], xlo, hs[hh][i]);
-                    }
-                }
-            }
-        }
-        // tables of sub-chunk k+2 into the table buffer k-1 has left
-        tables(k + 2, dn);
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        // the weights of step j + 1 (its dt was loaded NBUF - 1 steps before it)
+        weights(j + 1, dts[phw]);
     };
 
-    // ---- prologue: clear this wavefront's staging pieces, put sub-chunks 0 .. NBUF-2 in
-    // flight (each dt ahead of the copies after it, so that waiting for it never waits for
-    // them), load the entering state, build the tables of 0 and 1, and let everything land
-    // once, so that the waits in the loop can be counted exactly
+    // ---- prologue: clear the staging buffers (rows past the stream's end must hold finite
+    // values: they are weighted 0), put walk steps 0 .. NBUF - 2 in flight, let them land
     clear(std::integral_constant<int, 0>{});
     clear(std::integral_constant<int, 1>{});
     clear(std::integral_constant<int, 2>{});
+    if constexpr (NBUF > 3)
+        clear(std::integral_constant<int, 3>{});
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the clears precede the copies
-    {
-        unsigned short d0[HPW], d1[HPW];
-        load_dt(0, d0);
-        copy(std::integral_constant<int, 0>{}, 0);
-        load_dt(1, d1);
-        copy(std::integral_constant<int, 1>{}, 1);
-#pragma unroll
-        for (int hh = 0; hh < HPW; ++hh) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                hs[hh][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (a.h_in) {
-                const float *hin = a.h_in + ((static_cast<int64_t>(b) * a.nseg + sg) * H + h0 + hh) * NP;
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        hs[hh][i][j] = hin[(16 * i + 4 * q + j) * kP + p0 + r16];
-            }
-        }
-        tables(0, d0);
-        tables(1, d1);
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    load_dt(0, dts[0]);
+    copy(std::integral_constant<int, 0>{}, 0);
+    load_dt(1, dts[1]);
+    copy(std::integral_constant<int, 1>{}, 1);
+    if constexpr (NBUF > 3) {
+        load_dt(2, dts[2]);
+        copy(std::integral_constant<int, 2>{}, 2);
     }
-    int k = 0;
-    for (; k + NBUF <= nsub; k += NBUF) {  // whole groups: a body with no branch
-        step(std::integral_constant<int, 0>{}, k);
-        step(std::integral_constant<int, 1>{}, k + 1);
-        step(std::integral_constant<int, 2>{}, k + 2);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    weights(0, dts[0]);
+    int j = 0;
+    for (; j + NBUF <= nsub; j += NBUF) {  // whole groups: a body with no branch
+        step(std::integral_constant<int, 0>{}, j);
+        step(std::integral_constant<int, 1>{}, j + 1);
+        step(std::integral_constant<int, 2>{}, j + 2);
+        if constexpr (NBUF > 3)
+            step(std::integral_constant<int, 3>{}, j + 3);
     }
-    if (k < nsub)
-        step(std::integral_constant<int, 0>{}, k);
-    if (k + 1 < nsub)
-        step(std::integral_constant<int, 1>{}, k + 1);
+    if (j < nsub)
+        step(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < nsub)
+        step(std::integral_constant<int, 1>{}, j + 1);
+    if constexpr (NBUF > 3)
+        if (j + 2 < nsub)
+            step(std::integral_constant<int, 2>{}, j + 2);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // no copy outlives the workgroup
 
-    // ---- end of the segment
-    if (a.h_end) {
+    // ---- the segment's entering state, decayed over the whole segment (R of a head has then
+    // also taken the weights of the step past the segment, whose dt are zero)
+    if (wave < HPW && lane == 0)
+        sR[hd] = R;
+    __syncthreads();
 #pragma unroll
-        for (int hh = 0; hh < HPW; ++hh) {
-            float *base = a.h_end + ((static_cast<int64_t>(b) * a.nseg + sg) * H + h0 + hh) * NP;
+    for (int hh = 0; hh < HW; ++hh) {
+        const float Rh = sR[hb + hh];
+        const float decay = __builtin_amdgcn_exp2f(Rh);
+        const int64_t hofs = ((static_cast<int64_t>(b) * a.nseg + sg) * H + h0 + hb + hh) * NP;
+        if (a.h_in) {
+            const float *hin = a.h_in + hofs;
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    base[(16 * i + 4 * q + j) * kP + p0 + r16] = hs[hh][i][j];
+                for (int e = 0; e < 4; ++e)
+                    acc[hh][i][e] = fmaf(decay, hin[(16 * i + 4 * q + e) * kP + p0 + r16], acc[hh][i][e]);
         }
-    }
-    if (a.enc) {  // single segment: the end state is the stream's new state
-        const int64_t per = a.enc_hi_only ? NP : 2 * NP;
-#pragma unroll
-        for (int hh = 0; hh < HPW; ++hh)
+        if (a.h_end) {
+            float *base = a.h_end + hofs;
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                store_encoded4(static_cast<__bf16 *>(a.enc) + (static_cast<int64_t>(b) * H + h0 + hh) * per,
-                               a.enc_hi_only, 16 * i + 4 * q, p0 + r16, hs[hh][i]);
-    }
-    if (a.tot && tid == 0) {
 #pragma unroll
-        for (int hh = 0; hh < HPW; ++hh)
-            a.tot[(static_cast<int64_t>(b) * a.nseg + sg) * H + h0 + hh] = seg_tot[hh];
+                for (int e = 0; e < 4; ++e)
+                    base[(16 * i + 4 * q + e) * kP + p0 + r16] = acc[hh][i][e];
+        }
+        if (a.enc) {  // single segment: the end state is the stream's new state
+            const int64_t per = a.enc_hi_only ? NP : 2 * NP;
+            __bf16 *head = static_cast<__bf16 *>(a.enc) + (static_cast<int64_t>(b) * H + h0 + hb + hh) * per;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                store_encoded4(head, a.enc_hi_only, 16 * i + 4 * q, p0 + r16, acc[hh][i]);
+        }
+        if (a.tot && (wave & 3) == 0 && lane == 0)
+            a.tot[(static_cast<int64_t>(b) * a.nseg + sg) * H + h0 + hb + hh] = Rh / kLog2e;
     }
 }
 
-__global__ __launch_bounds__(256, 2) void k_state(ScanArgs a) { state_pass<false>(a); }
-__global__ __launch_bounds__(256, 2) void k_state_rev(ScanArgs a) { state_pass<true>(a); }
+__global__ __launch_bounds__(256, 2) void k_fold1(ScanArgs a) { fold_pass<1, 1, 3, false>(a); }
+__global__ __launch_bounds__(512, 1) void k_fold2(ScanArgs a) { fold_pass<2, 2, 4, false>(a); }
+__global__ __launch_bounds__(512, 1) void k_fold4(ScanArgs a) { fold_pass<4, 2, 3, false>(a); }
+__global__ __launch_bounds__(256, 2) void k_fold1_rev(ScanArgs a) { fold_pass<1, 1, 3, true>(a); }
+__global__ __launch_bounds__(512, 1) void k_fold2_rev(ScanArgs a) { fold_pass<2, 2, 4, true>(a); }
+__global__ __launch_bounds__(512, 1) void k_fold4_rev(ScanArgs a) { fold_pass<4, 2, 3, true>(a); }
 
 // ---- FULL pass with outputs, one head per workgroup, inputs copied straight into LDS
 //
-// The same computation as k_scan<true, true, 1> (and bitwise the same state walk as
-// k_state), with B, C and x copied into LDS by buffer loads to LDS in whole lines instead of
+// The same computation as k_scan<1> with y, with B, C and x copied into LDS by buffer loads
+// to LDS in whole lines instead of
 // through registers: B and x of sub-chunk k+1 are copied at the start of sub-chunk k into
 // the other of two buffers; C, read only before the mid-sub-chunk barrier, has one buffer
 // and its next copy is issued right after that barrier. 71.5 KB of LDS: two workgroups per
@@ -690,7 +757,7 @@ __global__ __launch_bounds__(256, 2) void k_state_rev(ScanArgs a) { state_pass<t
 // read patterns free of bank conflicts: 16-byte operand reads of 16 consecutive rows (score
 // tiles), transposing reads of 4 rows x 16 columns per 16 lanes (B in the state update) and
 // 8-byte reads of the permuted contraction order (C in the state product); x rows
-// (128 bytes) hold piece c of row t at slot c ^ 2 (t % 4), as in k_state.
+// (128 bytes) hold piece c of row t at slot c ^ 2 (t % 4).
 __device__ __forceinline__ int swz(int r)
 {
     return ((r & 3) << 2) | ((r & 4) >> 1) | ((r >> 3) & 1);
@@ -1006,8 +1073,7 @@ __device__ __forceinline__ void full_pass(const ScanArgs &a)
                         yr, off, 0, 0);
                 }
             }
-            // (4) state: h <- exp(c_63) h + B^T (w o x), w_s = exp(c_63 - c_s) dt_s (the same
-            // arithmetic as k_state, so that the walk is bitwise the state-only pass's)
+            // (4) state: h <- exp(c_63) h + B^T (w o x), w_s = exp(c_63 - c_s) dt_s
             {
                 const float tot = sTot[ph];
                 const float alpha = __expf(tot);
@@ -1103,62 +1169,74 @@ __global__ __launch_bounds__(256, 2) void k_full_f32(ScanArgs a) { full_pass<flo
 __global__ __launch_bounds__(256, 2) void k_full_bf16_rev(ScanArgs a) { full_pass<__bf16, true>(a); }
 __global__ __launch_bounds__(256, 2) void k_full_f32_rev(ScanArgs a) { full_pass<float, true>(a); }
 
-template <bool FULL, int HPW, typename Ty>
-hipError_t launch_scan(const ScanArgs &a, bool rev, hipStream_t st)
+// The full pass, one head per workgroup: k_full_* with y, k_scan with the chunk states only
+template <typename Ty>
+hipError_t launch_full(const ScanArgs &a, bool rev, hipStream_t st)
 {
-    const int nwg = a.s.b * a.nseg * (a.s.H / HPW);
-    if constexpr (FULL) {
-        static_assert(HPW == 1, "the full pass runs one head per workgroup");
-        if (a.y) {
-            if constexpr (sizeof(Ty) == 2) {
-                if (rev)
-                    k_full_bf16_rev<<<dim3(nwg), dim3(256), 0, st>>>(a);
-                else
-                    k_full_bf16<<<dim3(nwg), dim3(256), 0, st>>>(a);
-            } else {
-                if (rev)
-                    k_full_f32_rev<<<dim3(nwg), dim3(256), 0, st>>>(a);
-                else
-                    k_full_f32<<<dim3(nwg), dim3(256), 0, st>>>(a);
-            }
-            return hipGetLastError();
+    const int nwg = a.s.b * a.nseg * a.s.H;
+    if (a.y) {
+        if constexpr (sizeof(Ty) == 2) {
+            if (rev)
+                k_full_bf16_rev<<<dim3(nwg), dim3(256), 0, st>>>(a);
+            else
+                k_full_bf16<<<dim3(nwg), dim3(256), 0, st>>>(a);
+        } else {
+            if (rev)
+                k_full_f32_rev<<<dim3(nwg), dim3(256), 0, st>>>(a);
+            else
+                k_full_f32<<<dim3(nwg), dim3(256), 0, st>>>(a);
         }
+        return hipGetLastError();
     }
     if (rev)  // the reverse order exists for the passes with y only
         return hipErrorInvalidValue;
-    k_scan<FULL, HPW><<<dim3(nwg), dim3(256), 0, st>>>(a);
+    k_scan<1><<<dim3(nwg), dim3(256), 0, st>>>(a);
     return hipGetLastError();
 }
 
-template <bool FULL, typename Ty>
-hipError_t launch_scan_hpw(const ScanArgs &a, int hpw, bool rev, hipStream_t st)
+template <int HPW>
+hipError_t launch_fold(const ScanArgs &a, bool rev, hipStream_t st)
 {
-    if constexpr (!FULL) {  // the state-only pass
-        if (hpw == 2)
-            return launch_scan<FULL, 2, Ty>(a, rev, st);
-        const dim3 grid(static_cast<unsigned>(a.s.b * a.nseg * a.s.H));
-        if (rev)
-            k_state_rev<<<grid, dim3(256), 0, st>>>(a);
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.s.b) * a.nseg * (a.s.H / HPW)));
+    const dim3 block(HPW == 1 ? 256 : 512);  // HS = 2 for 2 and 4 heads: eight wavefronts
+    if (rev) {
+        if constexpr (HPW == 4)
+            k_fold4_rev<<<grid, block, 0, st>>>(a);
+        else if constexpr (HPW == 2)
+            k_fold2_rev<<<grid, block, 0, st>>>(a);
         else
-            k_state<<<grid, dim3(256), 0, st>>>(a);
-        return hipGetLastError();
+            k_fold1_rev<<<grid, block, 0, st>>>(a);
     } else {
-        return launch_scan<FULL, 1, Ty>(a, rev, st);
+        if constexpr (HPW == 4)
+            k_fold4<<<grid, block, 0, st>>>(a);
+        else if constexpr (HPW == 2)
+            k_fold2<<<grid, block, 0, st>>>(a);
+        else
+            k_fold1<<<grid, block, 0, st>>>(a);
     }
+    return hipGetLastError();
 }
 
-// Heads per workgroup: as many as the pass allows (shared B/C staging and scores), but
-// no fewer workgroups than CUs when the segment count is fixed at one.
-int pick_hpw(const Shape &s, bool full, bool single_segment)
+// The state-only pass (k_fold, HPW heads per workgroup)
+hipError_t launch_state_pass(const ScanArgs &a, int hpw, bool rev, hipStream_t st)
+{
+    if (hpw == 4)
+        return launch_fold<4>(a, rev, st);
+    if (hpw == 2)
+        return launch_fold<2>(a, rev, st);
+    return launch_fold<1>(a, rev, st);
+}
+
+// Heads per workgroup of the state-only pass: the largest of 4 and 2 that divides the heads
+// of one B/C group (a staged B then serves them all) and still leaves a workgroup for every
+// CU with nseg segments per stream; else 1 (two workgroups per CU).
+int pick_fold_hpw(const Shape &s, int64_t nseg)
 {
     const int hpg = s.H / s.G;
-    int hpw = full ? 1 : (static_cast<int64_t>(s.b) * s.H >= 2048 ? 2 : 1);
-    while (hpw > 1 && hpg % hpw != 0)
-        hpw /= 2;
-    if (single_segment)
-        while (hpw > 1 && static_cast<int64_t>(s.b) * (s.H / hpw) < 256)
-            hpw /= 2;
-    return hpw;
+    for (int hpw = 4; hpw > 1; hpw /= 2)
+        if (hpg % hpw == 0 && static_cast<int64_t>(s.b) * nseg * (s.H / hpw) >= device_cus())
+            return hpw;
+    return 1;
 }
 
 }  // namespace
@@ -1170,20 +1248,31 @@ bool prefix_mfma_supported(const Shape &s, int chunk)
 
 // Work plan: segments of consecutive sub-chunks, as many (stream, head group, segment)
 // workgroups as the GPU holds at once -- a few more would run as a second, mostly empty
-// round. The full pass holds 2 workgroups per CU, the state-only pass with one head per
-// workgroup 4.
+// round. The full pass runs one head per workgroup, 2 workgroups per CU. A state-only scan
+// takes a single segment when (stream, head group) workgroups already fill the GPU, else
+// the largest head group dividing the heads of one B/C group with as many segments as one
+// workgroup per CU allows (two per CU with one head each).
 PrefixPlan prefix_mfma_plan(const Shape &s, int64_t len, int chunk, bool full, bool single_segment)
 {
     (void)chunk;
     PrefixPlan p{};
-    const int hpw = pick_hpw(s, full, single_segment);
-    const int64_t groups = std::max<int64_t>(1, static_cast<int64_t>(s.b) * (s.H / hpw));
     const int64_t nsub = std::max<int64_t>(1, (len + SC - 1) / SC);
-    const int64_t slots = static_cast<int64_t>(full || hpw > 1 ? 2 : 4) * device_cus();
-    const int64_t want = single_segment ? 1 : std::max<int64_t>(1, slots / groups);
+    const int64_t bh = std::max<int64_t>(1, static_cast<int64_t>(s.b) * s.H);
+    int64_t want = 1;
+    int hpw = pick_fold_hpw(s, 1);
+    if (!single_segment) {
+        if (full) {
+            want = std::max<int64_t>(1, 2 * device_cus() / bh);
+        } else if (bh / hpw < device_cus()) {
+            const int hpg = s.H / s.G;
+            hpw = hpg % 4 == 0 ? 4 : hpg % 2 == 0 ? 2 : 1;
+            want = std::max<int64_t>(1, (hpw > 1 ? 1 : 2) * device_cus() / (bh / hpw));
+        }
+    }
     const int64_t seg_sub = (nsub + want - 1) / want;
     p.seg_sub = static_cast<int>(seg_sub);
     p.nseg = static_cast<int>((nsub + seg_sub - 1) / seg_sub);
+    p.hpw_state = full ? pick_fold_hpw(s, p.nseg) : hpw;
     const int64_t nbh = static_cast<int64_t>(s.b) * p.nseg * s.H;
     p.tot_bytes = p.nseg > 1 ? static_cast<size_t>((nbh * 4 + 255) / 256 * 256) : 0;
     p.ws_bytes = p.nseg > 1 ? p.tot_bytes + static_cast<size_t>(nbh) * kN * kP * 4 : 0;
@@ -1201,8 +1290,6 @@ hipError_t run_prefix_mfma(const Shape &s, int64_t len, int chunk, const Seq &in
     if (enc && (full || !single_segment))  // the encoded copy comes from a single state pass
         return hipErrorInvalidValue;
     const PrefixPlan p = prefix_mfma_plan(s, len, chunk, full, single_segment);
-    const int hpw_full = pick_hpw(s, true, single_segment);
-    const int hpw_state = rev ? 1 : pick_hpw(s, false, single_segment || p.nseg == 1);
     ScanArgs a{};
     a.s = s;
     a.len = len;
@@ -1219,8 +1306,7 @@ hipError_t run_prefix_mfma(const Shape &s, int64_t len, int chunk, const Seq &in
         a.y = y;
         a.chunk_states = chunk_states;
         a.h_last = h_out;
-        return s.y_dt ? launch_scan_hpw<true, __bf16>(a, hpw_full, rev, st)
-                      : launch_scan_hpw<true, float>(a, hpw_full, rev, st);
+        return s.y_dt ? launch_full<__bf16>(a, rev, st) : launch_full<float>(a, rev, st);
     };
     if (p.nseg == 1) {
         // one segment per (stream, head): a single pass from h_init straight to h_out
@@ -1229,7 +1315,7 @@ hipError_t run_prefix_mfma(const Shape &s, int64_t len, int chunk, const Seq &in
         if (full)
             return run_full();
         a.h_end = h_out;
-        return launch_scan_hpw<false, float>(a, hpw_state, rev, st);
+        return launch_state_pass(a, p.hpw_state, rev, st);
     }
     hipError_t e;
     float *tot = static_cast<float *>(ws);
@@ -1238,7 +1324,7 @@ hipError_t run_prefix_mfma(const Shape &s, int64_t len, int chunk, const Seq &in
     a.h_in = nullptr;
     a.h_end = segs;
     a.tot = tot;
-    if ((e = launch_scan_hpw<false, float>(a, hpw_state, rev, st)) != hipSuccess)
+    if ((e = launch_state_pass(a, p.hpw_state, rev, st)) != hipSuccess)
         return e;
     // 2. states entering each segment (in place); the final state when nothing else follows
     {

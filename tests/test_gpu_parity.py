@@ -65,8 +65,11 @@ def _check_commit(h, clean, A, D, label=""):
     hno, yo = oracle.commit(h, clean, A, D, want_y=True)
     assert within(rel(hn, hno), tol_for(clean.dtype), "commit state")
     assert within(rel(y, yo), tol_for(clean.dtype), "commit y")
+    # without y the commit runs the state-only walk (another summation order): the same
+    # state within the bound
     hn2, _ = gpu_commit(h, clean, A, D, want_y=False)
-    assert np.array_equal(hn, hn2), "commit state does not depend on whether y is written"
+    assert within(rel(hn2, hno), tol_for(clean.dtype), "commit state, no y")
+    assert within(rel(hn2, hn), tol_for(clean.dtype), "commit state with and without y")
     return hn
 
 
@@ -279,7 +282,7 @@ def test_commit_chain_equals_prefix_scan():
     for k in range(32):
         h, _ = gpu_commit(h, slice_seq(pre, 32 * k, 32 * (k + 1)), A, D)
         if (k + 1) % 8 == 0:
-            assert within(rel(h, cs[:, (k + 1) // 8 - 1]), 1e-5, "commit chain vs chunk state (same kernels)")
+            assert within(rel(h, cs[:, (k + 1) // 8 - 1]), 1e-5, "commit chain vs chunk state")
     assert within(rel(h, h_scan), 1e-5, "commit chain vs scan final state")
     _, _, ho = oracle.scan(pre, A, D, 256, want_y=False, want_chunk_states=False)
     assert within(rel(h, ho), TOL_BF16, "commit chain vs oracle")
