@@ -8,7 +8,7 @@
 // of the outputs, and keeps the NB+1 causal C B^T score tiles of its row block (forward for
 // s-blocks <= tb, reverse for s-blocks >= tb) in registers for all heads of the workgroup.
 // Per head, the state in operand form ([hi, lo][N/8][P][8] bf16, 32 KB) and x of both
-// directions (token-major, the 16-byte pieces of row t permuted by an XOR with 2 (t % 4)) are
+// directions (token-major, the 16-byte pieces of row t permuted by an XOR with swz_x(t)) are
 // copied straight into LDS with gfx950 buffer loads to LDS, in whole 1 KB pieces (no
 // registers on the way, no conversion). One buffer of each suffices because two workgroups
 // share a CU (about 71 KB of LDS and at most 128 registers each): while one waits for its
@@ -90,8 +90,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4, 
 
     // ---- copies into LDS. State: this wavefront's NS pieces of head h0 + hh, in place
     // (hh = hpw reads past the range: nothing moves). x: piece k = 8 rows of one direction;
-    // lane l takes row 8 (k % XPD) + l / 8, piece (l % 8) ^ 2 (row % 4) of it, so that the
-    // row's piece c sits at slot c ^ 2 (row % 4); skip = x_bytes puts a copy past the range.
+    // lane l takes row 8 (k % XPD) + l / 8, piece (l % 8) ^ swz_x(row) of it, so that the
+    // row's piece c sits at slot c ^ swz_x(row); skip = x_bytes puts a copy past the range.
     auto copy_state = [&](int hh) {
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4, 
 #pragma unroll
         for (int i = 0; i < NX; ++i) {
             const int k = w * NX + i, d = k / XPD, j = k % XPD;
-            const int tr = 8 * j + (lane >> 3), c = (lane & 7) ^ (2 * (tr & 3));
+            const int tr = 8 * j + (lane >> 3), c = (lane & 7) ^ swz_x(tr);
             copy_to_lds(d ? rXr : rXf, (d ? xs1 : xs0) + 8 * j * kP, (tr * rowX + h * kP + 8 * c) * 2 + skip_bytes);
         }
     };
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4, 
     // gets column pcol + r16 of tokens 32m + 4q + e (slots 0..3) and 32m + 16 + 4q + e (4..7)
     auto xfrag = [&](const __bf16 *X, int m, int pcol) {
         const int tr = 32 * m + 4 * q + (r16 >> 2), col = pcol + 4 * (r16 & 3);
-        const int off = 8 * ((col >> 3) ^ (2 * (tr & 3))) + (col & 7);
+        const int off = 8 * ((col >> 3) ^ swz_x(tr)) + (col & 7);
         return cat(tr_read(&X[tr * kP + off]), tr_read(&X[(tr + 16) * kP + off]));
     };
 
@@ -383,7 +383,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4, 
 #pragma unroll
             for (int pb = 0; pb < PBW; ++pb) {
                 const int p0 = (pgrp * PBW + pb) * 16 + 4 * q;
-                const int xo = t * kP + 8 * ((p0 >> 3) ^ (2 * (t & 3))) + (p0 & 7);
+                const int xo = t * kP + 8 * ((p0 >> 3) ^ swz_x(t)) + (p0 & 7);
                 const bf16x4 xf = *reinterpret_cast<const bf16x4 *>(&xs0[xo]);
                 const bf16x4 xr = *reinterpret_cast<const bf16x4 *>(&xs1[xo]);
                 float o[4];

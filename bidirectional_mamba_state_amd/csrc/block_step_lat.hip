@@ -143,7 +143,7 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
             copy_to_lds(r, &rows[i][4 * j * 128], ((row0_of(i) + rl) * rowBC + 8 * piece) * 2);
         } else {
             const int d = (k - 20) / 4, j = (k - 20) % 4;
-            const int tr = 8 * j + (lane >> 3), c = (lane & 7) ^ (2 * (tr & 3));
+            const int tr = 8 * j + (lane >> 3), c = (lane & 7) ^ swz_x(tr);
             copy_to_lds(d ? rXr : rXf, &xs[d][8 * j * kP], (tr * rowX + 8 * c) * 2);
         }
     };
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int tr = 16 * u + 4 * q + (r16 >> 2), col = 16 * pblk + 4 * (r16 & 3);
-            half[u] = tr_read(&xs[d][tr * kP + 8 * ((col >> 3) ^ (2 * (tr & 3))) + (col & 7)]);
+            half[u] = tr_read(&xs[d][tr * kP + 8 * ((col >> 3) ^ swz_x(tr)) + (col & 7)]);
         }
         xv[d] = cat(half[0], half[1]);
     }
@@ -394,7 +394,7 @@ __global__ __launch_bounds__(64 * WPG) void k_block_lat(BlockArgs a)
     // (bf16) or 16-byte (float32) store. Rows past T fall outside the output buffer's range
     // and are dropped.
     auto x4 = [&](int d) {  // x[t][p0 .. p0+3] of direction d, from the LDS tile
-        return *reinterpret_cast<const bf16x4 *>(&xs[d][t * kP + 8 * ((p0 >> 3) ^ (2 * (t & 3))) + (p0 & 7)]);
+        return *reinterpret_cast<const bf16x4 *>(&xs[d][t * kP + 8 * ((p0 >> 3) ^ swz_x(t)) + (p0 & 7)]);
     };
     float o[4];
     {

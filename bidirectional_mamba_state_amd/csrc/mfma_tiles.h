@@ -65,6 +65,15 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const float (&f)[8])
     return __builtin_bit_cast(bf16x8, w);
 }
 
+// Slot permutation of x tiles (token-major rows of 64 bf16 = 128 bytes, two rows per
+// 256-byte LDS bank period): the 16-byte piece c of row t sits at slot c ^ swz_x(t). gfx950's
+// LDS serves an 8-byte read 32 lanes at a time, and this keeps both of the kernels' 8-byte x
+// reads free of bank conflicts: transposing reads of 8 consecutive rows x 32 bytes
+// (distinct piece pairs among the even rows and among the odd ones) and reads of 16
+// consecutive rows x 16 bytes (distinct pieces among the 8 even rows and among the 8 odd
+// ones). Rows t and t + 16 share a permutation.
+__device__ __forceinline__ int swz_x(int t) { return 2 * ((t >> 1) & 3) + ((t >> 3) & 1); }
+
 // Transposing LDS read (gfx950 ds_read_b64_tr_b16): in each 16-lane group, lanes 4r .. 4r+3
 // address row r (four consecutive elements each) and lane j receives column j of the four
 // rows.

@@ -410,13 +410,11 @@ __device__ __forceinline__ int opaque_int(int v)
     return v;
 }
 
-// Piece permutations of the fold pass's tiles: a transposing read of 32 lanes covers 8
-// consecutive rows x 32 bytes, and each 16-byte piece c of row t sits at slot c ^ swz(t) so
-// that those 256 bytes fall in distinct banks: B rows (256 bytes, one bank period) need 8
-// distinct piece pairs; x rows (128 bytes, two rows per period) need distinct pairs among the
-// even rows and among the odd ones.
+// Piece permutation of the fold pass's B tiles: a transposing read of 32 lanes covers 8
+// consecutive rows x 32 bytes, and the 16-byte piece c of row t sits at slot c ^ swz_b(t) so
+// that those 256 bytes fall in distinct banks (B rows are 256 bytes, one bank period: 8
+// distinct piece pairs). x tiles use swz_x.
 __device__ __forceinline__ int swz_b(int t) { return 2 * (t & 7); }
-__device__ __forceinline__ int swz_x(int t) { return 2 * ((t >> 1) & 3); }
 
 template <int HPW, int HS, int NBUF, bool REV>
 __device__ __forceinline__ void fold_pass(const ScanArgs &a)
@@ -755,13 +753,15 @@ __global__ __launch_bounds__(512, 1) void k_fold4_rev(ScanArgs a) { fold_pass<4,
 // and its next copy is issued right after that barrier. 71.5 KB of LDS: two workgroups per
 // CU. B and C rows (256 bytes) hold piece c of row r at slot c ^ swz(r), which keeps three
 // read patterns free of bank conflicts: 16-byte operand reads of 16 consecutive rows (score
-// tiles), transposing reads of 4 rows x 16 columns per 16 lanes (B in the state update) and
-// 8-byte reads of the permuted contraction order (C in the state product); x rows
-// (128 bytes) hold piece c of row t at slot c ^ 2 (t % 4).
+// tiles), transposing reads of 8 rows x 16 columns per 32 lanes (B in the state update) and
+// 8-byte reads of the permuted contraction order (C in the state product); x rows hold
+// piece c of row t at slot c ^ swz_x(t) (conflict-free for the transposing reads and the
+// output's skip-term reads).
 __device__ __forceinline__ int swz(int r)
 {
     return ((r & 3) << 2) | ((r & 4) >> 1) | ((r >> 3) & 1);
 }
+
 
 // (the body is a device function template with one kernel per output type: a kernel
 // template built from generic lambdas loses its host-side launch stub in this compiler)
@@ -843,7 +843,7 @@ __device__ __forceinline__ void full_pass(const ScanArgs &a)
         const auto r = mk(xg + first_token<REV>(len, t0, nrows) * rowX, nrows > 0 ? ((nrows - 1) * rowX + kP) * 2 : 0);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int px = wave + 4 * u, row = 8 * px + (lane >> 3), c = (lane & 7) ^ (2 * (row & 3));
+            const int px = wave + 4 * u, row = 8 * px + (lane >> 3), c = (lane & 7) ^ swz_x(row);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(dst + 8 * px * kP),
                                                      16, (mem_row<REV>(row, nrows) * rowX + 8 * c) * 2, 0, 0, 0);
         }
@@ -894,7 +894,7 @@ __device__ __forceinline__ void full_pass(const ScanArgs &a)
     };
     // x~: lane (r16, q) gets x[32 m + 4 q + e][p0 + r16] and x[32 m + 16 + 4 q + e][..]
     auto x_frag = [&](const __bf16 *X, int m, int p0) {
-        const int tr = 32 * m + 4 * q + (r16 >> 2), col = p0 + 4 * (r16 & 3), sw = 2 * (tr & 3);
+        const int tr = 32 * m + 4 * q + (r16 >> 2), col = p0 + 4 * (r16 & 3), sw = swz_x(tr);
         const __bf16 *p = X + tr * kP + 8 * ((col >> 3) ^ sw) + (col & 7);
         return cat(tr_read(p), tr_read(p + 16 * kP));
     };
@@ -1050,7 +1050,7 @@ __device__ __forceinline__ void full_pass(const ScanArgs &a)
                 }
                 const int pc = p0 + 4 * q;
                 const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(
-                    bufX(PH) + t * kP + 8 * ((pc >> 3) ^ (2 * (t & 3))) + (pc & 7));
+                    bufX(PH) + t * kP + 8 * ((pc >> 3) ^ swz_x(t)) + (pc & 7));
                 float o[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
