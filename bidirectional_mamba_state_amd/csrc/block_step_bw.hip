@@ -39,7 +39,7 @@ enum { TAB_CF, TAB_CR, TAB_LGF, TAB_LGR, TAB_COLF, TAB_COLR, TAB_EF, NTAB };
 // HI_ONLY: the cached state is its bf16 hi part only (the bf16 cached state): half the state
 // copies, one state product instead of two. DCH: skip weights per head and channel.
 template <int NB, typename Ty, bool HI_ONLY, bool DCH>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_block_bw(BlockArgs a, int hpw, int n_hg)
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_block_bw(BlockArgs a, int hpw, int n_hg)
 {
     constexpr int kStateElems = HI_ONLY ? kOpsElems / 2 : kOpsElems;  // one head's state in HBM
     constexpr int TP = 16 * NB;         // padded block length
@@ -50,9 +50,36 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4, 
     constexpr int NX = 2 * XPD / kWaves;               // per wavefront
     constexpr int NS = kStateElems * 2 / 1024 / kWaves;  // state copies per wavefront (4, or 2)
 
-    __shared__ __attribute__((aligned(16))) __bf16 hop[kOpsElems];  // the head's state
-    __shared__ __attribute__((aligned(16))) __bf16 xs0[TP * kP];    // x, forward
-    __shared__ __attribute__((aligned(16))) __bf16 xs1[TP * kP];    // x, reverse
+    // two buffer sets, by head parity: the next head's state and x stream in while the
+    // current one is computed (set 1 first holds the staged B and C rows)
+    __shared__ __attribute__((aligned(16))) __bf16 hop0[kOpsElems];  // the head's state
+    __shared__ __attribute__((aligned(16))) __bf16 hop1[kOpsElems];
+    __shared__ __attribute__((aligned(16))) __bf16 xf0[TP * kP];     // x, forward
+    __shared__ __attribute__((aligned(16))) __bf16 xf1[TP * kP];
+    __shared__ __attribute__((aligned(16))) __bf16 xr0[TP * kP];     // x, reverse
+    __shared__ __attribute__((aligned(16))) __bf16 xr1[TP * kP];
+    // each set its own LDS array, chosen at compile time, so that the compiler can tell the
+    // copies into one set from the reads of the other
+    auto HOP = [&](auto P) -> __bf16 * {
+        if constexpr (decltype(P)::value == 0)
+            return hop0;
+        else
+            return hop1;
+    };
+    auto XF = [&](auto P) -> __bf16 * {
+        if constexpr (decltype(P)::value == 0)
+            return xf0;
+        else
+            return xf1;
+    };
+    auto XR = [&](auto P) -> __bf16 * {
+        if constexpr (decltype(P)::value == 0)
+            return xr0;
+        else
+            return xr1;
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
     __shared__ __attribute__((aligned(16))) float tab[2][NTAB][TP]; // decay tables, two heads
     __shared__ float skip[2][2];                                     // D, D_rev of those heads
     __shared__ __attribute__((aligned(16))) float skipc[DCH ? 2 : 1][2][DCH ? kP : 1];  // DCH: per channel
@@ -92,19 +119,19 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4, 
     // (hh = hpw reads past the range: nothing moves). x: piece k = 8 rows of one direction;
     // lane l takes row 8 (k % XPD) + l / 8, piece (l % 8) ^ swz_x(row) of it, so that the
     // row's piece c sits at slot c ^ swz_x(row); skip = x_bytes puts a copy past the range.
-    auto copy_state = [&](int hh) {
+    auto copy_state = [&](auto P, int hh) {
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
             const int k = w * NS + i;
-            copy_to_lds(rH, &hop[k * 512], (hh * kStateElems + k * 512 + 8 * lane) * 2);
+            copy_to_lds(rH, HOP(P) + k * 512, (hh * kStateElems + k * 512 + 8 * lane) * 2);
         }
     };
-    auto copy_x = [&](int h, int skip_bytes) {
+    auto copy_x = [&](auto P, int h, int skip_bytes) {
 #pragma unroll
         for (int i = 0; i < NX; ++i) {
             const int k = w * NX + i, d = k / XPD, j = k % XPD;
             const int tr = 8 * j + (lane >> 3), c = (lane & 7) ^ swz_x(tr);
-            copy_to_lds(d ? rXr : rXf, (d ? xs1 : xs0) + 8 * j * kP, (tr * rowX + h * kP + 8 * c) * 2 + skip_bytes);
+            copy_to_lds(d ? rXr : rXf, (d ? XR(P) : XF(P)) + 8 * j * kP, (tr * rowX + h * kP + 8 * c) * 2 + skip_bytes);
         }
     };
 
@@ -175,11 +202,15 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4, 
     // cleared once, before any copy (later contents are always finite inputs).
     if (T < TP) {
         const uint4 z = make_uint4(0, 0, 0, 0);
-        for (int i = threadIdx.x; i < kOpsElems / 8; i += 64 * kWaves)
-            *reinterpret_cast<uint4 *>(hop + 8 * i) = z;
+        for (int i = threadIdx.x; i < kOpsElems / 8; i += 64 * kWaves) {
+            *reinterpret_cast<uint4 *>(hop0 + 8 * i) = z;
+            *reinterpret_cast<uint4 *>(hop1 + 8 * i) = z;
+        }
         for (int i = threadIdx.x; i < TP * kP / 8; i += 64 * kWaves) {
-            *reinterpret_cast<uint4 *>(xs0 + 8 * i) = z;
-            *reinterpret_cast<uint4 *>(xs1 + 8 * i) = z;
+            *reinterpret_cast<uint4 *>(xf0 + 8 * i) = z;
+            *reinterpret_cast<uint4 *>(xr0 + 8 * i) = z;
+            *reinterpret_cast<uint4 *>(xf1 + 8 * i) = z;
+            *reinterpret_cast<uint4 *>(xr1 + 8 * i) = z;
         }
         workgroup_lds_barrier<63>();
     }
@@ -188,18 +219,19 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4, 
     // (a matrix-core operand read straight from a row-major tensor touches 16 rows for 64
     // bytes per load, which costs the load path several times what whole lines cost). Rows
     // of N = 128 bf16 in blocks of 16, piece c (8 elements) of row r at slot c ^ (r % 16);
-    // C rows go to the state buffer, B rows to the two x buffers (TP/2 rows each).
+    // C rows go to the state buffer of set 1, B rows to its two x buffers (TP/2 rows each),
+    // while the first head's state and x land in set 0.
     constexpr int RPW = TP / 4 / kWaves;  // 1 KB pieces (4 rows) of one tensor per wavefront
     auto copy_rows = [&](__amdgpu_buffer_rsrc_t r, __bf16 *lo_half, __bf16 *hi_half, int k) {
         const int row = 4 * k + (lane >> 4), c = (lane & 15) ^ (row & 15);
         __bf16 *dst = (4 * k < TP / 2 ? lo_half + 4 * k * kN : hi_half + (4 * k - TP / 2) * kN);
         copy_to_lds(r, dst, (row * rowBC + 8 * c) * 2);
     };
-    auto copy_bc = [&](int dir) {  // C -> hop, B -> xs0 | xs1
+    auto copy_bc = [&](int dir) {  // C -> hop1, B -> xf1 | xr1
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
-            copy_rows(dir ? rCr : rCf, hop, hop + (TP / 2) * kN, w * RPW + i);
-            copy_rows(dir ? rBr : rBf, xs0, xs1, w * RPW + i);
+            copy_rows(dir ? rCr : rCf, hop1, hop1 + (TP / 2) * kN, w * RPW + i);
+            copy_rows(dir ? rBr : rBf, xf1, xr1, w * RPW + i);
         }
     };
     // operand fragment of row 16 blk + r16 of the staged rows: n = 32 kk + 8 q .. +7
@@ -227,6 +259,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4, 
         Head hd{0, 0, 0.f, 0.f};
         if constexpr (table_wave)
             load_head(DIR, h0, hd);
+        copy_state(P0{}, 0);
+        copy_x(P0{}, h0, 0);
 
         // ---- score tiles of this row block, once per workgroup: S[ut] lane (r16, q) holds
         // S[t = 16 TB + r16][s = 16 sb + 4q + j]; forward tiles (s-blocks 0..TB) from the
@@ -237,13 +271,13 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4, 
         workgroup_lds_barrier<0>();
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
-            cfw[kk] = row_frag(hop, hop + (TP / 2) * kN, TB, kk);
+            cfw[kk] = row_frag(hop1, hop1 + (TP / 2) * kN, TB, kk);
 #pragma unroll
         for (int ut = 0; ut <= TB; ++ut) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
-                acc = mfma(row_frag(xs0, xs1, ut, kk), cfw[kk], acc);
+                acc = mfma(row_frag(xf1, xr1, ut, kk), cfw[kk], acc);
             S[ut] = acc;
         }
         if constexpr (table_wave)
@@ -255,29 +289,37 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4, 
             bf16x8 crv[4];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
-                crv[kk] = row_frag(hop, hop + (TP / 2) * kN, TB, kk);
+                crv[kk] = row_frag(hop1, hop1 + (TP / 2) * kN, TB, kk);
 #pragma unroll
             for (int ut = TB + 1; ut <= NB; ++ut) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk)
-                    acc = mfma(row_frag(xs0, xs1, ut - 1, kk), crv[kk], acc);
+                    acc = mfma(row_frag(xf1, xr1, ut - 1, kk), crv[kk], acc);
                 S[ut] = acc;
             }
         }
-        workgroup_lds_barrier<63>();  // everyone's reads of the reverse rows are done
-        copy_state(0);
-        copy_x(h0, 0);
 
-        // the loop body has no branch (after the last head the next head's copies move
-        // nothing and its tables are rebuilt for the last one), so that the compiler's waits
-        // count exactly the loads and copies in flight
-        for (int hh = 0; hh < hpw; ++hh) {
-            const int h = h0 + hh, cur = hh & 1;
+        // one head: its state, x and tables are in set P (copied during the head before); the
+        // next head's go to the other set while this one is computed. No branch on the copies'
+        // path (after the last head the next head's copies move nothing and its tables are
+        // rebuilt for the last one), so that the compiler's waits count exactly the loads and
+        // copies in flight.
+        auto head = [&](auto P, int hh) {
+            constexpr int cur = decltype(P)::value;
+            using PN = std::integral_constant<int, 1 - cur>;
+            const int h = h0 + hh;
             const bool more = hh + 1 < hpw;
             const int hn = more ? h + 1 : h;
-            workgroup_lds_barrier<0>();  // the head's state, x and tables are in
-
+            // the head's copies are in, and every read of the other set (the head before) is done
+            workgroup_lds_barrier<0>();
+            if constexpr (table_wave)
+                load_head(DIR, hn, hd);
+            copy_state(PN{}, hh + 1);
+            copy_x(PN{}, hn, more ? 0 : static_cast<int>(x_bytes));
+            const __bf16 *hop = HOP(P);
+            const __bf16 *xs0 = XF(P);
+            const __bf16 *xs1 = XR(P);
             // eq. (11), cached-state term: y^T = (h_hi + h_lo)^T C^T
             f32x4 acc[PBW];
 #pragma unroll
@@ -296,10 +338,6 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4, 
                     }
                 }
             }
-            workgroup_lds_barrier<63>();  // everyone's state reads are done
-            if constexpr (table_wave)
-                load_head(DIR, hn, hd);
-            copy_state(hh + 1);
             {
                 const float et = tab[cur][TAB_EF][t];  // exp(c_t)
 #pragma unroll
@@ -413,9 +451,14 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4, 
                         rY, off, 0, 0);
                 }
             }
-            workgroup_lds_barrier<63>();  // everyone's x reads are done
-            copy_x(hn, more ? 0 : static_cast<int>(x_bytes));
+        };
+        int hh = 0;
+        for (; hh + 2 <= hpw; hh += 2) {
+            head(P0{}, hh);
+            head(P1{}, hh + 1);
         }
+        if (hh < hpw)
+            head(P0{}, hh);
         // no copy into this workgroup's LDS may still be in flight when it ends
         __builtin_amdgcn_s_waitcnt(0);
     };
@@ -469,12 +512,12 @@ bool block_bw_supported(const Shape &s, int T)
 
 int block_bw_plan(const Shape &s)
 {
-    // heads per workgroup: the largest divisor of the heads per group that still leaves two
-    // workgroups per CU (512 on 256 CUs), so that the score tiles are shared by as many heads
-    // as possible without idling CUs
+    // heads per workgroup: the largest divisor of the heads per group that still leaves a
+    // workgroup for every CU (one per CU: 256), so that the score tiles are shared by as many
+    // heads as possible without idling CUs
     const int hpg = s.H / s.G;
     const int64_t pairs = static_cast<int64_t>(s.b) * s.H;
-    const int64_t want = 2 * static_cast<int64_t>(device_cus());
+    const int64_t want = static_cast<int64_t>(device_cus());
     int best = 1;
     for (int d = 1; d <= hpg; ++d) {
         if (hpg % d == 0 && pairs / d >= want)
