@@ -49,8 +49,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--only", choices=("headline", "c1", "c2prefix", "builds", "fullwindow"),
-                    help="run one workload only (for profiler runs)")
+    ap.add_argument("--only", choices=("headline", "c1", "c2prefix", "builds", "fullwindow", "step4", "build4",
+                                       "build3"),
+                    help="run one workload only (for profiler runs); step4: the running set's step "
+                         "(16 block steps + commit) on a seeded cached state, no prefix build; build4, "
+                         "build3: the running set's / the long-context cache's prefix build alone")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -222,6 +225,55 @@ def dev_seq(torch, gen, b, L, H, P, G, N, with_c=True, chunk_streams=4):
 
 
 # ---------------------------------------------------------------- headline: config 4
+def step4(torch, bdssm, configs, inputs, reps=3):
+    """The running set's step alone, for counter runs (each dispatch is then serialized and
+    counted, so the prefix build's input draws are left out): the cached state is seeded
+    random, put in operand form; 16 block steps (T = 128) and the commit of the oldest 32
+    tokens, reps times, each call on its own."""
+    cfg = configs.get(4)
+    b, H, P, N, G = cfg.batch, cfg.nheads, cfg.headdim, cfg.d_state, cfg.ngroups
+    T, S, TC = cfg.block_len, cfg.steps_per_block, cfg.commit_len
+    A, D = inputs.params(cfg)
+    Ad, Dd = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
+    d = bdssm.dims(b, H, P, N, G, cfg.in_dtype, bdssm.BF16)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(44)
+    h = torch.randn((b, H, N, P), device="cuda", generator=gen) * 0.05
+    ops = torch.empty(bdssm.state_ops_bytes(d), dtype=torch.uint8, device="cuda")
+    bdssm.state_ops(d, h, ops)
+    steps = [(dev_seq(torch, gen, b, T, H, P, G, N), dev_seq(torch, gen, b, T, H, P, G, N)) for _ in range(S)]
+    clean = dev_seq(torch, gen, b, TC, H, P, G, N, with_c=False)
+    y = torch.empty((b, T, H, P), dtype=torch.bfloat16, device="cuda")
+    fns = [(lambda f=f, r=r: bdssm.block_step_ops(d, T, ops, f, r, Ad, Dd, y)) for f, r in steps]
+    fns.append(lambda: bdssm.commit_refresh(d, TC, clean, Ad, Dd, h, ops, bdssm.STATE_OPS))
+    t = launch_times_us(torch, fns, reps=reps)
+    return {"workload": "running set step: 64 streams x 48 heads, 16 block steps (T=128) + commit of 32 tokens",
+            "block_step_us": round(median([x for v in t[:-1] for x in v]), 3),
+            "commit_refresh_us": round(median(t[-1]), 3)}
+
+
+def build_only(torch, bdssm, configs, inputs, index, reps=3):
+    """A state-only prefix build alone, reps times, for counter runs: the running set's
+    (config 4: 64 streams x 32,768 tokens) or the long-context cache's (config 3: 262,144
+    tokens x 80 heads)."""
+    cfg = configs.get(index)
+    b, H, P, N, G, L, Q = cfg.batch, cfg.nheads, cfg.headdim, cfg.d_state, cfg.ngroups, cfg.prefix_len, cfg.chunk
+    A, D = inputs.params(cfg)
+    Ad, Dd = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
+    d = bdssm.dims(b, H, P, N, G, cfg.in_dtype, bdssm.BF16)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(40 + index)
+    pre = dev_seq(torch, gen, b, L, H, P, G, N, with_c=False, chunk_streams=4 if b > 1 else 1)
+    h = torch.empty((b, H, N, P), device="cuda")
+    wsb = bdssm.prefix_scan_workspace(d, L, Q, False, False)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    fn = lambda: bdssm.prefix_scan(d, L, Q, pre, Ad, Dd, None, None, None, h, ws, wsb)
+    t = launch_times_us(torch, [fn], reps=reps)[0]
+    return {"workload": f"state-only prefix build, {b} stream(s) x {L:,} tokens, {H} heads x {P}, "
+                        f"{G} group(s), d_state {N}",
+            "avg_us": round(median(t), 1), "alg_bytes": prefix_state_bytes(b, H, P, N, G, L, 2)}
+
+
 def headline(args, torch, np, bdssm, configs, inputs):
     cfg = configs.get(4)
     b, H, P, N, G, L, Q = cfg.batch, cfg.nheads, cfg.headdim, cfg.d_state, cfg.ngroups, cfg.prefix_len, cfg.chunk
@@ -700,7 +752,10 @@ def main():
               "c1": lambda: config1(args, torch, np, bdssm, configs, inputs),
               "c2prefix": lambda: config2_prefix(torch, np, bdssm, configs, inputs),
               "builds": lambda: builds(torch, np, bdssm, configs, inputs),
-              "fullwindow": lambda: full_window_c1(torch, np, bdssm, configs, inputs)}.get(args.only)
+              "fullwindow": lambda: full_window_c1(torch, np, bdssm, configs, inputs),
+              "step4": lambda: step4(torch, bdssm, configs, inputs),
+              "build4": lambda: build_only(torch, bdssm, configs, inputs, 4),
+              "build3": lambda: build_only(torch, bdssm, configs, inputs, 3)}.get(args.only)
         print(json.dumps({args.only: fn()}), flush=True)
         return
     out = headline(args, torch, np, bdssm, configs, inputs)

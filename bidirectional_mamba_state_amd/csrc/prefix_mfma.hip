@@ -1259,7 +1259,9 @@ PrefixPlan prefix_mfma_plan(const Shape &s, int64_t len, int chunk, bool full, b
     const int64_t nsub = std::max<int64_t>(1, (len + SC - 1) / SC);
     const int64_t bh = std::max<int64_t>(1, static_cast<int64_t>(s.b) * s.H);
     int64_t want = 1;
-    int hpw = pick_fold_hpw(s, 1);
+    // a scan of one or two sub-chunks (a commit) is bound by its states' traffic: one head per
+    // workgroup puts the most workgroups, and so the most of that traffic, in flight
+    int hpw = nsub <= 2 ? 1 : pick_fold_hpw(s, 1);
     if (!single_segment) {
         if (full) {
             want = std::max<int64_t>(1, 2 * device_cus() / bh);
