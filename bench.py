@@ -392,7 +392,7 @@ def headline(args, torch, np, bdssm, configs, inputs):
     dom = max(shares, key=shares.get)
     work = {"block_step": nb_step, "commit_refresh": nb_commit}[dom]
     avg = {"block_step": blk_us, "commit_refresh": commit_us}[dom]
-    kname = {"block_step": "k_block_bw", "commit_refresh": "k_scan (state pass, two heads per workgroup)"}[dom]
+    kname = {"block_step": "k_block_bw", "commit_refresh": "k_fold1 (state-only walk writing the operand form)"}[dom]
     roof = make_roofline("hbm", work, avg, traffic_for({"block_step": "block_step_c4"}.get(dom, dom)))
     roof.update({"kernel": kname, "part": dom, "work_per_launch": work, "avg_launch_us": round(avg, 3),
                  "launches_per_step": S if dom == "block_step" else 1})
