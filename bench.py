@@ -241,8 +241,9 @@ def step4(torch, bdssm, configs, inputs, reps=3):
     h = torch.randn((b, H, N, P), device="cuda", generator=gen) * 0.05
     ops = torch.empty(bdssm.state_ops_bytes(d), dtype=torch.uint8, device="cuda")
     bdssm.state_ops(d, h, ops)
-    steps = [(dev_seq(torch, gen, b, T, H, P, G, N), dev_seq(torch, gen, b, T, H, P, G, N)) for _ in range(S)]
-    clean = dev_seq(torch, gen, b, TC, H, P, G, N, with_c=False)
+    steps = [(dev_seq(torch, gen, b, T, H, P, G, N, chunk_streams=b), dev_seq(torch, gen, b, T, H, P, G, N, chunk_streams=b))
+             for _ in range(S)]
+    clean = dev_seq(torch, gen, b, TC, H, P, G, N, with_c=False, chunk_streams=b)
     y = torch.empty((b, T, H, P), dtype=torch.bfloat16, device="cuda")
     fns = [(lambda f=f, r=r: bdssm.block_step_ops(d, T, ops, f, r, Ad, Dd, y)) for f, r in steps]
     fns.append(lambda: bdssm.commit_refresh(d, TC, clean, Ad, Dd, h, ops, bdssm.STATE_OPS))
@@ -393,7 +394,8 @@ def headline(args, torch, np, bdssm, configs, inputs):
     work = {"block_step": nb_step, "commit_refresh": nb_commit}[dom]
     avg = {"block_step": blk_us, "commit_refresh": commit_us}[dom]
     kname = {"block_step": "k_block_bw", "commit_refresh": "k_fold1 (state-only walk writing the operand form)"}[dom]
-    roof = make_roofline("hbm", work, avg, traffic_for({"block_step": "block_step_c4"}.get(dom, dom)))
+    roof = make_roofline("hbm", work, avg, traffic_for({"block_step": "block_step_c4",
+                                                        "commit_refresh": "commit_refresh_c4"}[dom]))
     roof.update({"kernel": kname, "part": dom, "work_per_launch": work, "avg_launch_us": round(avg, 3),
                  "launches_per_step": S if dom == "block_step" else 1})
     out = {"metric": METRIC, "value": round(active / (wall / args.steps), 1), "unit": "tokens/s", "n_gpus": 1,
