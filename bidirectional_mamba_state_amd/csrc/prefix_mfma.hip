@@ -352,11 +352,24 @@ __global__ __launch_bounds__(256) void k_seg_scan(float *buf, const float *tot, 
     if (e >= NP)
         return;
     float v = h_init ? h_init[(static_cast<int64_t>(b) * H + h) * NP + e] : 0.f;
-    for (int s = 0; s < nseg; ++s) {
-        const int64_t bh = (static_cast<int64_t>(b) * nseg + s) * H + h;
-        const float loc = buf[bh * NP + e];
-        buf[bh * NP + e] = v;
-        v = fmaf(__expf(tot[bh]), v, loc);
+    // U segments at a time: their loads are issued together, then the recurrence runs
+    constexpr int U = 16;
+    for (int s0 = 0; s0 < nseg; s0 += U) {
+        float loc[U], dec[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {  // (past the last segment: the last one, unused)
+            const int64_t bh = (static_cast<int64_t>(b) * nseg + min(s0 + u, nseg - 1)) * H + h;
+            loc[u] = buf[bh * NP + e];
+            dec[u] = __expf(tot[bh]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (s0 + u < nseg) {
+                const int64_t bh = (static_cast<int64_t>(b) * nseg + s0 + u) * H + h;
+                buf[bh * NP + e] = v;
+                v = fmaf(dec[u], v, loc[u]);
+            }
+        }
     }
     if (h_out)
         h_out[(static_cast<int64_t>(b) * H + h) * NP + e] = v;
@@ -762,15 +775,34 @@ __device__ __forceinline__ int swz(int r)
     return ((r & 3) << 2) | ((r & 4) >> 1) | ((r >> 3) & 1);
 }
 
+// B and C tiles of the full pass: rows of 256 bytes (pieces permuted by swz) in blocks of 16
+// rows, each block followed by 16 bytes of padding. The padding keeps a block's rows in the
+// same banks but puts reads of two blocks at a distance no paired read (ds_read2) can encode:
+// a pair of the 8-byte fragment reads below, merged into one instruction, conflicts, while
+// each alone does not.
+constexpr int BC_PAD = 8;  // elements
+constexpr int BC_TILE = SC * kN + (SC / 16) * BC_PAD;
+__device__ __forceinline__ int bc_row(int row) { return row * kN + (row >> 4) * BC_PAD; }
+
+// The 10 score tiles of a sub-chunk (a causal 4 x 4 grid of 16 x 16 blocks): tile tau is row
+// block tile_tb(tau), column block tile_sb(tau) <= tile_tb(tau) (tau = tb (tb + 1) / 2 + sb)
+__host__ __device__ constexpr int tile_tb(int tau) { return tau >= 6 ? 3 : tau >= 3 ? 2 : tau >= 1 ? 1 : 0; }
+__host__ __device__ constexpr int tile_sb(int tau) { return tau - tile_tb(tau) * (tile_tb(tau) + 1) / 2; }
+// whether one of tiles w, w + 4, .. (nt of them) lies in row block tb
+__host__ __device__ constexpr bool tile_row_of(int w, int nt, int tb)
+{
+    return tile_tb(w) == tb || (nt > 1 && tile_tb(w + 4) == tb) || (nt > 2 && tile_tb(w + 8) == tb);
+}
+
 
 // (the body is a device function template with one kernel per output type: a kernel
 // template built from generic lambdas loses its host-side launch stub in this compiler)
 template <typename Ty, bool REV>
 __device__ __forceinline__ void full_pass(const ScanArgs &a)
 {
-    __shared__ __attribute__((aligned(16))) __bf16 sB0[SC * kN];
-    __shared__ __attribute__((aligned(16))) __bf16 sB1[SC * kN];
-    __shared__ __attribute__((aligned(16))) __bf16 sC[SC * kN];
+    __shared__ __attribute__((aligned(16))) __bf16 sB0[BC_TILE];
+    __shared__ __attribute__((aligned(16))) __bf16 sB1[BC_TILE];
+    __shared__ __attribute__((aligned(16))) __bf16 sC[BC_TILE];
     __shared__ __attribute__((aligned(16))) __bf16 sX0[SC * kP];
     __shared__ __attribute__((aligned(16))) __bf16 sX1[SC * kP];
     __shared__ __attribute__((aligned(16))) float sT[2][NTAB][SC];  // decay tables by parity
@@ -833,7 +865,7 @@ __device__ __forceinline__ void full_pass(const ScanArgs &a)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int pc = wave + 4 * u, row = 4 * pc + (lane >> 4), c = (lane & 15) ^ swz(row);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(dst + 4 * pc * kN),
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(dst + bc_row(4 * pc)),
                                                      16, (mem_row<REV>(row, nrows) * rowBC + 8 * c) * 2, 0, 0, 0);
         }
     };
@@ -855,41 +887,44 @@ __device__ __forceinline__ void full_pass(const ScanArgs &a)
         const auto r = mk(dtg + first_token<REV>(len, t0, nrows) * H, nrows > 0 ? ((nrows - 1) * H + 1) * 2 : 0);
         return __builtin_amdgcn_raw_buffer_load_b16(r, mem_row<REV>(lane, nrows) * H * 2, 0, 0);
     };
-    // cumulative log2-decays of a sub-chunk from its dt, into table buffer PH
-    auto tables = [&](auto PH, unsigned short dbits) {
+    // cumulative log2-decays of a sub-chunk from its dt, into table buffer PH: every wavefront
+    // forms the sums and writes its share of the tables
+    auto tables = [&](auto Wc, auto PH, unsigned short dbits) {
+        constexpr int W = decltype(Wc)::value;
         const float d = __uint_as_float(static_cast<uint32_t>(dbits) << 16);
         const float inc = wave_prefix_sum(d * Ah);
         const float c = inc * kLog2e;
-        const float c31 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 31));
-        const float clast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 63));
-        const float ref = lane < 32 ? c31 : clast;  // end of this token's 32-token pair
         float(*tb)[SC] = sT[decltype(PH)::value];
-        tb[TAB_C][lane] = c;
-        tb[TAB_EF][lane] = __builtin_amdgcn_exp2f(c);
-        tb[TAB_LG][lane] = __builtin_amdgcn_logf(d) - c;
-        tb[TAB_COL][lane] = __builtin_amdgcn_exp2f(ref - c) * d;
-        tb[TAB_W][lane] = __builtin_amdgcn_exp2f(clast - c) * d;
-        sTot[decltype(PH)::value] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inc), 63));
+        if constexpr (W == 0) {
+            tb[TAB_C][lane] = c;
+            sTot[decltype(PH)::value] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inc), 63));
+        } else if constexpr (W == 1) {
+            tb[TAB_EF][lane] = __builtin_amdgcn_exp2f(c);
+        } else if constexpr (W == 2) {
+            tb[TAB_LG][lane] = __builtin_amdgcn_logf(d) - c;
+        } else {
+            const float c31 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 31));
+            const float clast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 63));
+            const float ref = lane < 32 ? c31 : clast;  // end of this token's 32-token pair
+            tb[TAB_COL][lane] = __builtin_amdgcn_exp2f(ref - c) * d;
+            tb[TAB_W][lane] = __builtin_amdgcn_exp2f(clast - c) * d;
+        }
     };
 
     // ---- operand reads
-    // B or C rows 16 blk + r16, contraction n = 32 m + 8 q .. +7 (score tiles)
-    auto row_frag = [&](const __bf16 *T, int blk, int m) {
-        const int row = 16 * blk + r16;
-        return *reinterpret_cast<const bf16x8 *>(T + row * kN + 8 * ((4 * m + q) ^ swz(row)));
-    };
-    // C rows 16 tb + r16, contraction n = 32 m + 4 q + e and 32 m + 16 + 4 q + e (state product)
-    auto c_frag = [&](int tb, int m) {
-        const int row = 16 * tb + r16, sw = swz(row);
-        const __bf16 *p = sC + row * kN + 4 * (q & 1);
+    // B or C rows 16 blk + r16, contraction n = 32 m + 4 q + e and 32 m + 16 + 4 q + e (e < 4):
+    // the order of the state product's h operand, taken by both operands of the score tiles too
+    auto k_frag = [&](const __bf16 *T, int blk, int m) {
+        const int row = 16 * blk + r16, sw = swz(row);
+        const __bf16 *p = T + bc_row(row) + 4 * (q & 1);
         return cat(*reinterpret_cast<const bf16x4 *>(p + 8 * ((4 * m + (q >> 1)) ^ sw)),
                    *reinterpret_cast<const bf16x4 *>(p + 8 * ((4 * m + 2 + (q >> 1)) ^ sw)));
     };
     // B^T: lane (r16, q) gets B[32 ks + 4 q + e][16 i + r16] and B[32 ks + 16 + 4 q + e][..]
     auto bt_frag = [&](const __bf16 *T, int ks, int i) {
         const int tr = 32 * ks + 4 * q + (r16 >> 2), col = 16 * i + 4 * (r16 & 3);
-        const __bf16 *p = T + tr * kN + 8 * ((col >> 3) ^ swz(tr)) + (col & 7);
-        const __bf16 *p16 = T + (tr + 16) * kN + 8 * ((col >> 3) ^ swz(tr + 16)) + (col & 7);
+        const __bf16 *p = T + bc_row(tr) + 8 * ((col >> 3) ^ swz(tr)) + (col & 7);
+        const __bf16 *p16 = T + bc_row(tr + 16) + 8 * ((col >> 3) ^ swz(tr + 16)) + (col & 7);
         return cat(tr_read(p), tr_read(p16));
     };
     // x~: lane (r16, q) gets x[32 m + 4 q + e][p0 + r16] and x[32 m + 16 + 4 q + e][..]
@@ -907,19 +942,28 @@ __device__ __forceinline__ void full_pass(const ScanArgs &a)
             for (int j = 0; j < 4; ++j)
                 base[(16 * i + 4 * q + j) * kP + p0 + r16] = hs[i][j];
     };
-    auto emit_chunk_state = [&](int k, int p0) {  // state after sub-chunk k, at chunk ends and the end
-        const int64_t gsub = seg_t0 / SC + k;
-        if ((gsub + 1) % a.chunk_sub == 0 || gsub == nsub_all - 1) {
-            const int64_t c = gsub / a.chunk_sub;
-            store_state(a.chunk_states + ((static_cast<int64_t>(b) * a.nch + c) * H + h0) * NP, p0);
+    // a chunk state is the state after a chunk's last sub-chunk, and after the stream's last;
+    // kend: the segment's next chunk end (segment-local sub-chunk), cnext: that chunk
+    const int64_t gsub0 = seg_t0 / SC;
+    const int kstream_end = gsub0 + nsub == nsub_all ? nsub - 1 : -1;
+    int kend = static_cast<int>(a.chunk_sub - 1 - gsub0 % a.chunk_sub);
+    int64_t cnext = gsub0 / a.chunk_sub;
+    auto emit_chunk_state = [&](int k, int p0) {  // after sub-chunk k, for k = 0, 1, .. in turn
+        if (k == kend || k == kstream_end)
+            store_state(a.chunk_states + ((static_cast<int64_t>(b) * a.nch + cnext) * H + h0) * NP, p0);
+        if (k == kend) {
+            kend += a.chunk_sub;
+            ++cnext;
         }
     };
 
-    // wavefront W owns state columns 16 W .. 16 W + 15 and score tiles W, W + 4, W + 8;
-    // wavefront 0 builds the decay tables. Everything below is specialized per wavefront.
+    // wavefront W owns state columns 16 W .. 16 W + 15 and score tiles W, W + 4, W + 8; it
+    // writes its share of the next sub-chunk's tables. Everything below is specialized per
+    // wavefront.
     auto body = [&](auto Wc) {
         constexpr int W = decltype(Wc)::value;
         constexpr int p0 = 16 * W;
+        unsigned short dnext = 0;  // dt of the sub-chunk after the current one
 
         // one sub-chunk k, in buffers PH = k % 2
         auto step = [&](auto PH, int k) {
@@ -932,7 +976,23 @@ __device__ __forceinline__ void full_pass(const ScanArgs &a)
             workgroup_lds_barrier<4>();
             if (a.chunk_states && k > 0)
                 emit_chunk_state(k - 1, p0);
-            bf16x8 xf[2];
+            // operand reads go out a group ahead of their products: the first score tile's
+            // (B and C blocks) before the copies and the tables, so that those cover their
+            // latency; the C blocks stay for the state product
+            constexpr int NT = W < 2 ? 3 : 2;  // score tiles W, W + 4, W + 8 (of 10)
+            bf16x8 cf[4][4], bf[2][4], xf[2];
+            auto read_c = [&](auto TBc) {
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    cf[decltype(TBc)::value][m] = k_frag(sC, decltype(TBc)::value, m);
+            };
+            auto read_b = [&](auto SLc, int sb) {
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    bf[decltype(SLc)::value][m] = k_frag(bufB(PH), sb, m);
+            };
+            read_c(std::integral_constant<int, tile_tb(W)>{});
+            read_b(std::integral_constant<int, 0>{}, tile_sb(W));
 #pragma unroll
             for (int m = 0; m < 2; ++m)
                 xf[m] = x_frag(bufX(PH), m, p0);
@@ -946,72 +1006,75 @@ __device__ __forceinline__ void full_pass(const ScanArgs &a)
             };
             // REV: the forward half's outputs of this wavefront's columns, loaded ahead of the
             // copies so that waiting for them never waits for a copy
-            f32x4 yprev[4];
+            using YRaw = std::conditional_t<sizeof(Ty) == 2, bf16x4, f32x4>;  // as stored
+            YRaw yprev[4];
             __amdgpu_buffer_rsrc_t yr;
             if constexpr (REV) {
                 yr = y_res();
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) {
-                    if constexpr (sizeof(Ty) == 2) {
-                        const bf16x4 v =
-                            __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(yr, y_off(tb), 0, 0));
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            yprev[tb][j] = bf2f(v[j]);
-                    } else {
+                    if constexpr (sizeof(Ty) == 2)
+                        yprev[tb] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(yr, y_off(tb), 0, 0));
+                    else
                         yprev[tb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(yr, y_off(tb), 0, 0));
-                    }
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
-            unsigned short dn = 0;
-            if constexpr (W == 0)
-                dn = load_dt(k + 1);
+            const unsigned short dn = load_dt(k + 2);
             copy_rows(Bg, bufB(PN{}), k + 1);
             copy_x(bufX(PN{}), k + 1);
             __builtin_amdgcn_sched_barrier(0);
+            tables(Wc, PN{}, dnext);  // sub-chunk k+1, into the table buffer k-1 has left
+            dnext = dn;
             if constexpr (!REV)
                 yr = y_res();
             const float(*tbl)[SC] = sT[ph];
             // (1) this wavefront's score tiles S[tb][sb] = B_s . C_t, decay-weighted (factored
-            // below the diagonal 32-token pair, per element on it), stored for all
+            // below the diagonal 32-token pair, per element on it), stored for all; the next
+            // tile's blocks (after the last, the C blocks no tile read) are read first
+            static_for<NT>([&](auto Ic) {
+                constexpr int i = decltype(Ic)::value, tau = W + 4 * i, tb = tile_tb(tau), sb = tile_sb(tau);
+                if constexpr (i + 1 < NT) {
+                    read_c(std::integral_constant<int, tile_tb(tau + 4)>{});
+                    read_b(std::integral_constant<int, (i + 1) & 1>{}, tile_sb(tau + 4));
+                } else if constexpr (!REV) {
+                    static_for<4>([&](auto Tc) {
+                        if constexpr (!tile_row_of(W, NT, decltype(Tc)::value))
+                            read_c(Tc);
+                    });
+                }
+                f32x4 S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int rr = 0; rr < 3; ++rr) {
-                const int tau = W + 4 * rr;
-                if (tau < 10) {
-                    const int tb = tau >= 6 ? 3 : tau >= 3 ? 2 : tau >= 1 ? 1 : 0;
-                    const int sb = tau - tb * (tb + 1) / 2;
-                    f32x4 S = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int m = 0; m < 4; ++m)
-                        S = mfma(row_frag(bufB(PH), sb, m), row_frag(sC, tb, m), S);
-                    // lane (t, q) holds S[s = 16 sb + 4q + j][t]
-                    const int t = 16 * tb + r16, mp = sb >> 1, s0 = 16 * sb + 4 * q;
-                    const float ct = tbl[TAB_C][t];
-                    float mv[4];
-                    if (mp < (tb >> 1)) {  // pair wholly below the row block
-                        const float rowf = __builtin_amdgcn_exp2f(ct - tbl[TAB_C][32 * mp + 31]);
-                        const float4 cw = *reinterpret_cast<const float4 *>(&tbl[TAB_COL][s0]);
-                        mv[0] = S[0] * cw.x * rowf;
-                        mv[1] = S[1] * cw.y * rowf;
-                        mv[2] = S[2] * cw.z * rowf;
-                        mv[3] = S[3] * cw.w * rowf;
-                    } else {  // the pair holding the row block: masked to s <= t
-                        const float4 lg = *reinterpret_cast<const float4 *>(&tbl[TAB_LG][s0]);
-                        const float l4[4] = {lg.x, lg.y, lg.z, lg.w};
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            mv[j] = s0 + j <= t ? S[j] * __builtin_amdgcn_exp2f(ct + l4[j]) : 0.f;
-                    }
-                    bf16x4 mb;
+                for (int m = 0; m < 4; ++m)
+                    S = mfma(bf[i & 1][m], cf[tb][m], S);
+                // lane (t, q) holds S[s = 16 sb + 4q + j][t]
+                const int t = 16 * tb + r16, s0 = 16 * sb + 4 * q;
+                constexpr int mp = sb >> 1;
+                const float ct = tbl[TAB_C][t];
+                float mv[4];
+                if constexpr (mp < (tb >> 1)) {  // pair wholly below the row block
+                    const float rowf = __builtin_amdgcn_exp2f(ct - tbl[TAB_C][32 * mp + 31]);
+                    const float4 cw = *reinterpret_cast<const float4 *>(&tbl[TAB_COL][s0]);
+                    mv[0] = S[0] * cw.x * rowf;
+                    mv[1] = S[1] * cw.y * rowf;
+                    mv[2] = S[2] * cw.z * rowf;
+                    mv[3] = S[3] * cw.w * rowf;
+                } else {  // the pair holding the row block: masked to s <= t
+                    const float4 lg = *reinterpret_cast<const float4 *>(&tbl[TAB_LG][s0]);
+                    const float l4[4] = {lg.x, lg.y, lg.z, lg.w};
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        mb[j] = static_cast<__bf16>(mv[j]);
-                    *reinterpret_cast<bf16x4 *>(&sM[tau][4 * lane]) = mb;
+                        mv[j] = s0 + j <= t ? S[j] * __builtin_amdgcn_exp2f(ct + l4[j]) : 0.f;
                 }
-            }
+                bf16x4 mb;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    mb[j] = static_cast<__bf16>(mv[j]);
+                *reinterpret_cast<bf16x4 *>(&sM[tau][4 * lane]) = mb;
+            });
             // (2) the state entering the sub-chunk: y^T[p][t] = sum_n h[n][p] C[t][n], the
-            // state accumulators split into bf16 hi + lo as the A operand
+            // state as the A operand: rounded to bf16 for a bf16 y (the rounding y takes
+            // anyway), split into bf16 hi + lo for an fp32 y
             f32x4 acc[4];
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb)
@@ -1021,12 +1084,21 @@ __device__ __forceinline__ void full_pass(const ScanArgs &a)
                 const float hv[8] = {hs[2 * m][0], hs[2 * m][1], hs[2 * m][2], hs[2 * m][3],
                                      hs[2 * m + 1][0], hs[2 * m + 1][1], hs[2 * m + 1][2], hs[2 * m + 1][3]};
                 bf16x8 hfh, hfl;
-                split8(hv, hfh, hfl);
+                if constexpr (sizeof(Ty) == 2) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        hfh[e] = static_cast<__bf16>(hv[e]);
+                } else {
+                    split8(hv, hfh, hfl);
+                }
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) {
-                    const bf16x8 cf = c_frag(tb, m);
-                    acc[tb] = mfma(hfh, cf, acc[tb]);
-                    acc[tb] = mfma(hfl, cf, acc[tb]);
+                    // (the reverse order, which also holds the forward outputs, reads C again
+                    // rather than keep it)
+                    const bf16x8 c = REV ? k_frag(sC, tb, m) : cf[tb][m];
+                    acc[tb] = mfma(hfh, c, acc[tb]);
+                    if constexpr (sizeof(Ty) != 2)
+                        acc[tb] = mfma(hfl, c, acc[tb]);
                 }
             }
             workgroup_lds_barrier<63>();  // (A2) the weighted tiles are stored; C is free
@@ -1034,31 +1106,55 @@ __device__ __forceinline__ void full_pass(const ScanArgs &a)
             // the copies stay ahead of the y stores: barrier (A) counts on exactly four
             // operations after them
             __builtin_amdgcn_sched_barrier(0);
+            // the operands of (3), and of the first half of (4), read ahead of the products
+            bf16x4 mt[10];  // the weighted tiles, in lane order
+#pragma unroll
+            for (int tau = 0; tau < 10; ++tau)
+                mt[tau] = *reinterpret_cast<const bf16x4 *>(&sM[tau][4 * lane]);
+            bf16x4 xv[4];
+            float ef[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                const int t = 16 * tb + r16, pc = p0 + 4 * q;
+                xv[tb] = *reinterpret_cast<const bf16x4 *>(bufX(PH) + t * kP + 8 * ((pc >> 3) ^ swz_x(t)) + (pc & 7));
+                ef[tb] = tbl[TAB_EF][t];
+            }
+            bf16x8 bt[2][8];
+            float wv[2][8];
+            auto read_bt = [&](auto KSc) {
+                constexpr int ks = decltype(KSc)::value;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    bt[ks][i] = bt_frag(bufB(PH), ks, i);
+                const float4 w0 = *reinterpret_cast<const float4 *>(&tbl[TAB_W][32 * ks + 4 * q]);
+                const float4 w1 = *reinterpret_cast<const float4 *>(&tbl[TAB_W][32 * ks + 16 + 4 * q]);
+                wv[ks][0] = w0.x, wv[ks][1] = w0.y, wv[ks][2] = w0.z, wv[ks][3] = w0.w;
+                wv[ks][4] = w1.x, wv[ks][5] = w1.y, wv[ks][6] = w1.z, wv[ks][7] = w1.w;
+            };
+            read_bt(std::integral_constant<int, 0>{});
             // (3) + sum_{s<=t} M[t][s] x_s per 32-token pair, + D x_t; the lane holds
             // y[t][p0 + 4q .. p0 + 4q + 3]
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
-                const int t = 16 * tb + r16, md = tb >> 1;
-                acc[tb] *= tbl[TAB_EF][t];
+                const int md = tb >> 1;
+                acc[tb] *= ef[tb];
 #pragma unroll
                 for (int m = 0; m <= md; ++m) {
                     const int lo = tb * (tb + 1) / 2 + 2 * m;  // tile (tb, 2m); (tb, 2m+1) follows
-                    const bf16x4 m0 = *reinterpret_cast<const bf16x4 *>(&sM[lo][4 * lane]);
-                    const bf16x4 m1 =
-                        2 * m + 1 <= tb ? *reinterpret_cast<const bf16x4 *>(&sM[lo + 1][4 * lane]) : bf16x4{};
-                    acc[tb] = mfma(xf[m], cat(m0, m1), acc[tb]);
+                    acc[tb] = mfma(xf[m], cat(mt[lo], 2 * m + 1 <= tb ? mt[lo + 1] : bf16x4{}), acc[tb]);
                 }
-                const int pc = p0 + 4 * q;
-                const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(
-                    bufX(PH) + t * kP + 8 * ((pc >> 3) ^ swz_x(t)) + (pc & 7));
                 float o[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    o[j] = fmaf(Dh, bf2f(xv[j]), acc[tb][j]);
+                    o[j] = fmaf(Dh, bf2f(xv[tb][j]), acc[tb][j]);
                 if constexpr (REV) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        o[j] += yprev[tb][j];
+                    for (int j = 0; j < 4; ++j) {
+                        if constexpr (sizeof(Ty) == 2)
+                            o[j] += bf2f(yprev[tb][j]);
+                        else
+                            o[j] += yprev[tb][j];
+                    }
                 }
                 const int off = y_off(tb);
                 if constexpr (sizeof(Ty) == 2) {
@@ -1073,38 +1169,30 @@ __device__ __forceinline__ void full_pass(const ScanArgs &a)
                         yr, off, 0, 0);
                 }
             }
+            read_bt(std::integral_constant<int, 1>{});
             // (4) state: h <- exp(c_63) h + B^T (w o x), w_s = exp(c_63 - c_s) dt_s
             {
-                const float tot = sTot[ph];
-                const float alpha = __expf(tot);
+                const float alpha = __expf(sTot[ph]);
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
                     hs[i] *= alpha;
             }
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                bf16x8 bt[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    bt[i] = bt_frag(bufB(PH), ks, i);
-                const float4 w0 = *reinterpret_cast<const float4 *>(&tbl[TAB_W][32 * ks + 4 * q]);
-                const float4 w1 = *reinterpret_cast<const float4 *>(&tbl[TAB_W][32 * ks + 16 + 4 * q]);
-                const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
                 float xw[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    xw[e] = bf2f(xf[ks][e]) * wv[e];
+                    xw[e] = bf2f(xf[ks][e]) * wv[ks][e];
                 bf16x8 xhi, xlo;
                 split8(xw, xhi, xlo);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    hs[i] = mfma(bt[i], xhi, hs[i]);
-                    hs[i] = mfma(bt[i], xlo, hs[i]);
+                    hs[i] = mfma(bt[ks][i], xhi, hs[i]);
+                    hs[i] = mfma(bt[ks][i], xlo, hs[i]);
                 }
             }
-            workgroup_lds_barrier<63>();  // (B) every LDS read for sub-chunk k is done
-            if constexpr (W == 0)
-                tables(PN{}, dn);  // sub-chunk k+1, into the table buffer k-1 has left
+            // no barrier here: the next step's barrier (A) comes before any buffer or table
+            // read in this step is written again
         };
 
         // ---- prologue: clear the staging buffers when the stream ends inside a sub-chunk
@@ -1112,7 +1200,7 @@ __device__ __forceinline__ void full_pass(const ScanArgs &a)
         // in flight, load the entering state, build the tables of 0, let everything land
         if (len % SC != 0) {
             const uint4 z = make_uint4(0, 0, 0, 0);
-            for (int i = tid; i < SC * kN / 8; i += 256) {
+            for (int i = tid; i < BC_TILE / 8; i += 256) {
                 *reinterpret_cast<uint4 *>(sB0 + 8 * i) = z;
                 *reinterpret_cast<uint4 *>(sB1 + 8 * i) = z;
                 *reinterpret_cast<uint4 *>(sC + 8 * i) = z;
@@ -1123,9 +1211,8 @@ __device__ __forceinline__ void full_pass(const ScanArgs &a)
             }
             workgroup_lds_barrier<63>();
         }
-        unsigned short d0 = 0;
-        if constexpr (W == 0)
-            d0 = load_dt(0);
+        const unsigned short d0 = load_dt(0);
+        dnext = load_dt(1);
         copy_rows(Bg, sB0, 0);
         copy_rows(Cg, sC, 0);
         copy_x(sX0, 0);
@@ -1140,8 +1227,7 @@ __device__ __forceinline__ void full_pass(const ScanArgs &a)
                 for (int j = 0; j < 4; ++j)
                     hs[i][j] = hin[(16 * i + 4 * q + j) * kP + p0 + r16];
         }
-        if constexpr (W == 0)
-            tables(std::integral_constant<int, 0>{}, d0);
+        tables(Wc, std::integral_constant<int, 0>{}, d0);
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         int k = 0;
         for (; k + 2 <= nsub; k += 2) {  // pairs of sub-chunks: a body with no branch

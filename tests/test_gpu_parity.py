@@ -22,7 +22,9 @@ def _case(msg):
 
 
 def _check_prefix(seq, A, D, chunk, h_init=None, want_y=True, want_cs=True, heads=None,
-                  y_dtype=bdssm.F32, in_place=False, label=""):
+                  y_dtype=bdssm.F32, in_place=False, label="", also_bf16_y=False):
+    """also_bf16_y: the same scan again with a bf16 y (and chunk states), against the same
+    oracle results."""
     _case(f"prefix {label} len={seq.length} chunk={chunk} y={want_y} cs={want_cs} "
           f"y_dtype={y_dtype} in_place={in_place}")
     tol = tol_for(seq.dtype) if y_dtype == bdssm.F32 else max(tol_for(seq.dtype), 5e-3)
@@ -42,6 +44,16 @@ def _check_prefix(seq, A, D, chunk, h_init=None, want_y=True, want_cs=True, head
         yz, _, _ = gpu_prefix(seq, A, Dz, chunk, h_init, True, False, y_dtype)
         yzo, _, _ = oracle.scan(seq, A, Dz, chunk, h_init=h_init, want_chunk_states=False, heads=heads)
         assert within(rel(yz[:, :, hs], yzo[:, :, hs]), tol, "y - D x")
+        if also_bf16_y:
+            tb = max(tol_for(seq.dtype), 5e-3)
+            yb, csb, hb = gpu_prefix(seq, A, D, chunk, h_init, True, want_cs, bdssm.BF16)
+            assert within(rel(yb[:, :, hs], yo[:, :, hs]), tb, "bf16 y")
+            assert within(max_head_rel(yb[:, :, hs], yo[:, :, hs], 2), 4 * tb, "bf16 y, worst head")
+            assert within(rel(hb[:, hs], ho[:, hs]), tol_for(seq.dtype), "final state, bf16 y")
+            if want_cs:
+                assert within(rel(csb[:, :, hs], cso[:, :, hs]), tol_for(seq.dtype), "chunk states, bf16 y")
+            yzb, _, _ = gpu_prefix(seq, A, Dz, chunk, h_init, True, False, bdssm.BF16)
+            assert within(rel(yzb[:, :, hs], yzo[:, :, hs]), tb, "bf16 y - D x")
     return h
 
 
@@ -121,7 +133,7 @@ def test_config2_prefix_chunk_states_all_heads():
     cfg = configs.get(2)
     A, D = inputs.params(cfg)
     pre = inputs.prefix(cfg)
-    h = _check_prefix(pre, A, D, cfg.chunk, label="c2 (all 32 heads)")
+    h = _check_prefix(pre, A, D, cfg.chunk, label="c2 (all 32 heads)", also_bf16_y=True)
     _check_commit(f32_round(h), inputs.block(cfg, 0, 0, inputs.CLEAN), A, D, label="c2")
 
 
