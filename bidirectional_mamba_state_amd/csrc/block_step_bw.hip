@@ -320,23 +320,33 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
             const __bf16 *hop = HOP(P);
             const __bf16 *xs0 = XF(P);
             const __bf16 *xs1 = XR(P);
-            // eq. (11), cached-state term: y^T = (h_hi + h_lo)^T C^T
+            // eq. (11), cached-state term: y^T = (h_hi + h_lo)^T C^T; the state fragments of
+            // contraction block kk + 1 are read while those of kk are multiplied
+            constexpr int NH = HI_ONLY ? 1 : 2;  // hi (, lo)
             f32x4 acc[PBW];
 #pragma unroll
             for (int pb = 0; pb < PBW; ++pb)
                 acc[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
+            bf16x8 hf[2][PBW][NH];
+            auto read_h = [&](int kk, bf16x8 (&dst)[PBW][NH]) {
 #pragma unroll
                 for (int pb = 0; pb < PBW; ++pb) {
                     const int pc = (pgrp * PBW + pb) * 16 + r16;
-                    const bf16x8 hi = *reinterpret_cast<const bf16x8 *>(&hop[((4 * kk + q) * kP + pc) * 8]);
-                    acc[pb] = mfma(hi, cfw[kk], acc[pb]);
-                    if constexpr (!HI_ONLY) {
-                        const bf16x8 lo = *reinterpret_cast<const bf16x8 *>(&hop[((16 + 4 * kk + q) * kP + pc) * 8]);
-                        acc[pb] = mfma(lo, cfw[kk], acc[pb]);
-                    }
+#pragma unroll
+                    for (int e = 0; e < NH; ++e)
+                        dst[pb][e] = *reinterpret_cast<const bf16x8 *>(&hop[((16 * e + 4 * kk + q) * kP + pc) * 8]);
                 }
+            };
+            read_h(0, hf[0]);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                if (kk + 1 < 4)
+                    read_h(kk + 1, hf[(kk + 1) & 1]);
+#pragma unroll
+                for (int pb = 0; pb < PBW; ++pb)
+#pragma unroll
+                    for (int e = 0; e < NH; ++e)
+                        acc[pb] = mfma(hf[kk & 1][pb][e], cfw[kk], acc[pb]);
             }
             {
                 const float et = tab[cur][TAB_EF][t];  // exp(c_t)
@@ -344,10 +354,27 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
                 for (int pb = 0; pb < PBW; ++pb)
                     acc[pb] *= et;
             }
-            auto mx = [&](const bf16x8 &af, const __bf16 *X, int m) {
+            // x fragments of the M X rounds: forward pairs m = 0 .. MD, then reverse pairs
+            // m = MD .. NB/2 - 1; round r + 1's are read while round r is weighted and multiplied
+            constexpr int NRF = MD + 1, NR = NRF + NB / 2 - MD;
+            bf16x8 xq[2][PBW];
+            auto read_x = [&](int r, bf16x8 (&dst)[PBW]) {
+                const __bf16 *X = r < NRF ? xs0 : xs1;
+                const int m = r < NRF ? r : MD + (r - NRF);
 #pragma unroll
                 for (int pb = 0; pb < PBW; ++pb)
-                    acc[pb] = mfma(xfrag(X, m, (pgrp * PBW + pb) * 16), af, acc[pb]);
+                    dst[pb] = xfrag(X, m, (pgrp * PBW + pb) * 16);
+            };
+            read_x(0, xq[0]);
+            int rnd = 0;
+            auto mx = [&](const bf16x8 &af, const __bf16 *, int) {
+                const int cur_r = rnd;
+                if (cur_r + 1 < NR)
+                    read_x(cur_r + 1, xq[(cur_r + 1) & 1]);
+#pragma unroll
+                for (int pb = 0; pb < PBW; ++pb)
+                    acc[pb] = mfma(xq[cur_r & 1][pb], af, acc[pb]);
+                ++rnd;
             };
             const float *cf = tab[cur][TAB_CF], *cr = tab[cur][TAB_CR], *lgf = tab[cur][TAB_LGF],
                         *lgr = tab[cur][TAB_LGR], *colf = tab[cur][TAB_COLF], *colr = tab[cur][TAB_COLR];
