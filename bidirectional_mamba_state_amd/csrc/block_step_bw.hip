@@ -10,15 +10,16 @@
 // Per head, the state in operand form ([hi, lo][N/8][P][8] bf16, 32 KB) and x of both
 // directions (token-major, the 16-byte pieces of row t permuted by an XOR with swz_x(t)) are
 // copied straight into LDS with gfx950 buffer loads to LDS, in whole 1 KB pieces (no
-// registers on the way, no conversion). One buffer of each suffices because two workgroups
-// share a CU (about 71 KB of LDS and at most 128 registers each): while one waits for its
-// copies, the other computes. Per head:
-//   barrier (the head's copies and tables are in) -> y^T = h^T C^T from the state ->
-//   barrier (the state buffer is free) -> the next head's dt loads and state copies ->
-//   y^T += X^T M^T of both directions (x by transposing reads), the next head's decay tables,
-//   D x, y stores -> barrier (the x buffers are free) -> the next head's x copies.
-// Each wavefront's code is specialized on its row block, so the causal structure is resolved
-// at compile time and the compiler's waits count exactly the copies in flight.
+// registers on the way, no conversion), into one of two buffer sets by head parity: the next
+// head's copies stream into the other set while the current head is computed (one workgroup
+// per CU, two wavefronts per SIMD). Per head:
+//   barrier (the head's copies and tables are in; the other set is free) -> the next head's
+//   dt loads and copies -> y^T = h^T C^T from the state -> y^T += X^T M^T of both directions
+//   (x by transposing reads) -> the next head's decay tables -> D x, y stores.
+// Operand reads run one group ahead of their products (the state fragments of the next
+// contraction block, the x fragments of the next M X round). Each wavefront's code is
+// specialized on its row block, so the causal structure is resolved at compile time and the
+// compiler's waits count exactly the copies in flight.
 #include <type_traits>
 
 #include "internal.h"
@@ -35,7 +36,7 @@ constexpr int kOpsElems = 2 * kN * kP;  // one head's state in operand form, bf1
 
 enum { TAB_CF, TAB_CR, TAB_LGF, TAB_LGR, TAB_COLF, TAB_COLR, TAB_EF, NTAB };
 
-// two workgroups per CU: four wavefronts per SIMD, 128 registers each
+// one workgroup per CU: two wavefronts per SIMD
 // HI_ONLY: the cached state is its bf16 hi part only (the bf16 cached state): half the state
 // copies, one state product instead of two. DCH: skip weights per head and channel.
 template <int NB, typename Ty, bool HI_ONLY, bool DCH>
