@@ -325,14 +325,26 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
 #pragma unroll
         for (int pb = 0; pb < PBW; ++pb)
             acc[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // eq. (11), cached-state term: C_t . h, h = hi + lo
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        // eq. (11), cached-state term: C_t . h, h = hi + lo; the state fragments of
+        // contraction block kk + 1 are read while those of kk are multiplied
+        bf16x8 hf[2][PBW][2];
+        auto read_h = [&](int kk, bf16x8 (&dst)[PBW][2]) {
 #pragma unroll
             for (int pb = 0; pb < PBW; ++pb) {
                 const int pc = (pgrp * PBW + pb) * 16 + r16;
-                acc[pb] = mfma(ld16(&hhi[pc * HS + 32 * kk + 8 * q]), cfw[kk], acc[pb]);
-                acc[pb] = mfma(ld16(&hlo[pc * HS + 32 * kk + 8 * q]), cfw[kk], acc[pb]);
+                dst[pb][0] = ld16(&hhi[pc * HS + 32 * kk + 8 * q]);
+                dst[pb][1] = ld16(&hlo[pc * HS + 32 * kk + 8 * q]);
+            }
+        };
+        read_h(0, hf[0]);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            if (kk + 1 < 4)
+                read_h(kk + 1, hf[(kk + 1) & 1]);
+#pragma unroll
+            for (int pb = 0; pb < PBW; ++pb) {
+                acc[pb] = mfma(hf[kk & 1][pb][0], cfw[kk], acc[pb]);
+                acc[pb] = mfma(hf[kk & 1][pb][1], cfw[kk], acc[pb]);
             }
         }
         // the rest of the next head's loads (its state was issued after the last barrier):
@@ -346,16 +358,25 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
             for (int pb = 0; pb < PBW; ++pb)
                 acc[pb] *= et;
         }
-        auto mx = [&](const bf16x8 &af, const __bf16 *XT, int m) {
+        // x fragments of the M X rounds, read one round ahead (forward pairs m = 0 ..
+        // NB/2 - 1, then reverse pairs; a round the row block skips is read all the same)
+        bf16x8 xq[2][PBW];
+        auto read_x = [&](const __bf16 *XT, int m, bf16x8 (&dst)[PBW]) {
 #pragma unroll
             for (int pb = 0; pb < PBW; ++pb) {
                 const int pc = (pgrp * PBW + pb) * 16 + r16;
                 const __bf16 *xp = &XT[pc * XS + 32 * m + 4 * q];
                 const bf16x4 lo4 = *reinterpret_cast<const bf16x4 *>(xp);
                 const bf16x4 hi4 = *reinterpret_cast<const bf16x4 *>(xp + 16);
-                acc[pb] = mfma(__builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7), af, acc[pb]);
+                dst[pb] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
             }
         };
+        auto mx = [&](const bf16x8 &af, const bf16x8 (&xf)[PBW]) {
+#pragma unroll
+            for (int pb = 0; pb < PBW; ++pb)
+                acc[pb] = mfma(xf[pb], af, acc[pb]);
+        };
+        read_x(xtf, 0, xq[0]);
         // eq. (11), inside the block (s <= t). Pairs wholly below the row block use the
         // factored decay exp2(c_t - c_ref) * [exp2(c_ref - c_s) dt_s], c_ref = c at the
         // pair's last token: both factors are <= 1. The pair holding the row block uses
@@ -363,6 +384,10 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
         const float ctf = cf[t];
 #pragma unroll
         for (int m = 0; m < NB / 2; ++m) {
+            if (m + 1 < NB / 2)
+                read_x(xtf, m + 1, xq[(m + 1) & 1]);
+            else
+                read_x(xtr, 0, xq[(m + 1) & 1]);
             if (m < md) {
                 const float rowf = __builtin_amdgcn_exp2f(ctf - cf[32 * m + 31]);
                 const float4 c0 = *reinterpret_cast<const float4 *>(&colf[32 * m + 4 * q]);
@@ -372,7 +397,7 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
                     mv[j] = (j < 4 ? S[2 * m][j] : S[2 * m + 1][j & 3]) * cw[j] * rowf;
-                mx(to_bf16x8(mv), xtf, m);
+                mx(to_bf16x8(mv), xq[m & 1]);
             } else if (m == md) {
                 const float4 l0 = *reinterpret_cast<const float4 *>(&lgf[32 * m + 4 * q]);
                 const float4 l1 = *reinterpret_cast<const float4 *>(&lgf[32 * m + 16 + 4 * q]);
@@ -386,7 +411,7 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
                     const float w = __builtin_amdgcn_exp2f(ctf + lg[j]);
                     mv[j] = s <= t ? sv * w : 0.f;
                 }
-                mx(to_bf16x8(mv), xtf, m);
+                mx(to_bf16x8(mv), xq[m & 1]);
             }
         }
         // eq. (12), reverse inside the block (s >= t); pairs wholly above the row block use
@@ -394,6 +419,9 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
         const float ctr = cr[t];
 #pragma unroll
         for (int m = 0; m < NB / 2; ++m) {
+            constexpr int R0 = NB / 2;  // round index of reverse pair 0
+            if (m + 1 < NB / 2)
+                read_x(xtr, m + 1, xq[(R0 + m + 1) & 1]);
             if (m > md) {
                 const float rowr = __builtin_amdgcn_exp2f(ctr - cr[32 * m]);
                 const float4 c0 = *reinterpret_cast<const float4 *>(&colr[32 * m + 4 * q]);
@@ -403,7 +431,7 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
                     mv[j] = (j < 4 ? S[2 * m + 1][j] : S[2 * m + 2][j & 3]) * cw[j] * rowr;
-                mx(to_bf16x8(mv), xtr, m);
+                mx(to_bf16x8(mv), xq[(R0 + m) & 1]);
             } else if (m == md) {
                 const float4 l0 = *reinterpret_cast<const float4 *>(&lgr[32 * m + 4 * q]);
                 const float4 l1 = *reinterpret_cast<const float4 *>(&lgr[32 * m + 16 + 4 * q]);
@@ -417,7 +445,7 @@ __global__ __launch_bounds__((Geo<NB, PS>::THREADS), 2) void k_block_mfma(BlockA
                     const float w = __builtin_amdgcn_exp2f(ctr + lg[j]);
                     mv[j] = s >= t ? sv * w : 0.f;
                 }
-                mx(to_bf16x8(mv), xtr, m);
+                mx(to_bf16x8(mv), xq[(R0 + m) & 1]);
             }
         }
         // eq. (13) + D x, written once: the lane holds y[t][pcb + 4q .. pcb + 4q + 3] of each

@@ -232,11 +232,18 @@ __global__ __launch_bounds__(256, 2) void k_scan(ScanArgs a)
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh)
         seg_tot[hh] = 0.f;
-    auto emit_chunk_state = [&](int k) {  // state after sub-chunk k, at chunk ends and the end
-        const int64_t gsub = seg_t0 / SC + k;  // sub-chunk index within the stream
-        if ((gsub + 1) % a.chunk_sub == 0 || gsub == nsub_all - 1) {
-            const int64_t c = gsub / a.chunk_sub;
-            store_state(a.chunk_states + ((static_cast<int64_t>(b) * a.nch + c) * H + h0) * NP);
+    // a chunk state is the state after a chunk's last sub-chunk, and after the stream's last;
+    // kend: the segment's next chunk end (segment-local sub-chunk), cnext: that chunk
+    const int64_t gsub0 = seg_t0 / SC;
+    const int kstream_end = gsub0 + nsub == nsub_all ? nsub - 1 : -1;
+    int kend = static_cast<int>(a.chunk_sub - 1 - gsub0 % a.chunk_sub);
+    int64_t cnext = gsub0 / a.chunk_sub;
+    auto emit_chunk_state = [&](int k) {  // after sub-chunk k, for k = 0, 1, .. in turn
+        if (k == kend || k == kstream_end)
+            store_state(a.chunk_states + ((static_cast<int64_t>(b) * a.nch + cnext) * H + h0) * NP);
+        if (k == kend) {
+            kend += a.chunk_sub;
+            ++cnext;
         }
     };
     load_stage(0);
