@@ -983,9 +983,9 @@ __device__ __forceinline__ void full_pass(const ScanArgs &a)
             workgroup_lds_barrier<4>();
             if (a.chunk_states && k > 0)
                 emit_chunk_state(k - 1, p0);
-            // operand reads go out a group ahead of their products: the first score tile's
-            // (B and C blocks) before the copies and the tables, so that those cover their
-            // latency; the C blocks stay for the state product
+            // operand reads go out a group ahead of their products: the first two score
+            // tiles' (B and C blocks) before the copies and the tables, so that those cover
+            // their latency; the C blocks stay for the state product
             constexpr int NT = W < 2 ? 3 : 2;  // score tiles W, W + 4, W + 8 (of 10)
             bf16x8 cf[4][4], bf[2][4], xf[2];
             auto read_c = [&](auto TBc) {
@@ -1000,6 +1000,10 @@ __device__ __forceinline__ void full_pass(const ScanArgs &a)
             };
             read_c(std::integral_constant<int, tile_tb(W)>{});
             read_b(std::integral_constant<int, 0>{}, tile_sb(W));
+            if constexpr (!REV) {  // (the reverse order, which holds more, takes it later)
+                read_c(std::integral_constant<int, tile_tb(W + 4)>{});
+                read_b(std::integral_constant<int, 1>{}, tile_sb(W + 4));
+            }
 #pragma unroll
             for (int m = 0; m < 2; ++m)
                 xf[m] = x_frag(bufX(PH), m, p0);
@@ -1039,21 +1043,10 @@ __device__ __forceinline__ void full_pass(const ScanArgs &a)
             // (1) this wavefront's score tiles S[tb][sb] = B_s . C_t, decay-weighted (factored
             // below the diagonal 32-token pair, per element on it), stored for all; the next
             // tile's blocks (after the last, the C blocks no tile read) are read first
-            static_for<NT>([&](auto Ic) {
+            // decay weights of tile i (factored below the diagonal 32-token pair, per element
+            // on it) and its store for all
+            auto weigh = [&](auto Ic, const f32x4 &S) {
                 constexpr int i = decltype(Ic)::value, tau = W + 4 * i, tb = tile_tb(tau), sb = tile_sb(tau);
-                if constexpr (i + 1 < NT) {
-                    read_c(std::integral_constant<int, tile_tb(tau + 4)>{});
-                    read_b(std::integral_constant<int, (i + 1) & 1>{}, tile_sb(tau + 4));
-                } else if constexpr (!REV) {
-                    static_for<4>([&](auto Tc) {
-                        if constexpr (!tile_row_of(W, NT, decltype(Tc)::value))
-                            read_c(Tc);
-                    });
-                }
-                f32x4 S = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int m = 0; m < 4; ++m)
-                    S = mfma(bf[i & 1][m], cf[tb][m], S);
                 // lane (t, q) holds S[s = 16 sb + 4q + j][t]
                 const int t = 16 * tb + r16, s0 = 16 * sb + 4 * q;
                 constexpr int mp = sb >> 1;
@@ -1078,7 +1071,54 @@ __device__ __forceinline__ void full_pass(const ScanArgs &a)
                 for (int j = 0; j < 4; ++j)
                     mb[j] = static_cast<__bf16>(mv[j]);
                 *reinterpret_cast<bf16x4 *>(&sM[tau][4 * lane]) = mb;
-            });
+            };
+            auto read_rest_c = [&]() {  // the C blocks no tile read, for the state product
+                if constexpr (!REV)
+                    static_for<4>([&](auto Tc) {
+                        if constexpr (!tile_row_of(W, NT, decltype(Tc)::value))
+                            read_c(Tc);
+                    });
+            };
+            // (1) this wavefront's score tiles S[tb][sb] = B_s . C_t: tiles 0 and 1 with their
+            // products interleaved (their blocks were read before the copies; the reverse
+            // order: tile 1's read after tile 0's products), then tile 2
+            {
+                constexpr int tb0 = tile_tb(W), tb1 = tile_tb(W + 4);
+                f32x4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (REV) {
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+                        S0 = mfma(bf[0][m], cf[tb0][m], S0);
+                    read_c(std::integral_constant<int, tb1>{});
+                    read_b(std::integral_constant<int, 1>{}, tile_sb(W + 4));
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+                        S1 = mfma(bf[1][m], cf[tb1][m], S1);
+                } else {
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        S0 = mfma(bf[0][m], cf[tb0][m], S0);
+                        S1 = mfma(bf[1][m], cf[tb1][m], S1);
+                    }
+                }
+                if constexpr (NT > 2) {
+                    read_c(std::integral_constant<int, tile_tb(W + 8)>{});
+                    read_b(std::integral_constant<int, 0>{}, tile_sb(W + 8));
+                } else {
+                    read_rest_c();
+                }
+                weigh(std::integral_constant<int, 0>{}, S0);
+                weigh(std::integral_constant<int, 1>{}, S1);
+            }
+            if constexpr (NT > 2) {
+                constexpr int tb2 = tile_tb(W + 8);
+                f32x4 S2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    S2 = mfma(bf[0][m], cf[tb2][m], S2);
+                read_rest_c();
+                weigh(std::integral_constant<int, 2>{}, S2);
+            }
             // (2) the state entering the sub-chunk: y^T[p][t] = sum_n h[n][p] C[t][n], the
             // state as the A operand: rounded to bf16 for a bf16 y (the rounding y takes
             // anyway), split into bf16 hi + lo for an fp32 y
