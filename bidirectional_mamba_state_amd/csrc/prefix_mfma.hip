@@ -348,38 +348,44 @@ __device__ __forceinline__ int mem_row(int row, int nrows)
         return row;
 }
 
-// Segment scan, one thread per state element: the end states of segments started from
-// zero become the states entering each segment (in place), and the final state.
+// Segment scan, one thread per four consecutive state elements (16-byte accesses): the end
+// states of segments started from zero become the states entering each segment (in place),
+// and the final state.
 __global__ __launch_bounds__(256) void k_seg_scan(float *buf, const float *tot, int nseg, int H,
                                                   const float *h_init, float *h_out)
 {
     const int64_t NP = static_cast<int64_t>(kN) * kP;
-    const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t e = 4 * (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x);
     const int h = blockIdx.y, b = blockIdx.z;
     if (e >= NP)
         return;
-    float v = h_init ? h_init[(static_cast<int64_t>(b) * H + h) * NP + e] : 0.f;
+    float4 v = h_init ? *reinterpret_cast<const float4 *>(h_init + (static_cast<int64_t>(b) * H + h) * NP + e)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
     // U segments at a time: their loads are issued together, then the recurrence runs
     constexpr int U = 16;
     for (int s0 = 0; s0 < nseg; s0 += U) {
-        float loc[U], dec[U];
+        float4 loc[U];
+        float dec[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {  // (past the last segment: the last one, unused)
             const int64_t bh = (static_cast<int64_t>(b) * nseg + min(s0 + u, nseg - 1)) * H + h;
-            loc[u] = buf[bh * NP + e];
+            loc[u] = *reinterpret_cast<const float4 *>(buf + bh * NP + e);
             dec[u] = __expf(tot[bh]);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (s0 + u < nseg) {
                 const int64_t bh = (static_cast<int64_t>(b) * nseg + s0 + u) * H + h;
-                buf[bh * NP + e] = v;
-                v = fmaf(dec[u], v, loc[u]);
+                *reinterpret_cast<float4 *>(buf + bh * NP + e) = v;
+                v.x = fmaf(dec[u], v.x, loc[u].x);
+                v.y = fmaf(dec[u], v.y, loc[u].y);
+                v.z = fmaf(dec[u], v.z, loc[u].z);
+                v.w = fmaf(dec[u], v.w, loc[u].w);
             }
         }
     }
     if (h_out)
-        h_out[(static_cast<int64_t>(b) * H + h) * NP + e] = v;
+        *reinterpret_cast<float4 *>(h_out + (static_cast<int64_t>(b) * H + h) * NP + e) = v;
 }
 
 
@@ -1463,7 +1469,7 @@ hipError_t run_prefix_mfma(const Shape &s, int64_t len, int chunk, const Seq &in
         return e;
     // 2. states entering each segment (in place); the final state when nothing else follows
     {
-        dim3 grid(static_cast<unsigned>((kN * kP + 255) / 256), s.H, s.b);
+        dim3 grid(static_cast<unsigned>((kN * kP / 4 + 255) / 256), s.H, s.b);
         k_seg_scan<<<grid, 256, 0, st>>>(segs, tot, p.nseg, s.H, h_init, full ? nullptr : h_out);
         if ((e = hipGetLastError()) != hipSuccess || !full)
             return e;
