@@ -312,12 +312,16 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
             const int h = h0 + hh;
             const bool more = hh + 1 < hpw;
             const int hn = more ? h + 1 : h;
-            // the head's copies are in, and every read of the other set (the head before) is done
-            workgroup_lds_barrier<0>();
+            // the head's copies are in, and every read of the other set (the head before) is
+            // done. Memory operations complete in order and the last PBW of this wavefront are
+            // the head before's y stores (issued after the copies): those may still be in
+            // flight (before the first head, nothing is)
+            workgroup_lds_barrier<PBW>();
             if constexpr (table_wave)
                 load_head(DIR, hn, hd);
             copy_state(PN{}, hh + 1);
             copy_x(PN{}, hn, more ? 0 : static_cast<int>(x_bytes));
+            __builtin_amdgcn_sched_barrier(0);  // the copies stay ahead of the y stores
             const __bf16 *hop = HOP(P);
             const __bf16 *xs0 = XF(P);
             const __bf16 *xs1 = XR(P);
