@@ -149,15 +149,17 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
         const auto r = dir ? rDr : rDf;
         hd.d0 = __builtin_amdgcn_raw_buffer_load_b16(r, (2 * lane * H + h) * 2, 0, 0);
         hd.d1 = __builtin_amdgcn_raw_buffer_load_b16(r, ((2 * lane + 1) * H + h) * 2, 0, 0);
-        hd.A = dir ? a.A_rev[h] : a.A[h];  // the reverse scan has its own decay
-        if constexpr (DCH) {
-            const float *dsrc = dir ? a.D_rev : a.D;
+        const float *asrc = dir ? a.A_rev : a.A;  // the reverse scan has its own decay
+        hd.A = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_range(asrc, H * 4), h * 4, 0, 0));
+        // the reverse skip weight reads 0 when there is none (a zero-byte range): a select on
+        // the loaded value would have to wait for the load before the copies that follow
+        const float *dsrc = dir ? a.D_rev : a.D;
+        if constexpr (DCH)
             hd.D = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                                  buffer_range(dsrc, dsrc ? H * kP * 4 : 0), (h * kP + lane) * 4, 0, 0));
-        } else {
-            const float dv = (dir && a.D_rev ? a.D_rev : a.D)[h];
-            hd.D = dir && !a.D_rev ? 0.f : dv;
-        }
+        else
+            hd.D = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                 buffer_range(dsrc, dsrc ? H * 4 : 0), h * 4, 0, 0));
         __builtin_amdgcn_sched_barrier(0);  // all of them ahead of the copies that follow
     };
     auto build_tables = [&](int dir, int buf, const Head &hd) {
