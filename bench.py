@@ -51,8 +51,8 @@ def parse():
                          "ramps up over the first ~20 ms of work after the host-side set-up)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--only", choices=("headline", "c1", "c2prefix", "builds", "fullwindow", "step4", "build4",
-                                       "build3"),
+    ap.add_argument("--only", choices=("headline", "c0", "c1", "c2prefix", "builds", "fullwindow", "step4",
+                                       "build4", "build3"),
                     help="run one workload only (for profiler runs); step4: the running set's step "
                          "(16 block steps + commit) on a seeded cached state, no prefix build; build4, "
                          "build3: the running set's / the long-context cache's prefix build alone")
@@ -369,6 +369,18 @@ def headline(args, torch, np, bdssm, configs, inputs):
               file=sys.stderr, flush=True)
         sys.exit(3)
 
+    # cold: the same 16 steps with the cached states rotated over R copies of the operand form
+    # (R x 100.7 MB > 512 MiB), so that no state a step reads can still sit in the 256 MB
+    # last-level cache from an earlier read; the inputs are distinct per step anyway
+    nb_ops_one = bdssm.state_ops_bytes(d)
+    R = (512 << 20) // nb_ops_one + 1
+    ops_rot = [ops.clone() for _ in range(R)]
+    cold_fns = [(lambda f=f, r=r, y=y, o=ops_rot[i % R]: bdssm.block_step_ops(d, T, o, f, r, Ad, Dd, y))
+                for i, ((f, r), y) in enumerate(zip(steps, ys))]
+    cold_us = graph_us(torch, lambda: [fn() for fn in cold_fns], reps=max(args.steps, 5)) / S
+    del ops_rot, cold_fns
+    torch.cuda.empty_cache()
+
     # the dominant kernel's launches one by one (HIP events on the launch stream)
     per_launch = launch_times_us(torch, step_fns, reps=3)
     blk_us = median([t for v in per_launch for t in v])
@@ -389,6 +401,8 @@ def headline(args, torch, np, bdssm, configs, inputs):
         "block_step": {"launches_per_step": S, "graph_us": round(part_us["block_step"], 3),
                        "launch_us": round(blk_us, 3), "alg_bytes": nb_step,
                        "hbm_frac": round(nb_step / (blk_us * 1e-6) / HBM_PEAK, 4),
+                       "cold_us": round(cold_us, 3), "cold_hbm_frac": round(nb_step / (cold_us * 1e-6) / HBM_PEAK, 4),
+                       "cold_states": R,
                        "active_tokens_per_s": round(b * T / (blk_us * 1e-6), 1)},
         "commit_refresh": {"launches_per_step": 1, "graph_us": round(part_us["commit_refresh"], 3),
                            "launch_us": round(commit_us, 3), "alg_bytes": nb_commit,
@@ -406,6 +420,15 @@ def headline(args, torch, np, bdssm, configs, inputs):
                                                         "commit_refresh": "commit_refresh_c4"}[dom]))
     roof.update({"kernel": kname, "part": dom, "work_per_launch": work, "avg_launch_us": round(avg, 3),
                  "launches_per_step": S if dom == "block_step" else 1})
+    if dom == "block_step":
+        # the window's 16 steps read the same cached states (100.7 MB), part of which the 256 MB
+        # last-level cache still holds from the step before; with the states rotated over
+        # more than 512 MiB every byte comes from HBM
+        roof.update({"cold_avg_launch_us": round(cold_us, 3),
+                     "cold_frac": round(work / (cold_us * 1e-6) / HBM_PEAK, 4),
+                     "note": "frac: the workload as it runs (each cached state re-read by the window's 16 "
+                             "steps, partly served by the last-level cache); cold_frac: states rotated over "
+                             "> 512 MiB, every byte from HBM"})
     out = {"metric": METRIC, "value": round(active / (wall / args.steps), 1), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
            "gpu_ms_per_step": round(gpu_ms_per_step, 4),
@@ -429,6 +452,32 @@ def headline(args, torch, np, bdssm, configs, inputs):
     del steps, clean, ys, ops, h, h0, ws
     torch.cuda.empty_cache()
     return out
+
+
+# ---------------------------------------------------------------- config 0: tiny fp32 block step
+def config0(torch, bdssm, configs, inputs, steps=64):
+    """The tiny fp32 shape (4 heads x 16, d_state 16, T = 16): 64 block steps from the fp32
+    cached state, seeded host draws with distinct inputs per step, in one graph; and one
+    launch between synchronizations."""
+    cfg = configs.get(0)
+    b, H, P, N, G, T = cfg.batch, cfg.nheads, cfg.headdim, cfg.d_state, cfg.ngroups, cfg.block_len
+    A, D = inputs.params(cfg)
+    Ad, Dd = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
+    d = bdssm.dims(b, H, P, N, G, cfg.in_dtype, bdssm.F32)
+    st = [(bdssm.seq_to_device(inputs.block(cfg, 0, s, inputs.FWD)), bdssm.seq_to_device(inputs.block(cfg, 0, s, inputs.REV)))
+          for s in range(steps)]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(10)
+    h = torch.randn((b, H, N, P), device="cuda", generator=gen) * 0.1
+    ys = [torch.empty((b, T, H, P), device="cuda") for _ in range(steps)]
+    us = graph_us(torch, lambda: [bdssm.block_step(d, T, h, f, r, Ad, Dd, y) for (f, r), y in zip(st, ys)], reps=20) / steps
+    one = median(launch_times_us(torch, [lambda: bdssm.block_step(d, T, h, st[0][0], st[0][1], Ad, Dd, ys[0])],
+                                 reps=20)[0])
+    nb = block_step_bytes(b, H, P, N, G, T, 4, 4)
+    return {"workload": "tiny fp32 shape (4 heads x 16, d_state 16), T=16: 64 block steps with distinct inputs "
+                        "in one graph", "us_per_step": round(us, 3), "single_launch_us": round(one, 3),
+            "active_tokens_per_s": round(b * T / (us * 1e-6), 1), "alg_bytes": nb,
+            "hbm_frac": round(nb / (us * 1e-6) / HBM_PEAK, 5)}
 
 
 # ---------------------------------------------------------------- config 1: batch-1 block cycle
@@ -505,6 +554,19 @@ def config1(args, torch, np, bdssm, configs, inputs):
     res["prefix_scan_us"] = round(graph_us(torch, run_prefix, reps=20), 3)
     nb = block_step_bytes(b, H, P, N, G, T, 2, 2)
     res["block_step_hbm_frac"] = round(nb / (res["block_step_us"] * 1e-6) / HBM_PEAK, 4)
+    # cold: RC steps in one graph, each with its own copy of the cached state's operand form,
+    # its own inputs and output (RC x ~3.7 MB > 512 MiB: nothing a step reads was read before)
+    per_set = bdssm.state_ops_bytes(d) + 2 * b * T * (H * P + H + 2 * G * N) * 2 + b * T * H * P * 2
+    RC = (512 << 20) // per_set + 1
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(21)
+    cold = [(h_ops.clone(), dev_seq(torch, gen, b, T, H, P, G, N), dev_seq(torch, gen, b, T, H, P, G, N),
+             torch.empty((b, T, H, P), dtype=torch.bfloat16, device="cuda")) for _ in range(RC)]
+    us = graph_us(torch, lambda: [bdssm.block_step_ops(d, T, o, f, r, Ad, Dd, y) for o, f, r, y in cold], reps=5)
+    res["block_step_cold_us"] = round(us / RC, 3)
+    res["block_step_cold_sets"] = RC
+    del cold
+    torch.cuda.empty_cache()
     res["block_step_from_fp32_state_us"] = round(graph_us(torch, run_blocks_fp32, reps=20) / S, 3)
     pf = prefix_flops(b, H, P, N, G, L, Q)
     res["prefix_mfma_frac"] = round(pf / (res["prefix_scan_us"] * 1e-6) / MFMA_BF16_PEAK, 4)
@@ -559,11 +621,15 @@ def full_window_c1(torch, np, bdssm, configs, inputs, block_step_us=None, reps=1
     fn = lambda: bdssm.full_window(d, L, Q, fwd, rev, Ad, Dd, None, None, y, ws)
     fn()
     torch.cuda.synchronize()
-    us = median(launch_times_us(torch, [fn], reps=reps)[0])
+    # device time of one call (a warmed graph of the call, median over replays), as the block
+    # step it is compared with is timed; the call's latency from the host beside it
+    us = graph_us(torch, fn, reps=reps)
+    single_us = median(launch_times_us(torch, [fn], reps=reps)[0])
     nb = 2 * prefix_bytes(b, H, P, N, G, L, Q, 2, 2, False) + b * L * H * P * 2
     out = {"workload": "full-window bidirectional scan (both directions from zero over 8192 prefix + 32 block "
                        "tokens, all outputs, bf16 y), 700M shape, batch 1: one denoising step of the "
-                       "comparison system", "avg_us": round(us, 2), "window_tokens": L,
+                       "comparison system", "avg_us": round(us, 2), "single_call_us": round(single_us, 2),
+           "window_tokens": L,
            "hbm_frac": round(nb / (us * 1e-6) / HBM_PEAK, 4), "alg_bytes": nb,
            "mfma_frac": round(2 * prefix_flops(b, H, P, N, G, L, Q) / (us * 1e-6) / MFMA_BF16_PEAK, 4)}
     if block_step_us:
@@ -588,11 +654,15 @@ def config2_prefix(torch, np, bdssm, configs, inputs, reps=10):
     fn = lambda: bdssm.prefix_scan(d, L, Q, pre, Ad, Dd, None, y, cs, ho, ws, wsb)
     fn()
     torch.cuda.synchronize()
-    us = median(launch_times_us(torch, [fn], reps=reps)[0])
+    # device time of one call: its three kernels captured as one graph, warmed, median over
+    # replays (the launches' host gaps are not the kernels' work); the latency of a single
+    # call from the host, launch by launch on an idle GPU, is reported beside it
+    us = graph_us(torch, fn, reps=reps)
+    single_us = median(launch_times_us(torch, [fn], reps=reps)[0])
     fl = prefix_flops(b, H, P, N, G, L, Q)
     nb = prefix_bytes(b, H, P, N, G, L, Q, 2, 2, True)
     return {"workload": "prefix scan, 350M shape (32 heads x 64, d_state 128), 65,536 tokens, chunk 256, bf16 y + "
-                        "fp32 chunk states", "avg_us": round(us, 3),
+                        "fp32 chunk states", "avg_us": round(us, 3), "single_call_us": round(single_us, 3),
             "prefix_tokens_per_s": round(b * L / (us * 1e-6), 1),
             "roofline": make_roofline("mfma", fl, us, traffic_for("prefix_scan_c2")),
             "mfma_frac_causal_count": round(prefix_flops_causal(b, H, P, N, G, L, Q) / (us * 1e-6) / MFMA_BF16_PEAK, 4),
@@ -767,6 +837,7 @@ def main():
     bdssm.load()
     if args.only:
         fn = {"headline": lambda: headline(args, torch, np, bdssm, configs, inputs),
+              "c0": lambda: config0(torch, bdssm, configs, inputs),
               "c1": lambda: config1(args, torch, np, bdssm, configs, inputs),
               "c2prefix": lambda: config2_prefix(torch, np, bdssm, configs, inputs),
               "builds": lambda: builds(torch, np, bdssm, configs, inputs),
@@ -780,7 +851,8 @@ def main():
     if not args.no_secondary:
         print("[bench] secondary workloads", file=sys.stderr, flush=True)
         c1 = config1(args, torch, np, bdssm, configs, inputs)
-        out["secondary"] = {"config1_block_cycle": c1,
+        out["secondary"] = {"config0_block_step": config0(torch, bdssm, configs, inputs),
+                            "config1_block_cycle": c1,
                             "config2_prefix_scan": config2_prefix(torch, np, bdssm, configs, inputs),
                             "full_window_config1": full_window_c1(torch, np, bdssm, configs, inputs,
                                                                   c1["block_step_us"])}
