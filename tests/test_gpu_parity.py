@@ -368,6 +368,8 @@ def test_config4_running_set_shape():
     (1, 4, 1, 4096, 256, False, False, True),   # state only, several segments + scan
     (64, 8, 1, 192, 64, True, True, True),      # one segment per (stream, head): single pass
     (64, 8, 4, 300, 64, False, False, True),    # single pass, state only, ragged
+    # one stream, 32 segments of 10 sub-chunks, the last a single ragged one
+    (1, 16, 1, 20037, 256, True, True, True),
 ])
 def test_prefix_matrix_core_paths(b, H, G, L, chunk, want_y, want_cs, init):
     rng = np.random.default_rng(L + H)
