@@ -150,7 +150,9 @@ def block_step_bytes(b, H, P, N, G, T, in_bytes, y_bytes):
 
 
 def commit_bytes(b, H, P, N, G, T, in_bytes):
-    return 2 * b * H * N * P * 4 + b * T * (H * P + H + G * N) * in_bytes + 2 * H * 4
+    """State read and written, the clean block's x, dt and B, and A (a commit writes no y, so
+    neither C nor D is read)."""
+    return 2 * b * H * N * P * 4 + b * T * (H * P + H + G * N) * in_bytes + H * 4
 
 
 def state_ops_bytes(b, H, P, N):
