@@ -557,7 +557,7 @@ def config1(args, torch, np, bdssm, configs, inputs):
     nb = block_step_bytes(b, H, P, N, G, T, 2, 2)
     res["block_step_hbm_frac"] = round(nb / (res["block_step_us"] * 1e-6) / HBM_PEAK, 4)
     # cold: RC steps in one graph, each with its own copy of the cached state's operand form,
-    # its own inputs and output (RC x ~3.7 MB > 512 MiB: nothing a step reads was read before)
+    # its own inputs and output (RC x ~2.2 MB > 512 MiB: nothing a step reads was read before)
     per_set = bdssm.state_ops_bytes(d) + 2 * b * T * (H * P + H + 2 * G * N) * 2 + b * T * H * P * 2
     RC = (512 << 20) // per_set + 1
     gen = torch.Generator(device="cuda")
